@@ -1,0 +1,269 @@
+// libspecverify C ABI: argument checks, workspace layout, kernel launches.
+// The operations and their contracts are documented in include/specverify.h.
+#include "specverify.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+sv_status fail(sv_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+sv_status device_fail(hipError_t e, const char* what) {
+  return fail(SV_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool dtype_ok(int32_t d) { return d == SV_F32 || d == SV_BF16; }
+
+sv_status check_workspace(const void* ws, size_t have, size_t need) {
+  if (need == 0) return SV_OK;
+  if (ws == nullptr) return fail(SV_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(SV_E_WORKSPACE, "workspace is not 256-byte aligned");
+  if (have < need) return fail(SV_E_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+  return SV_OK;
+}
+
+constexpr int64_t kMaxGrid = 0x7fffffff;
+
+}  // namespace
+
+extern "C" {
+
+int sv_abi_version(void) { return SV_ABI_VERSION; }
+
+const char* sv_status_string(int status) {
+  switch (status) {
+    case SV_OK: return "ok";
+    case SV_E_ARG: return "invalid argument";
+    case SV_E_DTYPE: return "unsupported dtype";
+    case SV_E_WORKSPACE: return "workspace missing, misaligned or too small";
+    case SV_E_DEVICE: return "HIP device error";
+    default: return "unknown status";
+  }
+}
+
+const char* sv_last_error(void) { return g_err; }
+
+size_t sv_workspace_bytes(int op, int64_t batch, int64_t total_rows, int64_t vocab) {
+  if (batch < 0 || total_rows < 0 || vocab <= 0) return 0;
+  switch (op) {
+    case SV_OP_GREEDY:
+    case SV_OP_TREE:
+      return sv::align256(static_cast<size_t>(total_rows * sv::row_segments(total_rows, vocab)) * 8);
+    case SV_OP_SAMPLE:
+      return sv::sample_layout(batch, total_rows, vocab).bytes;
+    default:
+      return 0;
+  }
+}
+
+sv_status sv_ngram_draft(const int32_t* ctx, const int32_t* ctx_len, int32_t batch,
+                         int32_t ctx_stride, int32_t window, int32_t k, int32_t* draft_ids,
+                         int32_t* draft_len, int32_t* dev_status, void* stream) {
+  if (batch < 0) return fail(SV_E_ARG, "batch < 0");
+  if (ctx_stride < 1) return fail(SV_E_ARG, "ctx_stride < 1");
+  if (window < 1 || window > sv::kMaxWindow) return fail(SV_E_ARG, "window must be in [1, 64]");
+  if (k < 0 || k > 1024) return fail(SV_E_ARG, "k must be in [0, 1024]");
+  if (batch == 0) return SV_OK;
+  if (ctx == nullptr || ctx_len == nullptr || draft_len == nullptr || (k > 0 && draft_ids == nullptr))
+    return fail(SV_E_ARG, "null pointer argument");
+  (void)hipGetLastError();
+  const hipError_t e = sv::launch_ngram(ctx, ctx_len, batch, ctx_stride, window, k, draft_ids, draft_len,
+                                        dev_status, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SV_OK : device_fail(e, "sv_ngram_draft launch");
+}
+
+sv_status sv_verify_greedy(const void* target_logits, int32_t t_dtype, int32_t t_rows, int64_t vocab,
+                           const int32_t* t_row_start, const int32_t* draft_ids,
+                           const int32_t* draft_len, int32_t batch, int32_t k_max,
+                           const int32_t* max_new, int32_t eos_id, int32_t* out_tokens,
+                           int32_t* out_count, int32_t* out_accepted, int32_t* dev_status,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(t_dtype)) return fail(SV_E_DTYPE, "t_dtype must be SV_F32 or SV_BF16");
+  if (batch < 0) return fail(SV_E_ARG, "batch < 0");
+  if (vocab < 1 || vocab > INT32_MAX) return fail(SV_E_ARG, "vocab must be in [1, 2^31)");
+  if (k_max < 0 || k_max >= sv::kMaxChainRows) return fail(SV_E_ARG, "k_max must be in [0, 255]");
+  if (t_rows < 0) return fail(SV_E_ARG, "t_rows < 0");
+  if (batch == 0) return SV_OK;
+  if (t_rows < 1) return fail(SV_E_ARG, "t_rows < 1");
+  if (target_logits == nullptr || t_row_start == nullptr || draft_len == nullptr ||
+      out_tokens == nullptr || out_count == nullptr || out_accepted == nullptr ||
+      (k_max > 0 && draft_ids == nullptr))
+    return fail(SV_E_ARG, "null pointer argument");
+  const int32_t nseg = sv::row_segments(t_rows, vocab);
+  if (static_cast<int64_t>(t_rows) * nseg > kMaxGrid) return fail(SV_E_ARG, "too many rows");
+  const size_t need = sv_workspace_bytes(SV_OP_GREEDY, batch, t_rows, vocab);
+  if (sv_status s = check_workspace(workspace, workspace_bytes, need)) return s;
+
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  uint64_t* keys = static_cast<uint64_t*>(workspace);
+  hipError_t e = sv::launch_row_argmax(t_dtype, target_logits, t_rows, vocab, nseg, keys, st);
+  if (e != hipSuccess) return device_fail(e, "sv_verify_greedy argmax launch");
+  sv::GreedyArgs a{};
+  a.tgt = target_logits;
+  a.V = vocab;
+  a.t_rows = t_rows;
+  a.t_rs = t_row_start;
+  a.ids = draft_ids;
+  a.dlen = draft_len;
+  a.B = batch;
+  a.k_max = k_max;
+  a.max_new = max_new;
+  a.eos = eos_id;
+  a.out_tok = out_tokens;
+  a.out_cnt = out_count;
+  a.out_acc = out_accepted;
+  a.status = dev_status;
+  a.keys = keys;
+  a.nseg = nseg;
+  e = sv::launch_greedy_resolve(a, st);
+  return e == hipSuccess ? SV_OK : device_fail(e, "sv_verify_greedy resolve launch");
+}
+
+sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t_rows,
+                           const void* draft_probs, int32_t q_dtype, int32_t q_rows, int64_t vocab,
+                           const int32_t* t_row_start, const int32_t* q_row_start,
+                           const int32_t* draft_ids, const int32_t* draft_len, int32_t batch,
+                           int32_t k_max, float temperature, const float* uniforms,
+                           const int32_t* max_new, int32_t eos_id, int32_t* out_tokens,
+                           int32_t* out_count, int32_t* out_accepted, float* out_diag,
+                           float* out_resid, int32_t* dev_status, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(t_dtype) || !dtype_ok(q_dtype))
+    return fail(SV_E_DTYPE, "t_dtype and q_dtype must be SV_F32 or SV_BF16");
+  if (batch < 0) return fail(SV_E_ARG, "batch < 0");
+  if (vocab < 1 || vocab > INT32_MAX) return fail(SV_E_ARG, "vocab must be in [1, 2^31)");
+  if (k_max < 0 || k_max >= sv::kMaxChainRows) return fail(SV_E_ARG, "k_max must be in [0, 255]");
+  if (t_rows < 0 || q_rows < 0) return fail(SV_E_ARG, "t_rows and q_rows must be >= 0");
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(SV_E_ARG, "temperature must be finite and > 0 (T = 0 is sv_verify_greedy)");
+  if (batch == 0) return SV_OK;
+  if (t_rows < 1) return fail(SV_E_ARG, "t_rows < 1");
+  if (target_logits == nullptr || t_row_start == nullptr || q_row_start == nullptr ||
+      draft_len == nullptr || uniforms == nullptr || out_tokens == nullptr || out_count == nullptr ||
+      out_accepted == nullptr || (k_max > 0 && draft_ids == nullptr) ||
+      (q_rows > 0 && draft_probs == nullptr))
+    return fail(SV_E_ARG, "null pointer argument");
+  const int32_t nseg = sv::row_segments(t_rows, vocab);
+  const int64_t ntiles = sv::tiles_of(vocab);
+  const int64_t chunks = (ntiles + sv::kSampleTilesPerBlock - 1) / sv::kSampleTilesPerBlock;
+  if (static_cast<int64_t>(t_rows) * nseg > kMaxGrid || static_cast<int64_t>(batch) * chunks > kMaxGrid)
+    return fail(SV_E_ARG, "problem too large for one launch");
+  const sv::SampleLayout L = sv::sample_layout(batch, t_rows, vocab);
+  if (sv_status s = check_workspace(workspace, workspace_bytes, L.bytes)) return s;
+
+  char* ws = static_cast<char*>(workspace);
+  const float c = sv::kLog2e / temperature;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  float2* partial = reinterpret_cast<float2*>(ws + L.partial_off);
+  hipError_t e = sv::launch_row_stats(t_dtype, target_logits, t_rows, vocab, nseg, c, partial, st);
+  if (e != hipSuccess) return device_fail(e, "sv_verify_sample row-stats launch");
+  sv::SampleArgs a{};
+  a.tgt = target_logits;
+  a.dq = draft_probs;
+  a.V = vocab;
+  a.t_rows = t_rows;
+  a.q_rows = q_rows;
+  a.t_rs = t_row_start;
+  a.q_rs = q_row_start;
+  a.ids = draft_ids;
+  a.dlen = draft_len;
+  a.B = batch;
+  a.k_max = k_max;
+  a.c = c;
+  a.invT = 1.f / temperature;
+  a.u = uniforms;
+  a.max_new = max_new;
+  a.eos = eos_id;
+  a.out_tok = out_tokens;
+  a.out_cnt = out_count;
+  a.out_acc = out_accepted;
+  a.diag = out_diag;
+  a.resid = out_resid;
+  a.status = dev_status;
+  a.partial = partial;
+  a.nseg = nseg;
+  a.tiles = reinterpret_cast<double*>(ws + L.tiles_off);
+  a.counters = reinterpret_cast<uint32_t*>(ws + L.counter_off);
+  a.ntiles = static_cast<int32_t>(ntiles);
+  a.tpb = sv::kSampleTilesPerBlock;
+  a.chunks = static_cast<int32_t>(chunks);
+  e = sv::launch_sample_resolve(t_dtype, q_dtype, a, st);
+  return e == hipSuccess ? SV_OK : device_fail(e, "sv_verify_sample resolve launch");
+}
+
+sv_status sv_verify_tree(const void* target_logits, int32_t t_dtype, const void* draft_probs,
+                         int32_t q_dtype, int64_t vocab, const int32_t* parent,
+                         const int32_t* node_token, int32_t batch, int32_t n_nodes,
+                         float temperature, const float* uniforms, int32_t* out_tokens,
+                         int32_t* out_count, int32_t* out_accepted, int32_t* out_path,
+                         float* out_diag, int32_t* dev_status, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(t_dtype) || !dtype_ok(q_dtype))
+    return fail(SV_E_DTYPE, "t_dtype and q_dtype must be SV_F32 or SV_BF16");
+  if (batch < 0) return fail(SV_E_ARG, "batch < 0");
+  if (n_nodes < 1 || n_nodes > sv::kMaxTreeNodes) return fail(SV_E_ARG, "n_nodes must be in [1, 1024]");
+  if (vocab < 1 || vocab > static_cast<int64_t>(sv::kMaxTreeTiles) * 4096)
+    return fail(SV_E_ARG, "tree vocab must be in [1, 1048576]");
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(SV_E_ARG, "temperature must be finite and > 0");
+  if (batch == 0) return SV_OK;
+  if (target_logits == nullptr || draft_probs == nullptr || parent == nullptr ||
+      node_token == nullptr || uniforms == nullptr || out_tokens == nullptr ||
+      out_count == nullptr || out_accepted == nullptr || out_path == nullptr)
+    return fail(SV_E_ARG, "null pointer argument");
+  const int64_t rows = static_cast<int64_t>(batch) * n_nodes;
+  if (rows > INT32_MAX) return fail(SV_E_ARG, "too many rows");
+  const int32_t nseg = sv::row_segments(rows, vocab);
+  if (rows * nseg > kMaxGrid) return fail(SV_E_ARG, "too many rows");
+  const size_t need = sv_workspace_bytes(SV_OP_TREE, batch, rows, vocab);
+  if (sv_status s = check_workspace(workspace, workspace_bytes, need)) return s;
+
+  const float c = sv::kLog2e / temperature;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  float2* partial = static_cast<float2*>(workspace);
+  hipError_t e = sv::launch_row_stats(t_dtype, target_logits, rows, vocab, nseg, c, partial, st);
+  if (e != hipSuccess) return device_fail(e, "sv_verify_tree row-stats launch");
+  sv::TreeArgs a{};
+  a.tgt = target_logits;
+  a.dq = draft_probs;
+  a.V = vocab;
+  a.parent = parent;
+  a.token = node_token;
+  a.B = batch;
+  a.N = n_nodes;
+  a.c = c;
+  a.invT = 1.f / temperature;
+  a.u = uniforms;
+  a.out_tok = out_tokens;
+  a.out_cnt = out_count;
+  a.out_acc = out_accepted;
+  a.out_path = out_path;
+  a.diag = out_diag;
+  a.status = dev_status;
+  a.partial = partial;
+  a.nseg = nseg;
+  a.ntiles = static_cast<int32_t>(sv::tiles_of(vocab));
+  e = sv::launch_tree_walk(t_dtype, q_dtype, a, st);
+  return e == hipSuccess ? SV_OK : device_fail(e, "sv_verify_tree walk launch");
+}
+
+}  // extern "C"

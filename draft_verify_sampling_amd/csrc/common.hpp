@@ -1,0 +1,216 @@
+// Device helpers shared by the verify kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kBlock = 256;            // threads per block for the streaming kernels
+constexpr int kWave = 64;
+constexpr int kTile = 4096;            // elements per sampling tile (inverse-CDF unit)
+constexpr int kPerThreadTile = kTile / kBlock;  // 16 contiguous elements per thread
+
+
+// Status bits (the public header documents them).
+constexpr int kFlagBadRequest = 1;
+constexpr int kFlagBadToken = 2;
+constexpr int kFlagNonfinite = 4;
+constexpr int kFlagOverBudget = 8;
+constexpr int kFlagFallback = 16;
+constexpr int kFlagBadTree = 32;
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Element formats.  A 16-byte vector holds kPerVec elements.
+// ---------------------------------------------------------------------------
+struct F32 {
+  static constexpr int kSize = 4;
+  static constexpr int kPerVec = 4;
+  __device__ __forceinline__ static float at(const void* row, int64_t i) {
+    return static_cast<const float*>(row)[i];
+  }
+  __device__ __forceinline__ static void unpack(const uint4& w, float* v) {
+    v[0] = __uint_as_float(w.x);
+    v[1] = __uint_as_float(w.y);
+    v[2] = __uint_as_float(w.z);
+    v[3] = __uint_as_float(w.w);
+  }
+};
+
+struct BF16 {
+  static constexpr int kSize = 2;
+  static constexpr int kPerVec = 8;
+  // bfloat16 -> float is exact: the pattern is the upper half of a float.
+  __device__ __forceinline__ static float at(const void* row, int64_t i) {
+    return __uint_as_float(static_cast<uint32_t>(static_cast<const uint16_t*>(row)[i]) << 16);
+  }
+  __device__ __forceinline__ static void unpack(const uint4& w, float* v) {
+    v[0] = __uint_as_float(w.x << 16);
+    v[1] = __uint_as_float(w.x & 0xffff0000u);
+    v[2] = __uint_as_float(w.y << 16);
+    v[3] = __uint_as_float(w.y & 0xffff0000u);
+    v[4] = __uint_as_float(w.z << 16);
+    v[5] = __uint_as_float(w.z & 0xffff0000u);
+    v[6] = __uint_as_float(w.w << 16);
+    v[7] = __uint_as_float(w.w & 0xffff0000u);
+  }
+};
+
+template <class D>
+__device__ __forceinline__ const void* row_ptr(const void* base, int64_t row, int64_t V) {
+  return static_cast<const char*>(base) + row * V * D::kSize;
+}
+
+// Number of leading elements of a row before its first 16-byte boundary.
+template <class D>
+__device__ __forceinline__ int64_t head_elems(const void* row, int64_t V) {
+  int64_t h = static_cast<int64_t>((16u - (reinterpret_cast<uintptr_t>(row) & 15u)) & 15u) / D::kSize;
+  return h < V ? h : V;
+}
+
+// Load `n` consecutive elements starting at element e of a row.  Uses 16-byte
+// loads when the run is aligned and complete, element loads otherwise; elements
+// at or beyond V read as `fill`.
+template <class D, int n>
+__device__ __forceinline__ void load_run(const void* row, int64_t V, int64_t e, float* v,
+                                         float fill) {
+  static_assert(n % D::kPerVec == 0, "run must be whole vectors");
+  const bool fast = ((reinterpret_cast<uintptr_t>(row) + e * D::kSize) & 15u) == 0 && e + n <= V;
+  if (fast) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const char*>(row) + e * D::kSize);
+#pragma unroll
+    for (int j = 0; j < n / D::kPerVec; ++j) D::unpack(p[j], v + j * D::kPerVec);
+  } else {
+#pragma unroll
+    for (int j = 0; j < n; ++j) v[j] = (e + j < V) ? D::at(row, e + j) : fill;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Online softmax pairs: (m, s) with s = sum exp2((x - m) * c), c = log2(e)/T.
+// ---------------------------------------------------------------------------
+struct MS {
+  float m;
+  float s;
+};
+
+__device__ __forceinline__ MS ms_combine(MS a, MS b, float c) {
+  const float M = fmaxf(a.m, b.m);
+  if (M == -INFINITY) return MS{M, 0.f};
+  const float Mc = M * c;
+  return MS{M, a.s * ex2(fmaf(a.m, c, -Mc)) + b.s * ex2(fmaf(b.m, c, -Mc))};
+}
+
+// Fold n values into a running pair: one rescale per group, pairwise group sum.
+template <int n>
+__device__ __forceinline__ void ms_fold(MS& acc, const float* x, float c) {
+  float cm = x[0];
+#pragma unroll
+  for (int j = 1; j < n; ++j) cm = fmaxf(cm, x[j]);
+  const float M = fmaxf(acc.m, cm);
+  if (M == -INFINITY) return;
+  const float Mc = M * c;
+  float e[n];
+#pragma unroll
+  for (int j = 0; j < n; ++j) e[j] = ex2(fmaf(x[j], c, -Mc));
+#pragma unroll
+  for (int w = 1; w < n; w *= 2) {
+#pragma unroll
+    for (int j = 0; j + w < n; j += 2 * w) e[j] += e[j + w];
+  }
+  acc.s = acc.s * ex2(fmaf(acc.m, c, -Mc)) + e[0];
+  acc.m = M;
+}
+
+__device__ __forceinline__ MS wave_ms(MS v, float c) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    MS o{__shfl_xor(v.m, off, kWave), __shfl_xor(v.s, off, kWave)};
+    v = ms_combine(v, o, c);
+  }
+  return v;
+}
+
+// Block-wide (m, s) reduction; result valid in every thread.  `sh` holds
+// 2 * (blockDim/64) floats.
+__device__ __forceinline__ MS block_ms(MS v, float c, float* sh) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+  v = wave_ms(v, c);
+  if (lane == 0) {
+    sh[2 * wid] = v.m;
+    sh[2 * wid + 1] = v.s;
+  }
+  __syncthreads();
+  MS r{sh[0], sh[1]};
+  for (int w = 1; w < nw; ++w) r = ms_combine(r, MS{sh[2 * w], sh[2 * w + 1]}, c);
+  __syncthreads();
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Plain block reductions / scans.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Sum over the block of up to 3 doubles at once; results valid in every thread.
+// `sh` holds 3 * (blockDim/64) doubles.
+template <int n>
+__device__ __forceinline__ void block_sum(double* v, double* sh) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+#pragma unroll
+  for (int j = 0; j < n; ++j) v[j] = wave_sum(v[j]);
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < n; ++j) sh[n * wid + j] = v[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < n; ++j) {
+    double t = 0.0;
+    for (int w = 0; w < nw; ++w) t += sh[n * w + j];
+    v[j] = t;
+  }
+  __syncthreads();
+}
+
+// Exclusive prefix sum over the block (thread order); returns this thread's
+// exclusive prefix, and the block total in *total.  `sh` holds blockDim/64 + 1
+// doubles.
+__device__ __forceinline__ double block_exclusive_scan(double x, double* total, double* sh) {
+  // (x only enters through the inclusive wave scan below)
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const int nw = blockDim.x / kWave;
+  double incl = x;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const double y = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += y;
+  }
+  if (lane == kWave - 1) sh[wid] = incl;
+  __syncthreads();
+  double base = 0.0, tot = 0.0;
+  for (int w = 0; w < nw; ++w) {
+    const double t = sh[w];
+    if (w < wid) base += t;
+    tot += t;
+  }
+  __syncthreads();
+  *total = tot;
+  double excl = __shfl_up(incl, 1, kWave);
+  if (lane == 0) excl = 0.0;
+  return base + excl;
+}
+
+__device__ __forceinline__ void flag(int32_t* status, int bits) {
+  if (status != nullptr && bits != 0) atomicOr(status, bits);
+}
+
+}  // namespace sv

@@ -1,0 +1,186 @@
+// Greedy (T = 0) chain verify.
+//
+// Method ("第 13 篇：推理引擎一次猜几个字——草稿 + 验证", section ③ and its notes;
+// "Speculative decoding explained", four-case table): the target's pick at each
+// drafted position is the argmax of its row; drafts are compared left to right,
+// the round stops at the first difference, the drafts before it are kept and the
+// target's own pick is appended (after a full match: the pick of the row after
+// the last draft, unless the request's budget is used up).
+//
+// Two kernels.  k_row_argmax: grid = rows * nseg blocks; each block streams a
+// slice of one row with 16-byte loads and leaves one 64-bit key per slice,
+// (order-preserving bits of the value) << 32 | ~index, so that one unsigned max
+// picks the largest value and, among equal values, the lowest index; a slice
+// holding a NaN leaves the key 0xFFFF...F instead.  k_greedy_resolve: one thread
+// per request combines the keys of its k_b + 1 rows and runs the prefix compare.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace sv {
+
+namespace {
+
+constexpr uint64_t kNanKey = ~0ull;
+
+__device__ __forceinline__ uint32_t order_bits(float v) {
+  uint32_t b = __float_as_uint(v);
+  if ((b & 0x7fffffffu) == 0u) b = 0u;  // -0 and +0 compare equal
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+struct Best {
+  float v;
+  int64_t i;
+  bool nan;
+};
+
+__device__ __forceinline__ void best_update(Best& s, float v, int64_t i) {
+  s.nan |= (v != v);
+  if (v > s.v || (v == s.v && i < s.i)) {
+    s.v = v;
+    s.i = i;
+  }
+}
+
+__device__ __forceinline__ uint64_t best_key(const Best& s) {
+  if (s.nan) return kNanKey;
+  return (static_cast<uint64_t>(order_bits(s.v)) << 32) |
+         static_cast<uint64_t>(~static_cast<uint32_t>(s.i));
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, kWave);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, kWave);
+    const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+}  // namespace
+
+template <class D, int U>
+__global__ __launch_bounds__(kBlock) void k_row_argmax(const void* __restrict__ rows, int64_t V,
+                                                       int32_t nseg, uint64_t* __restrict__ keys) {
+  __shared__ uint64_t sh[kBlock / kWave];
+  const int64_t row = blockIdx.x / nseg;
+  const int32_t seg = blockIdx.x - static_cast<int32_t>(row) * nseg;
+  const void* base = row_ptr<D>(rows, row, V);
+  const int64_t head = head_elems<D>(base, V);
+  const int64_t nvec = (V - head) / D::kPerVec;
+  const int64_t v0 = nvec * seg / nseg, v1 = nvec * (seg + 1) / nseg;
+  const uint4* vp = reinterpret_cast<const uint4*>(static_cast<const char*>(base) + head * D::kSize);
+
+  // sentinel index INT32_MAX: loses every tie against a real element
+  Best best{-INFINITY, 0x7fffffff, false};
+  int64_t v = v0 + threadIdx.x;
+  for (; v + (U - 1) * kBlock < v1; v += U * kBlock) {
+    uint4 w[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) w[j] = vp[v + j * kBlock];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      float x[D::kPerVec];
+      D::unpack(w[j], x);
+      const int64_t e = head + (v + j * kBlock) * D::kPerVec;
+#pragma unroll
+      for (int t = 0; t < D::kPerVec; ++t) best_update(best, x[t], e + t);
+    }
+  }
+  for (; v < v1; v += kBlock) {
+    float x[D::kPerVec];
+    D::unpack(vp[v], x);
+    const int64_t e = head + v * D::kPerVec;
+#pragma unroll
+    for (int t = 0; t < D::kPerVec; ++t) best_update(best, x[t], e + t);
+  }
+  if (seg == 0)
+    for (int64_t i = threadIdx.x; i < head; i += kBlock) best_update(best, D::at(base, i), i);
+  if (seg == nseg - 1)
+    for (int64_t i = head + nvec * D::kPerVec + threadIdx.x; i < V; i += kBlock)
+      best_update(best, D::at(base, i), i);
+
+  uint64_t key = wave_max_u64(best_key(best));
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  if (lane == 0) sh[wid] = key;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint64_t r = sh[0];
+    for (int w = 1; w < kBlock / kWave; ++w) r = sh[w] > r ? sh[w] : r;
+    keys[blockIdx.x] = r;
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void k_greedy_resolve(GreedyArgs a) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= a.B) return;
+  const int ustride = a.k_max + 1;
+  int32_t* out = a.out_tok + static_cast<int64_t>(b) * ustride;
+  const int k = a.dlen[b];
+  const int ts = a.t_rs[b];
+  int bits = 0;
+  if (k < 0 || k > a.k_max || ts < 0 || static_cast<int64_t>(ts) + k >= a.t_rows) bits = kFlagBadRequest;
+  const int32_t* x = a.ids + static_cast<int64_t>(b) * a.k_max;
+  if (!bits)
+    for (int i = 0; i < k; ++i)
+      if (x[i] < 0 || x[i] >= a.V) bits = kFlagBadToken;
+  int m = 0, pick = 0;
+  if (!bits) {
+    if (a.max_new != nullptr && k > a.max_new[b]) flag(a.status, kFlagOverBudget);
+    // every row of the request must be NaN-free; stop comparing at the first mismatch
+    m = k;
+    for (int i = 0; i <= k; ++i) {
+      const uint64_t* kk = a.keys + static_cast<int64_t>(ts + i) * a.nseg;
+      uint64_t best = 0;
+      for (int s = 0; s < a.nseg; ++s) best = kk[s] > best ? kk[s] : best;
+      if (best == kNanKey) {
+        bits = kFlagNonfinite;
+        break;
+      }
+      const int am = static_cast<int>(~static_cast<uint32_t>(best));
+      if (i < m && i < k && x[i] != am) m = i;
+      if (i == m) pick = am;
+    }
+  }
+  if (bits) {
+    for (int i = 0; i < ustride; ++i) out[i] = -1;
+    a.out_cnt[b] = 0;
+    a.out_acc[b] = 0;
+    flag(a.status, bits);
+    return;
+  }
+  int cnt = 0;
+  bool stop = false;
+  for (int i = 0; i < m && !stop; ++i) {
+    out[cnt++] = x[i];
+    if (a.eos >= 0 && x[i] == a.eos) stop = true;
+  }
+  if (!stop) out[cnt++] = pick;
+  if (a.max_new != nullptr) {
+    const int budget = a.max_new[b] > 0 ? a.max_new[b] : 0;
+    if (cnt > budget) cnt = budget;
+  }
+  for (int i = cnt; i < ustride; ++i) out[i] = -1;
+  a.out_cnt[b] = cnt;
+  a.out_acc[b] = m;
+}
+
+hipError_t launch_row_argmax(int dtype, const void* rows, int64_t n_rows, int64_t V, int32_t nseg,
+                             uint64_t* keys, hipStream_t stream) {
+  const dim3 grid(static_cast<uint32_t>(n_rows * nseg)), block(kBlock);
+  if (dtype == kDtypeBF16)
+    hipLaunchKernelGGL((k_row_argmax<BF16, 4>), grid, block, 0, stream, rows, V, nseg, keys);
+  else
+    hipLaunchKernelGGL((k_row_argmax<F32, 4>), grid, block, 0, stream, rows, V, nseg, keys);
+  return hipGetLastError();
+}
+
+hipError_t launch_greedy_resolve(const GreedyArgs& a, hipStream_t stream) {
+  const dim3 grid(static_cast<uint32_t>((a.B + kBlock - 1) / kBlock)), block(kBlock);
+  hipLaunchKernelGGL(k_greedy_resolve, grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,129 @@
+// Host-side launchers of the verify kernels and the workspace layout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kDtypeF32 = 0;
+constexpr int kDtypeBF16 = 1;
+constexpr int kMaxChainRows = 256;     // k_max + 1 rows per request at most
+constexpr int kMaxTreeNodes = 1024;
+constexpr int kMaxTreeTiles = 256;     // tree vocab <= 256 * 4096
+constexpr int kSampleTilesPerBlock = 4;
+constexpr int kMaxWindow = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Segments per row for the streaming statistics kernels: about 32 Ki elements
+// per block, and at least ~1024 blocks in total when rows are few.
+inline int32_t row_segments(int64_t rows, int64_t V) {
+  int64_t nseg = (V + 32767) / 32768;
+  if (rows > 0 && rows * nseg < 1024) {
+    const int64_t want = (1024 + rows - 1) / rows;
+    const int64_t cap = (V + 2047) / 2048;
+    nseg = want < cap ? want : cap;
+  }
+  if (nseg < 1) nseg = 1;
+  if (nseg > 64) nseg = 64;
+  return static_cast<int32_t>(nseg);
+}
+
+inline int64_t tiles_of(int64_t V) { return (V + 4095) / 4096; }
+
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+struct SampleLayout {
+  size_t partial_off, tiles_off, counter_off, bytes;
+};
+
+inline SampleLayout sample_layout(int64_t B, int64_t t_rows, int64_t V) {
+  SampleLayout L{};
+  const int64_t nseg = row_segments(t_rows, V);
+  L.partial_off = 0;
+  L.tiles_off = align256(static_cast<size_t>(t_rows * nseg) * 8);
+  L.counter_off = L.tiles_off + align256(static_cast<size_t>(B * tiles_of(V)) * 3 * 8);
+  L.bytes = L.counter_off + align256(static_cast<size_t>(B) * 4);
+  return L;
+}
+
+struct SampleArgs {
+  const void* tgt;
+  const void* dq;
+  int64_t V;
+  int32_t t_rows, q_rows;
+  const int32_t* t_rs;
+  const int32_t* q_rs;
+  const int32_t* ids;
+  const int32_t* dlen;
+  int32_t B, k_max;
+  float c;      // log2(e) / T
+  float invT;   // 1 / T
+  const float* u;
+  const int32_t* max_new;
+  int32_t eos;
+  int32_t* out_tok;
+  int32_t* out_cnt;
+  int32_t* out_acc;
+  float* diag;
+  float* resid;
+  int32_t* status;
+  const float2* partial;
+  int32_t nseg;
+  double* tiles;
+  uint32_t* counters;
+  int32_t ntiles, tpb, chunks;
+};
+
+struct GreedyArgs {
+  const void* tgt;
+  int64_t V;
+  int32_t t_rows;
+  const int32_t* t_rs;
+  const int32_t* ids;
+  const int32_t* dlen;
+  int32_t B, k_max;
+  const int32_t* max_new;
+  int32_t eos;
+  int32_t* out_tok;
+  int32_t* out_cnt;
+  int32_t* out_acc;
+  int32_t* status;
+  const uint64_t* keys;
+  int32_t nseg;
+};
+
+struct TreeArgs {
+  const void* tgt;
+  const void* dq;
+  int64_t V;
+  const int32_t* parent;
+  const int32_t* token;
+  int32_t B, N;
+  float c, invT;
+  const float* u;
+  int32_t* out_tok;
+  int32_t* out_cnt;
+  int32_t* out_acc;
+  int32_t* out_path;
+  float* diag;
+  int32_t* status;
+  const float2* partial;
+  int32_t nseg;
+  int32_t ntiles;
+};
+
+hipError_t launch_row_stats(int dtype, const void* rows, int64_t n_rows, int64_t V, int32_t nseg,
+                            float c, float2* partial, hipStream_t stream);
+hipError_t launch_sample_resolve(int t_dtype, int q_dtype, const SampleArgs& a,
+                                 hipStream_t stream);
+hipError_t launch_row_argmax(int dtype, const void* rows, int64_t n_rows, int64_t V, int32_t nseg,
+                             uint64_t* keys, hipStream_t stream);
+hipError_t launch_greedy_resolve(const GreedyArgs& a, hipStream_t stream);
+hipError_t launch_ngram(const int32_t* ctx, const int32_t* ctx_len, int32_t B, int32_t stride,
+                        int32_t window, int32_t k, int32_t* ids, int32_t* lens, int32_t* status,
+                        hipStream_t stream);
+hipError_t launch_tree_walk(int t_dtype, int q_dtype, const TreeArgs& a, hipStream_t stream);
+
+}  // namespace sv

@@ -1,0 +1,189 @@
+/*
+ * libspecverify -- the verify step of speculative decoding on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Four operations, each following the pages that define it:
+ *
+ *   sv_ngram_draft    history n-gram (prompt-lookup) drafter
+ *                     ("第 13 篇：推理引擎一次猜几个字——草稿 + 验证", notes under
+ *                     section ③: take the context's last tokens as a window,
+ *                     find the same fragment earlier, propose what followed).
+ *   sv_verify_greedy  greedy (T = 0) prefix verify
+ *                     (same article, section ③ pseudocode; "Speculative
+ *                     decoding explained", four-case table).
+ *   sv_verify_sample  speculative sampling: keep draft x with probability
+ *                     min(1, p(x)/q(x)), stop at the first rejection, draw the
+ *                     replacement from norm(max(0, p - q)), or one extra token
+ *                     from p when every draft is kept
+ *                     ("投机解码:为什么一个字都不改", sections "改进" and
+ *                     "一轮能出几个 token"; p = softmax(logits / T) per the
+ *                     figure "一次目标前向验 k 个草稿 token").
+ *   sv_verify_tree    recursive speculative sampling over a flattened draft
+ *                     tree, siblings tried in order with the residual update
+ *                     in between ("Speculative Decoding II", EAGLE section:
+ *                     the SpecInfer-style tree verify; EAGLE-2 worked example
+ *                     for the flattened layout).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All array arguments are DEVICE pointers on the current HIP device, except
+ *   where marked "host".  `stream` is a hipStream_t (NULL = the default
+ *   stream).  Every call only enqueues work on `stream` and returns; outputs,
+ *   `dev_status` and the workspace are valid after the caller synchronises
+ *   that stream.
+ * - The caller owns every buffer.  The library allocates nothing, keeps no
+ *   pointer after returning, and holds no global mutable state except the
+ *   thread-local text behind sv_last_error().
+ * - Row data: `t_dtype` / `q_dtype` select SV_F32 (float) or SV_BF16 (bfloat16
+ *   bit patterns).  A row is `vocab` consecutive elements; row r starts at
+ *   element r * vocab.  Any alignment is accepted; 16-byte aligned rows take the
+ *   fastest path.
+ * - Host-side argument checks return an error code and launch nothing.  Data
+ *   problems found on the device never trap: they OR an SV_FLAG_* bit into
+ *   *dev_status (if not NULL; the caller clears it) and the affected request
+ *   gets a defined output.  A request with SV_FLAG_BAD_REQUEST, BAD_TOKEN,
+ *   NONFINITE or BAD_TREE is invalid: count 0, accepted 0, all tokens -1.
+ * - Workspace (greedy, sample, tree): caller-owned device memory of at least
+ *   sv_workspace_bytes(...) bytes, 256-byte aligned, ZERO-FILLED ONCE before
+ *   its first use.  Every call leaves its counters at zero again, so it can be
+ *   reused without clearing.  Calls that may run concurrently (different
+ *   streams) need separate workspaces.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SV_ABI_VERSION 1
+
+typedef enum {
+  SV_OK = 0,
+  SV_E_ARG = 1,        /* bad argument (null pointer, size out of range, T <= 0, ...) */
+  SV_E_DTYPE = 2,      /* unsupported dtype */
+  SV_E_WORKSPACE = 3,  /* workspace missing, misaligned or too small */
+  SV_E_DEVICE = 4      /* a HIP call failed; sv_last_error() has its text */
+} sv_status;
+
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+typedef enum { SV_OP_GREEDY = 0, SV_OP_SAMPLE = 1, SV_OP_TREE = 2 } sv_op;
+
+/* dev_status bits */
+#define SV_FLAG_BAD_REQUEST 1   /* draft count outside [0,k_max], row index out of range,
+                                   context length outside [0,stride] */
+#define SV_FLAG_BAD_TOKEN 2     /* a draft / node token outside [0,vocab) */
+#define SV_FLAG_NONFINITE 4     /* sampled: a target row whose normaliser sum exp(l/T - M)
+                                   is not finite and positive; the draft row a residual is
+                                   taken from sums to NaN; a non-finite residual mass.
+                                   greedy: a NaN in a target row */
+#define SV_FLAG_OVER_BUDGET 8   /* more drafts than max_new[b] (output still produced,
+                                   truncated to max_new[b]) */
+#define SV_FLAG_FALLBACK 16     /* a residual max(0, p - q) had zero mass: the token was
+                                   drawn from p (chain) / p was left unchanged (tree) */
+#define SV_FLAG_BAD_TREE 32     /* parent[b,0] != -1, or parent[b,c] not in [0,c) */
+
+int sv_abi_version(void);
+const char* sv_status_string(int status);
+/* Text of the last non-OK return on the calling thread ("" if none). */
+const char* sv_last_error(void);
+
+/* Workspace bytes for op (SV_OP_GREEDY / SV_OP_SAMPLE / SV_OP_TREE), for a call
+ * with `batch` requests, `total_rows` target rows (greedy/sample: t_rows; tree:
+ * batch * n_nodes) and `vocab` columns.  Host function.  0 on bad input. */
+size_t sv_workspace_bytes(int op, int64_t batch, int64_t total_rows, int64_t vocab);
+
+/* History n-gram drafter.
+ * ctx [batch, ctx_stride] int32 tokens; ctx_len [batch]: tokens of request b are
+ * ctx[b, 0..ctx_len[b]).  Key = the last `window` tokens.  The most recent
+ * earlier occurrence of the key that is followed by at least one token (start j
+ * <= n - window - 1) wins; the draft is the up-to-k tokens after it (it stops at
+ * the context end).  No occurrence, or n < window + 1: draft_len = 0.
+ * Outputs: draft_ids [batch, k] int32 (-1 padded), draft_len [batch].
+ * Limits: 1 <= window <= 64, 0 <= k <= 1024, batch >= 0 (0: nothing launched),
+ * ctx_stride >= 1.  A ctx_len outside [0, ctx_stride] gives draft_len 0 and
+ * SV_FLAG_BAD_REQUEST. */
+sv_status sv_ngram_draft(const int32_t* ctx, const int32_t* ctx_len, int32_t batch,
+                         int32_t ctx_stride, int32_t window, int32_t k,
+                         int32_t* draft_ids, int32_t* draft_len,
+                         int32_t* dev_status, void* stream);
+
+/* Greedy (T = 0) verify.
+ * target_logits: t_rows rows of `vocab` scores.  Request b (draft count
+ * k_b = draft_len[b], drafts draft_ids[b, 0..k_b), row stride k_max) uses rows
+ * t_row_start[b] .. t_row_start[b] + k_b.  a_i = argmax of row i (lowest id
+ * among equal maxima; +0 and -0 are equal).  m = first i < k_b with
+ * draft_ids[b,i] != a_i, else k_b.  Emitted: draft_ids[b,0..m) then a_m,
+ * cut after the first eos_id (if eos_id >= 0) and at max_new[b] tokens (if
+ * max_new is not NULL).
+ * Outputs: out_tokens [batch, k_max+1] int32 (-1 padded), out_count [batch],
+ * out_accepted [batch] (= m).  draft_ids may be NULL when k_max == 0. */
+sv_status sv_verify_greedy(const void* target_logits, int32_t t_dtype, int32_t t_rows,
+                           int64_t vocab, const int32_t* t_row_start,
+                           const int32_t* draft_ids, const int32_t* draft_len,
+                           int32_t batch, int32_t k_max, const int32_t* max_new,
+                           int32_t eos_id, int32_t* out_tokens, int32_t* out_count,
+                           int32_t* out_accepted, int32_t* dev_status,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Speculative-sampling chain verify.
+ * target_logits [t_rows, vocab]; draft_probs [q_rows, vocab] holds the draft's
+ * probabilities (used as given, not renormalised).  Request b uses target rows
+ * t_row_start[b] + i (i = 0..k_b) and draft rows q_row_start[b] + i (i < k_b);
+ * requests may share rows.  p_i = softmax(target row i / temperature).
+ * uniforms [batch, k_max+1] float in [0,1): u[b,i] (i < k_b) tests draft i,
+ * which is kept iff u * q_i(x_i) < p_i(x_i); m = first draft not kept (else k_b).
+ * u[b,k_b] draws the last token: from max(0, p_m - q_m) if m < k_b (from p_m,
+ * with SV_FLAG_FALLBACK, if that has zero mass), else from p_{k_b}: the
+ * smallest id whose running mass exceeds u times the total.  Emission,
+ * eos_id, max_new and outputs as for sv_verify_greedy.
+ * Optional outputs (NULL to skip): out_diag [batch, k_max+1, 4] float =
+ * (M_i = max(l/T), S_i = sum exp(l/T - M_i), p_i(x_i), q_i(x_i)) for i <= k_b
+ * (p, q = 0 at i = k_b; rows beyond k_b untouched); out_resid [batch] = total
+ * mass of the weights the last token was drawn from.
+ * temperature must be finite and > 0. */
+sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t_rows,
+                           const void* draft_probs, int32_t q_dtype, int32_t q_rows,
+                           int64_t vocab, const int32_t* t_row_start,
+                           const int32_t* q_row_start, const int32_t* draft_ids,
+                           const int32_t* draft_len, int32_t batch, int32_t k_max,
+                           float temperature, const float* uniforms,
+                           const int32_t* max_new, int32_t eos_id,
+                           int32_t* out_tokens, int32_t* out_count, int32_t* out_accepted,
+                           float* out_diag, float* out_resid, int32_t* dev_status,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* Tree verify.
+ * Node c of request b (flattened order, node 0 = root) owns target row
+ * b*n_nodes + c and draft row b*n_nodes + c; the draft row of a node is the q
+ * its children were proposed from.  parent [batch, n_nodes] int32 (root -1,
+ * else an earlier node); node_token [batch, n_nodes] (root entry ignored).
+ * uniforms [batch, n_nodes]: u[b,c-1] tests node c, u[b,n_nodes-1] draws the
+ * last token.  Walk: cur = root, p = softmax(target row of cur / T),
+ * q = draft row of cur; children of cur in index order: keep c iff
+ * u * q(x_c) < p(x_c); kept -> emit x_c, descend, reload p and q; not kept ->
+ * p <- norm(max(0, p - q)) before the next sibling.  When no child is kept the
+ * last token is drawn from the current p.
+ * Outputs: out_tokens [batch, n_nodes] (-1 padded), out_count, out_accepted
+ * (kept nodes), out_path [batch, n_nodes] (kept node ids, -1 padded).
+ * Optional out_diag [batch, n_nodes, 4] = (M_c, S_c, p_parent(x_c),
+ * q_parent(x_c)) with the parent's softmax before any residual update
+ * (p, q = 0 at the root).  1 <= n_nodes <= 1024. */
+sv_status sv_verify_tree(const void* target_logits, int32_t t_dtype,
+                         const void* draft_probs, int32_t q_dtype, int64_t vocab,
+                         const int32_t* parent, const int32_t* node_token,
+                         int32_t batch, int32_t n_nodes, float temperature,
+                         const float* uniforms, int32_t* out_tokens, int32_t* out_count,
+                         int32_t* out_accepted, int32_t* out_path, float* out_diag,
+                         int32_t* dev_status, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

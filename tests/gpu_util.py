@@ -1,0 +1,82 @@
+"""Helpers for the GPU tests: move generated inputs to the device, run the
+library, compare with the oracle."""
+import sys
+
+import numpy as np
+import torch
+
+import draft_verify_sampling_amd as sv
+
+DEV = "cuda"
+BOUNDARY = 1e-6      # a uniform this close to a decision edge may flip it
+RTOL = 1e-5          # probabilities, normalisers, ratios, residual mass
+
+
+def say(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def rows_to_dev(a, kind):
+    if kind == "f32":
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+    bits = np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)
+    return torch.from_numpy(bits).to(DEV).view(torch.bfloat16)
+
+
+def i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+
+
+def f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def run_sample(ci, status=None, workspace=None, max_new=None, eos_id=-1):
+    tgt = rows_to_dev(ci.target, ci.t_kind)
+    dft = rows_to_dev(ci.draft, ci.q_kind)
+    mn = i32(max_new) if max_new is not None else None
+    tok, cnt, acc, dg, rs = sv.sv_verify_sample(
+        tgt, dft, i32(ci.t_row_start), i32(ci.q_row_start), i32(ci.draft_ids[:, :ci.k_max]),
+        i32(ci.draft_len), ci.T, f32(ci.uniforms), max_new=mn, eos_id=eos_id, diag=True,
+        dev_status=status, workspace=workspace)
+    torch.cuda.synchronize()
+    return dict(tokens=tok.cpu().numpy(), count=cnt.cpu().numpy(), accepted=acc.cpu().numpy(),
+                diag=dg.cpu().numpy(), resid=rs.cpu().numpy())
+
+
+def run_greedy(target, kind, t_row_start, draft_ids, draft_len, max_new=None, eos_id=-1,
+               status=None):
+    tok, cnt, acc = sv.sv_verify_greedy(rows_to_dev(target, kind), i32(t_row_start), i32(draft_ids),
+                                        i32(draft_len), i32(max_new) if max_new is not None else None,
+                                        eos_id, dev_status=status)
+    torch.cuda.synchronize()
+    return dict(tokens=tok.cpu().numpy(), count=cnt.cpu().numpy(), accepted=acc.cpu().numpy())
+
+
+def run_tree(ti, status=None):
+    tok, cnt, acc, pth, dg = sv.sv_verify_tree(
+        rows_to_dev(ti.target, ti.t_kind), rows_to_dev(ti.draft, ti.q_kind), i32(ti.parent),
+        i32(ti.token), ti.T, f32(ti.uniforms), diag=True, dev_status=status)
+    torch.cuda.synchronize()
+    return dict(tokens=tok.cpu().numpy(), count=cnt.cpu().numpy(), accepted=acc.cpu().numpy(),
+                path=pth.cpu().numpy(), diag=dg.cpu().numpy())
+
+
+def close(a, b, rtol=RTOL, atol=1e-30):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return np.abs(a - b) <= atol + rtol * np.abs(b)
+
+
+def compare_tokens(got, want, keys=("tokens", "count", "accepted")):
+    """Per request: equal, or a boundary case (some decision of the oracle lies
+    within BOUNDARY of its edge), or a failure.  Returns (n_boundary, failures)."""
+    B = want["count"].shape[0]
+    same = np.ones(B, dtype=bool)
+    for k in keys:
+        g, w = got[k], want[k]
+        same &= (g.reshape(B, -1) == w.reshape(B, -1)).all(axis=1)
+    near = np.nanmin(np.where(np.isnan(want["margins"]), np.inf, want["margins"]), axis=1) < BOUNDARY
+    bad = ~same & ~near
+    return int((~same & near).sum()), np.nonzero(bad)[0]

@@ -1,0 +1,111 @@
+"""The C-ABI library loads and exports what include/specverify.h declares; host-side
+argument checks return their documented codes without launching anything
+(CPU only: no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import draft_verify_sampling_amd as sv
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "specverify.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return set(re.findall(r"^\s*(?:sv_status|int|size_t|const char\*)\s+(sv_\w+)\s*\(",
+                          text, flags=re.M))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return sv.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert names == set(sv.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_strings(lib):
+    assert sv.abi_version() == 1
+    assert lib.sv_status_string(0) == b"ok"
+    assert b"argument" in lib.sv_status_string(1)
+    assert lib.sv_status_string(99) == b"unknown status"
+
+
+def test_workspace_sizes(lib):
+    assert sv.workspace_bytes(sv.SV_OP_SAMPLE, 64, 320, 248_320) % 256 == 0
+    assert sv.workspace_bytes(sv.SV_OP_SAMPLE, 64, 320, 248_320) >= 320 * 8 + 64 * 61 * 24 + 64 * 4
+    assert sv.workspace_bytes(sv.SV_OP_GREEDY, 64, 320, 32_000) >= 320 * 8
+    assert sv.workspace_bytes(sv.SV_OP_TREE, 32, 1920, 128_256) >= 1920 * 8
+    assert sv.workspace_bytes(sv.SV_OP_SAMPLE, -1, 1, 1) == 0
+    assert sv.workspace_bytes(7, 1, 1, 1) == 0
+
+
+def _err(lib):
+    return lib.sv_last_error().decode()
+
+
+def test_host_checks_sample(lib):
+    f = lib.sv_verify_sample
+    dummy = ctypes.c_void_p(256)  # never dereferenced: every call below fails on the host
+    base = dict(tgt=dummy, tdt=0, t_rows=5, dq=dummy, qdt=0, q_rows=4, V=100, trs=dummy, qrs=dummy,
+                ids=dummy, dlen=dummy, B=1, k_max=4, T=1.0, u=dummy, max_new=None, eos=-1,
+                out=dummy, cnt=dummy, acc=dummy, diag=None, resid=None, st=None, ws=None, wsb=0,
+                stream=None)
+
+    def call(**kw):
+        a = {**base, **kw}
+        return f(*a.values())
+
+    assert call(T=0.0) == 1 and "temperature" in _err(lib)
+    assert call(T=float("nan")) == 1
+    assert call(T=-1.0) == 1
+    assert call(tdt=5) == 2
+    assert call(qdt=-1) == 2
+    assert call(k_max=256) == 1
+    assert call(V=0) == 1
+    assert call(B=-1) == 1
+    assert call(tgt=None) == 1 and "null" in _err(lib)
+    assert call() == 3 and "workspace" in _err(lib)                     # workspace NULL
+    assert call(ws=ctypes.c_void_p(4096 + 8), wsb=1 << 30) == 3          # misaligned
+    assert call(ws=ctypes.c_void_p(4096), wsb=16) == 3                   # too small
+    assert call(B=0) == 0                                                # nothing to do
+
+
+def test_host_checks_greedy_tree_ngram(lib):
+    d = ctypes.c_void_p(256)
+    g = lib.sv_verify_greedy
+    assert g(d, 3, 5, 100, d, d, d, 1, 4, None, -1, d, d, d, None, None, 0, None) == 2
+    assert g(d, 1, 5, 100, d, d, d, 1, 300, None, -1, d, d, d, None, None, 0, None) == 1
+    assert g(d, 1, 5, 100, d, d, d, 1, 4, None, -1, d, d, d, None, None, 0, None) == 3
+    t = lib.sv_verify_tree
+    assert t(d, 1, d, 1, 100, d, d, 1, 0, 1.0, d, d, d, d, d, None, None, None, 0, None) == 1
+    assert t(d, 1, d, 1, 100, d, d, 1, 2000, 1.0, d, d, d, d, d, None, None, None, 0, None) == 1
+    assert t(d, 1, d, 1, 1 << 21, d, d, 1, 60, 1.0, d, d, d, d, d, None, None, None, 0, None) == 1
+    assert t(d, 1, d, 1, 100, d, d, 1, 60, 0.0, d, d, d, d, d, None, None, None, 0, None) == 1
+    assert t(d, 1, d, 1, 100, d, d, 1, 60, 1.0, d, d, d, d, d, None, None, None, 0, None) == 3
+    n = lib.sv_ngram_draft
+    assert n(d, d, 1, 16, 0, 4, d, d, None, None) == 1
+    assert n(d, d, 1, 16, 65, 4, d, d, None, None) == 1
+    assert n(d, d, 1, 16, 3, -1, d, d, None, None) == 1
+    assert n(d, d, 1, 0, 3, 4, d, d, None, None) == 1
+    assert n(None, d, 1, 16, 3, 4, d, d, None, None) == 1
+    assert n(d, d, 0, 16, 3, 4, d, d, None, None) == 0
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    import importlib
+    monkeypatch.setenv("SPECVERIFY_LIB", str(tmp_path / "nope.so"))
+    mod = importlib.reload(sv)
+    try:
+        with pytest.raises(mod.SpecVerifyError):
+            mod.load()
+    finally:
+        monkeypatch.delenv("SPECVERIFY_LIB")
+        importlib.reload(sv)

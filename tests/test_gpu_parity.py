@@ -1,0 +1,400 @@
+"""Parity of the HIP verify path with the float64 oracle, on an MI355X.
+
+Greedy and prompt-lookup results must be bit-exact.  Sampled results: the
+normalisers, probabilities at the drafted tokens and the residual mass within
+1e-5 relative; token ids equal except in requests where some uniform lies within
+1e-6 of its decision edge (counted, and required to be rare).
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import softmax as scipy_softmax
+
+import oracle
+import synth
+from tests.gpu_util import (say, run_sample, run_greedy, run_tree, close, compare_tokens,
+                            rows_to_dev, i32, f32, DEV)
+
+pytestmark = pytest.mark.gpu
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _status():
+    return torch.zeros(1, dtype=torch.int32, device=DEV)
+
+
+def _or(flags):
+    out = 0
+    for f in np.asarray(flags).ravel():
+        out |= int(f)
+    return out
+
+
+def _check_chain(ci, got, want, name, max_boundary_frac=1e-3):
+    nb, bad = compare_tokens(got, want)
+    say(f"{name}: {ci.B} requests, {nb} boundary cases")
+    assert bad.size == 0, f"{name}: mismatching requests {bad[:10]}"
+    assert nb <= max(2, max_boundary_frac * ci.B)
+    valid = want["count"] > 0
+    for b in np.nonzero(valid)[0][:4096]:
+        k = int(ci.draft_len[b])
+        d, e = got["diag"][b, :k + 1], want["diag"][b, :k + 1]
+        assert close(d[:, 0], e[:, 0], atol=1e-6).all(), (name, b, "M")
+        assert close(d[:, 1], e[:, 1]).all(), (name, b, "S")
+        assert close(d[:k, 2], e[:k, 2]).all(), (name, b, "p(x)")
+        assert close(d[:k, 3], e[:k, 3]).all(), (name, b, "q(x)")
+    same = (got["count"] == want["count"]) & (got["accepted"] == want["accepted"]) & valid
+    assert close(got["resid"][same], want["resid"][same], rtol=1e-5, atol=1e-12).all(), name
+
+
+def _oracle_sample(ci, **kw):
+    return oracle.verify_sample(ci.target, ci.t_kind, ci.draft, ci.q_kind, ci.V, ci.t_row_start,
+                                ci.q_row_start, ci.draft_ids[:, :ci.k_max], ci.draft_len, ci.k_max,
+                                ci.T, ci.uniforms, **kw)
+
+
+# ---------------------------------------------------------------------------
+# greedy + prompt lookup
+# ---------------------------------------------------------------------------
+def test_gpu_greedy_four_case_table():
+    say("greedy four-case table")
+    rows = [ln.split() for ln in open(os.path.join(GOLD, "p3_four_cases.txt"), encoding="utf-8")
+            if ln.strip() and not ln.startswith("#")]
+    path = rows[0][1]
+    sym = {s: i for i, s in enumerate("ABCDEFGX")}
+    for r in rows[1:]:
+        prefix, guess, kept, added, new = (("" if v == "-" else v) for v in r[1:])
+        k = len(guess)
+        tgt = np.zeros((k + 1, 8), dtype=np.float32)
+        for i in range(k + 1):
+            pos = len(prefix) + i
+            tgt[i, sym[path[pos] if pos < len(path) else "A"]] = 1.0
+        ids = np.array([[sym[s] for s in guess]], dtype=np.int32)
+        out = run_greedy(tgt, "f32", [0], ids, [k], max_new=[len(path) - len(prefix)])
+        got = "".join("ABCDEFGX"[t] for t in out["tokens"][0, :out["count"][0]])
+        assert got == kept + added and prefix + got == new
+        assert out["accepted"][0] == len(kept)
+
+
+@pytest.fixture(scope="module")
+def c2():
+    return synth.c2_greedy()
+
+
+def test_gpu_ngram_then_greedy_c2(c2):
+    say("prompt lookup + greedy, B=64 ctx=4096 V=32000")
+    import draft_verify_sampling_amd as sv
+    st = _status()
+    ids, lens = sv.sv_ngram_draft(i32(c2.ctx), i32(c2.ctx_len), c2.window, c2.k, dev_status=st)
+    torch.cuda.synchronize()
+    w_ids, w_lens, w_flags = oracle.ngram_draft(c2.ctx, c2.ctx_len, c2.window, c2.k)
+    assert np.array_equal(lens.cpu().numpy(), w_lens)
+    assert np.array_equal(ids.cpu().numpy(), w_ids)
+    assert int(st.item()) == 0
+    assert (w_lens > 0).sum() >= 8, "the planted repeats should give drafts"
+    t_rs = np.arange(c2.B, dtype=np.int32) * (c2.k + 1)
+    got = run_greedy(c2.target, "bf16", t_rs, w_ids, w_lens, status=st)
+    want = oracle.verify_greedy(c2.target, "bf16", c2.V, t_rs, w_ids, w_lens, c2.k)
+    for key in ("tokens", "count", "accepted"):
+        assert np.array_equal(got[key], want[key]), key
+    assert int(st.item()) == 0
+    say(f"  mean accepted {want['accepted'].mean():.2f}, mean tokens {want['count'].mean():.2f}")
+
+
+@pytest.mark.parametrize("kind,V", [("bf16", 4999), ("bf16", 8), ("f32", 3001), ("f32", 1)])
+def test_gpu_greedy_ties_ragged_unaligned(kind, V):
+    say(f"greedy ties/ragged kind={kind} V={V}")
+    rng = np.random.default_rng(V)
+    B, k_max = 97, 6
+    ks = rng.integers(0, k_max + 1, size=B).astype(np.int32)
+    t_rs = np.concatenate([[0], np.cumsum(ks + 1)[:-1]]).astype(np.int32)
+    rows = int((ks + 1).sum())
+    vals = rng.integers(-3, 4, size=(rows, V)).astype(np.float32)   # many ties
+    vals[vals == 0] = rng.choice([0.0, -0.0], size=int((vals == 0).sum()))
+    tgt = synth.to_bf16_bits(vals) if kind == "bf16" else vals
+    dec = oracle.widen(tgt, kind)
+    ids = np.full((B, k_max), -1, dtype=np.int32)
+    for b in range(B):
+        for i in range(ks[b]):
+            a = int(np.argmax(dec[t_rs[b] + i]))
+            ids[b, i] = a if rng.random() < 0.8 else int(rng.integers(0, V))
+    max_new = rng.integers(0, k_max + 3, size=B).astype(np.int32)
+    eos = int(rng.integers(0, V))
+    for mn, eo in ((None, -1), (max_new, eos)):
+        st = _status()
+        got = run_greedy(tgt, kind, t_rs, ids, ks, max_new=mn, eos_id=eo, status=st)
+        want = oracle.verify_greedy(tgt, kind, V, t_rs, ids, ks, k_max, max_new=mn, eos_id=eo)
+        for key in ("tokens", "count", "accepted"):
+            assert np.array_equal(got[key], want[key]), key
+        assert int(st.item()) == _or(want["flags"])
+
+
+def test_gpu_greedy_invalid_inputs():
+    say("greedy invalid inputs")
+    V, k = 300, 3
+    rng = np.random.default_rng(0)
+    tgt = rng.standard_normal((12, V)).astype(np.float32)
+    tgt[5, 17] = np.nan                   # request 1 uses rows 4..7
+    ids = rng.integers(0, V, size=(4, k)).astype(np.int32)
+    ids[2, 1] = V                         # bad token
+    t_rs = np.array([0, 4, 8, 11], dtype=np.int32)   # request 3: rows 11..14 out of range
+    ks = np.array([3, 3, 3, 3], dtype=np.int32)
+    st = _status()
+    got = run_greedy(tgt, "f32", t_rs, ids, ks, status=st)
+    want = oracle.verify_greedy(tgt, "f32", V, t_rs, ids, ks, k)
+    for key in ("tokens", "count", "accepted"):
+        assert np.array_equal(got[key], want[key]), key
+    assert list(want["count"]) == [int(want["count"][0]), 0, 0, 0]
+    assert int(st.item()) == _or(want["flags"]) == (oracle.FLAG_NONFINITE | oracle.FLAG_BAD_TOKEN |
+                                                    oracle.FLAG_BAD_REQUEST)
+
+
+def test_gpu_ngram_small_contexts():
+    say("prompt lookup, brute-force-sized contexts")
+    import draft_verify_sampling_amd as sv
+    rng = np.random.default_rng(2)
+    B, stride = 300, 700
+    ctx = rng.integers(0, 3, size=(B, stride)).astype(np.int32)
+    lens = rng.integers(0, stride + 1, size=B).astype(np.int32)
+    lens[:5] = [0, 1, 2, 3, 4]
+    lens[5] = stride + 1                 # bad length
+    for w in (1, 2, 3, 7):
+        for k in (0, 1, 4, 9):
+            st = _status()
+            ids, dl = sv.sv_ngram_draft(i32(ctx), i32(lens), w, k, dev_status=st)
+            torch.cuda.synchronize()
+            wi, wl, wf = oracle.ngram_draft(ctx, lens, w, k)
+            assert np.array_equal(dl.cpu().numpy(), wl), (w, k)
+            assert np.array_equal(ids.cpu().numpy(), wi), (w, k)
+            assert int(st.item()) == _or(wf)
+
+
+# ---------------------------------------------------------------------------
+# sampled chain
+# ---------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def c1():
+    return synth.c1_chain()
+
+
+def test_gpu_sample_c1_parity_and_tv(c1):
+    say("sampled chain, fixed prefix, V=2048 fp32, 200,000 rounds")
+    st = _status()
+    got = run_sample(c1, status=st)
+    want = _oracle_sample(c1)
+    _check_chain(c1, got, want, "c1")
+    assert int(st.item()) == 0
+    rng = np.random.default_rng(99)
+    for i in range(c1.k_max + 1):
+        sel = got["count"] > i
+        n = int(sel.sum())
+        if n < 2000:
+            continue
+        p = scipy_softmax(c1.target[i].astype(np.float64) / c1.T)
+        emp = np.bincount(got["tokens"][sel, i], minlength=c1.V) / n
+        tv = 0.5 * np.abs(emp - p).sum()
+        noise = np.percentile([0.5 * np.abs(rng.multinomial(n, p) / n - p).sum() for _ in range(100)], 99)
+        say(f"  position {i}: n={n} TV={tv:.4f} noise q99={noise:.4f}")
+        assert tv <= noise
+
+
+@pytest.fixture(scope="module")
+def c3():
+    return synth.c3_sampled()
+
+
+def test_gpu_sample_c3_full(c3):
+    say("sampled chain B=64 k=4 V=248320 bf16 T=0.7")
+    st = _status()
+    got = run_sample(c3, status=st)
+    want = _oracle_sample(c3)
+    _check_chain(c3, got, want, "c3")
+    assert int(st.item()) == 0
+    say(f"  mean accepted {want['accepted'].mean():.2f}")
+
+
+def test_gpu_sample_deterministic(c3):
+    say("sampled chain run twice")
+    a = run_sample(c3)
+    b = run_sample(c3)
+    for key in a:
+        assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("tk,qk,V", [("bf16", "bf16", 4999), ("f32", "bf16", 12289),
+                                     ("f32", "f32", 777), ("bf16", "f32", 4096), ("bf16", "bf16", 1)])
+def test_gpu_sample_small_ragged(tk, qk, V):
+    say(f"sampled ragged tk={tk} qk={qk} V={V}")
+    ci = synth.sampled_chain(40 + V % 7, 41, np.random.default_rng(V).integers(0, 9, size=41), V,
+                             0.9, sd=2.0, n_boost=min(3, V), boost=4.0, sigma=1.0, kind=tk)
+    if qk != tk:
+        dec = synth.decode(ci.draft, tk)
+        ci.draft = synth.encode(dec, qk)
+        ci.q_kind = qk
+    st = _status()
+    got = run_sample(ci, status=st)
+    want = _oracle_sample(ci)
+    _check_chain(ci, got, want, f"ragged {tk}/{qk}/{V}", max_boundary_frac=0.05)
+    assert int(st.item()) == _or(want["flags"])
+
+
+@pytest.fixture(scope="module")
+def c4():
+    return synth.c4_ragged()
+
+
+def test_gpu_sample_c4_full(c4):
+    say("ragged sampled chain B=256 k in 1..8 V=151936 bf16 T=1")
+    st = _status()
+    got = run_sample(c4, status=st)
+    want = _oracle_sample(c4)
+    _check_chain(c4, got, want, "c4")
+    assert int(st.item()) == 0
+
+
+def test_gpu_sample_edge_cases():
+    say("sampled chain edge cases")
+    rng = np.random.default_rng(8)
+    V, k = 5000, 3
+    B = 12
+    ks = np.array([0, 3, 3, 3, 3, 3, 3, 3, 3, 3, 2, 3], dtype=np.int32)
+    ci = synth.sampled_chain(90, B, ks, V, 1.0, sd=2.0, n_boost=3, boost=5.0, sigma=1.0, kind="f32")
+    t = ci.target
+    q = ci.draft
+    # request 2: residual with zero mass -> fallback to p (draft row of position 0 all ones)
+    q[ci.q_row_start[2]] = 1.0
+    ci.uniforms[2, 0] = 0.99
+    # request 3: NaN in a target row
+    t[ci.t_row_start[3] + 1, 10] = np.nan
+    # request 4: +inf in a target row
+    t[ci.t_row_start[4] + 2, 11] = np.inf
+    # request 5: NaN in the draft row at the break (force a rejection at 0)
+    q[ci.q_row_start[5], 12] = np.nan
+    ci.draft_ids[5, 0] = 13
+    q[ci.q_row_start[5], 13] = 1.0
+    ci.uniforms[5, 0] = 0.999
+    # request 6: bad token
+    ci.draft_ids[6, 1] = V + 3
+    # request 7: row start out of range
+    ci.t_row_start[7] = t.shape[0] - 2
+    # request 8: -inf logits are allowed (zero probability)
+    t[ci.t_row_start[8]:ci.t_row_start[8] + 4, :100] = -np.inf
+    # request 9: u = 0 everywhere
+    ci.uniforms[9] = 0.0
+    ci.uniforms[11] = 0.0                # keep every draft with p > 0
+    max_new = np.array([5, 5, 5, 5, 5, 5, 5, 5, 5, 5, 1, 2], dtype=np.int32)  # 10, 11: over budget
+    eos = int(ci.draft_ids[1, 1]) if ks[1] > 1 else -1
+    for mn, eo in ((None, -1), (max_new, eos)):
+        st = _status()
+        got = run_sample(ci, status=st, max_new=mn, eos_id=eo)
+        want = _oracle_sample(ci, max_new=mn, eos_id=eo)
+        nb, bad = compare_tokens(got, want)
+        assert bad.size == 0, bad
+        assert int(st.item()) == _or(want["flags"])
+    fl = want["flags"]
+    assert fl[2] & oracle.FLAG_FALLBACK and fl[3] & oracle.FLAG_NONFINITE
+    assert fl[4] & oracle.FLAG_NONFINITE and fl[5] & oracle.FLAG_NONFINITE
+    assert fl[6] & oracle.FLAG_BAD_TOKEN and fl[7] & oracle.FLAG_BAD_REQUEST
+    assert fl[11] & oracle.FLAG_OVER_BUDGET and got["count"][11] == 2
+
+
+def test_gpu_greedy_equals_sampling_on_one_hot():
+    say("one-hot targets: sampled == greedy")
+    rng = np.random.default_rng(31)
+    V, k, B = 1000, 4, 64
+    a = rng.integers(0, V, size=B * (k + 1))
+    tgt = np.zeros((B * (k + 1), V), dtype=np.float32)
+    tgt[np.arange(B * (k + 1)), a] = 800.0
+    q = rng.dirichlet(np.ones(V), size=B * k).astype(np.float32) + 1e-6
+    ids = np.where(rng.random((B, k)) < 0.6, a.reshape(B, k + 1)[:, :k],
+                   rng.integers(0, V, size=(B, k))).astype(np.int32)
+    ks = rng.integers(0, k + 1, size=B).astype(np.int32)
+    t_rs = (np.arange(B) * (k + 1)).astype(np.int32)
+    q_rs = (np.arange(B) * k).astype(np.int32)
+    ci = synth.ChainInputs("onehot", V, "f32", tgt, "f32", q, t_rs, q_rs, ids, ks, k, 1.0,
+                           rng.random((B, k + 1)).astype(np.float32))
+    s = run_sample(ci)
+    g = run_greedy(tgt, "f32", t_rs, ids, ks)
+    for key in ("tokens", "count", "accepted"):
+        assert np.array_equal(s[key], g[key]), key
+
+
+# ---------------------------------------------------------------------------
+# tree
+# ---------------------------------------------------------------------------
+def _check_tree(ti, got, want, name, max_boundary_frac=1e-3):
+    nb, bad = compare_tokens(got, want, keys=("tokens", "count", "accepted", "path"))
+    say(f"{name}: {ti.B} requests, {nb} boundary cases, mean kept {want['accepted'].mean():.2f}")
+    assert bad.size == 0, f"{name}: mismatching requests {bad[:10]}"
+    assert nb <= max(2, max_boundary_frac * ti.B)
+    for b in np.nonzero(want["count"] > 0)[0]:
+        d, e = got["diag"][b], want["diag"][b]
+        assert close(d[:, 0], e[:, 0], atol=1e-6).all(), (name, b, "M")
+        assert close(d[:, 1], e[:, 1]).all(), (name, b, "S")
+        assert close(d[1:, 2], e[1:, 2]).all(), (name, b, "p(x)")
+        assert close(d[1:, 3], e[1:, 3]).all(), (name, b, "q(x)")
+
+
+def _oracle_tree(ti):
+    return oracle.verify_tree(ti.target, ti.t_kind, ti.draft, ti.q_kind, ti.V, ti.parent, ti.token,
+                              ti.T, ti.uniforms)
+
+
+@pytest.fixture(scope="module")
+def c5():
+    return synth.c5_tree()
+
+
+def test_gpu_tree_c5_full(c5):
+    say("tree B=32 N=60 V=128256 bf16 T=1")
+    st = _status()
+    got = run_tree(c5, status=st)
+    want = _oracle_tree(c5)
+    _check_tree(c5, got, want, "c5")
+    assert int(st.item()) == _or(want["flags"])
+
+
+@pytest.mark.parametrize("kind,V,N", [("bf16", 4999, 12), ("f32", 3000, 20), ("bf16", 9, 7)])
+def test_gpu_tree_small(kind, V, N):
+    say(f"tree small kind={kind} V={V} N={N}")
+    ti = synth.c5_tree(B=24, N=N, V=V, top_children=3 if V > 9 else 2, expand_per_layer=3,
+                       max_depth=4, sigma=0.7, salt=V, kind=kind)
+    st = _status()
+    got = run_tree(ti, status=st)
+    want = _oracle_tree(ti)
+    _check_tree(ti, got, want, f"tree {kind}/{V}/{N}", max_boundary_frac=0.05)
+    assert int(st.item()) == _or(want["flags"])
+
+
+def test_gpu_tree_invalid_and_chain_equivalence():
+    say("tree invalid inputs; chain-as-tree equals chain")
+    ch = synth.c3_sampled(B=20, k=4, V=6000, T=0.8, salt=4)
+    B, k, V = ch.B, ch.k_max, ch.V
+    N = k + 1
+    tgt = np.zeros((B * N, V), dtype=np.uint16)
+    dft = np.zeros((B * N, V), dtype=np.uint16)
+    parent = np.tile(np.arange(-1, N - 1), (B, 1)).astype(np.int32)
+    tok = np.full((B, N), -1, dtype=np.int32)
+    for b in range(B):
+        tgt[b * N:(b + 1) * N] = ch.target[ch.t_row_start[b]:ch.t_row_start[b] + N]
+        dft[b * N:b * N + k] = ch.draft[ch.q_row_start[b]:ch.q_row_start[b] + k]
+        tok[b, 1:] = ch.draft_ids[b, :k]
+    ti = synth.TreeInputs("chain", V, N, "bf16", tgt, "bf16", dft, parent, tok,
+                          np.tile(np.arange(N), (B, 1)), ch.T, ch.uniforms.copy())
+    g_tree = run_tree(ti)
+    g_chain = run_sample(ch)
+    for key in ("tokens", "count", "accepted"):
+        assert np.array_equal(g_tree[key][:, :N], g_chain[key]), key
+    ti.parent[3, 2] = 3          # parent not before child
+    ti.parent[4, 0] = 0          # root with a parent
+    ti.token[5, 3] = V           # bad token
+    st = _status()
+    got = run_tree(ti, status=st)
+    want = _oracle_tree(ti)
+    nb, bad = compare_tokens(got, want, keys=("tokens", "count", "accepted", "path"))
+    assert bad.size == 0
+    assert list(got["count"][3:6]) == [0, 0, 0]
+    assert int(st.item()) == _or(want["flags"]) == oracle.FLAG_BAD_TREE | oracle.FLAG_BAD_TOKEN
