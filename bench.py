@@ -1,0 +1,278 @@
+"""Benchmark of the speculative-decoding verify step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
+
+A step is one sampled chain verify (sv_verify_sample: softmax statistics of
+every target row, accept scan, residual and inverse-CDF draw) over one batch
+of synthetic inputs already resident in HBM.  The default workload is the
+sampled chain at B=64 requests, k=4 drafts, V=248,320, bf16 target logits and
+bf16 draft probabilities, T=0.7; two input sets alternate so consecutive steps
+do not reuse cached rows.  Prints one JSON line.
+
+Other workloads (``--workload c1|c2|c4|c5``) print the same kind of line for
+the other configurations (fixed-prefix chain, greedy + prompt lookup, ragged
+chain, tree).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified rounds/s + achieved HBM GB/s (% peak), B=64 k=4 V=248,320 bf16"
+PEAK_HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "row_stats_c3_traffic.json")
+STATS_SRC = os.path.join(ROOT, "draft_verify_sampling_amd", "csrc", "k_stats.hip")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _rows(a, kind, torch, dev):
+    if kind == "f32":
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).to(dev).view(
+        torch.bfloat16)
+
+
+def _i32(a, torch, dev):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+
+def chain_formula_bytes(ci):
+    """Logit rows read once + draft rows + draft ids + uniforms."""
+    st = 4 if ci.t_kind == "f32" else 2
+    sq = 4 if ci.q_kind == "f32" else 2
+    ks = ci.draft_len.astype(np.int64)
+    return int(((ks + 1) * ci.V * st).sum() + (ks * ci.V * sq).sum() + 4 * ks.sum() + 4 * (ks + 1).sum())
+
+
+def stats_traffic(step_kernel_src_hash):
+    """HBM bytes per launch of the row-statistics kernel from the committed
+    counter summary, or None if absent or taken on a different kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha1") != step_kernel_src_hash:
+        return None
+    return t.get("bytes_per_launch")
+
+
+def timed(fn, steps, warmup, torch):
+    """W untimed calls, then K timed calls bracketed by synchronisations; also
+    records a HIP event pair around every timed call on the current stream.
+    Returns (wall seconds, list of per-call event milliseconds)."""
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        fn(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, [a.elapsed_time(b) for a, b in ev]
+
+
+def cpu_baseline_chain(ci, gpu_out, budget_s):
+    """The float64 oracle on the host on the same inputs: whole batches of this
+    workload's requests, repeated until about budget_s seconds have passed."""
+    import oracle
+    reps, t0 = 0, time.perf_counter()
+    want = None
+    while True:
+        want = oracle.verify_sample(ci.target, ci.t_kind, ci.draft, ci.q_kind, ci.V, ci.t_row_start,
+                                    ci.q_row_start, ci.draft_ids[:, :ci.k_max], ci.draft_len,
+                                    ci.k_max, ci.T, ci.uniforms)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    tok, cnt = gpu_out
+    same = (cnt == want["count"]) & (tok == want["tokens"]).all(axis=1)
+    near = np.nanmin(np.where(np.isnan(want["margins"]), np.inf, want["margins"]), axis=1) < 1e-6
+    return dict(value=round(reps * ci.B / el, 3), unit="rounds/s", cores=1, kind="oracle",
+                sample=f"{reps} x all {ci.B} requests of input set 0 ({el:.1f} s, numpy float64, "
+                       f"one thread)"), dict(requests=int(ci.B), mismatched=int((~same & ~near).sum()),
+                                             boundary=int((~same & near).sum()))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import draft_verify_sampling_amd as sv
+    import synth
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    sv.load()
+    with open(STATS_SRC, "rb") as f:
+        src_hash = hashlib.sha1(f.read()).hexdigest()
+
+    result = dict(metric=METRIC, n_gpus=1, steps=args.steps, warmup=args.warmup,
+                  higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
+                  data="synthetic")
+    W = args.workload
+    if W in ("c1", "c3", "c4"):
+        log(f"generating {W} inputs")
+        if W == "c3":
+            sets = [synth.c3_sampled(salt=s) for s in (0, 1)]
+            cfg = dict(workload="sampled chain verify (speculative sampling): 64 requests, k=4 drafts, "
+                                "V=248,320, bf16 target logits ~N(0,2.5^2)+6 on 5 ids, bf16 draft "
+                                "probabilities, T=0.7", batch=64, k=4, vocab=248_320,
+                       temperature=0.7, inputs="bf16", input_sets=2)
+        elif W == "c4":
+            sets = [synth.c4_ragged(salt=s) for s in (0, 1)]
+            cfg = dict(workload="ragged sampled chain verify: 256 requests, k in 1..8, V=151,936, bf16, "
+                                "T=1", batch=256, vocab=151_936, temperature=1.0, inputs="bf16",
+                       input_sets=2)
+        else:
+            sets = [synth.c1_chain()]
+            cfg = dict(workload="fixed-prefix sampled chain: 200,000 rounds sharing 5 target and 4 draft "
+                                "rows, k=4, V=2048, fp32, T=1", batch=200_000, k=4, vocab=2048,
+                       temperature=1.0, inputs="f32", input_sets=1)
+        ci0 = sets[0]
+        dsets = []
+        for ci in sets:
+            dsets.append(dict(
+                tgt=_rows(ci.target, ci.t_kind, torch, dev), dft=_rows(ci.draft, ci.q_kind, torch, dev),
+                trs=_i32(ci.t_row_start, torch, dev), qrs=_i32(ci.q_row_start, torch, dev),
+                ids=_i32(ci.draft_ids[:, :ci.k_max], torch, dev), dl=_i32(ci.draft_len, torch, dev),
+                u=torch.from_numpy(ci.uniforms).to(dev)))
+        B, k_max = ci0.B, ci0.k_max
+        out = (torch.empty((B, k_max + 1), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev), None, None)
+        ws = sv.Workspace(dev)
+
+        def step(i):
+            d = dsets[i % len(dsets)]
+            sv.sv_verify_sample(d["tgt"], d["dft"], d["trs"], d["qrs"], d["ids"], d["dl"], ci0.T, d["u"],
+                                workspace=ws, out=out)
+
+        log(f"timing {args.steps} steps")
+        wall, ev_ms = timed(step, args.steps, args.warmup, torch)
+        # one more call on set 0 for the parity sample and token counts
+        step(0)
+        torch.cuda.synchronize()
+        tok0, cnt0 = out[0].cpu().numpy(), out[1].cpu().numpy()
+        ms = 1e3 * wall / args.steps
+        rows_bytes = int(ci0.target.shape[0]) * ci0.V * (4 if ci0.t_kind == "f32" else 2)
+        # the dominant kernel alone: row statistics of every target row
+        part = torch.empty((ci0.target.shape[0], sv.sv_softmax_segments(ci0.target.shape[0], ci0.V), 2),
+                           dtype=torch.float32, device=dev)
+
+        def stats(i):
+            sv.sv_softmax_partials(dsets[i % len(dsets)]["tgt"], ci0.T, out=part)
+
+        _, st_ms = timed(stats, args.steps, args.warmup, torch)
+        st_avg = float(np.mean(st_ms)) * 1e-3
+        achieved = rows_bytes / st_avg / 1e9
+        fb = chain_formula_bytes(ci0)
+        result.update(
+            value=round(B / (ms * 1e-3), 1), unit="rounds/s", ms_per_step=round(ms, 5), config=cfg,
+            tokens_per_s=round(float(cnt0.sum()) / (ms * 1e-3), 1),
+            mean_tokens_per_round=round(float(cnt0.mean()), 4),
+            event_ms_per_step=dict(mean=round(float(np.mean(ev_ms)), 5),
+                                   p10=round(float(np.percentile(ev_ms, 10)), 5),
+                                   p50=round(float(np.percentile(ev_ms, 50)), 5),
+                                   p90=round(float(np.percentile(ev_ms, 90)), 5)),
+            formula_bytes_per_step=fb,
+            formula_GBps=round(fb / (ms * 1e-3) / 1e9, 1),
+            formula_frac_of_peak=round(fb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
+            roofline=dict(bound="hbm", kernel="k_row_stats (softmax statistics of every target row)",
+                          achieved=round(achieved, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
+                          frac=round(achieved / PEAK_HBM_GBPS, 4),
+                          traffic=stats_traffic(src_hash) if W == "c3" else None,
+                          algorithmic_bytes_per_launch=rows_bytes,
+                          avg_launch_us=round(st_avg * 1e6, 3)))
+        if not args.no_cpu:
+            log("timing the oracle on the host")
+            cb, par = cpu_baseline_chain(ci0, (tok0, cnt0), args.cpu_seconds)
+            result["cpu_baseline"] = cb
+            result["parity_sample"] = par
+    elif W == "c5":
+        log("generating c5 inputs")
+        ti = synth.c5_tree()
+        d = dict(tgt=_rows(ti.target, "bf16", torch, dev), dft=_rows(ti.draft, "bf16", torch, dev),
+                 par=_i32(ti.parent, torch, dev), tok=_i32(ti.token, torch, dev),
+                 u=torch.from_numpy(ti.uniforms).to(dev))
+        ws = sv.Workspace(dev)
+        B, N = ti.parent.shape
+        out = (torch.empty((B, N), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev), torch.empty((B, N), dtype=torch.int32, device=dev),
+               None)
+
+        def step(i):
+            sv.sv_verify_tree(d["tgt"], d["dft"], d["par"], d["tok"], ti.T, d["u"], workspace=ws, out=out)
+
+        wall, ev_ms = timed(step, args.steps, args.warmup, torch)
+        ms = 1e3 * wall / args.steps
+        part = torch.empty((B * N, sv.sv_softmax_segments(B * N, ti.V), 2), dtype=torch.float32, device=dev)
+        _, st_ms = timed(lambda i: sv.sv_softmax_partials(d["tgt"], ti.T, out=part), args.steps,
+                         args.warmup, torch)
+        st_avg = float(np.mean(st_ms)) * 1e-3
+        rows_bytes = B * N * ti.V * 2
+        fb = 2 * rows_bytes + 2 * 4 * B * N
+        result.update(value=round(B / (ms * 1e-3), 1), unit="rounds/s", ms_per_step=round(ms, 5),
+                      config=dict(workload="tree verify: 32 requests, 60-node draft trees (depth <= 6, "
+                                           "branching <= 4), V=128,256, bf16, T=1", batch=32, nodes=60,
+                                  vocab=128_256, temperature=1.0, inputs="bf16"),
+                      tokens_per_s=round(float(out[1].sum().item()) / (ms * 1e-3), 1),
+                      formula_bytes_per_step=fb, formula_GBps=round(fb / (ms * 1e-3) / 1e9, 1),
+                      roofline=dict(bound="hbm", kernel="k_row_stats", achieved=round(rows_bytes / st_avg / 1e9, 1),
+                                    peak=PEAK_HBM_GBPS, unit="GB/s",
+                                    frac=round(rows_bytes / st_avg / 1e9 / PEAK_HBM_GBPS, 4), traffic=None,
+                                    algorithmic_bytes_per_launch=rows_bytes,
+                                    avg_launch_us=round(st_avg * 1e6, 3)))
+    else:  # c2: prompt lookup + greedy verify
+        log("generating c2 inputs")
+        g = synth.c2_greedy()
+        ctx = _i32(g.ctx, torch, dev)
+        cl = _i32(g.ctx_len, torch, dev)
+        tgt = _rows(g.target, "bf16", torch, dev)
+        trs = _i32(np.arange(g.B) * (g.k + 1), torch, dev)
+        ws = sv.Workspace(dev)
+
+        def step(i):
+            ids, lens = sv.sv_ngram_draft(ctx, cl, g.window, g.k)
+            return sv.sv_verify_greedy(tgt, trs, ids, lens, workspace=ws)
+
+        wall, ev_ms = timed(step, args.steps, args.warmup, torch)
+        ms = 1e3 * wall / args.steps
+        fb = g.target.size * 2 + g.ctx.size * 4
+        result.update(value=round(g.B / (ms * 1e-3), 1), unit="rounds/s", ms_per_step=round(ms, 5),
+                      config=dict(workload="prompt-lookup draft + greedy verify: 64 requests, contexts of "
+                                           "4,096 tokens, window 3, k=4, V=32,000, bf16", batch=64, k=4,
+                                  vocab=32_000, inputs="bf16"),
+                      formula_bytes_per_step=fb, formula_GBps=round(fb / (ms * 1e-3) / 1e9, 1),
+                      dtype="int32+f32", roofline=None)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -21,7 +21,7 @@ import torch
 __all__ = [
     "SpecVerifyError", "lib_path", "load", "abi_version", "workspace_bytes",
     "sv_ngram_draft", "sv_verify_greedy", "sv_verify_sample", "sv_verify_tree",
-    "SV_F32", "SV_BF16", "SV_OP_GREEDY", "SV_OP_SAMPLE", "SV_OP_TREE",
+    "sv_softmax_partials", "sv_softmax_segments", "SV_F32", "SV_BF16", "SV_OP_GREEDY", "SV_OP_SAMPLE", "SV_OP_TREE",
     "FLAG_BAD_REQUEST", "FLAG_BAD_TOKEN", "FLAG_NONFINITE", "FLAG_OVER_BUDGET",
     "FLAG_FALLBACK", "FLAG_BAD_TREE", "EXPORTS",
 ]
@@ -32,6 +32,7 @@ FLAG_BAD_REQUEST, FLAG_BAD_TOKEN, FLAG_NONFINITE = 1, 2, 4
 FLAG_OVER_BUDGET, FLAG_FALLBACK, FLAG_BAD_TREE = 8, 16, 32
 
 EXPORTS = ("sv_abi_version", "sv_status_string", "sv_last_error", "sv_workspace_bytes",
+           "sv_softmax_segments", "sv_softmax_partials",
            "sv_ngram_draft", "sv_verify_greedy", "sv_verify_sample", "sv_verify_tree")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -49,6 +50,8 @@ _SIGS = {
     "sv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "sv_last_error": (ctypes.c_char_p, []),
     "sv_workspace_bytes": (SZ, [ctypes.c_int, I64, I64, I64]),
+    "sv_softmax_segments": (I32, [I64, I64]),
+    "sv_softmax_partials": (ctypes.c_int, [P, I32, I64, I64, F32, P, P]),
     "sv_ngram_draft": (ctypes.c_int, [P, P, I32, I32, I32, I32, P, P, P, P]),
     "sv_verify_greedy": (ctypes.c_int, [P, I32, I32, I64, P, P, P, I32, I32, P, I32,
                                         P, P, P, P, P, SZ, P]),
@@ -134,8 +137,8 @@ def _stream(stream) -> Optional[int]:
 
 
 class Workspace:
-    """Caller-side workspace: a zero-filled device buffer, reused across calls
-    on one stream (the library leaves its counters at zero after every call)."""
+    """Caller-side workspace: a device buffer grown on demand and reused across
+    calls on one stream (the library needs no particular initial contents)."""
 
     def __init__(self, device=None):
         self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
@@ -144,7 +147,7 @@ class Workspace:
 
     def get(self, nbytes: int) -> torch.Tensor:
         if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
         return self.buf
 
 
@@ -156,6 +159,25 @@ def _workspace(ws: Optional[Workspace], device, stream, nbytes: int) -> torch.Te
         key = (str(device), _stream(stream))
         ws = _DEFAULT_WS.setdefault(key, Workspace(device))
     return ws.get(nbytes)
+
+
+def sv_softmax_segments(n_rows: int, vocab: int) -> int:
+    return int(load().sv_softmax_segments(n_rows, vocab))
+
+
+def sv_softmax_partials(rows: torch.Tensor, temperature: float, out: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """Per-segment softmax pairs of every row: returns float32 [n_rows, nseg, 2]
+    (scaled-domain max, sum); see include/specverify.h."""
+    lib = load()
+    n_rows, V = rows.shape
+    nseg = sv_softmax_segments(n_rows, V)
+    if out is None:
+        out = torch.empty((n_rows, nseg, 2), dtype=torch.float32, device=rows.device)
+    _check(lib.sv_softmax_partials(_dev(rows, "rows"), _dtype_code(rows), n_rows, V,
+                                   float(temperature), _dev(out, "out", torch.float32, rows.device),
+                                   _stream(stream)), "sv_softmax_partials")
+    return out
 
 
 def sv_ngram_draft(ctx: torch.Tensor, ctx_len: torch.Tensor, window: int, k: int,

@@ -72,6 +72,28 @@ size_t sv_workspace_bytes(int op, int64_t batch, int64_t total_rows, int64_t voc
   }
 }
 
+int32_t sv_softmax_segments(int64_t n_rows, int64_t vocab) {
+  if (n_rows < 0 || vocab < 1) return 0;
+  return sv::row_segments(n_rows, vocab);
+}
+
+sv_status sv_softmax_partials(const void* rows, int32_t dtype, int64_t n_rows, int64_t vocab,
+                              float temperature, float* out_partials, void* stream) {
+  if (!dtype_ok(dtype)) return fail(SV_E_DTYPE, "dtype must be SV_F32 or SV_BF16");
+  if (n_rows < 0 || vocab < 1) return fail(SV_E_ARG, "n_rows must be >= 0 and vocab >= 1");
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(SV_E_ARG, "temperature must be finite and > 0");
+  if (n_rows == 0) return SV_OK;
+  if (rows == nullptr || out_partials == nullptr) return fail(SV_E_ARG, "null pointer argument");
+  const int32_t nseg = sv::row_segments(n_rows, vocab);
+  if (n_rows * nseg > kMaxGrid) return fail(SV_E_ARG, "too many rows");
+  (void)hipGetLastError();
+  const hipError_t e = sv::launch_row_stats(dtype, rows, n_rows, vocab, nseg, sv::kLog2e / temperature,
+                                            reinterpret_cast<float2*>(out_partials), nullptr, 0,
+                                            static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SV_OK : device_fail(e, "sv_softmax_partials launch");
+}
+
 sv_status sv_ngram_draft(const int32_t* ctx, const int32_t* ctx_len, int32_t batch,
                          int32_t ctx_stride, int32_t window, int32_t k, int32_t* draft_ids,
                          int32_t* draft_len, int32_t* dev_status, void* stream) {
@@ -173,7 +195,9 @@ sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t
   const hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   float2* partial = reinterpret_cast<float2*>(ws + L.partial_off);
-  hipError_t e = sv::launch_row_stats(t_dtype, target_logits, t_rows, vocab, nseg, c, partial, st);
+  uint32_t* counters = reinterpret_cast<uint32_t*>(ws + L.counter_off);
+  hipError_t e = sv::launch_row_stats(t_dtype, target_logits, t_rows, vocab, nseg, c, partial, counters,
+                                      batch, st);
   if (e != hipSuccess) return device_fail(e, "sv_verify_sample row-stats launch");
   sv::SampleArgs a{};
   a.tgt = target_logits;
@@ -188,7 +212,6 @@ sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t
   a.B = batch;
   a.k_max = k_max;
   a.c = c;
-  a.invT = 1.f / temperature;
   a.u = uniforms;
   a.max_new = max_new;
   a.eos = eos_id;
@@ -201,7 +224,7 @@ sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t
   a.partial = partial;
   a.nseg = nseg;
   a.tiles = reinterpret_cast<double*>(ws + L.tiles_off);
-  a.counters = reinterpret_cast<uint32_t*>(ws + L.counter_off);
+  a.counters = counters;
   a.ntiles = static_cast<int32_t>(ntiles);
   a.tpb = sv::kSampleTilesPerBlock;
   a.chunks = static_cast<int32_t>(chunks);
@@ -240,7 +263,8 @@ sv_status sv_verify_tree(const void* target_logits, int32_t t_dtype, const void*
   const hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   float2* partial = static_cast<float2*>(workspace);
-  hipError_t e = sv::launch_row_stats(t_dtype, target_logits, rows, vocab, nseg, c, partial, st);
+  hipError_t e = sv::launch_row_stats(t_dtype, target_logits, rows, vocab, nseg, c, partial, nullptr, 0,
+                                      st);
   if (e != hipSuccess) return device_fail(e, "sv_verify_tree row-stats launch");
   sv::TreeArgs a{};
   a.tgt = target_logits;
@@ -251,7 +275,6 @@ sv_status sv_verify_tree(const void* target_logits, int32_t t_dtype, const void*
   a.B = batch;
   a.N = n_nodes;
   a.c = c;
-  a.invT = 1.f / temperature;
   a.u = uniforms;
   a.out_tok = out_tokens;
   a.out_cnt = out_count;

@@ -10,6 +10,7 @@ constexpr int kBlock = 256;            // threads per block for the streaming ke
 constexpr int kWave = 64;
 constexpr int kTile = 4096;            // elements per sampling tile (inverse-CDF unit)
 constexpr int kPerThreadTile = kTile / kBlock;  // 16 contiguous elements per thread
+constexpr float kLn2 = 0.6931471805599453f;
 
 
 // Status bits (the public header documents them).
@@ -89,63 +90,65 @@ __device__ __forceinline__ void load_run(const void* row, int64_t V, int64_t e, 
 }
 
 // ---------------------------------------------------------------------------
-// Online softmax pairs: (m, s) with s = sum exp2((x - m) * c), c = log2(e)/T.
+// Online softmax pairs over scaled scores y = l * c (c = log2(e) / T):
+// m = max of the rounded products l * c, s = sum 2^(l * c - m) with each term
+// formed by one fused multiply-add.  Because m is itself a representable value
+// of the scaled domain, merging two pairs rescales by 2^(m_a - M) with the
+// dominant side's factor exactly 1, so no rounding of the max leaks into s.
 // ---------------------------------------------------------------------------
 struct MS {
   float m;
   float s;
 };
 
-__device__ __forceinline__ MS ms_combine(MS a, MS b, float c) {
+__device__ __forceinline__ MS ms_combine(MS a, MS b) {
   const float M = fmaxf(a.m, b.m);
   if (M == -INFINITY) return MS{M, 0.f};
-  const float Mc = M * c;
-  return MS{M, a.s * ex2(fmaf(a.m, c, -Mc)) + b.s * ex2(fmaf(b.m, c, -Mc))};
+  return MS{M, a.s * ex2(a.m - M) + b.s * ex2(b.m - M)};
 }
 
-// Fold n values into a running pair: one rescale per group, pairwise group sum.
+// Fold n raw scores into a running pair: one rescale per group, pairwise group sum.
 template <int n>
 __device__ __forceinline__ void ms_fold(MS& acc, const float* x, float c) {
   float cm = x[0];
 #pragma unroll
   for (int j = 1; j < n; ++j) cm = fmaxf(cm, x[j]);
-  const float M = fmaxf(acc.m, cm);
+  const float M = fmaxf(acc.m, cm * c);
   if (M == -INFINITY) return;
-  const float Mc = M * c;
   float e[n];
 #pragma unroll
-  for (int j = 0; j < n; ++j) e[j] = ex2(fmaf(x[j], c, -Mc));
+  for (int j = 0; j < n; ++j) e[j] = ex2(fmaf(x[j], c, -M));
 #pragma unroll
   for (int w = 1; w < n; w *= 2) {
 #pragma unroll
     for (int j = 0; j + w < n; j += 2 * w) e[j] += e[j + w];
   }
-  acc.s = acc.s * ex2(fmaf(acc.m, c, -Mc)) + e[0];
+  acc.s = acc.s * ex2(acc.m - M) + e[0];
   acc.m = M;
 }
 
-__device__ __forceinline__ MS wave_ms(MS v, float c) {
+__device__ __forceinline__ MS wave_ms(MS v) {
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) {
     MS o{__shfl_xor(v.m, off, kWave), __shfl_xor(v.s, off, kWave)};
-    v = ms_combine(v, o, c);
+    v = ms_combine(v, o);
   }
   return v;
 }
 
 // Block-wide (m, s) reduction; result valid in every thread.  `sh` holds
 // 2 * (blockDim/64) floats.
-__device__ __forceinline__ MS block_ms(MS v, float c, float* sh) {
+__device__ __forceinline__ MS block_ms(MS v, float* sh) {
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   const int nw = blockDim.x / kWave;
-  v = wave_ms(v, c);
+  v = wave_ms(v);
   if (lane == 0) {
     sh[2 * wid] = v.m;
     sh[2 * wid + 1] = v.s;
   }
   __syncthreads();
   MS r{sh[0], sh[1]};
-  for (int w = 1; w < nw; ++w) r = ms_combine(r, MS{sh[2 * w], sh[2 * w + 1]}, c);
+  for (int w = 1; w < nw; ++w) r = ms_combine(r, MS{sh[2 * w], sh[2 * w + 1]});
   __syncthreads();
   return r;
 }

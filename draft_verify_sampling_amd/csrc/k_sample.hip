@@ -15,7 +15,8 @@
 // agree on the break position m without talking to each other.  Each block then
 // streams its tiles of target row m (and draft row m when m < k), writing per
 // tile the float64 sums of the draw weights r, of p, and of q.  The last block
-// of the request to arrive (agent-scope counter, reset to zero by that block)
+// of the request to arrive (agent-scope counter, cleared by the row-statistics
+// kernel at the start of the call)
 // scans the tile sums, finds the tile holding u_k * total, rescans that one
 // tile with a block prefix sum and picks the smallest id whose running weight
 // exceeds it.  Only the break row's draft row is read from HBM: the accept
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_resolve(SampleArgs a) {
     MS r{-INFINITY, 0.f};
     for (int s = 0; s < a.nseg; ++s) {
       const float2 v = pp[s];
-      r = ms_combine(r, MS{v.x, v.y}, a.c);
+      r = ms_combine(r, MS{v.x, v.y});
     }
     s_m[tid] = r.m;
     s_S[tid] = r.s;
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_resolve(SampleArgs a) {
   // ---- p, q at the drafted tokens; accept scan ----
   if (tid < k) {
     const float l = DT::at(row_ptr<DT>(a.tgt, ts + tid, a.V), x);
-    const float p = ex2(fmaf(l, a.c, -(s_m[tid] * a.c))) * (1.f / s_S[tid]);
+    const float p = ex2(fmaf(l, a.c, -s_m[tid])) * (1.f / s_S[tid]);
     const float q = DQ::at(row_ptr<DQ>(a.dq, qs + tid, a.V), x);
     s_p[tid] = p;
     s_q[tid] = q;
@@ -148,7 +149,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_resolve(SampleArgs a) {
     if (tid == 0 && a.max_new != nullptr && k > a.max_new[b]) flag(a.status, kFlagOverBudget);
     if (a.diag != nullptr && tid <= k) {
       float* d = a.diag + (static_cast<int64_t>(b) * ustride + tid) * 4;
-      d[0] = s_m[tid] * a.invT;
+      d[0] = s_m[tid] * kLn2;
       d[1] = s_S[tid];
       d[2] = tid < k ? s_p[tid] : 0.f;
       d[3] = tid < k ? s_q[tid] : 0.f;
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(kBlock) void k_sample_resolve(SampleArgs a) {
 
   // ---- tile sums of the draw row ----
   const bool resid = m < k;
-  const float Mc = s_m[m] * a.c;
+  const float Mc = s_m[m];
   const float invS = 1.f / s_S[m];
   const void* trow = row_ptr<DT>(a.tgt, ts + m, a.V);
   const void* qrow = resid ? row_ptr<DQ>(a.dq, qs + m, a.V) : nullptr;
@@ -195,7 +196,6 @@ __global__ __launch_bounds__(kBlock) void k_sample_resolve(SampleArgs a) {
     __syncthreads();
     if (!s_int[2]) return;
     __threadfence();
-    if (tid == 0) a.counters[b] = 0u;
   } else {
     __syncthreads();
   }

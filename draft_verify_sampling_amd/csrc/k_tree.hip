@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeArgs a) {
     MS r{-INFINITY, 0.f};
     for (int s = 0; s < a.nseg; ++s) {
       const float2 v = pp[s];
-      r = ms_combine(r, MS{v.x, v.y}, a.c);
+      r = ms_combine(r, MS{v.x, v.y});
     }
     s_m[c] = r.m;
     s_S[c] = r.s;
@@ -126,13 +126,13 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeArgs a) {
   if (a.diag != nullptr) {
     for (int c = tid; c < N; c += kBlock) {
       float* d = a.diag + (row0 + c) * 4;
-      d[0] = s_m[c] * a.invT;
+      d[0] = s_m[c] * kLn2;
       d[1] = s_S[c];
       float pv = 0.f, qv = 0.f;
       if (c > 0) {
         const int pr = s_par[c];
         const float l = DT::at(row_ptr<DT>(a.tgt, row0 + pr, V), s_tok[c]);
-        pv = ex2(fmaf(l, a.c, -(s_m[pr] * a.c))) * (1.f / s_S[pr]);
+        pv = ex2(fmaf(l, a.c, -s_m[pr])) * (1.f / s_S[pr]);
         qv = DQ::at(row_ptr<DQ>(a.dq, row0 + pr, V), s_tok[c]);
       }
       d[2] = pv;
@@ -163,7 +163,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeArgs a) {
     const int nk = s_int[1];
     const void* trow = row_ptr<DT>(a.tgt, row0 + cur, V);
     const void* qrow = row_ptr<DQ>(a.dq, row0 + cur, V);
-    const float Mc = s_m[cur] * a.c;
+    const float Mc = s_m[cur];
     const float invS = 1.f / s_S[cur];
     for (int j = tid; j < nk; j += kBlock) {
       const int x = s_tok[s_kids[j]];
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_walk(TreeArgs a) {
   // ---- final draw from the current distribution ----
   const void* trow = row_ptr<DT>(a.tgt, row0 + cur, V);
   const void* qrow = row_ptr<DQ>(a.dq, row0 + cur, V);
-  const float Mc = s_m[cur] * a.c;
+  const float Mc = s_m[cur];
   const float invS = 1.f / s_S[cur];
   if (!have_tiles) {
     for (int t = 0; t < a.ntiles; ++t) {

@@ -59,7 +59,6 @@ struct SampleArgs {
   const int32_t* dlen;
   int32_t B, k_max;
   float c;      // log2(e) / T
-  float invT;   // 1 / T
   const float* u;
   const int32_t* max_new;
   int32_t eos;
@@ -101,7 +100,7 @@ struct TreeArgs {
   const int32_t* parent;
   const int32_t* token;
   int32_t B, N;
-  float c, invT;
+  float c;      // log2(e) / T
   const float* u;
   int32_t* out_tok;
   int32_t* out_cnt;
@@ -115,7 +114,8 @@ struct TreeArgs {
 };
 
 hipError_t launch_row_stats(int dtype, const void* rows, int64_t n_rows, int64_t V, int32_t nseg,
-                            float c, float2* partial, hipStream_t stream);
+                            float c, float2* partial, uint32_t* zero, int64_t n_zero,
+                            hipStream_t stream);
 hipError_t launch_sample_resolve(int t_dtype, int q_dtype, const SampleArgs& a,
                                  hipStream_t stream);
 hipError_t launch_row_argmax(int dtype, const void* rows, int64_t n_rows, int64_t V, int32_t nseg,

@@ -44,10 +44,11 @@
  *   gets a defined output.  A request with SV_FLAG_BAD_REQUEST, BAD_TOKEN,
  *   NONFINITE or BAD_TREE is invalid: count 0, accepted 0, all tokens -1.
  * - Workspace (greedy, sample, tree): caller-owned device memory of at least
- *   sv_workspace_bytes(...) bytes, 256-byte aligned, ZERO-FILLED ONCE before
- *   its first use.  Every call leaves its counters at zero again, so it can be
- *   reused without clearing.  Calls that may run concurrently (different
- *   streams) need separate workspaces.
+ *   sv_workspace_bytes(...) bytes, 256-byte aligned.  Its contents need not be
+ *   initialised: each call writes everything it later reads (the sampled
+ *   verify clears its per-request arrival counters in its first kernel), so
+ *   one buffer can serve calls of any shape in turn on one stream.  Calls that
+ *   may run concurrently (different streams) need separate workspaces.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -96,6 +97,19 @@ const char* sv_last_error(void);
  * with `batch` requests, `total_rows` target rows (greedy/sample: t_rows; tree:
  * batch * n_nodes) and `vocab` columns.  Host function.  0 on bad input. */
 size_t sv_workspace_bytes(int op, int64_t batch, int64_t total_rows, int64_t vocab);
+
+/* Streaming first pass of sv_verify_sample and sv_verify_tree, exposed on its
+ * own: the temperature softmax of every row needs max(l)/T and
+ * sum exp(l/T - max) over the whole vocabulary
+ * ("投机解码:为什么一个字都不改", figure "一次目标前向验 k 个草稿 token").
+ * Each of n_rows rows is split into sv_softmax_segments(n_rows, vocab) segments;
+ * out_partials [n_rows, nseg, 2] float receives, per segment, the pair
+ * (m = max over the segment of l * log2(e)/T, s = sum 2^(l * log2(e)/T - m)).
+ * A row's pairs combine as m = max_j m_j, s = sum_j s_j * 2^(m_j - m); then
+ * max(l)/T = m * ln 2 and sum exp(l/T - max(l)/T) = s.  temperature finite > 0. */
+int32_t sv_softmax_segments(int64_t n_rows, int64_t vocab);
+sv_status sv_softmax_partials(const void* rows, int32_t dtype, int64_t n_rows, int64_t vocab,
+                              float temperature, float* out_partials, void* stream);
 
 /* History n-gram drafter.
  * ctx [batch, ctx_stride] int32 tokens; ctx_len [batch]: tokens of request b are

@@ -15,7 +15,7 @@ HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))
 
 def _declared():
     text = open(HEADER).read()
-    return set(re.findall(r"^\s*(?:sv_status|int|size_t|const char\*)\s+(sv_\w+)\s*\(",
+    return set(re.findall(r"^\s*(?:sv_status|int|int32_t|size_t|const char\*)\s+(sv_\w+)\s*\(",
                           text, flags=re.M))
 
 

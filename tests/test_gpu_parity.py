@@ -386,8 +386,9 @@ def test_gpu_tree_invalid_and_chain_equivalence():
                           np.tile(np.arange(N), (B, 1)), ch.T, ch.uniforms.copy())
     g_tree = run_tree(ti)
     g_chain = run_sample(ch)
-    for key in ("tokens", "count", "accepted"):
-        assert np.array_equal(g_tree[key][:, :N], g_chain[key]), key
+    assert np.array_equal(g_tree["tokens"][:, :N], g_chain["tokens"])
+    for key in ("count", "accepted"):
+        assert np.array_equal(g_tree[key], g_chain[key]), key
     ti.parent[3, 2] = 3          # parent not before child
     ti.parent[4, 0] = 0          # root with a parent
     ti.token[5, 3] = V           # bad token
@@ -398,3 +399,20 @@ def test_gpu_tree_invalid_and_chain_equivalence():
     assert bad.size == 0
     assert list(got["count"][3:6]) == [0, 0, 0]
     assert int(st.item()) == _or(want["flags"]) == oracle.FLAG_BAD_TREE | oracle.FLAG_BAD_TOKEN
+
+
+@pytest.mark.parametrize("kind,V,T", [("bf16", 248_320, 0.7), ("f32", 4099, 1.3), ("bf16", 7, 1.0)])
+def test_gpu_softmax_partials(kind, V, T):
+    say(f"softmax partials kind={kind} V={V} T={T}")
+    import draft_verify_sampling_amd as sv
+    rng = np.random.default_rng(V)
+    rows = rng.standard_normal((9, V)) * 2.5
+    rows[3, :V // 2] = -np.inf
+    stored = synth.encode(rows, kind)
+    part = sv.sv_softmax_partials(rows_to_dev(stored, kind), T).cpu().numpy().astype(np.float64)
+    for r in range(rows.shape[0]):
+        m = part[r, :, 0].max()
+        s = (part[r, :, 1] * np.exp2(part[r, :, 0] - m)).sum()
+        _, M, S = oracle.softmax_T(oracle.widen(stored[r], kind), T)
+        assert close(m * np.log(2.0), M, atol=1e-6), r
+        assert close(s, S), r
