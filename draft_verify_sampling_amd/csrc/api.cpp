@@ -89,7 +89,7 @@ sv_status sv_softmax_partials(const void* rows, int32_t dtype, int64_t n_rows, i
   if (n_rows * nseg > kMaxGrid) return fail(SV_E_ARG, "too many rows");
   (void)hipGetLastError();
   const hipError_t e = sv::launch_row_stats(dtype, rows, n_rows, vocab, nseg, sv::kLog2e / temperature,
-                                            reinterpret_cast<float2*>(out_partials), nullptr, 0,
+                                            reinterpret_cast<float2*>(out_partials),
                                             static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SV_OK : device_fail(e, "sv_softmax_partials launch");
 }
@@ -184,8 +184,7 @@ sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t
     return fail(SV_E_ARG, "null pointer argument");
   const int32_t nseg = sv::row_segments(t_rows, vocab);
   const int64_t ntiles = sv::tiles_of(vocab);
-  const int64_t chunks = (ntiles + sv::kSampleTilesPerBlock - 1) / sv::kSampleTilesPerBlock;
-  if (static_cast<int64_t>(t_rows) * nseg > kMaxGrid || static_cast<int64_t>(batch) * chunks > kMaxGrid)
+  if (static_cast<int64_t>(t_rows) * nseg > kMaxGrid || static_cast<int64_t>(batch) * ntiles > kMaxGrid)
     return fail(SV_E_ARG, "problem too large for one launch");
   const sv::SampleLayout L = sv::sample_layout(batch, t_rows, vocab);
   if (sv_status s = check_workspace(workspace, workspace_bytes, L.bytes)) return s;
@@ -195,9 +194,7 @@ sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t
   const hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   float2* partial = reinterpret_cast<float2*>(ws + L.partial_off);
-  uint32_t* counters = reinterpret_cast<uint32_t*>(ws + L.counter_off);
-  hipError_t e = sv::launch_row_stats(t_dtype, target_logits, t_rows, vocab, nseg, c, partial, counters,
-                                      batch, st);
+  hipError_t e = sv::launch_row_stats(t_dtype, target_logits, t_rows, vocab, nseg, c, partial, st);
   if (e != hipSuccess) return device_fail(e, "sv_verify_sample row-stats launch");
   sv::SampleArgs a{};
   a.tgt = target_logits;
@@ -224,10 +221,8 @@ sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t
   a.partial = partial;
   a.nseg = nseg;
   a.tiles = reinterpret_cast<double*>(ws + L.tiles_off);
-  a.counters = counters;
+  a.records = reinterpret_cast<int4*>(ws + L.records_off);
   a.ntiles = static_cast<int32_t>(ntiles);
-  a.tpb = sv::kSampleTilesPerBlock;
-  a.chunks = static_cast<int32_t>(chunks);
   e = sv::launch_sample_resolve(t_dtype, q_dtype, a, st);
   return e == hipSuccess ? SV_OK : device_fail(e, "sv_verify_sample resolve launch");
 }
@@ -263,8 +258,7 @@ sv_status sv_verify_tree(const void* target_logits, int32_t t_dtype, const void*
   const hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   float2* partial = static_cast<float2*>(workspace);
-  hipError_t e = sv::launch_row_stats(t_dtype, target_logits, rows, vocab, nseg, c, partial, nullptr, 0,
-                                      st);
+  hipError_t e = sv::launch_row_stats(t_dtype, target_logits, rows, vocab, nseg, c, partial, st);
   if (e != hipSuccess) return device_fail(e, "sv_verify_tree row-stats launch");
   sv::TreeArgs a{};
   a.tgt = target_logits;

@@ -8,25 +8,121 @@
 // kept one more token is drawn from p_k.
 //
 // Runs after the row-statistics kernel has left the softmax partials of every
-// target row.  Grid: batch * chunks blocks; block (b, ch) owns tiles
-// [ch * tpb, ch * tpb + tpb) of request b's draw row.  Every block of a
-// request first repeats the request's small preamble (row normalisers from the
-// partials, p and q at the drafted tokens, the accept scan), so all of them
-// agree on the break position m without talking to each other.  Each block then
-// streams its tiles of target row m (and draft row m when m < k), writing per
-// tile the float64 sums of the draw weights r, of p, and of q.  The last block
-// of the request to arrive (agent-scope counter, cleared by the row-statistics
-// kernel at the start of the call)
-// scans the tile sums, finds the tile holding u_k * total, rescans that one
-// tile with a block prefix sum and picks the smallest id whose running weight
-// exceeds it.  Only the break row's draft row is read from HBM: the accept
-// test needs just q_i(x_i).
+// target row.  Two kernels, with no communication between blocks of one grid:
+//
+// k_sample_tiles: grid = batch * ntiles blocks, one 4096-element tile each.
+//   Every block repeats the request's small preamble (row normalisers from
+//   the partials, p and q at the drafted tokens, the accept scan), so all of
+//   a request's blocks agree on the break position m.  The block then reads
+//   its tile of target row m (and of draft row m when m < k) and writes the
+//   float64 sums of the draw weights r, of p and of q for that tile.  Tile 0
+//   also writes the request's record (status bits, m, row scale) and the
+//   diagnostics.  When the vocabulary fits one tile the block draws the token
+//   itself and no second kernel runs.
+// k_sample_draw: one block per request.  Scans the tile sums, finds the tile
+//   holding u_k * total, rescans that tile with a block prefix sum and picks
+//   the smallest id whose running weight exceeds it; writes the tokens.
+//
+// Only the break row's draft row is read from HBM: the accept test needs just
+// q_i(x_i) from the other draft rows.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace sv {
 
 namespace {
+
+constexpr int kMaxPartialsInLds = 1024;
+
+struct Pre {
+  int bits;     // status bits; INVALID ones end the request
+  int k, m;
+  int ts, qs;
+  float Mc;     // scaled-domain max of the draw row
+  float invS;   // 1 / normaliser of the draw row
+};
+
+struct SampleShared {
+  float m[kMaxChainRows], S[kMaxChainRows], p[kMaxChainRows], q[kMaxChainRows];
+  float2 part[kMaxPartialsInLds];
+  double red[3 * (kBlock / kWave)];
+  int i[4];
+};
+
+constexpr int kInvalid = kFlagBadRequest | kFlagBadToken | kFlagNonfinite;
+
+// The request's preamble; identical in every block that runs it.
+template <class DT, class DQ>
+__device__ Pre preamble(const SampleArgs& a, int b, bool write_diag, SampleShared& sh) {
+  const int tid = threadIdx.x;
+  const int ustride = a.k_max + 1;
+  Pre r{};
+  r.k = a.dlen[b];
+  r.ts = a.t_rs[b];
+  r.qs = a.q_rs[b];
+  const int k = r.k;
+  if (k < 0 || k > a.k_max || r.ts < 0 || static_cast<int64_t>(r.ts) + k >= a.t_rows ||
+      (k > 0 && (r.qs < 0 || static_cast<int64_t>(r.qs) + k > a.q_rows))) {
+    r.bits = kFlagBadRequest;
+    return r;
+  }
+  if (tid == 0) {
+    sh.i[0] = k;
+    sh.i[1] = 0;
+  }
+  const int np = (k + 1) * a.nseg;
+  const bool lds_parts = np <= kMaxPartialsInLds;
+  if (lds_parts) {
+    const float2* src = a.partial + static_cast<int64_t>(r.ts) * a.nseg;
+    for (int i = tid; i < np; i += kBlock) sh.part[i] = src[i];
+  }
+  __syncthreads();
+  int x = 0;
+  if (tid < k) {
+    x = a.ids[static_cast<int64_t>(b) * a.k_max + tid];
+    if (x < 0 || x >= a.V) atomicOr(&sh.i[1], kFlagBadToken);
+  }
+  if (tid <= k) {
+    const float2* pp = lds_parts ? sh.part + tid * a.nseg
+                                 : a.partial + static_cast<int64_t>(r.ts + tid) * a.nseg;
+    MS acc{-INFINITY, 0.f};
+    for (int s = 0; s < a.nseg; ++s) acc = ms_combine(acc, MS{pp[s].x, pp[s].y});
+    sh.m[tid] = acc.m;
+    sh.S[tid] = acc.s;
+    if (!(acc.s > 0.f && acc.s < INFINITY)) atomicOr(&sh.i[1], kFlagNonfinite);
+  }
+  __syncthreads();
+  if (sh.i[1] & kFlagBadToken) {
+    r.bits = kFlagBadToken;
+    return r;
+  }
+  if (sh.i[1]) {
+    r.bits = sh.i[1];
+    return r;
+  }
+  if (tid < k) {
+    const float l = DT::at(row_ptr<DT>(a.tgt, r.ts + tid, a.V), x);
+    const float p = ex2(fmaf(l, a.c, -sh.m[tid])) * (1.f / sh.S[tid]);
+    const float q = DQ::at(row_ptr<DQ>(a.dq, r.qs + tid, a.V), x);
+    sh.p[tid] = p;
+    sh.q[tid] = q;
+    const float uu = a.u[static_cast<int64_t>(b) * ustride + tid];
+    if (!(uu * q < p)) atomicMin(&sh.i[0], tid);
+  }
+  __syncthreads();
+  r.m = sh.i[0];
+  if (write_diag && a.diag != nullptr && tid <= k) {
+    float* d = a.diag + (static_cast<int64_t>(b) * ustride + tid) * 4;
+    d[0] = sh.m[tid] * kLn2;
+    d[1] = sh.S[tid];
+    d[2] = tid < k ? sh.p[tid] : 0.f;
+    d[3] = tid < k ? sh.q[tid] : 0.f;
+  }
+  if (a.max_new != nullptr && k > a.max_new[b]) r.bits |= kFlagOverBudget;
+  r.Mc = sh.m[r.m];
+  r.invS = 1.f / sh.S[r.m];
+  return r;
+}
 
 __device__ void write_invalid(const SampleArgs& a, int b, int bits) {
   const int ustride = a.k_max + 1;
@@ -39,8 +135,8 @@ __device__ void write_invalid(const SampleArgs& a, int b, int bits) {
   }
 }
 
-// Draw weights of 16 consecutive elements starting at e: residual
-// max(0, p - q) (resid) or p itself; p = 2^((l - M) c) / S.
+// Draw weights of the 16 elements this thread owns starting at e: residual
+// max(0, p - q) (resid) or p itself, and p and q.
 template <class DT, class DQ>
 __device__ __forceinline__ void draw_weights(const void* trow, const void* qrow, int64_t V, int64_t e,
                                              float c, float Mc, float invS, bool resid, float* w,
@@ -73,160 +169,52 @@ __device__ __forceinline__ float pairwise(const float* x) {
   return t[0];
 }
 
-}  // namespace
-
+// Sums (r, p, q) of one tile over the block; valid in every thread.
 template <class DT, class DQ>
-__global__ __launch_bounds__(kBlock) void k_sample_resolve(SampleArgs a) {
-  constexpr int kWaves = kBlock / kWave;
-  __shared__ float s_m[kMaxChainRows], s_S[kMaxChainRows], s_p[kMaxChainRows], s_q[kMaxChainRows];
-  __shared__ double s_tile[kSampleTilesPerBlock][kWaves][3];
-  __shared__ double s_red[3 * kWaves];
-  __shared__ int s_int[4];
+__device__ __forceinline__ void tile_sums(const SampleArgs& a, const void* trow, const void* qrow,
+                                          const Pre& pr, int t, double* v, double* red) {
+  float w[kPerThreadTile], p[kPerThreadTile], q[kPerThreadTile];
+  draw_weights<DT, DQ>(trow, qrow, a.V, static_cast<int64_t>(t) * kTile + threadIdx.x * kPerThreadTile,
+                       a.c, pr.Mc, pr.invS, pr.m < pr.k, w, p, q);
+  v[0] = pairwise<kPerThreadTile>(w);
+  v[1] = pairwise<kPerThreadTile>(p);
+  v[2] = pairwise<kPerThreadTile>(q);
+  block_sum<3>(v, red);
+}
 
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  const int b = blockIdx.x / a.chunks;
-  const int ch = blockIdx.x - b * a.chunks;
+// Draw the last token from the tile sums T[ntiles][3] and write the outputs.
+template <class DT, class DQ>
+__device__ void draw_and_emit(const SampleArgs& a, int b, const Pre& pr, const double* T,
+                              SampleShared& sh) {
+  const int tid = threadIdx.x;
   const int ustride = a.k_max + 1;
-  const int k = a.dlen[b];
-  const int ts = a.t_rs[b];
-  const int qs = a.q_rs[b];
-
-  // ---- request checks (identical in every block of the request) ----
-  const bool bad = k < 0 || k > a.k_max || ts < 0 || static_cast<int64_t>(ts) + k >= a.t_rows ||
-                   (k > 0 && (qs < 0 || static_cast<int64_t>(qs) + k > a.q_rows));
-  if (bad) {
-    if (ch == 0) write_invalid(a, b, kFlagBadRequest);
-    return;
-  }
-  if (tid == 0) {
-    s_int[0] = k;
-    s_int[1] = 0;
-  }
-  __syncthreads();
-  int x = 0;
-  if (tid < k) {
-    x = a.ids[static_cast<int64_t>(b) * a.k_max + tid];
-    if (x < 0 || x >= a.V) atomicOr(&s_int[1], kFlagBadToken);
-  }
-  __syncthreads();
-  if (s_int[1]) {
-    if (ch == 0) write_invalid(a, b, s_int[1]);
-    return;
-  }
-
-  // ---- row normalisers ----
-  if (tid <= k) {
-    const float2* pp = a.partial + static_cast<int64_t>(ts + tid) * a.nseg;
-    MS r{-INFINITY, 0.f};
-    for (int s = 0; s < a.nseg; ++s) {
-      const float2 v = pp[s];
-      r = ms_combine(r, MS{v.x, v.y});
-    }
-    s_m[tid] = r.m;
-    s_S[tid] = r.s;
-    if (!(r.s > 0.f && r.s < INFINITY)) atomicOr(&s_int[1], kFlagNonfinite);
-  }
-  __syncthreads();
-  if (s_int[1]) {
-    if (ch == 0) write_invalid(a, b, s_int[1]);
-    return;
-  }
-
-  // ---- p, q at the drafted tokens; accept scan ----
-  if (tid < k) {
-    const float l = DT::at(row_ptr<DT>(a.tgt, ts + tid, a.V), x);
-    const float p = ex2(fmaf(l, a.c, -s_m[tid])) * (1.f / s_S[tid]);
-    const float q = DQ::at(row_ptr<DQ>(a.dq, qs + tid, a.V), x);
-    s_p[tid] = p;
-    s_q[tid] = q;
-    const float uu = a.u[static_cast<int64_t>(b) * ustride + tid];
-    if (!(uu * q < p)) atomicMin(&s_int[0], tid);
-  }
-  __syncthreads();
-  const int m = s_int[0];
-
-  if (ch == 0) {
-    if (tid == 0 && a.max_new != nullptr && k > a.max_new[b]) flag(a.status, kFlagOverBudget);
-    if (a.diag != nullptr && tid <= k) {
-      float* d = a.diag + (static_cast<int64_t>(b) * ustride + tid) * 4;
-      d[0] = s_m[tid] * kLn2;
-      d[1] = s_S[tid];
-      d[2] = tid < k ? s_p[tid] : 0.f;
-      d[3] = tid < k ? s_q[tid] : 0.f;
-    }
-  }
-
-  // ---- tile sums of the draw row ----
-  const bool resid = m < k;
-  const float Mc = s_m[m];
-  const float invS = 1.f / s_S[m];
-  const void* trow = row_ptr<DT>(a.tgt, ts + m, a.V);
-  const void* qrow = resid ? row_ptr<DQ>(a.dq, qs + m, a.V) : nullptr;
-  const int t0 = ch * a.tpb;
-  const int t1 = min(t0 + a.tpb, a.ntiles);
-  for (int t = t0; t < t1; ++t) {
-    float w[kPerThreadTile], p[kPerThreadTile], q[kPerThreadTile];
-    draw_weights<DT, DQ>(trow, qrow, a.V, static_cast<int64_t>(t) * kTile + tid * kPerThreadTile, a.c,
-                         Mc, invS, resid, w, p, q);
-    double v0 = wave_sum(static_cast<double>(pairwise<kPerThreadTile>(w)));
-    double v1 = wave_sum(static_cast<double>(pairwise<kPerThreadTile>(p)));
-    double v2 = wave_sum(static_cast<double>(pairwise<kPerThreadTile>(q)));
-    if (lane == 0) {
-      s_tile[t - t0][wid][0] = v0;
-      s_tile[t - t0][wid][1] = v1;
-      s_tile[t - t0][wid][2] = v2;
-    }
-  }
-  __syncthreads();
-  if (tid < (t1 - t0) * 3) {
-    const int t = tid / 3, j = tid - 3 * (tid / 3);
-    double s = 0.0;
-    for (int wv = 0; wv < kWaves; ++wv) s += s_tile[t][wv][j];
-    a.tiles[(static_cast<int64_t>(b) * a.ntiles + t0 + t) * 3 + j] = s;
-  }
-
-  // ---- last block of the request draws the token ----
-  if (a.chunks > 1) {
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-      const unsigned prev = atomicAdd(&a.counters[b], 1u);
-      s_int[2] = (prev == static_cast<unsigned>(a.chunks - 1));
-    }
-    __syncthreads();
-    if (!s_int[2]) return;
-    __threadfence();
-  } else {
-    __syncthreads();
-  }
-
-  const double* T = a.tiles + static_cast<int64_t>(b) * a.ntiles * 3;
+  const bool resid = pr.m < pr.k;
   double tot[3] = {0.0, 0.0, 0.0};
   for (int t = tid; t < a.ntiles; t += kBlock) {
     tot[0] += T[3 * t];
     tot[1] += T[3 * t + 1];
     tot[2] += T[3 * t + 2];
   }
-  block_sum<3>(tot, s_red);
-  int bits = 0;
+  block_sum<3>(tot, sh.red);
+  int bits = pr.bits;
   int which = 0;  // 0: weights are r; 1: weights are p
   if (resid) {
     if (isnan(tot[2]) || !isfinite(tot[0])) {
-      write_invalid(a, b, kFlagNonfinite);
+      write_invalid(a, b, kFlagNonfinite | bits);
       return;
     }
     if (!(tot[0] > 0.0)) {
-      bits = kFlagFallback;
+      bits |= kFlagFallback;
       which = 1;
     }
   }
   const double total = tot[which];
-  const double target = static_cast<double>(a.u[static_cast<int64_t>(b) * ustride + k]) * total;
+  const double target = static_cast<double>(a.u[static_cast<int64_t>(b) * ustride + pr.k]) * total;
 
-  // first tile whose running sum exceeds the target (else the last tile with mass)
+  // first tile with mass whose running sum exceeds the target (else the last tile with mass)
   if (tid == 0) {
-    s_int[2] = a.ntiles;   // first crossing tile
-    s_int[3] = -1;         // last tile with mass
+    sh.i[2] = a.ntiles;
+    sh.i[3] = -1;
   }
   __syncthreads();
   double carry = 0.0, tile_base = 0.0;
@@ -234,73 +222,75 @@ __global__ __launch_bounds__(kBlock) void k_sample_resolve(SampleArgs a) {
     const int t = c0 + tid;
     const double wt = t < a.ntiles ? T[3 * t + which] : 0.0;
     double chunk_total;
-    const double excl = carry + block_exclusive_scan(wt, &chunk_total, s_red);
-    if (t < a.ntiles) {
-      if (wt > 0.0 && excl + wt > target) atomicMin(&s_int[2], t);
-      if (wt > 0.0) atomicMax(&s_int[3], t);
+    const double excl = carry + block_exclusive_scan(wt, &chunk_total, sh.red);
+    if (t < a.ntiles && wt > 0.0) {
+      if (excl + wt > target) atomicMin(&sh.i[2], t);
+      atomicMax(&sh.i[3], t);
     }
     __syncthreads();
-    const int hit = s_int[2];
+    const int hit = sh.i[2];
     if (hit >= c0 && hit < c0 + kBlock) {
-      if (t == hit) s_red[0] = excl;
+      if (t == hit) sh.red[0] = excl;
       __syncthreads();
-      tile_base = s_red[0];
+      tile_base = sh.red[0];
       __syncthreads();
       break;
     }
     carry += chunk_total;
   }
-  int tile = s_int[2];
-  bool overshoot = false;
-  if (tile >= a.ntiles) {
-    tile = s_int[3];
-    overshoot = true;
-  }
+  int tile = sh.i[2];
+  const bool overshoot = tile >= a.ntiles;
+  if (overshoot) tile = sh.i[3];
   __syncthreads();
-  if (tile < 0) {          // no mass anywhere (cannot happen with S > 0); defined output
-    write_invalid(a, b, kFlagNonfinite);
+  if (tile < 0) {  // no mass anywhere (cannot happen when S > 0); defined output
+    write_invalid(a, b, kFlagNonfinite | bits);
     return;
   }
 
-  // rescan the chosen tile: smallest id whose running weight exceeds target
+  // rescan the chosen tile: smallest id with positive weight whose running
+  // weight exceeds the target (else the last id with weight)
   if (tid == 0) {
-    s_int[2] = INT32_MAX;  // first crossing element
-    s_int[3] = -1;         // last element with weight
+    sh.i[2] = INT32_MAX;
+    sh.i[3] = -1;
   }
   __syncthreads();
+  const void* trow = row_ptr<DT>(a.tgt, pr.ts + pr.m, a.V);
+  const void* qrow = resid ? row_ptr<DQ>(a.dq, pr.qs + pr.m, a.V) : nullptr;
   {
     float w[kPerThreadTile], p[kPerThreadTile], q[kPerThreadTile];
-    const int64_t e0 = static_cast<int64_t>(tile) * kTile + tid * kPerThreadTile;
-    draw_weights<DT, DQ>(trow, qrow, a.V, e0, a.c, Mc, invS, resid, w, p, q);
-    double cum[kPerThreadTile];
-    double run = 0.0;
+    const int off = tid * kPerThreadTile;
+    draw_weights<DT, DQ>(trow, qrow, a.V, static_cast<int64_t>(tile) * kTile + off, a.c, pr.Mc, pr.invS,
+                         resid, w, p, q);
+    if (which) {
 #pragma unroll
-    for (int j = 0; j < kPerThreadTile; ++j) {
-      run += static_cast<double>(which ? p[j] : w[j]);
-      cum[j] = run;
+      for (int j = 0; j < kPerThreadTile; ++j) w[j] = p[j];
     }
+    double own = 0.0;
+#pragma unroll
+    for (int j = 0; j < kPerThreadTile; ++j) own += static_cast<double>(w[j]);
     double tile_total;
-    const double excl = block_exclusive_scan(run, &tile_total, s_red);
+    double run = tile_base + block_exclusive_scan(own, &tile_total, sh.red);
     int first = INT32_MAX, lastpos = -1;
 #pragma unroll
-    for (int j = kPerThreadTile - 1; j >= 0; --j) {
-      const float wj = which ? p[j] : w[j];
-      if (!overshoot && wj > 0.f && tile_base + excl + cum[j] > target)
-        first = static_cast<int>(e0 - static_cast<int64_t>(tile) * kTile) + j;
-      if (wj > 0.f && lastpos < 0) lastpos = static_cast<int>(e0 - static_cast<int64_t>(tile) * kTile) + j;
+    for (int j = 0; j < kPerThreadTile; ++j) {
+      run += static_cast<double>(w[j]);
+      if (w[j] > 0.f) {
+        if (first == INT32_MAX && !overshoot && run > target) first = off + j;
+        lastpos = off + j;
+      }
     }
-    if (first != INT32_MAX) atomicMin(&s_int[2], first);
-    if (lastpos >= 0) atomicMax(&s_int[3], lastpos);
+    if (first != INT32_MAX) atomicMin(&sh.i[2], first);
+    if (lastpos >= 0) atomicMax(&sh.i[3], lastpos);
   }
   __syncthreads();
-  int pick = s_int[2] != INT32_MAX ? s_int[2] : s_int[3];
+  const int pick = sh.i[2] != INT32_MAX ? sh.i[2] : sh.i[3];
   const int y = static_cast<int>(static_cast<int64_t>(tile) * kTile + pick);
 
   if (tid == 0) {
     int32_t* out = a.out_tok + static_cast<int64_t>(b) * ustride;
     int cnt = 0;
     bool stop = false;
-    for (int i = 0; i < m && !stop; ++i) {
+    for (int i = 0; i < pr.m && !stop; ++i) {
       const int32_t tok = a.ids[static_cast<int64_t>(b) * a.k_max + i];
       out[cnt++] = tok;
       if (a.eos >= 0 && tok == a.eos) stop = true;
@@ -312,23 +302,88 @@ __global__ __launch_bounds__(kBlock) void k_sample_resolve(SampleArgs a) {
     }
     for (int i = cnt; i < ustride; ++i) out[i] = -1;
     a.out_cnt[b] = cnt;
-    a.out_acc[b] = m;
+    a.out_acc[b] = pr.m;
     if (a.resid) a.resid[b] = static_cast<float>(total);
     flag(a.status, bits);
   }
 }
 
-hipError_t launch_sample_resolve(int t_dtype, int q_dtype, const SampleArgs& a, hipStream_t stream) {
-  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.chunks)), block(kBlock);
-  if (t_dtype == kDtypeBF16 && q_dtype == kDtypeBF16)
-    hipLaunchKernelGGL((k_sample_resolve<BF16, BF16>), grid, block, 0, stream, a);
-  else if (t_dtype == kDtypeBF16)
-    hipLaunchKernelGGL((k_sample_resolve<BF16, F32>), grid, block, 0, stream, a);
-  else if (q_dtype == kDtypeBF16)
-    hipLaunchKernelGGL((k_sample_resolve<F32, BF16>), grid, block, 0, stream, a);
-  else
-    hipLaunchKernelGGL((k_sample_resolve<F32, F32>), grid, block, 0, stream, a);
+}  // namespace
+
+template <class DT, class DQ>
+__global__ __launch_bounds__(kBlock) void k_sample_tiles(SampleArgs a) {
+  __shared__ SampleShared sh;
+  __shared__ double s_tile[3];
+  const int b = blockIdx.x / a.ntiles;
+  const int t = blockIdx.x - b * a.ntiles;
+  const Pre pr = preamble<DT, DQ>(a, b, t == 0, sh);
+  if (pr.bits & kInvalid) {
+    if (a.ntiles == 1) {
+      write_invalid(a, b, pr.bits);
+    } else if (t == 0 && threadIdx.x == 0) {
+      a.records[b] = make_int4(pr.bits, 0, 0, 0);
+    }
+    return;
+  }
+  const void* trow = row_ptr<DT>(a.tgt, pr.ts + pr.m, a.V);
+  const void* qrow = pr.m < pr.k ? row_ptr<DQ>(a.dq, pr.qs + pr.m, a.V) : nullptr;
+  double v[3];
+  tile_sums<DT, DQ>(a, trow, qrow, pr, t, v, sh.red);
+  if (a.ntiles == 1) {
+    if (threadIdx.x == 0) {
+      s_tile[0] = v[0];
+      s_tile[1] = v[1];
+      s_tile[2] = v[2];
+    }
+    __syncthreads();
+    draw_and_emit<DT, DQ>(a, b, pr, s_tile, sh);
+    return;
+  }
+  if (threadIdx.x == 0) {
+    double* T = a.tiles + (static_cast<int64_t>(b) * a.ntiles + t) * 3;
+    T[0] = v[0];
+    T[1] = v[1];
+    T[2] = v[2];
+    if (t == 0)
+      a.records[b] = make_int4(pr.bits, pr.m, __float_as_int(pr.Mc), __float_as_int(pr.invS));
+  }
+}
+
+template <class DT, class DQ>
+__global__ __launch_bounds__(kBlock) void k_sample_draw(SampleArgs a) {
+  __shared__ SampleShared sh;
+  const int b = blockIdx.x;
+  const int4 rec = a.records[b];
+  if (rec.x & kInvalid) {
+    write_invalid(a, b, rec.x);
+    return;
+  }
+  Pre pr{};
+  pr.bits = rec.x;
+  pr.m = rec.y;
+  pr.Mc = __int_as_float(rec.z);
+  pr.invS = __int_as_float(rec.w);
+  pr.k = a.dlen[b];
+  pr.ts = a.t_rs[b];
+  pr.qs = a.q_rs[b];
+  draw_and_emit<DT, DQ>(a, b, pr, a.tiles + static_cast<int64_t>(b) * a.ntiles * 3, sh);
+}
+
+template <class DT, class DQ>
+static hipError_t launch_pair(const SampleArgs& a, hipStream_t stream) {
+  const dim3 block(kBlock);
+  hipLaunchKernelGGL((k_sample_tiles<DT, DQ>),
+                     dim3(static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.ntiles)), block, 0, stream, a);
+  if (a.ntiles > 1)
+    hipLaunchKernelGGL((k_sample_draw<DT, DQ>), dim3(static_cast<uint32_t>(a.B)), block, 0, stream, a);
   return hipGetLastError();
+}
+
+hipError_t launch_sample_resolve(int t_dtype, int q_dtype, const SampleArgs& a, hipStream_t stream) {
+  if (t_dtype == kDtypeBF16 && q_dtype == kDtypeBF16) return launch_pair<BF16, BF16>(a, stream);
+  if (t_dtype == kDtypeBF16) return launch_pair<BF16, F32>(a, stream);
+  if (q_dtype == kDtypeBF16) return launch_pair<F32, BF16>(a, stream);
+  return launch_pair<F32, F32>(a, stream);
 }
 
 }  // namespace sv

@@ -20,8 +20,7 @@ namespace sv {
 template <class D, int U>
 __global__ __launch_bounds__(kBlock) void k_row_stats(const void* __restrict__ rows, int64_t V,
                                                       int32_t nseg, float c,
-                                                      float2* __restrict__ partial,
-                                                      uint32_t* __restrict__ zero, int64_t n_zero) {
+                                                      float2* __restrict__ partial) {
   __shared__ float sh[2 * (kBlock / kWave)];
   const int64_t row = blockIdx.x / nseg;
   const int32_t seg = blockIdx.x - static_cast<int32_t>(row) * nseg;
@@ -61,22 +60,15 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(const void* __restrict__ r
   }
   const MS r = block_ms(acc, sh);
   if (threadIdx.x == 0) partial[blockIdx.x] = make_float2(r.m, r.s);
-  // clear the consumer's per-request arrival counters for this call
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n_zero;
-       i += static_cast<int64_t>(gridDim.x) * kBlock)
-    zero[i] = 0u;
 }
 
 hipError_t launch_row_stats(int dtype, const void* rows, int64_t n_rows, int64_t V, int32_t nseg,
-                            float c, float2* partial, uint32_t* zero, int64_t n_zero,
-                            hipStream_t stream) {
+                            float c, float2* partial, hipStream_t stream) {
   const dim3 grid(static_cast<uint32_t>(n_rows * nseg)), block(kBlock);
   if (dtype == kDtypeBF16)
-    hipLaunchKernelGGL((k_row_stats<BF16, 4>), grid, block, 0, stream, rows, V, nseg, c, partial, zero,
-                       n_zero);
+    hipLaunchKernelGGL((k_row_stats<BF16, 4>), grid, block, 0, stream, rows, V, nseg, c, partial);
   else
-    hipLaunchKernelGGL((k_row_stats<F32, 4>), grid, block, 0, stream, rows, V, nseg, c, partial, zero,
-                       n_zero);
+    hipLaunchKernelGGL((k_row_stats<F32, 4>), grid, block, 0, stream, rows, V, nseg, c, partial);
   return hipGetLastError();
 }
 

@@ -12,7 +12,6 @@ constexpr int kDtypeBF16 = 1;
 constexpr int kMaxChainRows = 256;     // k_max + 1 rows per request at most
 constexpr int kMaxTreeNodes = 1024;
 constexpr int kMaxTreeTiles = 256;     // tree vocab <= 256 * 4096
-constexpr int kSampleTilesPerBlock = 4;
 constexpr int kMaxWindow = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -35,7 +34,7 @@ inline int64_t tiles_of(int64_t V) { return (V + 4095) / 4096; }
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 struct SampleLayout {
-  size_t partial_off, tiles_off, counter_off, bytes;
+  size_t partial_off, tiles_off, records_off, bytes;
 };
 
 inline SampleLayout sample_layout(int64_t B, int64_t t_rows, int64_t V) {
@@ -43,8 +42,8 @@ inline SampleLayout sample_layout(int64_t B, int64_t t_rows, int64_t V) {
   const int64_t nseg = row_segments(t_rows, V);
   L.partial_off = 0;
   L.tiles_off = align256(static_cast<size_t>(t_rows * nseg) * 8);
-  L.counter_off = L.tiles_off + align256(static_cast<size_t>(B * tiles_of(V)) * 3 * 8);
-  L.bytes = L.counter_off + align256(static_cast<size_t>(B) * 4);
+  L.records_off = L.tiles_off + align256(static_cast<size_t>(B * tiles_of(V)) * 3 * 8);
+  L.bytes = L.records_off + align256(static_cast<size_t>(B) * 16);
   return L;
 }
 
@@ -70,9 +69,9 @@ struct SampleArgs {
   int32_t* status;
   const float2* partial;
   int32_t nseg;
-  double* tiles;
-  uint32_t* counters;
-  int32_t ntiles, tpb, chunks;
+  double* tiles;     // [B, ntiles, 3] sums of (draw weights, p, q) per tile
+  int4* records;     // [B] (status bits, m, scaled max, 1/normaliser) of the draw row
+  int32_t ntiles;
 };
 
 struct GreedyArgs {
@@ -114,8 +113,7 @@ struct TreeArgs {
 };
 
 hipError_t launch_row_stats(int dtype, const void* rows, int64_t n_rows, int64_t V, int32_t nseg,
-                            float c, float2* partial, uint32_t* zero, int64_t n_zero,
-                            hipStream_t stream);
+                            float c, float2* partial, hipStream_t stream);
 hipError_t launch_sample_resolve(int t_dtype, int q_dtype, const SampleArgs& a,
                                  hipStream_t stream);
 hipError_t launch_row_argmax(int dtype, const void* rows, int64_t n_rows, int64_t V, int32_t nseg,

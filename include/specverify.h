@@ -45,9 +45,8 @@
  *   NONFINITE or BAD_TREE is invalid: count 0, accepted 0, all tokens -1.
  * - Workspace (greedy, sample, tree): caller-owned device memory of at least
  *   sv_workspace_bytes(...) bytes, 256-byte aligned.  Its contents need not be
- *   initialised: each call writes everything it later reads (the sampled
- *   verify clears its per-request arrival counters in its first kernel), so
- *   one buffer can serve calls of any shape in turn on one stream.  Calls that
+ *   initialised: each call writes everything it later reads, so one buffer
+ *   can serve calls of any shape in turn on one stream.  Calls that
  *   may run concurrently (different streams) need separate workspaces.
  */
 #ifndef SPECVERIFY_H
