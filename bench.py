@@ -6,8 +6,8 @@ A step is one sampled chain verify (sv_verify_sample: softmax statistics of
 every target row, accept scan, residual and inverse-CDF draw) over one batch
 of synthetic inputs already resident in HBM.  The default workload is the
 sampled chain at B=64 requests, k=4 drafts, V=248,320, bf16 target logits and
-bf16 draft probabilities, T=0.7; two input sets alternate so consecutive steps
-do not reuse cached rows.  Prints one JSON line.
+bf16 draft probabilities, T=0.7; three input sets rotate so that no step finds
+its rows in the 256 MB last-level cache.  Prints one JSON line.
 
 Other workloads (``--workload c1|c2|c4|c5``) print the same kind of line for
 the other configurations (fixed-prefix chain, greedy + prompt lookup, ragged
@@ -140,16 +140,16 @@ def main():
     if W in ("c1", "c3", "c4"):
         log(f"generating {W} inputs")
         if W == "c3":
-            sets = [synth.c3_sampled(salt=s) for s in (0, 1)]
+            sets = [synth.c3_sampled(salt=s) for s in (0, 1, 2)]
             cfg = dict(workload="sampled chain verify (speculative sampling): 64 requests, k=4 drafts, "
                                 "V=248,320, bf16 target logits ~N(0,2.5^2)+6 on 5 ids, bf16 draft "
                                 "probabilities, T=0.7", batch=64, k=4, vocab=248_320,
-                       temperature=0.7, inputs="bf16", input_sets=2)
+                       temperature=0.7, inputs="bf16", input_sets=3)
         elif W == "c4":
-            sets = [synth.c4_ragged(salt=s) for s in (0, 1)]
+            sets = [synth.c4_ragged(salt=s) for s in (0, 1, 2)]
             cfg = dict(workload="ragged sampled chain verify: 256 requests, k in 1..8, V=151,936, bf16, "
                                 "T=1", batch=256, vocab=151_936, temperature=1.0, inputs="bf16",
-                       input_sets=2)
+                       input_sets=3)
         else:
             sets = [synth.c1_chain()]
             cfg = dict(workload="fixed-prefix sampled chain: 200,000 rounds sharing 5 target and 4 draft "

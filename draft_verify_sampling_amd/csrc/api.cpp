@@ -63,6 +63,7 @@ size_t sv_workspace_bytes(int op, int64_t batch, int64_t total_rows, int64_t voc
   if (batch < 0 || total_rows < 0 || vocab <= 0) return 0;
   switch (op) {
     case SV_OP_GREEDY:
+      return sv::align256(static_cast<size_t>(total_rows * sv::argmax_segments(total_rows, vocab)) * 8);
     case SV_OP_TREE:
       return sv::align256(static_cast<size_t>(total_rows * sv::row_segments(total_rows, vocab)) * 8);
     case SV_OP_SAMPLE:
@@ -127,7 +128,7 @@ sv_status sv_verify_greedy(const void* target_logits, int32_t t_dtype, int32_t t
       out_tokens == nullptr || out_count == nullptr || out_accepted == nullptr ||
       (k_max > 0 && draft_ids == nullptr))
     return fail(SV_E_ARG, "null pointer argument");
-  const int32_t nseg = sv::row_segments(t_rows, vocab);
+  const int32_t nseg = sv::argmax_segments(t_rows, vocab);
   if (static_cast<int64_t>(t_rows) * nseg > kMaxGrid) return fail(SV_E_ARG, "too many rows");
   const size_t need = sv_workspace_bytes(SV_OP_GREEDY, batch, t_rows, vocab);
   if (sv_status s = check_workspace(workspace, workspace_bytes, need)) return s;

@@ -154,6 +154,63 @@ __device__ __forceinline__ MS block_ms(MS v, float* sh) {
 }
 
 // ---------------------------------------------------------------------------
+// Wave-level scans with DPP lane moves (GFX9 row shifts and row broadcasts):
+// each step is a register move between lanes, no LDS round trip.  Lanes whose
+// source is outside the move's reach read `ident`.
+// ---------------------------------------------------------------------------
+template <int ctrl, int row_mask>
+__device__ __forceinline__ float dpp_f(float v, float ident) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(ident), __float_as_int(v), ctrl,
+                                                    row_mask, 0xf, false));
+}
+
+template <int ctrl, int row_mask>
+__device__ __forceinline__ double dpp_d(double v) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(v));
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u)), ctrl, row_mask, 0xf, false));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(u >> 32)), ctrl, row_mask, 0xf, false));
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (lane order).
+__device__ __forceinline__ double wave_incl_scan(double x) {
+  x += dpp_d<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_d<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_d<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_d<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_d<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_d<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
+__device__ __forceinline__ double lane_value(double x, int lane) {
+  const uint64_t u = static_cast<uint64_t>(__double_as_longlong(x));
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u)), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(u >> 32)), lane);
+  return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
+}
+
+// Sum over the wave, valid in every lane.
+__device__ __forceinline__ double wave_total(double x) { return lane_value(wave_incl_scan(x), kWave - 1); }
+
+// Online-softmax pair over the wave, valid in every lane.
+__device__ __forceinline__ MS wave_ms_dpp(MS v) {
+#define SV_MS_STEP(ctrl, rm)                                                     \
+  v = ms_combine(v, MS{dpp_f<ctrl, rm>(v.m, -INFINITY), dpp_f<ctrl, rm>(v.s, 0.f)});
+  SV_MS_STEP(0x111, 0xf)
+  SV_MS_STEP(0x112, 0xf)
+  SV_MS_STEP(0x114, 0xf)
+  SV_MS_STEP(0x118, 0xf)
+  SV_MS_STEP(0x142, 0xa)
+  SV_MS_STEP(0x143, 0xc)
+#undef SV_MS_STEP
+  return MS{__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v.m), kWave - 1)),
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v.s), kWave - 1))};
+}
+
+// ---------------------------------------------------------------------------
 // Plain block reductions / scans.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ double wave_sum(double v) {

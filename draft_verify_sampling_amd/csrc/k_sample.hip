@@ -10,17 +10,19 @@
 // Runs after the row-statistics kernel has left the softmax partials of every
 // target row.  Two kernels, with no communication between blocks of one grid:
 //
-// k_sample_tiles: grid = batch * ntiles blocks, one 4096-element tile each.
-//   Every block repeats the request's small preamble (row normalisers from
-//   the partials, p and q at the drafted tokens, the accept scan), so all of
-//   a request's blocks agree on the break position m.  The block then reads
-//   its tile of target row m (and of draft row m when m < k) and writes the
-//   float64 sums of the draw weights r, of p and of q for that tile.  Tile 0
-//   also writes the request's record (status bits, m, row scale) and the
-//   diagnostics.  When the vocabulary fits one tile the block draws the token
-//   itself and no second kernel runs.
-// k_sample_draw: one block per request.  Scans the tile sums, finds the tile
-//   holding u_k * total, rescans that tile with a block prefix sum and picks
+// k_sample_tiles: grid = batch * ceil(ntiles / 4) blocks, so the whole grid
+//   is resident at once.  Every block repeats the request's small preamble
+//   (row normalisers from the partials, p and q at the drafted tokens, the
+//   accept scan), so all of a request's blocks agree on the break position m.
+//   Then each of the block's four waves reads one 4096-element tile of target
+//   row m (and of draft row m when m < k), all of its loads in flight at once,
+//   and writes the float64 sums of the draw weights r, of p and of q for that
+//   tile.  Block 0 of a request also writes the request's record (status bits,
+//   m, row scale) and the diagnostics.
+// k_sample_single replaces both when the vocabulary fits one tile: one block
+//   per request runs the preamble, then one wave sums the tile and draws.
+// k_sample_draw: one wave per request.  Scans the tile sums, finds the tile
+//   holding u_k * total, rescans that tile with a wave prefix sum and picks
 //   the smallest id whose running weight exceeds it; writes the tokens.
 //
 // Only the break row's draft row is read from HBM: the accept test needs just
@@ -42,12 +44,16 @@ struct Pre {
   float invS;   // 1 / normaliser of the draw row
 };
 
+
 struct SampleShared {
   float m[kMaxChainRows], S[kMaxChainRows], p[kMaxChainRows], q[kMaxChainRows];
+  int32_t ids[kMaxChainRows];
   float2 part[kMaxPartialsInLds];
   double red[3 * (kBlock / kWave)];
+  float ufinal;
   int i[4];
 };
+
 
 constexpr int kInvalid = kFlagBadRequest | kFlagBadToken | kFlagNonfinite;
 
@@ -80,8 +86,10 @@ __device__ Pre preamble(const SampleArgs& a, int b, bool write_diag, SampleShare
   int x = 0;
   if (tid < k) {
     x = a.ids[static_cast<int64_t>(b) * a.k_max + tid];
+    sh.ids[tid] = x;
     if (x < 0 || x >= a.V) atomicOr(&sh.i[1], kFlagBadToken);
   }
+  if (tid == kBlock - 1) sh.ufinal = a.u[static_cast<int64_t>(b) * ustride + k];
   if (tid <= k) {
     const float2* pp = lds_parts ? sh.part + tid * a.nseg
                                  : a.partial + static_cast<int64_t>(r.ts + tid) * a.nseg;
@@ -169,129 +177,172 @@ __device__ __forceinline__ float pairwise(const float* x) {
   return t[0];
 }
 
-// Sums (r, p, q) of one tile over the block; valid in every thread.
-template <class DT, class DQ>
-__device__ __forceinline__ void tile_sums(const SampleArgs& a, const void* trow, const void* qrow,
-                                          const Pre& pr, int t, double* v, double* red) {
-  float w[kPerThreadTile], p[kPerThreadTile], q[kPerThreadTile];
-  draw_weights<DT, DQ>(trow, qrow, a.V, static_cast<int64_t>(t) * kTile + threadIdx.x * kPerThreadTile,
-                       a.c, pr.Mc, pr.invS, pr.m < pr.k, w, p, q);
-  v[0] = pairwise<kPerThreadTile>(w);
-  v[1] = pairwise<kPerThreadTile>(p);
-  v[2] = pairwise<kPerThreadTile>(q);
-  block_sum<3>(v, red);
+// Shift a wave-inclusive scan into an exclusive one (lane 0 reads 0).
+__device__ __forceinline__ double wave_exclusive_from_inclusive(double incl) {
+  return dpp_d<0x138, 0xf>(incl);  // wave_shr:1
 }
 
 // Draw the last token from the tile sums T[ntiles][3] and write the outputs.
+// Run by exactly one wave (64 lanes); ids[0..m) and ufinal are the request's
+// drafted tokens and final uniform.  Lane l owns the contiguous tiles
+// [l * tpl, (l + 1) * tpl), then the contiguous 64 elements [64 l, 64 l + 64)
+// of the chosen tile; crossings are located with wave scans and ballots.
 template <class DT, class DQ>
-__device__ void draw_and_emit(const SampleArgs& a, int b, const Pre& pr, const double* T,
-                              SampleShared& sh) {
-  const int tid = threadIdx.x;
+__device__ void wave_draw_emit(const SampleArgs& a, int b, const Pre& pr, const double* T,
+                               const int32_t* ids, float ufinal) {
+  const int lane = threadIdx.x & (kWave - 1);
   const int ustride = a.k_max + 1;
   const bool resid = pr.m < pr.k;
-  double tot[3] = {0.0, 0.0, 0.0};
-  for (int t = tid; t < a.ntiles; t += kBlock) {
-    tot[0] += T[3 * t];
-    tot[1] += T[3 * t + 1];
-    tot[2] += T[3 * t + 2];
+  const int tpl = (a.ntiles + kWave - 1) / kWave;
+  const int ta = lane * tpl;
+  const int tb = min(ta + tpl, a.ntiles);
+  double own[3] = {0.0, 0.0, 0.0};
+  for (int t = ta; t < tb; ++t) {
+    own[0] += T[3 * t];
+    own[1] += T[3 * t + 1];
+    own[2] += T[3 * t + 2];
   }
-  block_sum<3>(tot, sh.red);
+  const double tot_r = wave_total(own[0]), tot_p = wave_total(own[1]), tot_q = wave_total(own[2]);
   int bits = pr.bits;
   int which = 0;  // 0: weights are r; 1: weights are p
   if (resid) {
-    if (isnan(tot[2]) || !isfinite(tot[0])) {
+    if (isnan(tot_q) || !isfinite(tot_r)) {
       write_invalid(a, b, kFlagNonfinite | bits);
       return;
     }
-    if (!(tot[0] > 0.0)) {
+    if (!(tot_r > 0.0)) {
       bits |= kFlagFallback;
       which = 1;
     }
   }
-  const double total = tot[which];
-  const double target = static_cast<double>(a.u[static_cast<int64_t>(b) * ustride + pr.k]) * total;
+  const double total = which ? tot_p : tot_r;
+  const double target = static_cast<double>(ufinal) * total;
 
-  // first tile with mass whose running sum exceeds the target (else the last tile with mass)
-  if (tid == 0) {
-    sh.i[2] = a.ntiles;
-    sh.i[3] = -1;
-  }
-  __syncthreads();
-  double carry = 0.0, tile_base = 0.0;
-  for (int c0 = 0; c0 < a.ntiles; c0 += kBlock) {
-    const int t = c0 + tid;
-    const double wt = t < a.ntiles ? T[3 * t + which] : 0.0;
-    double chunk_total;
-    const double excl = carry + block_exclusive_scan(wt, &chunk_total, sh.red);
-    if (t < a.ntiles && wt > 0.0) {
-      if (excl + wt > target) atomicMin(&sh.i[2], t);
-      atomicMax(&sh.i[3], t);
+  // the tile: first one with mass whose running sum exceeds the target
+  const double mine = which ? own[1] : own[0];
+  double run = wave_exclusive_from_inclusive(wave_incl_scan(mine));
+  int hit = -1, lastpos = -1;
+  double hit_base = 0.0;
+  for (int t = ta; t < tb; ++t) {
+    const double wt = T[3 * t + which];
+    if (wt > 0.0) {
+      if (hit < 0 && run + wt > target) {
+        hit = t;
+        hit_base = run;
+      }
+      lastpos = t;
     }
-    __syncthreads();
-    const int hit = sh.i[2];
-    if (hit >= c0 && hit < c0 + kBlock) {
-      if (t == hit) sh.red[0] = excl;
-      __syncthreads();
-      tile_base = sh.red[0];
-      __syncthreads();
-      break;
-    }
-    carry += chunk_total;
+    run += wt;
   }
-  int tile = sh.i[2];
-  const bool overshoot = tile >= a.ntiles;
-  if (overshoot) tile = sh.i[3];
-  __syncthreads();
-  if (tile < 0) {  // no mass anywhere (cannot happen when S > 0); defined output
-    write_invalid(a, b, kFlagNonfinite | bits);
-    return;
+  int tile;
+  double tile_base = 0.0;
+  bool overshoot = false;
+  {
+    const uint64_t found = __ballot(hit >= 0);
+    if (found) {
+      const int src = __ffsll(static_cast<long long>(found)) - 1;
+      tile = __builtin_amdgcn_readlane(hit, src);
+      tile_base = lane_value(hit_base, src);
+    } else {
+      const uint64_t any = __ballot(lastpos >= 0);
+      if (!any) {  // no mass anywhere (cannot happen when S > 0); defined output
+        write_invalid(a, b, kFlagNonfinite | bits);
+        return;
+      }
+      const int src = 63 - __clzll(static_cast<long long>(any));
+      tile = __builtin_amdgcn_readlane(lastpos, src);
+      overshoot = true;
+    }
   }
 
-  // rescan the chosen tile: smallest id with positive weight whose running
-  // weight exceeds the target (else the last id with weight)
-  if (tid == 0) {
-    sh.i[2] = INT32_MAX;
-    sh.i[3] = -1;
-  }
-  __syncthreads();
+  // the id: rescan the tile; lane l owns its elements [64 l, 64 l + 64), read
+  // in one round (raw 16-byte vectors when aligned) and walked twice from
+  // registers: once for the lane's sum, once for the crossing.
   const void* trow = row_ptr<DT>(a.tgt, pr.ts + pr.m, a.V);
   const void* qrow = resid ? row_ptr<DQ>(a.dq, pr.qs + pr.m, a.V) : nullptr;
-  {
-    float w[kPerThreadTile], p[kPerThreadTile], q[kPerThreadTile];
-    const int off = tid * kPerThreadTile;
-    draw_weights<DT, DQ>(trow, qrow, a.V, static_cast<int64_t>(tile) * kTile + off, a.c, pr.Mc, pr.invS,
-                         resid, w, p, q);
-    if (which) {
+  const int64_t e0 = static_cast<int64_t>(tile) * kTile + lane * 64;
+  constexpr int kTV = 64 / DT::kPerVec, kQV = 64 / DQ::kPerVec;
+  uint4 tv[kTV], qv[kQV];
+  const bool fast = e0 + 64 <= a.V &&
+                    ((reinterpret_cast<uintptr_t>(trow) + e0 * DT::kSize) & 15u) == 0 &&
+                    (!resid || ((reinterpret_cast<uintptr_t>(qrow) + e0 * DQ::kSize) & 15u) == 0);
+  if (fast) {
 #pragma unroll
-      for (int j = 0; j < kPerThreadTile; ++j) w[j] = p[j];
+    for (int j = 0; j < kTV; ++j)
+      tv[j] = *reinterpret_cast<const uint4*>(static_cast<const char*>(trow) + (e0 + j * DT::kPerVec) * DT::kSize);
+    if (resid) {
+#pragma unroll
+      for (int j = 0; j < kQV; ++j)
+        qv[j] = *reinterpret_cast<const uint4*>(static_cast<const char*>(qrow) + (e0 + j * DQ::kPerVec) * DQ::kSize);
     }
-    double own = 0.0;
+  }
+  // the lane's 64 draw weights, in groups of 8 elements
+  float wv[64];
 #pragma unroll
-    for (int j = 0; j < kPerThreadTile; ++j) own += static_cast<double>(w[j]);
-    double tile_total;
-    double run = tile_base + block_exclusive_scan(own, &tile_total, sh.red);
-    int first = INT32_MAX, lastpos = -1;
+  for (int g = 0; g < 8; ++g) {
+    float l[8], q[8];
+    if (fast) {
+      if (DT::kPerVec == 8) {
+        DT::unpack(tv[g], l);
+      } else {
+        DT::unpack(tv[2 * g], l);
+        DT::unpack(tv[2 * g + 1], l + 4);
+      }
+      if (resid) {
+        if (DQ::kPerVec == 8) {
+          DQ::unpack(qv[g], q);
+        } else {
+          DQ::unpack(qv[2 * g], q);
+          DQ::unpack(qv[2 * g + 1], q + 4);
+        }
+      }
+    } else {
 #pragma unroll
-    for (int j = 0; j < kPerThreadTile; ++j) {
-      run += static_cast<double>(w[j]);
-      if (w[j] > 0.f) {
-        if (first == INT32_MAX && !overshoot && run > target) first = off + j;
-        lastpos = off + j;
+      for (int j = 0; j < 8; ++j) {
+        const int64_t e = e0 + 8 * g + j;
+        const bool in = e < a.V;
+        l[j] = in ? DT::at(trow, e) : -INFINITY;
+        q[j] = (in && resid) ? DQ::at(qrow, e) : 0.f;
       }
     }
-    if (first != INT32_MAX) atomicMin(&sh.i[2], first);
-    if (lastpos >= 0) atomicMax(&sh.i[3], lastpos);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = ex2(fmaf(l[j], a.c, -pr.Mc)) * pr.invS;
+      wv[8 * g + j] = (which || !resid) ? p : fmaxf(p - (resid ? q[j] : 0.f), 0.f);
+    }
   }
-  __syncthreads();
-  const int pick = sh.i[2] != INT32_MAX ? sh.i[2] : sh.i[3];
+  double lsum = 0.0;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) lsum += static_cast<double>(wv[i]);
+  double erun = tile_base + wave_exclusive_from_inclusive(wave_incl_scan(lsum));
+  int first = -1, lastw = -1;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) {
+    const float wj = wv[i];
+    if (wj > 0.f) {
+      if (first < 0 && !overshoot && erun + wj > target) first = lane * 64 + i;
+      lastw = lane * 64 + i;
+    }
+    erun += static_cast<double>(wj);
+  }
+  int pick;
+  {
+    const uint64_t found = __ballot(first >= 0);
+    if (found) {
+      pick = __builtin_amdgcn_readlane(first, __ffsll(static_cast<long long>(found)) - 1);
+    } else {
+      const uint64_t any = __ballot(lastw >= 0);
+      pick = any ? __builtin_amdgcn_readlane(lastw, 63 - __clzll(static_cast<long long>(any))) : 0;
+    }
+  }
   const int y = static_cast<int>(static_cast<int64_t>(tile) * kTile + pick);
 
-  if (tid == 0) {
+  if (lane == 0) {
     int32_t* out = a.out_tok + static_cast<int64_t>(b) * ustride;
     int cnt = 0;
     bool stop = false;
     for (int i = 0; i < pr.m && !stop; ++i) {
-      const int32_t tok = a.ids[static_cast<int64_t>(b) * a.k_max + i];
+      const int32_t tok = ids[i];
       out[cnt++] = tok;
       if (a.eos >= 0 && tok == a.eos) stop = true;
     }
@@ -310,72 +361,179 @@ __device__ void draw_and_emit(const SampleArgs& a, int b, const Pre& pr, const d
 
 }  // namespace
 
+// Sums (r, p, q) of one 4096-element tile, computed by one wave: lane l takes
+// the 16-byte vectors l, l + 64, l + 128, ... of the tile (coalesced), loads a
+// batch of them as raw words and unpacks while folding; the result is valid in
+// every lane of the wave.  Rows that are not 16-byte aligned, and the row's
+// last partial tile, take element loads.
+template <class D>
+__device__ __forceinline__ uint4 ld16(const void* row, int64_t e) {
+  return *reinterpret_cast<const uint4*>(static_cast<const char*>(row) + e * D::kSize);
+}
+
+template <class DT, class DQ>
+__device__ __forceinline__ void wave_tile_sums(const SampleArgs& a, const void* trow, const void* qrow,
+                                               const Pre& pr, int t, double* v) {
+  // elements per run: the wider of the two vector widths, so each row's share
+  // of a run is a whole number of 16-byte vectors
+  constexpr int kPer = DT::kPerVec > DQ::kPerVec ? DT::kPerVec : DQ::kPerVec;
+  constexpr int kRuns = kTile / (kWave * kPer);                               // runs per lane
+  constexpr int kBatch = kRuns < 4 ? kRuns : 4;
+  const int lane = threadIdx.x & (kWave - 1);
+  const bool resid = pr.m < pr.k;
+  const int64_t t0 = static_cast<int64_t>(t) * kTile;
+  const bool fast = t0 + kTile <= a.V &&
+                    ((reinterpret_cast<uintptr_t>(trow) + t0 * DT::kSize) & 15u) == 0 &&
+                    (!resid || ((reinterpret_cast<uintptr_t>(qrow) + t0 * DQ::kSize) & 15u) == 0);
+  float rs = 0.f, ps = 0.f, qs = 0.f;
+  constexpr int nt = kPer * DT::kSize / 16, nq = kPer * DQ::kSize / 16;
+  static_assert(nt >= 1 && nq >= 1, "a run must cover whole vectors of both rows");
+  if (fast) {
+#pragma unroll
+    for (int r0 = 0; r0 < kRuns; r0 += kBatch) {
+      uint4 tw[kBatch][nt];
+      uint4 qw[kBatch][nq];
+#pragma unroll
+      for (int r = 0; r < kBatch; ++r) {
+        const int64_t e = t0 + static_cast<int64_t>((r0 + r) * kWave + lane) * kPer;
+#pragma unroll
+        for (int j = 0; j < nt; ++j) tw[r][j] = ld16<DT>(trow, e + j * DT::kPerVec);
+        if (resid) {
+#pragma unroll
+          for (int j = 0; j < nq; ++j) qw[r][j] = ld16<DQ>(qrow, e + j * DQ::kPerVec);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kBatch; ++r) {
+        float l[kPer], q[kPer], w[kPer], p[kPer];
+#pragma unroll
+        for (int j = 0; j < nt; ++j) DT::unpack(tw[r][j], l + j * DT::kPerVec);
+        if (resid) {
+#pragma unroll
+          for (int j = 0; j < nq; ++j) DQ::unpack(qw[r][j], q + j * DQ::kPerVec);
+        } else {
+#pragma unroll
+          for (int j = 0; j < kPer; ++j) q[j] = 0.f;
+        }
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          p[j] = ex2(fmaf(l[j], a.c, -pr.Mc)) * pr.invS;
+          w[j] = resid ? fmaxf(p[j] - q[j], 0.f) : p[j];
+        }
+        rs += pairwise<kPer>(w);
+        ps += pairwise<kPer>(p);
+        qs += pairwise<kPer>(q);
+      }
+    }
+  } else {
+    // unaligned rows or the partial last tile: element loads, one run at a time
+#pragma unroll 1
+    for (int r = 0; r < kRuns; ++r) {
+      const int64_t e = t0 + static_cast<int64_t>(r * kWave + lane) * kPer;
+#pragma unroll 1
+      for (int j = 0; j < kPer; ++j) {
+        const bool in = e + j < a.V;
+        const float l = in ? DT::at(trow, e + j) : -INFINITY;
+        const float q = (in && resid) ? DQ::at(qrow, e + j) : 0.f;
+        const float p = ex2(fmaf(l, a.c, -pr.Mc)) * pr.invS;
+        rs += resid ? fmaxf(p - q, 0.f) : p;
+        ps += p;
+        qs += q;
+      }
+    }
+  }
+  v[0] = wave_total(static_cast<double>(rs));
+  v[1] = wave_total(static_cast<double>(ps));
+  v[2] = wave_total(static_cast<double>(qs));
+}
+
 template <class DT, class DQ>
 __global__ __launch_bounds__(kBlock) void k_sample_tiles(SampleArgs a) {
+  constexpr int kTilesPerBlock = kBlock / kWave;
   __shared__ SampleShared sh;
-  __shared__ double s_tile[3];
-  const int b = blockIdx.x / a.ntiles;
-  const int t = blockIdx.x - b * a.ntiles;
-  const Pre pr = preamble<DT, DQ>(a, b, t == 0, sh);
+  const int bpr = (a.ntiles + kTilesPerBlock - 1) / kTilesPerBlock;  // blocks per request
+  const int b = blockIdx.x / bpr;
+  const int g = blockIdx.x - b * bpr;
+  const Pre pr = preamble<DT, DQ>(a, b, g == 0, sh);
   if (pr.bits & kInvalid) {
-    if (a.ntiles == 1) {
-      write_invalid(a, b, pr.bits);
-    } else if (t == 0 && threadIdx.x == 0) {
-      a.records[b] = make_int4(pr.bits, 0, 0, 0);
-    }
+    if (g == 0 && threadIdx.x == 0) a.records[b] = make_int4(pr.bits, 0, 0, 0);
     return;
   }
+  if (g == 0 && threadIdx.x == 0)
+    a.records[b] = make_int4(pr.bits, pr.m, __float_as_int(pr.Mc), __float_as_int(pr.invS));
+  const int t = g * kTilesPerBlock + threadIdx.x / kWave;
+  if (t >= a.ntiles) return;
   const void* trow = row_ptr<DT>(a.tgt, pr.ts + pr.m, a.V);
   const void* qrow = pr.m < pr.k ? row_ptr<DQ>(a.dq, pr.qs + pr.m, a.V) : nullptr;
   double v[3];
-  tile_sums<DT, DQ>(a, trow, qrow, pr, t, v, sh.red);
-  if (a.ntiles == 1) {
-    if (threadIdx.x == 0) {
-      s_tile[0] = v[0];
-      s_tile[1] = v[1];
-      s_tile[2] = v[2];
-    }
-    __syncthreads();
-    draw_and_emit<DT, DQ>(a, b, pr, s_tile, sh);
-    return;
-  }
-  if (threadIdx.x == 0) {
+  wave_tile_sums<DT, DQ>(a, trow, qrow, pr, t, v);
+  if ((threadIdx.x & (kWave - 1)) == 0) {
     double* T = a.tiles + (static_cast<int64_t>(b) * a.ntiles + t) * 3;
     T[0] = v[0];
     T[1] = v[1];
     T[2] = v[2];
-    if (t == 0)
-      a.records[b] = make_int4(pr.bits, pr.m, __float_as_int(pr.Mc), __float_as_int(pr.invS));
   }
 }
 
+// Vocabularies of one tile: one block per request runs the preamble, then its
+// first wave sums the tile and draws.
 template <class DT, class DQ>
-__global__ __launch_bounds__(kBlock) void k_sample_draw(SampleArgs a) {
+__global__ __launch_bounds__(kBlock) void k_sample_single(SampleArgs a) {
   __shared__ SampleShared sh;
+  __shared__ double s_tile[3];
   const int b = blockIdx.x;
+  const Pre pr = preamble<DT, DQ>(a, b, true, sh);
+  if (pr.bits & kInvalid) {
+    write_invalid(a, b, pr.bits);
+    return;
+  }
+  if (threadIdx.x >= kWave) return;
+  const void* trow = row_ptr<DT>(a.tgt, pr.ts + pr.m, a.V);
+  const void* qrow = pr.m < pr.k ? row_ptr<DQ>(a.dq, pr.qs + pr.m, a.V) : nullptr;
+  double v[3];
+  wave_tile_sums<DT, DQ>(a, trow, qrow, pr, 0, v);
+  if (threadIdx.x == 0) {
+    s_tile[0] = v[0];
+    s_tile[1] = v[1];
+    s_tile[2] = v[2];
+  }
+  wave_draw_emit<DT, DQ>(a, b, pr, s_tile, sh.ids, sh.ufinal);
+}
+
+template <class DT, class DQ>
+__global__ __launch_bounds__(kWave) void k_sample_draw(SampleArgs a) {
+  __shared__ int32_t s_ids[kMaxChainRows];
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x;
   const int4 rec = a.records[b];
+  Pre pr{};
+  pr.k = a.dlen[b];
+  pr.ts = a.t_rs[b];
+  pr.qs = a.q_rs[b];
   if (rec.x & kInvalid) {
     write_invalid(a, b, rec.x);
     return;
   }
-  Pre pr{};
   pr.bits = rec.x;
   pr.m = rec.y;
   pr.Mc = __int_as_float(rec.z);
   pr.invS = __int_as_float(rec.w);
-  pr.k = a.dlen[b];
-  pr.ts = a.t_rs[b];
-  pr.qs = a.q_rs[b];
-  draw_and_emit<DT, DQ>(a, b, pr, a.tiles + static_cast<int64_t>(b) * a.ntiles * 3, sh);
+  for (int i = lane; i < pr.m; i += kWave) s_ids[i] = a.ids[static_cast<int64_t>(b) * a.k_max + i];
+  const float uf = a.u[static_cast<int64_t>(b) * (a.k_max + 1) + pr.k];
+  __syncthreads();
+  wave_draw_emit<DT, DQ>(a, b, pr, a.tiles + static_cast<int64_t>(b) * a.ntiles * 3, s_ids, uf);
 }
 
 template <class DT, class DQ>
 static hipError_t launch_pair(const SampleArgs& a, hipStream_t stream) {
   const dim3 block(kBlock);
-  hipLaunchKernelGGL((k_sample_tiles<DT, DQ>),
-                     dim3(static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.ntiles)), block, 0, stream, a);
-  if (a.ntiles > 1)
-    hipLaunchKernelGGL((k_sample_draw<DT, DQ>), dim3(static_cast<uint32_t>(a.B)), block, 0, stream, a);
+  if (a.ntiles == 1) {
+    hipLaunchKernelGGL((k_sample_single<DT, DQ>), dim3(static_cast<uint32_t>(a.B)), block, 0, stream, a);
+    return hipGetLastError();
+  }
+  const int64_t bpr = (a.ntiles + (kBlock / kWave) - 1) / (kBlock / kWave);
+  hipLaunchKernelGGL((k_sample_tiles<DT, DQ>), dim3(static_cast<uint32_t>(a.B * bpr)), block, 0, stream, a);
+  hipLaunchKernelGGL((k_sample_draw<DT, DQ>), dim3(static_cast<uint32_t>(a.B)), dim3(kWave), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -8,43 +8,61 @@
 // pairs of a row.  The pair is kept in the scaled domain: m = max(l) * log2(e) / T
 // (rounded once), s = sum 2^(l * log2(e) / T - m).
 //
-// Layout: grid = rows * nseg blocks of 256 threads; block (row, seg) streams
-// the seg-th slice of the row's 16-byte-aligned body with coalesced 16-byte
-// loads, U vectors in flight per thread; segment 0 also takes the unaligned
-// head elements and the last segment the tail.
+// Layout: grid = rows * nseg blocks of 256 threads, nseg = ceil(V / 8192);
+// block (row, seg) reads the seg-th 8192-element chunk of the row's
+// 16-byte-aligned body with coalesced 16-byte non-temporal loads, all of a
+// thread's loads in flight at once; segment 0 also takes the unaligned head
+// elements and the last segment the tail.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace sv {
 
-template <class D, int U>
+// One 8192-element chunk per block: every thread issues its U 16-byte loads
+// at once (lanes past the row's end read nothing and fold -inf), so each
+// block has its whole chunk in flight; NT selects non-temporal loads.
+template <class D, bool NT>
 __global__ __launch_bounds__(kBlock) void k_row_stats(const void* __restrict__ rows, int64_t V,
                                                       int32_t nseg, float c,
                                                       float2* __restrict__ partial) {
+  constexpr int U = kSegElems / (kBlock * D::kPerVec);
+  constexpr int kSegVecs = kSegElems / D::kPerVec;
   __shared__ float sh[2 * (kBlock / kWave)];
   const int64_t row = blockIdx.x / nseg;
   const int32_t seg = blockIdx.x - static_cast<int32_t>(row) * nseg;
   const void* base = row_ptr<D>(rows, row, V);
   const int64_t head = head_elems<D>(base, V);
   const int64_t nvec = (V - head) / D::kPerVec;
-  const int64_t v0 = nvec * seg / nseg, v1 = nvec * (seg + 1) / nseg;
   const uint4* vp = reinterpret_cast<const uint4*>(static_cast<const char*>(base) + head * D::kSize);
 
   MS acc{-INFINITY, 0.f};
-  int64_t v = v0 + threadIdx.x;
-  for (; v + (U - 1) * kBlock < v1; v += U * kBlock) {
+  {
+    const int64_t v0 = static_cast<int64_t>(seg) * kSegVecs + threadIdx.x;
     uint4 w[U];
 #pragma unroll
-    for (int j = 0; j < U; ++j) w[j] = vp[v + j * kBlock];
+    for (int j = 0; j < U; ++j) {
+      const int64_t v = v0 + j * kBlock;
+      w[j] = uint4{0u, 0u, 0u, 0u};
+      if (v < nvec) {
+        if (NT) {
+          const uint32_t* q = reinterpret_cast<const uint32_t*>(vp + v);
+          w[j] = uint4{__builtin_nontemporal_load(q), __builtin_nontemporal_load(q + 1),
+                       __builtin_nontemporal_load(q + 2), __builtin_nontemporal_load(q + 3)};
+        } else {
+          w[j] = vp[v];
+        }
+      }
+    }
     float x[U * D::kPerVec];
 #pragma unroll
-    for (int j = 0; j < U; ++j) D::unpack(w[j], x + j * D::kPerVec);
+    for (int j = 0; j < U; ++j) {
+      D::unpack(w[j], x + j * D::kPerVec);
+      if (v0 + j * kBlock >= nvec) {
+#pragma unroll
+        for (int t = 0; t < D::kPerVec; ++t) x[j * D::kPerVec + t] = -INFINITY;
+      }
+    }
     ms_fold<U * D::kPerVec>(acc, x, c);
-  }
-  for (; v < v1; v += kBlock) {
-    float x[D::kPerVec];
-    D::unpack(vp[v], x);
-    ms_fold<D::kPerVec>(acc, x, c);
   }
   if (seg == 0) {
     for (int64_t i = threadIdx.x; i < head; i += kBlock) {
@@ -58,17 +76,28 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(const void* __restrict__ r
       ms_fold<1>(acc, &x, c);
     }
   }
-  const MS r = block_ms(acc, sh);
-  if (threadIdx.x == 0) partial[blockIdx.x] = make_float2(r.m, r.s);
+  // block reduction: DPP within each wave, then the four wave results
+  const MS r = wave_ms_dpp(acc);
+  const int wid = threadIdx.x / kWave;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    sh[2 * wid] = r.m;
+    sh[2 * wid + 1] = r.s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    MS t{sh[0], sh[1]};
+    for (int w = 1; w < kBlock / kWave; ++w) t = ms_combine(t, MS{sh[2 * w], sh[2 * w + 1]});
+    partial[blockIdx.x] = make_float2(t.m, t.s);
+  }
 }
 
 hipError_t launch_row_stats(int dtype, const void* rows, int64_t n_rows, int64_t V, int32_t nseg,
                             float c, float2* partial, hipStream_t stream) {
   const dim3 grid(static_cast<uint32_t>(n_rows * nseg)), block(kBlock);
   if (dtype == kDtypeBF16)
-    hipLaunchKernelGGL((k_row_stats<BF16, 4>), grid, block, 0, stream, rows, V, nseg, c, partial);
+    hipLaunchKernelGGL((k_row_stats<BF16, true>), grid, block, 0, stream, rows, V, nseg, c, partial);
   else
-    hipLaunchKernelGGL((k_row_stats<F32, 4>), grid, block, 0, stream, rows, V, nseg, c, partial);
+    hipLaunchKernelGGL((k_row_stats<F32, true>), grid, block, 0, stream, rows, V, nseg, c, partial);
   return hipGetLastError();
 }
 

@@ -15,9 +15,19 @@ constexpr int kMaxTreeTiles = 256;     // tree vocab <= 256 * 4096
 constexpr int kMaxWindow = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Segments per row for the streaming statistics kernels: about 32 Ki elements
-// per block, and at least ~1024 blocks in total when rows are few.
-inline int32_t row_segments(int64_t rows, int64_t V) {
+// Segments per row of the softmax-statistics kernel: one 8192-element chunk
+// per block (for any row alignment the 16-byte-aligned body of a row needs at
+// most this many chunks; the unaligned head and tail ride on the first and
+// last segment).
+constexpr int64_t kSegElems = 8192;
+inline int32_t row_segments(int64_t /*rows*/, int64_t V) {
+  const int64_t n = (V + kSegElems - 1) / kSegElems;
+  return static_cast<int32_t>(n < 1 ? 1 : n);
+}
+
+// Segments per row of the argmax kernel: about 32 Ki elements per block, and at
+// least ~1024 blocks in total when rows are few.
+inline int32_t argmax_segments(int64_t rows, int64_t V) {
   int64_t nseg = (V + 32767) / 32768;
   if (rows > 0 && rows * nseg < 1024) {
     const int64_t want = (1024 + rows - 1) / rows;
