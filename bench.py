@@ -117,6 +117,11 @@ def main():
     ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch every step eagerly instead of replaying captured HIP graphs")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run plain 256 MiB device-to-device copies (a counter calibration "
+                         "reference for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
@@ -130,6 +135,13 @@ def main():
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     sv.load()
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     with open(STATS_SRC, "rb") as f:
         src_hash = hashlib.sha1(f.read()).hexdigest()
 
@@ -169,10 +181,29 @@ def main():
                torch.empty((B,), dtype=torch.int32, device=dev), None, None)
         ws = sv.Workspace(dev)
 
-        def step(i):
+        def eager(i):
             d = dsets[i % len(dsets)]
             sv.sv_verify_sample(d["tgt"], d["dft"], d["trs"], d["qrs"], d["ids"], d["dl"], ci0.T, d["u"],
                                 workspace=ws, out=out)
+
+        step = eager
+        if not args.no_graph:
+            # one captured graph per input set: the step's kernels, replayed
+            # without per-launch host work
+            graphs = []
+            side = torch.cuda.Stream()
+            for j in range(len(dsets)):
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    eager(j)
+                torch.cuda.current_stream().wait_stream(side)
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    eager(j)
+                graphs.append(g)
+
+            def step(i):
+                graphs[i % len(graphs)].replay()
 
         log(f"timing {args.steps} steps")
         wall, ev_ms = timed(step, args.steps, args.warmup, torch)
@@ -193,6 +224,7 @@ def main():
         st_avg = float(np.mean(st_ms)) * 1e-3
         achieved = rows_bytes / st_avg / 1e9
         fb = chain_formula_bytes(ci0)
+        cfg["launch"] = "eager" if args.no_graph else "hip graph per step"
         result.update(
             value=round(B / (ms * 1e-3), 1), unit="rounds/s", ms_per_step=round(ms, 5), config=cfg,
             tokens_per_s=round(float(cnt0.sum()) / (ms * 1e-3), 1),

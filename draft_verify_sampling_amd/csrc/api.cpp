@@ -184,7 +184,7 @@ sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t
       (q_rows > 0 && draft_probs == nullptr))
     return fail(SV_E_ARG, "null pointer argument");
   const int32_t nseg = sv::row_segments(t_rows, vocab);
-  const int64_t ntiles = sv::tiles_of(vocab);
+  const int64_t ntiles = sv::sample_tiles(vocab);
   if (static_cast<int64_t>(t_rows) * nseg > kMaxGrid || static_cast<int64_t>(batch) * ntiles > kMaxGrid)
     return fail(SV_E_ARG, "problem too large for one launch");
   const sv::SampleLayout L = sv::sample_layout(batch, t_rows, vocab);

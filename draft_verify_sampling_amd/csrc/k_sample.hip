@@ -14,7 +14,7 @@
 //   is resident at once.  Every block repeats the request's small preamble
 //   (row normalisers from the partials, p and q at the drafted tokens, the
 //   accept scan), so all of a request's blocks agree on the break position m.
-//   Then each of the block's four waves reads one 4096-element tile of target
+//   Then each of the block's four waves reads one 2048-element tile of target
 //   row m (and of draft row m when m < k), all of its loads in flight at once,
 //   and writes the float64 sums of the draw weights r, of p and of q for that
 //   tile.  Block 0 of a request also writes the request's record (status bits,
@@ -57,39 +57,45 @@ struct SampleShared {
 
 constexpr int kInvalid = kFlagBadRequest | kFlagBadToken | kFlagNonfinite;
 
-// The request's preamble; identical in every block that runs it.
+// The request's preamble; identical in every block that runs it.  Two rounds
+// of loads: (1) the request's row starts, draft count, drafted tokens and
+// uniforms; (2) its rows' softmax partials and the target/draft values at the
+// drafted tokens.
 template <class DT, class DQ>
 __device__ Pre preamble(const SampleArgs& a, int b, bool write_diag, SampleShared& sh) {
   const int tid = threadIdx.x;
   const int ustride = a.k_max + 1;
   Pre r{};
+  // round 1
   r.k = a.dlen[b];
   r.ts = a.t_rs[b];
   r.qs = a.q_rs[b];
+  const int x = tid < a.k_max ? a.ids[static_cast<int64_t>(b) * a.k_max + tid] : 0;
+  const float uu = tid <= a.k_max ? a.u[static_cast<int64_t>(b) * ustride + tid] : 0.f;
   const int k = r.k;
   if (k < 0 || k > a.k_max || r.ts < 0 || static_cast<int64_t>(r.ts) + k >= a.t_rows ||
       (k > 0 && (r.qs < 0 || static_cast<int64_t>(r.qs) + k > a.q_rows))) {
     r.bits = kFlagBadRequest;
     return r;
   }
-  if (tid == 0) {
-    sh.i[0] = k;
-    sh.i[1] = 0;
-  }
+  const bool xin = tid < k && x >= 0 && x < a.V;
+  // round 2
   const int np = (k + 1) * a.nseg;
   const bool lds_parts = np <= kMaxPartialsInLds;
   if (lds_parts) {
     const float2* src = a.partial + static_cast<int64_t>(r.ts) * a.nseg;
     for (int i = tid; i < np; i += kBlock) sh.part[i] = src[i];
   }
-  __syncthreads();
-  int x = 0;
-  if (tid < k) {
-    x = a.ids[static_cast<int64_t>(b) * a.k_max + tid];
-    sh.ids[tid] = x;
-    if (x < 0 || x >= a.V) atomicOr(&sh.i[1], kFlagBadToken);
+  const float lx = xin ? DT::at(row_ptr<DT>(a.tgt, r.ts + tid, a.V), x) : 0.f;
+  const float qx = xin ? DQ::at(row_ptr<DQ>(a.dq, r.qs + tid, a.V), x) : 0.f;
+  if (tid == 0) {
+    sh.i[0] = k;
+    sh.i[1] = 0;
   }
-  if (tid == kBlock - 1) sh.ufinal = a.u[static_cast<int64_t>(b) * ustride + k];
+  if (tid < k) sh.ids[tid] = x;
+  if (tid == k) sh.ufinal = uu;
+  __syncthreads();
+  if (tid < k && !xin) atomicOr(&sh.i[1], kFlagBadToken);
   if (tid <= k) {
     const float2* pp = lds_parts ? sh.part + tid * a.nseg
                                  : a.partial + static_cast<int64_t>(r.ts + tid) * a.nseg;
@@ -109,13 +115,10 @@ __device__ Pre preamble(const SampleArgs& a, int b, bool write_diag, SampleShare
     return r;
   }
   if (tid < k) {
-    const float l = DT::at(row_ptr<DT>(a.tgt, r.ts + tid, a.V), x);
-    const float p = ex2(fmaf(l, a.c, -sh.m[tid])) * (1.f / sh.S[tid]);
-    const float q = DQ::at(row_ptr<DQ>(a.dq, r.qs + tid, a.V), x);
+    const float p = ex2(fmaf(lx, a.c, -sh.m[tid])) * (1.f / sh.S[tid]);
     sh.p[tid] = p;
-    sh.q[tid] = q;
-    const float uu = a.u[static_cast<int64_t>(b) * ustride + tid];
-    if (!(uu * q < p)) atomicMin(&sh.i[0], tid);
+    sh.q[tid] = qx;
+    if (!(uu * qx < p)) atomicMin(&sh.i[0], tid);
   }
   __syncthreads();
   r.m = sh.i[0];
@@ -143,27 +146,6 @@ __device__ void write_invalid(const SampleArgs& a, int b, int bits) {
   }
 }
 
-// Draw weights of the 16 elements this thread owns starting at e: residual
-// max(0, p - q) (resid) or p itself, and p and q.
-template <class DT, class DQ>
-__device__ __forceinline__ void draw_weights(const void* trow, const void* qrow, int64_t V, int64_t e,
-                                             float c, float Mc, float invS, bool resid, float* w,
-                                             float* p, float* q) {
-  float l[kPerThreadTile];
-  load_run<DT, kPerThreadTile>(trow, V, e, l, -INFINITY);
-  if (resid) {
-    load_run<DQ, kPerThreadTile>(qrow, V, e, q, 0.f);
-  } else {
-#pragma unroll
-    for (int j = 0; j < kPerThreadTile; ++j) q[j] = 0.f;
-  }
-#pragma unroll
-  for (int j = 0; j < kPerThreadTile; ++j) {
-    p[j] = ex2(fmaf(l[j], c, -Mc)) * invS;
-    w[j] = resid ? fmaxf(p[j] - q[j], 0.f) : p[j];
-  }
-}
-
 template <int n>
 __device__ __forceinline__ float pairwise(const float* x) {
   float t[n];
@@ -185,7 +167,7 @@ __device__ __forceinline__ double wave_exclusive_from_inclusive(double incl) {
 // Draw the last token from the tile sums T[ntiles][3] and write the outputs.
 // Run by exactly one wave (64 lanes); ids[0..m) and ufinal are the request's
 // drafted tokens and final uniform.  Lane l owns the contiguous tiles
-// [l * tpl, (l + 1) * tpl), then the contiguous 64 elements [64 l, 64 l + 64)
+// [l * tpl, (l + 1) * tpl), then the contiguous 32 elements [32 l, 32 l + 32)
 // of the chosen tile; crossings are located with wave scans and ballots.
 template <class DT, class DQ>
 __device__ void wave_draw_emit(const SampleArgs& a, int b, const Pre& pr, const double* T,
@@ -255,15 +237,16 @@ __device__ void wave_draw_emit(const SampleArgs& a, int b, const Pre& pr, const 
     }
   }
 
-  // the id: rescan the tile; lane l owns its elements [64 l, 64 l + 64), read
-  // in one round (raw 16-byte vectors when aligned) and walked twice from
-  // registers: once for the lane's sum, once for the crossing.
+  // the id: rescan the tile; lane l owns its kLane contiguous elements, read
+  // in one round (raw 16-byte vectors when aligned); lane-local sums in fp32,
+  // sums across lanes in fp64.
+  constexpr int kLane = kSampleTile / kWave;  // 32
   const void* trow = row_ptr<DT>(a.tgt, pr.ts + pr.m, a.V);
   const void* qrow = resid ? row_ptr<DQ>(a.dq, pr.qs + pr.m, a.V) : nullptr;
-  const int64_t e0 = static_cast<int64_t>(tile) * kTile + lane * 64;
-  constexpr int kTV = 64 / DT::kPerVec, kQV = 64 / DQ::kPerVec;
+  const int64_t e0 = static_cast<int64_t>(tile) * kSampleTile + lane * kLane;
+  constexpr int kTV = kLane / DT::kPerVec, kQV = kLane / DQ::kPerVec;
   uint4 tv[kTV], qv[kQV];
-  const bool fast = e0 + 64 <= a.V &&
+  const bool fast = e0 + kLane <= a.V &&
                     ((reinterpret_cast<uintptr_t>(trow) + e0 * DT::kSize) & 15u) == 0 &&
                     (!resid || ((reinterpret_cast<uintptr_t>(qrow) + e0 * DQ::kSize) & 15u) == 0);
   if (fast) {
@@ -276,10 +259,10 @@ __device__ void wave_draw_emit(const SampleArgs& a, int b, const Pre& pr, const 
         qv[j] = *reinterpret_cast<const uint4*>(static_cast<const char*>(qrow) + (e0 + j * DQ::kPerVec) * DQ::kSize);
     }
   }
-  // the lane's 64 draw weights, in groups of 8 elements
-  float wv[64];
+  // the lane's draw weights, in groups of 8 elements
+  float wv[kLane];
 #pragma unroll
-  for (int g = 0; g < 8; ++g) {
+  for (int g = 0; g < kLane / 8; ++g) {
     float l[8], q[8];
     if (fast) {
       if (DT::kPerVec == 8) {
@@ -311,19 +294,19 @@ __device__ void wave_draw_emit(const SampleArgs& a, int b, const Pre& pr, const 
       wv[8 * g + j] = (which || !resid) ? p : fmaxf(p - (resid ? q[j] : 0.f), 0.f);
     }
   }
-  double lsum = 0.0;
-#pragma unroll
-  for (int i = 0; i < 64; ++i) lsum += static_cast<double>(wv[i]);
-  double erun = tile_base + wave_exclusive_from_inclusive(wave_incl_scan(lsum));
+  const double lane_base = tile_base + wave_exclusive_from_inclusive(
+                                           wave_incl_scan(static_cast<double>(pairwise<kLane>(wv))));
+  const float thr = static_cast<float>(target - lane_base);  // crossing: running weight > thr
   int first = -1, lastw = -1;
+  float lrun = 0.f;
 #pragma unroll
-  for (int i = 0; i < 64; ++i) {
+  for (int i = 0; i < kLane; ++i) {
     const float wj = wv[i];
     if (wj > 0.f) {
-      if (first < 0 && !overshoot && erun + wj > target) first = lane * 64 + i;
-      lastw = lane * 64 + i;
+      if (first < 0 && !overshoot && lrun + wj > thr) first = lane * kLane + i;
+      lastw = lane * kLane + i;
     }
-    erun += static_cast<double>(wj);
+    lrun += wj;
   }
   int pick;
   {
@@ -335,7 +318,7 @@ __device__ void wave_draw_emit(const SampleArgs& a, int b, const Pre& pr, const 
       pick = any ? __builtin_amdgcn_readlane(lastw, 63 - __clzll(static_cast<long long>(any))) : 0;
     }
   }
-  const int y = static_cast<int>(static_cast<int64_t>(tile) * kTile + pick);
+  const int y = static_cast<int>(static_cast<int64_t>(tile) * kSampleTile + pick);
 
   if (lane == 0) {
     int32_t* out = a.out_tok + static_cast<int64_t>(b) * ustride;
@@ -361,7 +344,7 @@ __device__ void wave_draw_emit(const SampleArgs& a, int b, const Pre& pr, const 
 
 }  // namespace
 
-// Sums (r, p, q) of one 4096-element tile, computed by one wave: lane l takes
+// Sums (r, p, q) of one 2048-element tile, computed by one wave: lane l takes
 // the 16-byte vectors l, l + 64, l + 128, ... of the tile (coalesced), loads a
 // batch of them as raw words and unpacks while folding; the result is valid in
 // every lane of the wave.  Rows that are not 16-byte aligned, and the row's
@@ -377,12 +360,12 @@ __device__ __forceinline__ void wave_tile_sums(const SampleArgs& a, const void* 
   // elements per run: the wider of the two vector widths, so each row's share
   // of a run is a whole number of 16-byte vectors
   constexpr int kPer = DT::kPerVec > DQ::kPerVec ? DT::kPerVec : DQ::kPerVec;
-  constexpr int kRuns = kTile / (kWave * kPer);                               // runs per lane
+  constexpr int kRuns = kSampleTile / (kWave * kPer);                         // runs per lane
   constexpr int kBatch = kRuns < 4 ? kRuns : 4;
   const int lane = threadIdx.x & (kWave - 1);
   const bool resid = pr.m < pr.k;
-  const int64_t t0 = static_cast<int64_t>(t) * kTile;
-  const bool fast = t0 + kTile <= a.V &&
+  const int64_t t0 = static_cast<int64_t>(t) * kSampleTile;
+  const bool fast = t0 + kSampleTile <= a.V &&
                     ((reinterpret_cast<uintptr_t>(trow) + t0 * DT::kSize) & 15u) == 0 &&
                     (!resid || ((reinterpret_cast<uintptr_t>(qrow) + t0 * DQ::kSize) & 15u) == 0);
   float rs = 0.f, ps = 0.f, qs = 0.f;
@@ -503,13 +486,18 @@ __global__ __launch_bounds__(kBlock) void k_sample_single(SampleArgs a) {
 template <class DT, class DQ>
 __global__ __launch_bounds__(kWave) void k_sample_draw(SampleArgs a) {
   __shared__ int32_t s_ids[kMaxChainRows];
+  __shared__ float s_u[kMaxChainRows];
   const int b = blockIdx.x;
   const int lane = threadIdx.x;
+  // one round of loads: the record, the request's metadata, its drafted
+  // tokens and uniforms (the tile sums follow inside the draw)
   const int4 rec = a.records[b];
   Pre pr{};
   pr.k = a.dlen[b];
   pr.ts = a.t_rs[b];
   pr.qs = a.q_rs[b];
+  for (int i = lane; i < a.k_max; i += kWave) s_ids[i] = a.ids[static_cast<int64_t>(b) * a.k_max + i];
+  for (int i = lane; i <= a.k_max; i += kWave) s_u[i] = a.u[static_cast<int64_t>(b) * (a.k_max + 1) + i];
   if (rec.x & kInvalid) {
     write_invalid(a, b, rec.x);
     return;
@@ -518,10 +506,8 @@ __global__ __launch_bounds__(kWave) void k_sample_draw(SampleArgs a) {
   pr.m = rec.y;
   pr.Mc = __int_as_float(rec.z);
   pr.invS = __int_as_float(rec.w);
-  for (int i = lane; i < pr.m; i += kWave) s_ids[i] = a.ids[static_cast<int64_t>(b) * a.k_max + i];
-  const float uf = a.u[static_cast<int64_t>(b) * (a.k_max + 1) + pr.k];
   __syncthreads();
-  wave_draw_emit<DT, DQ>(a, b, pr, a.tiles + static_cast<int64_t>(b) * a.ntiles * 3, s_ids, uf);
+  wave_draw_emit<DT, DQ>(a, b, pr, a.tiles + static_cast<int64_t>(b) * a.ntiles * 3, s_ids, s_u[pr.k]);
 }
 
 template <class DT, class DQ>

@@ -39,7 +39,11 @@ inline int32_t argmax_segments(int64_t rows, int64_t V) {
   return static_cast<int32_t>(nseg);
 }
 
-inline int64_t tiles_of(int64_t V) { return (V + 4095) / 4096; }
+inline int64_t tiles_of(int64_t V) { return (V + 4095) / 4096; }   // tree passes
+
+// The sampled verify's inverse-CDF unit: one wave sums one tile.
+constexpr int kSampleTile = 2048;
+inline int64_t sample_tiles(int64_t V) { return (V + kSampleTile - 1) / kSampleTile; }
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
@@ -52,7 +56,7 @@ inline SampleLayout sample_layout(int64_t B, int64_t t_rows, int64_t V) {
   const int64_t nseg = row_segments(t_rows, V);
   L.partial_off = 0;
   L.tiles_off = align256(static_cast<size_t>(t_rows * nseg) * 8);
-  L.records_off = L.tiles_off + align256(static_cast<size_t>(B * tiles_of(V)) * 3 * 8);
+  L.records_off = L.tiles_off + align256(static_cast<size_t>(B * sample_tiles(V)) * 3 * 8);
   L.bytes = L.records_off + align256(static_cast<size_t>(B) * 16);
   return L;
 }

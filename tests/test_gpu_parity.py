@@ -416,3 +416,40 @@ def test_gpu_softmax_partials(kind, V, T):
         _, M, S = oracle.softmax_T(oracle.widen(stored[r], kind), T)
         assert close(m * np.log(2.0), M, atol=1e-6), r
         assert close(s, S), r
+
+
+def test_gpu_graph_replay_matches_eager():
+    """The sampled verify allocates nothing, synchronises nothing and issues no
+    memset, so it can be captured in a HIP graph; every replay (with eager work
+    and synchronisations in between) must equal the eager result."""
+    say("graph capture and replay of sv_verify_sample")
+    import draft_verify_sampling_amd as sv
+    ci = synth.c3_sampled(B=16, k=4, V=20_000, T=0.8, salt=9)
+    other = synth.c3_sampled(B=16, k=4, V=20_000, T=0.8, salt=10)
+    args = [rows_to_dev(ci.target, "bf16"), rows_to_dev(ci.draft, "bf16"), i32(ci.t_row_start),
+            i32(ci.q_row_start), i32(ci.draft_ids), i32(ci.draft_len)]
+    u = f32(ci.uniforms)
+    eager = sv.sv_verify_sample(*args, ci.T, u)
+    torch.cuda.synchronize()
+    want = [t.clone() for t in eager[:3]]
+    ws = sv.Workspace()
+    out = (torch.empty_like(want[0]), torch.empty_like(want[1]), torch.empty_like(want[2]), None, None)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        sv.sv_verify_sample(*args, ci.T, u, workspace=ws, out=out)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        sv.sv_verify_sample(*args, ci.T, u, workspace=ws, out=out)
+    oargs = [rows_to_dev(other.target, "bf16"), rows_to_dev(other.draft, "bf16"),
+             i32(other.t_row_start), i32(other.q_row_start), i32(other.draft_ids), i32(other.draft_len)]
+    for rep in range(4):
+        for t in out[:3]:
+            t.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        for got, w in zip(out[:3], want):
+            assert torch.equal(got, w), rep
+        sv.sv_verify_sample(*oargs, other.T, f32(other.uniforms))   # eager work in between
+        torch.cuda.synchronize()
