@@ -68,22 +68,61 @@ def stats_traffic(step_kernel_src_hash):
 
 
 def timed(fn, steps, warmup, torch):
-    """W untimed calls, then K timed calls bracketed by synchronisations; also
-    records a HIP event pair around every timed call on the current stream.
-    Returns (wall seconds, list of per-call event milliseconds)."""
+    """W untimed calls, then exactly K timed calls bracketed by synchronisations
+    (host wall clock, and one HIP event pair on the current stream).  A second,
+    untimed-for-the-result pass records an event pair around every call for the
+    per-step distribution.  Returns (wall s, event ms over the K calls, per-call
+    event ms list)."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record()
     for i in range(steps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = e0.elapsed_time(e1)
+    n = min(steps, 200)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
         ev[i][0].record()
         fn(i)
         ev[i][1].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    return wall, [a.elapsed_time(b) for a, b in ev]
+    return wall, total_ms, [a.elapsed_time(b) for a, b in ev]
+
+
+def kernel_avg_us(launch, n_sets, steps, torch, per_graph=500):
+    """Average duration of one launch of a kernel: a graph of `per_graph`
+    back-to-back launches (rotating input sets) is replayed between a pair of
+    HIP events on the current stream, so host launch costs stay outside."""
+    graphs = []
+    side = torch.cuda.Stream()
+    for j in range(n_sets):
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for r in range(per_graph):
+                launch(j + r)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(per_graph):
+                launch(j + r)
+        graphs.append(g)
+    reps = max(1, steps // per_graph)
+    for i in range(3):
+        graphs[i % n_sets].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(reps):
+        graphs[i % n_sets].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return 1e3 * e0.elapsed_time(e1) / (reps * per_graph)
 
 
 def cpu_baseline_chain(ci, gpu_out, budget_s):
@@ -109,7 +148,46 @@ def cpu_baseline_chain(ci, gpu_out, budget_s):
                                              boundary=int((~same & near).sum()))
 
 
+def summarize_counters(fetch_db, write_db, out_json):
+    """Per-launch HBM traffic of the row-statistics kernel from two rocprofv3
+    --pmc databases (FETCH_SIZE and WRITE_SIZE passes of
+    `bench.py --calibrate-copy`), each counter scaled by what it reads for the
+    run's 256 MiB device-to-device copies; writes a JSON summary."""
+    import sqlite3
+
+    def per_kernel(db, counter):
+        cur = sqlite3.connect(db).cursor()
+        rows = cur.execute("select kernel_name, value from counters_collection where counter_name = ?",
+                           (counter,)).fetchall()
+        out = {}
+        for name, v in rows:
+            out.setdefault(name, []).append(float(v))
+        return out
+
+    ref_kib = 256 * 1024
+    res = {}
+    for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
+        k = per_kernel(db, counter)
+        copies = [v for name, vals in k.items() if "copyBuffer" in name for v in vals]
+        big = sorted(copies)[-8:]
+        scale = (sum(big) / len(big)) / ref_kib
+        stats = [vals for name, vals in k.items() if "k_row_stats" in name][0]
+        res[counter] = dict(raw_kib_per_launch=sum(stats) / len(stats), copy_reading_kib=sum(big) / len(big),
+                            copy_true_kib=ref_kib, scale=scale,
+                            bytes_per_launch=sum(stats) / len(stats) / scale * 1024)
+        res[counter + "_all_kernels_raw_kib"] = {n[:80]: sum(v) / len(v) for n, v in k.items()}
+    with open(STATS_SRC, "rb") as f:
+        res["kernel_source_sha1"] = hashlib.sha1(f.read()).hexdigest()
+    res["bytes_per_launch"] = int(res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"])
+    with open(out_json, "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps({k: res[k] for k in ("bytes_per_launch", "kernel_source_sha1")}))
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
+        summarize_counters(sys.argv[2], sys.argv[3], sys.argv[4])
+        return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
@@ -206,7 +284,7 @@ def main():
                 graphs[i % len(graphs)].replay()
 
         log(f"timing {args.steps} steps")
-        wall, ev_ms = timed(step, args.steps, args.warmup, torch)
+        wall, tot_ms, ev_ms = timed(step, args.steps, args.warmup, torch)
         # one more call on set 0 for the parity sample and token counts
         step(0)
         torch.cuda.synchronize()
@@ -220,8 +298,7 @@ def main():
         def stats(i):
             sv.sv_softmax_partials(dsets[i % len(dsets)]["tgt"], ci0.T, out=part)
 
-        _, st_ms = timed(stats, args.steps, args.warmup, torch)
-        st_avg = float(np.mean(st_ms)) * 1e-3
+        st_avg = kernel_avg_us(stats, len(dsets), args.steps, torch, per_graph=min(args.steps, 500)) * 1e-6
         achieved = rows_bytes / st_avg / 1e9
         fb = chain_formula_bytes(ci0)
         cfg["launch"] = "eager" if args.no_graph else "hip graph per step"
@@ -229,7 +306,8 @@ def main():
             value=round(B / (ms * 1e-3), 1), unit="rounds/s", ms_per_step=round(ms, 5), config=cfg,
             tokens_per_s=round(float(cnt0.sum()) / (ms * 1e-3), 1),
             mean_tokens_per_round=round(float(cnt0.mean()), 4),
-            event_ms_per_step=dict(mean=round(float(np.mean(ev_ms)), 5),
+            event_ms_per_step=dict(timed_region=round(tot_ms / args.steps, 5),
+                                   mean=round(float(np.mean(ev_ms)), 5),
                                    p10=round(float(np.percentile(ev_ms, 10)), 5),
                                    p50=round(float(np.percentile(ev_ms, 50)), 5),
                                    p90=round(float(np.percentile(ev_ms, 90)), 5)),
@@ -262,12 +340,11 @@ def main():
         def step(i):
             sv.sv_verify_tree(d["tgt"], d["dft"], d["par"], d["tok"], ti.T, d["u"], workspace=ws, out=out)
 
-        wall, ev_ms = timed(step, args.steps, args.warmup, torch)
+        wall, tot_ms, ev_ms = timed(step, args.steps, args.warmup, torch)
         ms = 1e3 * wall / args.steps
         part = torch.empty((B * N, sv.sv_softmax_segments(B * N, ti.V), 2), dtype=torch.float32, device=dev)
-        _, st_ms = timed(lambda i: sv.sv_softmax_partials(d["tgt"], ti.T, out=part), args.steps,
-                         args.warmup, torch)
-        st_avg = float(np.mean(st_ms)) * 1e-3
+        st_avg = kernel_avg_us(lambda i: sv.sv_softmax_partials(d["tgt"], ti.T, out=part), 1, args.steps,
+                               torch, per_graph=min(args.steps, 500)) * 1e-6
         rows_bytes = B * N * ti.V * 2
         fb = 2 * rows_bytes + 2 * 4 * B * N
         result.update(value=round(B / (ms * 1e-3), 1), unit="rounds/s", ms_per_step=round(ms, 5),
@@ -294,7 +371,7 @@ def main():
             ids, lens = sv.sv_ngram_draft(ctx, cl, g.window, g.k)
             return sv.sv_verify_greedy(tgt, trs, ids, lens, workspace=ws)
 
-        wall, ev_ms = timed(step, args.steps, args.warmup, torch)
+        wall, tot_ms, ev_ms = timed(step, args.steps, args.warmup, torch)
         ms = 1e3 * wall / args.steps
         fb = g.target.size * 2 + g.ctx.size * 4
         result.update(value=round(g.B / (ms * 1e-3), 1), unit="rounds/s", ms_per_step=round(ms, 5),
