@@ -239,7 +239,7 @@ sv_status sv_verify_tree(const void* target_logits, int32_t t_dtype, const void*
     return fail(SV_E_DTYPE, "t_dtype and q_dtype must be SV_F32 or SV_BF16");
   if (batch < 0) return fail(SV_E_ARG, "batch < 0");
   if (n_nodes < 1 || n_nodes > sv::kMaxTreeNodes) return fail(SV_E_ARG, "n_nodes must be in [1, 1024]");
-  if (vocab < 1 || vocab > static_cast<int64_t>(sv::kMaxTreeTiles) * 4096)
+  if (vocab < 1 || vocab > static_cast<int64_t>(sv::kMaxTreeTiles) * sv::kSampleTile)
     return fail(SV_E_ARG, "tree vocab must be in [1, 1048576]");
   if (!(temperature > 0.f) || !std::isfinite(temperature))
     return fail(SV_E_ARG, "temperature must be finite and > 0");
@@ -279,7 +279,7 @@ sv_status sv_verify_tree(const void* target_logits, int32_t t_dtype, const void*
   a.status = dev_status;
   a.partial = partial;
   a.nseg = nseg;
-  a.ntiles = static_cast<int32_t>(sv::tiles_of(vocab));
+  a.ntiles = static_cast<int32_t>(sv::sample_tiles(vocab));
   e = sv::launch_tree_walk(t_dtype, q_dtype, a, st);
   return e == hipSuccess ? SV_OK : device_fail(e, "sv_verify_tree walk launch");
 }

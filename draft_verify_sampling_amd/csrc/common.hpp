@@ -8,8 +8,6 @@ namespace sv {
 
 constexpr int kBlock = 256;            // threads per block for the streaming kernels
 constexpr int kWave = 64;
-constexpr int kTile = 4096;            // elements per sampling tile (inverse-CDF unit)
-constexpr int kPerThreadTile = kTile / kBlock;  // 16 contiguous elements per thread
 constexpr float kLn2 = 0.6931471805599453f;
 
 
@@ -71,24 +69,6 @@ __device__ __forceinline__ int64_t head_elems(const void* row, int64_t V) {
   return h < V ? h : V;
 }
 
-// Load `n` consecutive elements starting at element e of a row.  Uses 16-byte
-// loads when the run is aligned and complete, element loads otherwise; elements
-// at or beyond V read as `fill`.
-template <class D, int n>
-__device__ __forceinline__ void load_run(const void* row, int64_t V, int64_t e, float* v,
-                                         float fill) {
-  static_assert(n % D::kPerVec == 0, "run must be whole vectors");
-  const bool fast = ((reinterpret_cast<uintptr_t>(row) + e * D::kSize) & 15u) == 0 && e + n <= V;
-  if (fast) {
-    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const char*>(row) + e * D::kSize);
-#pragma unroll
-    for (int j = 0; j < n / D::kPerVec; ++j) D::unpack(p[j], v + j * D::kPerVec);
-  } else {
-#pragma unroll
-    for (int j = 0; j < n; ++j) v[j] = (e + j < V) ? D::at(row, e + j) : fill;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Online softmax pairs over scaled scores y = l * c (c = log2(e) / T):
 // m = max of the rounded products l * c, s = sum 2^(l * c - m) with each term
@@ -125,32 +105,6 @@ __device__ __forceinline__ void ms_fold(MS& acc, const float* x, float c) {
   }
   acc.s = acc.s * ex2(acc.m - M) + e[0];
   acc.m = M;
-}
-
-__device__ __forceinline__ MS wave_ms(MS v) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    MS o{__shfl_xor(v.m, off, kWave), __shfl_xor(v.s, off, kWave)};
-    v = ms_combine(v, o);
-  }
-  return v;
-}
-
-// Block-wide (m, s) reduction; result valid in every thread.  `sh` holds
-// 2 * (blockDim/64) floats.
-__device__ __forceinline__ MS block_ms(MS v, float* sh) {
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  const int nw = blockDim.x / kWave;
-  v = wave_ms(v);
-  if (lane == 0) {
-    sh[2 * wid] = v.m;
-    sh[2 * wid + 1] = v.s;
-  }
-  __syncthreads();
-  MS r{sh[0], sh[1]};
-  for (int w = 1; w < nw; ++w) r = ms_combine(r, MS{sh[2 * w], sh[2 * w + 1]});
-  __syncthreads();
-  return r;
 }
 
 // ---------------------------------------------------------------------------
@@ -208,65 +162,6 @@ __device__ __forceinline__ MS wave_ms_dpp(MS v) {
 #undef SV_MS_STEP
   return MS{__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v.m), kWave - 1)),
             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v.s), kWave - 1))};
-}
-
-// ---------------------------------------------------------------------------
-// Plain block reductions / scans.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
-
-// Sum over the block of up to 3 doubles at once; results valid in every thread.
-// `sh` holds 3 * (blockDim/64) doubles.
-template <int n>
-__device__ __forceinline__ void block_sum(double* v, double* sh) {
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  const int nw = blockDim.x / kWave;
-#pragma unroll
-  for (int j = 0; j < n; ++j) v[j] = wave_sum(v[j]);
-  if (lane == 0) {
-#pragma unroll
-    for (int j = 0; j < n; ++j) sh[n * wid + j] = v[j];
-  }
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < n; ++j) {
-    double t = 0.0;
-    for (int w = 0; w < nw; ++w) t += sh[n * w + j];
-    v[j] = t;
-  }
-  __syncthreads();
-}
-
-// Exclusive prefix sum over the block (thread order); returns this thread's
-// exclusive prefix, and the block total in *total.  `sh` holds blockDim/64 + 1
-// doubles.
-__device__ __forceinline__ double block_exclusive_scan(double x, double* total, double* sh) {
-  // (x only enters through the inclusive wave scan below)
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  const int nw = blockDim.x / kWave;
-  double incl = x;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const double y = __shfl_up(incl, off, kWave);
-    if (lane >= off) incl += y;
-  }
-  if (lane == kWave - 1) sh[wid] = incl;
-  __syncthreads();
-  double base = 0.0, tot = 0.0;
-  for (int w = 0; w < nw; ++w) {
-    const double t = sh[w];
-    if (w < wid) base += t;
-    tot += t;
-  }
-  __syncthreads();
-  *total = tot;
-  double excl = __shfl_up(incl, 1, kWave);
-  if (lane == 0) excl = 0.0;
-  return base + excl;
 }
 
 __device__ __forceinline__ void flag(int32_t* status, int bits) {

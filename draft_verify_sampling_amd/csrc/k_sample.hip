@@ -27,8 +27,7 @@
 //
 // Only the break row's draft row is read from HBM: the accept test needs just
 // q_i(x_i) from the other draft rows.
-#include "common.hpp"
-#include "launch.hpp"
+#include "tiles.hpp"
 
 namespace sv {
 
@@ -146,24 +145,6 @@ __device__ void write_invalid(const SampleArgs& a, int b, int bits) {
   }
 }
 
-template <int n>
-__device__ __forceinline__ float pairwise(const float* x) {
-  float t[n];
-#pragma unroll
-  for (int j = 0; j < n; ++j) t[j] = x[j];
-#pragma unroll
-  for (int w = 1; w < n; w *= 2) {
-#pragma unroll
-    for (int j = 0; j + w < n; j += 2 * w) t[j] += t[j + w];
-  }
-  return t[0];
-}
-
-// Shift a wave-inclusive scan into an exclusive one (lane 0 reads 0).
-__device__ __forceinline__ double wave_exclusive_from_inclusive(double incl) {
-  return dpp_d<0x138, 0xf>(incl);  // wave_shr:1
-}
-
 // Draw the last token from the tile sums T[ntiles][3] and write the outputs.
 // Run by exactly one wave (64 lanes); ids[0..m) and ufinal are the request's
 // drafted tokens and final uniform.  Lane l owns the contiguous tiles
@@ -175,9 +156,8 @@ __device__ void wave_draw_emit(const SampleArgs& a, int b, const Pre& pr, const 
   const int lane = threadIdx.x & (kWave - 1);
   const int ustride = a.k_max + 1;
   const bool resid = pr.m < pr.k;
-  const int tpl = (a.ntiles + kWave - 1) / kWave;
-  const int ta = lane * tpl;
-  const int tb = min(ta + tpl, a.ntiles);
+  int ta, tb;
+  lane_tiles(a.ntiles, lane, ta, tb);
   double own[3] = {0.0, 0.0, 0.0};
   for (int t = ta; t < tb; ++t) {
     own[0] += T[3 * t];
@@ -200,125 +180,16 @@ __device__ void wave_draw_emit(const SampleArgs& a, int b, const Pre& pr, const 
   const double total = which ? tot_p : tot_r;
   const double target = static_cast<double>(ufinal) * total;
 
-  // the tile: first one with mass whose running sum exceeds the target
-  const double mine = which ? own[1] : own[0];
-  double run = wave_exclusive_from_inclusive(wave_incl_scan(mine));
-  int hit = -1, lastpos = -1;
-  double hit_base = 0.0;
-  for (int t = ta; t < tb; ++t) {
-    const double wt = T[3 * t + which];
-    if (wt > 0.0) {
-      if (hit < 0 && run + wt > target) {
-        hit = t;
-        hit_base = run;
-      }
-      lastpos = t;
-    }
-    run += wt;
+  TileHit h;
+  if (!wave_find_tile(T + which, 3, a.ntiles, which ? own[1] : own[0], target, h)) {
+    // no mass anywhere (cannot happen when S > 0); defined output
+    write_invalid(a, b, kFlagNonfinite | bits);
+    return;
   }
-  int tile;
-  double tile_base = 0.0;
-  bool overshoot = false;
-  {
-    const uint64_t found = __ballot(hit >= 0);
-    if (found) {
-      const int src = __ffsll(static_cast<long long>(found)) - 1;
-      tile = __builtin_amdgcn_readlane(hit, src);
-      tile_base = lane_value(hit_base, src);
-    } else {
-      const uint64_t any = __ballot(lastpos >= 0);
-      if (!any) {  // no mass anywhere (cannot happen when S > 0); defined output
-        write_invalid(a, b, kFlagNonfinite | bits);
-        return;
-      }
-      const int src = 63 - __clzll(static_cast<long long>(any));
-      tile = __builtin_amdgcn_readlane(lastpos, src);
-      overshoot = true;
-    }
-  }
-
-  // the id: rescan the tile; lane l owns its kLane contiguous elements, read
-  // in one round (raw 16-byte vectors when aligned); lane-local sums in fp32,
-  // sums across lanes in fp64.
-  constexpr int kLane = kSampleTile / kWave;  // 32
-  const void* trow = row_ptr<DT>(a.tgt, pr.ts + pr.m, a.V);
-  const void* qrow = resid ? row_ptr<DQ>(a.dq, pr.qs + pr.m, a.V) : nullptr;
-  const int64_t e0 = static_cast<int64_t>(tile) * kSampleTile + lane * kLane;
-  constexpr int kTV = kLane / DT::kPerVec, kQV = kLane / DQ::kPerVec;
-  uint4 tv[kTV], qv[kQV];
-  const bool fast = e0 + kLane <= a.V &&
-                    ((reinterpret_cast<uintptr_t>(trow) + e0 * DT::kSize) & 15u) == 0 &&
-                    (!resid || ((reinterpret_cast<uintptr_t>(qrow) + e0 * DQ::kSize) & 15u) == 0);
-  if (fast) {
-#pragma unroll
-    for (int j = 0; j < kTV; ++j)
-      tv[j] = *reinterpret_cast<const uint4*>(static_cast<const char*>(trow) + (e0 + j * DT::kPerVec) * DT::kSize);
-    if (resid) {
-#pragma unroll
-      for (int j = 0; j < kQV; ++j)
-        qv[j] = *reinterpret_cast<const uint4*>(static_cast<const char*>(qrow) + (e0 + j * DQ::kPerVec) * DQ::kSize);
-    }
-  }
-  // the lane's draw weights, in groups of 8 elements
-  float wv[kLane];
-#pragma unroll
-  for (int g = 0; g < kLane / 8; ++g) {
-    float l[8], q[8];
-    if (fast) {
-      if (DT::kPerVec == 8) {
-        DT::unpack(tv[g], l);
-      } else {
-        DT::unpack(tv[2 * g], l);
-        DT::unpack(tv[2 * g + 1], l + 4);
-      }
-      if (resid) {
-        if (DQ::kPerVec == 8) {
-          DQ::unpack(qv[g], q);
-        } else {
-          DQ::unpack(qv[2 * g], q);
-          DQ::unpack(qv[2 * g + 1], q + 4);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int64_t e = e0 + 8 * g + j;
-        const bool in = e < a.V;
-        l[j] = in ? DT::at(trow, e) : -INFINITY;
-        q[j] = (in && resid) ? DQ::at(qrow, e) : 0.f;
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float p = ex2(fmaf(l[j], a.c, -pr.Mc)) * pr.invS;
-      wv[8 * g + j] = (which || !resid) ? p : fmaxf(p - (resid ? q[j] : 0.f), 0.f);
-    }
-  }
-  const double lane_base = tile_base + wave_exclusive_from_inclusive(
-                                           wave_incl_scan(static_cast<double>(pairwise<kLane>(wv))));
-  const float thr = static_cast<float>(target - lane_base);  // crossing: running weight > thr
-  int first = -1, lastw = -1;
-  float lrun = 0.f;
-#pragma unroll
-  for (int i = 0; i < kLane; ++i) {
-    const float wj = wv[i];
-    if (wj > 0.f) {
-      if (first < 0 && !overshoot && lrun + wj > thr) first = lane * kLane + i;
-      lastw = lane * kLane + i;
-    }
-    lrun += wj;
-  }
-  int pick;
-  {
-    const uint64_t found = __ballot(first >= 0);
-    if (found) {
-      pick = __builtin_amdgcn_readlane(first, __ffsll(static_cast<long long>(found)) - 1);
-    } else {
-      const uint64_t any = __ballot(lastw >= 0);
-      pick = any ? __builtin_amdgcn_readlane(lastw, 63 - __clzll(static_cast<long long>(any))) : 0;
-    }
-  }
-  const int y = static_cast<int>(static_cast<int64_t>(tile) * kSampleTile + pick);
+  const DrawRow row{row_ptr<DT>(a.tgt, pr.ts + pr.m, a.V),
+                    resid ? row_ptr<DQ>(a.dq, pr.qs + pr.m, a.V) : nullptr,
+                    a.c, pr.Mc, pr.invS, 1.f, resid && !which};
+  const int y = wave_pick_in_tile<DT, DQ>(row, a.V, h, target);
 
   if (lane == 0) {
     int32_t* out = a.out_tok + static_cast<int64_t>(b) * ustride;
@@ -344,92 +215,6 @@ __device__ void wave_draw_emit(const SampleArgs& a, int b, const Pre& pr, const 
 
 }  // namespace
 
-// Sums (r, p, q) of one 2048-element tile, computed by one wave: lane l takes
-// the 16-byte vectors l, l + 64, l + 128, ... of the tile (coalesced), loads a
-// batch of them as raw words and unpacks while folding; the result is valid in
-// every lane of the wave.  Rows that are not 16-byte aligned, and the row's
-// last partial tile, take element loads.
-template <class D>
-__device__ __forceinline__ uint4 ld16(const void* row, int64_t e) {
-  return *reinterpret_cast<const uint4*>(static_cast<const char*>(row) + e * D::kSize);
-}
-
-template <class DT, class DQ>
-__device__ __forceinline__ void wave_tile_sums(const SampleArgs& a, const void* trow, const void* qrow,
-                                               const Pre& pr, int t, double* v) {
-  // elements per run: the wider of the two vector widths, so each row's share
-  // of a run is a whole number of 16-byte vectors
-  constexpr int kPer = DT::kPerVec > DQ::kPerVec ? DT::kPerVec : DQ::kPerVec;
-  constexpr int kRuns = kSampleTile / (kWave * kPer);                         // runs per lane
-  constexpr int kBatch = kRuns < 4 ? kRuns : 4;
-  const int lane = threadIdx.x & (kWave - 1);
-  const bool resid = pr.m < pr.k;
-  const int64_t t0 = static_cast<int64_t>(t) * kSampleTile;
-  const bool fast = t0 + kSampleTile <= a.V &&
-                    ((reinterpret_cast<uintptr_t>(trow) + t0 * DT::kSize) & 15u) == 0 &&
-                    (!resid || ((reinterpret_cast<uintptr_t>(qrow) + t0 * DQ::kSize) & 15u) == 0);
-  float rs = 0.f, ps = 0.f, qs = 0.f;
-  constexpr int nt = kPer * DT::kSize / 16, nq = kPer * DQ::kSize / 16;
-  static_assert(nt >= 1 && nq >= 1, "a run must cover whole vectors of both rows");
-  if (fast) {
-#pragma unroll
-    for (int r0 = 0; r0 < kRuns; r0 += kBatch) {
-      uint4 tw[kBatch][nt];
-      uint4 qw[kBatch][nq];
-#pragma unroll
-      for (int r = 0; r < kBatch; ++r) {
-        const int64_t e = t0 + static_cast<int64_t>((r0 + r) * kWave + lane) * kPer;
-#pragma unroll
-        for (int j = 0; j < nt; ++j) tw[r][j] = ld16<DT>(trow, e + j * DT::kPerVec);
-        if (resid) {
-#pragma unroll
-          for (int j = 0; j < nq; ++j) qw[r][j] = ld16<DQ>(qrow, e + j * DQ::kPerVec);
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < kBatch; ++r) {
-        float l[kPer], q[kPer], w[kPer], p[kPer];
-#pragma unroll
-        for (int j = 0; j < nt; ++j) DT::unpack(tw[r][j], l + j * DT::kPerVec);
-        if (resid) {
-#pragma unroll
-          for (int j = 0; j < nq; ++j) DQ::unpack(qw[r][j], q + j * DQ::kPerVec);
-        } else {
-#pragma unroll
-          for (int j = 0; j < kPer; ++j) q[j] = 0.f;
-        }
-#pragma unroll
-        for (int j = 0; j < kPer; ++j) {
-          p[j] = ex2(fmaf(l[j], a.c, -pr.Mc)) * pr.invS;
-          w[j] = resid ? fmaxf(p[j] - q[j], 0.f) : p[j];
-        }
-        rs += pairwise<kPer>(w);
-        ps += pairwise<kPer>(p);
-        qs += pairwise<kPer>(q);
-      }
-    }
-  } else {
-    // unaligned rows or the partial last tile: element loads, one run at a time
-#pragma unroll 1
-    for (int r = 0; r < kRuns; ++r) {
-      const int64_t e = t0 + static_cast<int64_t>(r * kWave + lane) * kPer;
-#pragma unroll 1
-      for (int j = 0; j < kPer; ++j) {
-        const bool in = e + j < a.V;
-        const float l = in ? DT::at(trow, e + j) : -INFINITY;
-        const float q = (in && resid) ? DQ::at(qrow, e + j) : 0.f;
-        const float p = ex2(fmaf(l, a.c, -pr.Mc)) * pr.invS;
-        rs += resid ? fmaxf(p - q, 0.f) : p;
-        ps += p;
-        qs += q;
-      }
-    }
-  }
-  v[0] = wave_total(static_cast<double>(rs));
-  v[1] = wave_total(static_cast<double>(ps));
-  v[2] = wave_total(static_cast<double>(qs));
-}
-
 template <class DT, class DQ>
 __global__ __launch_bounds__(kBlock) void k_sample_tiles(SampleArgs a) {
   constexpr int kTilesPerBlock = kBlock / kWave;
@@ -448,13 +233,14 @@ __global__ __launch_bounds__(kBlock) void k_sample_tiles(SampleArgs a) {
   if (t >= a.ntiles) return;
   const void* trow = row_ptr<DT>(a.tgt, pr.ts + pr.m, a.V);
   const void* qrow = pr.m < pr.k ? row_ptr<DQ>(a.dq, pr.qs + pr.m, a.V) : nullptr;
-  double v[3];
-  wave_tile_sums<DT, DQ>(a, trow, qrow, pr, t, v);
+  const DrawRow row{trow, qrow, a.c, pr.Mc, pr.invS, 1.f, pr.m < pr.k};
+  double v[1][3];
+  wave_tile_sums<DT, DQ, 1>(row, a.V, t, 0, v);
   if ((threadIdx.x & (kWave - 1)) == 0) {
     double* T = a.tiles + (static_cast<int64_t>(b) * a.ntiles + t) * 3;
-    T[0] = v[0];
-    T[1] = v[1];
-    T[2] = v[2];
+    T[0] = v[0][0];
+    T[1] = v[0][1];
+    T[2] = v[0][2];
   }
 }
 
@@ -473,12 +259,13 @@ __global__ __launch_bounds__(kBlock) void k_sample_single(SampleArgs a) {
   if (threadIdx.x >= kWave) return;
   const void* trow = row_ptr<DT>(a.tgt, pr.ts + pr.m, a.V);
   const void* qrow = pr.m < pr.k ? row_ptr<DQ>(a.dq, pr.qs + pr.m, a.V) : nullptr;
-  double v[3];
-  wave_tile_sums<DT, DQ>(a, trow, qrow, pr, 0, v);
+  const DrawRow row{trow, qrow, a.c, pr.Mc, pr.invS, 1.f, pr.m < pr.k};
+  double v[1][3];
+  wave_tile_sums<DT, DQ, 1>(row, a.V, 0, 0, v);
   if (threadIdx.x == 0) {
-    s_tile[0] = v[0];
-    s_tile[1] = v[1];
-    s_tile[2] = v[2];
+    s_tile[0] = v[0][0];
+    s_tile[1] = v[0][1];
+    s_tile[2] = v[0][2];
   }
   wave_draw_emit<DT, DQ>(a, b, pr, s_tile, sh.ids, sh.ufinal);
 }

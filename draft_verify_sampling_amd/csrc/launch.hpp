@@ -11,7 +11,6 @@ constexpr int kDtypeF32 = 0;
 constexpr int kDtypeBF16 = 1;
 constexpr int kMaxChainRows = 256;     // k_max + 1 rows per request at most
 constexpr int kMaxTreeNodes = 1024;
-constexpr int kMaxTreeTiles = 256;     // tree vocab <= 256 * 4096
 constexpr int kMaxWindow = 64;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -39,11 +38,10 @@ inline int32_t argmax_segments(int64_t rows, int64_t V) {
   return static_cast<int32_t>(nseg);
 }
 
-inline int64_t tiles_of(int64_t V) { return (V + 4095) / 4096; }   // tree passes
-
 // The sampled verify's inverse-CDF unit: one wave sums one tile.
 constexpr int kSampleTile = 2048;
 inline int64_t sample_tiles(int64_t V) { return (V + kSampleTile - 1) / kSampleTile; }
+constexpr int kMaxTreeTiles = 512;     // tree vocab <= 512 * 2048
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 

@@ -1,0 +1,370 @@
+// Tile-level steps of an inverse-CDF draw over one vocabulary row, shared by
+// the chain and the tree verify kernels.  A tile is kSampleTile = 2048
+// consecutive ids and one wave handles one tile.
+//
+// Draw weights of a row: p = 2^(l c - Mc) / S, the temperature softmax of the
+// target logits l (c = log2(e) / T, Mc the row's scaled-domain max, S its
+// normaliser), either as they are or as the residual w = max(0, p - coef q)
+// against the draft probabilities q ("投机解码:为什么一个字都不改", section
+// "改进:接受概率 min(1, p/q),拒绝时从残差重采"; the tree walk of "Speculative
+// Decoding II", EAGLE section, applies it with a growing coef).  The drawn id
+// is the smallest one whose running weight exceeds u times the total weight:
+// ids of weight zero are never drawn, and when rounding leaves the target at or
+// beyond the last running sum the last id of positive weight is taken.
+#pragma once
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace sv {
+
+struct DrawRow {
+  const void* t;   // target logits of the row
+  const void* q;   // draft probabilities of the row, read only when use_q
+  float c;         // log2(e) / T
+  float Mc;        // scaled-domain max of the target row
+  float invS;      // 1 / softmax normaliser of the target row
+  float coef;      // residual coefficient
+  bool use_q;      // true: w = max(0, p - coef q); false: w = p
+};
+
+template <int n>
+__device__ __forceinline__ float pairwise(const float* x) {
+  float t[n];
+#pragma unroll
+  for (int j = 0; j < n; ++j) t[j] = x[j];
+#pragma unroll
+  for (int w = 1; w < n; w *= 2) {
+#pragma unroll
+    for (int j = 0; j + w < n; j += 2 * w) t[j] += t[j + w];
+  }
+  return t[0];
+}
+
+template <class D>
+__device__ __forceinline__ uint4 ld16(const void* row, int64_t e) {
+  return *reinterpret_cast<const uint4*>(static_cast<const char*>(row) + e * D::kSize);
+}
+
+template <class D>
+__device__ __forceinline__ bool aligned16(const void* row, int64_t e) {
+  return ((reinterpret_cast<uintptr_t>(row) + e * D::kSize) & 15u) == 0;
+}
+
+// Shift a wave-inclusive scan into an exclusive one (lane 0 reads 0).
+__device__ __forceinline__ double wave_exclusive_from_inclusive(double incl) {
+  return dpp_d<0x138, 0xf>(incl);  // wave_shr:1
+}
+
+__device__ __forceinline__ float draw_p(const DrawRow& r, float l) {
+  return ex2(fmaf(l, r.c, -r.Mc)) * r.invS;
+}
+
+__device__ __forceinline__ float draw_w(const DrawRow& r, float p, float q) {
+  return r.use_q ? fmaxf(p - r.coef * q, 0.f) : p;
+}
+
+// Layout of a tile for the sums: runs of kPer consecutive elements (the wider
+// of the two rows' 16-byte vector widths, so each row's share of a run is a
+// whole number of vectors); lane l takes runs l, l + 64, l + 128, ... so every
+// load instruction of the wave is coalesced.
+template <class DT, class DQ>
+struct TileRuns {
+  static constexpr int kPer = DT::kPerVec > DQ::kPerVec ? DT::kPerVec : DQ::kPerVec;
+  static constexpr int kRuns = kSampleTile / (kWave * kPer);  // runs per lane per tile
+  static constexpr int nt = kPer * DT::kSize / 16;            // target vectors per run
+  static constexpr int nq = kPer * DQ::kSize / 16;            // draft vectors per run
+  static_assert(nt >= 1 && nq >= 1, "a run must cover whole vectors of both rows");
+};
+
+// Sums (w, p, q) of tile t, in fp32 within a lane and fp64 across lanes; valid
+// in every lane.  Handles any tile: a row that is not 16-byte aligned, and the
+// row's last partial tile, take element loads run by run.
+template <class DT, class DQ>
+__device__ __forceinline__ void wave_tile_sums_any(const DrawRow& r, int64_t V, int t, double* v) {
+  using L = TileRuns<DT, DQ>;
+  constexpr int kPer = L::kPer;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t t0 = static_cast<int64_t>(t) * kSampleTile;
+  const bool al = aligned16<DT>(r.t, t0) && (!r.use_q || aligned16<DQ>(r.q, t0));
+  float ws = 0.f, ps = 0.f, qs = 0.f;
+#pragma unroll 1
+  for (int k = 0; k < L::kRuns; ++k) {
+    const int64_t e = t0 + static_cast<int64_t>(k * kWave + lane) * kPer;
+    if (e >= V) break;
+    float l[kPer], q[kPer];
+    if (al && e + kPer <= V) {
+#pragma unroll
+      for (int j = 0; j < L::nt; ++j) DT::unpack(ld16<DT>(r.t, e + j * DT::kPerVec), l + j * DT::kPerVec);
+      if (r.use_q) {
+#pragma unroll
+        for (int j = 0; j < L::nq; ++j) DQ::unpack(ld16<DQ>(r.q, e + j * DQ::kPerVec), q + j * DQ::kPerVec);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) q[j] = 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const bool in = e + j < V;
+        l[j] = in ? DT::at(r.t, e + j) : -INFINITY;
+        q[j] = (in && r.use_q) ? DQ::at(r.q, e + j) : 0.f;
+      }
+    }
+    float w[kPer], p[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      p[j] = draw_p(r, l[j]);
+      w[j] = draw_w(r, p[j], q[j]);
+    }
+    ws += pairwise<kPer>(w);
+    ps += pairwise<kPer>(p);
+    qs += pairwise<kPer>(q);
+  }
+  v[0] = wave_total(static_cast<double>(ws));
+  v[1] = wave_total(static_cast<double>(ps));
+  v[2] = wave_total(static_cast<double>(qs));
+}
+
+// Sums (w, p, q) of the kT tiles t, t + tstride, ... into v[i]; all of a
+// lane's loads for a batch of runs are in flight before the first is used.
+// Falls back to wave_tile_sums_any tile by tile unless every tile is complete
+// and the rows are 16-byte aligned.
+template <class DT, class DQ, int kT>
+__device__ __forceinline__ void wave_tile_sums(const DrawRow& r, int64_t V, int t, int tstride,
+                                               double (*v)[3]) {
+  using L = TileRuns<DT, DQ>;
+  constexpr int kPer = L::kPer;
+  constexpr int kAll = kT * L::kRuns;                           // runs per lane in total
+  constexpr int kCap = (L::nt + L::nq == 2) ? 8 : 4;            // runs per batch (<= 16 vectors)
+  constexpr int kBatch = kAll < kCap ? kAll : kCap;
+  static_assert(kAll % kBatch == 0, "whole batches");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t tlast = static_cast<int64_t>(t + (kT - 1) * tstride);
+  const bool fast = (tlast + 1) * kSampleTile <= V && aligned16<DT>(r.t, 0) &&
+                    (!r.use_q || aligned16<DQ>(r.q, 0));
+  if (!fast) {
+#pragma unroll 1
+    for (int i = 0; i < kT; ++i) wave_tile_sums_any<DT, DQ>(r, V, t + i * tstride, v[i]);
+    return;
+  }
+  float ws[kT], ps[kT], qs[kT];
+#pragma unroll
+  for (int i = 0; i < kT; ++i) ws[i] = ps[i] = qs[i] = 0.f;
+#pragma unroll
+  for (int r0 = 0; r0 < kAll; r0 += kBatch) {
+    uint4 tw[kBatch][L::nt];
+    uint4 qw[kBatch][L::nq];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int run = r0 + k, ti = run / L::kRuns, kr = run % L::kRuns;
+      const int64_t e = static_cast<int64_t>(t + ti * tstride) * kSampleTile +
+                        static_cast<int64_t>(kr * kWave + lane) * kPer;
+#pragma unroll
+      for (int j = 0; j < L::nt; ++j) tw[k][j] = ld16<DT>(r.t, e + j * DT::kPerVec);
+      if (r.use_q) {
+#pragma unroll
+        for (int j = 0; j < L::nq; ++j) qw[k][j] = ld16<DQ>(r.q, e + j * DQ::kPerVec);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int ti = (r0 + k) / L::kRuns;
+      float l[kPer], q[kPer], w[kPer], p[kPer];
+#pragma unroll
+      for (int j = 0; j < L::nt; ++j) DT::unpack(tw[k][j], l + j * DT::kPerVec);
+      if (r.use_q) {
+#pragma unroll
+        for (int j = 0; j < L::nq; ++j) DQ::unpack(qw[k][j], q + j * DQ::kPerVec);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) q[j] = 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        p[j] = draw_p(r, l[j]);
+        w[j] = draw_w(r, p[j], q[j]);
+      }
+      ws[ti] += pairwise<kPer>(w);
+      ps[ti] += pairwise<kPer>(p);
+      qs[ti] += pairwise<kPer>(q);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < kT; ++i) {
+    v[i][0] = wave_total(static_cast<double>(ws[i]));
+    v[i][1] = wave_total(static_cast<double>(ps[i]));
+    v[i][2] = wave_total(static_cast<double>(qs[i]));
+  }
+}
+
+// Online-softmax pair (scaled domain, as in common.hpp) of tile t of a target
+// row, valid in every lane.  Lane l takes the 16-byte vectors l, l + 64, ...
+// of the tile, all in flight at once, and folds them with one rescale; the
+// row's last partial tile and unaligned rows take element loads.
+template <class D>
+__device__ __forceinline__ MS wave_tile_ms(const void* row, int64_t V, float c, int t) {
+  constexpr int kPer = D::kPerVec;
+  constexpr int kRuns = kSampleTile / (kWave * kPer);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t t0 = static_cast<int64_t>(t) * kSampleTile;
+  MS acc{-INFINITY, 0.f};
+  if (t0 + kSampleTile <= V && aligned16<D>(row, t0)) {
+    uint4 w[kRuns];
+#pragma unroll
+    for (int k = 0; k < kRuns; ++k) w[k] = ld16<D>(row, t0 + static_cast<int64_t>(k * kWave + lane) * kPer);
+    float x[kRuns * kPer];
+#pragma unroll
+    for (int k = 0; k < kRuns; ++k) D::unpack(w[k], x + k * kPer);
+    ms_fold<kRuns * kPer>(acc, x, c);
+  } else {
+    const bool al = aligned16<D>(row, t0);
+#pragma unroll 1
+    for (int k = 0; k < kRuns; ++k) {
+      const int64_t e = t0 + static_cast<int64_t>(k * kWave + lane) * kPer;
+      if (e >= V) break;
+      float x[kPer];
+      if (al && e + kPer <= V) {
+        D::unpack(ld16<D>(row, e), x);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) x[j] = e + j < V ? D::at(row, e + j) : -INFINITY;
+      }
+      ms_fold<kPer>(acc, x, c);
+    }
+  }
+  return wave_ms_dpp(acc);
+}
+
+// Lane l's contiguous share [ta, tb) of ntiles tile sums for the tile search.
+__device__ __forceinline__ void lane_tiles(int ntiles, int lane, int& ta, int& tb) {
+  const int tpl = (ntiles + kWave - 1) / kWave;
+  ta = min(lane * tpl, ntiles);
+  tb = min(ta + tpl, ntiles);
+}
+
+struct TileHit {
+  int tile;         // tile holding the target (or the last tile with weight)
+  double base;      // running weight before that tile
+  bool overshoot;   // no tile's running sum exceeded the target
+};
+
+// The tile holding `target`: the first tile of positive weight whose running
+// sum exceeds it, else the last tile of positive weight.  ts[t * stride] is
+// tile t's weight and `mine` the lane's own sum over lane_tiles (summed in
+// order); returns false when no tile has weight.
+__device__ __forceinline__ bool wave_find_tile(const double* ts, int stride, int ntiles, double mine,
+                                               double target, TileHit& h) {
+  const int lane = threadIdx.x & (kWave - 1);
+  int ta, tb;
+  lane_tiles(ntiles, lane, ta, tb);
+  double run = wave_exclusive_from_inclusive(wave_incl_scan(mine));
+  int hit = -1, lastpos = -1;
+  double hit_base = 0.0;
+  for (int t = ta; t < tb; ++t) {
+    const double wt = ts[static_cast<int64_t>(t) * stride];
+    if (wt > 0.0) {
+      if (hit < 0 && run + wt > target) {
+        hit = t;
+        hit_base = run;
+      }
+      lastpos = t;
+    }
+    run += wt;
+  }
+  const uint64_t found = __ballot(hit >= 0);
+  if (found) {
+    const int src = __ffsll(static_cast<long long>(found)) - 1;
+    h.tile = __builtin_amdgcn_readlane(hit, src);
+    h.base = lane_value(hit_base, src);
+    h.overshoot = false;
+    return true;
+  }
+  const uint64_t any = __ballot(lastpos >= 0);
+  if (!any) return false;
+  h.tile = __builtin_amdgcn_readlane(lastpos, 63 - __clzll(static_cast<long long>(any)));
+  h.base = 0.0;
+  h.overshoot = true;
+  return true;
+}
+
+// The id inside tile h.tile: lane l owns the 32 contiguous elements
+// [32 l, 32 l + 32), read in one round (16-byte vectors when aligned and
+// complete); running weights in fp32 within a lane and fp64 across lanes.
+template <class DT, class DQ>
+__device__ __forceinline__ int wave_pick_in_tile(const DrawRow& r, int64_t V, const TileHit& h,
+                                                 double target) {
+  constexpr int kLane = kSampleTile / kWave;  // 32
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t e0 = static_cast<int64_t>(h.tile) * kSampleTile + lane * kLane;
+  constexpr int kTV = kLane / DT::kPerVec, kQV = kLane / DQ::kPerVec;
+  uint4 tv[kTV], qv[kQV];
+  const bool fast = e0 + kLane <= V && aligned16<DT>(r.t, e0) && (!r.use_q || aligned16<DQ>(r.q, e0));
+  if (fast) {
+#pragma unroll
+    for (int j = 0; j < kTV; ++j) tv[j] = ld16<DT>(r.t, e0 + j * DT::kPerVec);
+    if (r.use_q) {
+#pragma unroll
+      for (int j = 0; j < kQV; ++j) qv[j] = ld16<DQ>(r.q, e0 + j * DQ::kPerVec);
+    }
+  }
+  float wv[kLane];
+#pragma unroll
+  for (int g = 0; g < kLane / 8; ++g) {
+    float l[8], q[8];
+    if (fast) {
+      if (DT::kPerVec == 8) {
+        DT::unpack(tv[g], l);
+      } else {
+        DT::unpack(tv[2 * g], l);
+        DT::unpack(tv[2 * g + 1], l + 4);
+      }
+      if (r.use_q) {
+        if (DQ::kPerVec == 8) {
+          DQ::unpack(qv[g], q);
+        } else {
+          DQ::unpack(qv[2 * g], q);
+          DQ::unpack(qv[2 * g + 1], q + 4);
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) q[j] = 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int64_t e = e0 + 8 * g + j;
+        const bool in = e < V;
+        l[j] = in ? DT::at(r.t, e) : -INFINITY;
+        q[j] = (in && r.use_q) ? DQ::at(r.q, e) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) wv[8 * g + j] = draw_w(r, draw_p(r, l[j]), q[j]);
+  }
+  const double lane_base =
+      h.base + wave_exclusive_from_inclusive(wave_incl_scan(static_cast<double>(pairwise<kLane>(wv))));
+  const float thr = static_cast<float>(target - lane_base);  // crossing: running weight > thr
+  int first = -1, lastw = -1;
+  float lrun = 0.f;
+#pragma unroll
+  for (int i = 0; i < kLane; ++i) {
+    const float wj = wv[i];
+    if (wj > 0.f) {
+      if (first < 0 && !h.overshoot && lrun + wj > thr) first = lane * kLane + i;
+      lastw = lane * kLane + i;
+    }
+    lrun += wj;
+  }
+  int pick;
+  const uint64_t found = __ballot(first >= 0);
+  if (found) {
+    pick = __builtin_amdgcn_readlane(first, __ffsll(static_cast<long long>(found)) - 1);
+  } else {
+    const uint64_t any = __ballot(lastw >= 0);
+    pick = any ? __builtin_amdgcn_readlane(lastw, 63 - __clzll(static_cast<long long>(any))) : 0;
+  }
+  return static_cast<int>(static_cast<int64_t>(h.tile) * kSampleTile + pick);
+}
+
+}  // namespace sv

@@ -185,7 +185,7 @@ sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t
  * (kept nodes), out_path [batch, n_nodes] (kept node ids, -1 padded).
  * Optional out_diag [batch, n_nodes, 4] = (M_c, S_c, p_parent(x_c),
  * q_parent(x_c)) with the parent's softmax before any residual update
- * (p, q = 0 at the root).  1 <= n_nodes <= 1024. */
+ * (p, q = 0 at the root).  1 <= n_nodes <= 1024, 1 <= vocab <= 1048576. */
 sv_status sv_verify_tree(const void* target_logits, int32_t t_dtype,
                          const void* draft_probs, int32_t q_dtype, int64_t vocab,
                          const int32_t* parent, const int32_t* node_token,
