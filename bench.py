@@ -342,9 +342,10 @@ def main():
 
         wall, tot_ms, ev_ms = timed(step, args.steps, args.warmup, torch)
         ms = 1e3 * wall / args.steps
-        part = torch.empty((B * N, sv.sv_softmax_segments(B * N, ti.V), 2), dtype=torch.float32, device=dev)
-        st_avg = kernel_avg_us(lambda i: sv.sv_softmax_partials(d["tgt"], ti.T, out=part), 1, args.steps,
-                               torch, per_graph=min(args.steps, 500)) * 1e-6
+        acc = out[2].cpu().numpy()
+        # rows the walk must read: the target row of every visited node (root and
+        # kept path); draft rows are read only where a child was rejected
+        visited_bytes = int((1 + acc).sum()) * ti.V * 2
         rows_bytes = B * N * ti.V * 2
         fb = 2 * rows_bytes + 2 * 4 * B * N
         result.update(value=round(B / (ms * 1e-3), 1), unit="rounds/s", ms_per_step=round(ms, 5),
@@ -353,11 +354,8 @@ def main():
                                   vocab=128_256, temperature=1.0, inputs="bf16"),
                       tokens_per_s=round(float(out[1].sum().item()) / (ms * 1e-3), 1),
                       formula_bytes_per_step=fb, formula_GBps=round(fb / (ms * 1e-3) / 1e9, 1),
-                      roofline=dict(bound="hbm", kernel="k_row_stats", achieved=round(rows_bytes / st_avg / 1e9, 1),
-                                    peak=PEAK_HBM_GBPS, unit="GB/s",
-                                    frac=round(rows_bytes / st_avg / 1e9 / PEAK_HBM_GBPS, 4), traffic=None,
-                                    algorithmic_bytes_per_launch=rows_bytes,
-                                    avg_launch_us=round(st_avg * 1e6, 3)))
+                      visited_target_row_bytes=visited_bytes,
+                      roofline=None)
     else:  # c2: prompt lookup + greedy verify
         log("generating c2 inputs")
         g = synth.c2_greedy()

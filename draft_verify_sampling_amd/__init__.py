@@ -23,13 +23,13 @@ __all__ = [
     "sv_ngram_draft", "sv_verify_greedy", "sv_verify_sample", "sv_verify_tree",
     "sv_softmax_partials", "sv_softmax_segments", "SV_F32", "SV_BF16", "SV_OP_GREEDY", "SV_OP_SAMPLE", "SV_OP_TREE",
     "FLAG_BAD_REQUEST", "FLAG_BAD_TOKEN", "FLAG_NONFINITE", "FLAG_OVER_BUDGET",
-    "FLAG_FALLBACK", "FLAG_BAD_TREE", "EXPORTS",
+    "FLAG_FALLBACK", "FLAG_BAD_TREE", "FLAG_SYNC_TIMEOUT", "EXPORTS",
 ]
 
 SV_F32, SV_BF16 = 0, 1
 SV_OP_GREEDY, SV_OP_SAMPLE, SV_OP_TREE = 0, 1, 2
 FLAG_BAD_REQUEST, FLAG_BAD_TOKEN, FLAG_NONFINITE = 1, 2, 4
-FLAG_OVER_BUDGET, FLAG_FALLBACK, FLAG_BAD_TREE = 8, 16, 32
+FLAG_OVER_BUDGET, FLAG_FALLBACK, FLAG_BAD_TREE, FLAG_SYNC_TIMEOUT = 8, 16, 32, 64
 
 EXPORTS = ("sv_abi_version", "sv_status_string", "sv_last_error", "sv_workspace_bytes",
            "sv_softmax_segments", "sv_softmax_partials",

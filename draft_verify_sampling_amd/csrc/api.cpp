@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -40,6 +42,20 @@ sv_status check_workspace(const void* ws, size_t have, size_t need) {
 
 constexpr int64_t kMaxGrid = 0x7fffffff;
 
+// Compute units of the current device (cached per device; 0 if unknown).
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) {
+    if (const int n = cache[dev].load(std::memory_order_relaxed)) return n;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 }  // namespace
 
 extern "C" {
@@ -65,7 +81,7 @@ size_t sv_workspace_bytes(int op, int64_t batch, int64_t total_rows, int64_t voc
     case SV_OP_GREEDY:
       return sv::align256(static_cast<size_t>(total_rows * sv::argmax_segments(total_rows, vocab)) * 8);
     case SV_OP_TREE:
-      return sv::align256(static_cast<size_t>(total_rows * sv::row_segments(total_rows, vocab)) * 8);
+      return sv::tree_layout(batch, total_rows, vocab).bytes;
     case SV_OP_SAMPLE:
       return sv::sample_layout(batch, total_rows, vocab).bytes;
     default:
@@ -257,10 +273,15 @@ sv_status sv_verify_tree(const void* target_logits, int32_t t_dtype, const void*
 
   const float c = sv::kLog2e / temperature;
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  const sv::TreeLayout L = sv::tree_layout(batch, rows, vocab);
+  char* ws = static_cast<char*>(workspace);
   (void)hipGetLastError();
-  float2* partial = static_cast<float2*>(workspace);
-  hipError_t e = sv::launch_row_stats(t_dtype, target_logits, rows, vocab, nseg, c, partial, st);
-  if (e != hipSuccess) return device_fail(e, "sv_verify_tree row-stats launch");
+  float2* partial = reinterpret_cast<float2*>(ws + L.partial_off);
+  hipError_t e = hipSuccess;
+  if (out_diag != nullptr) {  // the walk itself reads only the rows it visits
+    e = sv::launch_row_stats(t_dtype, target_logits, rows, vocab, nseg, c, partial, st);
+    if (e != hipSuccess) return device_fail(e, "sv_verify_tree row-stats launch");
+  }
   sv::TreeArgs a{};
   a.tgt = target_logits;
   a.dq = draft_probs;
@@ -280,6 +301,10 @@ sv_status sv_verify_tree(const void* target_logits, int32_t t_dtype, const void*
   a.partial = partial;
   a.nseg = nseg;
   a.ntiles = static_cast<int32_t>(sv::sample_tiles(vocab));
+  a.G = std::min<int64_t>(sv::tree_groups(batch, vocab, cu_count()), sv::tree_groups_bound(batch));
+  a.slots = reinterpret_cast<uint64_t*>(ws + L.slots_off);
+  a.max_sync = static_cast<int32_t>(sv::tree_max_sync(n_nodes));
+  a.spin_limit = sv::kSpinLimit;
   e = sv::launch_tree_walk(t_dtype, q_dtype, a, st);
   return e == hipSuccess ? SV_OK : device_fail(e, "sv_verify_tree walk launch");
 }

@@ -18,6 +18,7 @@ constexpr int kFlagNonfinite = 4;
 constexpr int kFlagOverBudget = 8;
 constexpr int kFlagFallback = 16;
 constexpr int kFlagBadTree = 32;
+constexpr int kFlagSyncTimeout = 64;
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -38,12 +38,51 @@ inline int32_t argmax_segments(int64_t rows, int64_t V) {
   return static_cast<int32_t>(nseg);
 }
 
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
 // The sampled verify's inverse-CDF unit: one wave sums one tile.
 constexpr int kSampleTile = 2048;
 inline int64_t sample_tiles(int64_t V) { return (V + kSampleTile - 1) / kSampleTile; }
 constexpr int kMaxTreeTiles = 512;     // tree vocab <= 512 * 2048
 
-inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+// Tree walk: workgroups per request (G) and the exchange words between them.
+constexpr int kMaxTreeGroups = 32;
+constexpr int kCoopBlocks = 256;       // B * G never exceeds this (nor the device's CU count)
+constexpr int kSpinLimit = 1 << 20;    // polls of one exchange before giving up
+
+inline int32_t tree_groups(int64_t B, int64_t V, int cu_count) {
+  const int64_t cap = cu_count < kCoopBlocks ? cu_count : kCoopBlocks;
+  int64_t g = B > 0 ? cap / B : 1;
+  const int64_t nt = sample_tiles(V);
+  if (g > kMaxTreeGroups) g = kMaxTreeGroups;
+  if (g > nt) g = nt;
+  return static_cast<int32_t>(g < 1 ? 1 : g);
+}
+
+// Upper bound of G over devices (the workspace query knows no device).
+inline int64_t tree_groups_bound(int64_t B) {
+  int64_t g = B > 0 ? kCoopBlocks / B : 1;
+  if (g > kMaxTreeGroups) g = kMaxTreeGroups;
+  return g < 1 ? 1 : g;
+}
+
+// At most one exchange per visited node and one per weight pass: 2 N.
+inline int64_t tree_max_sync(int64_t N) { return 2 * N; }
+
+struct TreeLayout {
+  size_t partial_off, slots_off, bytes;
+};
+
+inline TreeLayout tree_layout(int64_t B, int64_t rows, int64_t V) {
+  TreeLayout L{};
+  const int64_t N = B > 0 ? rows / B : 0;
+  const int64_t G = tree_groups_bound(B);
+  L.partial_off = 0;
+  L.slots_off = align256(static_cast<size_t>(rows * row_segments(rows, V)) * 8);
+  const size_t slots = G > 1 ? static_cast<size_t>(B * tree_max_sync(N) * 2 * G) * 8 : 0;
+  L.bytes = L.slots_off + align256(slots);
+  return L;
+}
 
 struct SampleLayout {
   size_t partial_off, tiles_off, records_off, bytes;
@@ -119,9 +158,13 @@ struct TreeArgs {
   int32_t* out_path;
   float* diag;
   int32_t* status;
-  const float2* partial;
+  const float2* partial;   // softmax partials of every row (diagnostics only)
   int32_t nseg;
   int32_t ntiles;
+  uint64_t* slots;         // [B, max_sync, 2 G] exchange words (G > 1)
+  int32_t G;               // workgroups per request
+  int32_t max_sync;
+  int32_t spin_limit;
 };
 
 hipError_t launch_row_stats(int dtype, const void* rows, int64_t n_rows, int64_t V, int32_t nseg,

@@ -86,6 +86,10 @@ typedef enum { SV_OP_GREEDY = 0, SV_OP_SAMPLE = 1, SV_OP_TREE = 2 } sv_op;
 #define SV_FLAG_FALLBACK 16     /* a residual max(0, p - q) had zero mass: the token was
                                    drawn from p (chain) / p was left unchanged (tree) */
 #define SV_FLAG_BAD_TREE 32     /* parent[b,0] != -1, or parent[b,c] not in [0,c) */
+#define SV_FLAG_SYNC_TIMEOUT 64 /* tree: the workgroups sharing a request did not all
+                                   report within the bounded wait (only possible when
+                                   other work keeps some of them from running); that
+                                   request's outputs are undefined */
 
 int sv_abi_version(void);
 const char* sv_status_string(int status);

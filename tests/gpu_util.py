@@ -54,13 +54,13 @@ def run_greedy(target, kind, t_row_start, draft_ids, draft_len, max_new=None, eo
     return dict(tokens=tok.cpu().numpy(), count=cnt.cpu().numpy(), accepted=acc.cpu().numpy())
 
 
-def run_tree(ti, status=None):
+def run_tree(ti, status=None, diag=True):
     tok, cnt, acc, pth, dg = sv.sv_verify_tree(
         rows_to_dev(ti.target, ti.t_kind), rows_to_dev(ti.draft, ti.q_kind), i32(ti.parent),
-        i32(ti.token), ti.T, f32(ti.uniforms), diag=True, dev_status=status)
+        i32(ti.token), ti.T, f32(ti.uniforms), diag=diag, dev_status=status)
     torch.cuda.synchronize()
     return dict(tokens=tok.cpu().numpy(), count=cnt.cpu().numpy(), accepted=acc.cpu().numpy(),
-                path=pth.cpu().numpy(), diag=dg.cpu().numpy())
+                path=pth.cpu().numpy(), diag=dg.cpu().numpy() if diag else None)
 
 
 def close(a, b, rtol=RTOL, atol=1e-30):

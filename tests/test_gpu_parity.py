@@ -348,12 +348,69 @@ def c5():
     return synth.c5_tree()
 
 
+def _same_walk(a, b):
+    for key in ("tokens", "count", "accepted", "path"):
+        assert np.array_equal(a[key], b[key]), key
+
+
 def test_gpu_tree_c5_full(c5):
     say("tree B=32 N=60 V=128256 bf16 T=1")
     st = _status()
     got = run_tree(c5, status=st)
     want = _oracle_tree(c5)
     _check_tree(c5, got, want, "c5")
+    assert int(st.item()) == _or(want["flags"])
+    # the walk reads only visited rows and never the diagnostics' statistics:
+    # the same tokens with and without diagnostics, and on a repeat
+    say("tree c5 without diagnostics, twice")
+    _same_walk(run_tree(c5, diag=False), got)
+    _same_walk(run_tree(c5, diag=False), got)
+
+
+@pytest.mark.parametrize("B", [1, 3, 300])
+def test_gpu_tree_group_counts(B):
+    # the library splits a request over G = min(32, 256 // B, tiles) workgroups:
+    # B=1 -> 32, B=3 -> 32 (V=70000 has 35 tiles), B=300 -> 1
+    say(f"tree B={B} N=9 V=70000 (workgroups per request vary with B)")
+    ti = synth.c5_tree(B=B, N=9, V=70_000, top_children=2, expand_per_layer=2, max_depth=4,
+                       sigma=0.8, salt=B)
+    st = _status()
+    got = run_tree(ti, status=st, diag=False)
+    want = _oracle_tree(ti)
+    nb, bad = compare_tokens(got, want, keys=("tokens", "count", "accepted", "path"))
+    say(f"B={B}: {nb} boundary cases, mean kept {want['accepted'].mean():.2f}")
+    assert bad.size == 0, bad[:10]
+    assert nb <= max(2, 0.01 * B)
+    assert int(st.item()) == _or(want["flags"])
+
+
+def test_gpu_tree_nonfinite_rows():
+    say("tree non-finite rows: visited ones invalidate, unvisited ones do not")
+    ti = synth.c5_tree(B=40, N=10, V=4999, top_children=3, expand_per_layer=3, max_depth=3,
+                       sigma=1.5, salt=77)
+    base = _oracle_tree(ti)
+    N, V = ti.N, ti.V
+    rej = [b for b in range(ti.B) if base["accepted"][b] == 0 and base["count"][b] == 1]
+    assert len(rej) >= 5, rej          # requests whose root rejects every child
+    enc = lambda x, kind: synth.encode(np.array([x]), kind)[0]
+    tgt, dft = ti.target.copy(), ti.draft.copy()
+    r_t, r_unv, r_qnan, r_mix, r_pinf = rej[:5]
+    tgt[r_t * N, 17] = enc(np.nan, ti.t_kind)            # visited target row (root)
+    tgt[r_unv * N + N - 1, :] = enc(np.nan, ti.t_kind)   # a node the walk never reaches
+    dft[r_qnan * N, 4000] = enc(np.nan, ti.q_kind)       # root draft row, used by a residual
+    dft[r_mix * N, 5] = enc(np.inf, ti.q_kind)           # +inf and -inf in far apart slices
+    dft[r_mix * N, V - 3] = enc(-np.inf, ti.q_kind)
+    dft[r_pinf * N, 5] = enc(np.inf, ti.q_kind)          # +inf alone: zero residual weight there
+    bad_ti = synth.TreeInputs(ti.name, V, N, ti.t_kind, tgt, ti.q_kind, dft, ti.parent, ti.token,
+                              ti.depth, ti.T, ti.uniforms)
+    st = _status()
+    got = run_tree(bad_ti, status=st, diag=False)
+    with np.errstate(invalid="ignore", over="ignore"):
+        want = _oracle_tree(bad_ti)
+    nb, bad = compare_tokens(got, want, keys=("tokens", "count", "accepted", "path"))
+    assert bad.size == 0, bad
+    assert [int(want["count"][r]) for r in (r_t, r_qnan, r_mix)] == [0, 0, 0]
+    assert want["count"][r_unv] == 1 and want["count"][r_pinf] == 1
     assert int(st.item()) == _or(want["flags"])
 
 
