@@ -82,6 +82,8 @@ def verify_sample(target, t_kind, draft, q_kind, V, t_row_start, q_row_start,
 
     1. p_i = softmax(target row i / T) for i = 0..k (k+1 rows from one target
        forward) -- "投机解码:为什么一个字都不改", figure "一次目标前向验 k 个草稿 token".
+       The round reads rows 0..m (m below); a row it reads whose normaliser is
+       not finite and positive makes the request invalid (FLAG_NONFINITE).
     2. Draft i is kept with probability min(1, p_i(x_i) / q_i(x_i)): with the
        uniform u_i, kept iff u_i * q_i(x_i) < p_i(x_i); stop at the first draft
        that is not kept (m = its index, else m = k) -- same page, section
@@ -149,26 +151,33 @@ def verify_sample(target, t_kind, draft, q_kind, V, t_row_start, q_row_start,
         if budget is not None and k > budget:
             flags[b] |= FLAG_OVER_BUDGET
         stats = [target_dist(ts + i) for i in range(k + 1)]
-        if not all(np.isfinite(S) and S > 0 for (_, _, S) in stats):
-            flags[b] |= FLAG_NONFINITE
-            continue
         u = np.asarray(uniforms[b], dtype=np.float64)
         for i in range(k + 1):
             diag[b, i, 0], diag[b, i, 1] = stats[i][1], stats[i][2]
-        # position-by-position test, stopping at the first rejection
-        m = k
-        decided = False
         for i in range(k):
-            p_x = stats[i][0][x[i]]
-            q_x = widen(draft[qs + i, x[i]:x[i] + 1], q_kind)[0]
-            diag[b, i, 2], diag[b, i, 3] = p_x, q_x
-            if decided:
-                continue
-            keep = u[i] * q_x < p_x
+            diag[b, i, 2] = stats[i][0][x[i]]
+            diag[b, i, 3] = widen(draft[qs + i, x[i]:x[i] + 1], q_kind)[0]
+        # position-by-position test, stopping at the first rejection; the
+        # round reads target rows 0..m only, and a row it reads must have a
+        # finite, positive normaliser (rows after the break play no part)
+        m = k
+        finite = True
+        for i in range(k + 1):
+            S = stats[i][2]
+            if not (np.isfinite(S) and S > 0):
+                finite = False
+                break
+            if i == k:
+                break
+            p_x, q_x = diag[b, i, 2], diag[b, i, 3]
             margins[b, i] = abs(u[i] - p_x / q_x) if q_x > 0 else np.inf
-            if not keep:
+            if not u[i] * q_x < p_x:
                 m = i
-                decided = True
+                break
+        if not finite:
+            flags[b] |= FLAG_NONFINITE
+            margins[b] = np.nan
+            continue
         if m < k:
             if variant == "resample_from_p":
                 w, fl = stats[m][0], 0

@@ -325,6 +325,43 @@ def test_chain_as_tree_equals_chain():
     assert np.array_equal(out_c["accepted"], out_t["accepted"])
 
 
+def test_nonfinite_rows_count_only_where_read():
+    # A round reads target rows 0..m (m = first rejection, or k) and nothing
+    # after them ("改进" section: the round stops at the first draft that is not
+    # kept).  Hand case, V = 4, k = 2: row 0 keeps x_0 = 1 for certain
+    # (p >= q), row 1 rejects x_1 = 2 for certain (p = 0), row 2 is never read.
+    V, k = 4, 2
+    good = np.array([np.log(0.1), np.log(0.6), -np.inf, np.log(0.3)])
+    tgt = np.stack([good, good, good]).astype(np.float32)
+    dft = np.full((2, V), 0.25, dtype=np.float32)
+    ids = np.array([[1, 2]], dtype=np.int32)
+    u = np.array([[0.5, 0.5, 0.5]], dtype=np.float32)
+
+    def run(t):
+        with np.errstate(invalid="ignore"):
+            return oracle.verify_sample(t, "f32", dft, "f32", V, np.array([0]), np.array([0]), ids,
+                                        np.array([k]), k, 1.0, u)
+
+    ok = run(tgt)
+    assert (ok["accepted"][0], ok["count"][0], ok["flags"][0]) == (1, 2, 0)
+    t2 = tgt.copy()
+    t2[2, 0] = np.nan                       # after the break: no effect
+    out = run(t2)
+    assert out["flags"][0] == 0 and np.array_equal(out["tokens"], ok["tokens"])
+    for row in (0, 1):                      # read rows: the request is invalid
+        t3 = tgt.copy()
+        t3[row, 3] = np.nan
+        out = run(t3)
+        assert out["flags"][0] == oracle.FLAG_NONFINITE and out["count"][0] == 0
+    # the same rule as the tree walk, where only visited nodes' rows count
+    parent = np.array([[-1, 0, 1]], dtype=np.int32)
+    tok = np.array([[-1, 1, 2]], dtype=np.int32)
+    dft3 = np.concatenate([dft, np.zeros((1, V), np.float32)])
+    with np.errstate(invalid="ignore"):
+        tr = oracle.verify_tree(t2, "f32", dft3, "f32", V, parent, tok, 1.0, u)
+    assert tr["flags"][0] == 0 and np.array_equal(tr["tokens"], ok["tokens"])
+
+
 # ---------------------------------------------------------------------------
 # statistical exactness over 200,000 rounds (fixed prefix, V = 2048)
 # ---------------------------------------------------------------------------
