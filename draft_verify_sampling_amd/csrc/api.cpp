@@ -56,6 +56,47 @@ int cu_count() {
   return n;
 }
 
+
+// Shared tail of the sampled and tree verify: the split into G workgroups per
+// request, the workspace carve-up and the launches: the softmax partials of
+// every row first (chains always; trees only for the diagnostics), then the
+// walk.
+sv_status launch_walk_call(bool chain, int32_t t_dtype, int32_t q_dtype, sv::WalkArgs& a, int64_t rows,
+                           int64_t nodes, int64_t node_cap, void* workspace, hipStream_t st,
+                           const char* what) {
+  const int64_t ntiles = sv::sample_tiles(a.V);
+  const int64_t max_sync = sv::walk_max_sync(nodes);
+  const sv::WalkLayout L = sv::walk_layout(a.B, rows, a.V, chain ? sv::walk_max_sync(
+      std::min<int64_t>(rows, sv::kMaxChainRows)) : max_sync);
+  char* ws = static_cast<char*>(workspace);
+  // G from the occupancy at the largest slice this kernel may get
+  const size_t lds_max = sv::walk_lds_bytes(static_cast<int>(node_cap), static_cast<int>(ntiles));
+  const int occ = sv::walk_occupancy(chain, t_dtype, q_dtype, lds_max);
+  const int64_t resident = static_cast<int64_t>(occ) * std::max(cu_count(), 1);
+  a.G = std::min<int32_t>(sv::walk_groups(a.B, a.V, resident),
+                          static_cast<int32_t>(sv::walk_groups_bound(a.B)));
+  a.ntiles = static_cast<int32_t>(ntiles);
+  a.tile_cap = static_cast<int32_t>((ntiles + a.G - 1) / a.G);
+  a.node_cap = static_cast<int32_t>(node_cap);
+  a.max_sync = static_cast<int32_t>(max_sync);
+  a.spin_limit = sv::kSpinLimit;
+  a.slots = reinterpret_cast<uint64_t*>(ws + L.slots_off);
+  a.partial = reinterpret_cast<const float2*>(ws + L.partial_off);
+  if (static_cast<int64_t>(a.B) * a.G > kMaxGrid) return fail(SV_E_ARG, "too many requests");
+  (void)hipGetLastError();
+  const bool stats = chain || a.diag != nullptr;  // a chain walk reads every row's partials
+  const int64_t slot_words = a.G > 1 ? static_cast<int64_t>(a.B) * a.max_sync * 2 * a.G : 0;
+  if (stats) {  // the statistics kernel also zeroes the exchange words
+    const hipError_t e = sv::launch_row_stats(t_dtype, a.tgt, rows, a.V, a.nseg, a.c,
+                                              reinterpret_cast<float2*>(ws + L.partial_off), st,
+                                              a.slots, slot_words);
+    if (e != hipSuccess) return device_fail(e, what);
+  }
+  const size_t lds = sv::walk_lds_bytes(a.node_cap, a.tile_cap);
+  const hipError_t e = sv::launch_walk(chain, t_dtype, q_dtype, a, lds, !stats, st);
+  return e == hipSuccess ? SV_OK : device_fail(e, what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -81,9 +122,11 @@ size_t sv_workspace_bytes(int op, int64_t batch, int64_t total_rows, int64_t voc
     case SV_OP_GREEDY:
       return sv::align256(static_cast<size_t>(total_rows * sv::argmax_segments(total_rows, vocab)) * 8);
     case SV_OP_TREE:
-      return sv::tree_layout(batch, total_rows, vocab).bytes;
+      if (batch == 0) return 0;
+      return sv::walk_layout(batch, total_rows, vocab, sv::walk_max_sync(total_rows / batch)).bytes;
     case SV_OP_SAMPLE:
-      return sv::sample_layout(batch, total_rows, vocab).bytes;
+      return sv::walk_layout(batch, total_rows, vocab,
+                             sv::walk_max_sync(std::min<int64_t>(total_rows, sv::kMaxChainRows))).bytes;
     default:
       return 0;
   }
@@ -187,7 +230,7 @@ sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t
   if (!dtype_ok(t_dtype) || !dtype_ok(q_dtype))
     return fail(SV_E_DTYPE, "t_dtype and q_dtype must be SV_F32 or SV_BF16");
   if (batch < 0) return fail(SV_E_ARG, "batch < 0");
-  if (vocab < 1 || vocab > INT32_MAX) return fail(SV_E_ARG, "vocab must be in [1, 2^31)");
+  if (vocab < 1 || vocab > sv::kMaxSampleVocab) return fail(SV_E_ARG, "vocab must be in [1, 4194304]");
   if (k_max < 0 || k_max >= sv::kMaxChainRows) return fail(SV_E_ARG, "k_max must be in [0, 255]");
   if (t_rows < 0 || q_rows < 0) return fail(SV_E_ARG, "t_rows and q_rows must be >= 0");
   if (!(temperature > 0.f) || !std::isfinite(temperature))
@@ -200,48 +243,37 @@ sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t
       (q_rows > 0 && draft_probs == nullptr))
     return fail(SV_E_ARG, "null pointer argument");
   const int32_t nseg = sv::row_segments(t_rows, vocab);
-  const int64_t ntiles = sv::sample_tiles(vocab);
-  if (static_cast<int64_t>(t_rows) * nseg > kMaxGrid || static_cast<int64_t>(batch) * ntiles > kMaxGrid)
-    return fail(SV_E_ARG, "problem too large for one launch");
-  const sv::SampleLayout L = sv::sample_layout(batch, t_rows, vocab);
-  if (sv_status s = check_workspace(workspace, workspace_bytes, L.bytes)) return s;
+  if (static_cast<int64_t>(t_rows) * nseg > kMaxGrid) return fail(SV_E_ARG, "too many rows");
+  const size_t need = sv_workspace_bytes(SV_OP_SAMPLE, batch, t_rows, vocab);
+  if (sv_status s = check_workspace(workspace, workspace_bytes, need)) return s;
 
-  char* ws = static_cast<char*>(workspace);
-  const float c = sv::kLog2e / temperature;
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  (void)hipGetLastError();
-  float2* partial = reinterpret_cast<float2*>(ws + L.partial_off);
-  hipError_t e = sv::launch_row_stats(t_dtype, target_logits, t_rows, vocab, nseg, c, partial, st);
-  if (e != hipSuccess) return device_fail(e, "sv_verify_sample row-stats launch");
-  sv::SampleArgs a{};
+  sv::WalkArgs a{};
   a.tgt = target_logits;
   a.dq = draft_probs;
   a.V = vocab;
+  a.c = sv::kLog2e / temperature;
+  a.B = batch;
+  a.u = uniforms;
   a.t_rows = t_rows;
   a.q_rows = q_rows;
   a.t_rs = t_row_start;
   a.q_rs = q_row_start;
   a.ids = draft_ids;
   a.dlen = draft_len;
-  a.B = batch;
   a.k_max = k_max;
-  a.c = c;
-  a.u = uniforms;
   a.max_new = max_new;
   a.eos = eos_id;
+  a.resid = out_resid;
   a.out_tok = out_tokens;
   a.out_cnt = out_count;
   a.out_acc = out_accepted;
-  a.diag = out_diag;
-  a.resid = out_resid;
   a.status = dev_status;
-  a.partial = partial;
+  a.diag = out_diag;
   a.nseg = nseg;
-  a.tiles = reinterpret_cast<double*>(ws + L.tiles_off);
-  a.records = reinterpret_cast<int4*>(ws + L.records_off);
-  a.ntiles = static_cast<int32_t>(ntiles);
-  e = sv::launch_sample_resolve(t_dtype, q_dtype, a, st);
-  return e == hipSuccess ? SV_OK : device_fail(e, "sv_verify_sample resolve launch");
+  // a request has at most min(k_max + 1, t_rows) nodes
+  const int64_t nodes = std::min<int64_t>(k_max + 1, t_rows);
+  return launch_walk_call(true, t_dtype, q_dtype, a, t_rows, nodes, k_max + 1, workspace,
+                          static_cast<hipStream_t>(stream), "sv_verify_sample");
 }
 
 sv_status sv_verify_tree(const void* target_logits, int32_t t_dtype, const void* draft_probs,
@@ -255,8 +287,7 @@ sv_status sv_verify_tree(const void* target_logits, int32_t t_dtype, const void*
     return fail(SV_E_DTYPE, "t_dtype and q_dtype must be SV_F32 or SV_BF16");
   if (batch < 0) return fail(SV_E_ARG, "batch < 0");
   if (n_nodes < 1 || n_nodes > sv::kMaxTreeNodes) return fail(SV_E_ARG, "n_nodes must be in [1, 1024]");
-  if (vocab < 1 || vocab > static_cast<int64_t>(sv::kMaxTreeTiles) * sv::kSampleTile)
-    return fail(SV_E_ARG, "tree vocab must be in [1, 1048576]");
+  if (vocab < 1 || vocab > sv::kMaxSampleVocab) return fail(SV_E_ARG, "tree vocab must be in [1, 4194304]");
   if (!(temperature > 0.f) || !std::isfinite(temperature))
     return fail(SV_E_ARG, "temperature must be finite and > 0");
   if (batch == 0) return SV_OK;
@@ -271,42 +302,25 @@ sv_status sv_verify_tree(const void* target_logits, int32_t t_dtype, const void*
   const size_t need = sv_workspace_bytes(SV_OP_TREE, batch, rows, vocab);
   if (sv_status s = check_workspace(workspace, workspace_bytes, need)) return s;
 
-  const float c = sv::kLog2e / temperature;
-  const hipStream_t st = static_cast<hipStream_t>(stream);
-  const sv::TreeLayout L = sv::tree_layout(batch, rows, vocab);
-  char* ws = static_cast<char*>(workspace);
-  (void)hipGetLastError();
-  float2* partial = reinterpret_cast<float2*>(ws + L.partial_off);
-  hipError_t e = hipSuccess;
-  if (out_diag != nullptr) {  // the walk itself reads only the rows it visits
-    e = sv::launch_row_stats(t_dtype, target_logits, rows, vocab, nseg, c, partial, st);
-    if (e != hipSuccess) return device_fail(e, "sv_verify_tree row-stats launch");
-  }
-  sv::TreeArgs a{};
+  sv::WalkArgs a{};
   a.tgt = target_logits;
   a.dq = draft_probs;
   a.V = vocab;
+  a.c = sv::kLog2e / temperature;
+  a.B = batch;
+  a.u = uniforms;
   a.parent = parent;
   a.token = node_token;
-  a.B = batch;
   a.N = n_nodes;
-  a.c = c;
-  a.u = uniforms;
+  a.out_path = out_path;
   a.out_tok = out_tokens;
   a.out_cnt = out_count;
   a.out_acc = out_accepted;
-  a.out_path = out_path;
-  a.diag = out_diag;
   a.status = dev_status;
-  a.partial = partial;
+  a.diag = out_diag;
   a.nseg = nseg;
-  a.ntiles = static_cast<int32_t>(sv::sample_tiles(vocab));
-  a.G = std::min<int64_t>(sv::tree_groups(batch, vocab, cu_count()), sv::tree_groups_bound(batch));
-  a.slots = reinterpret_cast<uint64_t*>(ws + L.slots_off);
-  a.max_sync = static_cast<int32_t>(sv::tree_max_sync(n_nodes));
-  a.spin_limit = sv::kSpinLimit;
-  e = sv::launch_tree_walk(t_dtype, q_dtype, a, st);
-  return e == hipSuccess ? SV_OK : device_fail(e, "sv_verify_tree walk launch");
+  return launch_walk_call(false, t_dtype, q_dtype, a, rows, n_nodes, n_nodes, workspace,
+                          static_cast<hipStream_t>(stream), "sv_verify_tree");
 }
 
 }  // extern "C"

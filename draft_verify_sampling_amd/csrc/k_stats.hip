@@ -21,10 +21,17 @@ namespace sv {
 // One 8192-element chunk per block: every thread issues its U 16-byte loads
 // at once (lanes past the row's end read nothing and fold -inf), so each
 // block has its whole chunk in flight; NT selects non-temporal loads.
+//
+// `clear` (optional, n16 16-byte words) is zeroed on the side, for the exchange
+// words of the walk that follows this kernel on the stream.
 template <class D, bool NT>
 __global__ __launch_bounds__(kBlock) void k_row_stats(const void* __restrict__ rows, int64_t V,
                                                       int32_t nseg, float c,
-                                                      float2* __restrict__ partial) {
+                                                      float2* __restrict__ partial,
+                                                      uint4* __restrict__ clear, int64_t n16) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n16;
+       i += static_cast<int64_t>(gridDim.x) * kBlock)
+    clear[i] = uint4{0u, 0u, 0u, 0u};
   constexpr int U = kSegElems / (kBlock * D::kPerVec);
   constexpr int kSegVecs = kSegElems / D::kPerVec;
   __shared__ float sh[2 * (kBlock / kWave)];
@@ -92,12 +99,15 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(const void* __restrict__ r
 }
 
 hipError_t launch_row_stats(int dtype, const void* rows, int64_t n_rows, int64_t V, int32_t nseg,
-                            float c, float2* partial, hipStream_t stream) {
+                            float c, float2* partial, hipStream_t stream, uint64_t* clear,
+                            int64_t clear_words) {
   const dim3 grid(static_cast<uint32_t>(n_rows * nseg)), block(kBlock);
+  uint4* c16 = reinterpret_cast<uint4*>(clear);
+  const int64_t n16 = clear != nullptr ? (clear_words + 1) / 2 : 0;
   if (dtype == kDtypeBF16)
-    hipLaunchKernelGGL((k_row_stats<BF16, true>), grid, block, 0, stream, rows, V, nseg, c, partial);
+    hipLaunchKernelGGL((k_row_stats<BF16, true>), grid, block, 0, stream, rows, V, nseg, c, partial, c16, n16);
   else
-    hipLaunchKernelGGL((k_row_stats<F32, true>), grid, block, 0, stream, rows, V, nseg, c, partial);
+    hipLaunchKernelGGL((k_row_stats<F32, true>), grid, block, 0, stream, rows, V, nseg, c, partial, c16, n16);
   return hipGetLastError();
 }
 

@@ -1,0 +1,824 @@
+// Speculative-sampling verify as a walk: chain drafts and draft trees.
+//
+// Method ("投机解码:为什么一个字都不改", sections "改进:接受概率 min(1, p/q),
+// 拒绝时从残差重采" and "一轮能出几个 token"; "Speculative Decoding II", EAGLE
+// section, for trees verified by applying speculative sampling recursively as
+// SpecInfer does):
+//   cur = root, p = softmax(target row of cur / T), q = draft row of cur;
+//   for each child c of cur in index order: keep iff u * q(x_c) < p(x_c);
+//   kept -> emit x_c, descend, reload p and q; rejected -> p <- norm(max(0, p - q)).
+//   With no child kept (or at a leaf) the last token is drawn from the current
+//   p: the smallest id whose running mass exceeds u times the total.
+// A chain of k drafts is the tree whose node c (c = 0..k) has parent c - 1:
+// node c reads target row t_row_start + c and draft row q_row_start + c, draft
+// x_{c-1} is node c's token, and u[i] tests node i + 1 and u[k] draws, as in
+// the tree.  A chain has at most one rejection; a full accept draws the bonus
+// token from p_k.
+//
+// Repeated residual updates against one q stay in closed form: after j
+// rejections the current distribution is max(0, p - c_j q) / R_j with
+// c_0 = 0, R_0 = 1, c_{j+1} = c_j + R_j and R_{j+1} = sum max(0, p - c_{j+1} q),
+// so every rejection costs one pass over the node's two rows that yields
+// R_{j+1} and the per-tile sums the final inverse-CDF draw needs.
+//
+// Statistics: a chain takes every row's softmax pair from the statistics
+// kernel, which streams all k + 1 target rows at full HBM rate before the
+// walk; the walk then needs no pass before its one weight pass.  A tree walk
+// computes the statistics of a node when it arrives there (one pass over that
+// row), so only the rows of its kept path are read.
+//
+// Work split: G workgroups of 1024 threads per request, G chosen by the host
+// from the occupancy of this kernel so that the whole grid is resident at
+// once (one workgroup per CU: G = CUs / requests, at most 32).  Workgroup g owns a contiguous slice of the vocabulary's 2048-element
+// tiles; each pass (softmax pair of a target row, or a residual / plain weight
+// pass) covers only the slice.  The G partial results of a pass are exchanged
+// through 64-bit words in the workspace: each workgroup stores its words with
+// relaxed agent-scope atomic stores and reads the others' with relaxed
+// agent-scope atomic loads until all carry their valid bit.  The data travels
+// inside the atomic words, so no fence is needed; k_walk_clear zeroes the
+// words before the walk.  Every workgroup combines the G words in the same
+// order, so all of them take the same decisions.  The wait is bounded: on
+// expiry the workgroup sets the sync-timeout status bit and exits.  With G = 1
+// nothing is exchanged through memory.
+//
+// The last token is drawn by the workgroup whose slice holds u * R: one wave
+// scans the slice's tile sums (kept in LDS) and rescans the chosen tile.
+#include <algorithm>
+#include <mutex>
+
+#include "tiles.hpp"
+
+namespace sv {
+
+namespace {
+
+constexpr int kWalkWaves = kWalkBlock / kWave;
+constexpr int kMaxNodeGroups = kMaxTreeNodes / kWave;
+static_assert(2 * kMaxWalkGroups <= kWave, "one wave reads every exchanged word");
+static_assert(kMaxChainRows <= kWalkBlock, "one chain row per thread");
+constexpr int kPartStage = 2048;  // partials of a chain request staged in LDS
+
+constexpr uint64_t kValid = 1ull << 63;
+
+// ---- exchanged words (bit 63 set = written in this call) ----
+__device__ __forceinline__ uint64_t enc_ms(MS v) {
+  return (static_cast<uint64_t>(__float_as_uint(v.s) | 0x80000000u) << 32) | __float_as_uint(v.m);
+}
+__device__ __forceinline__ MS dec_ms(uint64_t w) {
+  return MS{__uint_as_float(static_cast<uint32_t>(w)),
+            __uint_as_float(static_cast<uint32_t>(w >> 32) & 0x7fffffffu)};
+}
+// A sum of non-negative terms (or NaN): its sign bit carries the valid bit.
+__device__ __forceinline__ uint64_t enc_sum(double x) {
+  if (isnan(x)) return 0xfff8000000000001ull;
+  return static_cast<uint64_t>(__double_as_longlong(x)) | kValid;
+}
+__device__ __forceinline__ double dec_sum(uint64_t w) {
+  return __longlong_as_double(static_cast<long long>(w & ~kValid));
+}
+// Class of a slice's draft-row sum: NaN, +inf, -inf.  The row's total is NaN
+// iff some slice is NaN or the slices hold both infinities.
+__device__ __forceinline__ uint64_t enc_qclass(double q) {
+  return kValid | (isnan(q) ? 1u : 0u) | (q == INFINITY ? 2u : 0u) | (q == -INFINITY ? 4u : 0u);
+}
+
+struct Walk {
+  const WalkArgs* a;
+  int b, g;
+  int lo, hi;       // this workgroup's tiles [lo, hi)
+  int nsync;        // exchanges so far (the same count in every workgroup)
+  uint64_t* s_x;    // LDS [2][2 * kMaxWalkGroups]
+  int* s_ok;        // LDS [2]
+};
+
+// Publish (w0, w1) and collect every workgroup's pair into the LDS words
+// [2h], [2h + 1] of the current buffer.  Returns false when the bounded wait
+// expired.  Ends with a block barrier.
+__device__ bool exchange(Walk& wk, uint64_t w0, uint64_t w1) {
+  const WalkArgs& a = *wk.a;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int buf = wk.nsync & 1;
+  uint64_t* x = wk.s_x + buf * 2 * kMaxWalkGroups;
+  if (a.G == 1) {
+    if (threadIdx.x == 0) {
+      x[0] = w0;
+      x[1] = w1;
+      wk.s_ok[buf] = 1;
+    }
+  } else if (wk.nsync >= a.max_sync) {  // more exchanges than a walk can need: never taken
+    if (threadIdx.x == 0) wk.s_ok[buf] = 0;
+  } else {
+    uint64_t* row = a.slots + (static_cast<int64_t>(wk.b) * a.max_sync + wk.nsync) * 2 * a.G;
+    if (threadIdx.x == 0) {
+      __hip_atomic_store(row + 2 * wk.g, w0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(row + 2 * wk.g + 1, w1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (threadIdx.x < kWave) {
+      const int n = 2 * a.G;
+      uint64_t v = 0;
+      int done = 0;
+      for (int it = 0; it < a.spin_limit; ++it) {
+        if (lane < n) v = __hip_atomic_load(row + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__all(lane >= n || (v & kValid) != 0)) {
+          done = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if (lane < n) x[lane] = v;
+      if (lane == 0) wk.s_ok[buf] = done;
+    }
+  }
+  ++wk.nsync;
+  __syncthreads();
+  return wk.s_ok[buf] != 0;
+}
+
+__device__ __forceinline__ const uint64_t* last_words(const Walk& wk) {
+  return wk.s_x + ((wk.nsync - 1) & 1) * 2 * kMaxWalkGroups;
+}
+
+// Softmax pair of a target row over the slice, combined across the request.
+template <class DT>
+__device__ bool row_stats(Walk& wk, const void* trow, MS* s_wms, MS& out) {
+  const WalkArgs& a = *wk.a;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  MS acc{-INFINITY, 0.f};
+  for (int t = wk.lo + wid; t < wk.hi; t += kWalkWaves) {
+    MS v, unused;
+    wave_tile_ms<DT, false>(trow, nullptr, a.V, a.c, t, v, unused);
+    acc = ms_combine(acc, v);
+  }
+  if (lane == 0) s_wms[wid] = acc;
+  __syncthreads();
+  MS r = s_wms[0];
+  for (int w = 1; w < kWalkWaves; ++w) r = ms_combine(r, s_wms[w]);
+  if (!exchange(wk, enc_ms(r), kValid)) return false;
+  const uint64_t* x = last_words(wk);
+  MS m = dec_ms(x[0]);
+  for (int h = 1; h < a.G; ++h) m = ms_combine(m, dec_ms(x[2 * h]));
+  out = m;
+  return true;
+}
+
+// One weight pass over the slice: per-tile weight sums into wt[] (slice-local
+// index); then, across the request, the total W and the NaN-ness of the draft
+// row's sum.  Every slice's total stays readable in the exchanged words until
+// the next exchange.
+template <class DT, class DQ>
+__device__ bool weight_pass(Walk& wk, const DrawRow& r, double* wt, double* s_wq, double& W, bool& qnan) {
+  const WalkArgs& a = *wk.a;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  double qw = 0.0;
+  for (int t = wk.lo + wid; t < wk.hi; t += kWalkWaves) {
+    double v[1][3];
+    wave_tile_sums<DT, DQ, 1>(r, a.V, t, 0, v);
+    if (lane == 0) wt[t - wk.lo] = v[0][0];
+    qw += v[0][2];
+  }
+  if (lane == 0) s_wq[wid] = qw;
+  __syncthreads();
+  int ta, tb;
+  lane_tiles(wk.hi - wk.lo, lane, ta, tb);
+  double w = 0.0;
+  for (int i = ta; i < tb; ++i) w += wt[i];
+  w = wave_total(w);
+  double q = s_wq[0];
+  for (int i = 1; i < kWalkWaves; ++i) q += s_wq[i];
+  if (!exchange(wk, enc_sum(w), enc_qclass(q))) return false;
+  const uint64_t* x = last_words(wk);
+  double tot = 0.0;
+  uint64_t cls = 0;
+  for (int h = 0; h < a.G; ++h) {
+    tot += dec_sum(x[2 * h]);
+    cls |= x[2 * h + 1];
+  }
+  W = tot;
+  qnan = (cls & 1u) || ((cls & 2u) && (cls & 4u));
+  return true;
+}
+
+// Outputs of an invalid request: every token slot -1, counts 0, status bits.
+// Threads [first, first + stride, ...) write.
+template <bool kChain>
+__device__ void walk_invalid(const WalkArgs& a, int b, int bits, int first, int stride) {
+  const int width = kChain ? a.k_max + 1 : a.N;
+  const int64_t o = static_cast<int64_t>(b) * width;
+  for (int c = first; c < width; c += stride) {
+    a.out_tok[o + c] = -1;
+    if (!kChain) a.out_path[o + c] = -1;
+  }
+  if (first == 0) {
+    a.out_cnt[b] = 0;
+    a.out_acc[b] = 0;
+    if (kChain && a.resid != nullptr) a.resid[b] = 0.f;
+    flag(a.status, bits);
+  }
+}
+
+}  // namespace
+
+template <bool kChain, class DT, class DQ>
+__global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ uint64_t s_kids[2][kMaxNodeGroups];
+  __shared__ uint64_t s_x[2][2 * kMaxWalkGroups];
+  __shared__ MS s_wms[kWalkWaves];
+  __shared__ double s_wq[kWalkWaves];
+  __shared__ int s_ok[2];
+  __shared__ int s_bad;
+  __shared__ float2 s_part[kChain ? kPartStage : 1];  // chain: partials of the request's rows
+
+  // dynamic LDS: tile sums [2][tile_cap] doubles, then node arrays [node_cap]
+  double* s_wt0 = reinterpret_cast<double*>(smem);
+  double* s_wt1 = s_wt0 + a.tile_cap;
+  int32_t* s_par = reinterpret_cast<int32_t*>(s_wt1 + a.tile_cap);
+  int32_t* s_tok = s_par + a.node_cap;
+  int32_t* s_path = s_tok + a.node_cap;
+  float* s_px = reinterpret_cast<float*>(s_path + a.node_cap);
+  float* s_qx = s_px + a.node_cap;
+  float* s_u = s_qx + a.node_cap;
+  float* s_m = s_u + a.node_cap;     // chain: softmax pair of every row, from the partials
+  float* s_S = s_m + a.node_cap;
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  Walk wk{&a, static_cast<int>(blockIdx.x) / a.G, static_cast<int>(blockIdx.x) % a.G, 0, 0, 0,
+          &s_x[0][0], s_ok};
+  wk.lo = static_cast<int>(static_cast<int64_t>(wk.g) * a.ntiles / a.G);
+  wk.hi = static_cast<int>(static_cast<int64_t>(wk.g + 1) * a.ntiles / a.G);
+  const int b = wk.b;
+  const int64_t V = a.V;
+
+  // ---- the request: its nodes, rows and uniforms ----
+  int N;                   // nodes (chain: k_b + 1)
+  int64_t trow0, qrow0;    // node c reads target row trow0 + c and draft row qrow0 + c
+  int extra = 0;           // status bits that do not invalidate
+  if (tid == 0) s_bad = 0;
+  if constexpr (kChain) {
+    // round 1: the request's row starts and draft count, its drafted tokens
+    // and its uniforms (their addresses depend on b only)
+    const int k = a.dlen[b];
+    const int ts = a.t_rs[b], qs = a.q_rs[b];
+    const int tokv = tid < a.k_max ? a.ids[static_cast<int64_t>(b) * a.k_max + tid] : -1;
+    const float uv = tid <= a.k_max ? a.u[static_cast<int64_t>(b) * (a.k_max + 1) + tid] : 0.f;
+    if (k < 0 || k > a.k_max || ts < 0 || static_cast<int64_t>(ts) + k >= a.t_rows ||
+        (k > 0 && (qs < 0 || static_cast<int64_t>(qs) + k > a.q_rows))) {
+      if (wk.g == 0) walk_invalid<kChain>(a, b, kFlagBadRequest, tid, kWalkBlock);
+      return;
+    }
+    N = k + 1;
+    trow0 = ts;
+    qrow0 = qs;
+    if (a.max_new != nullptr && k > a.max_new[b]) extra = kFlagOverBudget;
+    __syncthreads();
+    // node c = draft c - 1 (parent c - 1); thread i holds draft i
+    const bool tok_ok = tokv >= 0 && tokv < V;
+    if (tid < N) {
+      s_par[tid] = tid - 1;
+      s_u[tid] = uv;
+    }
+    if (tid == 0) s_tok[0] = -1;
+    if (tid < k) {
+      s_tok[tid + 1] = tokv;
+      if (!tok_ok) atomicOr(&s_bad, kFlagBadToken);
+    }
+    // round 2: every row's softmax partials (staged in LDS) and the target
+    // logit / draft probability at each drafted token
+    const int np = N * a.nseg;
+    const float2* pbase = a.partial + trow0 * a.nseg;
+    const bool staged = np <= kPartStage;
+    if (staged)
+      for (int i = tid; i < np; i += kWalkBlock) s_part[i] = pbase[i];
+    float lx = 0.f, qv = 0.f;
+    if (tid < k && tok_ok) {
+      lx = DT::at(row_ptr<DT>(a.tgt, trow0 + tid, V), tokv);
+      qv = DQ::at(row_ptr<DQ>(a.dq, qrow0 + tid, V), tokv);
+    }
+    __syncthreads();
+    if (const int bad = s_bad) {
+      if (wk.g == 0) walk_invalid<kChain>(a, b, bad, tid, kWalkBlock);
+      return;
+    }
+    if (tid < N) {
+      const float2* pp = staged ? s_part + tid * a.nseg : pbase + static_cast<int64_t>(tid) * a.nseg;
+      MS acc{-INFINITY, 0.f};
+      for (int sg = 0; sg < a.nseg; ++sg) {
+        const float2 v = pp[sg];
+        acc = ms_combine(acc, MS{v.x, v.y});
+      }
+      s_m[tid] = acc.m;
+      s_S[tid] = acc.s;
+    }
+    __syncthreads();
+    if (tid < k) {  // node tid + 1 is tested against row tid (its parent)
+      s_px[tid + 1] = ex2(fmaf(lx, a.c, -s_m[tid])) * (1.f / s_S[tid]);
+      s_qx[tid + 1] = qv;
+    }
+  } else {
+    // round 1: the tree and the uniforms
+    N = a.N;
+    trow0 = qrow0 = static_cast<int64_t>(b) * a.N;
+    __syncthreads();
+    for (int c = tid; c < N; c += kWalkBlock) {
+      const int par = a.parent[trow0 + c];
+      const int tok = a.token[trow0 + c];
+      int bad = 0;
+      if (c == 0 ? par != -1 : (par < 0 || par >= c)) bad |= kFlagBadTree;
+      if (c > 0 && (tok < 0 || tok >= V)) bad |= kFlagBadToken;
+      if (bad) atomicOr(&s_bad, bad);
+      s_par[c] = par;
+      s_tok[c] = tok;
+      s_u[c] = a.u[trow0 + c];
+    }
+    __syncthreads();
+    if (const int bad = s_bad) {
+      if (wk.g == 0) walk_invalid<kChain>(a, b, (bad & kFlagBadTree) ? kFlagBadTree : bad, tid, kWalkBlock);
+      return;
+    }
+  }
+
+  // ---- the walk ----
+  constexpr int kNodesPerThread = kMaxTreeNodes / kWalkBlock;
+  const int ngroups = (N + kWave - 1) / kWave;
+  int n_emit = 0, fallback = 0, step = 0, npass = 0, tiles_buf = -1;
+  int cur = 0;
+  bool ok = true, synced = true;
+  float coef = 0.f, R = 1.f;
+  double Rd = 1.0;
+  MS st{0.f, 0.f};
+  while (true) {
+    // children of cur (one bit mask per 64 nodes, index order), and the target
+    // logit / draft probability at their tokens, in flight during the pass
+    for (int gi = wid; gi < ngroups; gi += kWalkWaves) {
+      const int c = gi * kWave + lane;
+      const uint64_t km = __ballot(c < N && c > 0 && s_par[c] == cur);
+      if (lane == 0) s_kids[step & 1][gi] = km;
+    }
+    const void* trow = row_ptr<DT>(a.tgt, trow0 + cur, V);
+    const void* qrow = row_ptr<DQ>(a.dq, qrow0 + cur, V);
+    if constexpr (kChain) {
+      st = MS{s_m[cur], s_S[cur]};
+      ok = st.s > 0.f && st.s < INFINITY;
+      if (!ok) break;
+    } else {
+      float lx[kNodesPerThread], qv[kNodesPerThread];
+#pragma unroll
+      for (int j = 0; j < kNodesPerThread; ++j) {
+        const int c = tid + j * kWalkBlock;
+        lx[j] = qv[j] = 0.f;
+        if (c < N && c > 0 && s_par[c] == cur) {
+          lx[j] = DT::at(trow, s_tok[c]);
+          qv[j] = DQ::at(qrow, s_tok[c]);
+        }
+      }
+      if (!row_stats<DT>(wk, trow, s_wms, st)) {
+        synced = false;
+        break;
+      }
+      ok = st.s > 0.f && st.s < INFINITY;
+      if (!ok) break;
+      const float invS = 1.f / st.s;
+#pragma unroll
+      for (int j = 0; j < kNodesPerThread; ++j) {
+        const int c = tid + j * kWalkBlock;
+        if (c < N && c > 0 && s_par[c] == cur) {
+          s_px[c] = ex2(fmaf(lx[j], a.c, -st.m)) * invS;
+          s_qx[c] = qv[j];
+        }
+      }
+    }
+    const float invS = 1.f / st.s;
+    __syncthreads();
+    const DrawRow base{trow, qrow, a.c, st.m, invS, 0.f, false};
+    int kept = -1;
+    for (int gi = 0; gi < ngroups && kept < 0 && ok && synced; ++gi) {
+      uint64_t m = s_kids[step & 1][gi];
+      while (m != 0 && ok && synced) {
+        const int ch = gi * kWave + __ffsll(static_cast<long long>(m)) - 1;
+        m &= m - 1;
+        const float p = s_px[ch], q = s_qx[ch];
+        const float pc = coef == 0.f ? p : fmaxf(p - coef * q, 0.f) / R;
+        if (s_u[ch - 1] * q < pc) {
+          kept = ch;
+          break;
+        }
+        // rejected: residual pass with the next coefficient
+        DrawRow rr = base;
+        rr.coef = coef + R;
+        rr.use_q = true;
+        const int nb = npass & 1;
+        ++npass;
+        double W;
+        bool qnan;
+        if (!weight_pass<DT, DQ>(wk, rr, nb ? s_wt1 : s_wt0, s_wq, W, qnan)) {
+          synced = false;
+        } else if (qnan || !isfinite(W)) {
+          ok = false;
+        } else if (W > 0.0) {
+          coef = rr.coef;
+          R = static_cast<float>(W);
+          Rd = W;
+          tiles_buf = nb;
+        } else {  // no residual mass: keep the current distribution
+          fallback = kFlagFallback;
+          tiles_buf = -1;
+        }
+      }
+    }
+    if (!ok || !synced || kept < 0) break;
+    if (tid == 0) s_path[n_emit] = kept;
+    ++n_emit;
+    ++step;
+    cur = kept;
+    coef = 0.f;
+    R = 1.f;
+    Rd = 1.0;
+    tiles_buf = -1;
+  }
+  if (!synced) {
+    if (tid == 0) flag(a.status, kFlagSyncTimeout);
+    return;
+  }
+  if (!ok) {
+    if (wk.g == 0) walk_invalid<kChain>(a, b, kFlagNonfinite | fallback | extra, tid, kWalkBlock);
+    return;
+  }
+
+  // ---- the last token, from the current distribution ----
+  const DrawRow row{row_ptr<DT>(a.tgt, trow0 + cur, V), row_ptr<DQ>(a.dq, qrow0 + cur, V), a.c,
+                    st.m, 1.f / st.s, coef, coef != 0.f};
+  if (tiles_buf < 0) {
+    tiles_buf = npass & 1;
+    bool qnan;
+    if (!weight_pass<DT, DQ>(wk, row, tiles_buf ? s_wt1 : s_wt0, s_wq, Rd, qnan)) {
+      if (tid == 0) flag(a.status, kFlagSyncTimeout);
+      return;
+    }
+  }
+  const double target = static_cast<double>(s_u[N - 1]) * Rd;
+  // the slice holding the target: the first with weight whose running sum
+  // exceeds it, else the last slice with weight (the slice totals are the
+  // words of the last exchange, the weight pass of the current distribution)
+  const uint64_t* sw = last_words(wk);
+  int gs = -1, glast = -1;
+  double base_s = 0.0, run = 0.0, base_last = 0.0;
+  for (int h = 0; h < a.G; ++h) {
+    const double w = dec_sum(sw[2 * h]);
+    if (w > 0.0) {
+      if (gs < 0 && run + w > target) {
+        gs = h;
+        base_s = run;
+      }
+      glast = h;
+      base_last = run;
+    }
+    run += w;
+  }
+  if (gs < 0) {
+    gs = glast;
+    base_s = base_last;
+  }
+  if (gs < 0) {  // no mass anywhere: cannot happen with S > 0; defined output
+    if (wk.g == 0) walk_invalid<kChain>(a, b, kFlagNonfinite | fallback | extra, tid, kWalkBlock);
+    return;
+  }
+  if (wk.g != gs || wid != 0) return;
+  const double* wt = tiles_buf ? s_wt1 : s_wt0;
+  const int nsl = wk.hi - wk.lo;
+  int ta, tb;
+  lane_tiles(nsl, lane, ta, tb);
+  double own = 0.0;
+  for (int i = ta; i < tb; ++i) own += wt[i];
+  TileHit h;
+  if (!wave_find_tile(wt, 1, nsl, own, target - base_s, h)) {
+    walk_invalid<kChain>(a, b, kFlagNonfinite | fallback | extra, lane, kWave);
+    return;
+  }
+  h.tile += wk.lo;
+  h.base += base_s;
+  const int y = wave_pick_in_tile<DT, DQ>(row, V, h, target);
+  if constexpr (kChain) {
+    if (lane == 0) {
+      const int width = a.k_max + 1;
+      int32_t* out = a.out_tok + static_cast<int64_t>(b) * width;
+      int cnt = 0;
+      bool stop = false;
+      for (int i = 0; i < n_emit && !stop; ++i) {
+        const int32_t tok = s_tok[i + 1];
+        out[cnt++] = tok;
+        if (a.eos >= 0 && tok == a.eos) stop = true;
+      }
+      if (!stop) out[cnt++] = y;
+      if (a.max_new != nullptr) {
+        const int budget = a.max_new[b] > 0 ? a.max_new[b] : 0;
+        if (cnt > budget) cnt = budget;
+      }
+      for (int i = cnt; i < width; ++i) out[i] = -1;
+      a.out_cnt[b] = cnt;
+      a.out_acc[b] = n_emit;
+      if (a.resid != nullptr) a.resid[b] = static_cast<float>(Rd);
+      flag(a.status, fallback | extra);
+    }
+  } else {
+    const int64_t o = static_cast<int64_t>(b) * N;
+    for (int i = lane; i < N; i += kWave) {
+      a.out_tok[o + i] = i < n_emit ? s_tok[s_path[i]] : (i == n_emit ? y : -1);
+      a.out_path[o + i] = i < n_emit ? s_path[i] : -1;
+    }
+    if (lane == 0) {
+      a.out_cnt[b] = n_emit + 1;
+      a.out_acc[b] = n_emit;
+      flag(a.status, fallback);
+    }
+  }
+}
+
+// Chains whose vocabulary is one tile (V <= 2048): one wave per request does
+// the whole round with wave scans and ballots, no LDS and no barriers.  Lane
+// i holds draft i and row i: softmax pair (one segment), p_i(x_i), q_i(x_i)
+// and u_i.  Same decisions and draw as k_walk.
+template <class DT, class DQ>
+__global__ __launch_bounds__(kBlock) void k_walk_small(WalkArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t b = static_cast<int64_t>(blockIdx.x) * (kBlock / kWave) + threadIdx.x / kWave;
+  if (b >= a.B) return;
+  const int64_t V = a.V;
+  const int width = a.k_max + 1;
+  auto invalid = [&](int bits) {
+    for (int i = lane; i < width; i += kWave) a.out_tok[b * width + i] = -1;
+    if (lane == 0) {
+      a.out_cnt[b] = 0;
+      a.out_acc[b] = 0;
+      if (a.resid != nullptr) a.resid[b] = 0.f;
+      flag(a.status, bits);
+    }
+  };
+  const int k = a.dlen[b];
+  const int ts = a.t_rs[b], qs = a.q_rs[b];
+  if (k < 0 || k > a.k_max || ts < 0 || static_cast<int64_t>(ts) + k >= a.t_rows ||
+      (k > 0 && (qs < 0 || static_cast<int64_t>(qs) + k > a.q_rows))) {
+    invalid(kFlagBadRequest);
+    return;
+  }
+  const int extra = (a.max_new != nullptr && k > a.max_new[b]) ? kFlagOverBudget : 0;
+  // rows are handled kWave at a time (k_max < 256); every drafted token is
+  // checked, also those after the break
+  int m = k;               // first draft not kept
+  bool bad_tok = false, nonfinite = false;
+  for (int i0 = kWave; i0 < k; i0 += kWave) {
+    const int i = i0 + lane;
+    const int x = i < k ? a.ids[b * a.k_max + i] : 0;
+    if (__ballot(i < k && (x < 0 || x >= V))) bad_tok = true;
+  }
+  float Mm = 0.f, Sm = 1.f;
+  for (int i0 = 0; i0 <= k; i0 += kWave) {
+    const int i = i0 + lane;
+    const bool row = i <= k, draft = i < k;
+    const int x = draft ? a.ids[b * a.k_max + i] : 0;
+    const bool xin = x >= 0 && x < V;
+    if (__ballot(draft && !xin)) bad_tok = true;
+    const float u = row ? a.u[b * width + i] : 0.f;
+    float2 ms = make_float2(-INFINITY, 0.f);
+    float lx = 0.f, qx = 0.f;
+    if (row) ms = a.partial[static_cast<int64_t>(ts + i) * a.nseg];
+    if (draft && xin) {
+      lx = DT::at(row_ptr<DT>(a.tgt, ts + i, V), x);
+      qx = DQ::at(row_ptr<DQ>(a.dq, qs + i, V), x);
+    }
+    if (bad_tok) continue;
+    const bool fin = ms.y > 0.f && ms.y < INFINITY;
+    const float p = ex2(fmaf(lx, a.c, -ms.x)) * (1.f / ms.y);
+    // stop at the first row that is not finite or whose draft is not kept
+    const bool stop = row && (!fin || (draft && !(u * qx < p)) || i == k);
+    const uint64_t st = __ballot(stop);
+    if (st == 0) continue;
+    const int j = __ffsll(static_cast<long long>(st)) - 1;
+    const int ij = i0 + j;
+    const int fin_j = __shfl(fin ? 1 : 0, j, kWave);
+    if (!fin_j) {
+      nonfinite = true;
+    } else {
+      m = ij;
+      Mm = __shfl(ms.x, j, kWave);
+      Sm = __shfl(ms.y, j, kWave);
+    }
+    break;
+  }
+  if (bad_tok) {
+    invalid(kFlagBadToken);
+    return;
+  }
+  if (nonfinite) {
+    invalid(kFlagNonfinite | extra);
+    return;
+  }
+  // the last token: residual max(0, p_m - q_m) after a rejection, else p_k
+  const bool resid = m < k;
+  DrawRow row{row_ptr<DT>(a.tgt, ts + m, V), resid ? row_ptr<DQ>(a.dq, qs + m, V) : nullptr, a.c, Mm,
+              1.f / Sm, 1.f, resid};
+  double v[1][3];
+  wave_tile_sums<DT, DQ, 1>(row, V, 0, 0, v);
+  int bits = extra;
+  double total = v[0][0];
+  if (resid) {
+    if (isnan(v[0][2]) || !isfinite(v[0][0])) {
+      invalid(kFlagNonfinite | extra);
+      return;
+    }
+    if (!(v[0][0] > 0.0)) {  // no residual mass: draw from p_m
+      bits |= kFlagFallback;
+      row.use_q = false;
+      total = v[0][1];
+    }
+  }
+  const double target = static_cast<double>(a.u[b * width + k]) * total;
+  const TileHit h{0, 0.0, false};
+  const int y = wave_pick_in_tile<DT, DQ>(row, V, h, target);
+  if (lane == 0) {
+    int32_t* out = a.out_tok + b * width;
+    int cnt = 0;
+    bool stop = false;
+    for (int i = 0; i < m && !stop; ++i) {
+      const int32_t tok = a.ids[b * a.k_max + i];
+      out[cnt++] = tok;
+      if (a.eos >= 0 && tok == a.eos) stop = true;
+    }
+    if (!stop) out[cnt++] = y;
+    if (a.max_new != nullptr) {
+      const int budget = a.max_new[b] > 0 ? a.max_new[b] : 0;
+      if (cnt > budget) cnt = budget;
+    }
+    for (int i = cnt; i < width; ++i) out[i] = -1;
+    a.out_cnt[b] = cnt;
+    a.out_acc[b] = m;
+    if (a.resid != nullptr) a.resid[b] = static_cast<float>(total);
+    flag(a.status, bits);
+  }
+}
+
+// Zero the exchange words before the walk.
+__global__ __launch_bounds__(kBlock) void k_walk_clear(uint4* w, int64_t n16) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n16;
+       i += static_cast<int64_t>(gridDim.x) * kBlock)
+    w[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+// ---- diagnostics (only when asked for), from the softmax partials of every row ----
+
+// Tree: (M_c, S_c, p_parent(x_c), q_parent(x_c)), p being the parent's softmax
+// before any residual update.  One block per request, one node per thread.
+template <class DT, class DQ>
+__global__ __launch_bounds__(kMaxTreeNodes) void k_tree_diag(WalkArgs a) {
+  __shared__ float s_m[kMaxTreeNodes], s_S[kMaxTreeNodes];
+  const int b = blockIdx.x, c = threadIdx.x;
+  const int64_t row0 = static_cast<int64_t>(b) * a.N;
+  const bool mine = c < a.N;
+  int par = -1, tok = 0;
+  float lx = 0.f, qx = 0.f;
+  if (mine) {
+    par = a.parent[row0 + c];
+    tok = a.token[row0 + c];
+  }
+  const bool edge = mine && c > 0 && par >= 0 && par < c && tok >= 0 && tok < a.V;
+  if (edge) {
+    lx = DT::at(row_ptr<DT>(a.tgt, row0 + par, a.V), tok);
+    qx = DQ::at(row_ptr<DQ>(a.dq, row0 + par, a.V), tok);
+  }
+  MS st{-INFINITY, 0.f};
+  if (mine) {
+    const float2* pp = a.partial + (row0 + c) * a.nseg;
+#pragma unroll 8
+    for (int s = 0; s < a.nseg; ++s) {
+      const float2 v = pp[s];
+      st = ms_combine(st, MS{v.x, v.y});
+    }
+    s_m[c] = st.m;
+    s_S[c] = st.s;
+  }
+  __syncthreads();
+  if (mine) {
+    float* d = a.diag + (row0 + c) * 4;
+    d[0] = st.m * kLn2;
+    d[1] = st.s;
+    d[2] = edge ? ex2(fmaf(lx, a.c, -s_m[par])) * (1.f / s_S[par]) : 0.f;
+    d[3] = edge ? qx : 0.f;
+  }
+}
+
+// Chain: (M_i, S_i, p_i(x_i), q_i(x_i)) for i <= k_b (p, q = 0 at i = k_b),
+// for requests whose rows and tokens are in range.  One block per request,
+// one position per thread.
+template <class DT, class DQ>
+__global__ __launch_bounds__(kWalkBlock) void k_chain_diag(WalkArgs a) {
+  __shared__ int s_bad;
+  const int b = blockIdx.x, i = threadIdx.x;
+  const int k = a.dlen[b], ts = a.t_rs[b], qs = a.q_rs[b];
+  if (k < 0 || k > a.k_max || ts < 0 || static_cast<int64_t>(ts) + k >= a.t_rows ||
+      (k > 0 && (qs < 0 || static_cast<int64_t>(qs) + k > a.q_rows)))
+    return;
+  if (i == 0) s_bad = 0;
+  __syncthreads();
+  const int x = i < k ? a.ids[static_cast<int64_t>(b) * a.k_max + i] : 0;
+  if (i < k && (x < 0 || x >= a.V)) atomicOr(&s_bad, 1);
+  __syncthreads();
+  if (s_bad || i > k) return;
+  const float2* pp = a.partial + (static_cast<int64_t>(ts) + i) * a.nseg;
+  MS st{-INFINITY, 0.f};
+  for (int s = 0; s < a.nseg; ++s) {
+    const float2 v = pp[s];
+    st = ms_combine(st, MS{v.x, v.y});
+  }
+  float* d = a.diag + (static_cast<int64_t>(b) * (a.k_max + 1) + i) * 4;
+  d[0] = st.m * kLn2;
+  d[1] = st.s;
+  d[2] = i < k ? ex2(fmaf(DT::at(row_ptr<DT>(a.tgt, ts + i, a.V), x), a.c, -st.m)) * (1.f / st.s) : 0.f;
+  d[3] = i < k ? DQ::at(row_ptr<DQ>(a.dq, qs + i, a.V), x) : 0.f;
+}
+
+// ---- host side ----
+
+namespace {
+
+template <bool kChain, class DT, class DQ>
+const void* walk_fn() {
+  return reinterpret_cast<const void*>(&k_walk<kChain, DT, DQ>);
+}
+
+const void* pick_walk(bool chain, int t_dtype, int q_dtype) {
+  const bool tb = t_dtype == kDtypeBF16, qb = q_dtype == kDtypeBF16;
+  if (chain) {
+    if (tb && qb) return walk_fn<true, BF16, BF16>();
+    if (tb) return walk_fn<true, BF16, F32>();
+    if (qb) return walk_fn<true, F32, BF16>();
+    return walk_fn<true, F32, F32>();
+  }
+  if (tb && qb) return walk_fn<false, BF16, BF16>();
+  if (tb) return walk_fn<false, BF16, F32>();
+  if (qb) return walk_fn<false, F32, BF16>();
+  return walk_fn<false, F32, F32>();
+}
+
+template <bool kChain, class DT, class DQ>
+void launch_t(const WalkArgs& a, size_t lds, bool clear_slots, hipStream_t stream) {
+  if (a.diag != nullptr) {
+    if (kChain)
+      hipLaunchKernelGGL((k_chain_diag<DT, DQ>), dim3(static_cast<uint32_t>(a.B)), dim3(kWalkBlock), 0, stream, a);
+    else
+      hipLaunchKernelGGL((k_tree_diag<DT, DQ>), dim3(static_cast<uint32_t>(a.B)), dim3(kMaxTreeNodes), 0, stream, a);
+  }
+  if (a.G > 1 && clear_slots) {
+    const int64_t n16 = (static_cast<int64_t>(a.B) * a.max_sync * 2 * a.G + 1) / 2;
+    const int64_t blocks = std::min<int64_t>((n16 + kBlock - 1) / kBlock, 2048);
+    hipLaunchKernelGGL(k_walk_clear, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream,
+                       reinterpret_cast<uint4*>(a.slots), n16);
+  }
+  if (kChain && a.ntiles == 1) {
+    const int64_t blocks = (static_cast<int64_t>(a.B) + kBlock / kWave - 1) / (kBlock / kWave);
+    hipLaunchKernelGGL((k_walk_small<DT, DQ>), dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream, a);
+    return;
+  }
+  hipLaunchKernelGGL((k_walk<kChain, DT, DQ>), dim3(static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.G)),
+                     dim3(kWalkBlock), lds, stream, a);
+}
+
+}  // namespace
+
+size_t walk_lds_bytes(int node_cap, int tile_cap) {
+  return static_cast<size_t>(tile_cap) * 2 * sizeof(double) + static_cast<size_t>(node_cap) * 8 * 4;
+}
+
+int walk_occupancy(bool chain, int t_dtype, int q_dtype, size_t lds) {
+  static std::mutex mu;
+  static int cache[2][2][2][9] = {};  // by chain, dtypes, lds bucket of 8 KB
+  const size_t bucket = std::min<size_t>(lds / 8192, 8);
+  const size_t lds_key = (bucket + 1) * 8192;
+  std::lock_guard<std::mutex> lock(mu);
+  int& slot = cache[chain][t_dtype == kDtypeBF16][q_dtype == kDtypeBF16][bucket];
+  if (slot == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick_walk(chain, t_dtype, q_dtype), kWalkBlock,
+                                                     lds_key) != hipSuccess)
+      n = 1;
+    slot = n < 1 ? 1 : n;
+  }
+  return slot;
+}
+
+hipError_t launch_walk(bool chain, int t_dtype, int q_dtype, const WalkArgs& a, size_t lds,
+                       bool clear_slots, hipStream_t stream) {
+  const bool tb = t_dtype == kDtypeBF16, qb = q_dtype == kDtypeBF16;
+  if (chain) {
+    if (tb && qb) launch_t<true, BF16, BF16>(a, lds, clear_slots, stream);
+    else if (tb) launch_t<true, BF16, F32>(a, lds, clear_slots, stream);
+    else if (qb) launch_t<true, F32, BF16>(a, lds, clear_slots, stream);
+    else launch_t<true, F32, F32>(a, lds, clear_slots, stream);
+  } else {
+    if (tb && qb) launch_t<false, BF16, BF16>(a, lds, clear_slots, stream);
+    else if (tb) launch_t<false, BF16, F32>(a, lds, clear_slots, stream);
+    else if (qb) launch_t<false, F32, BF16>(a, lds, clear_slots, stream);
+    else launch_t<false, F32, F32>(a, lds, clear_slots, stream);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sv

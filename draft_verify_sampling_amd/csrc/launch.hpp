@@ -40,90 +40,103 @@ inline int32_t argmax_segments(int64_t rows, int64_t V) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// The sampled verify's inverse-CDF unit: one wave sums one tile.
+// The inverse-CDF unit of the sampled verify: one wave sums one tile.
 constexpr int kSampleTile = 2048;
 inline int64_t sample_tiles(int64_t V) { return (V + kSampleTile - 1) / kSampleTile; }
-constexpr int kMaxTreeTiles = 512;     // tree vocab <= 512 * 2048
+constexpr int64_t kMaxSampleVocab = 4194304;   // 2048 tiles: their sums fit in LDS
 
-// Tree walk: workgroups per request (G) and the exchange words between them.
-constexpr int kMaxTreeGroups = 32;
-constexpr int kCoopBlocks = 256;       // B * G never exceeds this (nor the device's CU count)
-constexpr int kSpinLimit = 1 << 20;    // polls of one exchange before giving up
+// The walk (chain and tree verify): G workgroups of kWalkBlock threads per
+// request, each owning a slice of the tiles, exchanging 64-bit words.
+constexpr int kWalkBlock = 1024;
+constexpr int kMaxWalkGroups = 32;
+constexpr int64_t kMaxCoopBlocks = 2048;       // B * G never exceeds this
+constexpr int kSpinLimit = 1 << 20;            // polls of one exchange before giving up
 
-inline int32_t tree_groups(int64_t B, int64_t V, int cu_count) {
-  const int64_t cap = cu_count < kCoopBlocks ? cu_count : kCoopBlocks;
-  int64_t g = B > 0 ? cap / B : 1;
+// G for a call: as many as keep every workgroup of the grid resident
+// (occupancy per CU times the CU count), at most one per tile and 32.
+inline int32_t walk_groups(int64_t B, int64_t V, int64_t resident) {
+  if (resident > kMaxCoopBlocks) resident = kMaxCoopBlocks;
+  int64_t g = B > 0 ? resident / B : 1;
   const int64_t nt = sample_tiles(V);
-  if (g > kMaxTreeGroups) g = kMaxTreeGroups;
+  if (g > kMaxWalkGroups) g = kMaxWalkGroups;
   if (g > nt) g = nt;
   return static_cast<int32_t>(g < 1 ? 1 : g);
 }
 
 // Upper bound of G over devices (the workspace query knows no device).
-inline int64_t tree_groups_bound(int64_t B) {
-  int64_t g = B > 0 ? kCoopBlocks / B : 1;
-  if (g > kMaxTreeGroups) g = kMaxTreeGroups;
+inline int64_t walk_groups_bound(int64_t B) {
+  int64_t g = B > 0 ? kMaxCoopBlocks / B : 1;
+  if (g > kMaxWalkGroups) g = kMaxWalkGroups;
   return g < 1 ? 1 : g;
 }
 
-// At most one exchange per visited node and one per weight pass: 2 N.
-inline int64_t tree_max_sync(int64_t N) { return 2 * N; }
+// Exchanges of one walk over n nodes: one per visited node (its softmax pair)
+// and one per weight pass (each rejected child, and the last distribution):
+// the visited nodes and the rejected children are distinct nodes, so n + 1.
+inline int64_t walk_max_sync(int64_t n_nodes) { return n_nodes + 1; }
 
-struct TreeLayout {
+// Workspace of the sampled and tree verify: softmax partials of every row
+// (diagnostics only), then the exchange words [B, max_sync, 2 G].
+struct WalkLayout {
   size_t partial_off, slots_off, bytes;
 };
 
-inline TreeLayout tree_layout(int64_t B, int64_t rows, int64_t V) {
-  TreeLayout L{};
-  const int64_t N = B > 0 ? rows / B : 0;
-  const int64_t G = tree_groups_bound(B);
+inline WalkLayout walk_layout(int64_t B, int64_t rows, int64_t V, int64_t max_sync) {
+  WalkLayout L{};
+  const int64_t G = walk_groups_bound(B);
   L.partial_off = 0;
   L.slots_off = align256(static_cast<size_t>(rows * row_segments(rows, V)) * 8);
-  const size_t slots = G > 1 ? static_cast<size_t>(B * tree_max_sync(N) * 2 * G) * 8 : 0;
+  const size_t slots = G > 1 ? static_cast<size_t>(B * max_sync * 2 * G) * 8 : 0;
   L.bytes = L.slots_off + align256(slots);
   return L;
 }
 
-struct SampleLayout {
-  size_t partial_off, tiles_off, records_off, bytes;
-};
-
-inline SampleLayout sample_layout(int64_t B, int64_t t_rows, int64_t V) {
-  SampleLayout L{};
-  const int64_t nseg = row_segments(t_rows, V);
-  L.partial_off = 0;
-  L.tiles_off = align256(static_cast<size_t>(t_rows * nseg) * 8);
-  L.records_off = L.tiles_off + align256(static_cast<size_t>(B * sample_tiles(V)) * 3 * 8);
-  L.bytes = L.records_off + align256(static_cast<size_t>(B) * 16);
-  return L;
-}
-
-struct SampleArgs {
+struct WalkArgs {
   const void* tgt;
   const void* dq;
   int64_t V;
+  float c;                  // log2(e) / T
+  int32_t B;
+  const float* u;
+  // chain: request b has k_b = dlen[b] drafts, rows t_rs[b] + i and q_rs[b] + i
   int32_t t_rows, q_rows;
   const int32_t* t_rs;
   const int32_t* q_rs;
   const int32_t* ids;
   const int32_t* dlen;
-  int32_t B, k_max;
-  float c;      // log2(e) / T
-  const float* u;
+  int32_t k_max;
   const int32_t* max_new;
   int32_t eos;
+  float* resid;
+  // tree: N nodes per request, rows b * N + c
+  const int32_t* parent;
+  const int32_t* token;
+  int32_t N;
+  int32_t* out_path;
+  // outputs
   int32_t* out_tok;
   int32_t* out_cnt;
   int32_t* out_acc;
-  float* diag;
-  float* resid;
   int32_t* status;
-  const float2* partial;
+  float* diag;
+  const float2* partial;    // softmax partials of every row (diagnostics only)
   int32_t nseg;
-  double* tiles;     // [B, ntiles, 3] sums of (draw weights, p, q) per tile
-  int4* records;     // [B] (status bits, m, scaled max, 1/normaliser) of the draw row
+  // the split
   int32_t ntiles;
+  int32_t G;
+  uint64_t* slots;          // [B, max_sync, 2 G] exchange words (G > 1)
+  int32_t max_sync;
+  int32_t spin_limit;
+  int32_t node_cap;         // LDS capacity in nodes (>= nodes of any request)
+  int32_t tile_cap;         // LDS capacity in tiles (>= tiles of any slice)
 };
+
+size_t walk_lds_bytes(int node_cap, int tile_cap);
+int walk_occupancy(bool chain, int t_dtype, int q_dtype, size_t lds);
+// Launches the walk (and the diagnostics, when asked for).  clear_slots: zero
+// the exchange words first (not needed when the statistics kernel did it).
+hipError_t launch_walk(bool chain, int t_dtype, int q_dtype, const WalkArgs& a, size_t lds,
+                       bool clear_slots, hipStream_t stream);
 
 struct GreedyArgs {
   const void* tgt;
@@ -143,40 +156,17 @@ struct GreedyArgs {
   int32_t nseg;
 };
 
-struct TreeArgs {
-  const void* tgt;
-  const void* dq;
-  int64_t V;
-  const int32_t* parent;
-  const int32_t* token;
-  int32_t B, N;
-  float c;      // log2(e) / T
-  const float* u;
-  int32_t* out_tok;
-  int32_t* out_cnt;
-  int32_t* out_acc;
-  int32_t* out_path;
-  float* diag;
-  int32_t* status;
-  const float2* partial;   // softmax partials of every row (diagnostics only)
-  int32_t nseg;
-  int32_t ntiles;
-  uint64_t* slots;         // [B, max_sync, 2 G] exchange words (G > 1)
-  int32_t G;               // workgroups per request
-  int32_t max_sync;
-  int32_t spin_limit;
-};
 
+// Softmax partials of every row; optionally zeroes clear_words 8-byte words
+// at `clear` (16-byte aligned) on the side.
 hipError_t launch_row_stats(int dtype, const void* rows, int64_t n_rows, int64_t V, int32_t nseg,
-                            float c, float2* partial, hipStream_t stream);
-hipError_t launch_sample_resolve(int t_dtype, int q_dtype, const SampleArgs& a,
-                                 hipStream_t stream);
+                            float c, float2* partial, hipStream_t stream, uint64_t* clear = nullptr,
+                            int64_t clear_words = 0);
 hipError_t launch_row_argmax(int dtype, const void* rows, int64_t n_rows, int64_t V, int32_t nseg,
                              uint64_t* keys, hipStream_t stream);
 hipError_t launch_greedy_resolve(const GreedyArgs& a, hipStream_t stream);
 hipError_t launch_ngram(const int32_t* ctx, const int32_t* ctx_len, int32_t B, int32_t stride,
                         int32_t window, int32_t k, int32_t* ids, int32_t* lens, int32_t* status,
                         hipStream_t stream);
-hipError_t launch_tree_walk(int t_dtype, int q_dtype, const TreeArgs& a, hipStream_t stream);
 
 }  // namespace sv

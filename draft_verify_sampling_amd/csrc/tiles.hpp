@@ -78,8 +78,11 @@ struct TileRuns {
 };
 
 // Sums (w, p, q) of tile t, in fp32 within a lane and fp64 across lanes; valid
-// in every lane.  Handles any tile: a row that is not 16-byte aligned, and the
-// row's last partial tile, take element loads run by run.
+// in every lane.  Handles any tile.  On 16-byte aligned rows every complete
+// run is one predicated vector load, all in flight at once (the row's last
+// partial tile costs one load round like any other); a run that the row's
+// end cuts (rows whose length is not a multiple of the vector width) and
+// unaligned rows take element loads.
 template <class DT, class DQ>
 __device__ __forceinline__ void wave_tile_sums_any(const DrawRow& r, int64_t V, int t, double* v) {
   using L = TileRuns<DT, DQ>;
@@ -88,38 +91,80 @@ __device__ __forceinline__ void wave_tile_sums_any(const DrawRow& r, int64_t V, 
   const int64_t t0 = static_cast<int64_t>(t) * kSampleTile;
   const bool al = aligned16<DT>(r.t, t0) && (!r.use_q || aligned16<DQ>(r.q, t0));
   float ws = 0.f, ps = 0.f, qs = 0.f;
-#pragma unroll 1
-  for (int k = 0; k < L::kRuns; ++k) {
-    const int64_t e = t0 + static_cast<int64_t>(k * kWave + lane) * kPer;
-    if (e >= V) break;
-    float l[kPer], q[kPer];
-    if (al && e + kPer <= V) {
+  constexpr int kAB = (L::nt + L::nq == 2) ? 4 : 2;  // runs per load round (<= 8 vectors)
+  static_assert(L::kRuns % kAB == 0, "whole rounds");
+  if (al) {
 #pragma unroll
-      for (int j = 0; j < L::nt; ++j) DT::unpack(ld16<DT>(r.t, e + j * DT::kPerVec), l + j * DT::kPerVec);
-      if (r.use_q) {
+    for (int k0 = 0; k0 < L::kRuns; k0 += kAB) {
+    uint4 tw[kAB][L::nt], qw[kAB][L::nq];
 #pragma unroll
-        for (int j = 0; j < L::nq; ++j) DQ::unpack(ld16<DQ>(r.q, e + j * DQ::kPerVec), q + j * DQ::kPerVec);
+    for (int kk = 0; kk < kAB; ++kk) {
+      const int64_t e = t0 + static_cast<int64_t>((k0 + kk) * kWave + lane) * kPer;
+      if (e + kPer <= V) {
+#pragma unroll
+        for (int j = 0; j < L::nt; ++j) tw[kk][j] = ld16<DT>(r.t, e + j * DT::kPerVec);
+        if (r.use_q) {
+#pragma unroll
+          for (int j = 0; j < L::nq; ++j) qw[kk][j] = ld16<DQ>(r.q, e + j * DQ::kPerVec);
+        }
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < kAB; ++kk) {
+      const int64_t e = t0 + static_cast<int64_t>((k0 + kk) * kWave + lane) * kPer;
+      if (e >= V) continue;
+      float l[kPer], q[kPer];
+      if (e + kPer <= V) {
+#pragma unroll
+        for (int j = 0; j < L::nt; ++j) DT::unpack(tw[kk][j], l + j * DT::kPerVec);
+        if (r.use_q) {
+#pragma unroll
+          for (int j = 0; j < L::nq; ++j) DQ::unpack(qw[kk][j], q + j * DQ::kPerVec);
+        } else {
+#pragma unroll
+          for (int j = 0; j < kPer; ++j) q[j] = 0.f;
+        }
       } else {
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) q[j] = 0.f;
+        for (int j = 0; j < kPer; ++j) {
+          const bool in = e + j < V;
+          l[j] = in ? DT::at(r.t, e + j) : -INFINITY;
+          q[j] = (in && r.use_q) ? DQ::at(r.q, e + j) : 0.f;
+        }
       }
-    } else {
+      float w[kPer], p[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        p[j] = draw_p(r, l[j]);
+        w[j] = draw_w(r, p[j], q[j]);
+      }
+      ws += pairwise<kPer>(w);
+      ps += pairwise<kPer>(p);
+      qs += pairwise<kPer>(q);
+    }
+    }
+  } else {
+#pragma unroll 1
+    for (int k = 0; k < L::kRuns; ++k) {
+      const int64_t e = t0 + static_cast<int64_t>(k * kWave + lane) * kPer;
+      if (e >= V) break;
+      float l[kPer], q[kPer];
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
         const bool in = e + j < V;
         l[j] = in ? DT::at(r.t, e + j) : -INFINITY;
         q[j] = (in && r.use_q) ? DQ::at(r.q, e + j) : 0.f;
       }
-    }
-    float w[kPer], p[kPer];
+      float w[kPer], p[kPer];
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      p[j] = draw_p(r, l[j]);
-      w[j] = draw_w(r, p[j], q[j]);
+      for (int j = 0; j < kPer; ++j) {
+        p[j] = draw_p(r, l[j]);
+        w[j] = draw_w(r, p[j], q[j]);
+      }
+      ws += pairwise<kPer>(w);
+      ps += pairwise<kPer>(p);
+      qs += pairwise<kPer>(q);
     }
-    ws += pairwise<kPer>(w);
-    ps += pairwise<kPer>(p);
-    qs += pairwise<kPer>(q);
   }
   v[0] = wave_total(static_cast<double>(ws));
   v[1] = wave_total(static_cast<double>(ps));
@@ -199,41 +244,94 @@ __device__ __forceinline__ void wave_tile_sums(const DrawRow& r, int64_t V, int 
 }
 
 // Online-softmax pair (scaled domain, as in common.hpp) of tile t of a target
-// row, valid in every lane.  Lane l takes the 16-byte vectors l, l + 64, ...
-// of the tile, all in flight at once, and folds them with one rescale; the
-// row's last partial tile and unaligned rows take element loads.
+// row, valid in every lane, for any tile: on aligned rows every complete
+// 16-byte vector is one predicated load, all in flight at once; a vector the
+// row's end cuts and unaligned rows take element loads.
 template <class D>
-__device__ __forceinline__ MS wave_tile_ms(const void* row, int64_t V, float c, int t) {
+__device__ MS wave_tile_ms_any(const void* row, int64_t V, float c, int t) {
   constexpr int kPer = D::kPerVec;
   constexpr int kRuns = kSampleTile / (kWave * kPer);
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t t0 = static_cast<int64_t>(t) * kSampleTile;
   MS acc{-INFINITY, 0.f};
-  if (t0 + kSampleTile <= V && aligned16<D>(row, t0)) {
-    uint4 w[kRuns];
+  if (aligned16<D>(row, t0)) {
+    constexpr int kAB = kRuns < 4 ? kRuns : 4;  // runs per load round
 #pragma unroll
-    for (int k = 0; k < kRuns; ++k) w[k] = ld16<D>(row, t0 + static_cast<int64_t>(k * kWave + lane) * kPer);
-    float x[kRuns * kPer];
+    for (int k0 = 0; k0 < kRuns; k0 += kAB) {
+      uint4 w[kAB];
 #pragma unroll
-    for (int k = 0; k < kRuns; ++k) D::unpack(w[k], x + k * kPer);
-    ms_fold<kRuns * kPer>(acc, x, c);
+      for (int kk = 0; kk < kAB; ++kk) {
+        const int64_t e = t0 + static_cast<int64_t>((k0 + kk) * kWave + lane) * kPer;
+        if (e + kPer <= V) w[kk] = ld16<D>(row, e);
+      }
+#pragma unroll
+      for (int kk = 0; kk < kAB; ++kk) {
+        const int64_t e = t0 + static_cast<int64_t>((k0 + kk) * kWave + lane) * kPer;
+        float x[kPer];
+        if (e + kPer <= V) {
+          D::unpack(w[kk], x);
+        } else {
+#pragma unroll
+          for (int j = 0; j < kPer; ++j) x[j] = e + j < V ? D::at(row, e + j) : -INFINITY;
+        }
+        ms_fold<kPer>(acc, x, c);
+      }
+    }
   } else {
-    const bool al = aligned16<D>(row, t0);
 #pragma unroll 1
     for (int k = 0; k < kRuns; ++k) {
       const int64_t e = t0 + static_cast<int64_t>(k * kWave + lane) * kPer;
       if (e >= V) break;
       float x[kPer];
-      if (al && e + kPer <= V) {
-        D::unpack(ld16<D>(row, e), x);
-      } else {
 #pragma unroll
-        for (int j = 0; j < kPer; ++j) x[j] = e + j < V ? D::at(row, e + j) : -INFINITY;
-      }
+      for (int j = 0; j < kPer; ++j) x[j] = e + j < V ? D::at(row, e + j) : -INFINITY;
       ms_fold<kPer>(acc, x, c);
     }
   }
   return wave_ms_dpp(acc);
+}
+
+// Online-softmax pairs of tile t of one target row (kTwo false; row1 unused) or two,
+// valid in every lane.  Lane l takes the 16-byte vectors l, l + 64, ... of the
+// tile; the loads of both rows are in flight at once and each row is folded
+// with one rescale.
+template <class D, bool kTwo>
+__device__ __forceinline__ void wave_tile_ms(const void* row0, const void* row1, int64_t V, float c, int t,
+                                             MS& out0, MS& out1) {
+  constexpr int kPer = D::kPerVec;
+  constexpr int kRuns = kSampleTile / (kWave * kPer);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t t0 = static_cast<int64_t>(t) * kSampleTile;
+  constexpr bool two = kTwo;
+  const bool fast = t0 + kSampleTile <= V && aligned16<D>(row0, t0) && (!two || aligned16<D>(row1, t0));
+  if (!fast) {
+    out0 = wave_tile_ms_any<D>(row0, V, c, t);
+    if (two) out1 = wave_tile_ms_any<D>(row1, V, c, t);
+    return;
+  }
+  uint4 w0[kRuns], w1[kTwo ? kRuns : 1];
+#pragma unroll
+  for (int k = 0; k < kRuns; ++k) w0[k] = ld16<D>(row0, t0 + static_cast<int64_t>(k * kWave + lane) * kPer);
+  if constexpr (kTwo) {
+#pragma unroll
+    for (int k = 0; k < kRuns; ++k) w1[k] = ld16<D>(row1, t0 + static_cast<int64_t>(k * kWave + lane) * kPer);
+  }
+  {
+    float x[kRuns * kPer];
+#pragma unroll
+    for (int k = 0; k < kRuns; ++k) D::unpack(w0[k], x + k * kPer);
+    MS acc{-INFINITY, 0.f};
+    ms_fold<kRuns * kPer>(acc, x, c);
+    out0 = wave_ms_dpp(acc);
+  }
+  if constexpr (kTwo) {
+    float x[kRuns * kPer];
+#pragma unroll
+    for (int k = 0; k < kRuns; ++k) D::unpack(w1[k], x + k * kPer);
+    MS acc{-INFINITY, 0.f};
+    ms_fold<kRuns * kPer>(acc, x, c);
+    out1 = wave_ms_dpp(acc);
+  }
 }
 
 // Lane l's contiguous share [ta, tb) of ntiles tile sums for the tile search.

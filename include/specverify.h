@@ -77,18 +77,19 @@ typedef enum { SV_OP_GREEDY = 0, SV_OP_SAMPLE = 1, SV_OP_TREE = 2 } sv_op;
 #define SV_FLAG_BAD_REQUEST 1   /* draft count outside [0,k_max], row index out of range,
                                    context length outside [0,stride] */
 #define SV_FLAG_BAD_TOKEN 2     /* a draft / node token outside [0,vocab) */
-#define SV_FLAG_NONFINITE 4     /* sampled: a target row whose normaliser sum exp(l/T - M)
-                                   is not finite and positive; the draft row a residual is
-                                   taken from sums to NaN; a non-finite residual mass.
-                                   greedy: a NaN in a target row */
+#define SV_FLAG_NONFINITE 4     /* sampled / tree: a target row the verify reads (chain:
+                                   rows 0..m; tree: the visited nodes) whose normaliser
+                                   sum exp(l/T - M) is not finite and positive; the draft
+                                   row a residual is taken from sums to NaN; a non-finite
+                                   residual mass.  greedy: a NaN in a target row */
 #define SV_FLAG_OVER_BUDGET 8   /* more drafts than max_new[b] (output still produced,
                                    truncated to max_new[b]) */
 #define SV_FLAG_FALLBACK 16     /* a residual max(0, p - q) had zero mass: the token was
                                    drawn from p (chain) / p was left unchanged (tree) */
 #define SV_FLAG_BAD_TREE 32     /* parent[b,0] != -1, or parent[b,c] not in [0,c) */
-#define SV_FLAG_SYNC_TIMEOUT 64 /* tree: the workgroups sharing a request did not all
-                                   report within the bounded wait (only possible when
-                                   other work keeps some of them from running); that
+#define SV_FLAG_SYNC_TIMEOUT 64 /* sampled / tree: the workgroups sharing a request did
+                                   not all report within the bounded wait (only possible
+                                   when other work keeps some of them from running); that
                                    request's outputs are undefined */
 
 int sv_abi_version(void);
@@ -162,7 +163,9 @@ sv_status sv_verify_greedy(const void* target_logits, int32_t t_dtype, int32_t t
  * (M_i = max(l/T), S_i = sum exp(l/T - M_i), p_i(x_i), q_i(x_i)) for i <= k_b
  * (p, q = 0 at i = k_b; rows beyond k_b untouched); out_resid [batch] = total
  * mass of the weights the last token was drawn from.
- * temperature must be finite and > 0. */
+ * The round reads target rows 0..m and draft row m only (every row when
+ * out_diag is asked for).  temperature must be finite and > 0; 1 <= vocab <=
+ * 4194304. */
 sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t_rows,
                            const void* draft_probs, int32_t q_dtype, int32_t q_rows,
                            int64_t vocab, const int32_t* t_row_start,
@@ -189,7 +192,10 @@ sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t
  * (kept nodes), out_path [batch, n_nodes] (kept node ids, -1 padded).
  * Optional out_diag [batch, n_nodes, 4] = (M_c, S_c, p_parent(x_c),
  * q_parent(x_c)) with the parent's softmax before any residual update
- * (p, q = 0 at the root).  1 <= n_nodes <= 1024, 1 <= vocab <= 1048576. */
+ * (p, q = 0 at the root).  1 <= n_nodes <= 1024, 1 <= vocab <= 4194304.
+ * Only the rows the walk reads are touched: the target rows of the visited
+ * nodes and the draft rows of nodes whose children were rejected (out_diag,
+ * when asked for, reads every row). */
 sv_status sv_verify_tree(const void* target_logits, int32_t t_dtype,
                          const void* draft_probs, int32_t q_dtype, int64_t vocab,
                          const int32_t* parent, const int32_t* node_token,

@@ -40,7 +40,10 @@ def test_version_and_strings(lib):
 
 def test_workspace_sizes(lib):
     assert sv.workspace_bytes(sv.SV_OP_SAMPLE, 64, 320, 248_320) % 256 == 0
-    assert sv.workspace_bytes(sv.SV_OP_SAMPLE, 64, 320, 248_320) >= 320 * 8 + 64 * 61 * 24 + 64 * 4
+    # softmax partials of every row (31 segments of 8192 at V = 248,320), then
+    # the exchange words between the workgroups that share a request
+    assert sv.workspace_bytes(sv.SV_OP_SAMPLE, 64, 320, 248_320) >= 320 * 31 * 8 + 64 * 6 * 2 * 8
+    assert sv.workspace_bytes(sv.SV_OP_TREE, 32, 1920, 128_256) >= 1920 * 16 * 8 + 32 * 61 * 2 * 8
     assert sv.workspace_bytes(sv.SV_OP_GREEDY, 64, 320, 32_000) >= 320 * 8
     assert sv.workspace_bytes(sv.SV_OP_TREE, 32, 1920, 128_256) >= 1920 * 8
     assert sv.workspace_bytes(sv.SV_OP_SAMPLE, -1, 1, 1) == 0
@@ -70,6 +73,7 @@ def test_host_checks_sample(lib):
     assert call(qdt=-1) == 2
     assert call(k_max=256) == 1
     assert call(V=0) == 1
+    assert call(V=(1 << 22) + 1) == 1 and "vocab" in _err(lib)
     assert call(B=-1) == 1
     assert call(tgt=None) == 1 and "null" in _err(lib)
     assert call() == 3 and "workspace" in _err(lib)                     # workspace NULL
@@ -87,7 +91,7 @@ def test_host_checks_greedy_tree_ngram(lib):
     t = lib.sv_verify_tree
     assert t(d, 1, d, 1, 100, d, d, 1, 0, 1.0, d, d, d, d, d, None, None, None, 0, None) == 1
     assert t(d, 1, d, 1, 100, d, d, 1, 2000, 1.0, d, d, d, d, d, None, None, None, 0, None) == 1
-    assert t(d, 1, d, 1, 1 << 21, d, d, 1, 60, 1.0, d, d, d, d, d, None, None, None, 0, None) == 1
+    assert t(d, 1, d, 1, (1 << 22) + 1, d, d, 1, 60, 1.0, d, d, d, d, d, None, None, None, 0, None) == 1
     assert t(d, 1, d, 1, 100, d, d, 1, 60, 0.0, d, d, d, d, d, None, None, None, 0, None) == 1
     assert t(d, 1, d, 1, 100, d, d, 1, 60, 1.0, d, d, d, d, d, None, None, None, 0, None) == 3
     n = lib.sv_ngram_draft

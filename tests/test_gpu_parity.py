@@ -259,18 +259,25 @@ def test_gpu_sample_edge_cases():
     say("sampled chain edge cases")
     rng = np.random.default_rng(8)
     V, k = 5000, 3
-    B = 12
-    ks = np.array([0, 3, 3, 3, 3, 3, 3, 3, 3, 3, 2, 3], dtype=np.int32)
+    B = 13
+    ks = np.array([0, 3, 3, 3, 3, 3, 3, 3, 3, 3, 2, 3, 3], dtype=np.int32)
     ci = synth.sampled_chain(90, B, ks, V, 1.0, sd=2.0, n_boost=3, boost=5.0, sigma=1.0, kind="f32")
     t = ci.target
     q = ci.draft
     # request 2: residual with zero mass -> fallback to p (draft row of position 0 all ones)
     q[ci.q_row_start[2]] = 1.0
     ci.uniforms[2, 0] = 0.99
-    # request 3: NaN in a target row
+    # request 3: NaN in a target row the round reads (u = 0 keeps draft 0)
     t[ci.t_row_start[3] + 1, 10] = np.nan
-    # request 4: +inf in a target row
+    ci.uniforms[3, 0] = 0.0
+    # request 4: +inf in a target row the round reads (drafts 0 and 1 kept)
     t[ci.t_row_start[4] + 2, 11] = np.inf
+    ci.uniforms[4, :2] = 0.0
+    # request 12: NaN in a row after a forced break at 0: never read, valid
+    ci.draft_ids[12, 0] = 13
+    q[ci.q_row_start[12], 13] = 1.0
+    ci.uniforms[12, 0] = 0.999
+    t[ci.t_row_start[12] + 2, 10] = np.nan
     # request 5: NaN in the draft row at the break (force a rejection at 0)
     q[ci.q_row_start[5], 12] = np.nan
     ci.draft_ids[5, 0] = 13
@@ -285,7 +292,7 @@ def test_gpu_sample_edge_cases():
     # request 9: u = 0 everywhere
     ci.uniforms[9] = 0.0
     ci.uniforms[11] = 0.0                # keep every draft with p > 0
-    max_new = np.array([5, 5, 5, 5, 5, 5, 5, 5, 5, 5, 1, 2], dtype=np.int32)  # 10, 11: over budget
+    max_new = np.array([5, 5, 5, 5, 5, 5, 5, 5, 5, 5, 1, 2, 5], dtype=np.int32)  # 10, 11: over budget
     eos = int(ci.draft_ids[1, 1]) if ks[1] > 1 else -1
     for mn, eo in ((None, -1), (max_new, eos)):
         st = _status()
@@ -299,6 +306,7 @@ def test_gpu_sample_edge_cases():
     assert fl[4] & oracle.FLAG_NONFINITE and fl[5] & oracle.FLAG_NONFINITE
     assert fl[6] & oracle.FLAG_BAD_TOKEN and fl[7] & oracle.FLAG_BAD_REQUEST
     assert fl[11] & oracle.FLAG_OVER_BUDGET and got["count"][11] == 2
+    assert fl[12] == 0 and want["accepted"][12] == 0 and got["count"][12] == 1
 
 
 def test_gpu_greedy_equals_sampling_on_one_hot():
