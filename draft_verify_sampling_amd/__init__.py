@@ -226,10 +226,12 @@ def sv_verify_sample(target: torch.Tensor, draft: torch.Tensor, t_row_start: tor
                      temperature: float, uniforms: torch.Tensor,
                      max_new: Optional[torch.Tensor] = None, eos_id: int = -1,
                      diag: bool = False, dev_status: Optional[torch.Tensor] = None,
-                     workspace: Optional[Workspace] = None, stream=None, out=None):
+                     workspace: Optional[Workspace] = None, stream=None, out=None,
+                     resid: Optional[bool] = None):
     """Speculative-sampling verify.  Returns (tokens [B, k_max+1], count, accepted,
     diag [B, k_max+1, 4] or None, resid [B] or None).  ``out`` may pass a
-    preallocated (tokens, count, accepted, diag, resid) tuple."""
+    preallocated (tokens, count, accepted, diag, resid) tuple.  ``resid``
+    (default: same as ``diag``) asks for the residual masses."""
     lib = load()
     t_rows, V = target.shape
     q_rows = draft.shape[0]
@@ -245,7 +247,8 @@ def sv_verify_sample(target: torch.Tensor, draft: torch.Tensor, t_row_start: tor
         cnt = torch.empty((B,), dtype=torch.int32, device=dev)
         acc = torch.empty((B,), dtype=torch.int32, device=dev)
         dg = torch.zeros((B, k_max + 1, 4), dtype=torch.float32, device=dev) if diag else None
-        rs = torch.zeros((B,), dtype=torch.float32, device=dev) if diag else None
+        want_resid = diag if resid is None else resid
+        rs = torch.zeros((B,), dtype=torch.float32, device=dev) if want_resid else None
     else:
         tok, cnt, acc, dg, rs = out
     nb = workspace_bytes(SV_OP_SAMPLE, B, t_rows, V)

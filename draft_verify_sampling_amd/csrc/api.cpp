@@ -58,16 +58,15 @@ int cu_count() {
 
 
 // Shared tail of the sampled and tree verify: the split into G workgroups per
-// request, the workspace carve-up and the launches: the softmax partials of
-// every row first (chains always; trees only for the diagnostics), then the
-// walk.
+// request, the workspace carve-up and the launches.  Chains whose requests
+// own their rows take the lazy statistics (rows after the break are skipped);
+// chains with shared rows, and any call asking for diagnostics, take the
+// softmax partials of every row.  Trees compute statistics in the walk.
 sv_status launch_walk_call(bool chain, int32_t t_dtype, int32_t q_dtype, sv::WalkArgs& a, int64_t rows,
                            int64_t nodes, int64_t node_cap, void* workspace, hipStream_t st,
                            const char* what) {
   const int64_t ntiles = sv::sample_tiles(a.V);
   const int64_t max_sync = sv::walk_max_sync(nodes);
-  const sv::WalkLayout L = sv::walk_layout(a.B, rows, a.V, chain ? sv::walk_max_sync(
-      std::min<int64_t>(rows, sv::kMaxChainRows)) : max_sync);
   char* ws = static_cast<char*>(workspace);
   // G from the occupancy at the largest slice this kernel may get
   const size_t lds_max = sv::walk_lds_bytes(static_cast<int>(node_cap), static_cast<int>(ntiles));
@@ -75,6 +74,16 @@ sv_status launch_walk_call(bool chain, int32_t t_dtype, int32_t q_dtype, sv::Wal
   const int64_t resident = static_cast<int64_t>(occ) * std::max(cu_count(), 1);
   a.G = std::min<int32_t>(sv::walk_groups(a.B, a.V, resident),
                           static_cast<int32_t>(sv::walk_groups_bound(a.B)));
+  // Lazy statistics skip a row only when its request's decision on the row
+  // before is known by the time the row's blocks start, which needs at least
+  // two waves of statistics blocks per row (8 resident blocks per CU); with
+  // fewer, streaming every row is faster.
+  const bool lazy = chain && a.diag == nullptr && ntiles > 1 && a.t_rows >= a.k_max + 1 &&
+                    2 * static_cast<int64_t>(a.t_rows) >= static_cast<int64_t>(a.B) * (a.k_max + 1) &&
+                    static_cast<int64_t>(a.B) * a.nseg >= 2 * 8 * static_cast<int64_t>(std::max(cu_count(), 1)) &&
+                    static_cast<int64_t>(a.k_max + 1) * a.B * a.nseg <= kMaxGrid;
+  const int64_t lazy_R = lazy ? a.k_max + 1 : 0;
+  const sv::WalkLayout L = sv::walk_layout(a.B, rows, a.V, a.G, max_sync, lazy_R);
   a.ntiles = static_cast<int32_t>(ntiles);
   a.tile_cap = static_cast<int32_t>((ntiles + a.G - 1) / a.G);
   a.node_cap = static_cast<int32_t>(node_cap);
@@ -84,19 +93,48 @@ sv_status launch_walk_call(bool chain, int32_t t_dtype, int32_t q_dtype, sv::Wal
   a.partial = reinterpret_cast<const float2*>(ws + L.partial_off);
   if (static_cast<int64_t>(a.B) * a.G > kMaxGrid) return fail(SV_E_ARG, "too many requests");
   (void)hipGetLastError();
-  const bool stats = chain || a.diag != nullptr;  // a chain walk reads every row's partials
-  const int64_t slot_words = a.G > 1 ? static_cast<int64_t>(a.B) * a.max_sync * 2 * a.G : 0;
-  if (stats) {  // the statistics kernel also zeroes the exchange words
+  bool clear_slots = true;
+  if (lazy) {
+    hipError_t e = sv::launch_clear(ws + L.slots_off, L.end - L.slots_off, st);
+    if (e != hipSuccess) return device_fail(e, what);
+    sv::ChainStatsArgs c{};
+    c.tgt = a.tgt;
+    c.dq = a.dq;
+    c.V = a.V;
+    c.c = a.c;
+    c.B = a.B;
+    c.k_max = a.k_max;
+    c.t_rows = a.t_rows;
+    c.q_rows = a.q_rows;
+    c.t_rs = a.t_rs;
+    c.q_rs = a.q_rs;
+    c.ids = a.ids;
+    c.dlen = a.dlen;
+    c.u = a.u;
+    c.nseg = a.nseg;
+    c.stop = reinterpret_cast<uint32_t*>(ws + L.stop_off);
+    c.count = reinterpret_cast<uint32_t*>(ws + L.count_off);
+    c.row_words = reinterpret_cast<uint64_t*>(ws + L.rows_off);
+    c.seg_words = reinterpret_cast<uint64_t*>(ws + L.segs_off);
+    c.status = a.status;
+    c.spin_limit = sv::kSpinLimit;
+    e = sv::launch_chain_stats(t_dtype, q_dtype, c, st);
+    if (e != hipSuccess) return device_fail(e, what);
+    a.stop = c.stop;
+    a.row_words = c.row_words;
+    clear_slots = false;
+  } else if (chain || a.diag != nullptr) {  // the walk reads every row's partials
+    const int64_t slot_words = static_cast<int64_t>(L.stop_off - L.slots_off) / 8;
     const hipError_t e = sv::launch_row_stats(t_dtype, a.tgt, rows, a.V, a.nseg, a.c,
                                               reinterpret_cast<float2*>(ws + L.partial_off), st,
                                               a.slots, slot_words);
     if (e != hipSuccess) return device_fail(e, what);
+    clear_slots = false;  // the statistics kernel zeroed the exchange words
   }
   const size_t lds = sv::walk_lds_bytes(a.node_cap, a.tile_cap);
-  const hipError_t e = sv::launch_walk(chain, t_dtype, q_dtype, a, lds, !stats, st);
+  const hipError_t e = sv::launch_walk(chain, t_dtype, q_dtype, a, lds, clear_slots, st);
   return e == hipSuccess ? SV_OK : device_fail(e, what);
 }
-
 }  // namespace
 
 extern "C" {
@@ -123,10 +161,14 @@ size_t sv_workspace_bytes(int op, int64_t batch, int64_t total_rows, int64_t voc
       return sv::align256(static_cast<size_t>(total_rows * sv::argmax_segments(total_rows, vocab)) * 8);
     case SV_OP_TREE:
       if (batch == 0) return 0;
-      return sv::walk_layout(batch, total_rows, vocab, sv::walk_max_sync(total_rows / batch)).bytes;
-    case SV_OP_SAMPLE:
-      return sv::walk_layout(batch, total_rows, vocab,
-                             sv::walk_max_sync(std::min<int64_t>(total_rows, sv::kMaxChainRows))).bytes;
+      return sv::walk_layout(batch, total_rows, vocab, sv::walk_groups_bound(batch),
+                             sv::walk_max_sync(total_rows / batch), 0).end;
+    case SV_OP_SAMPLE: {
+      // a request has at most min(t_rows, 256) rows
+      const int64_t R = std::min<int64_t>(total_rows, sv::kMaxChainRows);
+      return sv::walk_layout(batch, total_rows, vocab, sv::walk_groups_bound(batch), sv::walk_max_sync(R),
+                             R).end;
+    }
     default:
       return 0;
   }

@@ -2,42 +2,41 @@
 //
 // For every target row l (vocab elements) the verify step needs the softmax
 // normaliser of l / T ("投机解码:为什么一个字都不改", figure "一次目标前向验 k 个
-// 草稿 token": P = softmax(f / T) over the whole vocabulary).  This kernel reads
-// each row exactly once and leaves, per (row, segment), the online-softmax pair
+// 草稿 token": P = softmax(f / T) over the whole vocabulary).  A block reads one
+// 8192-element segment of a row and forms its online-softmax pair
 // (m = max l, s = sum 2^((l - m) log2(e) / T)); consumers combine the nseg
 // pairs of a row.  The pair is kept in the scaled domain: m = max(l) * log2(e) / T
 // (rounded once), s = sum 2^(l * log2(e) / T - m).
 //
-// Layout: grid = rows * nseg blocks of 256 threads, nseg = ceil(V / 8192);
-// block (row, seg) reads the seg-th 8192-element chunk of the row's
-// 16-byte-aligned body with coalesced 16-byte non-temporal loads, all of a
-// thread's loads in flight at once; segment 0 also takes the unaligned head
-// elements and the last segment the tail.
+// k_row_stats: grid = rows * nseg blocks of 256 threads; every row, every
+// segment.
+//
+// k_chain_stats: the chain verify's lazy variant.  A round reads target rows
+// 0..m only (m = the first draft that is not kept, "改进" section), so blocks
+// are ordered row-major over the requests -- all rows 0 first, then all rows
+// 1, ... -- and the last block to finish a (request, row) combines the row's
+// pairs and decides that row's draft at once (kept iff u q(x) < p(x)).  A
+// block whose request has already stopped at an earlier row does nothing.
+// Blocks never wait for a decision: a block that starts before the decision
+// it could use computes its segment anyway, which is only wasted bandwidth.
+//
+// Within a block, every thread issues its 16-byte loads of the segment at once
+// (coalesced, non-temporal); segment 0 also takes the row's unaligned head
+// elements and the last segment its tail.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace sv {
 
-// One 8192-element chunk per block: every thread issues its U 16-byte loads
-// at once (lanes past the row's end read nothing and fold -inf), so each
-// block has its whole chunk in flight; NT selects non-temporal loads.
-//
-// `clear` (optional, n16 16-byte words) is zeroed on the side, for the exchange
-// words of the walk that follows this kernel on the stream.
+namespace {
+
+// Online-softmax pair of segment `seg` of a row, valid in thread 0.  `sh`
+// holds 2 * (kBlock / 64) floats.
 template <class D, bool NT>
-__global__ __launch_bounds__(kBlock) void k_row_stats(const void* __restrict__ rows, int64_t V,
-                                                      int32_t nseg, float c,
-                                                      float2* __restrict__ partial,
-                                                      uint4* __restrict__ clear, int64_t n16) {
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n16;
-       i += static_cast<int64_t>(gridDim.x) * kBlock)
-    clear[i] = uint4{0u, 0u, 0u, 0u};
+__device__ __forceinline__ MS segment_ms(const void* base, int64_t V, int32_t seg, int32_t nseg, float c,
+                                         float* sh) {
   constexpr int U = kSegElems / (kBlock * D::kPerVec);
   constexpr int kSegVecs = kSegElems / D::kPerVec;
-  __shared__ float sh[2 * (kBlock / kWave)];
-  const int64_t row = blockIdx.x / nseg;
-  const int32_t seg = blockIdx.x - static_cast<int32_t>(row) * nseg;
-  const void* base = row_ptr<D>(rows, row, V);
   const int64_t head = head_elems<D>(base, V);
   const int64_t nvec = (V - head) / D::kPerVec;
   const uint4* vp = reinterpret_cast<const uint4*>(static_cast<const char*>(base) + head * D::kSize);
@@ -91,11 +90,28 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(const void* __restrict__ r
     sh[2 * wid + 1] = r.s;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    MS t{sh[0], sh[1]};
-    for (int w = 1; w < kBlock / kWave; ++w) t = ms_combine(t, MS{sh[2 * w], sh[2 * w + 1]});
-    partial[blockIdx.x] = make_float2(t.m, t.s);
-  }
+  MS t{sh[0], sh[1]};
+  for (int w = 1; w < kBlock / kWave; ++w) t = ms_combine(t, MS{sh[2 * w], sh[2 * w + 1]});
+  return t;
+}
+
+}  // namespace
+
+// `clear` (optional, n16 16-byte words) is zeroed on the side, for the exchange
+// words of the walk that follows this kernel on the stream.
+template <class D, bool NT>
+__global__ __launch_bounds__(kBlock) void k_row_stats(const void* __restrict__ rows, int64_t V,
+                                                      int32_t nseg, float c,
+                                                      float2* __restrict__ partial,
+                                                      uint4* __restrict__ clear, int64_t n16) {
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n16;
+       i += static_cast<int64_t>(gridDim.x) * kBlock)
+    clear[i] = uint4{0u, 0u, 0u, 0u};
+  __shared__ float sh[2 * (kBlock / kWave)];
+  const int64_t row = blockIdx.x / nseg;
+  const int32_t seg = blockIdx.x - static_cast<int32_t>(row) * nseg;
+  const MS t = segment_ms<D, NT>(row_ptr<D>(rows, row, V), V, seg, nseg, c, sh);
+  if (threadIdx.x == 0) partial[blockIdx.x] = make_float2(t.m, t.s);
 }
 
 hipError_t launch_row_stats(int dtype, const void* rows, int64_t n_rows, int64_t V, int32_t nseg,
@@ -108,6 +124,127 @@ hipError_t launch_row_stats(int dtype, const void* rows, int64_t n_rows, int64_t
     hipLaunchKernelGGL((k_row_stats<BF16, true>), grid, block, 0, stream, rows, V, nseg, c, partial, c16, n16);
   else
     hipLaunchKernelGGL((k_row_stats<F32, true>), grid, block, 0, stream, rows, V, nseg, c, partial, c16, n16);
+  return hipGetLastError();
+}
+
+// ---- the lazy statistics of the chain verify ----
+
+namespace {
+
+constexpr uint64_t kWordValid = 1ull << 63;
+
+// A softmax pair as one 64-bit word whose bit 63 is set (s >= 0 or NaN frees
+// its sign bit).
+__device__ __forceinline__ uint64_t pair_word(MS v) {
+  return (static_cast<uint64_t>(__float_as_uint(v.s) | 0x80000000u) << 32) | __float_as_uint(v.m);
+}
+__device__ __forceinline__ MS word_pair(uint64_t w) {
+  return MS{__uint_as_float(static_cast<uint32_t>(w)),
+            __uint_as_float(static_cast<uint32_t>(w >> 32) & 0x7fffffffu)};
+}
+
+}  // namespace
+
+template <class DT, class DQ>
+__global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
+  __shared__ float sh[2 * (kBlock / kWave)];
+  __shared__ uint64_t s_w[kMaxChainSegs];
+  __shared__ int s_last;
+  const int64_t per_row = static_cast<int64_t>(a.B) * a.nseg;
+  const int i = static_cast<int>(blockIdx.x / per_row);
+  const int64_t rem = blockIdx.x - static_cast<int64_t>(i) * per_row;
+  const int b = static_cast<int>(rem / a.nseg);
+  const int seg = static_cast<int>(rem - static_cast<int64_t>(b) * a.nseg);
+  const int R = a.k_max + 1;
+  uint32_t* stop = a.stop + b;
+  // one round: the request's metadata and, past row 0, whether its round has
+  // already stopped at an earlier row
+  const int k = a.dlen[b];
+  const int ts = a.t_rs[b], qs = a.q_rs[b];
+  const uint32_t sv = i > 0 ? __hip_atomic_load(stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+  if (i > k || k > a.k_max || ts < 0 || static_cast<int64_t>(ts) + k >= a.t_rows ||
+      (k > 0 && (qs < 0 || static_cast<int64_t>(qs) + k > a.q_rows)))
+    return;  // no such row, or a request the walk reports as invalid
+  if (sv > static_cast<uint32_t>(kMaxChainRows - i)) return;  // row i is not needed
+
+  // thread 0 fetches what the decision needs together with the segment
+  int x = -1;
+  float lx = 0.f, qx = 0.f, u = 0.f;
+  if (threadIdx.x == 0 && i < k) {
+    x = a.ids[static_cast<int64_t>(b) * a.k_max + i];
+    u = a.u[static_cast<int64_t>(b) * R + i];
+    if (x >= 0 && x < a.V) {
+      lx = DT::at(row_ptr<DT>(a.tgt, ts + i, a.V), x);
+      qx = DQ::at(row_ptr<DQ>(a.dq, qs + i, a.V), x);
+    }
+  }
+  const MS t = segment_ms<DT, true>(row_ptr<DT>(a.tgt, ts + i, a.V), a.V, seg, a.nseg, a.c, sh);
+  uint64_t* words = a.seg_words + (static_cast<int64_t>(b) * R + i) * a.nseg;
+  if (threadIdx.x == 0) {
+    __hip_atomic_store(words + seg, pair_word(t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t done = __hip_atomic_fetch_add(a.count + static_cast<int64_t>(b) * R + i, 1u,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_last = done == static_cast<uint32_t>(a.nseg - 1);
+  }
+  __syncthreads();
+  if (!s_last || threadIdx.x >= kWave) return;
+
+  // The last segment of row i: every segment has added its count, so every
+  // pair word is written; read them (waiting only for their visibility),
+  // combine in segment order and decide the row's draft.
+  const int lane = threadIdx.x;
+  int ok = 1;
+  for (int s0 = 0; s0 < a.nseg; s0 += kWave) {
+    const int s = s0 + lane;
+    uint64_t v = 0;
+    int done = 0;
+    for (int it = 0; it < a.spin_limit; ++it) {
+      if (s < a.nseg) v = __hip_atomic_load(words + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (__all(s >= a.nseg || (v & kWordValid) != 0)) {
+        done = 1;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    ok &= done;
+    if (s < a.nseg) s_w[s] = v;
+  }
+  if (lane != 0) return;
+  bool stop_here;
+  if (!ok) {
+    flag(a.status, kFlagSyncTimeout);
+    stop_here = true;
+  } else {
+    MS row = word_pair(s_w[0]);
+    for (int s = 1; s < a.nseg; ++s) row = ms_combine(row, word_pair(s_w[s]));
+    __hip_atomic_store(a.row_words + static_cast<int64_t>(b) * R + i, pair_word(row), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    stop_here = !(row.s > 0.f && row.s < INFINITY);
+    if (!stop_here && i < k) {
+      if (x < 0 || x >= a.V) {
+        stop_here = true;  // the walk reports the token
+      } else {
+        const float p = ex2(fmaf(lx, a.c, -row.m)) * (1.f / row.s);
+        stop_here = !(u * qx < p);
+      }
+    }
+  }
+  if (stop_here)
+    __hip_atomic_fetch_max(stop, static_cast<uint32_t>(kMaxChainRows - i), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t launch_chain_stats(int t_dtype, int q_dtype, const ChainStatsArgs& a, hipStream_t stream) {
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.k_max + 1) * a.B * a.nseg)), block(kBlock);
+  const bool tb = t_dtype == kDtypeBF16, qb = q_dtype == kDtypeBF16;
+  if (tb && qb)
+    hipLaunchKernelGGL((k_chain_stats<BF16, BF16>), grid, block, 0, stream, a);
+  else if (tb)
+    hipLaunchKernelGGL((k_chain_stats<BF16, F32>), grid, block, 0, stream, a);
+  else if (qb)
+    hipLaunchKernelGGL((k_chain_stats<F32, BF16>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_chain_stats<F32, F32>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -250,6 +250,7 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
   const int64_t V = a.V;
 
   // ---- the request: its nodes, rows and uniforms ----
+  int start = 0;           // the walk's first node (a lazy chain starts where it stops)
   int N;                   // nodes (chain: k_b + 1)
   int64_t trow0, qrow0;    // node c reads target row trow0 + c and draft row qrow0 + c
   int extra = 0;           // status bits that do not invalidate
@@ -282,6 +283,27 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
       s_tok[tid + 1] = tokv;
       if (!tok_ok) atomicOr(&s_bad, kFlagBadToken);
     }
+    if (a.stop != nullptr) {
+      // lazy statistics: the statistics kernel decided every row up to the
+      // one where the round stops; only that row's pair is needed here
+      __syncthreads();
+      if (const int bad = s_bad) {
+        if (wk.g == 0) walk_invalid<kChain>(a, b, bad, tid, kWalkBlock);
+        return;
+      }
+      const uint32_t sw = a.stop[b];
+      start = sw != 0 ? kMaxChainRows - static_cast<int>(sw) : k;
+      const uint64_t rw = a.row_words[static_cast<int64_t>(b) * (a.k_max + 1) + start];
+      if (tid == 0) {
+        s_m[start] = __uint_as_float(static_cast<uint32_t>(rw));
+        s_S[start] = (rw >> 63) ? __uint_as_float(static_cast<uint32_t>(rw >> 32) & 0x7fffffffu) : NAN;
+        if (start < k) {  // the draft after the kept prefix was not kept
+          s_px[start + 1] = 0.f;
+          s_qx[start + 1] = 1.f;
+        }
+      }
+      __syncthreads();
+    } else {
     // round 2: every row's softmax partials (staged in LDS) and the target
     // logit / draft probability at each drafted token
     const int np = N * a.nseg;
@@ -314,6 +336,7 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
       s_px[tid + 1] = ex2(fmaf(lx, a.c, -s_m[tid])) * (1.f / s_S[tid]);
       s_qx[tid + 1] = qv;
     }
+    }
   } else {
     // round 1: the tree and the uniforms
     N = a.N;
@@ -340,8 +363,8 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
   // ---- the walk ----
   constexpr int kNodesPerThread = kMaxTreeNodes / kWalkBlock;
   const int ngroups = (N + kWave - 1) / kWave;
-  int n_emit = 0, fallback = 0, step = 0, npass = 0, tiles_buf = -1;
-  int cur = 0;
+  int n_emit = start, fallback = 0, step = 0, npass = 0, tiles_buf = -1;
+  int cur = start;
   bool ok = true, synced = true;
   float coef = 0.f, R = 1.f;
   double Rd = 1.0;
@@ -661,6 +684,15 @@ __global__ __launch_bounds__(kBlock) void k_walk_clear(uint4* w, int64_t n16) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x; i < n16;
        i += static_cast<int64_t>(gridDim.x) * kBlock)
     w[i] = uint4{0u, 0u, 0u, 0u};
+}
+
+hipError_t launch_clear(void* p, size_t bytes, hipStream_t stream) {
+  const int64_t n16 = static_cast<int64_t>(bytes / 16);
+  if (n16 <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((n16 + kBlock - 1) / kBlock, 2048);
+  hipLaunchKernelGGL(k_walk_clear, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream,
+                     static_cast<uint4*>(p), n16);
+  return hipGetLastError();
 }
 
 // ---- diagnostics (only when asked for), from the softmax partials of every row ----

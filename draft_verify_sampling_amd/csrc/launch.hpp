@@ -75,21 +75,55 @@ inline int64_t walk_groups_bound(int64_t B) {
 // the visited nodes and the rejected children are distinct nodes, so n + 1.
 inline int64_t walk_max_sync(int64_t n_nodes) { return n_nodes + 1; }
 
-// Workspace of the sampled and tree verify: softmax partials of every row
-// (diagnostics only), then the exchange words [B, max_sync, 2 G].
+// Workspace of the sampled and tree verify, carved per call: softmax
+// partials of every row (shared-row chains and diagnostics), then the walk's
+// exchange words [B, max_sync, 2 G], then the lazy chain statistics: stop
+// words [B], finished-segment counts [B, R], row pairs [B, R] and segment
+// pairs [B, R, nseg] (R = k_max + 1).  Everything from the exchange words on
+// is zeroed before each call.
 struct WalkLayout {
-  size_t partial_off, slots_off, bytes;
+  size_t partial_off, slots_off, stop_off, count_off, rows_off, segs_off, end;
 };
 
-inline WalkLayout walk_layout(int64_t B, int64_t rows, int64_t V, int64_t max_sync) {
+inline WalkLayout walk_layout(int64_t B, int64_t rows, int64_t V, int64_t G, int64_t max_sync,
+                              int64_t lazy_R) {
   WalkLayout L{};
-  const int64_t G = walk_groups_bound(B);
+  const int64_t nseg = row_segments(rows, V);
   L.partial_off = 0;
-  L.slots_off = align256(static_cast<size_t>(rows * row_segments(rows, V)) * 8);
-  const size_t slots = G > 1 ? static_cast<size_t>(B * max_sync * 2 * G) * 8 : 0;
-  L.bytes = L.slots_off + align256(slots);
+  L.slots_off = align256(static_cast<size_t>(rows * nseg) * 8);
+  L.stop_off = L.slots_off + align256(G > 1 ? static_cast<size_t>(B * max_sync * 2 * G) * 8 : 0);
+  L.count_off = L.stop_off + align256(static_cast<size_t>(lazy_R > 0 ? B : 0) * 4);
+  L.rows_off = L.count_off + align256(static_cast<size_t>(B * lazy_R) * 4);
+  L.segs_off = L.rows_off + align256(static_cast<size_t>(B * lazy_R) * 8);
+  L.end = L.segs_off + align256(static_cast<size_t>(B * lazy_R * nseg) * 8);
   return L;
 }
+
+// Lazy chain statistics: the segments of one row fit the deciding block's LDS.
+constexpr int kMaxChainSegs = static_cast<int>(kMaxSampleVocab / kSegElems);
+
+struct ChainStatsArgs {
+  const void* tgt;
+  const void* dq;
+  int64_t V;
+  float c;
+  int32_t B, k_max, t_rows, q_rows;
+  const int32_t* t_rs;
+  const int32_t* q_rs;
+  const int32_t* ids;
+  const int32_t* dlen;
+  const float* u;
+  int32_t nseg;
+  uint32_t* stop;        // [B] kMaxChainRows - (first row that stops the round); 0: none
+  uint32_t* count;       // [B, R] finished segments
+  uint64_t* row_words;   // [B, R] row pairs
+  uint64_t* seg_words;   // [B, R, nseg] segment pairs
+  int32_t* status;
+  int32_t spin_limit;
+};
+
+hipError_t launch_chain_stats(int t_dtype, int q_dtype, const ChainStatsArgs& a, hipStream_t stream);
+hipError_t launch_clear(void* p, size_t bytes, hipStream_t stream);
 
 struct WalkArgs {
   const void* tgt;
@@ -129,6 +163,9 @@ struct WalkArgs {
   int32_t spin_limit;
   int32_t node_cap;         // LDS capacity in nodes (>= nodes of any request)
   int32_t tile_cap;         // LDS capacity in tiles (>= tiles of any slice)
+  // chain with lazy statistics: where the round stops and that row's pair
+  const uint32_t* stop;     // null: statistics from the partials of every row
+  const uint64_t* row_words;
 };
 
 size_t walk_lds_bytes(int node_cap, int tile_cap);

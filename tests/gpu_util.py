@@ -32,17 +32,27 @@ def f32(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
 
 
-def run_sample(ci, status=None, workspace=None, max_new=None, eos_id=-1):
+def run_sample(ci, status=None, workspace=None, max_new=None, eos_id=-1, diag=True):
+    """diag=True also asks for the per-row diagnostics, which makes the library
+    compute every row's statistics; diag=False is the lazy path that skips the
+    rows after the break (where rows are not shared between requests)."""
     tgt = rows_to_dev(ci.target, ci.t_kind)
     dft = rows_to_dev(ci.draft, ci.q_kind)
     mn = i32(max_new) if max_new is not None else None
     tok, cnt, acc, dg, rs = sv.sv_verify_sample(
         tgt, dft, i32(ci.t_row_start), i32(ci.q_row_start), i32(ci.draft_ids[:, :ci.k_max]),
-        i32(ci.draft_len), ci.T, f32(ci.uniforms), max_new=mn, eos_id=eos_id, diag=True,
-        dev_status=status, workspace=workspace)
+        i32(ci.draft_len), ci.T, f32(ci.uniforms), max_new=mn, eos_id=eos_id, diag=diag,
+        resid=True, dev_status=status, workspace=workspace)
     torch.cuda.synchronize()
     return dict(tokens=tok.cpu().numpy(), count=cnt.cpu().numpy(), accepted=acc.cpu().numpy(),
-                diag=dg.cpu().numpy(), resid=rs.cpu().numpy())
+                diag=dg.cpu().numpy() if diag else None, resid=rs.cpu().numpy())
+
+
+def same_round(a, b, keys=("tokens", "count", "accepted", "resid")):
+    """Both verify paths (all rows' statistics / lazy statistics) combine the
+    same segment pairs in the same order: identical outputs."""
+    for k in keys:
+        assert np.array_equal(a[k], b[k]), k
 
 
 def run_greedy(target, kind, t_row_start, draft_ids, draft_len, max_new=None, eos_id=-1,
