@@ -165,6 +165,18 @@ __device__ __forceinline__ MS wave_ms_dpp(MS v) {
             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v.s), kWave - 1))};
 }
 
+// Canonical combine of n per-segment pairs, shared by every consumer that
+// must agree bit for bit: lane l folds segments l, l + 64, l + 128, ... in
+// order, then the wave combines its lanes (wave_ms_dpp).  Valid in every lane
+// of the calling wave.  `pair(s)` returns segment s's pair.
+template <class Pair>
+__device__ __forceinline__ MS wave_combine_segments(int n, Pair pair) {
+  const int lane = threadIdx.x & (kWave - 1);
+  MS acc{-INFINITY, 0.f};
+  for (int s = lane; s < n; s += kWave) acc = ms_combine(acc, pair(s));
+  return wave_ms_dpp(acc);
+}
+
 __device__ __forceinline__ void flag(int32_t* status, int bits) {
   if (status != nullptr && bits != 0) atomicOr(status, bits);
 }

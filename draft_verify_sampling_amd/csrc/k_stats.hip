@@ -209,14 +209,15 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
     ok &= done;
     if (s < a.nseg) s_w[s] = v;
   }
+  // the canonical combine of the segment pairs (the walk combines the
+  // partials of every row the same way)
+  const MS row = wave_combine_segments(a.nseg, [&](int s) { return word_pair(s_w[s]); });
   if (lane != 0) return;
   bool stop_here;
   if (!ok) {
     flag(a.status, kFlagSyncTimeout);
     stop_here = true;
   } else {
-    MS row = word_pair(s_w[0]);
-    for (int s = 1; s < a.nseg; ++s) row = ms_combine(row, word_pair(s_w[s]));
     __hip_atomic_store(a.row_words + static_cast<int64_t>(b) * R + i, pair_word(row), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
     stop_here = !(row.s > 0.f && row.s < INFINITY);

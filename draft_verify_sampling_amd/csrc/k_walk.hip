@@ -321,15 +321,16 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
       if (wk.g == 0) walk_invalid<kChain>(a, b, bad, tid, kWalkBlock);
       return;
     }
-    if (tid < N) {
-      const float2* pp = staged ? s_part + tid * a.nseg : pbase + static_cast<int64_t>(tid) * a.nseg;
-      MS acc{-INFINITY, 0.f};
-      for (int sg = 0; sg < a.nseg; ++sg) {
+    for (int c = wid; c < N; c += kWalkWaves) {  // one wave per row
+      const float2* pp = staged ? s_part + c * a.nseg : pbase + static_cast<int64_t>(c) * a.nseg;
+      const MS acc = wave_combine_segments(a.nseg, [&](int sg) {
         const float2 v = pp[sg];
-        acc = ms_combine(acc, MS{v.x, v.y});
+        return MS{v.x, v.y};
+      });
+      if (lane == 0) {
+        s_m[c] = acc.m;
+        s_S[c] = acc.s;
       }
-      s_m[tid] = acc.m;
-      s_S[tid] = acc.s;
     }
     __syncthreads();
     if (tid < k) {  // node tid + 1 is tested against row tid (its parent)
