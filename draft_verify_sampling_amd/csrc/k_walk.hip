@@ -21,16 +21,18 @@
 // so every rejection costs one pass over the node's two rows that yields
 // R_{j+1} and the per-tile sums the final inverse-CDF draw needs.
 //
-// Statistics: a chain takes every row's softmax pair from the statistics
-// kernel, which streams all k + 1 target rows at full HBM rate before the
-// walk; the walk then needs no pass before its one weight pass.  A tree walk
-// computes the statistics of a node when it arrives there (one pass over that
-// row), so only the rows of its kept path are read.
+// Statistics: a chain takes its rows' softmax pairs from a statistics kernel
+// that runs before the walk -- either the segment pairs of every row, which
+// the prologue combines and decides, or (lazy statistics) the break row and
+// that row's pair, already decided -- so the walk needs no pass before its
+// one weight pass.  A tree walk computes the statistics of a node when it
+// arrives there (one pass over that row), so only the rows of its kept path
+// are read.
 //
 // Work split: G workgroups of 1024 threads per request, G chosen by the host
 // from the occupancy of this kernel so that the whole grid is resident at
-// once (one workgroup per CU: G = CUs / requests, at most 32).  Workgroup g owns a contiguous slice of the vocabulary's 2048-element
-// tiles; each pass (softmax pair of a target row, or a residual / plain weight
+// once (G = resident workgroups / requests, at most 32).  Workgroup g owns a
+// contiguous slice of the vocabulary's 2048-element tiles; each pass (softmax pair of a target row, or a residual / plain weight
 // pass) covers only the slice.  The G partial results of a pass are exchanged
 // through 64-bit words in the workspace: each workgroup stores its words with
 // relaxed agent-scope atomic stores and reads the others' with relaxed
