@@ -180,6 +180,30 @@ def sv_softmax_partials(rows: torch.Tensor, temperature: float, out: Optional[to
     return out
 
 
+def prepare_softmax_partials(rows: torch.Tensor, temperature: float, out: torch.Tensor, stream=None):
+    """sv_softmax_partials with its arguments marshalled once: returns a
+    callable that enqueues the same launch again (for tight launch loops
+    whose host cost must stay below the kernel's run time).  The callable
+    holds the tensors it points into."""
+    lib = load()
+    n_rows, V = rows.shape
+    nseg = sv_softmax_segments(n_rows, V)
+    if out.shape != (n_rows, nseg, 2):
+        raise SpecVerifyError(f"out must be [{n_rows}, {nseg}, 2]")
+    args = (_dev(rows, "rows"), _dtype_code(rows), n_rows, V, float(temperature),
+            _dev(out, "out", torch.float32, rows.device), _stream(stream))
+    fn = lib.sv_softmax_partials
+    keep = (rows, out)
+
+    def launch():
+        _ = keep
+        status = fn(*args)
+        if status != 0:
+            _check(status, "sv_softmax_partials")
+
+    return launch
+
+
 def sv_ngram_draft(ctx: torch.Tensor, ctx_len: torch.Tensor, window: int, k: int,
                    dev_status: Optional[torch.Tensor] = None, stream=None):
     """Prompt-lookup drafts: returns (draft_ids int32 [B, k], draft_len int32 [B])."""
@@ -221,18 +245,9 @@ def sv_verify_greedy(target: torch.Tensor, t_row_start: torch.Tensor, draft_ids:
     return tok, cnt, acc
 
 
-def sv_verify_sample(target: torch.Tensor, draft: torch.Tensor, t_row_start: torch.Tensor,
-                     q_row_start: torch.Tensor, draft_ids: torch.Tensor, draft_len: torch.Tensor,
-                     temperature: float, uniforms: torch.Tensor,
-                     max_new: Optional[torch.Tensor] = None, eos_id: int = -1,
-                     diag: bool = False, dev_status: Optional[torch.Tensor] = None,
-                     workspace: Optional[Workspace] = None, stream=None, out=None,
-                     resid: Optional[bool] = None):
-    """Speculative-sampling verify.  Returns (tokens [B, k_max+1], count, accepted,
-    diag [B, k_max+1, 4] or None, resid [B] or None).  ``out`` may pass a
-    preallocated (tokens, count, accepted, diag, resid) tuple.  ``resid``
-    (default: same as ``diag``) asks for the residual masses."""
-    lib = load()
+def _sample_args(target, draft, t_row_start, q_row_start, draft_ids, draft_len, temperature, uniforms,
+                 max_new, eos_id, diag, dev_status, workspace, stream, out, resid):
+    """Checked, marshalled argument list of sv_verify_sample and its outputs."""
     t_rows, V = target.shape
     q_rows = draft.shape[0]
     if draft.shape[1] != V:
@@ -253,20 +268,65 @@ def sv_verify_sample(target: torch.Tensor, draft: torch.Tensor, t_row_start: tor
         tok, cnt, acc, dg, rs = out
     nb = workspace_bytes(SV_OP_SAMPLE, B, t_rows, V)
     ws = _workspace(workspace, dev, stream, nb)
-    _check(lib.sv_verify_sample(_dev(target, "target"), _dtype_code(target), t_rows,
-                                _dev(draft, "draft"), _dtype_code(draft), q_rows, V,
-                                _dev(t_row_start, "t_row_start", torch.int32, dev),
-                                _dev(q_row_start, "q_row_start", torch.int32, dev),
-                                _dev(draft_ids, "draft_ids", torch.int32, dev),
-                                _dev(draft_len, "draft_len", torch.int32, dev), B, k_max,
-                                float(temperature), _dev(uniforms, "uniforms", torch.float32, dev),
-                                _dev(max_new, "max_new", torch.int32, dev), eos_id,
-                                _dev(tok, "out"), _dev(cnt, "cnt"), _dev(acc, "acc"),
-                                _dev(dg, "diag", torch.float32, dev), _dev(rs, "resid", torch.float32, dev),
-                                _dev(dev_status, "dev_status", torch.int32, dev),
-                                ws.data_ptr(), ws.numel(), _stream(stream)),
-           "sv_verify_sample")
-    return tok, cnt, acc, dg, rs
+    args = (_dev(target, "target"), _dtype_code(target), t_rows,
+            _dev(draft, "draft"), _dtype_code(draft), q_rows, V,
+            _dev(t_row_start, "t_row_start", torch.int32, dev),
+            _dev(q_row_start, "q_row_start", torch.int32, dev),
+            _dev(draft_ids, "draft_ids", torch.int32, dev),
+            _dev(draft_len, "draft_len", torch.int32, dev), B, k_max,
+            float(temperature), _dev(uniforms, "uniforms", torch.float32, dev),
+            _dev(max_new, "max_new", torch.int32, dev), eos_id,
+            _dev(tok, "out"), _dev(cnt, "cnt"), _dev(acc, "acc"),
+            _dev(dg, "diag", torch.float32, dev), _dev(rs, "resid", torch.float32, dev),
+            _dev(dev_status, "dev_status", torch.int32, dev),
+            ws.data_ptr(), ws.numel(), _stream(stream))
+    return args, (tok, cnt, acc, dg, rs), ws
+
+
+def sv_verify_sample(target: torch.Tensor, draft: torch.Tensor, t_row_start: torch.Tensor,
+                     q_row_start: torch.Tensor, draft_ids: torch.Tensor, draft_len: torch.Tensor,
+                     temperature: float, uniforms: torch.Tensor,
+                     max_new: Optional[torch.Tensor] = None, eos_id: int = -1,
+                     diag: bool = False, dev_status: Optional[torch.Tensor] = None,
+                     workspace: Optional[Workspace] = None, stream=None, out=None,
+                     resid: Optional[bool] = None):
+    """Speculative-sampling verify.  Returns (tokens [B, k_max+1], count, accepted,
+    diag [B, k_max+1, 4] or None, resid [B] or None).  ``out`` may pass a
+    preallocated (tokens, count, accepted, diag, resid) tuple.  ``resid``
+    (default: same as ``diag``) asks for the residual masses."""
+    lib = load()
+    args, outs, _ = _sample_args(target, draft, t_row_start, q_row_start, draft_ids, draft_len, temperature,
+                                 uniforms, max_new, eos_id, diag, dev_status, workspace, stream, out, resid)
+    _check(lib.sv_verify_sample(*args), "sv_verify_sample")
+    return outs
+
+
+def prepare_verify_sample(target: torch.Tensor, draft: torch.Tensor, t_row_start: torch.Tensor,
+                          q_row_start: torch.Tensor, draft_ids: torch.Tensor, draft_len: torch.Tensor,
+                          temperature: float, uniforms: torch.Tensor,
+                          max_new: Optional[torch.Tensor] = None, eos_id: int = -1,
+                          diag: bool = False, dev_status: Optional[torch.Tensor] = None,
+                          workspace: Optional[Workspace] = None, stream=None, out=None,
+                          resid: Optional[bool] = None):
+    """sv_verify_sample with its arguments checked and marshalled once.  Returns
+    (launch, outputs): launch() enqueues the same call again on the same
+    buffers, for loops whose host cost must stay below the GPU's.  The
+    callable holds every tensor it points into (the workspace buffer too), so
+    none is freed while it lives."""
+    lib = load()
+    args, outs, ws = _sample_args(target, draft, t_row_start, q_row_start, draft_ids, draft_len, temperature,
+                                  uniforms, max_new, eos_id, diag, dev_status, workspace, stream, out, resid)
+    fn = lib.sv_verify_sample
+    keep = (target, draft, t_row_start, q_row_start, draft_ids, draft_len, uniforms, max_new, dev_status,
+            outs, ws)
+
+    def launch():
+        _ = keep
+        status = fn(*args)
+        if status != 0:
+            _check(status, "sv_verify_sample")
+
+    return launch, outs
 
 
 def sv_verify_tree(target: torch.Tensor, draft: torch.Tensor, parent: torch.Tensor,

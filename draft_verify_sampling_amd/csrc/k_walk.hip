@@ -32,8 +32,9 @@
 // Work split: G workgroups of 1024 threads per request, G chosen by the host
 // from the occupancy of this kernel so that the whole grid is resident at
 // once (G = resident workgroups / requests, at most 32).  Workgroup g owns a
-// contiguous slice of the vocabulary's 2048-element tiles; each pass (softmax pair of a target row, or a residual / plain weight
-// pass) covers only the slice.  The G partial results of a pass are exchanged
+// contiguous slice of the vocabulary's 2048-element tiles; each pass (softmax
+// pair of a target row, or a residual / plain weight pass) covers only the
+// slice.  The G partial results of a pass are exchanged
 // through 64-bit words in the workspace: each workgroup stores its words with
 // relaxed agent-scope atomic stores and reads the others' with relaxed
 // agent-scope atomic loads until all carry their valid bit.  The data travels

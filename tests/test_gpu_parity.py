@@ -540,3 +540,28 @@ def test_gpu_graph_replay_matches_eager():
             assert torch.equal(got, w), rep
         sv.sv_verify_sample(*oargs, other.T, f32(other.uniforms))   # eager work in between
         torch.cuda.synchronize()
+
+
+def test_gpu_prepared_calls_match_direct_calls():
+    """The pre-marshalled launchers enqueue exactly the calls they were
+    prepared from: same outputs as the direct calls, call after call."""
+    say("prepared sv_verify_sample / sv_softmax_partials launchers")
+    import draft_verify_sampling_amd as sv
+    ci = synth.c3_sampled(B=12, k=3, V=30_001, T=0.9, salt=21)
+    args = [rows_to_dev(ci.target, "bf16"), rows_to_dev(ci.draft, "bf16"), i32(ci.t_row_start),
+            i32(ci.q_row_start), i32(ci.draft_ids), i32(ci.draft_len)]
+    u = f32(ci.uniforms)
+    want = [t.clone() for t in sv.sv_verify_sample(*args, ci.T, u)[:3]]
+    launch, outs = sv.prepare_verify_sample(*args, ci.T, u, workspace=sv.Workspace())
+    part_want = sv.sv_softmax_partials(args[0], ci.T)
+    part = torch.full_like(part_want, -5.0)
+    plaunch = sv.prepare_softmax_partials(args[0], ci.T, part)
+    for rep in range(3):
+        for t in outs[:3]:
+            t.fill_(-7)
+        launch()
+        plaunch()
+        torch.cuda.synchronize()
+        for got, w in zip(outs[:3], want):
+            assert torch.equal(got, w), rep
+        assert torch.equal(part, part_want), rep
