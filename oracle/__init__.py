@@ -42,18 +42,27 @@ print, closed forms, or brute force):
                                  small contexts, hand cases.
 * ``tree.verify_tree``          chain-as-tree equals ``verify_sample``; exact
                                  law on V=8 with i.i.d. sampled siblings.
+* ``tree.verify_tree_greedy``   chain-as-tree equals ``verify_greedy``; equals
+                                 ``verify_tree`` on one-hot target rows; every
+                                 emitted token is the argmax of the previous
+                                 kept node's row (brute force on small trees).
+* ``tree.verify_tree_pointmass`` exact law on V=8 for fixed candidate sets
+                                 (duplicates included): each emitted token
+                                 follows the row it is drawn against; equals
+                                 ``verify_tree`` when every draft row is one-hot
+                                 at the node's single child.
 """
 from .rows import widen, FLAG_BAD_REQUEST, FLAG_BAD_TOKEN, FLAG_NONFINITE, \
     FLAG_OVER_BUDGET, FLAG_FALLBACK, FLAG_BAD_TREE, INVALID_FLAGS
 from .chain import (verify_sample, verify_greedy, greedy_path_verify,
                     forward_accounting, naive_round, softmax_T, inverse_cdf)
 from .ngram import ngram_draft
-from .tree import verify_tree
+from .tree import verify_tree, verify_tree_greedy, verify_tree_pointmass
 
 __all__ = [
     "widen", "verify_sample", "verify_greedy", "greedy_path_verify",
     "forward_accounting", "naive_round", "softmax_T", "inverse_cdf",
-    "ngram_draft", "verify_tree",
+    "ngram_draft", "verify_tree", "verify_tree_greedy", "verify_tree_pointmass",
     "FLAG_BAD_REQUEST", "FLAG_BAD_TOKEN", "FLAG_NONFINITE", "FLAG_OVER_BUDGET",
     "FLAG_FALLBACK", "FLAG_BAD_TREE", "INVALID_FLAGS",
 ]

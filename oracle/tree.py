@@ -132,3 +132,162 @@ def verify_tree(target, t_kind, draft, q_kind, V, parent, token, T, uniforms,
     if with_diag:
         out["diag"] = diag
     return out
+
+
+def _tree_shape_flags(par, tok, V, N):
+    """FLAG_BAD_TREE / FLAG_BAD_TOKEN of one request's tree, else 0."""
+    if par[0] != -1 or any(not (0 <= par[c] < c) for c in range(1, N)):
+        return FLAG_BAD_TREE
+    if any(not (0 <= tok[c] < V) for c in range(1, N)):
+        return FLAG_BAD_TOKEN
+    return 0
+
+
+def verify_tree_greedy(target, t_kind, V, parent, token):
+    """Greedy (T = 0) tree verify.
+
+    "Speculative Decoding II", EAGLE section: the flattened tree is verified in
+    one target forward and the kept path is the one the target model itself
+    would have produced; at T = 0 the target's pick at a node is the argmax of
+    that node's row ("第 13 篇：推理引擎一次猜几个字——草稿 + 验证", section ③:
+    the model's own next token at each drafted position), so verification
+    follows the target's picks down the tree.
+
+    Steps, per request (node 0 is the root):
+
+    1. cur = root; a = argmax of cur's target row (the lowest id among equal
+       maxima; a row holding a NaN makes the request invalid).
+    2. The first child c of cur, in flattened order, whose token is a is kept:
+       emit a, cur = c, go to 1.  If no child carries a, emit a and stop (at a
+       leaf this is the extra token from the leaf's own row).
+
+    Only the rows of the visited nodes are read.  Returns tokens [B, N] (-1
+    padded), count [B], accepted [B], path [B, N] (kept node ids, -1 padded),
+    flags [B].
+    """
+    parent = np.asarray(parent)
+    token = np.asarray(token)
+    B, N = parent.shape
+    tokens = np.full((B, N), -1, dtype=np.int64)
+    count = np.zeros(B, dtype=np.int64)
+    accepted = np.zeros(B, dtype=np.int64)
+    path = np.full((B, N), -1, dtype=np.int64)
+    flags = np.zeros(B, dtype=np.int64)
+    for b in range(B):
+        par = [int(v) for v in parent[b]]
+        tok = [int(v) for v in token[b]]
+        bad = _tree_shape_flags(par, tok, V, N)
+        if bad:
+            flags[b] |= bad
+            continue
+        children = [[] for _ in range(N)]
+        for c in range(1, N):
+            children[par[c]].append(c)
+        cur, emitted, kept = 0, [], []
+        while True:
+            row = widen(target[b * N + cur], t_kind)
+            if np.isnan(row).any():
+                flags[b] |= FLAG_NONFINITE
+                break
+            a = int(np.argmax(row))
+            emitted.append(a)
+            nxt = next((c for c in children[cur] if tok[c] == a), None)
+            if nxt is None:
+                break
+            kept.append(nxt)
+            cur = nxt
+        if flags[b] & FLAG_NONFINITE:
+            continue
+        tokens[b, :len(emitted)] = emitted
+        count[b] = len(emitted)
+        accepted[b] = len(kept)
+        path[b, :len(kept)] = kept
+    return dict(tokens=tokens, count=count, accepted=accepted, path=path, flags=flags)
+
+
+def verify_tree_pointmass(target, t_kind, V, parent, token, T, uniforms):
+    """Tree verify with every sibling taken as a point mass.
+
+    The recursive speculative sampling of "Speculative Decoding II" (EAGLE
+    section, verification as in SpecInfer) keeps the target's law when each
+    candidate is a draw from the q it is tested against.  EAGLE-2's dynamic
+    tree (same page, worked example) picks its candidates deterministically
+    (top-k by confidence), so each one is tested here as a draw from the point
+    mass q = delta_x on its own token: keep x with probability
+    min(1, p(x)/1) = p(x); after a rejection p <- norm(max(0, p - delta_x)),
+    i.e. x's mass is removed and the rest renormalised (the residual step of
+    "投机解码:为什么一个字都不改", section "改进", with q = delta_x).  Each
+    step is then the identity min(p, q) + (1 - alpha) norm(max(0, p - q)) = p
+    of that section, so the output follows p for any candidate set.
+
+    Steps, per request:
+
+    1. cur = root, p = softmax(target row of cur / T).
+    2. For each child c of cur in flattened order, u = u[b, c-1]: keep c iff
+       u < p(x_c).  Kept: emit x_c, cur = c, reload p, go to 2.  Not kept:
+       r = p with x_c's entry set to 0; if sum r > 0, p <- r / sum r, else p
+       is left as it was and the fallback bit is set.
+    3. When no child is kept, or cur is a leaf, draw the last token from the
+       current p with u[b, N-1] (inverse CDF).
+
+    Returns tokens, count, accepted, path, flags and margins [B, N] (distance
+    of each used uniform to its decision edge) like ``verify_tree``.
+    """
+    parent = np.asarray(parent)
+    token = np.asarray(token)
+    B, N = parent.shape
+    tokens = np.full((B, N), -1, dtype=np.int64)
+    count = np.zeros(B, dtype=np.int64)
+    accepted = np.zeros(B, dtype=np.int64)
+    path = np.full((B, N), -1, dtype=np.int64)
+    flags = np.zeros(B, dtype=np.int64)
+    margins = np.full((B, N), np.nan, dtype=np.float64)
+    for b in range(B):
+        par = [int(v) for v in parent[b]]
+        tok = [int(v) for v in token[b]]
+        bad = _tree_shape_flags(par, tok, V, N)
+        if bad:
+            flags[b] |= bad
+            continue
+        children = [[] for _ in range(N)]
+        for c in range(1, N):
+            children[par[c]].append(c)
+        u = np.asarray(uniforms[b], dtype=np.float64)
+        cur = 0
+        p, _, S = softmax_T(widen(target[b * N + cur], t_kind), T)
+        ok = np.isfinite(S) and S > 0
+        emitted, kept = [], []
+        while ok:
+            nxt = None
+            for c in children[cur]:
+                x = tok[c]
+                margins[b, c - 1] = abs(u[c - 1] - p[x])
+                if u[c - 1] < p[x]:
+                    nxt = c
+                    break
+                r = p.copy()
+                r[x] = 0.0
+                R = np.sum(r)
+                if R > 0.0:
+                    p = r / R
+                else:
+                    flags[b] |= FLAG_FALLBACK
+            if nxt is None:
+                break
+            emitted.append(tok[nxt])
+            kept.append(nxt)
+            cur = nxt
+            p, _, S = softmax_T(widen(target[b * N + cur], t_kind), T)
+            ok = np.isfinite(S) and S > 0
+        if not ok:
+            flags[b] |= FLAG_NONFINITE
+            continue
+        y, _, marg = inverse_cdf(p, u[N - 1])
+        margins[b, N - 1] = marg
+        emitted.append(y)
+        tokens[b, :len(emitted)] = emitted
+        count[b] = len(emitted)
+        accepted[b] = len(kept)
+        path[b, :len(kept)] = kept
+    return dict(tokens=tokens, count=count, accepted=accepted, path=path,
+                flags=flags, margins=margins)

@@ -86,10 +86,13 @@ def chain_round_law(target, t_kind, draft, q_kind, V, k, T, seqs, weights):
     return dict(law)
 
 
-def tree_round_law(target, t_kind, draft, q_kind, V, T, parent, tokens_list, weights):
+def tree_round_law(target, t_kind, draft, q_kind, V, T, parent, tokens_list, weights,
+                   pointmass=False):
     """Law of the emitted tokens of one tree round.  All cases share the tree
     shape ``parent`` (N nodes) and rows (node c uses target/draft row c); case s
     has node tokens ``tokens_list[s]`` with probability ``weights[s]``.
+    ``pointmass``: the round is ``oracle.verify_tree_pointmass`` (no draft
+    rows) instead of ``oracle.verify_tree``.
 
     Decisions are integrated in the walk's order: the node-c test uses
     u[c-1]; the final draw uses u[N-1]."""
@@ -103,6 +106,8 @@ def tree_round_law(target, t_kind, draft, q_kind, V, T, parent, tokens_list, wei
         # every case reads the same rows: rows are indexed b*N + c, so give
         # each case a copy of the shared rows
         tgt = np.tile(target, (n, 1))
+        if pointmass:
+            return oracle.verify_tree_pointmass(tgt, t_kind, V, np.tile(parent, (n, 1)), tok_rows, T, u)
         dft = np.tile(draft, (n, 1))
         return oracle.verify_tree(tgt, t_kind, dft, q_kind, V,
                                   np.tile(parent, (n, 1)), tok_rows, T, u,
