@@ -181,7 +181,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c4", "c5", "c5g", "c5p"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--graph", action="store_true",
@@ -283,15 +283,17 @@ def main():
         torch.cuda.synchronize()
         tok0, cnt0 = out[0].cpu().numpy(), out[1].cpu().numpy()
         ms = 1e3 * wall / args.steps
-        rows_bytes = int(ci0.target.shape[0]) * ci0.V * (4 if ci0.t_kind == "f32" else 2)
-        # the dominant kernel alone: row statistics of every target row
-        part = torch.empty((ci0.target.shape[0], sv.sv_softmax_segments(ci0.target.shape[0], ci0.V), 2),
-                           dtype=torch.float32, device=dev)
-
-        stats = [sv.prepare_softmax_partials(d["tgt"], ci0.T, part) for d in dsets]
+        # the dominant kernel alone: row statistics of every target row (the
+        # input sets of a ragged workload differ in row count: one output
+        # buffer per set, and the mean of their bytes per launch)
+        esz = 4 if ci0.t_kind == "f32" else 2
+        rows_bytes = int(round(np.mean([d["tgt"].shape[0] * ci0.V * esz for d in dsets])))
+        parts = [torch.empty((d["tgt"].shape[0], sv.sv_softmax_segments(d["tgt"].shape[0], ci0.V), 2),
+                             dtype=torch.float32, device=dev) for d in dsets]
+        stats = [sv.prepare_softmax_partials(d["tgt"], ci0.T, p) for d, p in zip(dsets, parts)]
         st_avg = kernel_avg_us(stats, args.steps, args.warmup, torch) * 1e-6
         achieved = rows_bytes / st_avg / 1e9
-        fb = chain_formula_bytes(ci0)
+        fb = int(round(np.mean([chain_formula_bytes(ci) for ci in sets])))
         cfg["launch"] = "hip graph per step" if args.graph else "direct kernel launches per step"
         result.update(
             value=round(B / (ms * 1e-3), 1), unit="rounds/s", ms_per_step=round(ms, 5), config=cfg,
@@ -328,8 +330,11 @@ def main():
                torch.empty((B,), dtype=torch.int32, device=dev), torch.empty((B, N), dtype=torch.int32, device=dev),
                None)
 
+        launch = sv.prepare(sv.sv_verify_tree, d["tgt"], d["dft"], d["par"], d["tok"], ti.T, d["u"],
+                            workspace=ws, out=out)[0]
+
         def step(i):
-            sv.sv_verify_tree(d["tgt"], d["dft"], d["par"], d["tok"], ti.T, d["u"], workspace=ws, out=out)
+            launch()
 
         wall, tot_ms, ev_ms = timed(step, args.steps, args.warmup, torch)
         ms = 1e3 * wall / args.steps
@@ -346,6 +351,45 @@ def main():
                       tokens_per_s=round(float(out[1].sum().item()) / (ms * 1e-3), 1),
                       formula_bytes_per_step=fb, formula_GBps=round(fb / (ms * 1e-3) / 1e9, 1),
                       visited_target_row_bytes=visited_bytes,
+                      event_ms_per_step=dict(timed_region=round(tot_ms / args.steps, 5),
+                                             p50=round(float(np.percentile(ev_ms, 50)), 5)),
+                      roofline=None)
+    elif W in ("c5g", "c5p"):
+        # the same trees, verified greedily (argmax picks) or with every
+        # candidate tested as a point mass on its own token (no draft rows)
+        log("generating c5 inputs")
+        ti = synth.c5_tree()
+        tgt = _rows(ti.target, "bf16", torch, dev)
+        par, tok = _i32(ti.parent, torch, dev), _i32(ti.token, torch, dev)
+        u = torch.from_numpy(ti.uniforms).to(dev)
+        ws = sv.Workspace(dev)
+        B, N = ti.parent.shape
+        out = (torch.empty((B, N), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev), torch.empty((B, N), dtype=torch.int32, device=dev))
+        if W == "c5g":
+            launch = sv.prepare(sv.sv_verify_tree_greedy, tgt, par, tok, workspace=ws, out=out)[0]
+            name = "greedy tree verify (argmax picks)"
+        else:
+            launch = sv.prepare(sv.sv_verify_tree_pointmass, tgt, par, tok, ti.T, u, workspace=ws, out=out)[0]
+            name = "point-mass tree verify (each candidate tested as a point mass)"
+
+        def step(i):
+            launch()
+
+        wall, tot_ms, ev_ms = timed(step, args.steps, args.warmup, torch)
+        ms = 1e3 * wall / args.steps
+        acc = out[2].cpu().numpy()
+        visited_bytes = int((1 + acc).sum()) * ti.V * 2
+        result.update(value=round(B / (ms * 1e-3), 1), unit="rounds/s", ms_per_step=round(ms, 5),
+                      config=dict(workload=f"{name}: 32 requests, 60-node draft trees (depth <= 6, "
+                                           "branching <= 4), V=128,256, bf16 target rows, T=1", batch=32,
+                                  nodes=60, vocab=128_256, temperature=1.0, inputs="bf16"),
+                      tokens_per_s=round(float(out[1].sum().item()) / (ms * 1e-3), 1),
+                      mean_tokens_per_round=round(float(out[1].float().mean().item()), 4),
+                      visited_target_row_bytes=visited_bytes,
+                      visited_GBps=round(visited_bytes / (ms * 1e-3) / 1e9, 1),
+                      event_ms_per_step=dict(timed_region=round(tot_ms / args.steps, 5),
+                                             p50=round(float(np.percentile(ev_ms, 50)), 5)),
                       roofline=None)
     else:  # c2: prompt lookup + greedy verify
         log("generating c2 inputs")
@@ -356,9 +400,12 @@ def main():
         trs = _i32(np.arange(g.B) * (g.k + 1), torch, dev)
         ws = sv.Workspace(dev)
 
+        draft, (ids, lens) = sv.prepare(sv.sv_ngram_draft, ctx, cl, g.window, g.k)
+        verify = sv.prepare(sv.sv_verify_greedy, tgt, trs, ids, lens, workspace=ws)[0]
+
         def step(i):
-            ids, lens = sv.sv_ngram_draft(ctx, cl, g.window, g.k)
-            return sv.sv_verify_greedy(tgt, trs, ids, lens, workspace=ws)
+            draft()
+            verify()
 
         wall, tot_ms, ev_ms = timed(step, args.steps, args.warmup, torch)
         ms = 1e3 * wall / args.steps

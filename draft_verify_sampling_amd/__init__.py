@@ -24,6 +24,8 @@ __all__ = [
     "sv_softmax_partials", "sv_softmax_segments", "SV_F32", "SV_BF16", "SV_OP_GREEDY", "SV_OP_SAMPLE", "SV_OP_TREE",
     "FLAG_BAD_REQUEST", "FLAG_BAD_TOKEN", "FLAG_NONFINITE", "FLAG_OVER_BUDGET",
     "FLAG_FALLBACK", "FLAG_BAD_TREE", "FLAG_SYNC_TIMEOUT", "EXPORTS",
+    "sv_verify_tree_greedy", "sv_verify_tree_pointmass", "prepare", "prepare_verify_sample",
+    "prepare_softmax_partials",
 ]
 
 SV_F32, SV_BF16 = 0, 1
@@ -33,7 +35,8 @@ FLAG_OVER_BUDGET, FLAG_FALLBACK, FLAG_BAD_TREE, FLAG_SYNC_TIMEOUT = 8, 16, 32, 6
 
 EXPORTS = ("sv_abi_version", "sv_status_string", "sv_last_error", "sv_workspace_bytes",
            "sv_softmax_segments", "sv_softmax_partials",
-           "sv_ngram_draft", "sv_verify_greedy", "sv_verify_sample", "sv_verify_tree")
+           "sv_ngram_draft", "sv_verify_greedy", "sv_verify_sample", "sv_verify_tree",
+           "sv_verify_tree_greedy", "sv_verify_tree_pointmass")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -59,6 +62,9 @@ _SIGS = {
                                         F32, P, P, I32, P, P, P, P, P, P, P, SZ, P]),
     "sv_verify_tree": (ctypes.c_int, [P, I32, P, I32, I64, P, P, I32, I32, F32, P, P, P,
                                       P, P, P, P, P, SZ, P]),
+    "sv_verify_tree_greedy": (ctypes.c_int, [P, I32, I64, P, P, I32, I32, P, P, P, P, P, P, SZ, P]),
+    "sv_verify_tree_pointmass": (ctypes.c_int, [P, I32, I64, P, P, I32, I32, F32, P, P, P, P, P,
+                                                P, P, SZ, P]),
 }
 
 
@@ -131,6 +137,22 @@ def _dev(t: Optional[torch.Tensor], name: str, dtype=None, device=None):
     return t.data_ptr() if t.numel() else None
 
 
+def _shape(t: Optional[torch.Tensor], name: str, shape, dtype=None):
+    """A caller-provided tensor must have exactly the shape (and dtype) the
+    call reads or writes: the kernels index it by the call's sizes."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise SpecVerifyError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise SpecVerifyError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _status_arg(t: Optional[torch.Tensor]):
+    if t is not None and (t.numel() < 1 or t.dtype != torch.int32):
+        raise SpecVerifyError("dev_status must be an int32 tensor with at least one element")
+
+
 def _stream(stream) -> Optional[int]:
     s = torch.cuda.current_stream() if stream is None else stream
     return s.cuda_stream or None
@@ -161,6 +183,52 @@ def _workspace(ws: Optional[Workspace], device, stream, nbytes: int) -> torch.Te
     return ws.get(nbytes)
 
 
+# ---- calling the library -----------------------------------------------------
+#
+# Every entry point below checks its arguments, marshals them into one
+# argument tuple and hands it to _invoke, which calls the C function -- or,
+# inside prepare(), records the call so that it can be enqueued again later
+# without the host work of checking and marshalling.
+
+_CAPTURE = threading.local()
+
+
+def _invoke(name: str, args: tuple, keep: tuple, result):
+    rec = getattr(_CAPTURE, "calls", None)
+    fn = getattr(load(), name)
+    if rec is not None:
+        rec.append((fn, args, keep, name))
+    else:
+        _check(fn(*args), name)
+    return result
+
+
+def prepare(fn, *args, **kwargs):
+    """Check and marshal one call of a binding function (sv_verify_sample,
+    sv_verify_tree, ...) without running it.  Returns (launch, result):
+    launch() enqueues the identical call (same tensors, same stream, same
+    workspace buffer) and result holds the output tensors it writes.  For
+    loops whose host cost must stay below the GPU's run time.  The launcher
+    holds every tensor it points into, so none is freed while it lives."""
+    if getattr(_CAPTURE, "calls", None) is not None:
+        raise SpecVerifyError("prepare() does not nest")
+    _CAPTURE.calls = []
+    try:
+        result = fn(*args, **kwargs)
+        calls = _CAPTURE.calls
+    finally:
+        _CAPTURE.calls = None
+
+    def launch():
+        for f, a, keep, name in calls:
+            status = f(*a)
+            if status != 0:
+                _check(status, name)
+
+    launch.held = [c[2] for c in calls]
+    return launch, result
+
+
 def sv_softmax_segments(n_rows: int, vocab: int) -> int:
     return int(load().sv_softmax_segments(n_rows, vocab))
 
@@ -169,53 +237,34 @@ def sv_softmax_partials(rows: torch.Tensor, temperature: float, out: Optional[to
                         stream=None) -> torch.Tensor:
     """Per-segment softmax pairs of every row: returns float32 [n_rows, nseg, 2]
     (scaled-domain max, sum); see include/specverify.h."""
-    lib = load()
     n_rows, V = rows.shape
     nseg = sv_softmax_segments(n_rows, V)
     if out is None:
         out = torch.empty((n_rows, nseg, 2), dtype=torch.float32, device=rows.device)
-    _check(lib.sv_softmax_partials(_dev(rows, "rows"), _dtype_code(rows), n_rows, V,
-                                   float(temperature), _dev(out, "out", torch.float32, rows.device),
-                                   _stream(stream)), "sv_softmax_partials")
-    return out
+    elif tuple(out.shape) != (n_rows, nseg, 2):
+        raise SpecVerifyError(f"out must be [{n_rows}, {nseg}, 2], got {tuple(out.shape)}")
+    args = (_dev(rows, "rows"), _dtype_code(rows), n_rows, V, float(temperature),
+            _dev(out, "out", torch.float32, rows.device), _stream(stream))
+    return _invoke("sv_softmax_partials", args, (rows, out), out)
 
 
 def prepare_softmax_partials(rows: torch.Tensor, temperature: float, out: torch.Tensor, stream=None):
-    """sv_softmax_partials with its arguments marshalled once: returns a
-    callable that enqueues the same launch again (for tight launch loops
-    whose host cost must stay below the kernel's run time).  The callable
-    holds the tensors it points into."""
-    lib = load()
-    n_rows, V = rows.shape
-    nseg = sv_softmax_segments(n_rows, V)
-    if out.shape != (n_rows, nseg, 2):
-        raise SpecVerifyError(f"out must be [{n_rows}, {nseg}, 2]")
-    args = (_dev(rows, "rows"), _dtype_code(rows), n_rows, V, float(temperature),
-            _dev(out, "out", torch.float32, rows.device), _stream(stream))
-    fn = lib.sv_softmax_partials
-    keep = (rows, out)
-
-    def launch():
-        _ = keep
-        status = fn(*args)
-        if status != 0:
-            _check(status, "sv_softmax_partials")
-
-    return launch
+    """prepare(sv_softmax_partials, ...): the launcher alone."""
+    return prepare(sv_softmax_partials, rows, temperature, out=out, stream=stream)[0]
 
 
 def sv_ngram_draft(ctx: torch.Tensor, ctx_len: torch.Tensor, window: int, k: int,
                    dev_status: Optional[torch.Tensor] = None, stream=None):
     """Prompt-lookup drafts: returns (draft_ids int32 [B, k], draft_len int32 [B])."""
-    lib = load()
     B, stride = ctx.shape
+    _shape(ctx_len, "ctx_len", (B,))
+    _status_arg(dev_status)
     ids = torch.empty((B, k), dtype=torch.int32, device=ctx.device)
     lens = torch.empty((B,), dtype=torch.int32, device=ctx.device)
-    _check(lib.sv_ngram_draft(_dev(ctx, "ctx", torch.int32), _dev(ctx_len, "ctx_len", torch.int32),
-                              B, stride, window, k, _dev(ids, "draft_ids"), _dev(lens, "draft_len"),
-                              _dev(dev_status, "dev_status", torch.int32), _stream(stream)),
-           "sv_ngram_draft")
-    return ids, lens
+    args = (_dev(ctx, "ctx", torch.int32), _dev(ctx_len, "ctx_len", torch.int32), B, stride, window, k,
+            _dev(ids, "draft_ids"), _dev(lens, "draft_len"), _dev(dev_status, "dev_status", torch.int32),
+            _stream(stream))
+    return _invoke("sv_ngram_draft", args, (ctx, ctx_len, ids, lens, dev_status), (ids, lens))
 
 
 def sv_verify_greedy(target: torch.Tensor, t_row_start: torch.Tensor, draft_ids: torch.Tensor,
@@ -223,64 +272,28 @@ def sv_verify_greedy(target: torch.Tensor, t_row_start: torch.Tensor, draft_ids:
                      eos_id: int = -1, dev_status: Optional[torch.Tensor] = None,
                      workspace: Optional[Workspace] = None, stream=None):
     """Greedy verify; returns (tokens [B, k_max+1], count [B], accepted [B])."""
-    lib = load()
     t_rows, V = target.shape
     B = draft_len.shape[0]
     k_max = draft_ids.shape[1] if draft_ids.dim() == 2 else 0
+    _shape(t_row_start, "t_row_start", (B,))
+    _shape(draft_ids, "draft_ids", (B, k_max))
+    _shape(max_new, "max_new", (B,))
+    _status_arg(dev_status)
     dev = target.device
     tok = torch.empty((B, k_max + 1), dtype=torch.int32, device=dev)
     cnt = torch.empty((B,), dtype=torch.int32, device=dev)
     acc = torch.empty((B,), dtype=torch.int32, device=dev)
-    nb = workspace_bytes(SV_OP_GREEDY, B, t_rows, V)
-    ws = _workspace(workspace, dev, stream, nb)
-    _check(lib.sv_verify_greedy(_dev(target, "target"), _dtype_code(target), t_rows, V,
-                                _dev(t_row_start, "t_row_start", torch.int32, dev),
-                                _dev(draft_ids, "draft_ids", torch.int32, dev),
-                                _dev(draft_len, "draft_len", torch.int32, dev), B, k_max,
-                                _dev(max_new, "max_new", torch.int32, dev), eos_id,
-                                _dev(tok, "out"), _dev(cnt, "cnt"), _dev(acc, "acc"),
-                                _dev(dev_status, "dev_status", torch.int32, dev),
-                                ws.data_ptr(), ws.numel(), _stream(stream)),
-           "sv_verify_greedy")
-    return tok, cnt, acc
-
-
-def _sample_args(target, draft, t_row_start, q_row_start, draft_ids, draft_len, temperature, uniforms,
-                 max_new, eos_id, diag, dev_status, workspace, stream, out, resid):
-    """Checked, marshalled argument list of sv_verify_sample and its outputs."""
-    t_rows, V = target.shape
-    q_rows = draft.shape[0]
-    if draft.shape[1] != V:
-        raise SpecVerifyError("target and draft rows differ in length")
-    B = draft_len.shape[0]
-    k_max = draft_ids.shape[1] if draft_ids.dim() == 2 else 0
-    if uniforms.shape != (B, k_max + 1):
-        raise SpecVerifyError(f"uniforms must be [B, k_max+1] = [{B}, {k_max + 1}]")
-    dev = target.device
-    if out is None:
-        tok = torch.empty((B, k_max + 1), dtype=torch.int32, device=dev)
-        cnt = torch.empty((B,), dtype=torch.int32, device=dev)
-        acc = torch.empty((B,), dtype=torch.int32, device=dev)
-        dg = torch.zeros((B, k_max + 1, 4), dtype=torch.float32, device=dev) if diag else None
-        want_resid = diag if resid is None else resid
-        rs = torch.zeros((B,), dtype=torch.float32, device=dev) if want_resid else None
-    else:
-        tok, cnt, acc, dg, rs = out
-    nb = workspace_bytes(SV_OP_SAMPLE, B, t_rows, V)
-    ws = _workspace(workspace, dev, stream, nb)
-    args = (_dev(target, "target"), _dtype_code(target), t_rows,
-            _dev(draft, "draft"), _dtype_code(draft), q_rows, V,
+    ws = _workspace(workspace, dev, stream, workspace_bytes(SV_OP_GREEDY, B, t_rows, V))
+    args = (_dev(target, "target"), _dtype_code(target), t_rows, V,
             _dev(t_row_start, "t_row_start", torch.int32, dev),
-            _dev(q_row_start, "q_row_start", torch.int32, dev),
             _dev(draft_ids, "draft_ids", torch.int32, dev),
             _dev(draft_len, "draft_len", torch.int32, dev), B, k_max,
-            float(temperature), _dev(uniforms, "uniforms", torch.float32, dev),
             _dev(max_new, "max_new", torch.int32, dev), eos_id,
             _dev(tok, "out"), _dev(cnt, "cnt"), _dev(acc, "acc"),
-            _dev(dg, "diag", torch.float32, dev), _dev(rs, "resid", torch.float32, dev),
             _dev(dev_status, "dev_status", torch.int32, dev),
             ws.data_ptr(), ws.numel(), _stream(stream))
-    return args, (tok, cnt, acc, dg, rs), ws
+    keep = (target, t_row_start, draft_ids, draft_len, max_new, dev_status, tok, cnt, acc, ws)
+    return _invoke("sv_verify_greedy", args, keep, (tok, cnt, acc))
 
 
 def sv_verify_sample(target: torch.Tensor, draft: torch.Tensor, t_row_start: torch.Tensor,
@@ -294,39 +307,54 @@ def sv_verify_sample(target: torch.Tensor, draft: torch.Tensor, t_row_start: tor
     diag [B, k_max+1, 4] or None, resid [B] or None).  ``out`` may pass a
     preallocated (tokens, count, accepted, diag, resid) tuple.  ``resid``
     (default: same as ``diag``) asks for the residual masses."""
-    lib = load()
-    args, outs, _ = _sample_args(target, draft, t_row_start, q_row_start, draft_ids, draft_len, temperature,
-                                 uniforms, max_new, eos_id, diag, dev_status, workspace, stream, out, resid)
-    _check(lib.sv_verify_sample(*args), "sv_verify_sample")
-    return outs
-
-
-def prepare_verify_sample(target: torch.Tensor, draft: torch.Tensor, t_row_start: torch.Tensor,
-                          q_row_start: torch.Tensor, draft_ids: torch.Tensor, draft_len: torch.Tensor,
-                          temperature: float, uniforms: torch.Tensor,
-                          max_new: Optional[torch.Tensor] = None, eos_id: int = -1,
-                          diag: bool = False, dev_status: Optional[torch.Tensor] = None,
-                          workspace: Optional[Workspace] = None, stream=None, out=None,
-                          resid: Optional[bool] = None):
-    """sv_verify_sample with its arguments checked and marshalled once.  Returns
-    (launch, outputs): launch() enqueues the same call again on the same
-    buffers, for loops whose host cost must stay below the GPU's.  The
-    callable holds every tensor it points into (the workspace buffer too), so
-    none is freed while it lives."""
-    lib = load()
-    args, outs, ws = _sample_args(target, draft, t_row_start, q_row_start, draft_ids, draft_len, temperature,
-                                  uniforms, max_new, eos_id, diag, dev_status, workspace, stream, out, resid)
-    fn = lib.sv_verify_sample
+    t_rows, V = target.shape
+    q_rows = draft.shape[0]
+    if draft.shape[1] != V:
+        raise SpecVerifyError("target and draft rows differ in length")
+    B = draft_len.shape[0]
+    k_max = draft_ids.shape[1] if draft_ids.dim() == 2 else 0
+    if uniforms.shape != (B, k_max + 1):
+        raise SpecVerifyError(f"uniforms must be [B, k_max+1] = [{B}, {k_max + 1}]")
+    _shape(t_row_start, "t_row_start", (B,))
+    _shape(q_row_start, "q_row_start", (B,))
+    _shape(max_new, "max_new", (B,))
+    _status_arg(dev_status)
+    dev = target.device
+    if out is None:
+        tok = torch.empty((B, k_max + 1), dtype=torch.int32, device=dev)
+        cnt = torch.empty((B,), dtype=torch.int32, device=dev)
+        acc = torch.empty((B,), dtype=torch.int32, device=dev)
+        dg = torch.zeros((B, k_max + 1, 4), dtype=torch.float32, device=dev) if diag else None
+        want_resid = diag if resid is None else resid
+        rs = torch.zeros((B,), dtype=torch.float32, device=dev) if want_resid else None
+    else:
+        tok, cnt, acc, dg, rs = out
+        _shape(tok, "out tokens", (B, k_max + 1), torch.int32)
+        _shape(cnt, "out count", (B,), torch.int32)
+        _shape(acc, "out accepted", (B,), torch.int32)
+        _shape(dg, "out diag", (B, k_max + 1, 4), torch.float32)
+        _shape(rs, "out resid", (B,), torch.float32)
+    ws = _workspace(workspace, dev, stream, workspace_bytes(SV_OP_SAMPLE, B, t_rows, V))
+    args = (_dev(target, "target"), _dtype_code(target), t_rows,
+            _dev(draft, "draft"), _dtype_code(draft), q_rows, V,
+            _dev(t_row_start, "t_row_start", torch.int32, dev),
+            _dev(q_row_start, "q_row_start", torch.int32, dev),
+            _dev(draft_ids, "draft_ids", torch.int32, dev),
+            _dev(draft_len, "draft_len", torch.int32, dev), B, k_max,
+            float(temperature), _dev(uniforms, "uniforms", torch.float32, dev),
+            _dev(max_new, "max_new", torch.int32, dev), eos_id,
+            _dev(tok, "out"), _dev(cnt, "cnt"), _dev(acc, "acc"),
+            _dev(dg, "diag", torch.float32, dev), _dev(rs, "resid", torch.float32, dev),
+            _dev(dev_status, "dev_status", torch.int32, dev),
+            ws.data_ptr(), ws.numel(), _stream(stream))
     keep = (target, draft, t_row_start, q_row_start, draft_ids, draft_len, uniforms, max_new, dev_status,
-            outs, ws)
+            tok, cnt, acc, dg, rs, ws)
+    return _invoke("sv_verify_sample", args, keep, (tok, cnt, acc, dg, rs))
 
-    def launch():
-        _ = keep
-        status = fn(*args)
-        if status != 0:
-            _check(status, "sv_verify_sample")
 
-    return launch, outs
+def prepare_verify_sample(*args, **kwargs):
+    """prepare(sv_verify_sample, ...): (launch, outputs)."""
+    return prepare(sv_verify_sample, *args, **kwargs)
 
 
 def sv_verify_tree(target: torch.Tensor, draft: torch.Tensor, parent: torch.Tensor,
@@ -335,29 +363,90 @@ def sv_verify_tree(target: torch.Tensor, draft: torch.Tensor, parent: torch.Tens
                    workspace: Optional[Workspace] = None, stream=None, out=None):
     """Tree verify.  target/draft rows [B*N, V]; parent/node_token/uniforms [B, N].
     Returns (tokens [B, N], count, accepted, path [B, N], diag [B, N, 4] or None)."""
-    lib = load()
     B, N = parent.shape
     rows, V = target.shape
     if rows != B * N or draft.shape != target.shape:
         raise SpecVerifyError("target/draft must be [B*N, V]")
+    _shape(node_token, "node_token", (B, N))
+    _shape(uniforms, "uniforms", (B, N))
+    _status_arg(dev_status)
     dev = target.device
     if out is None:
-        tok = torch.empty((B, N), dtype=torch.int32, device=dev)
-        cnt = torch.empty((B,), dtype=torch.int32, device=dev)
-        acc = torch.empty((B,), dtype=torch.int32, device=dev)
-        pth = torch.empty((B, N), dtype=torch.int32, device=dev)
+        tok, cnt, acc, pth = _tree_outputs(B, N, dev, None)
         dg = torch.zeros((B, N, 4), dtype=torch.float32, device=dev) if diag else None
     else:
         tok, cnt, acc, pth, dg = out
-    nb = workspace_bytes(SV_OP_TREE, B, B * N, V)
-    ws = _workspace(workspace, dev, stream, nb)
-    _check(lib.sv_verify_tree(_dev(target, "target"), _dtype_code(target), _dev(draft, "draft"),
-                              _dtype_code(draft), V, _dev(parent, "parent", torch.int32, dev),
-                              _dev(node_token, "node_token", torch.int32, dev), B, N,
-                              float(temperature), _dev(uniforms, "uniforms", torch.float32, dev),
-                              _dev(tok, "out"), _dev(cnt, "cnt"), _dev(acc, "acc"), _dev(pth, "path"),
-                              _dev(dg, "diag", torch.float32, dev),
-                              _dev(dev_status, "dev_status", torch.int32, dev),
-                              ws.data_ptr(), ws.numel(), _stream(stream)),
-           "sv_verify_tree")
-    return tok, cnt, acc, pth, dg
+        _tree_outputs(B, N, dev, (tok, cnt, acc, pth))
+        _shape(dg, "out diag", (B, N, 4), torch.float32)
+    ws = _workspace(workspace, dev, stream, workspace_bytes(SV_OP_TREE, B, B * N, V))
+    args = (_dev(target, "target"), _dtype_code(target), _dev(draft, "draft"),
+            _dtype_code(draft), V, _dev(parent, "parent", torch.int32, dev),
+            _dev(node_token, "node_token", torch.int32, dev), B, N,
+            float(temperature), _dev(uniforms, "uniforms", torch.float32, dev),
+            _dev(tok, "out"), _dev(cnt, "cnt"), _dev(acc, "acc"), _dev(pth, "path"),
+            _dev(dg, "diag", torch.float32, dev),
+            _dev(dev_status, "dev_status", torch.int32, dev),
+            ws.data_ptr(), ws.numel(), _stream(stream))
+    keep = (target, draft, parent, node_token, uniforms, dev_status, tok, cnt, acc, pth, dg, ws)
+    return _invoke("sv_verify_tree", args, keep, (tok, cnt, acc, pth, dg))
+
+
+def _tree_outputs(B, N, dev, out):
+    if out is not None:
+        tok, cnt, acc, pth = out
+        _shape(tok, "out tokens", (B, N), torch.int32)
+        _shape(cnt, "out count", (B,), torch.int32)
+        _shape(acc, "out accepted", (B,), torch.int32)
+        _shape(pth, "out path", (B, N), torch.int32)
+        return out
+    return (torch.empty((B, N), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev),
+            torch.empty((B,), dtype=torch.int32, device=dev), torch.empty((B, N), dtype=torch.int32, device=dev))
+
+
+def sv_verify_tree_greedy(target: torch.Tensor, parent: torch.Tensor, node_token: torch.Tensor,
+                          dev_status: Optional[torch.Tensor] = None,
+                          workspace: Optional[Workspace] = None, stream=None, out=None):
+    """Greedy (T = 0) tree verify.  target rows [B*N, V]; parent/node_token [B, N].
+    Returns (tokens [B, N], count, accepted, path [B, N])."""
+    B, N = parent.shape
+    rows, V = target.shape
+    if rows != B * N:
+        raise SpecVerifyError("target must be [B*N, V]")
+    _shape(node_token, "node_token", (B, N))
+    _status_arg(dev_status)
+    dev = target.device
+    tok, cnt, acc, pth = _tree_outputs(B, N, dev, out)
+    ws = _workspace(workspace, dev, stream, workspace_bytes(SV_OP_TREE, B, B * N, V))
+    args = (_dev(target, "target"), _dtype_code(target), V, _dev(parent, "parent", torch.int32, dev),
+            _dev(node_token, "node_token", torch.int32, dev), B, N,
+            _dev(tok, "out"), _dev(cnt, "cnt"), _dev(acc, "acc"), _dev(pth, "path"),
+            _dev(dev_status, "dev_status", torch.int32, dev), ws.data_ptr(), ws.numel(), _stream(stream))
+    keep = (target, parent, node_token, dev_status, tok, cnt, acc, pth, ws)
+    return _invoke("sv_verify_tree_greedy", args, keep, (tok, cnt, acc, pth))
+
+
+def sv_verify_tree_pointmass(target: torch.Tensor, parent: torch.Tensor, node_token: torch.Tensor,
+                             temperature: float, uniforms: torch.Tensor,
+                             dev_status: Optional[torch.Tensor] = None,
+                             workspace: Optional[Workspace] = None, stream=None, out=None):
+    """Tree verify with every candidate tested as a point mass on its token.
+    target rows [B*N, V]; parent/node_token/uniforms [B, N].  Returns (tokens
+    [B, N], count, accepted, path [B, N])."""
+    B, N = parent.shape
+    rows, V = target.shape
+    if rows != B * N:
+        raise SpecVerifyError("target must be [B*N, V]")
+    if uniforms.shape != (B, N):
+        raise SpecVerifyError(f"uniforms must be [B, N] = [{B}, {N}]")
+    _shape(node_token, "node_token", (B, N))
+    _status_arg(dev_status)
+    dev = target.device
+    tok, cnt, acc, pth = _tree_outputs(B, N, dev, out)
+    ws = _workspace(workspace, dev, stream, workspace_bytes(SV_OP_TREE, B, B * N, V))
+    args = (_dev(target, "target"), _dtype_code(target), V, _dev(parent, "parent", torch.int32, dev),
+            _dev(node_token, "node_token", torch.int32, dev), B, N,
+            float(temperature), _dev(uniforms, "uniforms", torch.float32, dev),
+            _dev(tok, "out"), _dev(cnt, "cnt"), _dev(acc, "acc"), _dev(pth, "path"),
+            _dev(dev_status, "dev_status", torch.int32, dev), ws.data_ptr(), ws.numel(), _stream(stream))
+    keep = (target, parent, node_token, uniforms, dev_status, tok, cnt, acc, pth, ws)
+    return _invoke("sv_verify_tree_pointmass", args, keep, (tok, cnt, acc, pth))

@@ -62,15 +62,16 @@ int cu_count() {
 // own their rows take the lazy statistics (rows after the break are skipped);
 // chains with shared rows, and any call asking for diagnostics, take the
 // softmax partials of every row.  Trees compute statistics in the walk.
-sv_status launch_walk_call(bool chain, int32_t t_dtype, int32_t q_dtype, sv::WalkArgs& a, int64_t rows,
+sv_status launch_walk_call(int mode, int32_t t_dtype, int32_t q_dtype, sv::WalkArgs& a, int64_t rows,
                            int64_t nodes, int64_t node_cap, void* workspace, hipStream_t st,
                            const char* what) {
+  const bool chain = mode == sv::kWalkChain;
   const int64_t ntiles = sv::sample_tiles(a.V);
   const int64_t max_sync = sv::walk_max_sync(nodes);
   char* ws = static_cast<char*>(workspace);
   // G from the occupancy at the largest slice this kernel may get
   const size_t lds_max = sv::walk_lds_bytes(static_cast<int>(node_cap), static_cast<int>(ntiles));
-  const int occ = sv::walk_occupancy(chain, t_dtype, q_dtype, lds_max);
+  const int occ = sv::walk_occupancy(mode, t_dtype, q_dtype, lds_max);
   const int64_t resident = static_cast<int64_t>(occ) * std::max(cu_count(), 1);
   a.G = std::min<int32_t>(sv::walk_groups(a.B, a.V, resident),
                           static_cast<int32_t>(sv::walk_groups_bound(a.B)));
@@ -132,7 +133,7 @@ sv_status launch_walk_call(bool chain, int32_t t_dtype, int32_t q_dtype, sv::Wal
     clear_slots = false;  // the statistics kernel zeroed the exchange words
   }
   const size_t lds = sv::walk_lds_bytes(a.node_cap, a.tile_cap);
-  const hipError_t e = sv::launch_walk(chain, t_dtype, q_dtype, a, lds, clear_slots, st);
+  const hipError_t e = sv::launch_walk(mode, t_dtype, q_dtype, a, lds, clear_slots, st);
   return e == hipSuccess ? SV_OK : device_fail(e, what);
 }
 }  // namespace
@@ -314,7 +315,7 @@ sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t
   a.nseg = nseg;
   // a request has at most min(k_max + 1, t_rows) nodes
   const int64_t nodes = std::min<int64_t>(k_max + 1, t_rows);
-  return launch_walk_call(true, t_dtype, q_dtype, a, t_rows, nodes, k_max + 1, workspace,
+  return launch_walk_call(sv::kWalkChain, t_dtype, q_dtype, a, t_rows, nodes, k_max + 1, workspace,
                           static_cast<hipStream_t>(stream), "sv_verify_sample");
 }
 
@@ -361,8 +362,74 @@ sv_status sv_verify_tree(const void* target_logits, int32_t t_dtype, const void*
   a.status = dev_status;
   a.diag = out_diag;
   a.nseg = nseg;
-  return launch_walk_call(false, t_dtype, q_dtype, a, rows, n_nodes, n_nodes, workspace,
+  return launch_walk_call(sv::kWalkTree, t_dtype, q_dtype, a, rows, n_nodes, n_nodes, workspace,
                           static_cast<hipStream_t>(stream), "sv_verify_tree");
+}
+
+// Greedy and point-mass tree verify: the same walk without draft rows.
+static sv_status tree_variant(int mode, const void* target_logits, int32_t t_dtype, int64_t vocab,
+                              const int32_t* parent, const int32_t* node_token, int32_t batch,
+                              int32_t n_nodes, float temperature, const float* uniforms,
+                              int32_t* out_tokens, int32_t* out_count, int32_t* out_accepted,
+                              int32_t* out_path, int32_t* dev_status, void* workspace,
+                              size_t workspace_bytes, void* stream, const char* what) {
+  if (!dtype_ok(t_dtype)) return fail(SV_E_DTYPE, "t_dtype must be SV_F32 or SV_BF16");
+  if (batch < 0) return fail(SV_E_ARG, "batch < 0");
+  if (n_nodes < 1 || n_nodes > sv::kMaxTreeNodes) return fail(SV_E_ARG, "n_nodes must be in [1, 1024]");
+  if (vocab < 1 || vocab > sv::kMaxSampleVocab) return fail(SV_E_ARG, "tree vocab must be in [1, 4194304]");
+  const bool greedy = mode == sv::kWalkGreedy;
+  if (!greedy && (!(temperature > 0.f) || !std::isfinite(temperature)))
+    return fail(SV_E_ARG, "temperature must be finite and > 0");
+  if (batch == 0) return SV_OK;
+  if (target_logits == nullptr || parent == nullptr || node_token == nullptr ||
+      (!greedy && uniforms == nullptr) || out_tokens == nullptr || out_count == nullptr ||
+      out_accepted == nullptr || out_path == nullptr)
+    return fail(SV_E_ARG, "null pointer argument");
+  const int64_t rows = static_cast<int64_t>(batch) * n_nodes;
+  if (rows > INT32_MAX) return fail(SV_E_ARG, "too many rows");
+  const int32_t nseg = sv::row_segments(rows, vocab);
+  if (rows * nseg > kMaxGrid) return fail(SV_E_ARG, "too many rows");
+  const size_t need = sv_workspace_bytes(SV_OP_TREE, batch, rows, vocab);
+  if (sv_status s = check_workspace(workspace, workspace_bytes, need)) return s;
+
+  sv::WalkArgs a{};
+  a.tgt = target_logits;
+  a.V = vocab;
+  a.c = greedy ? 1.f : sv::kLog2e / temperature;
+  a.B = batch;
+  a.u = uniforms;
+  a.parent = parent;
+  a.token = node_token;
+  a.N = n_nodes;
+  a.out_path = out_path;
+  a.out_tok = out_tokens;
+  a.out_cnt = out_count;
+  a.out_acc = out_accepted;
+  a.status = dev_status;
+  a.nseg = nseg;
+  return launch_walk_call(mode, t_dtype, t_dtype, a, rows, n_nodes, n_nodes, workspace,
+                          static_cast<hipStream_t>(stream), what);
+}
+
+sv_status sv_verify_tree_greedy(const void* target_logits, int32_t t_dtype, int64_t vocab,
+                                const int32_t* parent, const int32_t* node_token, int32_t batch,
+                                int32_t n_nodes, int32_t* out_tokens, int32_t* out_count,
+                                int32_t* out_accepted, int32_t* out_path, int32_t* dev_status,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return tree_variant(sv::kWalkGreedy, target_logits, t_dtype, vocab, parent, node_token, batch, n_nodes,
+                      0.f, nullptr, out_tokens, out_count, out_accepted, out_path, dev_status, workspace,
+                      workspace_bytes, stream, "sv_verify_tree_greedy");
+}
+
+sv_status sv_verify_tree_pointmass(const void* target_logits, int32_t t_dtype, int64_t vocab,
+                                   const int32_t* parent, const int32_t* node_token, int32_t batch,
+                                   int32_t n_nodes, float temperature, const float* uniforms,
+                                   int32_t* out_tokens, int32_t* out_count, int32_t* out_accepted,
+                                   int32_t* out_path, int32_t* dev_status, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return tree_variant(sv::kWalkPoint, target_logits, t_dtype, vocab, parent, node_token, batch, n_nodes,
+                      temperature, uniforms, out_tokens, out_count, out_accepted, out_path, dev_status,
+                      workspace, workspace_bytes, stream, "sv_verify_tree_pointmass");
 }
 
 }  // extern "C"

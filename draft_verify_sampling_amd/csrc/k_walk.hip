@@ -168,14 +168,14 @@ __device__ bool row_stats(Walk& wk, const void* trow, MS* s_wms, MS& out) {
 // index); then, across the request, the total W and the NaN-ness of the draft
 // row's sum.  Every slice's total stays readable in the exchanged words until
 // the next exchange.
-template <class DT, class DQ>
+template <class DT, class DQ, bool kQ = true>
 __device__ bool weight_pass(Walk& wk, const DrawRow& r, double* wt, double* s_wq, double& W, bool& qnan) {
   const WalkArgs& a = *wk.a;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   double qw = 0.0;
   for (int t = wk.lo + wid; t < wk.hi; t += kWalkWaves) {
     double v[1][3];
-    wave_tile_sums<DT, DQ, 1>(r, a.V, t, 0, v);
+    wave_tile_sums<DT, DQ, 1, kQ>(r, a.V, t, 0, v);
     if (lane == 0) wt[t - wk.lo] = v[0][0];
     qw += v[0][2];
   }
@@ -201,6 +201,58 @@ __device__ bool weight_pass(Walk& wk, const DrawRow& r, double* wt, double* s_wq
   return true;
 }
 
+// Argmax of a target row over the slice, combined across the request (the
+// largest value, the lowest id among equal values); nan: the row holds a NaN.
+template <class DT>
+__device__ bool row_argmax(Walk& wk, const void* trow, uint64_t* s_key, uint32_t* s_knan, int& amax,
+                           bool& nan) {
+  const WalkArgs& a = *wk.a;
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  ArgBest s{-INFINITY, 0x7fffffff, false};
+  for (int t = wk.lo + wid; t < wk.hi; t += kWalkWaves) lane_tile_argmax<DT>(trow, a.V, t, s);
+  uint64_t key = (static_cast<uint64_t>(order_bits(s.v)) << 32) | static_cast<uint32_t>(~s.i);
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(key), off, kWave);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(key >> 32), off, kWave);
+    const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
+    key = o > key ? o : key;
+  }
+  const bool wnan = __ballot(s.nan) != 0;
+  if (lane == 0) {
+    s_key[wid] = key;
+    s_knan[wid] = wnan ? 1u : 0u;
+  }
+  __syncthreads();
+  uint64_t k = s_key[0];
+  uint32_t n = s_knan[0];
+  for (int w = 1; w < kWalkWaves; ++w) {
+    k = s_key[w] > k ? s_key[w] : k;
+    n |= s_knan[w];
+  }
+  if (!exchange(wk, kValid | (static_cast<uint64_t>(n) << 32) | (k >> 32), kValid | (k & 0xffffffffull)))
+    return false;
+  const uint64_t* x = last_words(wk);
+  uint64_t best = 0;
+  bool any_nan = false;
+  for (int h = 0; h < a.G; ++h) {
+    const uint64_t kk = ((x[2 * h] & 0xffffffffull) << 32) | (x[2 * h + 1] & 0xffffffffull);
+    best = kk > best ? kk : best;
+    any_nan |= ((x[2 * h] >> 32) & 1u) != 0;
+  }
+  amax = static_cast<int>(~static_cast<uint32_t>(best));
+  nan = any_nan;
+  return true;
+}
+
+// The workgroup whose slice holds tile t.
+__device__ __forceinline__ int tile_owner(int t, int ntiles, int G) {
+  int h = 0;
+  for (int g = 1; g < G; ++g)
+    if (static_cast<int64_t>(g) * ntiles / G <= t) h = g;
+  return h;
+}
+
 // Outputs of an invalid request: every token slot -1, counts 0, status bits.
 // Threads [first, first + stride, ...) write.
 template <bool kChain>
@@ -221,13 +273,21 @@ __device__ void walk_invalid(const WalkArgs& a, int b, int bits, int first, int 
 
 }  // namespace
 
-template <bool kChain, class DT, class DQ>
+template <int kMode, class DT, class DQ>
 __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
+  constexpr bool kChain = kMode == kWalkChain;
+  constexpr bool kPoint = kMode == kWalkPoint;
+  constexpr bool kGreedy = kMode == kWalkGreedy;
+  constexpr bool kUseQ = kMode == kWalkChain || kMode == kWalkTree;  // reads draft rows
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ uint64_t s_kids[2][kMaxNodeGroups];
   __shared__ uint64_t s_x[2][2 * kMaxWalkGroups];
   __shared__ MS s_wms[kWalkWaves];
   __shared__ double s_wq[kWalkWaves];
+  __shared__ uint64_t s_key[kGreedy ? kWalkWaves : 1];  // greedy: per-wave argmax keys
+  __shared__ uint32_t s_knan[kGreedy ? kWalkWaves : 1];
+  __shared__ double s_tot[kPoint ? kMaxWalkGroups : 1];  // point mass: slice totals
+  __shared__ double s_two[2];                            // point mass: one tile's sums
   __shared__ int s_ok[2];
   __shared__ int s_bad;
   __shared__ float2 s_part[kChain ? kPartStage : 1];  // chain: partials of the request's rows
@@ -243,6 +303,7 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
   float* s_u = s_qx + a.node_cap;
   float* s_m = s_u + a.node_cap;     // chain: softmax pair of every row, from the partials
   float* s_S = s_m + a.node_cap;
+  int32_t* s_ex = reinterpret_cast<int32_t*>(s_S + a.node_cap);  // point mass: ids removed at cur
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   Walk wk{&a, static_cast<int>(blockIdx.x) / a.G, static_cast<int>(blockIdx.x) % a.G, 0, 0, 0,
@@ -307,42 +368,42 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
       }
       __syncthreads();
     } else {
-    // round 2: every row's softmax partials (staged in LDS) and the target
-    // logit / draft probability at each drafted token
-    const int np = N * a.nseg;
-    const float2* pbase = a.partial + trow0 * a.nseg;
-    const bool staged = np <= kPartStage;
-    if (staged)
-      for (int i = tid; i < np; i += kWalkBlock) s_part[i] = pbase[i];
-    float lx = 0.f, qv = 0.f;
-    if (tid < k && tok_ok) {
-      lx = DT::at(row_ptr<DT>(a.tgt, trow0 + tid, V), tokv);
-      qv = DQ::at(row_ptr<DQ>(a.dq, qrow0 + tid, V), tokv);
-    }
-    __syncthreads();
-    if (const int bad = s_bad) {
-      if (wk.g == 0) walk_invalid<kChain>(a, b, bad, tid, kWalkBlock);
-      return;
-    }
-    for (int c = wid; c < N; c += kWalkWaves) {  // one wave per row
-      const float2* pp = staged ? s_part + c * a.nseg : pbase + static_cast<int64_t>(c) * a.nseg;
-      const MS acc = wave_combine_segments(a.nseg, [&](int sg) {
-        const float2 v = pp[sg];
-        return MS{v.x, v.y};
-      });
-      if (lane == 0) {
-        s_m[c] = acc.m;
-        s_S[c] = acc.s;
+      // round 2: every row's softmax partials (staged in LDS) and the target
+      // logit / draft probability at each drafted token
+      const int np = N * a.nseg;
+      const float2* pbase = a.partial + trow0 * a.nseg;
+      const bool staged = np <= kPartStage;
+      if (staged)
+        for (int i = tid; i < np; i += kWalkBlock) s_part[i] = pbase[i];
+      float lx = 0.f, qv = 0.f;
+      if (tid < k && tok_ok) {
+        lx = DT::at(row_ptr<DT>(a.tgt, trow0 + tid, V), tokv);
+        qv = DQ::at(row_ptr<DQ>(a.dq, qrow0 + tid, V), tokv);
+      }
+      __syncthreads();
+      if (const int bad = s_bad) {
+        if (wk.g == 0) walk_invalid<kChain>(a, b, bad, tid, kWalkBlock);
+        return;
+      }
+      for (int c = wid; c < N; c += kWalkWaves) {  // one wave per row
+        const float2* pp = staged ? s_part + c * a.nseg : pbase + static_cast<int64_t>(c) * a.nseg;
+        const MS acc = wave_combine_segments(a.nseg, [&](int sg) {
+          const float2 v = pp[sg];
+          return MS{v.x, v.y};
+        });
+        if (lane == 0) {
+          s_m[c] = acc.m;
+          s_S[c] = acc.s;
+        }
+      }
+      __syncthreads();
+      if (tid < k) {  // node tid + 1 is tested against row tid (its parent)
+        s_px[tid + 1] = ex2(fmaf(lx, a.c, -s_m[tid])) * (1.f / s_S[tid]);
+        s_qx[tid + 1] = qv;
       }
     }
-    __syncthreads();
-    if (tid < k) {  // node tid + 1 is tested against row tid (its parent)
-      s_px[tid + 1] = ex2(fmaf(lx, a.c, -s_m[tid])) * (1.f / s_S[tid]);
-      s_qx[tid + 1] = qv;
-    }
-    }
   } else {
-    // round 1: the tree and the uniforms
+    // round 1: the tree and the uniforms (the greedy walk has none)
     N = a.N;
     trow0 = qrow0 = static_cast<int64_t>(b) * a.N;
     __syncthreads();
@@ -355,7 +416,7 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
       if (bad) atomicOr(&s_bad, bad);
       s_par[c] = par;
       s_tok[c] = tok;
-      s_u[c] = a.u[trow0 + c];
+      s_u[c] = kGreedy ? 0.f : a.u[trow0 + c];
     }
     __syncthreads();
     if (const int bad = s_bad) {
@@ -373,6 +434,10 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
   float coef = 0.f, R = 1.f;
   double Rd = 1.0;
   MS st{0.f, 0.f};
+  int amax = 0;            // greedy: the argmax of cur's row
+  int n_ex = 0;            // point mass: ids removed from cur's distribution (s_ex)
+  bool have_pass = false;  // point mass: cur's tile sums are in s_wt0, slice totals in s_tot
+  double Wrest = 1.0;      // point mass: mass of cur's distribution left after the removals
   while (true) {
     // children of cur (one bit mask per 64 nodes, index order), and the target
     // logit / draft probability at their tokens, in flight during the pass
@@ -382,10 +447,18 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
       if (lane == 0) s_kids[step & 1][gi] = km;
     }
     const void* trow = row_ptr<DT>(a.tgt, trow0 + cur, V);
-    const void* qrow = row_ptr<DQ>(a.dq, qrow0 + cur, V);
+    const void* qrow = kUseQ ? row_ptr<DQ>(a.dq, qrow0 + cur, V) : nullptr;
     if constexpr (kChain) {
       st = MS{s_m[cur], s_S[cur]};
       ok = st.s > 0.f && st.s < INFINITY;
+      if (!ok) break;
+    } else if constexpr (kGreedy) {
+      bool nan = false;
+      if (!row_argmax<DT>(wk, trow, s_key, s_knan, amax, nan)) {
+        synced = false;
+        break;
+      }
+      ok = !nan;
       if (!ok) break;
     } else {
       float lx[kNodesPerThread], qv[kNodesPerThread];
@@ -395,7 +468,7 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
         lx[j] = qv[j] = 0.f;
         if (c < N && c > 0 && s_par[c] == cur) {
           lx[j] = DT::at(trow, s_tok[c]);
-          qv[j] = DQ::at(qrow, s_tok[c]);
+          if constexpr (kUseQ) qv[j] = DQ::at(qrow, s_tok[c]);
         }
       }
       if (!row_stats<DT>(wk, trow, s_wms, st)) {
@@ -414,7 +487,7 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
         }
       }
     }
-    const float invS = 1.f / st.s;
+    const float invS = kGreedy ? 1.f : 1.f / st.s;
     __syncthreads();
     const DrawRow base{trow, qrow, a.c, st.m, invS, 0.f, false};
     int kept = -1;
@@ -423,32 +496,100 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
       while (m != 0 && ok && synced) {
         const int ch = gi * kWave + __ffsll(static_cast<long long>(m)) - 1;
         m &= m - 1;
-        const float p = s_px[ch], q = s_qx[ch];
-        const float pc = coef == 0.f ? p : fmaxf(p - coef * q, 0.f) / R;
-        if (s_u[ch - 1] * q < pc) {
-          kept = ch;
-          break;
-        }
-        // rejected: residual pass with the next coefficient
-        DrawRow rr = base;
-        rr.coef = coef + R;
-        rr.use_q = true;
-        const int nb = npass & 1;
-        ++npass;
-        double W;
-        bool qnan;
-        if (!weight_pass<DT, DQ>(wk, rr, nb ? s_wt1 : s_wt0, s_wq, W, qnan)) {
-          synced = false;
-        } else if (qnan || !isfinite(W)) {
-          ok = false;
-        } else if (W > 0.0) {
-          coef = rr.coef;
-          R = static_cast<float>(W);
-          Rd = W;
-          tiles_buf = nb;
-        } else {  // no residual mass: keep the current distribution
-          fallback = kFlagFallback;
-          tiles_buf = -1;
+        if constexpr (kGreedy) {
+          // the target's own pick: the first child carrying it is kept
+          if (s_tok[ch] == amax) {
+            kept = ch;
+            break;
+          }
+        } else if constexpr (kPoint) {
+          // candidate x tested as a draw from the point mass on x: kept iff
+          // u < p'(x), p' = cur's distribution with the removed ids' mass
+          // taken out and renormalised (u Wrest < p(x))
+          const int x = s_tok[ch];
+          bool gone = false;
+          for (int i = 0; i < n_ex; ++i) gone |= s_ex[i] == x;
+          const float p = gone ? 0.f : s_px[ch];
+          if (static_cast<double>(s_u[ch - 1]) * Wrest < static_cast<double>(p)) {
+            kept = ch;
+            break;
+          }
+          if (gone) continue;  // removing it again changes nothing
+          // rejected: x leaves the distribution.  The first time at this
+          // node, one pass gives cur's tile sums and slice totals; after
+          // that only x's tile changes, re-summed by every workgroup alike.
+          if (!have_pass) {
+            double W;
+            bool qnan;
+            if (!weight_pass<DT, DQ, false>(wk, base, s_wt0, s_wq, W, qnan)) {
+              synced = false;
+              break;
+            }
+            if (tid == 0) {
+              const uint64_t* xw = last_words(wk);
+              for (int h = 0; h < a.G; ++h) s_tot[h] = dec_sum(xw[2 * h]);
+            }
+            have_pass = true;
+            tiles_buf = 0;
+          }
+          DrawRow rr = base;
+          rr.excl = s_ex;
+          rr.nexcl = n_ex;
+          const int t = x / kSampleTile;
+          if (wid == 0) {
+            float with, without;
+            lane_partial_excl<DT, DQ>(rr, V, t, x, with, without);
+            if (lane == 0) {
+              s_two[0] = with;
+              s_two[1] = without;
+            }
+          }
+          __syncthreads();
+          const double d = s_two[0] - s_two[1];  // x's share of its tile's sum
+          const int h = tile_owner(t, a.ntiles, a.G);
+          double Wn = 0.0;
+          for (int hh = 0; hh < a.G; ++hh) Wn += hh == h ? s_tot[hh] - d : s_tot[hh];
+          __syncthreads();
+          if (Wn > 0.0) {
+            if (tid == 0) {
+              s_tot[h] -= d;
+              s_ex[n_ex] = x;
+              if (wk.g == h) s_wt0[t - wk.lo] -= d;
+            }
+            ++n_ex;
+            Wrest = Wn;
+          } else {  // nothing left: keep the distribution as it was
+            fallback = kFlagFallback;
+          }
+          __syncthreads();
+        } else {
+          const float p = s_px[ch], q = s_qx[ch];
+          const float pc = coef == 0.f ? p : fmaxf(p - coef * q, 0.f) / R;
+          if (s_u[ch - 1] * q < pc) {
+            kept = ch;
+            break;
+          }
+          // rejected: residual pass with the next coefficient
+          DrawRow rr = base;
+          rr.coef = coef + R;
+          rr.use_q = true;
+          const int nb = npass & 1;
+          ++npass;
+          double W;
+          bool qnan;
+          if (!weight_pass<DT, DQ>(wk, rr, nb ? s_wt1 : s_wt0, s_wq, W, qnan)) {
+            synced = false;
+          } else if (qnan || !isfinite(W)) {
+            ok = false;
+          } else if (W > 0.0) {
+            coef = rr.coef;
+            R = static_cast<float>(W);
+            Rd = W;
+            tiles_buf = nb;
+          } else {  // no residual mass: keep the current distribution
+            fallback = kFlagFallback;
+            tiles_buf = -1;
+          }
         }
       }
     }
@@ -461,6 +602,9 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
     R = 1.f;
     Rd = 1.0;
     tiles_buf = -1;
+    n_ex = 0;
+    have_pass = false;
+    Wrest = 1.0;
   }
   if (!synced) {
     if (tid == 0) flag(a.status, kFlagSyncTimeout);
@@ -471,59 +615,79 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
     return;
   }
 
-  // ---- the last token, from the current distribution ----
-  const DrawRow row{row_ptr<DT>(a.tgt, trow0 + cur, V), row_ptr<DQ>(a.dq, qrow0 + cur, V), a.c,
-                    st.m, 1.f / st.s, coef, coef != 0.f};
-  if (tiles_buf < 0) {
-    tiles_buf = npass & 1;
-    bool qnan;
-    if (!weight_pass<DT, DQ>(wk, row, tiles_buf ? s_wt1 : s_wt0, s_wq, Rd, qnan)) {
-      if (tid == 0) flag(a.status, kFlagSyncTimeout);
+  // ---- the last token: the greedy pick, or a draw from the current distribution ----
+  int y = amax;
+  if constexpr (!kGreedy) {
+    DrawRow row{row_ptr<DT>(a.tgt, trow0 + cur, V), kUseQ ? row_ptr<DQ>(a.dq, qrow0 + cur, V) : nullptr,
+                a.c, st.m, 1.f / st.s, coef, coef != 0.f};
+    row.excl = s_ex;
+    row.nexcl = kPoint ? n_ex : 0;
+    if (tiles_buf < 0) {
+      tiles_buf = npass & 1;
+      bool qnan;
+      if (!weight_pass<DT, DQ, kUseQ>(wk, row, tiles_buf ? s_wt1 : s_wt0, s_wq, Rd, qnan)) {
+        if (tid == 0) flag(a.status, kFlagSyncTimeout);
+        return;
+      }
+      if constexpr (kPoint) {
+        if (tid == 0) {
+          const uint64_t* xw = last_words(wk);
+          for (int h = 0; h < a.G; ++h) s_tot[h] = dec_sum(xw[2 * h]);
+        }
+        __syncthreads();
+      }
+    }
+    // slice h's weight: the words of the last exchange (the weight pass of the
+    // current distribution), or the point-mass walk's updated totals
+    const uint64_t* sw = last_words(wk);
+    auto slice_w = [&](int h) { return kPoint ? s_tot[h] : dec_sum(sw[2 * h]); };
+    if constexpr (kPoint) {
+      Rd = 0.0;
+      for (int h = 0; h < a.G; ++h) Rd += slice_w(h);
+    }
+    const double target = static_cast<double>(s_u[N - 1]) * Rd;
+    // the slice holding the target: the first with weight whose running sum
+    // exceeds it, else the last slice with weight
+    int gs = -1, glast = -1;
+    double base_s = 0.0, run = 0.0, base_last = 0.0;
+    for (int h = 0; h < a.G; ++h) {
+      const double w = slice_w(h);
+      if (w > 0.0) {
+        if (gs < 0 && run + w > target) {
+          gs = h;
+          base_s = run;
+        }
+        glast = h;
+        base_last = run;
+      }
+      run += w;
+    }
+    if (gs < 0) {
+      gs = glast;
+      base_s = base_last;
+    }
+    if (gs < 0) {  // no mass anywhere: cannot happen with S > 0; defined output
+      if (wk.g == 0) walk_invalid<kChain>(a, b, kFlagNonfinite | fallback | extra, tid, kWalkBlock);
       return;
     }
-  }
-  const double target = static_cast<double>(s_u[N - 1]) * Rd;
-  // the slice holding the target: the first with weight whose running sum
-  // exceeds it, else the last slice with weight (the slice totals are the
-  // words of the last exchange, the weight pass of the current distribution)
-  const uint64_t* sw = last_words(wk);
-  int gs = -1, glast = -1;
-  double base_s = 0.0, run = 0.0, base_last = 0.0;
-  for (int h = 0; h < a.G; ++h) {
-    const double w = dec_sum(sw[2 * h]);
-    if (w > 0.0) {
-      if (gs < 0 && run + w > target) {
-        gs = h;
-        base_s = run;
-      }
-      glast = h;
-      base_last = run;
+    if (wk.g != gs || wid != 0) return;
+    const double* wt = tiles_buf ? s_wt1 : s_wt0;
+    const int nsl = wk.hi - wk.lo;
+    int ta, tb;
+    lane_tiles(nsl, lane, ta, tb);
+    double own = 0.0;
+    for (int i = ta; i < tb; ++i) own += wt[i];
+    TileHit hit;
+    if (!wave_find_tile(wt, 1, nsl, own, target - base_s, hit)) {
+      walk_invalid<kChain>(a, b, kFlagNonfinite | fallback | extra, lane, kWave);
+      return;
     }
-    run += w;
+    hit.tile += wk.lo;
+    hit.base += base_s;
+    y = wave_pick_in_tile<DT, DQ, kPoint>(row, V, hit, target);
+  } else {
+    if (wk.g != 0 || wid != 0) return;
   }
-  if (gs < 0) {
-    gs = glast;
-    base_s = base_last;
-  }
-  if (gs < 0) {  // no mass anywhere: cannot happen with S > 0; defined output
-    if (wk.g == 0) walk_invalid<kChain>(a, b, kFlagNonfinite | fallback | extra, tid, kWalkBlock);
-    return;
-  }
-  if (wk.g != gs || wid != 0) return;
-  const double* wt = tiles_buf ? s_wt1 : s_wt0;
-  const int nsl = wk.hi - wk.lo;
-  int ta, tb;
-  lane_tiles(nsl, lane, ta, tb);
-  double own = 0.0;
-  for (int i = ta; i < tb; ++i) own += wt[i];
-  TileHit h;
-  if (!wave_find_tile(wt, 1, nsl, own, target - base_s, h)) {
-    walk_invalid<kChain>(a, b, kFlagNonfinite | fallback | extra, lane, kWave);
-    return;
-  }
-  h.tile += wk.lo;
-  h.base += base_s;
-  const int y = wave_pick_in_tile<DT, DQ>(row, V, h, target);
   if constexpr (kChain) {
     if (lane == 0) {
       const int width = a.k_max + 1;
@@ -775,31 +939,39 @@ __global__ __launch_bounds__(kWalkBlock) void k_chain_diag(WalkArgs a) {
 
 namespace {
 
-template <bool kChain, class DT, class DQ>
+template <int kMode, class DT, class DQ>
 const void* walk_fn() {
-  return reinterpret_cast<const void*>(&k_walk<kChain, DT, DQ>);
+  return reinterpret_cast<const void*>(&k_walk<kMode, DT, DQ>);
 }
 
-const void* pick_walk(bool chain, int t_dtype, int q_dtype) {
+// The point-mass and greedy walks read no draft rows: one instantiation per
+// target dtype (DQ = DT, unused).
+const void* pick_walk(int mode, int t_dtype, int q_dtype) {
   const bool tb = t_dtype == kDtypeBF16, qb = q_dtype == kDtypeBF16;
-  if (chain) {
-    if (tb && qb) return walk_fn<true, BF16, BF16>();
-    if (tb) return walk_fn<true, BF16, F32>();
-    if (qb) return walk_fn<true, F32, BF16>();
-    return walk_fn<true, F32, F32>();
+  switch (mode) {
+    case kWalkChain:
+      if (tb && qb) return walk_fn<kWalkChain, BF16, BF16>();
+      if (tb) return walk_fn<kWalkChain, BF16, F32>();
+      if (qb) return walk_fn<kWalkChain, F32, BF16>();
+      return walk_fn<kWalkChain, F32, F32>();
+    case kWalkTree:
+      if (tb && qb) return walk_fn<kWalkTree, BF16, BF16>();
+      if (tb) return walk_fn<kWalkTree, BF16, F32>();
+      if (qb) return walk_fn<kWalkTree, F32, BF16>();
+      return walk_fn<kWalkTree, F32, F32>();
+    case kWalkPoint:
+      return tb ? walk_fn<kWalkPoint, BF16, BF16>() : walk_fn<kWalkPoint, F32, F32>();
+    default:
+      return tb ? walk_fn<kWalkGreedy, BF16, BF16>() : walk_fn<kWalkGreedy, F32, F32>();
   }
-  if (tb && qb) return walk_fn<false, BF16, BF16>();
-  if (tb) return walk_fn<false, BF16, F32>();
-  if (qb) return walk_fn<false, F32, BF16>();
-  return walk_fn<false, F32, F32>();
 }
 
-template <bool kChain, class DT, class DQ>
+template <int kMode, class DT, class DQ>
 void launch_t(const WalkArgs& a, size_t lds, bool clear_slots, hipStream_t stream) {
   if (a.diag != nullptr) {
-    if (kChain)
+    if constexpr (kMode == kWalkChain)
       hipLaunchKernelGGL((k_chain_diag<DT, DQ>), dim3(static_cast<uint32_t>(a.B)), dim3(kWalkBlock), 0, stream, a);
-    else
+    else if constexpr (kMode == kWalkTree)
       hipLaunchKernelGGL((k_tree_diag<DT, DQ>), dim3(static_cast<uint32_t>(a.B)), dim3(kMaxTreeNodes), 0, stream, a);
   }
   if (a.G > 1 && clear_slots) {
@@ -808,31 +980,49 @@ void launch_t(const WalkArgs& a, size_t lds, bool clear_slots, hipStream_t strea
     hipLaunchKernelGGL(k_walk_clear, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream,
                        reinterpret_cast<uint4*>(a.slots), n16);
   }
-  if (kChain && a.ntiles == 1) {
-    const int64_t blocks = (static_cast<int64_t>(a.B) + kBlock / kWave - 1) / (kBlock / kWave);
-    hipLaunchKernelGGL((k_walk_small<DT, DQ>), dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream, a);
-    return;
+  if constexpr (kMode == kWalkChain) {
+    if (a.ntiles == 1) {
+      const int64_t blocks = (static_cast<int64_t>(a.B) + kBlock / kWave - 1) / (kBlock / kWave);
+      hipLaunchKernelGGL((k_walk_small<DT, DQ>), dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream, a);
+      return;
+    }
   }
-  hipLaunchKernelGGL((k_walk<kChain, DT, DQ>), dim3(static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.G)),
+  hipLaunchKernelGGL((k_walk<kMode, DT, DQ>), dim3(static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.G)),
                      dim3(kWalkBlock), lds, stream, a);
+}
+
+template <int kMode>
+void launch_mode(int t_dtype, int q_dtype, const WalkArgs& a, size_t lds, bool clear_slots,
+                 hipStream_t stream) {
+  const bool tb = t_dtype == kDtypeBF16, qb = q_dtype == kDtypeBF16;
+  if constexpr (kMode == kWalkPoint || kMode == kWalkGreedy) {
+    if (tb) launch_t<kMode, BF16, BF16>(a, lds, clear_slots, stream);
+    else launch_t<kMode, F32, F32>(a, lds, clear_slots, stream);
+  } else {
+    if (tb && qb) launch_t<kMode, BF16, BF16>(a, lds, clear_slots, stream);
+    else if (tb) launch_t<kMode, BF16, F32>(a, lds, clear_slots, stream);
+    else if (qb) launch_t<kMode, F32, BF16>(a, lds, clear_slots, stream);
+    else launch_t<kMode, F32, F32>(a, lds, clear_slots, stream);
+  }
 }
 
 }  // namespace
 
 size_t walk_lds_bytes(int node_cap, int tile_cap) {
-  return static_cast<size_t>(tile_cap) * 2 * sizeof(double) + static_cast<size_t>(node_cap) * 8 * 4;
+  return static_cast<size_t>(tile_cap) * 2 * sizeof(double) + static_cast<size_t>(node_cap) * 9 * 4;
 }
 
-int walk_occupancy(bool chain, int t_dtype, int q_dtype, size_t lds) {
+int walk_occupancy(int mode, int t_dtype, int q_dtype, size_t lds) {
   static std::mutex mu;
-  static int cache[2][2][2][9] = {};  // by chain, dtypes, lds bucket of 8 KB
+  static int cache[4][2][2][9] = {};  // by mode, dtypes, lds bucket of 8 KB
   const size_t bucket = std::min<size_t>(lds / 8192, 8);
   const size_t lds_key = (bucket + 1) * 8192;
+  const int m = mode < 0 || mode > 3 ? 0 : mode;
   std::lock_guard<std::mutex> lock(mu);
-  int& slot = cache[chain][t_dtype == kDtypeBF16][q_dtype == kDtypeBF16][bucket];
+  int& slot = cache[m][t_dtype == kDtypeBF16][q_dtype == kDtypeBF16][bucket];
   if (slot == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick_walk(chain, t_dtype, q_dtype), kWalkBlock,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick_walk(m, t_dtype, q_dtype), kWalkBlock,
                                                      lds_key) != hipSuccess)
       n = 1;
     slot = n < 1 ? 1 : n;
@@ -840,19 +1030,13 @@ int walk_occupancy(bool chain, int t_dtype, int q_dtype, size_t lds) {
   return slot;
 }
 
-hipError_t launch_walk(bool chain, int t_dtype, int q_dtype, const WalkArgs& a, size_t lds,
+hipError_t launch_walk(int mode, int t_dtype, int q_dtype, const WalkArgs& a, size_t lds,
                        bool clear_slots, hipStream_t stream) {
-  const bool tb = t_dtype == kDtypeBF16, qb = q_dtype == kDtypeBF16;
-  if (chain) {
-    if (tb && qb) launch_t<true, BF16, BF16>(a, lds, clear_slots, stream);
-    else if (tb) launch_t<true, BF16, F32>(a, lds, clear_slots, stream);
-    else if (qb) launch_t<true, F32, BF16>(a, lds, clear_slots, stream);
-    else launch_t<true, F32, F32>(a, lds, clear_slots, stream);
-  } else {
-    if (tb && qb) launch_t<false, BF16, BF16>(a, lds, clear_slots, stream);
-    else if (tb) launch_t<false, BF16, F32>(a, lds, clear_slots, stream);
-    else if (qb) launch_t<false, F32, BF16>(a, lds, clear_slots, stream);
-    else launch_t<false, F32, F32>(a, lds, clear_slots, stream);
+  switch (mode) {
+    case kWalkChain: launch_mode<kWalkChain>(t_dtype, q_dtype, a, lds, clear_slots, stream); break;
+    case kWalkTree: launch_mode<kWalkTree>(t_dtype, q_dtype, a, lds, clear_slots, stream); break;
+    case kWalkPoint: launch_mode<kWalkPoint>(t_dtype, q_dtype, a, lds, clear_slots, stream); break;
+    default: launch_mode<kWalkGreedy>(t_dtype, q_dtype, a, lds, clear_slots, stream); break;
   }
   return hipGetLastError();
 }

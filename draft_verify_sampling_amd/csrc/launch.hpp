@@ -125,6 +125,11 @@ struct ChainStatsArgs {
 hipError_t launch_chain_stats(int t_dtype, int q_dtype, const ChainStatsArgs& a, hipStream_t stream);
 hipError_t launch_clear(void* p, size_t bytes, hipStream_t stream);
 
+// Walk variants: speculative sampling over a chain of drafts or a draft tree,
+// the tree with every candidate tested as a point mass on its own token, and
+// the greedy (T = 0) tree.
+enum WalkMode : int { kWalkChain = 0, kWalkTree = 1, kWalkPoint = 2, kWalkGreedy = 3 };
+
 struct WalkArgs {
   const void* tgt;
   const void* dq;
@@ -169,10 +174,11 @@ struct WalkArgs {
 };
 
 size_t walk_lds_bytes(int node_cap, int tile_cap);
-int walk_occupancy(bool chain, int t_dtype, int q_dtype, size_t lds);
+int walk_occupancy(int mode, int t_dtype, int q_dtype, size_t lds);
 // Launches the walk (and the diagnostics, when asked for).  clear_slots: zero
 // the exchange words first (not needed when the statistics kernel did it).
-hipError_t launch_walk(bool chain, int t_dtype, int q_dtype, const WalkArgs& a, size_t lds,
+// The point-mass and greedy walks read no draft rows (q_dtype is ignored).
+hipError_t launch_walk(int mode, int t_dtype, int q_dtype, const WalkArgs& a, size_t lds,
                        bool clear_slots, hipStream_t stream);
 
 struct GreedyArgs {

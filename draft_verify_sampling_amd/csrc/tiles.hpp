@@ -26,6 +26,8 @@ struct DrawRow {
   float invS;      // 1 / softmax normaliser of the target row
   float coef;      // residual coefficient
   bool use_q;      // true: w = max(0, p - coef q); false: w = p
+  const int32_t* excl = nullptr;  // ids whose weight is 0 (point-mass residual),
+  int nexcl = 0;                  // honoured by the one-tile steps built with kExcl
 };
 
 template <int n>
@@ -83,13 +85,14 @@ struct TileRuns {
 // partial tile costs one load round like any other); a run that the row's
 // end cuts (rows whose length is not a multiple of the vector width) and
 // unaligned rows take element loads.
-template <class DT, class DQ>
+template <class DT, class DQ, bool kQ = true>
 __device__ __forceinline__ void wave_tile_sums_any(const DrawRow& r, int64_t V, int t, double* v) {
   using L = TileRuns<DT, DQ>;
   constexpr int kPer = L::kPer;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t t0 = static_cast<int64_t>(t) * kSampleTile;
-  const bool al = aligned16<DT>(r.t, t0) && (!r.use_q || aligned16<DQ>(r.q, t0));
+  const bool use_q = kQ && r.use_q;
+  const bool al = aligned16<DT>(r.t, t0) && (!use_q || aligned16<DQ>(r.q, t0));
   float ws = 0.f, ps = 0.f, qs = 0.f;
   constexpr int kAB = (L::nt + L::nq == 2) ? 4 : 2;  // runs per load round (<= 8 vectors)
   static_assert(L::kRuns % kAB == 0, "whole rounds");
@@ -103,7 +106,7 @@ __device__ __forceinline__ void wave_tile_sums_any(const DrawRow& r, int64_t V, 
       if (e + kPer <= V) {
 #pragma unroll
         for (int j = 0; j < L::nt; ++j) tw[kk][j] = ld16<DT>(r.t, e + j * DT::kPerVec);
-        if (r.use_q) {
+        if (use_q) {
 #pragma unroll
           for (int j = 0; j < L::nq; ++j) qw[kk][j] = ld16<DQ>(r.q, e + j * DQ::kPerVec);
         }
@@ -117,7 +120,7 @@ __device__ __forceinline__ void wave_tile_sums_any(const DrawRow& r, int64_t V, 
       if (e + kPer <= V) {
 #pragma unroll
         for (int j = 0; j < L::nt; ++j) DT::unpack(tw[kk][j], l + j * DT::kPerVec);
-        if (r.use_q) {
+        if (use_q) {
 #pragma unroll
           for (int j = 0; j < L::nq; ++j) DQ::unpack(qw[kk][j], q + j * DQ::kPerVec);
         } else {
@@ -129,7 +132,7 @@ __device__ __forceinline__ void wave_tile_sums_any(const DrawRow& r, int64_t V, 
         for (int j = 0; j < kPer; ++j) {
           const bool in = e + j < V;
           l[j] = in ? DT::at(r.t, e + j) : -INFINITY;
-          q[j] = (in && r.use_q) ? DQ::at(r.q, e + j) : 0.f;
+          q[j] = (in && use_q) ? DQ::at(r.q, e + j) : 0.f;
         }
       }
       float w[kPer], p[kPer];
@@ -153,7 +156,7 @@ __device__ __forceinline__ void wave_tile_sums_any(const DrawRow& r, int64_t V, 
       for (int j = 0; j < kPer; ++j) {
         const bool in = e + j < V;
         l[j] = in ? DT::at(r.t, e + j) : -INFINITY;
-        q[j] = (in && r.use_q) ? DQ::at(r.q, e + j) : 0.f;
+        q[j] = (in && use_q) ? DQ::at(r.q, e + j) : 0.f;
       }
       float w[kPer], p[kPer];
 #pragma unroll
@@ -175,7 +178,7 @@ __device__ __forceinline__ void wave_tile_sums_any(const DrawRow& r, int64_t V, 
 // lane's loads for a batch of runs are in flight before the first is used.
 // Falls back to wave_tile_sums_any tile by tile unless every tile is complete
 // and the rows are 16-byte aligned.
-template <class DT, class DQ, int kT>
+template <class DT, class DQ, int kT, bool kQ = true>
 __device__ __forceinline__ void wave_tile_sums(const DrawRow& r, int64_t V, int t, int tstride,
                                                double (*v)[3]) {
   using L = TileRuns<DT, DQ>;
@@ -186,11 +189,12 @@ __device__ __forceinline__ void wave_tile_sums(const DrawRow& r, int64_t V, int 
   static_assert(kAll % kBatch == 0, "whole batches");
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t tlast = static_cast<int64_t>(t + (kT - 1) * tstride);
+  const bool use_q = kQ && r.use_q;
   const bool fast = (tlast + 1) * kSampleTile <= V && aligned16<DT>(r.t, 0) &&
-                    (!r.use_q || aligned16<DQ>(r.q, 0));
+                    (!use_q || aligned16<DQ>(r.q, 0));
   if (!fast) {
 #pragma unroll 1
-    for (int i = 0; i < kT; ++i) wave_tile_sums_any<DT, DQ>(r, V, t + i * tstride, v[i]);
+    for (int i = 0; i < kT; ++i) wave_tile_sums_any<DT, DQ, kQ>(r, V, t + i * tstride, v[i]);
     return;
   }
   float ws[kT], ps[kT], qs[kT];
@@ -207,7 +211,7 @@ __device__ __forceinline__ void wave_tile_sums(const DrawRow& r, int64_t V, int 
                         static_cast<int64_t>(kr * kWave + lane) * kPer;
 #pragma unroll
       for (int j = 0; j < L::nt; ++j) tw[k][j] = ld16<DT>(r.t, e + j * DT::kPerVec);
-      if (r.use_q) {
+      if (use_q) {
 #pragma unroll
         for (int j = 0; j < L::nq; ++j) qw[k][j] = ld16<DQ>(r.q, e + j * DQ::kPerVec);
       }
@@ -218,7 +222,7 @@ __device__ __forceinline__ void wave_tile_sums(const DrawRow& r, int64_t V, int 
       float l[kPer], q[kPer], w[kPer], p[kPer];
 #pragma unroll
       for (int j = 0; j < L::nt; ++j) DT::unpack(tw[k][j], l + j * DT::kPerVec);
-      if (r.use_q) {
+      if (use_q) {
 #pragma unroll
         for (int j = 0; j < L::nq; ++j) DQ::unpack(qw[k][j], q + j * DQ::kPerVec);
       } else {
@@ -386,15 +390,25 @@ __device__ __forceinline__ bool wave_find_tile(const double* ts, int stride, int
   return true;
 }
 
-// The id inside tile h.tile: lane l owns the 32 contiguous elements
-// [32 l, 32 l + 32), read in one round (16-byte vectors when aligned and
-// complete); running weights in fp32 within a lane and fp64 across lanes.
-template <class DT, class DQ>
-__device__ __forceinline__ int wave_pick_in_tile(const DrawRow& r, int64_t V, const TileHit& h,
-                                                 double target) {
+// Bit i set: element e0 + i of the lane's 32 is one of the ids r.excl.
+__device__ __forceinline__ uint32_t lane_excl_mask(const DrawRow& r, int64_t e0) {
+  uint32_t m = 0;
+  for (int x = 0; x < r.nexcl; ++x) {
+    const int64_t off = static_cast<int64_t>(r.excl[x]) - e0;
+    if (off >= 0 && off < kSampleTile / kWave) m |= 1u << off;
+  }
+  return m;
+}
+
+// Weights of the 32 contiguous elements [32 l, 32 l + 32) of tile `tile` in
+// lane l, read in one round (16-byte vectors when aligned and complete);
+// elements past the row's end weigh 0, and with kExcl the ids in r.excl too.
+template <class DT, class DQ, bool kExcl = false>
+__device__ __forceinline__ void lane_tile_weights(const DrawRow& r, int64_t V, int tile,
+                                                  float (&wv)[kSampleTile / kWave]) {
   constexpr int kLane = kSampleTile / kWave;  // 32
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t e0 = static_cast<int64_t>(h.tile) * kSampleTile + lane * kLane;
+  const int64_t e0 = static_cast<int64_t>(tile) * kSampleTile + lane * kLane;
   constexpr int kTV = kLane / DT::kPerVec, kQV = kLane / DQ::kPerVec;
   uint4 tv[kTV], qv[kQV];
   const bool fast = e0 + kLane <= V && aligned16<DT>(r.t, e0) && (!r.use_q || aligned16<DQ>(r.q, e0));
@@ -406,7 +420,6 @@ __device__ __forceinline__ int wave_pick_in_tile(const DrawRow& r, int64_t V, co
       for (int j = 0; j < kQV; ++j) qv[j] = ld16<DQ>(r.q, e0 + j * DQ::kPerVec);
     }
   }
-  float wv[kLane];
 #pragma unroll
   for (int g = 0; g < kLane / 8; ++g) {
     float l[8], q[8];
@@ -440,6 +453,63 @@ __device__ __forceinline__ int wave_pick_in_tile(const DrawRow& r, int64_t V, co
 #pragma unroll
     for (int j = 0; j < 8; ++j) wv[8 * g + j] = draw_w(r, draw_p(r, l[j]), q[j]);
   }
+  if constexpr (kExcl) {
+    const uint32_t xm = lane_excl_mask(r, e0);
+#pragma unroll
+    for (int i = 0; i < kLane; ++i) wv[i] = ((xm >> i) & 1u) ? 0.f : wv[i];
+  }
+}
+
+// The fp32 partial sum that lane Lx of a tile pass (wave_tile_sums over tile
+// t, no draft row) forms, Lx being the lane whose runs hold id `extra`: its
+// runs Lx, Lx + 64, ... of kPer elements, each summed pairwise, added in
+// order from 0.  a: with the ids of r.excl weighing 0; b: with `extra` as well.
+// The same element weights in the same order as the pass, so replacing a by
+// b in a tile sum removes `extra` exactly up to fp64 rounding.  Valid in
+// every lane; lanes [0, runs) do the loads.
+template <class DT, class DQ>
+__device__ __forceinline__ void lane_partial_excl(const DrawRow& r, int64_t V, int t, int extra, float& a,
+                                                  float& b) {
+  using L = TileRuns<DT, DQ>;
+  constexpr int kPer = L::kPer;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t t0 = static_cast<int64_t>(t) * kSampleTile;
+  const int lx = static_cast<int>(((static_cast<int64_t>(extra) - t0) / kPer) % kWave);
+  float pa = 0.f, pb = 0.f;
+  if (lane < L::kRuns) {
+    const int64_t e = t0 + static_cast<int64_t>(lane * kWave + lx) * kPer;
+    float w[kPer], wb[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int64_t id = e + j;
+      const float l = id < V ? DT::at(r.t, id) : -INFINITY;
+      bool gone = false;
+      for (int x = 0; x < r.nexcl; ++x) gone |= r.excl[x] == id;
+      w[j] = gone ? 0.f : draw_w(r, draw_p(r, l), 0.f);
+      wb[j] = id == extra ? 0.f : w[j];
+    }
+    pa = pairwise<kPer>(w);
+    pb = pairwise<kPer>(wb);
+  }
+  float sa = 0.f, sb = 0.f;
+#pragma unroll
+  for (int k = 0; k < L::kRuns; ++k) {
+    sa += __shfl(pa, k, kWave);
+    sb += __shfl(pb, k, kWave);
+  }
+  a = sa;
+  b = sb;
+}
+
+// The id inside tile h.tile: running weights in fp32 within a lane's 32
+// contiguous elements and fp64 across lanes.
+template <class DT, class DQ, bool kExcl = false>
+__device__ __forceinline__ int wave_pick_in_tile(const DrawRow& r, int64_t V, const TileHit& h,
+                                                 double target) {
+  constexpr int kLane = kSampleTile / kWave;  // 32
+  const int lane = threadIdx.x & (kWave - 1);
+  float wv[kLane];
+  lane_tile_weights<DT, DQ, kExcl>(r, V, h.tile, wv);
   const double lane_base =
       h.base + wave_exclusive_from_inclusive(wave_incl_scan(static_cast<double>(pairwise<kLane>(wv))));
   const float thr = static_cast<float>(target - lane_base);  // crossing: running weight > thr
@@ -463,6 +533,64 @@ __device__ __forceinline__ int wave_pick_in_tile(const DrawRow& r, int64_t V, co
     pick = any ? __builtin_amdgcn_readlane(lastw, 63 - __clzll(static_cast<long long>(any))) : 0;
   }
   return static_cast<int>(static_cast<int64_t>(h.tile) * kSampleTile + pick);
+}
+
+// ---- greedy (T = 0): the argmax of a row ----
+
+// Running argmax of one lane: the largest value, the lowest id among equal
+// values (+0 and -0 are equal), and whether a NaN was seen.
+struct ArgBest {
+  float v;
+  int32_t i;
+  bool nan;
+};
+
+__device__ __forceinline__ void arg_update(ArgBest& s, float v, int32_t i) {
+  s.nan |= (v != v);
+  if (v > s.v || (v == s.v && i < s.i)) {
+    s.v = v;
+    s.i = i;
+  }
+}
+
+// Order-preserving bits of a value (-0 -> +0): for a, b not NaN, a < b iff
+// bits(a) < bits(b).
+__device__ __forceinline__ uint32_t order_bits(float v) {
+  uint32_t b = __float_as_uint(v);
+  if ((b & 0x7fffffffu) == 0u) b = 0u;
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+// Fold tile t of a row into the lane's running argmax: lane l takes the
+// 16-byte vectors l, l + 64, ... of the tile (element loads where the row is
+// unaligned or the tile is cut by the row's end).
+template <class D>
+__device__ __forceinline__ void lane_tile_argmax(const void* row, int64_t V, int t, ArgBest& s) {
+  constexpr int kPer = D::kPerVec;
+  constexpr int kRuns = kSampleTile / (kWave * kPer);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t t0 = static_cast<int64_t>(t) * kSampleTile;
+  if (t0 + kSampleTile <= V && aligned16<D>(row, t0)) {
+    uint4 w[kRuns];
+#pragma unroll
+    for (int k = 0; k < kRuns; ++k) w[k] = ld16<D>(row, t0 + static_cast<int64_t>(k * kWave + lane) * kPer);
+#pragma unroll
+    for (int k = 0; k < kRuns; ++k) {
+      float x[kPer];
+      D::unpack(w[k], x);
+      const int32_t e = static_cast<int32_t>(t0) + (k * kWave + lane) * kPer;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) arg_update(s, x[j], e + j);
+    }
+  } else {
+#pragma unroll 1
+    for (int k = 0; k < kRuns; ++k) {
+      const int64_t e = t0 + static_cast<int64_t>(k * kWave + lane) * kPer;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if (e + j < V) arg_update(s, D::at(row, e + j), static_cast<int32_t>(e + j));
+    }
+  }
 }
 
 }  // namespace sv

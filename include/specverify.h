@@ -2,7 +2,7 @@
  * libspecverify -- the verify step of speculative decoding on AMD Instinct
  * MI355X (gfx950).
  *
- * Four operations, each following the pages that define it:
+ * The operations, each following the pages that define it:
  *
  *   sv_ngram_draft    history n-gram (prompt-lookup) drafter
  *                     ("第 13 篇：推理引擎一次猜几个字——草稿 + 验证", notes under
@@ -23,6 +23,10 @@
  *                     in between ("Speculative Decoding II", EAGLE section:
  *                     the SpecInfer-style tree verify; EAGLE-2 worked example
  *                     for the flattened layout).
+ *   sv_verify_tree_greedy     the same tree at T = 0 (argmax picks).
+ *   sv_verify_tree_pointmass  the same tree with each candidate tested as a
+ *                     point mass on its own token (deterministic top-k
+ *                     candidates).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -204,6 +208,54 @@ sv_status sv_verify_tree(const void* target_logits, int32_t t_dtype,
                          int32_t* out_accepted, int32_t* out_path, float* out_diag,
                          int32_t* dev_status, void* workspace, size_t workspace_bytes,
                          void* stream);
+
+/* Greedy (T = 0) tree verify.
+ * "Speculative Decoding II", EAGLE section: the flattened tree is verified in
+ * one target forward and the kept path is the one the target itself would
+ * produce; at T = 0 the target's pick at a node is the argmax of the node's
+ * row ("第 13 篇：推理引擎一次猜几个字——草稿 + 验证", section ③).
+ * Walk: cur = root; a = argmax of cur's target row (lowest id among equal
+ * maxima, +0 and -0 equal); the first child of cur (index order) whose token
+ * is a is kept (emit a, descend); when none is, emit a and stop (at a leaf:
+ * the extra token from the leaf's row).  Layout, parent / node_token checks,
+ * outputs and workspace (SV_OP_TREE) as for sv_verify_tree; no draft rows,
+ * no temperature, no uniforms.  Only the target rows of visited nodes are
+ * read; a NaN in one of them makes the request invalid (SV_FLAG_NONFINITE).
+ * 1 <= n_nodes <= 1024, 1 <= vocab <= 4194304. */
+sv_status sv_verify_tree_greedy(const void* target_logits, int32_t t_dtype, int64_t vocab,
+                                const int32_t* parent, const int32_t* node_token,
+                                int32_t batch, int32_t n_nodes, int32_t* out_tokens,
+                                int32_t* out_count, int32_t* out_accepted, int32_t* out_path,
+                                int32_t* dev_status, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/* Tree verify with every candidate taken as a point mass on its own token.
+ * The recursive speculative sampling of "Speculative Decoding II" (EAGLE
+ * section, as in SpecInfer) applied with q = delta_x for each candidate x, as
+ * suits candidates chosen deterministically (EAGLE-2's top-k tree): keep x
+ * with probability p(x); after a rejection p <- norm(max(0, p - delta_x)), x's
+ * mass removed and the rest renormalised ("投机解码:为什么一个字都不改",
+ * section "改进", with q = delta_x).  Every step is then that section's
+ * identity, so the emitted tokens follow the target for any candidate set.
+ * Walk: cur = root, p = softmax(target row of cur / T); children of cur in
+ * index order, u = uniforms[b, c-1]: keep c iff u < p(x_c) (p the current,
+ * renormalised distribution; a candidate already removed at this node has
+ * p = 0); kept -> emit x_c, descend, reload p; not kept -> remove x_c (if the
+ * rest has no mass, p is left as it was and SV_FLAG_FALLBACK is set).  When no
+ * child is kept the last token is drawn from the current p with
+ * uniforms[b, n_nodes-1] (smallest id whose running mass exceeds u times the
+ * total).  Layout, checks, outputs and workspace (SV_OP_TREE) as for
+ * sv_verify_tree; no draft rows.  Reads the target rows of the visited
+ * nodes only; a visited row whose normaliser is not finite and positive makes
+ * the request invalid (SV_FLAG_NONFINITE).  temperature finite and > 0;
+ * 1 <= n_nodes <= 1024, 1 <= vocab <= 4194304. */
+sv_status sv_verify_tree_pointmass(const void* target_logits, int32_t t_dtype, int64_t vocab,
+                                   const int32_t* parent, const int32_t* node_token,
+                                   int32_t batch, int32_t n_nodes, float temperature,
+                                   const float* uniforms, int32_t* out_tokens,
+                                   int32_t* out_count, int32_t* out_accepted, int32_t* out_path,
+                                   int32_t* dev_status, void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 #ifdef __cplusplus
 }

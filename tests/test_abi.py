@@ -94,6 +94,19 @@ def test_host_checks_greedy_tree_ngram(lib):
     assert t(d, 1, d, 1, (1 << 22) + 1, d, d, 1, 60, 1.0, d, d, d, d, d, None, None, None, 0, None) == 1
     assert t(d, 1, d, 1, 100, d, d, 1, 60, 0.0, d, d, d, d, d, None, None, None, 0, None) == 1
     assert t(d, 1, d, 1, 100, d, d, 1, 60, 1.0, d, d, d, d, d, None, None, None, 0, None) == 3
+    tg = lib.sv_verify_tree_greedy
+    assert tg(d, 3, 100, d, d, 1, 60, d, d, d, d, None, None, 0, None) == 2
+    assert tg(d, 1, 100, d, d, 1, 0, d, d, d, d, None, None, 0, None) == 1
+    assert tg(d, 1, 0, d, d, 1, 60, d, d, d, d, None, None, 0, None) == 1
+    assert tg(None, 1, 100, d, d, 1, 60, d, d, d, d, None, None, 0, None) == 1
+    assert tg(d, 1, 100, d, d, 1, 60, d, d, d, d, None, None, 0, None) == 3   # no workspace
+    assert tg(d, 1, 100, d, d, 0, 60, d, d, d, d, None, None, 0, None) == 0   # nothing to do
+    tp = lib.sv_verify_tree_pointmass
+    assert tp(d, 1, 100, d, d, 1, 60, 0.0, d, d, d, d, d, None, None, 0, None) == 1
+    assert tp(d, 1, 100, d, d, 1, 60, 1.0, None, d, d, d, d, None, None, 0, None) == 1
+    assert tp(d, 1, (1 << 22) + 1, d, d, 1, 60, 1.0, d, d, d, d, d, None, None, 0, None) == 1
+    assert tp(d, 1, 100, d, d, 1, 1025, 1.0, d, d, d, d, d, None, None, 0, None) == 1
+    assert tp(d, 1, 100, d, d, 1, 60, 1.0, d, d, d, d, d, None, None, 0, None) == 3
     n = lib.sv_ngram_draft
     assert n(d, d, 1, 16, 0, 4, d, d, None, None) == 1
     assert n(d, d, 1, 16, 65, 4, d, d, None, None) == 1
@@ -113,3 +126,31 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     finally:
         monkeypatch.delenv("SPECVERIFY_LIB")
         importlib.reload(sv)
+
+
+def test_binding_rejects_mismatched_buffers():
+    """Caller-provided outputs and index arrays must match the call's sizes
+    (the kernels index them by B, k_max, N): a mismatch raises before any
+    launch.  CPU tensors suffice, the shape checks come first."""
+    import torch
+    B, k, V = 4, 3, 50
+    tgt = torch.zeros((B * (k + 1), V))
+    dft = torch.zeros((B * k, V))
+    trs = torch.zeros(B, dtype=torch.int32)
+    ids = torch.zeros((B, k), dtype=torch.int32)
+    dl = torch.full((B,), k, dtype=torch.int32)
+    u = torch.zeros((B, k + 1))
+    bad_out = (torch.zeros((B, k), dtype=torch.int32), torch.zeros(B, dtype=torch.int32),
+               torch.zeros(B, dtype=torch.int32), None, None)
+    with pytest.raises(sv.SpecVerifyError, match="out tokens must have shape"):
+        sv.sv_verify_sample(tgt, dft, trs, trs, ids, dl, 1.0, u, out=bad_out)
+    with pytest.raises(sv.SpecVerifyError, match="t_row_start must have shape"):
+        sv.sv_verify_sample(tgt, dft, trs[:2], trs, ids, dl, 1.0, u)
+    with pytest.raises(sv.SpecVerifyError, match="out must be"):
+        sv.sv_softmax_partials(tgt, 1.0, out=torch.zeros((B, 1, 2)))
+    par = torch.zeros((B, 5), dtype=torch.int32)
+    with pytest.raises(sv.SpecVerifyError, match="node_token must have shape"):
+        sv.sv_verify_tree_greedy(torch.zeros((B * 5, V)), par, par[:, :4])
+    with pytest.raises(sv.SpecVerifyError, match="out path must have shape"):
+        sv.sv_verify_tree_pointmass(torch.zeros((B * 5, V)), par, par, 1.0, torch.zeros((B, 5)),
+                                    out=(par, par[:, 0], par[:, 0], par[:, :3]))

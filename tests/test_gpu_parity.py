@@ -565,3 +565,21 @@ def test_gpu_prepared_calls_match_direct_calls():
         for got, w in zip(outs[:3], want):
             assert torch.equal(got, w), rep
         assert torch.equal(part, part_want), rep
+    # tree and greedy entry points through the generic prepare()
+    ti = synth.c5_tree(B=6, N=9, V=5000, top_children=2, expand_per_layer=2, max_depth=4, salt=3)
+    targs = (rows_to_dev(ti.target, "bf16"), rows_to_dev(ti.draft, "bf16"), i32(ti.parent), i32(ti.token))
+    tu = f32(ti.uniforms)
+    direct = [t.clone() for t in sv.sv_verify_tree(*targs, ti.T, tu)[:4]]
+    tl, touts = sv.prepare(sv.sv_verify_tree, *targs, ti.T, tu)
+    gd = [t.clone() for t in sv.sv_verify_tree_greedy(targs[0], targs[2], targs[3])]
+    gl, gouts = sv.prepare(sv.sv_verify_tree_greedy, targs[0], targs[2], targs[3])
+    for rep in range(2):
+        for t in list(touts[:4]) + list(gouts):
+            t.fill_(-7)
+        tl()
+        gl()
+        torch.cuda.synchronize()
+        for got, w in zip(touts[:4], direct):
+            assert torch.equal(got, w), rep
+        for got, w in zip(gouts, gd):
+            assert torch.equal(got, w), rep
