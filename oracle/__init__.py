@@ -51,6 +51,11 @@ print, closed forms, or brute force):
                                  follows the row it is drawn against; equals
                                  ``verify_tree`` when every draft row is one-hot
                                  at the node's single child.
+* ``philox.philox4x64_10``      numpy's Philox bit generator (an independent
+                                 implementation of the same published function)
+                                 on many keys and counters, carries included.
+* ``philox.philox_uniforms``    the slot-to-word mapping against those blocks;
+                                 grid and range.
 """
 from .rows import widen, FLAG_BAD_REQUEST, FLAG_BAD_TOKEN, FLAG_NONFINITE, \
     FLAG_OVER_BUDGET, FLAG_FALLBACK, FLAG_BAD_TREE, INVALID_FLAGS
@@ -58,11 +63,13 @@ from .chain import (verify_sample, verify_greedy, greedy_path_verify,
                     forward_accounting, naive_round, softmax_T, inverse_cdf)
 from .ngram import ngram_draft
 from .tree import verify_tree, verify_tree_greedy, verify_tree_pointmass
+from .philox import philox4x64_10, philox_uniforms
 
 __all__ = [
     "widen", "verify_sample", "verify_greedy", "greedy_path_verify",
     "forward_accounting", "naive_round", "softmax_T", "inverse_cdf",
     "ngram_draft", "verify_tree", "verify_tree_greedy", "verify_tree_pointmass",
+    "philox4x64_10", "philox_uniforms",
     "FLAG_BAD_REQUEST", "FLAG_BAD_TOKEN", "FLAG_NONFINITE", "FLAG_OVER_BUDGET",
     "FLAG_FALLBACK", "FLAG_BAD_TREE", "INVALID_FLAGS",
 ]
