@@ -114,16 +114,19 @@ def kernel_avg_us(launchers, steps, warmup, torch):
     return 1e3 * e0.elapsed_time(e1) / steps
 
 
-def cpu_baseline_chain(ci, gpu_out, budget_s):
+def cpu_baseline_chain(ci, gpu_out, budget_s, philox=None):
     """The float64 oracle on the host on the same inputs: whole batches of this
-    workload's requests, repeated until about budget_s seconds have passed."""
+    workload's requests, repeated until about budget_s seconds have passed.
+    philox = (seed, offset): the GPU drew its uniforms on the device; the
+    oracle draws the same ones with its own generator (outside the timing)."""
     import oracle
+    u = ci.uniforms if philox is None else oracle.philox_uniforms(philox[0], philox[1], ci.B, ci.k_max + 1)
     reps, t0 = 0, time.perf_counter()
     want = None
     while True:
         want = oracle.verify_sample(ci.target, ci.t_kind, ci.draft, ci.q_kind, ci.V, ci.t_row_start,
                                     ci.q_row_start, ci.draft_ids[:, :ci.k_max], ci.draft_len,
-                                    ci.k_max, ci.T, ci.uniforms)
+                                    ci.k_max, ci.T, u)
         reps += 1
         if time.perf_counter() - t0 >= budget_s:
             break
@@ -181,7 +184,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c4", "c5", "c5g", "c5p"])
+    ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c3p", "c4", "c5", "c5g", "c5p"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--graph", action="store_true",
@@ -217,14 +220,18 @@ def main():
                   higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
                   data="synthetic")
     W = args.workload
+    philox = W == "c3p"  # the headline workload with its uniforms drawn on the device
+    if philox:
+        W = "c3"
     if W in ("c1", "c3", "c4"):
         log(f"generating {W} inputs")
         if W == "c3":
             sets = [synth.c3_sampled(salt=s) for s in (0, 1, 2)]
             cfg = dict(workload="sampled chain verify (speculative sampling): 64 requests, k=4 drafts, "
                                 "V=248,320, bf16 target logits ~N(0,2.5^2)+6 on 5 ids, bf16 draft "
-                                "probabilities, T=0.7", batch=64, k=4, vocab=248_320,
-                       temperature=0.7, inputs="bf16", input_sets=3)
+                                "probabilities, T=0.7" + (", uniforms drawn on the device (Philox4x64-10)"
+                                                          if philox else ""),
+                       batch=64, k=4, vocab=248_320, temperature=0.7, inputs="bf16", input_sets=3)
         elif W == "c4":
             sets = [synth.c4_ragged(salt=s) for s in (0, 1, 2)]
             cfg = dict(workload="ragged sampled chain verify: 256 requests, k in 1..8, V=151,936, bf16, "
@@ -251,8 +258,12 @@ def main():
 
         # one pre-marshalled call per input set: the host enqueues a step in a
         # few microseconds, well below the step's GPU time
-        calls = [sv.prepare_verify_sample(d["tgt"], d["dft"], d["trs"], d["qrs"], d["ids"], d["dl"], ci0.T,
-                                          d["u"], workspace=ws, out=out)[0] for d in dsets]
+        if philox:
+            calls = [sv.prepare(sv.sv_verify_sample_philox, d["tgt"], d["dft"], d["trs"], d["qrs"], d["ids"],
+                                d["dl"], ci0.T, 2026, j, workspace=ws, out=out)[0] for j, d in enumerate(dsets)]
+        else:
+            calls = [sv.prepare_verify_sample(d["tgt"], d["dft"], d["trs"], d["qrs"], d["ids"], d["dl"], ci0.T,
+                                              d["u"], workspace=ws, out=out)[0] for d in dsets]
 
         def eager(i):
             calls[i % len(calls)]()
@@ -315,7 +326,7 @@ def main():
                           avg_launch_us=round(st_avg * 1e6, 3)))
         if not args.no_cpu:
             log("timing the oracle on the host")
-            cb, par = cpu_baseline_chain(ci0, (tok0, cnt0), args.cpu_seconds)
+            cb, par = cpu_baseline_chain(ci0, (tok0, cnt0), args.cpu_seconds, (2026, 0) if philox else None)
             result["cpu_baseline"] = cb
             result["parity_sample"] = par
     elif W == "c5":

@@ -25,6 +25,7 @@ __all__ = [
     "FLAG_BAD_REQUEST", "FLAG_BAD_TOKEN", "FLAG_NONFINITE", "FLAG_OVER_BUDGET",
     "FLAG_FALLBACK", "FLAG_BAD_TREE", "FLAG_SYNC_TIMEOUT", "EXPORTS",
     "sv_verify_tree_greedy", "sv_verify_tree_pointmass", "prepare", "prepare_verify_sample",
+    "sv_philox_uniforms", "sv_verify_sample_philox",
     "prepare_softmax_partials",
 ]
 
@@ -36,7 +37,8 @@ FLAG_OVER_BUDGET, FLAG_FALLBACK, FLAG_BAD_TREE, FLAG_SYNC_TIMEOUT = 8, 16, 32, 6
 EXPORTS = ("sv_abi_version", "sv_status_string", "sv_last_error", "sv_workspace_bytes",
            "sv_softmax_segments", "sv_softmax_partials",
            "sv_ngram_draft", "sv_verify_greedy", "sv_verify_sample", "sv_verify_tree",
-           "sv_verify_tree_greedy", "sv_verify_tree_pointmass")
+           "sv_verify_tree_greedy", "sv_verify_tree_pointmass", "sv_philox_uniforms",
+           "sv_verify_sample_philox")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -46,6 +48,7 @@ P = ctypes.c_void_p
 I32 = ctypes.c_int32
 I64 = ctypes.c_int64
 SZ = ctypes.c_size_t
+U64 = ctypes.c_uint64
 F32 = ctypes.c_float
 
 _SIGS = {
@@ -63,6 +66,9 @@ _SIGS = {
     "sv_verify_tree": (ctypes.c_int, [P, I32, P, I32, I64, P, P, I32, I32, F32, P, P, P,
                                       P, P, P, P, P, SZ, P]),
     "sv_verify_tree_greedy": (ctypes.c_int, [P, I32, I64, P, P, I32, I32, P, P, P, P, P, P, SZ, P]),
+    "sv_philox_uniforms": (ctypes.c_int, [U64, U64, I32, I32, P, P]),
+    "sv_verify_sample_philox": (ctypes.c_int, [P, I32, I32, P, I32, I32, I64, P, P, P, P, I32, I32,
+                                               F32, U64, U64, P, I32, P, P, P, P, P, P, P, SZ, P]),
     "sv_verify_tree_pointmass": (ctypes.c_int, [P, I32, I64, P, P, I32, I32, F32, P, P, P, P, P,
                                                 P, P, SZ, P]),
 }
@@ -307,13 +313,44 @@ def sv_verify_sample(target: torch.Tensor, draft: torch.Tensor, t_row_start: tor
     diag [B, k_max+1, 4] or None, resid [B] or None).  ``out`` may pass a
     preallocated (tokens, count, accepted, diag, resid) tuple.  ``resid``
     (default: same as ``diag``) asks for the residual masses."""
+    return _sample(target, draft, t_row_start, q_row_start, draft_ids, draft_len, temperature, uniforms,
+                   None, max_new, eos_id, diag, dev_status, workspace, stream, out, resid)
+
+
+def sv_verify_sample_philox(target: torch.Tensor, draft: torch.Tensor, t_row_start: torch.Tensor,
+                            q_row_start: torch.Tensor, draft_ids: torch.Tensor, draft_len: torch.Tensor,
+                            temperature: float, seed: int, offset: int,
+                            max_new: Optional[torch.Tensor] = None, eos_id: int = -1,
+                            diag: bool = False, dev_status: Optional[torch.Tensor] = None,
+                            workspace: Optional[Workspace] = None, stream=None, out=None,
+                            resid: Optional[bool] = None):
+    """sv_verify_sample with the uniforms of the Philox stream (seed, offset)
+    drawn on the device (see sv_philox_uniforms)."""
+    return _sample(target, draft, t_row_start, q_row_start, draft_ids, draft_len, temperature, None,
+                   (int(seed), int(offset)), max_new, eos_id, diag, dev_status, workspace, stream, out, resid)
+
+
+def sv_philox_uniforms(seed: int, offset: int, batch: int, slots: int, out: Optional[torch.Tensor] = None,
+                       device=None, stream=None) -> torch.Tensor:
+    """The verify's uniforms u [batch, slots] of the Philox stream (seed, offset)."""
+    if out is None:
+        out = torch.empty((batch, slots), dtype=torch.float32,
+                          device=device if device is not None else torch.device("cuda"))
+    _shape(out, "out", (batch, slots), torch.float32)
+    args = (int(seed) & (2 ** 64 - 1), int(offset) & (2 ** 64 - 1), batch, slots,
+            _dev(out, "out", torch.float32), _stream(stream))
+    return _invoke("sv_philox_uniforms", args, (out,), out)
+
+
+def _sample(target, draft, t_row_start, q_row_start, draft_ids, draft_len, temperature, uniforms, philox,
+            max_new, eos_id, diag, dev_status, workspace, stream, out, resid):
     t_rows, V = target.shape
     q_rows = draft.shape[0]
     if draft.shape[1] != V:
         raise SpecVerifyError("target and draft rows differ in length")
     B = draft_len.shape[0]
     k_max = draft_ids.shape[1] if draft_ids.dim() == 2 else 0
-    if uniforms.shape != (B, k_max + 1):
+    if philox is None and uniforms.shape != (B, k_max + 1):
         raise SpecVerifyError(f"uniforms must be [B, k_max+1] = [{B}, {k_max + 1}]")
     _shape(t_row_start, "t_row_start", (B,))
     _shape(q_row_start, "q_row_start", (B,))
@@ -335,13 +372,17 @@ def sv_verify_sample(target: torch.Tensor, draft: torch.Tensor, t_row_start: tor
         _shape(dg, "out diag", (B, k_max + 1, 4), torch.float32)
         _shape(rs, "out resid", (B,), torch.float32)
     ws = _workspace(workspace, dev, stream, workspace_bytes(SV_OP_SAMPLE, B, t_rows, V))
-    args = (_dev(target, "target"), _dtype_code(target), t_rows,
+    head = (_dev(target, "target"), _dtype_code(target), t_rows,
             _dev(draft, "draft"), _dtype_code(draft), q_rows, V,
             _dev(t_row_start, "t_row_start", torch.int32, dev),
             _dev(q_row_start, "q_row_start", torch.int32, dev),
             _dev(draft_ids, "draft_ids", torch.int32, dev),
-            _dev(draft_len, "draft_len", torch.int32, dev), B, k_max,
-            float(temperature), _dev(uniforms, "uniforms", torch.float32, dev),
+            _dev(draft_len, "draft_len", torch.int32, dev), B, k_max, float(temperature))
+    if philox is None:
+        rng = (_dev(uniforms, "uniforms", torch.float32, dev),)
+    else:
+        rng = (philox[0] & (2 ** 64 - 1), philox[1] & (2 ** 64 - 1))
+    args = head + rng + (
             _dev(max_new, "max_new", torch.int32, dev), eos_id,
             _dev(tok, "out"), _dev(cnt, "cnt"), _dev(acc, "acc"),
             _dev(dg, "diag", torch.float32, dev), _dev(rs, "resid", torch.float32, dev),
@@ -349,7 +390,8 @@ def sv_verify_sample(target: torch.Tensor, draft: torch.Tensor, t_row_start: tor
             ws.data_ptr(), ws.numel(), _stream(stream))
     keep = (target, draft, t_row_start, q_row_start, draft_ids, draft_len, uniforms, max_new, dev_status,
             tok, cnt, acc, dg, rs, ws)
-    return _invoke("sv_verify_sample", args, keep, (tok, cnt, acc, dg, rs))
+    name = "sv_verify_sample" if philox is None else "sv_verify_sample_philox"
+    return _invoke(name, args, keep, (tok, cnt, acc, dg, rs))
 
 
 def prepare_verify_sample(*args, **kwargs):

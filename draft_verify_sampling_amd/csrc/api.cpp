@@ -112,6 +112,8 @@ sv_status launch_walk_call(int mode, int32_t t_dtype, int32_t q_dtype, sv::WalkA
     c.ids = a.ids;
     c.dlen = a.dlen;
     c.u = a.u;
+    c.seed = a.seed;
+    c.offset = a.offset;
     c.nseg = a.nseg;
     c.stop = reinterpret_cast<uint32_t*>(ws + L.stop_off);
     c.count = reinterpret_cast<uint32_t*>(ws + L.count_off);
@@ -261,15 +263,17 @@ sv_status sv_verify_greedy(const void* target_logits, int32_t t_dtype, int32_t t
   return e == hipSuccess ? SV_OK : device_fail(e, "sv_verify_greedy resolve launch");
 }
 
-sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t_rows,
-                           const void* draft_probs, int32_t q_dtype, int32_t q_rows, int64_t vocab,
-                           const int32_t* t_row_start, const int32_t* q_row_start,
-                           const int32_t* draft_ids, const int32_t* draft_len, int32_t batch,
-                           int32_t k_max, float temperature, const float* uniforms,
-                           const int32_t* max_new, int32_t eos_id, int32_t* out_tokens,
-                           int32_t* out_count, int32_t* out_accepted, float* out_diag,
-                           float* out_resid, int32_t* dev_status, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+// Sampled chain verify, with the uniforms from the caller (uniforms != null)
+// or from the Philox stream (seed, offset).
+static sv_status sample_impl(const void* target_logits, int32_t t_dtype, int32_t t_rows,
+                             const void* draft_probs, int32_t q_dtype, int32_t q_rows, int64_t vocab,
+                             const int32_t* t_row_start, const int32_t* q_row_start,
+                             const int32_t* draft_ids, const int32_t* draft_len, int32_t batch,
+                             int32_t k_max, float temperature, const float* uniforms, bool philox,
+                             uint64_t seed, uint64_t offset, const int32_t* max_new, int32_t eos_id,
+                             int32_t* out_tokens, int32_t* out_count, int32_t* out_accepted,
+                             float* out_diag, float* out_resid, int32_t* dev_status, void* workspace,
+                             size_t workspace_bytes, void* stream, const char* what) {
   if (!dtype_ok(t_dtype) || !dtype_ok(q_dtype))
     return fail(SV_E_DTYPE, "t_dtype and q_dtype must be SV_F32 or SV_BF16");
   if (batch < 0) return fail(SV_E_ARG, "batch < 0");
@@ -281,7 +285,7 @@ sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t
   if (batch == 0) return SV_OK;
   if (t_rows < 1) return fail(SV_E_ARG, "t_rows < 1");
   if (target_logits == nullptr || t_row_start == nullptr || q_row_start == nullptr ||
-      draft_len == nullptr || uniforms == nullptr || out_tokens == nullptr || out_count == nullptr ||
+      draft_len == nullptr || (!philox && uniforms == nullptr) || out_tokens == nullptr || out_count == nullptr ||
       out_accepted == nullptr || (k_max > 0 && draft_ids == nullptr) ||
       (q_rows > 0 && draft_probs == nullptr))
     return fail(SV_E_ARG, "null pointer argument");
@@ -296,7 +300,9 @@ sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t
   a.V = vocab;
   a.c = sv::kLog2e / temperature;
   a.B = batch;
-  a.u = uniforms;
+  a.u = philox ? nullptr : uniforms;
+  a.seed = seed;
+  a.offset = offset;
   a.t_rows = t_rows;
   a.q_rows = q_rows;
   a.t_rs = t_row_start;
@@ -316,7 +322,48 @@ sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t
   // a request has at most min(k_max + 1, t_rows) nodes
   const int64_t nodes = std::min<int64_t>(k_max + 1, t_rows);
   return launch_walk_call(sv::kWalkChain, t_dtype, q_dtype, a, t_rows, nodes, k_max + 1, workspace,
-                          static_cast<hipStream_t>(stream), "sv_verify_sample");
+                          static_cast<hipStream_t>(stream), what);
+}
+
+sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t_rows,
+                           const void* draft_probs, int32_t q_dtype, int32_t q_rows, int64_t vocab,
+                           const int32_t* t_row_start, const int32_t* q_row_start,
+                           const int32_t* draft_ids, const int32_t* draft_len, int32_t batch,
+                           int32_t k_max, float temperature, const float* uniforms,
+                           const int32_t* max_new, int32_t eos_id, int32_t* out_tokens,
+                           int32_t* out_count, int32_t* out_accepted, float* out_diag,
+                           float* out_resid, int32_t* dev_status, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return sample_impl(target_logits, t_dtype, t_rows, draft_probs, q_dtype, q_rows, vocab, t_row_start,
+                     q_row_start, draft_ids, draft_len, batch, k_max, temperature, uniforms, false, 0, 0,
+                     max_new, eos_id, out_tokens, out_count, out_accepted, out_diag, out_resid, dev_status,
+                     workspace, workspace_bytes, stream, "sv_verify_sample");
+}
+
+sv_status sv_verify_sample_philox(const void* target_logits, int32_t t_dtype, int32_t t_rows,
+                                  const void* draft_probs, int32_t q_dtype, int32_t q_rows, int64_t vocab,
+                                  const int32_t* t_row_start, const int32_t* q_row_start,
+                                  const int32_t* draft_ids, const int32_t* draft_len, int32_t batch,
+                                  int32_t k_max, float temperature, uint64_t seed, uint64_t offset,
+                                  const int32_t* max_new, int32_t eos_id, int32_t* out_tokens,
+                                  int32_t* out_count, int32_t* out_accepted, float* out_diag,
+                                  float* out_resid, int32_t* dev_status, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  return sample_impl(target_logits, t_dtype, t_rows, draft_probs, q_dtype, q_rows, vocab, t_row_start,
+                     q_row_start, draft_ids, draft_len, batch, k_max, temperature, nullptr, true, seed,
+                     offset, max_new, eos_id, out_tokens, out_count, out_accepted, out_diag, out_resid,
+                     dev_status, workspace, workspace_bytes, stream, "sv_verify_sample_philox");
+}
+
+sv_status sv_philox_uniforms(uint64_t seed, uint64_t offset, int32_t batch, int32_t slots, float* out,
+                             void* stream) {
+  if (batch < 0 || slots < 0) return fail(SV_E_ARG, "batch and slots must be >= 0");
+  if (static_cast<int64_t>(batch) * slots == 0) return SV_OK;
+  if (out == nullptr) return fail(SV_E_ARG, "null pointer argument");
+  if (static_cast<int64_t>(batch) * slots > kMaxGrid * 256) return fail(SV_E_ARG, "too many slots");
+  (void)hipGetLastError();
+  const hipError_t e = sv::launch_philox_fill(seed, offset, batch, slots, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SV_OK : device_fail(e, "sv_philox_uniforms");
 }
 
 sv_status sv_verify_tree(const void* target_logits, int32_t t_dtype, const void* draft_probs,

@@ -181,4 +181,48 @@ __device__ __forceinline__ void flag(int32_t* status, int bits) {
   if (status != nullptr && bits != 0) atomicOr(status, bits);
 }
 
+// ---- counter-based uniforms: Philox4x64-10 ----
+// Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2,
+// 3" (SC 2011): ten rounds of two 64 x 64 -> 128-bit products of counter
+// words with the multipliers, high halves xored with the other words and the
+// round keys, the words permuted, the key bumped by the Weyl constants.
+constexpr uint64_t kPhiloxM0 = 0xD2E7470EE14C6C93ull;
+constexpr uint64_t kPhiloxM1 = 0xCA5A826395121157ull;
+constexpr uint64_t kPhiloxW0 = 0x9E3779B97F4A7C15ull;
+constexpr uint64_t kPhiloxW1 = 0xBB67AE8584CAA73Bull;
+
+__device__ __forceinline__ void philox4x64_10(uint64_t& x0, uint64_t& x1, uint64_t& x2, uint64_t& x3,
+                                              uint64_t k0, uint64_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t hi0 = __umul64hi(kPhiloxM0, x0), lo0 = kPhiloxM0 * x0;
+    const uint64_t hi1 = __umul64hi(kPhiloxM1, x2), lo1 = kPhiloxM1 * x2;
+    const uint64_t y0 = hi1 ^ x1 ^ k0, y2 = hi0 ^ x3 ^ k1;
+    x0 = y0;
+    x1 = lo1;
+    x2 = y2;
+    x3 = lo0;
+    k0 += kPhiloxW0;
+    k1 += kPhiloxW1;
+  }
+}
+
+// Uniform of slot i of request b: word i mod 4 of the Philox block at
+// counter (i div 4, b, offset, 0) under key (seed, 0), its top 24 bits
+// times 2^-24 (a value on the 2^-24 grid in [0, 1), exact in float).
+__device__ __forceinline__ float philox_uniform(uint64_t seed, uint64_t offset, int64_t b, int i) {
+  uint64_t x0 = static_cast<uint64_t>(i) >> 2, x1 = static_cast<uint64_t>(b), x2 = offset, x3 = 0;
+  philox4x64_10(x0, x1, x2, x3, seed, 0);
+  const int w = i & 3;
+  const uint64_t v = w == 0 ? x0 : (w == 1 ? x1 : (w == 2 ? x2 : x3));
+  return static_cast<float>(v >> 40) * 0x1p-24f;
+}
+
+// Uniform slot i of request b: the caller's array u [B, slots], or the
+// Philox stream (seed, offset) when u is null.
+__device__ __forceinline__ float slot_uniform(const float* u, uint64_t seed, uint64_t offset, int64_t b,
+                                              int slots, int i) {
+  return u != nullptr ? u[b * slots + i] : philox_uniform(seed, offset, b, i);
+}
+
 }  // namespace sv

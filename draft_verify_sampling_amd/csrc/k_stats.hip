@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
   float lx = 0.f, qx = 0.f, u = 0.f;
   if (threadIdx.x == 0 && i < k) {
     x = a.ids[static_cast<int64_t>(b) * a.k_max + i];
-    u = a.u[static_cast<int64_t>(b) * R + i];
+    u = slot_uniform(a.u, a.seed, a.offset, b, R, i);
     if (x >= 0 && x < a.V) {
       lx = DT::at(row_ptr<DT>(a.tgt, ts + i, a.V), x);
       qx = DQ::at(row_ptr<DQ>(a.dq, qs + i, a.V), x);

@@ -325,7 +325,7 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
     const int k = a.dlen[b];
     const int ts = a.t_rs[b], qs = a.q_rs[b];
     const int tokv = tid < a.k_max ? a.ids[static_cast<int64_t>(b) * a.k_max + tid] : -1;
-    const float uv = tid <= a.k_max ? a.u[static_cast<int64_t>(b) * (a.k_max + 1) + tid] : 0.f;
+    const float uv = tid <= a.k_max ? slot_uniform(a.u, a.seed, a.offset, b, a.k_max + 1, tid) : 0.f;
     if (k < 0 || k > a.k_max || ts < 0 || static_cast<int64_t>(ts) + k >= a.t_rows ||
         (k > 0 && (qs < 0 || static_cast<int64_t>(qs) + k > a.q_rows))) {
       if (wk.g == 0) walk_invalid<kChain>(a, b, kFlagBadRequest, tid, kWalkBlock);
@@ -416,7 +416,7 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
       if (bad) atomicOr(&s_bad, bad);
       s_par[c] = par;
       s_tok[c] = tok;
-      s_u[c] = kGreedy ? 0.f : a.u[trow0 + c];
+      s_u[c] = kGreedy ? 0.f : slot_uniform(a.u, a.seed, a.offset, b, N, c);
     }
     __syncthreads();
     if (const int bad = s_bad) {
@@ -768,7 +768,7 @@ __global__ __launch_bounds__(kBlock) void k_walk_small(WalkArgs a) {
     const int x = draft ? a.ids[b * a.k_max + i] : 0;
     const bool xin = x >= 0 && x < V;
     if (__ballot(draft && !xin)) bad_tok = true;
-    const float u = row ? a.u[b * width + i] : 0.f;
+    const float u = row ? slot_uniform(a.u, a.seed, a.offset, b, width, i) : 0.f;
     float2 ms = make_float2(-INFINITY, 0.f);
     float lx = 0.f, qx = 0.f;
     if (row) ms = a.partial[static_cast<int64_t>(ts + i) * a.nseg];
@@ -822,7 +822,7 @@ __global__ __launch_bounds__(kBlock) void k_walk_small(WalkArgs a) {
       total = v[0][1];
     }
   }
-  const double target = static_cast<double>(a.u[b * width + k]) * total;
+  const double target = static_cast<double>(slot_uniform(a.u, a.seed, a.offset, b, width, k)) * total;
   const TileHit h{0, 0.0, false};
   const int y = wave_pick_in_tile<DT, DQ>(row, V, h, target);
   if (lane == 0) {
@@ -860,6 +860,23 @@ hipError_t launch_clear(void* p, size_t bytes, hipStream_t stream) {
   const int64_t blocks = std::min<int64_t>((n16 + kBlock - 1) / kBlock, 2048);
   hipLaunchKernelGGL(k_walk_clear, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream,
                      static_cast<uint4*>(p), n16);
+  return hipGetLastError();
+}
+
+// The Philox uniforms of [B, slots] slots, one thread per slot.
+__global__ __launch_bounds__(kBlock) void k_philox_fill(uint64_t seed, uint64_t offset, int32_t slots,
+                                                        int64_t n, float* u) {
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kBlock + threadIdx.x;
+  if (t >= n) return;
+  u[t] = philox_uniform(seed, offset, t / slots, static_cast<int>(t % slots));
+}
+
+hipError_t launch_philox_fill(uint64_t seed, uint64_t offset, int32_t B, int32_t slots, float* u,
+                              hipStream_t stream) {
+  const int64_t n = static_cast<int64_t>(B) * slots;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_philox_fill, dim3(static_cast<uint32_t>((n + kBlock - 1) / kBlock)), dim3(kBlock), 0,
+                     stream, seed, offset, slots, n, u);
   return hipGetLastError();
 }
 

@@ -112,7 +112,8 @@ struct ChainStatsArgs {
   const int32_t* q_rs;
   const int32_t* ids;
   const int32_t* dlen;
-  const float* u;
+  const float* u;        // [B, k_max + 1], or null: Philox stream (seed, offset)
+  uint64_t seed, offset;
   int32_t nseg;
   uint32_t* stop;        // [B] kMaxChainRows - (first row that stops the round); 0: none
   uint32_t* count;       // [B, R] finished segments
@@ -136,7 +137,8 @@ struct WalkArgs {
   int64_t V;
   float c;                  // log2(e) / T
   int32_t B;
-  const float* u;
+  const float* u;           // [B, slots], or null: Philox stream (seed, offset)
+  uint64_t seed, offset;
   // chain: request b has k_b = dlen[b] drafts, rows t_rs[b] + i and q_rs[b] + i
   int32_t t_rows, q_rows;
   const int32_t* t_rs;
@@ -208,6 +210,9 @@ hipError_t launch_row_stats(int dtype, const void* rows, int64_t n_rows, int64_t
 hipError_t launch_row_argmax(int dtype, const void* rows, int64_t n_rows, int64_t V, int32_t nseg,
                              uint64_t* keys, hipStream_t stream);
 hipError_t launch_greedy_resolve(const GreedyArgs& a, hipStream_t stream);
+// Fill u [B, slots] with the Philox stream (seed, offset).
+hipError_t launch_philox_fill(uint64_t seed, uint64_t offset, int32_t B, int32_t slots, float* u,
+                              hipStream_t stream);
 hipError_t launch_ngram(const int32_t* ctx, const int32_t* ctx_len, int32_t B, int32_t stride,
                         int32_t window, int32_t k, int32_t* ids, int32_t* lens, int32_t* status,
                         hipStream_t stream);

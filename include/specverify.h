@@ -27,6 +27,8 @@
  *   sv_verify_tree_pointmass  the same tree with each candidate tested as a
  *                     point mass on its own token (deterministic top-k
  *                     candidates).
+ *   sv_philox_uniforms, sv_verify_sample_philox  the verify's uniforms from a
+ *                     counter-based generator on the device.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -180,6 +182,32 @@ sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t
                            int32_t* out_tokens, int32_t* out_count, int32_t* out_accepted,
                            float* out_diag, float* out_resid, int32_t* dev_status,
                            void* workspace, size_t workspace_bytes, void* stream);
+
+/* Counter-based uniforms (Philox4x64-10; Salmon, Moraes, Dror and Shaw,
+ * "Parallel random numbers: as easy as 1, 2, 3", SC 2011), so that a serving
+ * loop need not generate and upload the verify's uniforms.  Slot i of request
+ * b is word i mod 4 of the Philox block at counter (i div 4, b, offset, 0)
+ * under key (seed, 0), its top 24 bits times 2^-24: a value on the 2^-24 grid
+ * in [0, 1), exact in float.  Use a new offset (or seed) for every round.
+ * sv_philox_uniforms writes out [batch, slots] float (batch, slots >= 0). */
+sv_status sv_philox_uniforms(uint64_t seed, uint64_t offset, int32_t batch, int32_t slots,
+                             float* out, void* stream);
+
+/* sv_verify_sample with its uniforms drawn on the device: u[b, i] is slot i
+ * of request b of the Philox stream (seed, offset) above, with
+ * slots = k_max + 1 (the same values sv_philox_uniforms writes); everything
+ * else as for sv_verify_sample. */
+sv_status sv_verify_sample_philox(const void* target_logits, int32_t t_dtype, int32_t t_rows,
+                                  const void* draft_probs, int32_t q_dtype, int32_t q_rows,
+                                  int64_t vocab, const int32_t* t_row_start,
+                                  const int32_t* q_row_start, const int32_t* draft_ids,
+                                  const int32_t* draft_len, int32_t batch, int32_t k_max,
+                                  float temperature, uint64_t seed, uint64_t offset,
+                                  const int32_t* max_new, int32_t eos_id,
+                                  int32_t* out_tokens, int32_t* out_count,
+                                  int32_t* out_accepted, float* out_diag, float* out_resid,
+                                  int32_t* dev_status, void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /* Tree verify.
  * Node c of request b (flattened order, node 0 = root) owns target row

@@ -90,3 +90,28 @@ def compare_tokens(got, want, keys=("tokens", "count", "accepted")):
     near = np.nanmin(np.where(np.isnan(want["margins"]), np.inf, want["margins"]), axis=1) < BOUNDARY
     bad = ~same & ~near
     return int((~same & near).sum()), np.nonzero(bad)[0]
+
+
+def tv_at_noise_level(emitted, n_positions, p_rows, count, rng, family_alpha=0.01, reps=1000):
+    """TV of the emitted token at each position (rounds that reach it) against
+    the target row there, and the fraction of `reps` multinomial draws of the
+    same size from that row whose TV is at least as large (a p-value).  The
+    positions are tested together at family-wise level `family_alpha`
+    (Bonferroni: each p-value must exceed family_alpha / positions tested).
+    Returns [(position, n, tv, p-value)]; asserts the criterion."""
+    res = []
+    for i in range(n_positions):
+        sel = count > i
+        n = int(sel.sum())
+        if n < 2000:
+            continue
+        p = p_rows[i]
+        emp = np.bincount(emitted[sel, i], minlength=p.shape[0]) / n
+        tv = 0.5 * np.abs(emp - p).sum()
+        noise = np.array([0.5 * np.abs(rng.multinomial(n, p) / n - p).sum() for _ in range(reps)])
+        res.append((i, n, float(tv), float((noise >= tv).mean())))
+    for i, n, tv, pv in res:
+        say(f"  position {i}: n={n} TV={tv:.4f} p-value {pv:.3f}")
+    assert res, "no position reached often enough"
+    assert min(pv for *_, pv in res) > family_alpha / len(res), res
+    return res

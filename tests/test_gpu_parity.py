@@ -15,7 +15,7 @@ from scipy.special import softmax as scipy_softmax
 import oracle
 import synth
 from tests.gpu_util import (say, run_sample, run_greedy, run_tree, close, compare_tokens, same_round,
-                            rows_to_dev, i32, f32, DEV)
+                            rows_to_dev, i32, f32, DEV, tv_at_noise_level)
 
 pytestmark = pytest.mark.gpu
 
@@ -187,18 +187,8 @@ def test_gpu_sample_c1_parity_and_tv(c1):
     want = _oracle_sample(c1)
     _check_chain(c1, got, want, "c1")
     assert int(st.item()) == 0
-    rng = np.random.default_rng(99)
-    for i in range(c1.k_max + 1):
-        sel = got["count"] > i
-        n = int(sel.sum())
-        if n < 2000:
-            continue
-        p = scipy_softmax(c1.target[i].astype(np.float64) / c1.T)
-        emp = np.bincount(got["tokens"][sel, i], minlength=c1.V) / n
-        tv = 0.5 * np.abs(emp - p).sum()
-        noise = np.percentile([0.5 * np.abs(rng.multinomial(n, p) / n - p).sum() for _ in range(100)], 99)
-        say(f"  position {i}: n={n} TV={tv:.4f} noise q99={noise:.4f}")
-        assert tv <= noise
+    rows = [scipy_softmax(c1.target[i].astype(np.float64) / c1.T) for i in range(c1.k_max + 1)]
+    tv_at_noise_level(got["tokens"], c1.k_max + 1, rows, got["count"], np.random.default_rng(99))
 
 
 @pytest.fixture(scope="module")
