@@ -56,6 +56,10 @@ print, closed forms, or brute force):
                                  on many keys and counters, carries included.
 * ``philox.philox_uniforms``    the slot-to-word mapping against those blocks;
                                  grid and range.
+* ``tree_build``                the EAGLE-2 worked example (values, kept set,
+                                 flattened order, positions); brute-force
+                                 top-k; connectivity and ancestor-mask
+                                 invariants on random rounds.
 """
 from .rows import widen, FLAG_BAD_REQUEST, FLAG_BAD_TOKEN, FLAG_NONFINITE, \
     FLAG_OVER_BUDGET, FLAG_FALLBACK, FLAG_BAD_TREE, INVALID_FLAGS
@@ -64,12 +68,13 @@ from .chain import (verify_sample, verify_greedy, greedy_path_verify,
 from .ngram import ngram_draft
 from .tree import verify_tree, verify_tree_greedy, verify_tree_pointmass
 from .philox import philox4x64_10, philox_uniforms
+from .tree_build import DraftTree, topk_children, build_tree
 
 __all__ = [
     "widen", "verify_sample", "verify_greedy", "greedy_path_verify",
     "forward_accounting", "naive_round", "softmax_T", "inverse_cdf",
     "ngram_draft", "verify_tree", "verify_tree_greedy", "verify_tree_pointmass",
-    "philox4x64_10", "philox_uniforms",
+    "philox4x64_10", "philox_uniforms", "DraftTree", "topk_children", "build_tree",
     "FLAG_BAD_REQUEST", "FLAG_BAD_TOKEN", "FLAG_NONFINITE", "FLAG_OVER_BUDGET",
     "FLAG_FALLBACK", "FLAG_BAD_TREE", "INVALID_FLAGS",
 ]
