@@ -184,7 +184,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c3p", "c4", "c5", "c5g", "c5p"])
+    ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c3p", "c4", "c5", "c5g", "c5p", "tb"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--graph", action="store_true",
@@ -399,6 +399,49 @@ def main():
                       mean_tokens_per_round=round(float(out[1].float().mean().item()), 4),
                       visited_target_row_bytes=visited_bytes,
                       visited_GBps=round(visited_bytes / (ms * 1e-3) / 1e9, 1),
+                      event_ms_per_step=dict(timed_region=round(tot_ms / args.steps, 5),
+                                             p50=round(float(np.percentile(ev_ms, 50)), 5)),
+                      roofline=None)
+    elif W == "tb":
+        # the EAGLE-2 tree built on the device at the tree workload's shape:
+        # 32 requests, top 4 children, the best 4 of each layer expanded, 6
+        # rounds, 60 nodes kept; a step = the 6 rounds (each a top-k pass over
+        # the expanded nodes' draft rows) and the finalize with the mask
+        log("generating draft rows for the tree builder")
+        B, V, top, exp, depth, N = 32, 128_256, 4, 4, 6, 60
+        rng = np.random.default_rng(2026)
+        rounds = []
+        for r in range(depth):
+            n = B * (1 if r == 0 else exp)
+            l = rng.standard_normal((n, V)).astype(np.float32) * 1.5
+            p = np.exp(l - l.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            rounds.append(_rows(synth.encode(p, "bf16"), "bf16", torch, dev))
+        state = sv.DraftTreeState(B, 1 + top + (depth - 1) * exp * top, dev)
+        ws = sv.Workspace(dev)
+        nexts = [torch.empty((B, exp), dtype=torch.int32, device=dev) for _ in range(depth)]
+        outs = ([torch.empty((B, N), dtype=torch.int32, device=dev) for _ in range(4)]
+                + [torch.empty((B, N, N), dtype=torch.uint8, device=dev)])
+        calls = []
+        for r in range(depth):
+            calls.append(sv.prepare(sv.sv_tree_expand, rounds[r], None if r == 0 else nexts[r - 1], top, exp,
+                                    state, next_exp=nexts[r], workspace=ws)[0])
+        calls.append(sv.prepare(sv.sv_tree_finalize, state, N, out=outs)[0])
+
+        def step(i):
+            for c in calls:
+                c()
+
+        wall, tot_ms, ev_ms = timed(step, args.steps, args.warmup, torch)
+        ms = 1e3 * wall / args.steps
+        row_bytes = sum(int(t.numel()) * 2 for t in rounds)
+        result.update(value=round(B / (ms * 1e-3), 1), unit="trees/s", ms_per_step=round(ms, 5),
+                      config=dict(workload="EAGLE-2 draft tree built on the device: 32 requests, V=128,256 bf16 "
+                                           "draft rows, top 4 children, 4 nodes expanded per round, 6 rounds, "
+                                           "60 nodes kept, ancestor mask", batch=B, vocab=V, top_children=top,
+                                  expand_per_round=exp, rounds=depth, nodes=N, inputs="bf16"),
+                      draft_row_bytes_per_step=row_bytes,
+                      row_GBps=round(row_bytes / (ms * 1e-3) / 1e9, 1),
                       event_ms_per_step=dict(timed_region=round(tot_ms / args.steps, 5),
                                              p50=round(float(np.percentile(ev_ms, 50)), 5)),
                       roofline=None)

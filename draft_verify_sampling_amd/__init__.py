@@ -25,12 +25,13 @@ __all__ = [
     "FLAG_BAD_REQUEST", "FLAG_BAD_TOKEN", "FLAG_NONFINITE", "FLAG_OVER_BUDGET",
     "FLAG_FALLBACK", "FLAG_BAD_TREE", "FLAG_SYNC_TIMEOUT", "EXPORTS",
     "sv_verify_tree_greedy", "sv_verify_tree_pointmass", "prepare", "prepare_verify_sample",
-    "sv_philox_uniforms", "sv_verify_sample_philox",
+    "sv_philox_uniforms", "sv_verify_sample_philox", "DraftTreeState", "sv_tree_expand",
+    "sv_tree_finalize", "SV_OP_TREE_EXPAND",
     "prepare_softmax_partials",
 ]
 
 SV_F32, SV_BF16 = 0, 1
-SV_OP_GREEDY, SV_OP_SAMPLE, SV_OP_TREE = 0, 1, 2
+SV_OP_GREEDY, SV_OP_SAMPLE, SV_OP_TREE, SV_OP_TREE_EXPAND = 0, 1, 2, 3
 FLAG_BAD_REQUEST, FLAG_BAD_TOKEN, FLAG_NONFINITE = 1, 2, 4
 FLAG_OVER_BUDGET, FLAG_FALLBACK, FLAG_BAD_TREE, FLAG_SYNC_TIMEOUT = 8, 16, 32, 64
 
@@ -38,7 +39,7 @@ EXPORTS = ("sv_abi_version", "sv_status_string", "sv_last_error", "sv_workspace_
            "sv_softmax_segments", "sv_softmax_partials",
            "sv_ngram_draft", "sv_verify_greedy", "sv_verify_sample", "sv_verify_tree",
            "sv_verify_tree_greedy", "sv_verify_tree_pointmass", "sv_philox_uniforms",
-           "sv_verify_sample_philox")
+           "sv_verify_sample_philox", "sv_tree_expand", "sv_tree_finalize")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -67,6 +68,9 @@ _SIGS = {
                                       P, P, P, P, P, SZ, P]),
     "sv_verify_tree_greedy": (ctypes.c_int, [P, I32, I64, P, P, I32, I32, P, P, P, P, P, P, SZ, P]),
     "sv_philox_uniforms": (ctypes.c_int, [U64, U64, I32, I32, P, P]),
+    "sv_tree_expand": (ctypes.c_int, [P, I32, I64, I32, I32, P, I32, I32, I32, P, P, P, P, P, P, P, P,
+                                      P, SZ, P]),
+    "sv_tree_finalize": (ctypes.c_int, [I32, I32, P, P, P, P, P, P, I32, P, P, P, P, P, P, P]),
     "sv_verify_sample_philox": (ctypes.c_int, [P, I32, I32, P, I32, I32, I64, P, P, P, P, I32, I32,
                                                F32, U64, U64, P, I32, P, P, P, P, P, P, P, SZ, P]),
     "sv_verify_tree_pointmass": (ctypes.c_int, [P, I32, I64, P, P, I32, I32, F32, P, P, P, P, P,
@@ -492,3 +496,70 @@ def sv_verify_tree_pointmass(target: torch.Tensor, parent: torch.Tensor, node_to
             _dev(dev_status, "dev_status", torch.int32, dev), ws.data_ptr(), ws.numel(), _stream(stream))
     keep = (target, parent, node_token, uniforms, dev_status, tok, cnt, acc, pth, ws)
     return _invoke("sv_verify_tree_pointmass", args, keep, (tok, cnt, acc, pth))
+
+
+class DraftTreeState:
+    """Device candidates of a batch of EAGLE-2 draft trees (see sv_tree_expand):
+    token, parent, depth [B, max_cand] int32, conf float32, value float64,
+    count [B] int32."""
+
+    def __init__(self, batch: int, max_cand: int, device=None):
+        dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+        self.batch, self.max_cand = batch, max_cand
+        self.token = torch.empty((batch, max_cand), dtype=torch.int32, device=dev)
+        self.parent = torch.empty((batch, max_cand), dtype=torch.int32, device=dev)
+        self.depth = torch.empty((batch, max_cand), dtype=torch.int32, device=dev)
+        self.conf = torch.empty((batch, max_cand), dtype=torch.float32, device=dev)
+        self.value = torch.empty((batch, max_cand), dtype=torch.float64, device=dev)
+        self.count = torch.zeros((batch,), dtype=torch.int32, device=dev)
+
+
+def sv_tree_expand(draft_rows: torch.Tensor, exp_node: Optional[torch.Tensor], top_children: int,
+                   expand_next: int, state: DraftTreeState, next_exp: Optional[torch.Tensor] = None,
+                   dev_status: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None,
+                   stream=None) -> torch.Tensor:
+    """One EAGLE-2 round.  draft_rows [B * n_exp, V]: the draft's distribution at
+    each node of exp_node [B, n_exp] (None: the first round, one root row per
+    request).  Returns next_exp [B, expand_next]: the candidates to expand next."""
+    B = state.batch
+    rows, V = draft_rows.shape
+    n_exp = 1 if exp_node is None else exp_node.shape[1]
+    if rows != B * n_exp:
+        raise SpecVerifyError(f"draft_rows must be [B * n_exp, V] = [{B * n_exp}, V]")
+    _shape(exp_node, "exp_node", (B, n_exp))
+    _status_arg(dev_status)
+    dev = draft_rows.device
+    if next_exp is None:
+        next_exp = torch.empty((B, expand_next), dtype=torch.int32, device=dev)
+    _shape(next_exp, "next_exp", (B, expand_next), torch.int32)
+    ws = _workspace(workspace, dev, stream, workspace_bytes(SV_OP_TREE_EXPAND, B, rows, V))
+    args = (_dev(draft_rows, "draft_rows"), _dtype_code(draft_rows), V, B, n_exp,
+            _dev(exp_node, "exp_node", torch.int32, dev), top_children, expand_next, state.max_cand,
+            _dev(state.token, "token"), _dev(state.parent, "parent"), _dev(state.depth, "depth"),
+            _dev(state.conf, "conf"), _dev(state.value, "value"), _dev(state.count, "count"),
+            _dev(next_exp, "next_exp"), _dev(dev_status, "dev_status", torch.int32, dev),
+            ws.data_ptr(), ws.numel(), _stream(stream))
+    keep = (draft_rows, exp_node, state, next_exp, dev_status, ws)
+    return _invoke("sv_tree_expand", args, keep, next_exp)
+
+
+def sv_tree_finalize(state: DraftTreeState, n_nodes: int, mask: bool = True,
+                     dev_status: Optional[torch.Tensor] = None, stream=None, out=None):
+    """Rerank and flatten: returns (parent, token, depth, cand [B, n_nodes] int32,
+    mask [B, n_nodes, n_nodes] uint8 or None)."""
+    B = state.batch
+    dev = state.token.device
+    _status_arg(dev_status)
+    if out is None:
+        outs = [torch.empty((B, n_nodes), dtype=torch.int32, device=dev) for _ in range(4)]
+        m = torch.empty((B, n_nodes, n_nodes), dtype=torch.uint8, device=dev) if mask else None
+    else:
+        *outs, m = out
+        for t, nm in zip(outs, ("parent", "token", "depth", "cand")):
+            _shape(t, f"out {nm}", (B, n_nodes), torch.int32)
+        _shape(m, "out mask", (B, n_nodes, n_nodes), torch.uint8)
+    args = (B, state.max_cand, _dev(state.token, "token"), _dev(state.parent, "parent"),
+            _dev(state.depth, "depth"), _dev(state.conf, "conf"), _dev(state.value, "value"),
+            _dev(state.count, "count"), n_nodes, *(_dev(t, "out") for t in outs), _dev(m, "mask"),
+            _dev(dev_status, "dev_status", torch.int32, dev), _stream(stream))
+    return _invoke("sv_tree_finalize", args, (state, outs, m, dev_status), (*outs, m))

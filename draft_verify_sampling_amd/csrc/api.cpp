@@ -166,6 +166,9 @@ size_t sv_workspace_bytes(int op, int64_t batch, int64_t total_rows, int64_t voc
       if (batch == 0) return 0;
       return sv::walk_layout(batch, total_rows, vocab, sv::walk_groups_bound(batch),
                              sv::walk_max_sync(total_rows / batch), 0).end;
+    case SV_OP_TREE_EXPAND:  // total_rows = batch * expanded nodes per request
+      return sv::align256(static_cast<size_t>(total_rows * sv::tree_topk_segments(total_rows, vocab)) *
+                          sv::kMaxTreeTop * 8);
     case SV_OP_SAMPLE: {
       // a request has at most min(t_rows, 256) rows
       const int64_t R = std::min<int64_t>(total_rows, sv::kMaxChainRows);
@@ -477,6 +480,86 @@ sv_status sv_verify_tree_pointmass(const void* target_logits, int32_t t_dtype, i
   return tree_variant(sv::kWalkPoint, target_logits, t_dtype, vocab, parent, node_token, batch, n_nodes,
                       temperature, uniforms, out_tokens, out_count, out_accepted, out_path, dev_status,
                       workspace, workspace_bytes, stream, "sv_verify_tree_pointmass");
+}
+
+sv_status sv_tree_expand(const void* draft_rows, int32_t q_dtype, int64_t vocab, int32_t batch,
+                         int32_t n_exp, const int32_t* exp_node, int32_t top_children,
+                         int32_t expand_next, int32_t max_cand, int32_t* cand_token,
+                         int32_t* cand_parent, int32_t* cand_depth, float* cand_conf,
+                         double* cand_value, int32_t* cand_count, int32_t* next_exp,
+                         int32_t* dev_status, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(q_dtype)) return fail(SV_E_DTYPE, "q_dtype must be SV_F32 or SV_BF16");
+  if (batch < 0) return fail(SV_E_ARG, "batch < 0");
+  if (n_exp < 1 || n_exp > sv::kMaxTreeExpand) return fail(SV_E_ARG, "n_exp must be in [1, 64]");
+  if (exp_node == nullptr && n_exp != 1) return fail(SV_E_ARG, "the first round expands one root per request");
+  if (top_children < 1 || top_children > sv::kMaxTreeTop) return fail(SV_E_ARG, "top_children must be in [1, 16]");
+  if (vocab < top_children || vocab > INT32_MAX) return fail(SV_E_ARG, "vocab must be in [top_children, 2^31)");
+  if (expand_next < 1 || expand_next > sv::kMaxTreeExpand) return fail(SV_E_ARG, "expand_next must be in [1, 64]");
+  if (max_cand < 1 || max_cand > sv::kMaxTreeCand) return fail(SV_E_ARG, "max_cand must be in [1, 1024]");
+  if (batch == 0) return SV_OK;
+  if (draft_rows == nullptr || cand_token == nullptr || cand_parent == nullptr || cand_depth == nullptr ||
+      cand_conf == nullptr || cand_value == nullptr || cand_count == nullptr || next_exp == nullptr)
+    return fail(SV_E_ARG, "null pointer argument");
+  const int64_t rows = static_cast<int64_t>(batch) * n_exp;
+  const int32_t nseg = sv::tree_topk_segments(rows, vocab);
+  if (rows * nseg > kMaxGrid) return fail(SV_E_ARG, "too many rows");
+  const size_t need = sv_workspace_bytes(SV_OP_TREE_EXPAND, batch, rows, vocab);
+  if (sv_status s = check_workspace(workspace, workspace_bytes, need)) return s;
+  sv::TreeRoundArgs a{};
+  a.B = batch;
+  a.n_exp = n_exp;
+  a.top = top_children;
+  a.expand_next = expand_next;
+  a.max_cand = max_cand;
+  a.nseg = nseg;
+  a.first = exp_node == nullptr;
+  a.exp = exp_node;
+  a.keys = static_cast<uint64_t*>(workspace);
+  a.token = cand_token;
+  a.parent = cand_parent;
+  a.depth = cand_depth;
+  a.conf = cand_conf;
+  a.value = cand_value;
+  a.count = cand_count;
+  a.next = next_exp;
+  a.status = dev_status;
+  (void)hipGetLastError();
+  const hipError_t e = sv::launch_tree_expand(q_dtype, draft_rows, rows, vocab, a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SV_OK : device_fail(e, "sv_tree_expand");
+}
+
+sv_status sv_tree_finalize(int32_t batch, int32_t max_cand, const int32_t* cand_token,
+                           const int32_t* cand_parent, const int32_t* cand_depth, const float* cand_conf,
+                           const double* cand_value, const int32_t* cand_count, int32_t n_nodes,
+                           int32_t* out_parent, int32_t* out_token, int32_t* out_depth, int32_t* out_cand,
+                           uint8_t* out_mask, int32_t* dev_status, void* stream) {
+  if (batch < 0) return fail(SV_E_ARG, "batch < 0");
+  if (max_cand < 1 || max_cand > sv::kMaxTreeCand) return fail(SV_E_ARG, "max_cand must be in [1, 1024]");
+  if (n_nodes < 1 || n_nodes > sv::kMaxTreeNodes) return fail(SV_E_ARG, "n_nodes must be in [1, 1024]");
+  if (batch == 0) return SV_OK;
+  if (cand_token == nullptr || cand_parent == nullptr || cand_depth == nullptr || cand_conf == nullptr ||
+      cand_value == nullptr || cand_count == nullptr || out_parent == nullptr || out_token == nullptr ||
+      out_depth == nullptr || out_cand == nullptr)
+    return fail(SV_E_ARG, "null pointer argument");
+  sv::TreeFinalArgs a{};
+  a.B = batch;
+  a.max_cand = max_cand;
+  a.n_nodes = n_nodes;
+  a.token = cand_token;
+  a.parent = cand_parent;
+  a.depth = cand_depth;
+  a.conf = cand_conf;
+  a.value = cand_value;
+  a.count = cand_count;
+  a.out_parent = out_parent;
+  a.out_token = out_token;
+  a.out_depth = out_depth;
+  a.out_cand = out_cand;
+  a.out_mask = out_mask;
+  a.status = dev_status;
+  (void)hipGetLastError();
+  const hipError_t e = sv::launch_tree_finalize(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SV_OK : device_fail(e, "sv_tree_finalize");
 }
 
 }  // extern "C"

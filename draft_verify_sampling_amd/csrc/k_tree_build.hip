@@ -1,0 +1,483 @@
+// EAGLE-2 dynamic draft tree, built on the device.
+//
+// Method ("Speculative Decoding II", EAGLE-2 section, "Context-Aware Dynamic
+// Draft Tree", and its worked example): a node's value is the product of the
+// draft's confidences on its path (the root's is 1); each round expands the
+// best nodes of the newest layer by value, each proposing the top-k tokens of
+// the draft's distribution at that node; afterwards the whole tree is
+// reranked by value and the best nodes are kept (ties to the shallower node,
+// which keeps the kept set connected), then flattened breadth-first for the
+// target's one forward with each node seeing itself and its ancestors.
+//
+// Candidates of request b live in caller-owned arrays [B, max_cand] (index =
+// creation order, 0 = the root): token, parent, depth, confidence, value.
+//
+// k_topk_partial: one block per (row, segment) of the expanded nodes' draft
+//   rows; every thread keeps the K best (value, id) keys of its elements in
+//   registers (key = order-preserving bits of the clamped value << 32 | ~id,
+//   so one unsigned compare ranks larger values first and lower ids first
+//   among equals); the block then extracts its k best keys in k rounds of a
+//   block max.
+// k_tree_round: one block per request: merges each expanded row's segment
+//   keys into its k children, appends them (parent value times confidence,
+//   in fp64), and ranks the appended candidates for the next frontier.
+// k_tree_finalize: one block per request (one thread per candidate): rank by
+//   (-value, depth, creation order), keep the best, flatten depth by depth by
+//   (parent's flat index, -confidence, token, creation order), write the flat
+//   arrays and the ancestor mask.
+#include <algorithm>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace sv {
+
+namespace {
+
+// A stored draft probability as a confidence: clamped into [0, 1], NaN -> 0.
+__device__ __forceinline__ float conf_of(float p) {
+  return p == p ? fminf(fmaxf(p, 0.f), 1.f) : 0.f;
+}
+
+// Key of a confidence (non-negative, so its bits order like the value) and id.
+__device__ __forceinline__ uint64_t conf_key(float c, int64_t id) {
+  return (static_cast<uint64_t>(__float_as_uint(c) | 0x80000000u) << 32) |
+         static_cast<uint32_t>(~static_cast<uint32_t>(id));
+}
+
+__device__ __forceinline__ float key_conf(uint64_t k) {
+  return __uint_as_float(static_cast<uint32_t>(k >> 32) & 0x7fffffffu);
+}
+
+__device__ __forceinline__ int32_t key_id(uint64_t k) {
+  return static_cast<int32_t>(~static_cast<uint32_t>(k));
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t min_u64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, kWave);
+    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, kWave);
+    v = max_u64(v, (static_cast<uint64_t>(hi) << 32) | lo);
+  }
+  return v;
+}
+
+// Insert key into the descending list top[0..K) (the smallest falls off).
+template <int K>
+__device__ __forceinline__ void list_insert(uint64_t (&top)[K], uint64_t key) {
+  if (key <= top[K - 1]) return;
+  uint64_t x = key;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const uint64_t hi = max_u64(top[j], x);
+    x = min_u64(top[j], x);
+    top[j] = hi;
+  }
+}
+
+// Candidate order of the rerank and the frontier: larger value first, then
+// the shallower, then the earlier created.
+__device__ __forceinline__ bool cand_before(double va, int da, int ia, double vb, int db, int ib) {
+  if (va != vb) return va > vb;
+  if (da != db) return da < db;
+  return ia < ib;
+}
+
+}  // namespace
+
+// The k largest lane values of a wave, in rounds of a wave max (one copy of
+// the maximum leaves per round); returns the r-th largest in round r's lane
+// 0 through `emit(r, value)`.
+template <class Emit>
+__device__ __forceinline__ void wave_k_largest(float v, int k, Emit emit) {
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int r = 0; r < k; ++r) {
+    float w = v;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) w = fmaxf(w, __shfl_xor(w, off, kWave));
+    const uint64_t at = __ballot(v == w);
+    if (lane == __ffsll(static_cast<long long>(at)) - 1) v = -2.f;
+    emit(r, w);
+  }
+}
+
+// The k-th largest of one value per thread over the block (k <= 16; values
+// >= -1): each wave's k largest, then the k-th largest of those (kWaves * k
+// <= 64 values, one wave).  Valid in every thread.
+__device__ __forceinline__ float block_kth_largest(float m, int k, float* s_tk) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  constexpr int kWaves = kBlock / kWave;
+  static_assert(kWaves * kMaxTreeTop <= kWave, "one wave holds every wave's k largest");
+  wave_k_largest(m, k, [&](int r, float w) {
+    if (lane == 0) s_tk[wid * k + r] = w;
+  });
+  __syncthreads();
+  if (wid == 0) {
+    const float v = lane < kWaves * k ? s_tk[lane] : -2.f;
+    wave_k_largest(v, k, [&](int r, float w) {
+      if (lane == 0 && r == k - 1) s_tk[kWave] = w;
+    });
+  }
+  __syncthreads();
+  return s_tk[kWave];
+}
+
+template <class D, int K>
+__global__ __launch_bounds__(kBlock) void k_topk_partial(const void* __restrict__ rows, int64_t V, int32_t nseg,
+                                                         int32_t k, uint64_t* __restrict__ keys) {
+  __shared__ uint64_t s_w[kBlock / kWave];
+  __shared__ float s_tk[kWave + 1];
+  const int64_t row = blockIdx.x / nseg;
+  const int32_t seg = blockIdx.x - static_cast<int32_t>(row) * nseg;
+  const void* base = row_ptr<D>(rows, row, V);
+  const int64_t head = head_elems<D>(base, V);
+  const int64_t nvec = (V - head) / D::kPerVec;
+  const int64_t v0 = nvec * seg / nseg, v1 = nvec * (seg + 1) / nseg;
+  const uint4* vp = reinterpret_cast<const uint4*>(static_cast<const char*>(base) + head * D::kSize);
+
+  uint64_t top[K];
+#pragma unroll
+  for (int j = 0; j < K; ++j) top[j] = 0;  // below every real key
+  // Chunks of U vectors per thread, all loads in flight.  After the first
+  // chunk the block knows a threshold T: the k-th largest of its threads'
+  // maxima, so at least k of its elements are >= T and no element below T
+  // can be among its k best.  Only elements >= T form keys.
+  constexpr int U = 8;
+  const int64_t nchunk = (v1 - v0 + U * kBlock - 1) / (U * kBlock);
+  float T = -1.f;
+  for (int64_t ch = 0; ch < nchunk; ++ch) {
+    const int64_t v = v0 + ch * U * kBlock + threadIdx.x;
+    uint4 w[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int64_t vv = v + j * kBlock;
+      w[j] = vv < v1 ? vp[vv] : uint4{0u, 0u, 0u, 0u};
+    }
+    if (ch == 0) {
+      float m = -1.f;
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        if (v + j * kBlock >= v1) break;
+        float x[D::kPerVec];
+        D::unpack(w[j], x);
+#pragma unroll
+        for (int t = 0; t < D::kPerVec; ++t) m = fmaxf(m, conf_of(x[t]));
+      }
+      T = block_kth_largest(m, k, s_tk);
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int64_t vv = v + j * kBlock;
+      if (vv >= v1) break;
+      float x[D::kPerVec];
+      D::unpack(w[j], x);
+#pragma unroll
+      for (int t = 0; t < D::kPerVec; ++t) {
+        const float c = conf_of(x[t]);
+        if (c >= T) list_insert<K>(top, conf_key(c, head + vv * D::kPerVec + t));
+      }
+    }
+  }
+  if (seg == 0)
+    for (int64_t i = threadIdx.x; i < head; i += kBlock) list_insert<K>(top, conf_key(conf_of(D::at(base, i)), i));
+  if (seg == nseg - 1)
+    for (int64_t i = head + nvec * D::kPerVec + threadIdx.x; i < V; i += kBlock)
+      list_insert<K>(top, conf_key(conf_of(D::at(base, i)), i));
+
+  // the block's k best: k rounds of a block max over the threads' list heads
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  uint64_t* out = keys + static_cast<int64_t>(blockIdx.x) * k;
+  for (int r = 0; r < k; ++r) {
+    const uint64_t m = wave_max_u64(top[0]);
+    if (lane == 0) s_w[wid] = m;
+    __syncthreads();
+    uint64_t bm = s_w[0];
+    for (int w = 1; w < kBlock / kWave; ++w) bm = max_u64(bm, s_w[w]);
+    if (top[0] == bm && bm != 0) {  // keys are distinct: one owner
+#pragma unroll
+      for (int j = 0; j + 1 < K; ++j) top[j] = top[j + 1];
+      top[K - 1] = 0;
+    }
+    if (threadIdx.x == 0) out[r] = bm;
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void k_tree_round(TreeRoundArgs a) {
+  static_assert(kMaxTreeExpand <= kWave, "one wave checks the expanded nodes");
+  __shared__ int s_base, s_bad, s_nv;
+  __shared__ int s_node[kMaxTreeExpand], s_slot[kMaxTreeExpand];
+  __shared__ double s_v[kMaxTreeExpand * kMaxTreeTop];  // the appended candidates' values
+  __shared__ int s_d[kMaxTreeExpand * kMaxTreeTop];     // ... and depths
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wid = tid / kWave;
+  const int64_t c0 = static_cast<int64_t>(b) * a.max_cand;
+  const int k = a.top;
+
+  // the expanded nodes of this request, one lane each (the first round: the
+  // root, created here), checked against the request's candidate count
+  if (wid == 0) {
+    int cnt = a.first ? 1 : a.count[b];
+    const int n = lane >= a.n_exp ? -1 : (a.first ? (lane == 0 ? 0 : -1) : a.exp[static_cast<int64_t>(b) * a.n_exp + lane]);
+    if (a.first && lane == 0) {
+      a.token[c0] = -1;
+      a.parent[c0] = -1;
+      a.depth[c0] = 0;
+      a.conf[c0] = 1.f;
+      a.value[c0] = 1.0;
+    }
+    const bool cnt_ok = cnt >= 1 && cnt <= a.max_cand;
+    if (!cnt_ok) cnt = 0;
+    const bool valid = lane < a.n_exp && n >= 0 && n < cnt;
+    const bool wrong = lane < a.n_exp && (n >= cnt || n < -1);
+    const uint64_t vm = __ballot(valid);
+    const uint64_t wm = __ballot(wrong);
+    const int nv = __popcll(vm);
+    if (lane < a.n_exp) {
+      s_node[lane] = valid ? n : -1;
+      s_slot[lane] = __popcll(vm & ((1ull << lane) - 1));
+    }
+    if (lane == 0) {
+      int bad = (!cnt_ok || wm != 0) ? kFlagBadRequest : 0;
+      if (!bad && cnt + nv * k > a.max_cand) bad = kFlagBadRequest;  // no room: nothing appended
+      s_bad = bad;
+      s_base = cnt;
+      s_nv = nv;
+    }
+  }
+  __syncthreads();
+  const int bad = s_bad, base = s_base;
+  if (bad) {  // nothing appended; the next frontier is empty
+    for (int j = tid; j < a.expand_next; j += kBlock) a.next[static_cast<int64_t>(b) * a.expand_next + j] = -1;
+    if (tid == 0) {
+      a.count[b] = base;
+      flag(a.status, bad);
+    }
+    return;
+  }
+  // slot of expanded row e among the appended groups
+  // (rows with no node contribute no children; the order is the order given)
+  for (int e = wid; e < a.n_exp; e += kBlock / kWave) {
+    const int node = s_node[e];
+    if (node < 0) continue;
+    const int slot = s_slot[e];
+    const int64_t row = static_cast<int64_t>(b) * a.n_exp + e;
+    const uint64_t* keys = a.keys + row * a.nseg * k;
+    const int nk = a.nseg * k;  // <= 64 segments x 16 keys: 16 per lane
+    constexpr int kPerLane = 64 * kMaxTreeTop / kWave;
+    uint64_t kv[kPerLane];
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+      const int idx = lane + j * kWave;
+      kv[j] = idx < nk ? keys[idx] : 0;
+    }
+    const double pv = a.value[c0 + node];
+    const int pd = a.depth[c0 + node];
+    uint64_t thr = ~0ull;
+    for (int r = 0; r < k; ++r) {  // r-th best key of the row: the largest below the previous one
+      uint64_t m = 0;
+#pragma unroll
+      for (int j = 0; j < kPerLane; ++j) m = kv[j] < thr ? max_u64(m, kv[j]) : m;
+      m = wave_max_u64(m);
+      thr = m;
+      if (lane == 0) {
+        const int slot_r = slot * k + r;
+        const int64_t ci = c0 + base + slot_r;
+        const float c = key_conf(m);
+        const double v = pv * static_cast<double>(c);
+        a.token[ci] = key_id(m);
+        a.parent[ci] = node;
+        a.depth[ci] = pd + 1;
+        a.conf[ci] = c;
+        a.value[ci] = v;
+        s_v[slot_r] = v;
+        s_d[slot_r] = pd + 1;
+      }
+    }
+  }
+  __syncthreads();
+  const int n_app = s_nv * k;
+  // the next frontier: the best expand_next of the appended candidates
+  for (int i = tid; i < n_app; i += kBlock) {
+    const double vi = s_v[i];
+    const int di = s_d[i];
+    int rank = 0;
+#pragma unroll 8
+    for (int j = 0; j < n_app; ++j) rank += cand_before(s_v[j], s_d[j], j, vi, di, i) ? 1 : 0;
+    if (rank < a.expand_next) a.next[static_cast<int64_t>(b) * a.expand_next + rank] = base + i;
+  }
+  for (int j = n_app + tid; j < a.expand_next; j += kBlock) a.next[static_cast<int64_t>(b) * a.expand_next + j] = -1;
+  if (tid == 0) a.count[b] = base + n_app;
+}
+
+// Exclusive scan of one int per thread over a block of kMaxTreeCand threads
+// (wave scans, then the wave totals); valid in every thread.
+__device__ __forceinline__ int block_excl_scan(int v, int* s_tot) {
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int y = __shfl_up(x, off, kWave);
+    if (lane >= off) x += y;
+  }
+  if (lane == kWave - 1) s_tot[wid] = x;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wid; ++w) before += s_tot[w];
+  return before + x - v;
+}
+
+__global__ __launch_bounds__(kMaxTreeCand) void k_tree_finalize(TreeFinalArgs a) {
+  __shared__ double s_val[kMaxTreeCand];
+  __shared__ float s_conf[kMaxTreeCand];
+  __shared__ int s_dep[kMaxTreeCand], s_par[kMaxTreeCand], s_tok[kMaxTreeCand], s_flat[kMaxTreeCand];
+  __shared__ int s_of[kMaxTreeCand];    // candidate at each flat index
+  __shared__ int s_pf[kMaxTreeCand];    // parent's flat index, set while a depth is placed
+  __shared__ int s_list[kMaxTreeCand];  // kept candidates grouped by depth
+  __shared__ int s_dcnt[kMaxTreeCand];  // kept candidates per depth
+  __shared__ int s_doff[kMaxTreeCand];  // flat index of each depth's first node
+  __shared__ int s_wtot[kMaxTreeCand / kWave];
+  __shared__ int s_maxd;
+  const int b = blockIdx.x, i = threadIdx.x;
+  const int64_t c0 = static_cast<int64_t>(b) * a.max_cand;
+  const int M = a.count[b];
+  const int N = a.n_nodes;
+  const int64_t o = static_cast<int64_t>(b) * N;
+  if (M < 1 || M > a.max_cand) {
+    for (int f = i; f < N; f += kMaxTreeCand) {
+      a.out_parent[o + f] = a.out_token[o + f] = a.out_depth[o + f] = a.out_cand[o + f] = -1;
+    }
+    if (a.out_mask != nullptr)
+      for (int64_t x = i; x < static_cast<int64_t>(N) * N; x += kMaxTreeCand) a.out_mask[o * N + x] = 0;
+    if (i == 0) flag(a.status, kFlagBadRequest);
+    return;
+  }
+  if (i < M) {
+    s_val[i] = a.value[c0 + i];
+    s_conf[i] = a.conf[c0 + i];
+    s_dep[i] = a.depth[c0 + i];
+    s_par[i] = a.parent[c0 + i];
+    s_tok[i] = a.token[c0 + i];
+  }
+  s_dcnt[i] = 0;
+  if (i == 0) s_maxd = 0;
+  __syncthreads();
+  // kept: the root and the best N - 1 others by (-value, depth, creation
+  // order); the comparisons are branch-free so the loads pipeline
+  bool kept = i == 0;
+  if (i > 0 && i < M) {
+    const double vi = s_val[i];
+    const int di = s_dep[i];
+    int rank = 0;
+#pragma unroll 8
+    for (int j = 1; j < M; ++j) {
+      const double vj = s_val[j];
+      const int dj = s_dep[j];
+      rank += (vj > vi) | ((vj == vi) & ((dj < di) | ((dj == di) & (j < i))));
+    }
+    kept = rank < N - 1;
+  }
+  int slot = 0;
+  if (kept) {
+    slot = atomicAdd(&s_dcnt[s_dep[i]], 1);
+    atomicMax(&s_maxd, s_dep[i]);
+  }
+  __syncthreads();
+  const int maxd = s_maxd;
+  const int off = block_excl_scan(s_dcnt[i], s_wtot);  // depth i's first flat index
+  s_doff[i] = off;
+  __syncthreads();
+  if (kept) s_list[s_doff[s_dep[i]] + slot] = i;
+  if (i == 0) {
+    s_flat[0] = 0;
+    s_of[0] = 0;
+  }
+  __syncthreads();
+  // flatten depth by depth: within a depth by (parent's flat index,
+  // -confidence, token, creation order) among that depth's kept nodes
+  const bool placed = kept && i > 0;
+  for (int d = 1; d <= maxd; ++d) {
+    const bool mine = placed && s_dep[i] == d;
+    const int pf = mine ? s_flat[s_par[i]] : 0;
+    if (mine) s_pf[i] = pf;
+    __syncthreads();
+    if (mine) {
+      const int lo = s_doff[d], cnt = s_dcnt[d];
+      const float ci = s_conf[i];
+      const int ti = s_tok[i];
+      int r = 0;
+#pragma unroll 4
+      for (int q = 0; q < cnt; ++q) {
+        const int j = s_list[lo + q];
+        const int pj = s_pf[j];
+        const float cj = s_conf[j];
+        const int tj = s_tok[j];
+        r += (pj < pf) | ((pj == pf) & ((cj > ci) | ((cj == ci) & ((tj < ti) | ((tj == ti) & (j < i))))));
+      }
+      s_flat[i] = lo + r;
+      s_of[lo + r] = i;
+    }
+    __syncthreads();
+  }
+  const int n = M < N ? M : N;  // kept nodes
+  for (int f = i; f < N; f += kMaxTreeCand) {
+    if (f < n) {
+      const int ci = s_of[f];
+      a.out_parent[o + f] = ci == 0 ? -1 : s_flat[s_par[ci]];
+      a.out_token[o + f] = s_tok[ci];
+      a.out_depth[o + f] = s_dep[ci];
+      a.out_cand[o + f] = ci;
+    } else {
+      a.out_parent[o + f] = a.out_token[o + f] = a.out_depth[o + f] = a.out_cand[o + f] = -1;
+    }
+  }
+  if (a.out_mask != nullptr) {
+    // row f: ones at f and its ancestors
+    for (int f = i; f < N; f += kMaxTreeCand) {
+      uint8_t* row = a.out_mask + (o + f) * N;
+      for (int j = 0; j < N; ++j) row[j] = 0;
+      if (f < n) {
+        int g = f;
+        while (g >= 0) {
+          row[g] = 1;
+          const int cg = s_of[g];
+          g = cg == 0 ? -1 : s_flat[s_par[cg]];
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_tree_expand(int dtype, const void* rows, int64_t n_rows, int64_t V, const TreeRoundArgs& a,
+                              hipStream_t stream) {
+  const dim3 grid(static_cast<uint32_t>(n_rows * a.nseg));
+  const bool bf = dtype == kDtypeBF16;
+#define SV_TOPK(KK)                                                                                   \
+  if (bf) hipLaunchKernelGGL((k_topk_partial<BF16, KK>), grid, dim3(kBlock), 0, stream, rows, V, a.nseg, \
+                             a.top, a.keys);                                                          \
+  else hipLaunchKernelGGL((k_topk_partial<F32, KK>), grid, dim3(kBlock), 0, stream, rows, V, a.nseg,     \
+                          a.top, a.keys);
+  if (n_rows > 0) {
+    if (a.top <= 4) {
+      SV_TOPK(4)
+    } else if (a.top <= 8) {
+      SV_TOPK(8)
+    } else {
+      SV_TOPK(16)
+    }
+  }
+#undef SV_TOPK
+  hipLaunchKernelGGL(k_tree_round, dim3(static_cast<uint32_t>(a.B)), dim3(kBlock), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_finalize(const TreeFinalArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL(k_tree_finalize, dim3(static_cast<uint32_t>(a.B)), dim3(kMaxTreeCand), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace sv

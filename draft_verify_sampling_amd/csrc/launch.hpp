@@ -2,6 +2,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -210,6 +212,60 @@ hipError_t launch_row_stats(int dtype, const void* rows, int64_t n_rows, int64_t
 hipError_t launch_row_argmax(int dtype, const void* rows, int64_t n_rows, int64_t V, int32_t nseg,
                              uint64_t* keys, hipStream_t stream);
 hipError_t launch_greedy_resolve(const GreedyArgs& a, hipStream_t stream);
+// ---- EAGLE-2 draft tree on the device ----
+constexpr int kMaxTreeCand = 1024;   // candidates per request (one finalize thread each)
+constexpr int kMaxTreeExpand = 64;   // expanded nodes per request and round
+constexpr int kMaxTreeTop = 16;      // children per expanded node
+
+// Segments per row of the top-k pass: about 16 Ki elements per block, and at
+// least ~1024 blocks in total when rows are few (never below 2 Ki elements).
+inline int32_t tree_topk_segments(int64_t rows, int64_t V) {
+  int64_t nseg = (V + 16383) / 16384;
+  if (rows > 0 && rows * nseg < 1024) {
+    const int64_t want = (1024 + rows - 1) / rows;
+    const int64_t cap = (V + 2047) / 2048;
+    nseg = std::max<int64_t>(nseg, std::min(want, cap));
+  }
+  if (nseg < 1) nseg = 1;
+  if (nseg > 64) nseg = 64;
+  return static_cast<int32_t>(nseg);
+}
+
+struct TreeRoundArgs {
+  int32_t B, n_exp, top, expand_next, max_cand, nseg;
+  bool first;             // the roots' round: node 0 is created here and expanded
+  const int32_t* exp;     // [B, n_exp] candidates whose rows are given (-1: none)
+  uint64_t* keys;         // [B * n_exp, nseg, top] segment keys (workspace)
+  int32_t* token;         // candidates [B, max_cand] ...
+  int32_t* parent;
+  int32_t* depth;
+  float* conf;
+  double* value;
+  int32_t* count;         // [B]
+  int32_t* next;          // [B, expand_next]
+  int32_t* status;
+};
+
+struct TreeFinalArgs {
+  int32_t B, max_cand, n_nodes;
+  const int32_t* token;
+  const int32_t* parent;
+  const int32_t* depth;
+  const float* conf;
+  const double* value;
+  const int32_t* count;
+  int32_t* out_parent;    // [B, n_nodes] flat arrays
+  int32_t* out_token;
+  int32_t* out_depth;
+  int32_t* out_cand;
+  uint8_t* out_mask;      // [B, n_nodes, n_nodes] or null
+  int32_t* status;
+};
+
+hipError_t launch_tree_expand(int dtype, const void* rows, int64_t n_rows, int64_t V, const TreeRoundArgs& a,
+                              hipStream_t stream);
+hipError_t launch_tree_finalize(const TreeFinalArgs& a, hipStream_t stream);
+
 // Fill u [B, slots] with the Philox stream (seed, offset).
 hipError_t launch_philox_fill(uint64_t seed, uint64_t offset, int32_t B, int32_t slots, float* u,
                               hipStream_t stream);

@@ -29,6 +29,9 @@
  *                     candidates).
  *   sv_philox_uniforms, sv_verify_sample_philox  the verify's uniforms from a
  *                     counter-based generator on the device.
+ *   sv_tree_expand, sv_tree_finalize  the EAGLE-2 draft tree the tree verify
+ *                     takes, built on the device ("Speculative Decoding II",
+ *                     EAGLE-2 section).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -77,7 +80,7 @@ typedef enum {
 
 typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 
-typedef enum { SV_OP_GREEDY = 0, SV_OP_SAMPLE = 1, SV_OP_TREE = 2 } sv_op;
+typedef enum { SV_OP_GREEDY = 0, SV_OP_SAMPLE = 1, SV_OP_TREE = 2, SV_OP_TREE_EXPAND = 3 } sv_op;
 
 /* dev_status bits */
 #define SV_FLAG_BAD_REQUEST 1   /* draft count outside [0,k_max], row index out of range,
@@ -103,9 +106,10 @@ const char* sv_status_string(int status);
 /* Text of the last non-OK return on the calling thread ("" if none). */
 const char* sv_last_error(void);
 
-/* Workspace bytes for op (SV_OP_GREEDY / SV_OP_SAMPLE / SV_OP_TREE), for a call
- * with `batch` requests, `total_rows` target rows (greedy/sample: t_rows; tree:
- * batch * n_nodes) and `vocab` columns.  Host function.  0 on bad input. */
+/* Workspace bytes for op (SV_OP_GREEDY / SV_OP_SAMPLE / SV_OP_TREE /
+ * SV_OP_TREE_EXPAND), for a call with `batch` requests, `total_rows` rows
+ * (greedy/sample: t_rows; tree: batch * n_nodes; tree expand: batch * n_exp
+ * draft rows) and `vocab` columns.  Host function.  0 on bad input. */
 size_t sv_workspace_bytes(int op, int64_t batch, int64_t total_rows, int64_t vocab);
 
 /* Streaming first pass of sv_verify_sample and sv_verify_tree, exposed on its
@@ -284,6 +288,55 @@ sv_status sv_verify_tree_pointmass(const void* target_logits, int32_t t_dtype, i
                                    int32_t* out_count, int32_t* out_accepted, int32_t* out_path,
                                    int32_t* dev_status, void* workspace, size_t workspace_bytes,
                                    void* stream);
+
+/* EAGLE-2 dynamic draft tree, built on the device ("Speculative Decoding II",
+ * EAGLE-2 section "Context-Aware Dynamic Draft Tree" and its worked example).
+ * A request's candidates live in caller-owned arrays [batch, max_cand]
+ * (index = creation order; 0 = the root): cand_token, cand_parent (candidate
+ * index, -1 at the root), cand_depth (root 0), cand_conf (float: the draft's
+ * probability of the token at its parent), cand_value (double: the product
+ * of the confidences on the path, 1 at the root); cand_count [batch].
+ *
+ * sv_tree_expand: one round.  draft_rows [batch * n_exp, vocab] (q_dtype):
+ * row b * n_exp + e is the draft's distribution at candidate
+ * exp_node[b, e] (-1: none, that row is ignored).  exp_node == NULL is the
+ * first round: n_exp must be 1, the root of each request is created (count
+ * 1) and expanded with its row.  Each expanded node gets top_children
+ * children: the ids of its row with the largest probabilities (lower id
+ * first among equals; a value is clamped into [0, 1], NaN counts as 0),
+ * appended in the order given, best first, with value = parent value x
+ * confidence (fp64).  next_exp [batch, expand_next] receives the best
+ * candidates appended in this round by (-value, depth, creation order),
+ * best first, -1 padded: the nodes whose rows the next round expands.  A
+ * round that would exceed max_cand, or names a candidate that does not
+ * exist, appends nothing and sets SV_FLAG_BAD_REQUEST.
+ * Limits: 1 <= n_exp, expand_next <= 64; 1 <= top_children <= min(16, vocab);
+ * 1 <= max_cand <= 1024.  Workspace: SV_OP_TREE_EXPAND with
+ * total_rows = batch * n_exp.
+ *
+ * sv_tree_finalize: keep the root and the best n_nodes - 1 candidates by
+ * (-value, depth, creation order) (a value never exceeds its parent's and
+ * ties go to the shallower node, so the kept set is connected) and flatten
+ * them breadth-first, each depth ordered by (parent's flat index,
+ * -confidence, token, creation order).  Outputs [batch, n_nodes]: out_parent
+ * (flat index, -1 at the root), out_token (-1 at the root), out_depth (the
+ * position offset), out_cand (candidate index); with fewer candidates than
+ * n_nodes the tail is -1.  out_mask [batch, n_nodes, n_nodes] uint8 (NULL to
+ * skip): row i has 1 at i and at each ancestor of i, else 0.  The flat
+ * arrays feed sv_verify_tree (parent, token).  1 <= n_nodes <= 1024. */
+sv_status sv_tree_expand(const void* draft_rows, int32_t q_dtype, int64_t vocab, int32_t batch,
+                         int32_t n_exp, const int32_t* exp_node, int32_t top_children,
+                         int32_t expand_next, int32_t max_cand, int32_t* cand_token,
+                         int32_t* cand_parent, int32_t* cand_depth, float* cand_conf,
+                         double* cand_value, int32_t* cand_count, int32_t* next_exp,
+                         int32_t* dev_status, void* workspace, size_t workspace_bytes,
+                         void* stream);
+sv_status sv_tree_finalize(int32_t batch, int32_t max_cand, const int32_t* cand_token,
+                           const int32_t* cand_parent, const int32_t* cand_depth,
+                           const float* cand_conf, const double* cand_value,
+                           const int32_t* cand_count, int32_t n_nodes, int32_t* out_parent,
+                           int32_t* out_token, int32_t* out_depth, int32_t* out_cand,
+                           uint8_t* out_mask, int32_t* dev_status, void* stream);
 
 #ifdef __cplusplus
 }

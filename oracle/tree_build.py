@@ -15,7 +15,9 @@ position = depth.
 
 Readings where the page is silent (used identically by the kernels):
 * a node's children are the top-k ids of its draft row by stored probability,
-  lower id first among equals; a NaN probability counts as 0;
+  lower id first among equals; a stored value is clamped into [0, 1] and a
+  NaN counts as 0, so a value never exceeds its parent's and the kept set
+  is connected for any input;
 * values are float64 products, parent value times the child's confidence;
 * layer selection and the rerank order candidates by (-value, depth,
   creation order); creation order = the order candidates are appended
@@ -31,9 +33,10 @@ from .rows import widen
 
 def topk_children(row, kind, k):
     """The k ids of a stored draft row with the largest probabilities (lower id
-    first among equals; NaN counts as 0), with their confidences (float64)."""
+    first among equals; values clamped into [0, 1], NaN counts as 0), with
+    their confidences (float64)."""
     p = widen(row, kind)
-    p = np.where(np.isnan(p), 0.0, p)
+    p = np.clip(np.where(np.isnan(p), 0.0, p), 0.0, 1.0)
     order = np.lexsort((np.arange(p.shape[0]), -p))[:k]
     return [(int(i), float(p[i])) for i in order]
 

@@ -107,6 +107,30 @@ def test_host_checks_greedy_tree_ngram(lib):
     assert tp(d, 1, (1 << 22) + 1, d, d, 1, 60, 1.0, d, d, d, d, d, None, None, 0, None) == 1
     assert tp(d, 1, 100, d, d, 1, 1025, 1.0, d, d, d, d, d, None, None, 0, None) == 1
     assert tp(d, 1, 100, d, d, 1, 60, 1.0, d, d, d, d, d, None, None, 0, None) == 3
+    te = lib.sv_tree_expand
+    base = [d, 1, 100, 2, 4, d, 4, 4, 85, d, d, d, d, d, d, d, None, None, 0, None]
+
+    def expand(**kw):
+        a = list(base)
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return te(*a)
+
+    assert expand(a1=7) == 2                                  # dtype
+    assert expand(a4=0) == 1 and expand(a4=65) == 1           # n_exp
+    assert expand(a5=None) == 1                               # first round needs n_exp == 1
+    assert expand(a6=0) == 1 and expand(a6=17) == 1           # top_children
+    assert expand(a2=3) == 1                                  # vocab < top_children
+    assert expand(a7=0) == 1                                  # expand_next
+    assert expand(a8=1025) == 1                               # max_cand
+    assert expand(a9=None) == 1                               # null candidate array
+    assert expand() == 3                                      # no workspace
+    assert expand(a3=0) == 0                                  # nothing to do
+    tf = lib.sv_tree_finalize
+    assert tf(2, 85, d, d, d, d, d, d, 0, d, d, d, d, None, None, None) == 1
+    assert tf(2, 2000, d, d, d, d, d, d, 60, d, d, d, d, None, None, None) == 1
+    assert tf(2, 85, d, d, d, d, d, d, 60, None, d, d, d, None, None, None) == 1
+    assert tf(0, 85, d, d, d, d, d, d, 60, d, d, d, d, None, None, None) == 0
     n = lib.sv_ngram_draft
     assert n(d, d, 1, 16, 0, 4, d, d, None, None) == 1
     assert n(d, d, 1, 16, 65, 4, d, d, None, None) == 1

@@ -74,10 +74,10 @@ def test_topk_brute_force():
     rng = np.random.default_rng(4)
     for trial in range(200):
         V = int(rng.integers(1, 12))
-        p = rng.choice([0.0, 0.1, 0.25, 0.5, np.nan], size=V) if trial % 2 else rng.random(V)
+        p = rng.choice([0.0, 0.1, 0.25, 0.5, np.nan, -0.3, 1.0, 1.7], size=V) if trial % 2 else rng.random(V)
         k = int(rng.integers(1, V + 1))
         got = oracle.topk_children(p, "f64", k)
-        q = np.where(np.isnan(p), 0.0, p)
+        q = np.array([0.0 if v != v else min(max(v, 0.0), 1.0) for v in p])
         # id i is chosen iff fewer than k ids beat it (larger, or equal with a lower id)
         beaten = [sum(1 for j in range(V) if q[j] > q[i] or (q[j] == q[i] and j < i)) for i in range(V)]
         want = sorted((i for i in range(V) if beaten[i] < k), key=lambda i: beaten[i])
