@@ -56,14 +56,37 @@ __device__ __forceinline__ int32_t key_id(uint64_t k) {
 __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t min_u64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, kWave);
-    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, kWave);
-    v = max_u64(v, (static_cast<uint64_t>(hi) << 32) | lo);
-  }
-  return v;
+// Wave maxima through DPP row shifts and broadcasts (an inclusive max scan
+// whose last lane holds the wave's maximum), read back from lane 63.
+template <int ctrl, int row_mask>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v)), ctrl, row_mask, 0xf, false));
+  const uint32_t hi = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(static_cast<uint32_t>(v >> 32)), ctrl, row_mask, 0xf, false));
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {  // v >= 0 (0 is the identity)
+  v = max_u64(v, dpp_u64<0x111, 0xf>(v));  // row_shr:1
+  v = max_u64(v, dpp_u64<0x112, 0xf>(v));  // row_shr:2
+  v = max_u64(v, dpp_u64<0x114, 0xf>(v));  // row_shr:4
+  v = max_u64(v, dpp_u64<0x118, 0xf>(v));  // row_shr:8
+  v = max_u64(v, dpp_u64<0x142, 0xa>(v));  // row_bcast:15 into rows 1 and 3
+  v = max_u64(v, dpp_u64<0x143, 0xc>(v));  // row_bcast:31 into rows 2 and 3
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), kWave - 1);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), kWave - 1);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, dpp_f<0x111, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<0x112, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<0x114, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<0x118, 0xf>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<0x142, 0xa>(v, -INFINITY));
+  v = fmaxf(v, dpp_f<0x143, 0xc>(v, -INFINITY));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
 }
 
 // Insert key into the descending list top[0..K) (the smallest falls off).
@@ -96,9 +119,7 @@ template <class Emit>
 __device__ __forceinline__ void wave_k_largest(float v, int k, Emit emit) {
   const int lane = threadIdx.x & (kWave - 1);
   for (int r = 0; r < k; ++r) {
-    float w = v;
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) w = fmaxf(w, __shfl_xor(w, off, kWave));
+    const float w = wave_max_f32(v);
     const uint64_t at = __ballot(v == w);
     if (lane == __ffsll(static_cast<long long>(at)) - 1) v = -2.f;
     emit(r, w);
