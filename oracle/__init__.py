@@ -38,6 +38,8 @@ print, closed forms, or brute force):
 * ``chain.verify_sample(variant="resample_from_p")``  TV equal to the closed
                                  form 1/2 sum |min(p,q) - alpha p|.
 * ``chain.naive_round``         acceptance = sum p q.
+* ``chain.shard_pairs`` / ``combine_pairs``  the combined pairs of any column
+                                 split equal the full row's (M, S) (1e-12).
 * ``ngram.ngram_draft``         brute force over every window position on
                                  small contexts, hand cases.
 * ``tree.verify_tree``          chain-as-tree equals ``verify_sample``; exact
@@ -64,7 +66,8 @@ print, closed forms, or brute force):
 from .rows import widen, FLAG_BAD_REQUEST, FLAG_BAD_TOKEN, FLAG_NONFINITE, \
     FLAG_OVER_BUDGET, FLAG_FALLBACK, FLAG_BAD_TREE, INVALID_FLAGS
 from .chain import (verify_sample, verify_greedy, greedy_path_verify,
-                    forward_accounting, naive_round, softmax_T, inverse_cdf)
+                    forward_accounting, naive_round, softmax_T, inverse_cdf,
+                    shard_pairs, combine_pairs)
 from .ngram import ngram_draft
 from .tree import verify_tree, verify_tree_greedy, verify_tree_pointmass
 from .philox import philox4x64_10, philox_uniforms
@@ -72,7 +75,7 @@ from .tree_build import DraftTree, topk_children, build_tree
 
 __all__ = [
     "widen", "verify_sample", "verify_greedy", "greedy_path_verify",
-    "forward_accounting", "naive_round", "softmax_T", "inverse_cdf",
+    "forward_accounting", "naive_round", "softmax_T", "inverse_cdf", "shard_pairs", "combine_pairs",
     "ngram_draft", "verify_tree", "verify_tree_greedy", "verify_tree_pointmass",
     "philox4x64_10", "philox_uniforms", "DraftTree", "topk_children", "build_tree",
     "FLAG_BAD_REQUEST", "FLAG_BAD_TOKEN", "FLAG_NONFINITE", "FLAG_OVER_BUDGET",

@@ -303,3 +303,31 @@ def naive_round(p, q, u_draft, u_target):
     x = inverse_cdf(np.asarray(q, dtype=np.float64), u_draft)[0]
     y = inverse_cdf(np.asarray(p, dtype=np.float64), u_target)[0]
     return x == y, y
+
+
+def shard_pairs(l: np.ndarray, bounds, T: float):
+    """Softmax pairs of column shards of one row of logits l: for each shard
+    [bounds[g], bounds[g+1]), (m_g, s_g) = (max of l/T over the shard, sum
+    exp(l/T - m_g) over it).  A vocabulary-parallel LM head leaves each device
+    one shard; the full row's statistics follow from the pairs alone
+    (combine_pairs)."""
+    z = np.asarray(l, dtype=np.float64) / T
+    out = []
+    with np.errstate(invalid="ignore", over="ignore"):
+        for g in range(len(bounds) - 1):
+            seg = z[bounds[g]:bounds[g + 1]]
+            m = np.max(seg) if seg.size else -np.inf
+            s = np.sum(np.exp(seg - m)) if seg.size and np.isfinite(m) else 0.0
+            out.append((m, s))
+    return out
+
+
+def combine_pairs(pairs):
+    """(M, S) of the whole row from its shards' pairs: M = max m_g,
+    S = sum s_g exp(m_g - M) (the softmax normaliser of the figure
+    "一次目标前向验 k 个草稿 token", split over the vocabulary)."""
+    ms = [m for m, _ in pairs]
+    M = max(ms)
+    with np.errstate(invalid="ignore", over="ignore"):
+        S = sum(s * np.exp(m - M) for m, s in pairs if np.isfinite(m) or m == M)
+    return M, S
