@@ -184,7 +184,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c3p", "c4", "c5", "c5g", "c5p", "tb"])
+    ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c3p", "c3s", "c4", "c5", "c5g", "c5p", "tb"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--graph", action="store_true",
@@ -399,6 +399,58 @@ def main():
                       mean_tokens_per_round=round(float(out[1].float().mean().item()), 4),
                       visited_target_row_bytes=visited_bytes,
                       visited_GBps=round(visited_bytes / (ms * 1e-3) / 1e9, 1),
+                      event_ms_per_step=dict(timed_region=round(tot_ms / args.steps, 5),
+                                             p50=round(float(np.percentile(ev_ms, 50)), 5)),
+                      roofline=None)
+    elif W == "c3s":
+        # the headline round with the vocabulary split over 8 devices: one
+        # device's share (31,040 columns of every row) through the three shard
+        # steps; the exchanges between them (a few KB) are filled once
+        log("generating c3 inputs for the sharded verify")
+        ci = synth.c3_sampled()
+        G, V, B, k = 8, ci.V, ci.B, ci.k_max
+        bounds = [V * g // G for g in range(G + 1)]
+        trs, qrs = _i32(ci.t_row_start, torch, dev), _i32(ci.q_row_start, torch, dev)
+        ids, dl = _i32(ci.draft_ids[:, :k], torch, dev), _i32(ci.draft_len, torch, dev)
+        u = torch.from_numpy(ci.uniforms).to(dev)
+        cols = [(_rows(np.ascontiguousarray(ci.target[:, bounds[g]:bounds[g + 1]]), "bf16", torch, dev),
+                 _rows(np.ascontiguousarray(ci.draft[:, bounds[g]:bounds[g + 1]]), "bf16", torch, dev))
+                for g in range(G)]
+        wss = [sv.Workspace(dev) for _ in range(G)]
+        st1 = [sv.sv_shard_stats(cols[g][0], cols[g][1], bounds, g, trs, qrs, ids, dl, ci.T, workspace=wss[g])
+               for g in range(G)]
+        all_pairs = torch.stack([p for p, _ in st1])
+        all_at = torch.stack([a for _, a in st1])
+        mass = torch.zeros((G, B, 3), dtype=torch.float64, device=dev)
+        for g in range(G):
+            sv.sv_shard_residual(cols[g][0], cols[g][1], bounds, g, trs, qrs, ids, dl, ci.T, u, all_pairs, all_at,
+                                 mass, workspace=wss[g])
+        out = (torch.empty((B, k + 1), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev),
+               torch.empty((B,), dtype=torch.int32, device=dev), None)
+        for g in range(G):
+            sv.sv_shard_draw(cols[g][0], cols[g][1], bounds, g, trs, qrs, ids, dl, ci.T, u, all_pairs, mass, out,
+                             workspace=wss[g])
+        tg, qg = cols[0]
+        calls = [sv.prepare(sv.sv_shard_stats, tg, qg, bounds, 0, trs, qrs, ids, dl, ci.T, out=st1[0],
+                            workspace=wss[0])[0],
+                 sv.prepare(sv.sv_shard_residual, tg, qg, bounds, 0, trs, qrs, ids, dl, ci.T, u, all_pairs, all_at,
+                            mass, workspace=wss[0])[0],
+                 sv.prepare(sv.sv_shard_draw, tg, qg, bounds, 0, trs, qrs, ids, dl, ci.T, u, all_pairs, mass, out,
+                            workspace=wss[0])[0]]
+
+        def step(i):
+            for c in calls:
+                c()
+
+        wall, tot_ms, ev_ms = timed(step, args.steps, args.warmup, torch)
+        ms = 1e3 * wall / args.steps
+        share = (bounds[1] - bounds[0]) * 2 * (ci.target.shape[0] + ci.draft.shape[0])
+        result.update(value=round(B / (ms * 1e-3), 1), unit="rounds/s", ms_per_step=round(ms, 5),
+                      config=dict(workload="sampled chain verify on one of 8 vocabulary shards: 64 requests, k=4, "
+                                           "31,040 of V=248,320 columns per device, bf16, T=0.7 (the three shard "
+                                           "steps of one device; the all-gathers between them not included)",
+                                  batch=B, k=k, vocab=V, shards=G, inputs="bf16"),
+                      shard_bytes=share,
                       event_ms_per_step=dict(timed_region=round(tot_ms / args.steps, 5),
                                              p50=round(float(np.percentile(ev_ms, 50)), 5)),
                       roofline=None)

@@ -26,12 +26,13 @@ __all__ = [
     "FLAG_FALLBACK", "FLAG_BAD_TREE", "FLAG_SYNC_TIMEOUT", "EXPORTS",
     "sv_verify_tree_greedy", "sv_verify_tree_pointmass", "prepare", "prepare_verify_sample",
     "sv_philox_uniforms", "sv_verify_sample_philox", "DraftTreeState", "sv_tree_expand",
-    "sv_tree_finalize", "SV_OP_TREE_EXPAND",
+    "sv_tree_finalize", "SV_OP_TREE_EXPAND", "SV_OP_SHARD", "sv_shard_stats", "sv_shard_residual",
+    "sv_shard_draw",
     "prepare_softmax_partials",
 ]
 
 SV_F32, SV_BF16 = 0, 1
-SV_OP_GREEDY, SV_OP_SAMPLE, SV_OP_TREE, SV_OP_TREE_EXPAND = 0, 1, 2, 3
+SV_OP_GREEDY, SV_OP_SAMPLE, SV_OP_TREE, SV_OP_TREE_EXPAND, SV_OP_SHARD = 0, 1, 2, 3, 4
 FLAG_BAD_REQUEST, FLAG_BAD_TOKEN, FLAG_NONFINITE = 1, 2, 4
 FLAG_OVER_BUDGET, FLAG_FALLBACK, FLAG_BAD_TREE, FLAG_SYNC_TIMEOUT = 8, 16, 32, 64
 
@@ -39,7 +40,8 @@ EXPORTS = ("sv_abi_version", "sv_status_string", "sv_last_error", "sv_workspace_
            "sv_softmax_segments", "sv_softmax_partials",
            "sv_ngram_draft", "sv_verify_greedy", "sv_verify_sample", "sv_verify_tree",
            "sv_verify_tree_greedy", "sv_verify_tree_pointmass", "sv_philox_uniforms",
-           "sv_verify_sample_philox", "sv_tree_expand", "sv_tree_finalize")
+           "sv_verify_sample_philox", "sv_tree_expand", "sv_tree_finalize", "sv_shard_stats",
+           "sv_shard_residual", "sv_shard_draw")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -71,6 +73,12 @@ _SIGS = {
     "sv_tree_expand": (ctypes.c_int, [P, I32, I64, I32, I32, P, I32, I32, I32, P, P, P, P, P, P, P, P,
                                       P, SZ, P]),
     "sv_tree_finalize": (ctypes.c_int, [I32, I32, P, P, P, P, P, P, I32, P, P, P, P, P, P, P]),
+    "sv_shard_stats": (ctypes.c_int, [P, I32, I32, P, I32, I32, I64, P, I32, I32, P, P, P, P, I32, I32, F32,
+                                      P, P, P, SZ, P]),
+    "sv_shard_residual": (ctypes.c_int, [P, I32, I32, P, I32, I32, I64, P, I32, I32, P, P, P, P, I32, I32,
+                                         F32, P, P, P, P, P, SZ, P]),
+    "sv_shard_draw": (ctypes.c_int, [P, I32, I32, P, I32, I32, I64, P, I32, I32, P, P, P, P, I32, I32, F32,
+                                     P, P, P, P, I32, P, P, P, P, P, P, SZ, P]),
     "sv_verify_sample_philox": (ctypes.c_int, [P, I32, I32, P, I32, I32, I64, P, P, P, P, I32, I32,
                                                F32, U64, U64, P, I32, P, P, P, P, P, P, P, SZ, P]),
     "sv_verify_tree_pointmass": (ctypes.c_int, [P, I32, I64, P, P, I32, I32, F32, P, P, P, P, P,
@@ -563,3 +571,90 @@ def sv_tree_finalize(state: DraftTreeState, n_nodes: int, mask: bool = True,
             _dev(state.count, "count"), n_nodes, *(_dev(t, "out") for t in outs), _dev(m, "mask"),
             _dev(dev_status, "dev_status", torch.int32, dev), _stream(stream))
     return _invoke("sv_tree_finalize", args, (state, outs, m, dev_status), (*outs, m))
+
+
+def _shard_common(target_cols, draft_cols, bounds, shard, t_row_start, q_row_start, draft_ids, draft_len,
+                  temperature):
+    """Checked head of a shard step's argument list, the sizes, and the
+    host bounds array (kept alive by the argument tuple)."""
+    t_rows, width = target_cols.shape
+    q_rows = draft_cols.shape[0]
+    G = len(bounds) - 1
+    if not 0 <= shard < G or bounds[shard + 1] - bounds[shard] != width or draft_cols.shape[1] != width:
+        raise SpecVerifyError("target_cols / draft_cols must hold the shard's columns")
+    B = draft_len.shape[0]
+    k_max = draft_ids.shape[1] if draft_ids.dim() == 2 else 0
+    _shape(t_row_start, "t_row_start", (B,))
+    _shape(q_row_start, "q_row_start", (B,))
+    _shape(draft_ids, "draft_ids", (B, k_max))
+    dev = target_cols.device
+    hb = (ctypes.c_int64 * (G + 1))(*[int(v) for v in bounds])
+    head = (_dev(target_cols, "target_cols"), _dtype_code(target_cols), t_rows, _dev(draft_cols, "draft_cols"),
+            _dtype_code(draft_cols), q_rows, int(bounds[-1]), hb, G, shard,
+            _dev(t_row_start, "t_row_start", torch.int32, dev), _dev(q_row_start, "q_row_start", torch.int32, dev),
+            _dev(draft_ids, "draft_ids", torch.int32, dev), _dev(draft_len, "draft_len", torch.int32, dev),
+            B, k_max, float(temperature))
+    return head, B, k_max, t_rows, width, G, dev
+
+
+def sv_shard_stats(target_cols, draft_cols, bounds, shard, t_row_start, q_row_start, draft_ids, draft_len,
+                   temperature, out=None, workspace: Optional[Workspace] = None, stream=None):
+    """Step 1 of the sharded verify: (pairs [t_rows, 2], at [B, k_max, 2]) of
+    this shard (see include/specverify.h)."""
+    head, B, k_max, t_rows, width, G, dev = _shard_common(target_cols, draft_cols, bounds, shard, t_row_start,
+                                                          q_row_start, draft_ids, draft_len, temperature)
+    if out is None:
+        pairs = torch.empty((t_rows, 2), dtype=torch.float32, device=dev)
+        at = torch.zeros((B, max(k_max, 1), 2), dtype=torch.float32, device=dev)
+    else:
+        pairs, at = out
+        _shape(pairs, "pairs", (t_rows, 2), torch.float32)
+        _shape(at, "at", (B, max(k_max, 1), 2), torch.float32)
+    ws = _workspace(workspace, dev, stream, workspace_bytes(SV_OP_SHARD, B, t_rows, width))
+    args = head + (_dev(pairs, "pairs"), _dev(at, "at"), ws.data_ptr(), ws.numel(), _stream(stream))
+    return _invoke("sv_shard_stats", args, (target_cols, draft_cols, t_row_start, q_row_start, draft_ids,
+                                            draft_len, pairs, at, ws), (pairs, at))
+
+
+def sv_shard_residual(target_cols, draft_cols, bounds, shard, t_row_start, q_row_start, draft_ids, draft_len,
+                      temperature, uniforms, all_pairs, all_at, mass, workspace: Workspace, stream=None):
+    """Step 2: writes this shard's row of mass [G, B, 3] (float64)."""
+    head, B, k_max, t_rows, width, G, dev = _shard_common(target_cols, draft_cols, bounds, shard, t_row_start,
+                                                          q_row_start, draft_ids, draft_len, temperature)
+    _shape(uniforms, "uniforms", (B, k_max + 1), torch.float32)
+    _shape(all_pairs, "all_pairs", (G, t_rows, 2), torch.float32)
+    _shape(all_at, "all_at", (G, B, max(k_max, 1), 2), torch.float32)
+    _shape(mass, "mass", (G, B, 3), torch.float64)
+    ws = _workspace(workspace, dev, stream, workspace_bytes(SV_OP_SHARD, B, t_rows, width))
+    args = head + (_dev(uniforms, "uniforms"), _dev(all_pairs, "all_pairs"), _dev(all_at, "all_at"),
+                   _dev(mass, "mass"), ws.data_ptr(), ws.numel(), _stream(stream))
+    return _invoke("sv_shard_residual", args, (target_cols, draft_cols, t_row_start, q_row_start, draft_ids,
+                                               draft_len, uniforms, all_pairs, all_at, mass, ws), mass)
+
+
+def sv_shard_draw(target_cols, draft_cols, bounds, shard, t_row_start, q_row_start, draft_ids, draft_len,
+                  temperature, uniforms, all_pairs, mass, out, max_new: Optional[torch.Tensor] = None,
+                  eos_id: int = -1, dev_status: Optional[torch.Tensor] = None,
+                  workspace: Optional[Workspace] = None, stream=None):
+    """Step 3: the shard holding the draw writes request b's outputs into
+    out = (tokens [B, k_max+1], count [B], accepted [B], resid [B] or None)."""
+    head, B, k_max, t_rows, width, G, dev = _shard_common(target_cols, draft_cols, bounds, shard, t_row_start,
+                                                          q_row_start, draft_ids, draft_len, temperature)
+    tok, cnt, acc, rs = out
+    _shape(tok, "out tokens", (B, k_max + 1), torch.int32)
+    _shape(cnt, "out count", (B,), torch.int32)
+    _shape(acc, "out accepted", (B,), torch.int32)
+    _shape(rs, "out resid", (B,), torch.float32)
+    _shape(max_new, "max_new", (B,))
+    _status_arg(dev_status)
+    _shape(uniforms, "uniforms", (B, k_max + 1), torch.float32)
+    _shape(all_pairs, "all_pairs", (G, t_rows, 2), torch.float32)
+    _shape(mass, "mass", (G, B, 3), torch.float64)
+    ws = _workspace(workspace, dev, stream, workspace_bytes(SV_OP_SHARD, B, t_rows, width))
+    args = head + (_dev(uniforms, "uniforms"), _dev(all_pairs, "all_pairs"), _dev(mass, "mass"),
+                   _dev(max_new, "max_new", torch.int32, dev), eos_id, _dev(tok, "out"), _dev(cnt, "cnt"),
+                   _dev(acc, "acc"), _dev(rs, "resid"), _dev(dev_status, "dev_status", torch.int32, dev),
+                   ws.data_ptr(), ws.numel(), _stream(stream))
+    return _invoke("sv_shard_draw", args, (target_cols, draft_cols, t_row_start, q_row_start, draft_ids,
+                                           draft_len, uniforms, all_pairs, mass, out, max_new, dev_status, ws),
+                   out)

@@ -169,6 +169,12 @@ size_t sv_workspace_bytes(int op, int64_t batch, int64_t total_rows, int64_t voc
     case SV_OP_TREE_EXPAND:  // total_rows = batch * expanded nodes per request
       return sv::align256(static_cast<size_t>(total_rows * sv::tree_topk_segments(total_rows, vocab)) *
                           sv::kMaxTreeTop * 8);
+    case SV_OP_SHARD: {  // total_rows = t_rows, vocab = the shard's column count
+      const size_t partials = static_cast<size_t>(total_rows * sv::row_segments(total_rows, vocab)) * 8;
+      const size_t state = sv::align256(static_cast<size_t>(batch) * 16);
+      const size_t tiles = static_cast<size_t>(batch * sv::sample_tiles(vocab)) * 16;
+      return sv::align256(std::max(partials, state + tiles));
+    }
     case SV_OP_SAMPLE: {
       // a request has at most min(t_rows, 256) rows
       const int64_t R = std::min<int64_t>(total_rows, sv::kMaxChainRows);
@@ -560,6 +566,142 @@ sv_status sv_tree_finalize(int32_t batch, int32_t max_cand, const int32_t* cand_
   (void)hipGetLastError();
   const hipError_t e = sv::launch_tree_finalize(a, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SV_OK : device_fail(e, "sv_tree_finalize");
+}
+
+// ---- vocabulary shards ----
+
+// Checks shared by the three shard steps; fills the common fields of a.
+static sv_status shard_setup(const void* target_cols, int32_t t_dtype, int32_t t_rows, const void* draft_cols,
+                             int32_t q_dtype, int32_t q_rows, int64_t vocab, const int64_t* bounds,
+                             int32_t n_shards, int32_t shard, const int32_t* t_row_start,
+                             const int32_t* q_row_start, const int32_t* draft_ids, const int32_t* draft_len,
+                             int32_t batch, int32_t k_max, float temperature, void* workspace,
+                             size_t workspace_bytes, sv::ShardArgs& a) {
+  if (!dtype_ok(t_dtype) || !dtype_ok(q_dtype))
+    return fail(SV_E_DTYPE, "t_dtype and q_dtype must be SV_F32 or SV_BF16");
+  if (batch < 0) return fail(SV_E_ARG, "batch < 0");
+  if (k_max < 0 || k_max >= sv::kMaxChainRows) return fail(SV_E_ARG, "k_max must be in [0, 255]");
+  if (t_rows < 1 || q_rows < 0) return fail(SV_E_ARG, "t_rows must be >= 1 and q_rows >= 0");
+  if (!(temperature > 0.f) || !std::isfinite(temperature))
+    return fail(SV_E_ARG, "temperature must be finite and > 0");
+  if (bounds == nullptr || n_shards < 1 || n_shards > sv::kMaxShards)
+    return fail(SV_E_ARG, "bounds (host) with 1 <= n_shards <= 64 are needed");
+  if (shard < 0 || shard >= n_shards) return fail(SV_E_ARG, "shard must be in [0, n_shards)");
+  if (bounds[0] != 0 || bounds[n_shards] != vocab) return fail(SV_E_ARG, "bounds must run from 0 to vocab");
+  for (int g = 0; g < n_shards; ++g)
+    if (bounds[g + 1] <= bounds[g]) return fail(SV_E_ARG, "bounds must increase");
+  const int64_t width = bounds[shard + 1] - bounds[shard];
+  if (vocab > INT32_MAX || width > sv::kMaxSampleVocab)
+    return fail(SV_E_ARG, "a shard holds at most 4194304 columns");
+  if (batch > 0 && (target_cols == nullptr || t_row_start == nullptr || q_row_start == nullptr ||
+                    draft_len == nullptr || (k_max > 0 && draft_ids == nullptr) ||
+                    (q_rows > 0 && draft_cols == nullptr)))
+    return fail(SV_E_ARG, "null pointer argument");
+  if (static_cast<int64_t>(t_rows) * sv::row_segments(t_rows, width) > kMaxGrid)
+    return fail(SV_E_ARG, "too many rows");
+  const size_t need = sv_workspace_bytes(SV_OP_SHARD, batch, t_rows, width);
+  if (batch > 0)
+    if (sv_status st = check_workspace(workspace, workspace_bytes, need)) return st;
+  a.tgt = target_cols;
+  a.dq = draft_cols;
+  a.V = vocab;
+  a.c = sv::kLog2e / temperature;
+  a.B = batch;
+  a.k_max = k_max;
+  a.t_rows = t_rows;
+  a.q_rows = q_rows;
+  a.t_rs = t_row_start;
+  a.q_rs = q_row_start;
+  a.ids = draft_ids;
+  a.dlen = draft_len;
+  a.shard = shard;
+  a.sb.G = n_shards;
+  for (int g = 0; g <= n_shards; ++g) a.sb.b[g] = bounds[g];
+  a.tile_cap = static_cast<int32_t>(sv::sample_tiles(width));
+  char* ws = static_cast<char*>(workspace);
+  a.state = reinterpret_cast<int64_t*>(ws);
+  a.tiles = reinterpret_cast<double*>(ws + sv::align256(static_cast<size_t>(batch) * 16));
+  return SV_OK;
+}
+
+sv_status sv_shard_stats(const void* target_cols, int32_t t_dtype, int32_t t_rows, const void* draft_cols,
+                         int32_t q_dtype, int32_t q_rows, int64_t vocab, const int64_t* bounds,
+                         int32_t n_shards, int32_t shard, const int32_t* t_row_start,
+                         const int32_t* q_row_start, const int32_t* draft_ids, const int32_t* draft_len,
+                         int32_t batch, int32_t k_max, float temperature, float* out_pairs, float* out_at,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  sv::ShardArgs a{};
+  if (sv_status st = shard_setup(target_cols, t_dtype, t_rows, draft_cols, q_dtype, q_rows, vocab, bounds,
+                                 n_shards, shard, t_row_start, q_row_start, draft_ids, draft_len, batch, k_max,
+                                 temperature, workspace, workspace_bytes, a))
+    return st;
+  if (batch == 0) return SV_OK;
+  if (out_pairs == nullptr || (k_max > 0 && out_at == nullptr)) return fail(SV_E_ARG, "null pointer argument");
+  const int64_t width = bounds[shard + 1] - bounds[shard];
+  const int32_t nseg = sv::row_segments(t_rows, width);
+  float2* partial = static_cast<float2*>(workspace);
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  hipError_t e = sv::launch_row_stats(t_dtype, target_cols, t_rows, width, nseg, a.c, partial, st);
+  if (e == hipSuccess) e = sv::launch_shard_fold(partial, t_rows, nseg, out_pairs, st);
+  if (e == hipSuccess) e = sv::launch_shard_step(1, t_dtype, q_dtype, a, out_at, st);
+  return e == hipSuccess ? SV_OK : device_fail(e, "sv_shard_stats");
+}
+
+sv_status sv_shard_residual(const void* target_cols, int32_t t_dtype, int32_t t_rows, const void* draft_cols,
+                            int32_t q_dtype, int32_t q_rows, int64_t vocab, const int64_t* bounds,
+                            int32_t n_shards, int32_t shard, const int32_t* t_row_start,
+                            const int32_t* q_row_start, const int32_t* draft_ids, const int32_t* draft_len,
+                            int32_t batch, int32_t k_max, float temperature, const float* uniforms,
+                            const float* all_pairs, const float* all_at, double* mass, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  sv::ShardArgs a{};
+  if (sv_status st = shard_setup(target_cols, t_dtype, t_rows, draft_cols, q_dtype, q_rows, vocab, bounds,
+                                 n_shards, shard, t_row_start, q_row_start, draft_ids, draft_len, batch, k_max,
+                                 temperature, workspace, workspace_bytes, a))
+    return st;
+  if (batch == 0) return SV_OK;
+  if (uniforms == nullptr || all_pairs == nullptr || (k_max > 0 && all_at == nullptr) || mass == nullptr)
+    return fail(SV_E_ARG, "null pointer argument");
+  a.u = uniforms;
+  a.pairs = all_pairs;
+  a.at = all_at;
+  a.mass = mass;
+  (void)hipGetLastError();
+  const hipError_t e = sv::launch_shard_step(2, t_dtype, q_dtype, a, nullptr, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SV_OK : device_fail(e, "sv_shard_residual");
+}
+
+sv_status sv_shard_draw(const void* target_cols, int32_t t_dtype, int32_t t_rows, const void* draft_cols,
+                        int32_t q_dtype, int32_t q_rows, int64_t vocab, const int64_t* bounds, int32_t n_shards,
+                        int32_t shard, const int32_t* t_row_start, const int32_t* q_row_start,
+                        const int32_t* draft_ids, const int32_t* draft_len, int32_t batch, int32_t k_max,
+                        float temperature, const float* uniforms, const float* all_pairs, const double* mass,
+                        const int32_t* max_new, int32_t eos_id, int32_t* out_tokens, int32_t* out_count,
+                        int32_t* out_accepted, float* out_resid, int32_t* dev_status, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  sv::ShardArgs a{};
+  if (sv_status st = shard_setup(target_cols, t_dtype, t_rows, draft_cols, q_dtype, q_rows, vocab, bounds,
+                                 n_shards, shard, t_row_start, q_row_start, draft_ids, draft_len, batch, k_max,
+                                 temperature, workspace, workspace_bytes, a))
+    return st;
+  if (batch == 0) return SV_OK;
+  if (uniforms == nullptr || all_pairs == nullptr || mass == nullptr || out_tokens == nullptr ||
+      out_count == nullptr || out_accepted == nullptr)
+    return fail(SV_E_ARG, "null pointer argument");
+  a.u = uniforms;
+  a.pairs = all_pairs;
+  a.mass = const_cast<double*>(mass);
+  a.max_new = max_new;
+  a.eos = eos_id;
+  a.out_tok = out_tokens;
+  a.out_cnt = out_count;
+  a.out_acc = out_accepted;
+  a.resid = out_resid;
+  a.status = dev_status;
+  (void)hipGetLastError();
+  const hipError_t e = sv::launch_shard_step(3, t_dtype, q_dtype, a, nullptr, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SV_OK : device_fail(e, "sv_shard_draw");
 }
 
 }  // extern "C"

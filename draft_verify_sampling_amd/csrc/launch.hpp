@@ -266,6 +266,48 @@ hipError_t launch_tree_expand(int dtype, const void* rows, int64_t n_rows, int64
                               hipStream_t stream);
 hipError_t launch_tree_finalize(const TreeFinalArgs& a, hipStream_t stream);
 
+// ---- vocabulary shards ----
+constexpr int kMaxShards = 64;
+
+struct ShardBounds {
+  int32_t G;                      // shards
+  int64_t b[kMaxShards + 1];      // shard g holds columns [b[g], b[g+1])
+};
+
+struct ShardArgs {
+  const void* tgt;                // this shard's columns of the target rows [t_rows, width]
+  const void* dq;                 // ... and of the draft rows [q_rows, width]
+  int64_t V;                      // the whole vocabulary
+  float c;                        // log2(e) / T
+  int32_t B, k_max, t_rows, q_rows;
+  const int32_t* t_rs;
+  const int32_t* q_rs;
+  const int32_t* ids;
+  const int32_t* dlen;
+  const float* u;                 // [B, k_max + 1], or null: Philox stream (seed, offset)
+  uint64_t seed, offset;
+  const int32_t* max_new;
+  int32_t eos;
+  int32_t shard;
+  ShardBounds sb;
+  const float* pairs;             // [G, t_rows, 2] every shard's pairs
+  const float* at;                // [G, B, k_max, 2] every shard's gathered (logit, q)
+  int64_t* state;                 // [B, 2] this shard's decision (m or -1, status bits)
+  double* mass;                   // [G, B, 3] every shard's (residual, p, q) sums
+  double* tiles;                  // [B, tile_cap, 2] this shard's tile sums
+  int32_t tile_cap;
+  int32_t* out_tok;
+  int32_t* out_cnt;
+  int32_t* out_acc;
+  float* resid;
+  int32_t* status;
+};
+
+hipError_t launch_shard_fold(const float2* partial, int64_t rows, int32_t nseg, float* pairs, hipStream_t stream);
+// step 1: gather the drafted tokens' values (at); step 2: decisions and this
+// shard's weight sums; step 3: the draw and the outputs.
+hipError_t launch_shard_step(int step, int t_dtype, int q_dtype, const ShardArgs& a, float* at, hipStream_t stream);
+
 // Fill u [B, slots] with the Philox stream (seed, offset).
 hipError_t launch_philox_fill(uint64_t seed, uint64_t offset, int32_t B, int32_t slots, float* u,
                               hipStream_t stream);

@@ -32,6 +32,8 @@
  *   sv_tree_expand, sv_tree_finalize  the EAGLE-2 draft tree the tree verify
  *                     takes, built on the device ("Speculative Decoding II",
  *                     EAGLE-2 section).
+ *   sv_shard_stats, sv_shard_residual, sv_shard_draw  the sampled chain verify
+ *                     on one device's column shard of the vocabulary.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -80,7 +82,13 @@ typedef enum {
 
 typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
 
-typedef enum { SV_OP_GREEDY = 0, SV_OP_SAMPLE = 1, SV_OP_TREE = 2, SV_OP_TREE_EXPAND = 3 } sv_op;
+typedef enum {
+  SV_OP_GREEDY = 0,
+  SV_OP_SAMPLE = 1,
+  SV_OP_TREE = 2,
+  SV_OP_TREE_EXPAND = 3,
+  SV_OP_SHARD = 4
+} sv_op;
 
 /* dev_status bits */
 #define SV_FLAG_BAD_REQUEST 1   /* draft count outside [0,k_max], row index out of range,
@@ -107,9 +115,10 @@ const char* sv_status_string(int status);
 const char* sv_last_error(void);
 
 /* Workspace bytes for op (SV_OP_GREEDY / SV_OP_SAMPLE / SV_OP_TREE /
- * SV_OP_TREE_EXPAND), for a call with `batch` requests, `total_rows` rows
- * (greedy/sample: t_rows; tree: batch * n_nodes; tree expand: batch * n_exp
- * draft rows) and `vocab` columns.  Host function.  0 on bad input. */
+ * SV_OP_TREE_EXPAND / SV_OP_SHARD), for a call with `batch` requests,
+ * `total_rows` rows (greedy/sample/shard: t_rows; tree: batch * n_nodes;
+ * tree expand: batch * n_exp draft rows) and `vocab` columns (shard: the
+ * shard's column count).  Host function.  0 on bad input. */
 size_t sv_workspace_bytes(int op, int64_t batch, int64_t total_rows, int64_t vocab);
 
 /* Streaming first pass of sv_verify_sample and sv_verify_tree, exposed on its
@@ -337,6 +346,67 @@ sv_status sv_tree_finalize(int32_t batch, int32_t max_cand, const int32_t* cand_
                            const int32_t* cand_count, int32_t n_nodes, int32_t* out_parent,
                            int32_t* out_token, int32_t* out_depth, int32_t* out_cand,
                            uint8_t* out_mask, int32_t* dev_status, void* stream);
+
+/* Sampled chain verify over a vocabulary split into column shards, as a
+ * vocabulary-parallel LM head leaves the logits: device g holds columns
+ * [bounds[g], bounds[g+1]) of every target and draft row ("投机解码:为什么一个字
+ * 都不改", sections "改进" and "一轮能出几个 token"; the softmax of the figure
+ * "一次目标前向验 k 个草稿 token" spans the whole vocabulary, so its max and
+ * normaliser are combined from the shards' pairs).  The result is the
+ * sv_verify_sample round; only the data movement differs.
+ *
+ * Common arguments: target_cols [t_rows, width] and draft_cols [q_rows, width]
+ * are this shard's columns (width = bounds[shard+1] - bounds[shard]); bounds
+ * is a HOST array of n_shards + 1 column offsets, 0 = bounds[0] < ... <
+ * bounds[n_shards] = vocab, 1 <= n_shards <= 64; row starts, drafts, batch,
+ * k_max, temperature as for sv_verify_sample.  Workspace: SV_OP_SHARD with
+ * total_rows = t_rows and vocab = width; the same workspace must serve one
+ * shard's three steps of a round.
+ *
+ * Step 1, sv_shard_stats: out_pairs [t_rows, 2] float = the shard's
+ * scaled-domain softmax pair of every target row (m = max over its columns
+ * of l log2(e)/T, s = sum 2^(l log2(e)/T - m)); out_at [batch, k_max, 2] =
+ * (target logit, draft probability) at each drafted token the shard holds
+ * (other entries are not written).
+ * Exchange: all_pairs [n_shards, t_rows, 2] and all_at [n_shards, batch,
+ * k_max, 2] hold every shard's step-1 outputs (an all-gather).
+ * Step 2, sv_shard_residual: every shard takes the same decisions (rows'
+ * pairs combined in shard order, p(x_i) from the shard holding x_i, the
+ * accept scan with uniforms [batch, k_max+1]) and writes its row of
+ * mass [n_shards, batch, 3] = (sum of max(0, p_m - q_m) over its columns, or
+ * of p_k after a full accept; sum of p; sum of q) in float64.
+ * Exchange: every shard's row of mass (an all-gather).
+ * Step 3, sv_shard_draw: the shard whose columns hold u[b, k_b] times the
+ * total (shard order) draws the token and writes request b's outputs
+ * (tokens [batch, k_max+1], count, accepted, optional resid, status bits);
+ * shard 0 writes the outputs of invalid requests; other shards write nothing
+ * for b.  Status bits and invalid requests as for sv_verify_sample. */
+sv_status sv_shard_stats(const void* target_cols, int32_t t_dtype, int32_t t_rows,
+                         const void* draft_cols, int32_t q_dtype, int32_t q_rows, int64_t vocab,
+                         const int64_t* bounds, int32_t n_shards, int32_t shard,
+                         const int32_t* t_row_start, const int32_t* q_row_start,
+                         const int32_t* draft_ids, const int32_t* draft_len, int32_t batch,
+                         int32_t k_max, float temperature, float* out_pairs, float* out_at,
+                         void* workspace, size_t workspace_bytes, void* stream);
+sv_status sv_shard_residual(const void* target_cols, int32_t t_dtype, int32_t t_rows,
+                            const void* draft_cols, int32_t q_dtype, int32_t q_rows,
+                            int64_t vocab, const int64_t* bounds, int32_t n_shards,
+                            int32_t shard, const int32_t* t_row_start,
+                            const int32_t* q_row_start, const int32_t* draft_ids,
+                            const int32_t* draft_len, int32_t batch, int32_t k_max,
+                            float temperature, const float* uniforms, const float* all_pairs,
+                            const float* all_at, double* mass, void* workspace,
+                            size_t workspace_bytes, void* stream);
+sv_status sv_shard_draw(const void* target_cols, int32_t t_dtype, int32_t t_rows,
+                        const void* draft_cols, int32_t q_dtype, int32_t q_rows, int64_t vocab,
+                        const int64_t* bounds, int32_t n_shards, int32_t shard,
+                        const int32_t* t_row_start, const int32_t* q_row_start,
+                        const int32_t* draft_ids, const int32_t* draft_len, int32_t batch,
+                        int32_t k_max, float temperature, const float* uniforms,
+                        const float* all_pairs, const double* mass, const int32_t* max_new,
+                        int32_t eos_id, int32_t* out_tokens, int32_t* out_count,
+                        int32_t* out_accepted, float* out_resid, int32_t* dev_status,
+                        void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -131,6 +131,26 @@ def test_host_checks_greedy_tree_ngram(lib):
     assert tf(2, 2000, d, d, d, d, d, d, 60, d, d, d, d, None, None, None) == 1
     assert tf(2, 85, d, d, d, d, d, d, 60, None, d, d, d, None, None, None) == 1
     assert tf(0, 85, d, d, d, d, d, d, 60, d, d, d, d, None, None, None) == 0
+    ss = lib.sv_shard_stats
+    hb = (ctypes.c_int64 * 3)(0, 40, 100)
+
+    def stats(**kw):
+        a = [d, 1, 5, d, 1, 4, 100, hb, 2, 0, d, d, d, d, 1, 4, 1.0, d, d, d, 1 << 20, None]
+        for i, v in kw.items():
+            a[int(i[1:])] = v
+        return ss(*a)
+
+    assert stats(a1=9) == 2
+    assert stats(a8=0) == 1 and stats(a8=65) == 1           # shard count
+    assert stats(a9=2) == 1 and stats(a9=-1) == 1            # shard index
+    assert stats(a6=99) == 1                                 # bounds must end at vocab
+    assert stats(a7=None) == 1                               # bounds are required
+    bad = (ctypes.c_int64 * 3)(0, 100, 100)
+    assert stats(a7=bad) == 1                                # bounds must increase
+    assert stats(a16=0.0) == 1
+    assert stats(a15=256) == 1
+    assert stats(a18=None, a19=None, a20=0) == 3             # workspace
+    assert stats(a14=0) == 0
     n = lib.sv_ngram_draft
     assert n(d, d, 1, 16, 0, 4, d, d, None, None) == 1
     assert n(d, d, 1, 16, 65, 4, d, d, None, None) == 1
