@@ -28,7 +28,18 @@ sys.path.insert(0, ROOT)
 METRIC = "verified rounds/s + achieved HBM GB/s (% peak), B=64 k=4 V=248,320 bf16"
 PEAK_HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "row_stats_c3_traffic.json")
-STATS_SRC = os.path.join(ROOT, "draft_verify_sampling_amd", "csrc", "k_stats.hip")
+# the sources the row-statistics kernel is compiled from (its counter summary
+# holds while their hash is unchanged)
+STATS_SRCS = [os.path.join(ROOT, "draft_verify_sampling_amd", "csrc", f)
+              for f in ("k_stats.hip", "segment.hpp", "common.hpp", "words.hpp", "launch.hpp")]
+
+
+def stats_source_hash():
+    h = hashlib.sha1()
+    for path in STATS_SRCS:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def log(msg):
@@ -168,8 +179,7 @@ def summarize_counters(fetch_db, write_db, out_json):
                             copy_true_kib=ref_kib, scale=scale,
                             bytes_per_launch=sum(stats) / len(stats) / scale * 1024)
         res[counter + "_all_kernels_raw_kib"] = {n[:80]: sum(v) / len(v) for n, v in k.items()}
-    with open(STATS_SRC, "rb") as f:
-        res["kernel_source_sha1"] = hashlib.sha1(f.read()).hexdigest()
+    res["kernel_source_sha1"] = stats_source_hash()
     res["bytes_per_launch"] = int(res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"])
     with open(out_json, "w") as f:
         json.dump(res, f, indent=1)
@@ -213,8 +223,7 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    with open(STATS_SRC, "rb") as f:
-        src_hash = hashlib.sha1(f.read()).hexdigest()
+    src_hash = stats_source_hash()
 
     result = dict(metric=METRIC, n_gpus=1, steps=args.steps, warmup=args.warmup,
                   higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",

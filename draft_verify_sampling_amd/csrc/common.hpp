@@ -76,6 +76,9 @@ __device__ __forceinline__ int64_t head_elems(const void* row, int64_t V) {
 // formed by one fused multiply-add.  Because m is itself a representable value
 // of the scaled domain, merging two pairs rescales by 2^(m_a - M) with the
 // dominant side's factor exactly 1, so no rounding of the max leaks into s.
+// Every multiply-add that is meant to be fused is written as fmaf, and the
+// library is built without implicit contraction, so each kernel that forms a
+// pair or a weight rounds exactly alike.
 // ---------------------------------------------------------------------------
 struct MS {
   float m;
@@ -85,7 +88,7 @@ struct MS {
 __device__ __forceinline__ MS ms_combine(MS a, MS b) {
   const float M = fmaxf(a.m, b.m);
   if (M == -INFINITY) return MS{M, 0.f};
-  return MS{M, a.s * ex2(a.m - M) + b.s * ex2(b.m - M)};
+  return MS{M, fmaf(a.s, ex2(a.m - M), b.s * ex2(b.m - M))};
 }
 
 // Fold n raw scores into a running pair: one rescale per group, pairwise group sum.
@@ -104,7 +107,7 @@ __device__ __forceinline__ void ms_fold(MS& acc, const float* x, float c) {
 #pragma unroll
     for (int j = 0; j + w < n; j += 2 * w) e[j] += e[j + w];
   }
-  acc.s = acc.s * ex2(acc.m - M) + e[0];
+  acc.s = fmaf(acc.s, ex2(acc.m - M), e[0]);
   acc.m = M;
 }
 

@@ -19,83 +19,12 @@
 // block whose request has already stopped at an earlier row does nothing.
 // Blocks never wait for a decision: a block that starts before the decision
 // it could use computes its segment anyway, which is only wasted bandwidth.
-//
-// Within a block, every thread issues its 16-byte loads of the segment at once
-// (coalesced, non-temporal); segment 0 also takes the row's unaligned head
-// elements and the last segment its tail.
 #include "common.hpp"
 #include "launch.hpp"
+#include "segment.hpp"
+#include "words.hpp"
 
 namespace sv {
-
-namespace {
-
-// Online-softmax pair of segment `seg` of a row, valid in thread 0.  `sh`
-// holds 2 * (kBlock / 64) floats.
-template <class D, bool NT>
-__device__ __forceinline__ MS segment_ms(const void* base, int64_t V, int32_t seg, int32_t nseg, float c,
-                                         float* sh) {
-  constexpr int U = kSegElems / (kBlock * D::kPerVec);
-  constexpr int kSegVecs = kSegElems / D::kPerVec;
-  const int64_t head = head_elems<D>(base, V);
-  const int64_t nvec = (V - head) / D::kPerVec;
-  const uint4* vp = reinterpret_cast<const uint4*>(static_cast<const char*>(base) + head * D::kSize);
-
-  MS acc{-INFINITY, 0.f};
-  {
-    const int64_t v0 = static_cast<int64_t>(seg) * kSegVecs + threadIdx.x;
-    uint4 w[U];
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
-      const int64_t v = v0 + j * kBlock;
-      w[j] = uint4{0u, 0u, 0u, 0u};
-      if (v < nvec) {
-        if (NT) {
-          const uint32_t* q = reinterpret_cast<const uint32_t*>(vp + v);
-          w[j] = uint4{__builtin_nontemporal_load(q), __builtin_nontemporal_load(q + 1),
-                       __builtin_nontemporal_load(q + 2), __builtin_nontemporal_load(q + 3)};
-        } else {
-          w[j] = vp[v];
-        }
-      }
-    }
-    float x[U * D::kPerVec];
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
-      D::unpack(w[j], x + j * D::kPerVec);
-      if (v0 + j * kBlock >= nvec) {
-#pragma unroll
-        for (int t = 0; t < D::kPerVec; ++t) x[j * D::kPerVec + t] = -INFINITY;
-      }
-    }
-    ms_fold<U * D::kPerVec>(acc, x, c);
-  }
-  if (seg == 0) {
-    for (int64_t i = threadIdx.x; i < head; i += kBlock) {
-      float x = D::at(base, i);
-      ms_fold<1>(acc, &x, c);
-    }
-  }
-  if (seg == nseg - 1) {
-    for (int64_t i = head + nvec * D::kPerVec + threadIdx.x; i < V; i += kBlock) {
-      float x = D::at(base, i);
-      ms_fold<1>(acc, &x, c);
-    }
-  }
-  // block reduction: DPP within each wave, then the four wave results
-  const MS r = wave_ms_dpp(acc);
-  const int wid = threadIdx.x / kWave;
-  if ((threadIdx.x & (kWave - 1)) == 0) {
-    sh[2 * wid] = r.m;
-    sh[2 * wid + 1] = r.s;
-  }
-  __syncthreads();
-  MS t{sh[0], sh[1]};
-  for (int w = 1; w < kBlock / kWave; ++w) t = ms_combine(t, MS{sh[2 * w], sh[2 * w + 1]});
-  return t;
-}
-
-}  // namespace
 
 // `clear` (optional, n16 16-byte words) is zeroed on the side, for the exchange
 // words of the walk that follows this kernel on the stream.
@@ -129,21 +58,6 @@ hipError_t launch_row_stats(int dtype, const void* rows, int64_t n_rows, int64_t
 
 // ---- the lazy statistics of the chain verify ----
 
-namespace {
-
-constexpr uint64_t kWordValid = 1ull << 63;
-
-// A softmax pair as one 64-bit word whose bit 63 is set (s >= 0 or NaN frees
-// its sign bit).
-__device__ __forceinline__ uint64_t pair_word(MS v) {
-  return (static_cast<uint64_t>(__float_as_uint(v.s) | 0x80000000u) << 32) | __float_as_uint(v.m);
-}
-__device__ __forceinline__ MS word_pair(uint64_t w) {
-  return MS{__uint_as_float(static_cast<uint32_t>(w)),
-            __uint_as_float(static_cast<uint32_t>(w >> 32) & 0x7fffffffu)};
-}
-
-}  // namespace
 
 template <class DT, class DQ>
 __global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
@@ -181,7 +95,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
   const MS t = segment_ms<DT, true>(row_ptr<DT>(a.tgt, ts + i, a.V), a.V, seg, a.nseg, a.c, sh);
   uint64_t* words = a.seg_words + (static_cast<int64_t>(b) * R + i) * a.nseg;
   if (threadIdx.x == 0) {
-    __hip_atomic_store(words + seg, pair_word(t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(words + seg, enc_ms(t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t done = __hip_atomic_fetch_add(a.count + static_cast<int64_t>(b) * R + i, 1u,
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = done == static_cast<uint32_t>(a.nseg - 1);
@@ -200,7 +114,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
     int done = 0;
     for (int it = 0; it < a.spin_limit; ++it) {
       if (s < a.nseg) v = __hip_atomic_load(words + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (__all(s >= a.nseg || (v & kWordValid) != 0)) {
+      if (__all(s >= a.nseg || (v & kValid) != 0)) {
         done = 1;
         break;
       }
@@ -211,14 +125,14 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
   }
   // the canonical combine of the segment pairs (the walk combines the
   // partials of every row the same way)
-  const MS row = wave_combine_segments(a.nseg, [&](int s) { return word_pair(s_w[s]); });
+  const MS row = wave_combine_segments(a.nseg, [&](int s) { return dec_ms(s_w[s]); });
   if (lane != 0) return;
   bool stop_here;
   if (!ok) {
     flag(a.status, kFlagSyncTimeout);
     stop_here = true;
   } else {
-    __hip_atomic_store(a.row_words + static_cast<int64_t>(b) * R + i, pair_word(row), __ATOMIC_RELAXED,
+    __hip_atomic_store(a.row_words + static_cast<int64_t>(b) * R + i, enc_ms(row), __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
     stop_here = !(row.s > 0.f && row.s < INFINITY);
     if (!stop_here && i < k) {

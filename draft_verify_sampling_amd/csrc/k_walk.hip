@@ -50,6 +50,7 @@
 #include <mutex>
 
 #include "tiles.hpp"
+#include "words.hpp"
 
 namespace sv {
 
@@ -60,30 +61,6 @@ constexpr int kMaxNodeGroups = kMaxTreeNodes / kWave;
 static_assert(2 * kMaxWalkGroups <= kWave, "one wave reads every exchanged word");
 static_assert(kMaxChainRows <= kWalkBlock, "one chain row per thread");
 constexpr int kPartStage = 2048;  // partials of a chain request staged in LDS
-
-constexpr uint64_t kValid = 1ull << 63;
-
-// ---- exchanged words (bit 63 set = written in this call) ----
-__device__ __forceinline__ uint64_t enc_ms(MS v) {
-  return (static_cast<uint64_t>(__float_as_uint(v.s) | 0x80000000u) << 32) | __float_as_uint(v.m);
-}
-__device__ __forceinline__ MS dec_ms(uint64_t w) {
-  return MS{__uint_as_float(static_cast<uint32_t>(w)),
-            __uint_as_float(static_cast<uint32_t>(w >> 32) & 0x7fffffffu)};
-}
-// A sum of non-negative terms (or NaN): its sign bit carries the valid bit.
-__device__ __forceinline__ uint64_t enc_sum(double x) {
-  if (isnan(x)) return 0xfff8000000000001ull;
-  return static_cast<uint64_t>(__double_as_longlong(x)) | kValid;
-}
-__device__ __forceinline__ double dec_sum(uint64_t w) {
-  return __longlong_as_double(static_cast<long long>(w & ~kValid));
-}
-// Class of a slice's draft-row sum: NaN, +inf, -inf.  The row's total is NaN
-// iff some slice is NaN or the slices hold both infinities.
-__device__ __forceinline__ uint64_t enc_qclass(double q) {
-  return kValid | (isnan(q) ? 1u : 0u) | (q == INFINITY ? 2u : 0u) | (q == -INFINITY ? 4u : 0u);
-}
 
 struct Walk {
   const WalkArgs* a;
@@ -197,7 +174,7 @@ __device__ bool weight_pass(Walk& wk, const DrawRow& r, double* wt, double* s_wq
     cls |= x[2 * h + 1];
   }
   W = tot;
-  qnan = (cls & 1u) || ((cls & 2u) && (cls & 4u));
+  qnan = qclass_nan(cls);
   return true;
 }
 
@@ -564,7 +541,7 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
           __syncthreads();
         } else {
           const float p = s_px[ch], q = s_qx[ch];
-          const float pc = coef == 0.f ? p : fmaxf(p - coef * q, 0.f) / R;
+          const float pc = coef == 0.f ? p : fmaxf(fmaf(-coef, q, p), 0.f) / R;
           if (s_u[ch - 1] * q < pc) {
             kept = ch;
             break;

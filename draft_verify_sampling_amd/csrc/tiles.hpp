@@ -63,7 +63,7 @@ __device__ __forceinline__ float draw_p(const DrawRow& r, float l) {
 }
 
 __device__ __forceinline__ float draw_w(const DrawRow& r, float p, float q) {
-  return r.use_q ? fmaxf(p - r.coef * q, 0.f) : p;
+  return r.use_q ? fmaxf(fmaf(-r.coef, q, p), 0.f) : p;
 }
 
 // Layout of a tile for the sums: runs of kPer consecutive elements (the wider

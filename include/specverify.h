@@ -182,9 +182,10 @@ sv_status sv_verify_greedy(const void* target_logits, int32_t t_dtype, int32_t t
  * (M_i = max(l/T), S_i = sum exp(l/T - M_i), p_i(x_i), q_i(x_i)) for i <= k_b
  * (p, q = 0 at i = k_b; rows beyond k_b untouched); out_resid [batch] = total
  * mass of the weights the last token was drawn from.
- * The round reads target rows 0..m and draft row m only (every row when
- * out_diag is asked for).  temperature must be finite and > 0; 1 <= vocab <=
- * 4194304. */
+ * The round reads target rows 0..k_b (0..m when the lazy statistics apply:
+ * requests own their rows, many statistics blocks per row, no out_diag), draft
+ * row m and the entries at the drafted tokens.  temperature must be finite and
+ * > 0; 1 <= vocab <= 4194304. */
 sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t_rows,
                            const void* draft_probs, int32_t q_dtype, int32_t q_rows,
                            int64_t vocab, const int32_t* t_row_start,
