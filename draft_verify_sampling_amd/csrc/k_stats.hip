@@ -79,7 +79,11 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
   if (i > k || k > a.k_max || ts < 0 || static_cast<int64_t>(ts) + k >= a.t_rows ||
       (k > 0 && (qs < 0 || static_cast<int64_t>(qs) + k > a.q_rows)))
     return;  // no such row, or a request the walk reports as invalid
-  if (sv > static_cast<uint32_t>(kMaxChainRows - i)) return;  // row i is not needed
+  // Row i is not needed.  The stop word can change while the block's waves
+  // read it, so some waves may leave and the rest form a partial pair; that
+  // happens only once an earlier row has stopped the round, so row i's pair
+  // and decision are never used (the stop word keeps the earliest row).
+  if (sv > static_cast<uint32_t>(kMaxChainRows - i)) return;
 
   // thread 0 fetches what the decision needs together with the segment
   int x = -1;
