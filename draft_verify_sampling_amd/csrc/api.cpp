@@ -75,6 +75,14 @@ sv_status launch_walk_call(int mode, int32_t t_dtype, int32_t q_dtype, sv::WalkA
   const int64_t resident = static_cast<int64_t>(occ) * std::max(cu_count(), 1);
   a.G = std::min<int32_t>(sv::walk_groups(a.B, a.V, resident),
                           static_cast<int32_t>(sv::walk_groups_bound(a.B)));
+  // The point-mass walk makes one pass per visited node and then only
+  // exchanges per rejected candidate: the fewest workgroups that still give
+  // every wave at most one tile per pass (measured 7% faster on the 60-node
+  // trees at V = 128,256 than one workgroup per CU).
+  if (mode == sv::kWalkPoint) {
+    constexpr int kWaves = sv::kWalkBlock / 64;
+    a.G = std::min<int32_t>(a.G, static_cast<int32_t>(std::max<int64_t>(1, (ntiles + kWaves - 1) / kWaves)));
+  }
   // Lazy statistics skip a row only when its request's decision on the row
   // before is known by the time the row's blocks start, which needs at least
   // two waves of statistics blocks per row (8 resident blocks per CU); with

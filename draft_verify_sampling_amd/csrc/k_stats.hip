@@ -99,7 +99,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
   const MS t = segment_ms<DT, true>(row_ptr<DT>(a.tgt, ts + i, a.V), a.V, seg, a.nseg, a.c, sh);
   uint64_t* words = a.seg_words + (static_cast<int64_t>(b) * R + i) * a.nseg;
   if (threadIdx.x == 0) {
-    __hip_atomic_store(words + seg, enc_ms(t), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    store_word(words + seg, enc_ms(t));
     const uint32_t done = __hip_atomic_fetch_add(a.count + static_cast<int64_t>(b) * R + i, 1u,
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = done == static_cast<uint32_t>(a.nseg - 1);
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
     uint64_t v = 0;
     int done = 0;
     for (int it = 0; it < a.spin_limit; ++it) {
-      if (s < a.nseg) v = __hip_atomic_load(words + s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (s < a.nseg) v = load_word(words + s);
       if (__all(s >= a.nseg || (v & kValid) != 0)) {
         done = 1;
         break;
@@ -136,8 +136,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
     flag(a.status, kFlagSyncTimeout);
     stop_here = true;
   } else {
-    __hip_atomic_store(a.row_words + static_cast<int64_t>(b) * R + i, enc_ms(row), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+    store_word(a.row_words + static_cast<int64_t>(b) * R + i, enc_ms(row));
     stop_here = !(row.s > 0.f && row.s < INFINITY);
     if (!stop_here && i < k) {
       if (x < 0 || x >= a.V) {

@@ -90,15 +90,15 @@ __device__ bool exchange(Walk& wk, uint64_t w0, uint64_t w1) {
   } else {
     uint64_t* row = a.slots + (static_cast<int64_t>(wk.b) * a.max_sync + wk.nsync) * 2 * a.G;
     if (threadIdx.x == 0) {
-      __hip_atomic_store(row + 2 * wk.g, w0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(row + 2 * wk.g + 1, w1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      store_word(row + 2 * wk.g, w0);
+      store_word(row + 2 * wk.g + 1, w1);
     }
     if (threadIdx.x < kWave) {
       const int n = 2 * a.G;
       uint64_t v = 0;
       int done = 0;
       for (int it = 0; it < a.spin_limit; ++it) {
-        if (lane < n) v = __hip_atomic_load(row + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (lane < n) v = load_word(row + lane);
         if (__all(lane >= n || (v & kValid) != 0)) {
           done = 1;
           break;
