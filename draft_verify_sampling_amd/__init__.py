@@ -28,7 +28,7 @@ __all__ = [
     "sv_philox_uniforms", "sv_verify_sample_philox", "DraftTreeState", "sv_tree_expand",
     "sv_tree_finalize", "SV_OP_TREE_EXPAND", "SV_OP_SHARD", "sv_shard_stats", "sv_shard_residual",
     "sv_shard_draw",
-    "prepare_softmax_partials",
+    "prepare_softmax_partials", "sv_time_statistics_once",
 ]
 
 SV_F32, SV_BF16 = 0, 1
@@ -41,7 +41,7 @@ EXPORTS = ("sv_abi_version", "sv_status_string", "sv_last_error", "sv_workspace_
            "sv_ngram_draft", "sv_verify_greedy", "sv_verify_sample", "sv_verify_tree",
            "sv_verify_tree_greedy", "sv_verify_tree_pointmass", "sv_philox_uniforms",
            "sv_verify_sample_philox", "sv_tree_expand", "sv_tree_finalize", "sv_shard_stats",
-           "sv_shard_residual", "sv_shard_draw")
+           "sv_shard_residual", "sv_shard_draw", "sv_time_statistics_once")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -70,6 +70,7 @@ _SIGS = {
                                       P, P, P, P, P, SZ, P]),
     "sv_verify_tree_greedy": (ctypes.c_int, [P, I32, I64, P, P, I32, I32, P, P, P, P, P, P, SZ, P]),
     "sv_philox_uniforms": (ctypes.c_int, [U64, U64, I32, I32, P, P]),
+    "sv_time_statistics_once": (ctypes.c_int, [P, P]),
     "sv_tree_expand": (ctypes.c_int, [P, I32, I64, I32, I32, P, I32, I32, I32, P, P, P, P, P, P, P, P,
                                       P, SZ, P]),
     "sv_tree_finalize": (ctypes.c_int, [I32, I32, P, P, P, P, P, P, I32, P, P, P, P, P, P, P]),
@@ -121,6 +122,23 @@ def abi_version() -> int:
 
 def workspace_bytes(op: int, batch: int, total_rows: int, vocab: int) -> int:
     return int(load().sv_workspace_bytes(op, batch, total_rows, vocab))
+
+
+def sv_time_statistics_once(before=None, after=None):
+    """Arm the measurement hook: the calling thread's next sampled chain call
+    records torch.cuda.Event `before` / `after` around its statistics kernel
+    (None, None disarms).  The events are created here if they are not yet."""
+    if (before is None) != (after is None):
+        raise SpecVerifyError("give both events or neither")
+    ptrs = []
+    for e in (before, after):
+        if e is None:
+            ptrs.append(None)
+            continue
+        if not e.cuda_event:  # torch creates its events on first use
+            e.record()
+        ptrs.append(ctypes.c_void_p(e.cuda_event))
+    _check(load().sv_time_statistics_once(*ptrs), "sv_time_statistics_once")
 
 
 def _check(status: int, what: str):

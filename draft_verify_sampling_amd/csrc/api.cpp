@@ -17,6 +17,15 @@ namespace {
 
 thread_local char g_err[512] = "";
 
+// Measurement hook (sv_time_statistics_once): events recorded around the
+// statistics kernel of this thread's next sampled chain call.
+thread_local hipEvent_t g_stat_ev[2] = {nullptr, nullptr};
+
+// Records g_stat_ev[which] on `st` if the hook is armed.
+void stat_event(int which, hipStream_t st) {
+  if (g_stat_ev[which] != nullptr) (void)hipEventRecord(g_stat_ev[which], st);
+}
+
 sv_status fail(sv_status s, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -129,17 +138,21 @@ sv_status launch_walk_call(int mode, int32_t t_dtype, int32_t q_dtype, sv::WalkA
     c.seg_words = reinterpret_cast<uint64_t*>(ws + L.segs_off);
     c.status = a.status;
     c.spin_limit = sv::kSpinLimit;
+    stat_event(0, st);
     e = sv::launch_chain_stats(t_dtype, q_dtype, c, st);
     if (e != hipSuccess) return device_fail(e, what);
+    stat_event(1, st);
     a.stop = c.stop;
     a.row_words = c.row_words;
     clear_slots = false;
   } else if (chain || a.diag != nullptr) {  // the walk reads every row's partials
     const int64_t slot_words = static_cast<int64_t>(L.stop_off - L.slots_off) / 8;
+    if (chain) stat_event(0, st);
     const hipError_t e = sv::launch_row_stats(t_dtype, a.tgt, rows, a.V, a.nseg, a.c,
                                               reinterpret_cast<float2*>(ws + L.partial_off), st,
                                               a.slots, slot_words);
     if (e != hipSuccess) return device_fail(e, what);
+    if (chain) stat_event(1, st);
     clear_slots = false;  // the statistics kernel zeroed the exchange words
   }
   const size_t lds = sv::walk_lds_bytes(a.node_cap, a.tile_cap);
@@ -192,6 +205,13 @@ size_t sv_workspace_bytes(int op, int64_t batch, int64_t total_rows, int64_t voc
     default:
       return 0;
   }
+}
+
+sv_status sv_time_statistics_once(void* before, void* after) {
+  if ((before == nullptr) != (after == nullptr)) return fail(SV_E_ARG, "give both events or neither");
+  g_stat_ev[0] = static_cast<hipEvent_t>(before);
+  g_stat_ev[1] = static_cast<hipEvent_t>(after);
+  return SV_OK;
 }
 
 int32_t sv_softmax_segments(int64_t n_rows, int64_t vocab) {
@@ -291,6 +311,9 @@ static sv_status sample_impl(const void* target_logits, int32_t t_dtype, int32_t
                              int32_t* out_tokens, int32_t* out_count, int32_t* out_accepted,
                              float* out_diag, float* out_resid, int32_t* dev_status, void* workspace,
                              size_t workspace_bytes, void* stream, const char* what) {
+  struct HookDone {  // the measurement hook serves this call at most
+    ~HookDone() { g_stat_ev[0] = g_stat_ev[1] = nullptr; }
+  } hook_done;
   if (!dtype_ok(t_dtype) || !dtype_ok(q_dtype))
     return fail(SV_E_DTYPE, "t_dtype and q_dtype must be SV_F32 or SV_BF16");
   if (batch < 0) return fail(SV_E_ARG, "batch < 0");

@@ -197,6 +197,17 @@ sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t
                            float* out_diag, float* out_resid, int32_t* dev_status,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Measurement hook, not an operation of the method: for the calling thread's
+ * next sv_verify_sample or sv_verify_sample_philox call, record `before` (a
+ * hipEvent_t) on that call's stream right before its statistics kernel and
+ * `after` right after it (every such call with batch > 0 launches one: the
+ * partials of every row, or the lazy statistics), so a caller can time that
+ * kernel inside a real call.  The hook then disarms, also when that call
+ * fails or has no requests.  NULL, NULL disarms it; giving one event only is
+ * SV_E_ARG.  The events must stay valid until that call returns.  Host
+ * function; thread-local. */
+sv_status sv_time_statistics_once(void* before, void* after);
+
 /* Counter-based uniforms (Philox4x64-10; Salmon, Moraes, Dror and Shaw,
  * "Parallel random numbers: as easy as 1, 2, 3", SC 2011), so that a serving
  * loop need not generate and upload the verify's uniforms.  Slot i of request

@@ -50,6 +50,14 @@ def test_workspace_sizes(lib):
     assert sv.workspace_bytes(7, 1, 1, 1) == 0
 
 
+def test_statistics_timing_hook_arguments(lib):
+    # host-only: both events or neither (nothing is recorded without a call)
+    assert lib.sv_time_statistics_once(None, None) == 0
+    assert lib.sv_time_statistics_once(ctypes.c_void_p(256), None) == 1
+    assert "both events" in lib.sv_last_error().decode()
+    assert lib.sv_time_statistics_once(None, None) == 0
+
+
 def _err(lib):
     return lib.sv_last_error().decode()
 
