@@ -6,18 +6,27 @@
 // Readings: the most recent occurrence that is followed by at least one token
 // wins (start j <= n - window - 1); the proposal stops at the context end.
 //
-// One block per request.  Threads test candidate starts in rounds of 256,
-// newest first; a round that finds a match ends the search (LDS max of the
-// matching starts), so a match near the end of a long context costs one round.
+// One block per request.  The candidate starts are tested newest first in
+// chunks of 4096: a chunk's tokens (plus the window's overlap) are staged in
+// LDS with coalesced loads, every thread tests its starts of the chunk from
+// LDS (newest first, stopping at its first match), and the block's largest
+// matching start ends the search; a match in the newest 4096 starts costs one
+// load round.  A chunk also stages the up to k tokens after its newest
+// window, so the proposal of a match comes from LDS too.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace sv {
 
+constexpr int kNgramChunk = 4096;
+constexpr int kMaxNgramDraft = 1024;  // k <= 1024 (checked on the host)
+
 __global__ __launch_bounds__(kBlock) void k_ngram(const int32_t* __restrict__ ctx,
                                                   const int32_t* __restrict__ ctx_len, int32_t stride,
                                                   int32_t window, int32_t k, int32_t* __restrict__ ids,
                                                   int32_t* __restrict__ lens, int32_t* status) {
+  __shared__ int32_t s_tok[kNgramChunk + kMaxWindow + kMaxNgramDraft];
+  __shared__ int s_lo, s_end;  // tokens [s_lo, s_end) of the last staged chunk
   __shared__ int32_t s_key[kMaxWindow];
   __shared__ int s_best;
   const int b = blockIdx.x;
@@ -33,20 +42,36 @@ __global__ __launch_bounds__(kBlock) void k_ngram(const int32_t* __restrict__ ct
     }
     return;
   }
-  if (tid == 0) s_best = -1;
+  if (tid == 0) {
+    s_best = -1;
+    s_lo = s_end = 0;
+  }
   if (k > 0 && n >= window + 1) {
     for (int i = tid; i < window; i += kBlock) s_key[i] = row[n - window + i];
-    __syncthreads();
-    for (int start = n - window - 1; start >= 0; start -= kBlock) {
-      const int j = start - tid;
-      if (j >= 0) {
+    // candidate starts j in [lo, hi], newest chunk first (j <= n - window - 1:
+    // at least one token follows the match)
+    for (int hi = n - window - 1; hi >= 0; hi -= kNgramChunk) {
+      const int lo = hi - kNgramChunk + 1 > 0 ? hi - kNgramChunk + 1 : 0;
+      // tokens [lo, hi + window + k) within the context: the windows of the
+      // chunk's starts and what follows the newest of them
+      const int end = hi + window + k < n ? hi + window + k : n;
+      for (int i = tid; i < end - lo; i += kBlock) s_tok[i] = row[lo + i];
+      if (tid == 0) {
+        s_lo = lo;
+        s_end = end;
+      }
+      __syncthreads();
+      for (int j = hi - tid; j >= lo; j -= kBlock) {
         bool match = true;
-        for (int i = 0; i < window && match; ++i) match = row[j + i] == s_key[i];
-        if (match) atomicMax(&s_best, j);
+        for (int i = 0; i < window && match; ++i) match = s_tok[j - lo + i] == s_key[i];
+        if (match) {
+          atomicMax(&s_best, j);
+          break;  // this thread's later starts are older
+        }
       }
       __syncthreads();
       const int found = s_best;
-      __syncthreads();  // every thread has read s_best before the next round writes it
+      __syncthreads();  // every thread has read s_best (and s_tok) before the next chunk
       if (found >= 0) break;
     }
   }
@@ -57,7 +82,13 @@ __global__ __launch_bounds__(kBlock) void k_ngram(const int32_t* __restrict__ ct
     len = n - (j + window);
     if (len > k) len = k;
   }
-  for (int i = tid; i < k; i += kBlock) out[i] = i < len ? row[j + window + i] : -1;
+  // the proposal: from the staged chunk when it holds it (a match found in
+  // the chunk), else from the context
+  const int lo = s_lo, end = s_end;
+  for (int i = tid; i < k; i += kBlock) {
+    const int at = j + window + i;
+    out[i] = i < len ? (at >= lo && at < end ? s_tok[at - lo] : row[at]) : -1;
+  }
   if (tid == 0) lens[b] = len;
 }
 
