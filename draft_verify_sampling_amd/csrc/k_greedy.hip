@@ -11,8 +11,9 @@
 // slice of one row with 16-byte loads and leaves one 64-bit key per slice,
 // (order-preserving bits of the value) << 32 | ~index, so that one unsigned max
 // picks the largest value and, among equal values, the lowest index; a slice
-// holding a NaN leaves the key 0xFFFF...F instead.  k_greedy_resolve: one thread
-// per request combines the keys of its k_b + 1 rows and runs the prefix compare.
+// holding a NaN leaves the key 0xFFFF...F instead.  k_greedy_resolve: one block
+// per request merges the keys of its k_b + 1 rows (thread i ends with row i's
+// argmax) and runs the prefix compare.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -75,26 +76,32 @@ __global__ __launch_bounds__(kBlock) void k_row_argmax(const void* __restrict__ 
 
   // sentinel index INT32_MAX: loses every tie against a real element
   Best best{-INFINITY, 0x7fffffff, false};
-  int64_t v = v0 + threadIdx.x;
-  for (; v + (U - 1) * kBlock < v1; v += U * kBlock) {
+  // chunks of U * kBlock vectors; a chunk's loads are all issued before any
+  // is used (non-temporal: the rows are read once), so a slice of up to
+  // U * kBlock vectors costs one load round
+  for (int64_t c0 = v0 + threadIdx.x; c0 < v1; c0 += U * kBlock) {
     uint4 w[U];
 #pragma unroll
-    for (int j = 0; j < U; ++j) w[j] = vp[v + j * kBlock];
+    for (int j = 0; j < U; ++j) {
+      const int64_t v = c0 + j * kBlock;
+      w[j] = uint4{0u, 0u, 0u, 0u};
+      if (v < v1) {
+        const uint32_t* q = reinterpret_cast<const uint32_t*>(vp + v);
+        w[j] = uint4{__builtin_nontemporal_load(q), __builtin_nontemporal_load(q + 1),
+                     __builtin_nontemporal_load(q + 2), __builtin_nontemporal_load(q + 3)};
+      }
+    }
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      float x[D::kPerVec];
-      D::unpack(w[j], x);
-      const int64_t e = head + (v + j * kBlock) * D::kPerVec;
+      const int64_t v = c0 + j * kBlock;
+      if (v < v1) {
+        float x[D::kPerVec];
+        D::unpack(w[j], x);
+        const int64_t e = head + v * D::kPerVec;
 #pragma unroll
-      for (int t = 0; t < D::kPerVec; ++t) best_update(best, x[t], e + t);
+        for (int t = 0; t < D::kPerVec; ++t) best_update(best, x[t], e + t);
+      }
     }
-  }
-  for (; v < v1; v += kBlock) {
-    float x[D::kPerVec];
-    D::unpack(vp[v], x);
-    const int64_t e = head + v * D::kPerVec;
-#pragma unroll
-    for (int t = 0; t < D::kPerVec; ++t) best_update(best, x[t], e + t);
   }
   if (seg == 0)
     for (int64_t i = threadIdx.x; i < head; i += kBlock) best_update(best, D::at(base, i), i);
@@ -113,58 +120,69 @@ __global__ __launch_bounds__(kBlock) void k_row_argmax(const void* __restrict__ 
   }
 }
 
+// One block per request; thread i holds draft i and, after the key merge,
+// row i's argmax.  Two dependent load rounds: the request (its row start,
+// draft count, budget and drafts), then the keys of its rows.
+static_assert(kMaxChainRows <= kBlock, "one chain row per thread");
 __global__ __launch_bounds__(kBlock) void k_greedy_resolve(GreedyArgs a) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= a.B) return;
+  __shared__ unsigned long long s_best[kMaxChainRows];
+  __shared__ int s_bits, s_m, s_eos, s_pick;
+  const int b = blockIdx.x, tid = threadIdx.x;
   const int ustride = a.k_max + 1;
   int32_t* out = a.out_tok + static_cast<int64_t>(b) * ustride;
   const int k = a.dlen[b];
   const int ts = a.t_rs[b];
-  int bits = 0;
-  if (k < 0 || k > a.k_max || ts < 0 || static_cast<int64_t>(ts) + k >= a.t_rows) bits = kFlagBadRequest;
-  const int32_t* x = a.ids + static_cast<int64_t>(b) * a.k_max;
-  if (!bits)
-    for (int i = 0; i < k; ++i)
-      if (x[i] < 0 || x[i] >= a.V) bits = kFlagBadToken;
-  int m = 0, pick = 0;
+  const int budget = a.max_new != nullptr ? a.max_new[b] : 0;
+  const int x = tid < a.k_max ? a.ids[static_cast<int64_t>(b) * a.k_max + tid] : -1;
+  if (tid == 0) {
+    s_bits = 0;
+    s_m = k;
+    s_eos = kMaxChainRows;
+  }
+  s_best[tid] = 0;
+  const bool bad_req = k < 0 || k > a.k_max || ts < 0 || static_cast<int64_t>(ts) + k >= a.t_rows;
+  __syncthreads();
+  if (!bad_req) {
+    if (tid < k && (x < 0 || x >= a.V)) atomicOr(&s_bits, kFlagBadToken);
+    const int64_t n = static_cast<int64_t>(k + 1) * a.nseg;
+    const uint64_t* kk = a.keys + static_cast<int64_t>(ts) * a.nseg;
+    for (int64_t j = tid; j < n; j += kBlock) atomicMax(&s_best[j / a.nseg], static_cast<unsigned long long>(kk[j]));
+  }
+  __syncthreads();
+  int bits = bad_req ? kFlagBadRequest : s_bits;
   if (!bits) {
-    if (a.max_new != nullptr && k > a.max_new[b]) flag(a.status, kFlagOverBudget);
-    // every row of the request must be NaN-free; stop comparing at the first mismatch
-    m = k;
-    for (int i = 0; i <= k; ++i) {
-      const uint64_t* kk = a.keys + static_cast<int64_t>(ts + i) * a.nseg;
-      uint64_t best = 0;
-      for (int s = 0; s < a.nseg; ++s) best = kk[s] > best ? kk[s] : best;
-      if (best == kNanKey) {
-        bits = kFlagNonfinite;
-        break;
+    // every row of the request must be NaN-free; the drafts are kept up to
+    // the first one that differs from its row's argmax
+    if (tid == 0 && a.max_new != nullptr && k > budget) flag(a.status, kFlagOverBudget);
+    const uint64_t best = s_best[tid];
+    if (tid <= k && best == kNanKey) atomicOr(&s_bits, kFlagNonfinite);
+    const int am = static_cast<int>(~static_cast<uint32_t>(best));
+    if (tid < k && x != am) atomicMin(&s_m, tid);
+    __syncthreads();
+    bits = s_bits;
+    if (!bits) {
+      const int m = s_m;
+      if (tid == m) s_pick = am;
+      if (tid < m && a.eos >= 0 && x == a.eos) atomicMin(&s_eos, tid);
+      __syncthreads();
+      // the kept drafts up to the first EOS among them; the target's pick
+      // after them unless an EOS ended the round; then the budget
+      int cnt = s_eos < m ? s_eos + 1 : m + 1;
+      if (a.max_new != nullptr) cnt = min(cnt, max(budget, 0));
+      if (tid < ustride) out[tid] = tid < cnt ? (tid < m ? x : s_pick) : -1;
+      if (tid == 0) {
+        a.out_cnt[b] = cnt;
+        a.out_acc[b] = m;
       }
-      const int am = static_cast<int>(~static_cast<uint32_t>(best));
-      if (i < m && i < k && x[i] != am) m = i;
-      if (i == m) pick = am;
+      return;
     }
   }
-  if (bits) {
-    for (int i = 0; i < ustride; ++i) out[i] = -1;
+  if (tid < ustride) out[tid] = -1;
+  if (tid == 0) {
     a.out_cnt[b] = 0;
     a.out_acc[b] = 0;
     flag(a.status, bits);
-    return;
   }
-  int cnt = 0;
-  bool stop = false;
-  for (int i = 0; i < m && !stop; ++i) {
-    out[cnt++] = x[i];
-    if (a.eos >= 0 && x[i] == a.eos) stop = true;
-  }
-  if (!stop) out[cnt++] = pick;
-  if (a.max_new != nullptr) {
-    const int budget = a.max_new[b] > 0 ? a.max_new[b] : 0;
-    if (cnt > budget) cnt = budget;
-  }
-  for (int i = cnt; i < ustride; ++i) out[i] = -1;
-  a.out_cnt[b] = cnt;
-  a.out_acc[b] = m;
 }
 
 hipError_t launch_row_argmax(int dtype, const void* rows, int64_t n_rows, int64_t V, int32_t nseg,
@@ -178,7 +196,7 @@ hipError_t launch_row_argmax(int dtype, const void* rows, int64_t n_rows, int64_
 }
 
 hipError_t launch_greedy_resolve(const GreedyArgs& a, hipStream_t stream) {
-  const dim3 grid(static_cast<uint32_t>((a.B + kBlock - 1) / kBlock)), block(kBlock);
+  const dim3 grid(static_cast<uint32_t>(a.B)), block(kBlock);
   hipLaunchKernelGGL(k_greedy_resolve, grid, block, 0, stream, a);
   return hipGetLastError();
 }

@@ -8,11 +8,12 @@
 //
 // One block per request.  The candidate starts are tested newest first in
 // chunks of 4096: a chunk's tokens (plus the window's overlap) are staged in
-// LDS with coalesced loads, every thread tests its starts of the chunk from
-// LDS (newest first, stopping at its first match), and the block's largest
-// matching start ends the search; a match in the newest 4096 starts costs one
-// load round.  A chunk also stages the up to k tokens after its newest
-// window, so the proposal of a match comes from LDS too.
+// LDS with coalesced 16-byte loads, all issued at once; every thread tests its
+// starts of the chunk from LDS (newest first, stopping at its first match),
+// and the block's largest matching start ends the search; a match in the
+// newest 4096 starts costs one load round.  A chunk also stages the up to k
+// tokens after its newest window, so the proposal of a match comes from LDS
+// too.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -20,12 +21,45 @@ namespace sv {
 
 constexpr int kNgramChunk = 4096;
 constexpr int kMaxNgramDraft = 1024;  // k <= 1024 (checked on the host)
+constexpr int kNgramStage = kNgramChunk + kMaxWindow + kMaxNgramDraft;
+constexpr int kStageVecs = (kNgramStage / 4 + kBlock - 1) / kBlock;  // 16-byte loads per thread
+
+// dst[0, n) = src[0, n): the 16-byte-aligned middle with every thread's loads
+// issued at once (one load round), the unaligned head and tail element-wise.
+__device__ __forceinline__ void stage_tokens(int32_t* dst, const int32_t* src, int n) {
+  const int mis = static_cast<int>((reinterpret_cast<uintptr_t>(src) >> 2) & 3);
+  const int head = min(mis != 0 ? 4 - mis : 0, n);
+  const int nv = (n - head) / 4;
+  const int4* vs = reinterpret_cast<const int4*>(src + head);
+  int4 w[kStageVecs];
+#pragma unroll
+  for (int u = 0; u < kStageVecs; ++u) {
+    const int v = threadIdx.x + u * kBlock;
+    if (v < nv) w[u] = vs[v];
+  }
+  const int tail = head + 4 * nv;
+  const int32_t e = threadIdx.x < head ? src[threadIdx.x]
+                                       : (threadIdx.x < head + n - tail ? src[tail + threadIdx.x - head] : 0);
+#pragma unroll
+  for (int u = 0; u < kStageVecs; ++u) {
+    const int v = threadIdx.x + u * kBlock;
+    if (v < nv) {
+      int32_t* d = dst + head + 4 * v;
+      d[0] = w[u].x;
+      d[1] = w[u].y;
+      d[2] = w[u].z;
+      d[3] = w[u].w;
+    }
+  }
+  if (threadIdx.x < head) dst[threadIdx.x] = e;
+  else if (threadIdx.x < head + n - tail) dst[tail + threadIdx.x - head] = e;
+}
 
 __global__ __launch_bounds__(kBlock) void k_ngram(const int32_t* __restrict__ ctx,
                                                   const int32_t* __restrict__ ctx_len, int32_t stride,
                                                   int32_t window, int32_t k, int32_t* __restrict__ ids,
                                                   int32_t* __restrict__ lens, int32_t* status) {
-  __shared__ int32_t s_tok[kNgramChunk + kMaxWindow + kMaxNgramDraft];
+  __shared__ int32_t s_tok[kNgramStage];
   __shared__ int s_lo, s_end;  // tokens [s_lo, s_end) of the last staged chunk
   __shared__ int32_t s_key[kMaxWindow];
   __shared__ int s_best;
@@ -55,7 +89,7 @@ __global__ __launch_bounds__(kBlock) void k_ngram(const int32_t* __restrict__ ct
       // tokens [lo, hi + window + k) within the context: the windows of the
       // chunk's starts and what follows the newest of them
       const int end = hi + window + k < n ? hi + window + k : n;
-      for (int i = tid; i < end - lo; i += kBlock) s_tok[i] = row[lo + i];
+      stage_tokens(s_tok, row + lo, end - lo);
       if (tid == 0) {
         s_lo = lo;
         s_end = end;
