@@ -16,15 +16,19 @@
 //   rows; every thread keeps the K best (value, id) keys of its elements in
 //   registers (key = order-preserving bits of the clamped value << 32 | ~id,
 //   so one unsigned compare ranks larger values first and lower ids first
-//   among equals); the block then extracts its k best keys in k rounds of a
-//   block max.
+//   among equals), only for elements at or above a threshold taken from the
+//   threads' maxima; each wave then extracts its k best keys and one wave the
+//   block's k best of those.
 // k_tree_round: one block per request: merges each expanded row's segment
 //   keys into its k children, appends them (parent value times confidence,
 //   in fp64), and ranks the appended candidates for the next frontier.
 // k_tree_finalize: one block per request (one thread per candidate): rank by
 //   (-value, depth, creation order), keep the best, flatten depth by depth by
 //   (parent's flat index, -confidence, token, creation order), write the flat
-//   arrays and the ancestor mask.
+//   arrays and the ancestor mask.  The pairwise counts (rank; rank among kept
+//   siblings) are split over all threads of the block; a node's flat index is
+//   the first index of its parent's kept children plus its sibling rank, and
+//   those first indices come from one wave's scan per depth.
 #include <algorithm>
 
 #include "common.hpp"
@@ -89,6 +93,22 @@ __device__ __forceinline__ float wave_max_f32(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
 }
 
+// Inclusive prefix sum of an int over the wave's lanes (DPP row shifts and
+// row broadcasts, no LDS round trip).
+template <int ctrl, int row_mask>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, ctrl, row_mask, 0xf, false);
+}
+__device__ __forceinline__ int wave_incl_scan_i(int x) {
+  x += dpp_i<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_i<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_i<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_i<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_i<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_i<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
 // Insert key into the descending list top[0..K) (the smallest falls off).
 template <int K>
 __device__ __forceinline__ void list_insert(uint64_t (&top)[K], uint64_t key) {
@@ -150,7 +170,7 @@ __device__ __forceinline__ float block_kth_largest(float m, int k, float* s_tk) 
 template <class D, int K>
 __global__ __launch_bounds__(kBlock) void k_topk_partial(const void* __restrict__ rows, int64_t V, int32_t nseg,
                                                          int32_t k, uint64_t* __restrict__ keys) {
-  __shared__ uint64_t s_w[kBlock / kWave];
+  __shared__ uint64_t s_w[kBlock / kWave * kMaxTreeTop];
   __shared__ float s_tk[kWave + 1];
   const int64_t row = blockIdx.x / nseg;
   const int32_t seg = blockIdx.x - static_cast<int32_t>(row) * nseg;
@@ -159,14 +179,20 @@ __global__ __launch_bounds__(kBlock) void k_topk_partial(const void* __restrict_
   const int64_t nvec = (V - head) / D::kPerVec;
   const int64_t v0 = nvec * seg / nseg, v1 = nvec * (seg + 1) / nseg;
   const uint4* vp = reinterpret_cast<const uint4*>(static_cast<const char*>(base) + head * D::kSize);
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
 
   uint64_t top[K];
 #pragma unroll
   for (int j = 0; j < K; ++j) top[j] = 0;  // below every real key
   // Chunks of U vectors per thread, all loads in flight.  After the first
   // chunk the block knows a threshold T: the k-th largest of its threads'
-  // maxima, so at least k of its elements are >= T and no element below T
-  // can be among its k best.  Only elements >= T form keys.
+  // largest confidences, so at least k of its elements have a confidence
+  // >= T and no element below T can be among its k best.  Only elements at
+  // or above T form keys.  Confidences are clamped raw values, and clamping
+  // commutes with the maximum (fmaxf skips NaN, whose confidence 0 is the
+  // floor anyway), so the thread maximum is taken on the raw values; with
+  // T > 0 an element passes iff its raw value is >= T (NaN fails), with T <= 0
+  // every element passes.
   constexpr int U = 8;
   const int64_t nchunk = (v1 - v0 + U * kBlock - 1) / (U * kBlock);
   float T = -1.f;
@@ -186,10 +212,13 @@ __global__ __launch_bounds__(kBlock) void k_topk_partial(const void* __restrict_
         float x[D::kPerVec];
         D::unpack(w[j], x);
 #pragma unroll
-        for (int t = 0; t < D::kPerVec; ++t) m = fmaxf(m, conf_of(x[t]));
+        for (int t = 0; t < D::kPerVec; ++t) m = fmaxf(m, x[t]);
       }
-      T = block_kth_largest(m, k, s_tk);
+      // the thread's largest confidence; -1 for a thread with no elements
+      const float mc = v < v1 ? fminf(fmaxf(m, 0.f), 1.f) : -1.f;
+      T = block_kth_largest(mc, k, s_tk);
     }
+    const bool every = !(T > 0.f);
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const int64_t vv = v + j * kBlock;
@@ -197,10 +226,8 @@ __global__ __launch_bounds__(kBlock) void k_topk_partial(const void* __restrict_
       float x[D::kPerVec];
       D::unpack(w[j], x);
 #pragma unroll
-      for (int t = 0; t < D::kPerVec; ++t) {
-        const float c = conf_of(x[t]);
-        if (c >= T) list_insert<K>(top, conf_key(c, head + vv * D::kPerVec + t));
-      }
+      for (int t = 0; t < D::kPerVec; ++t)
+        if (every || x[t] >= T) list_insert<K>(top, conf_key(conf_of(x[t]), head + vv * D::kPerVec + t));
     }
   }
   if (seg == 0)
@@ -209,22 +236,27 @@ __global__ __launch_bounds__(kBlock) void k_topk_partial(const void* __restrict_
     for (int64_t i = head + nvec * D::kPerVec + threadIdx.x; i < V; i += kBlock)
       list_insert<K>(top, conf_key(conf_of(D::at(base, i)), i));
 
-  // the block's k best: k rounds of a block max over the threads' list heads
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  uint64_t* out = keys + static_cast<int64_t>(blockIdx.x) * k;
+  // the block's k best: each wave's k best (k rounds of a wave max over its
+  // threads' list heads), then the k best of those in wave 0
   for (int r = 0; r < k; ++r) {
     const uint64_t m = wave_max_u64(top[0]);
-    if (lane == 0) s_w[wid] = m;
-    __syncthreads();
-    uint64_t bm = s_w[0];
-    for (int w = 1; w < kBlock / kWave; ++w) bm = max_u64(bm, s_w[w]);
-    if (top[0] == bm && bm != 0) {  // keys are distinct: one owner
+    if (top[0] == m && m != 0) {  // keys are distinct: one owner
 #pragma unroll
       for (int j = 0; j + 1 < K; ++j) top[j] = top[j + 1];
       top[K - 1] = 0;
     }
-    if (threadIdx.x == 0) out[r] = bm;
-    __syncthreads();
+    if (lane == 0) s_w[wid * k + r] = m;
+  }
+  __syncthreads();
+  if (wid == 0) {
+    static_assert(kBlock / kWave * kMaxTreeTop <= kWave, "one lane per wave key");
+    uint64_t x = lane < kBlock / kWave * k ? s_w[lane] : 0;
+    uint64_t* out = keys + static_cast<int64_t>(blockIdx.x) * k;
+    for (int r = 0; r < k; ++r) {
+      const uint64_t m = wave_max_u64(x);
+      if (x == m) x = 0;
+      if (lane == 0) out[r] = m;
+    }
   }
 }
 
@@ -298,11 +330,13 @@ __global__ __launch_bounds__(kBlock) void k_tree_round(TreeRoundArgs a) {
     }
     const double pv = a.value[c0 + node];
     const int pd = a.depth[c0 + node];
+    const int used = (nk + kWave - 1) / kWave;  // registers of kv holding keys
     uint64_t thr = ~0ull;
     for (int r = 0; r < k; ++r) {  // r-th best key of the row: the largest below the previous one
       uint64_t m = 0;
 #pragma unroll
-      for (int j = 0; j < kPerLane; ++j) m = kv[j] < thr ? max_u64(m, kv[j]) : m;
+      for (int j = 0; j < kPerLane; ++j)
+        if (j < used) m = kv[j] < thr ? max_u64(m, kv[j]) : m;
       m = wave_max_u64(m);
       thr = m;
       if (lane == 0) {
@@ -335,21 +369,22 @@ __global__ __launch_bounds__(kBlock) void k_tree_round(TreeRoundArgs a) {
   if (tid == 0) a.count[b] = base + n_app;
 }
 
-// Exclusive scan of one int per thread over a block of kMaxTreeCand threads
-// (wave scans, then the wave totals); valid in every thread.
-__device__ __forceinline__ int block_excl_scan(int v, int* s_tot) {
-  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
-  int x = v;
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int y = __shfl_up(x, off, kWave);
-    if (lane >= off) x += y;
-  }
-  if (lane == kWave - 1) s_tot[wid] = x;
-  __syncthreads();
-  int before = 0;
-  for (int w = 0; w < wid; ++w) before += s_tot[w];
-  return before + x - v;
+// Pairwise counts split over the block: candidate c (1 <= c < M) is handled
+// by P = kMaxTreeCand / (M - 1) threads, each over a contiguous part of
+// j = 1 .. M - 1; `count(c, j0, j1)` returns how many j in [j0, j1) come
+// before c, and the parts are added into s_cnt[c] (zeroed by the caller).
+template <class Count>
+__device__ __forceinline__ void split_count(int M, int* s_cnt, Count count) {
+  const int nc = M - 1;
+  if (nc <= 0) return;
+  const int P = max(1, kMaxTreeCand / nc);
+  const int ci = static_cast<int>(threadIdx.x) / P, part = static_cast<int>(threadIdx.x) - ci * P;
+  if (ci >= nc) return;
+  const int chunk = (nc + P - 1) / P;
+  const int j0 = 1 + part * chunk, j1 = min(M, j0 + chunk);
+  if (j0 >= j1) return;
+  const int r = count(1 + ci, j0, j1);
+  if (r != 0) atomicAdd(&s_cnt[1 + ci], r);
 }
 
 __global__ __launch_bounds__(kMaxTreeCand) void k_tree_finalize(TreeFinalArgs a) {
@@ -357,13 +392,14 @@ __global__ __launch_bounds__(kMaxTreeCand) void k_tree_finalize(TreeFinalArgs a)
   __shared__ float s_conf[kMaxTreeCand];
   __shared__ int s_dep[kMaxTreeCand], s_par[kMaxTreeCand], s_tok[kMaxTreeCand], s_flat[kMaxTreeCand];
   __shared__ int s_of[kMaxTreeCand];    // candidate at each flat index
-  __shared__ int s_pf[kMaxTreeCand];    // parent's flat index, set while a depth is placed
-  __shared__ int s_list[kMaxTreeCand];  // kept candidates grouped by depth
+  __shared__ int s_rank[kMaxTreeCand];  // candidates ranked before (value, depth, creation order)
+  __shared__ int s_sib[kMaxTreeCand];   // kept siblings placed before (confidence, token, creation order)
+  __shared__ int s_nk[kMaxTreeCand];    // kept children
+  __shared__ int s_cst[kMaxTreeCand];   // flat index of the first kept child
   __shared__ int s_dcnt[kMaxTreeCand];  // kept candidates per depth
-  __shared__ int s_doff[kMaxTreeCand];  // flat index of each depth's first node
-  __shared__ int s_wtot[kMaxTreeCand / kWave];
-  __shared__ int s_maxd;
+  __shared__ unsigned char s_kept[kMaxTreeCand];
   const int b = blockIdx.x, i = threadIdx.x;
+  const int lane = i & (kWave - 1), wid = i / kWave;
   const int64_t c0 = static_cast<int64_t>(b) * a.max_cand;
   const int M = a.count[b];
   const int N = a.n_nodes;
@@ -384,70 +420,86 @@ __global__ __launch_bounds__(kMaxTreeCand) void k_tree_finalize(TreeFinalArgs a)
     s_par[i] = a.parent[c0 + i];
     s_tok[i] = a.token[c0 + i];
   }
-  s_dcnt[i] = 0;
-  if (i == 0) s_maxd = 0;
+  s_rank[i] = s_sib[i] = s_nk[i] = s_dcnt[i] = 0;
+  s_of[i] = s_flat[i] = -1;
+  s_cst[i] = -2 * kMaxTreeCand;  // no place until the node's own place is known
   __syncthreads();
   // kept: the root and the best N - 1 others by (-value, depth, creation
-  // order); the comparisons are branch-free so the loads pipeline
-  bool kept = i == 0;
-  if (i > 0 && i < M) {
-    const double vi = s_val[i];
-    const int di = s_dep[i];
-    int rank = 0;
-#pragma unroll 8
-    for (int j = 1; j < M; ++j) {
+  // order)
+  split_count(M, s_rank, [&](int c, int j0, int j1) {
+    const double vc = s_val[c];
+    const int dc = s_dep[c];
+    int r = 0;
+    for (int j = j0; j < j1; ++j) {
       const double vj = s_val[j];
       const int dj = s_dep[j];
-      rank += (vj > vi) | ((vj == vi) & ((dj < di) | ((dj == di) & (j < i))));
+      r += (vj > vc) | ((vj == vc) & ((dj < dc) | ((dj == dc) & (j < c))));
     }
-    kept = rank < N - 1;
-  }
-  int slot = 0;
-  if (kept) {
-    slot = atomicAdd(&s_dcnt[s_dep[i]], 1);
-    atomicMax(&s_maxd, s_dep[i]);
+    return r;
+  });
+  __syncthreads();
+  const bool kept = i == 0 || (i < M && s_rank[i] < N - 1);
+  s_kept[i] = kept ? 1 : 0;
+  if (kept && i > 0) {  // (a parent precedes its children)
+    const int p = s_par[i], d = s_dep[i];
+    if (p >= 0 && p < i) atomicAdd(&s_nk[p], 1);
+    if (d >= 1 && d < kMaxTreeCand) atomicAdd(&s_dcnt[d], 1);
   }
   __syncthreads();
-  const int maxd = s_maxd;
-  const int off = block_excl_scan(s_dcnt[i], s_wtot);  // depth i's first flat index
-  s_doff[i] = off;
-  __syncthreads();
-  if (kept) s_list[s_doff[s_dep[i]] + slot] = i;
+  // breadth-first order: a depth's nodes by (parent's flat index,
+  // -confidence, token, creation order), so a node's place is the first
+  // place of its parent's children plus its rank among its kept siblings
+  split_count(M, s_sib, [&](int c, int j0, int j1) {
+    if (!s_kept[c]) return 0;
+    const int pc = s_par[c], tc = s_tok[c];
+    const float cc = s_conf[c];
+    int r = 0;
+    for (int j = j0; j < j1; ++j) {
+      const float cj = s_conf[j];
+      const int tj = s_tok[j];
+      r += (s_kept[j] != 0) & (s_par[j] == pc) &
+           ((cj > cc) | ((cj == cc) & ((tj < tc) | ((tj == tc) & (j < c)))));
+    }
+    return r;
+  });
   if (i == 0) {
     s_flat[0] = 0;
     s_of[0] = 0;
+    s_cst[0] = 1;
   }
   __syncthreads();
-  // flatten depth by depth: within a depth by (parent's flat index,
-  // -confidence, token, creation order) among that depth's kept nodes
-  const bool placed = kept && i > 0;
-  for (int d = 1; d <= maxd; ++d) {
-    const bool mine = placed && s_dep[i] == d;
-    const int pf = mine ? s_flat[s_par[i]] : 0;
-    if (mine) s_pf[i] = pf;
-    __syncthreads();
-    if (mine) {
-      const int lo = s_doff[d], cnt = s_dcnt[d];
-      const float ci = s_conf[i];
-      const int ti = s_tok[i];
-      int r = 0;
-#pragma unroll 4
-      for (int q = 0; q < cnt; ++q) {
-        const int j = s_list[lo + q];
-        const int pj = s_pf[j];
-        const float cj = s_conf[j];
-        const int tj = s_tok[j];
-        r += (pj < pf) | ((pj == pf) & ((cj > ci) | ((cj == ci) & ((tj < ti) | ((tj == ti) & (j < i))))));
+  const int n = M < N ? M : N;  // kept nodes
+  int off = 1;  // flat index of depth d's first node
+  // the kept set is connected, so its depths run 1, 2, ... without a gap
+  for (int d = 1; d < n; ++d) {
+    const int cnt = s_dcnt[d];
+    if (cnt == 0) break;
+    if (kept && i > 0 && s_dep[i] == d && s_par[i] >= 0 && s_par[i] < i) {
+      const int f = s_cst[s_par[i]] + s_sib[i];
+      if (f > 0 && f < n) {
+        s_flat[i] = f;
+        s_of[f] = i;
       }
-      s_flat[i] = lo + r;
-      s_of[lo + r] = i;
     }
     __syncthreads();
+    // first child places of depth d's nodes: after depth d, in their order
+    if (wid == 0) {
+      int carry = off + cnt;
+      for (int f0 = off; f0 < off + cnt; f0 += kWave) {
+        const int f = f0 + lane;
+        const int q = f < off + cnt ? s_of[f] : -1;
+        const int v = q >= 0 ? s_nk[q] : 0;
+        const int x = wave_incl_scan_i(v);
+        if (q >= 0) s_cst[q] = carry + x - v;
+        carry += __builtin_amdgcn_readlane(x, kWave - 1);
+      }
+    }
+    __syncthreads();
+    off += cnt;
   }
-  const int n = M < N ? M : N;  // kept nodes
   for (int f = i; f < N; f += kMaxTreeCand) {
-    if (f < n) {
-      const int ci = s_of[f];
+    const int ci = f < n ? s_of[f] : -1;
+    if (ci >= 0) {
       a.out_parent[o + f] = ci == 0 ? -1 : s_flat[s_par[ci]];
       a.out_token[o + f] = s_tok[ci];
       a.out_depth[o + f] = s_dep[ci];
@@ -463,10 +515,10 @@ __global__ __launch_bounds__(kMaxTreeCand) void k_tree_finalize(TreeFinalArgs a)
       for (int j = 0; j < N; ++j) row[j] = 0;
       if (f < n) {
         int g = f;
-        while (g >= 0) {
+        for (int step = 0; step < n && g >= 0 && g < n; ++step) {
           row[g] = 1;
           const int cg = s_of[g];
-          g = cg == 0 ? -1 : s_flat[s_par[cg]];
+          g = cg <= 0 ? -1 : s_flat[s_par[cg]];
         }
       }
     }
