@@ -57,6 +57,15 @@ def _i32(a, torch, dev):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
 
 
+# Input sets rotate so that a set is read again only after more than twice the
+# 256 MB MALL of other sets has streamed through: n copies of `touched` bytes.
+MALL_BYTES = 256 << 20
+
+
+def rotation(touched):
+    return max(2, -(-2 * MALL_BYTES // max(int(touched), 1)))
+
+
 def chain_formula_bytes(ci):
     """Logit rows read once + draft rows + draft ids + uniforms."""
     st = 4 if ci.t_kind == "f32" else 2
@@ -372,11 +381,15 @@ def main():
                torch.empty((B,), dtype=torch.int32, device=dev), torch.empty((B, N), dtype=torch.int32, device=dev),
                None)
 
-        launch = sv.prepare(sv.sv_verify_tree, d["tgt"], d["dft"], d["par"], d["tok"], ti.T, d["u"],
-                            workspace=ws, out=out)[0]
+        # a round reads the visited nodes' target rows and the rejected children's
+        # draft rows (~15 MB): device copies of both row sets rotate
+        nset = rotation(15 << 20)
+        copies = [(d["tgt"], d["dft"])] + [(d["tgt"].clone(), d["dft"].clone()) for _ in range(nset - 1)]
+        launches = [sv.prepare(sv.sv_verify_tree, t, q, d["par"], d["tok"], ti.T, d["u"], workspace=ws, out=out)[0]
+                    for t, q in copies]
 
         def step(i):
-            launch()
+            launches[i % nset]()
 
         wall, tot_ms, ev_ms = timed(step, args.steps, args.warmup, torch)
         ms = 1e3 * wall / args.steps
@@ -389,7 +402,7 @@ def main():
         result.update(value=round(B / (ms * 1e-3), 1), unit="rounds/s", ms_per_step=round(ms, 5),
                       config=dict(workload="tree verify: 32 requests, 60-node draft trees (depth <= 6, "
                                            "branching <= 4), V=128,256, bf16, T=1", batch=32, nodes=60,
-                                  vocab=128_256, temperature=1.0, inputs="bf16"),
+                                  vocab=128_256, temperature=1.0, inputs="bf16", input_sets=nset),
                       tokens_per_s=round(float(out[1].sum().item()) / (ms * 1e-3), 1),
                       formula_bytes_per_step=fb, formula_GBps=round(fb / (ms * 1e-3) / 1e9, 1),
                       visited_target_row_bytes=visited_bytes,
@@ -408,15 +421,19 @@ def main():
         B, N = ti.parent.shape
         out = (torch.empty((B, N), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev),
                torch.empty((B,), dtype=torch.int32, device=dev), torch.empty((B, N), dtype=torch.int32, device=dev))
+        # a round reads the visited nodes' target rows (~11 MB): device copies rotate
+        nset = rotation(11 << 20)
+        tgts = [tgt] + [tgt.clone() for _ in range(nset - 1)]
         if W == "c5g":
-            launch = sv.prepare(sv.sv_verify_tree_greedy, tgt, par, tok, workspace=ws, out=out)[0]
+            launches = [sv.prepare(sv.sv_verify_tree_greedy, t, par, tok, workspace=ws, out=out)[0] for t in tgts]
             name = "greedy tree verify (argmax picks)"
         else:
-            launch = sv.prepare(sv.sv_verify_tree_pointmass, tgt, par, tok, ti.T, u, workspace=ws, out=out)[0]
+            launches = [sv.prepare(sv.sv_verify_tree_pointmass, t, par, tok, ti.T, u, workspace=ws, out=out)[0]
+                        for t in tgts]
             name = "point-mass tree verify (each candidate tested as a point mass)"
 
         def step(i):
-            launch()
+            launches[i % nset]()
 
         wall, tot_ms, ev_ms = timed(step, args.steps, args.warmup, torch)
         ms = 1e3 * wall / args.steps
@@ -425,7 +442,7 @@ def main():
         result.update(value=round(B / (ms * 1e-3), 1), unit="rounds/s", ms_per_step=round(ms, 5),
                       config=dict(workload=f"{name}: 32 requests, 60-node draft trees (depth <= 6, "
                                            "branching <= 4), V=128,256, bf16 target rows, T=1", batch=32,
-                                  nodes=60, vocab=128_256, temperature=1.0, inputs="bf16"),
+                                  nodes=60, vocab=128_256, temperature=1.0, inputs="bf16", input_sets=nset),
                       tokens_per_s=round(float(out[1].sum().item()) / (ms * 1e-3), 1),
                       mean_tokens_per_round=round(float(out[1].float().mean().item()), 4),
                       visited_target_row_bytes=visited_bytes,
@@ -461,26 +478,30 @@ def main():
         for g in range(G):
             sv.sv_shard_draw(cols[g][0], cols[g][1], bounds, g, trs, qrs, ids, dl, ci.T, u, all_pairs, mass, out,
                              workspace=wss[g])
-        tg, qg = cols[0]
-        calls = [sv.prepare(sv.sv_shard_stats, tg, qg, bounds, 0, trs, qrs, ids, dl, ci.T, out=st1[0],
-                            workspace=wss[0])[0],
-                 sv.prepare(sv.sv_shard_residual, tg, qg, bounds, 0, trs, qrs, ids, dl, ci.T, u, all_pairs, all_at,
-                            mass, workspace=wss[0])[0],
-                 sv.prepare(sv.sv_shard_draw, tg, qg, bounds, 0, trs, qrs, ids, dl, ci.T, u, all_pairs, mass, out,
-                            workspace=wss[0])[0]]
+        # device copies of shard 0's columns rotate (40 MB a step)
+        share = (bounds[1] - bounds[0]) * 2 * (ci.target.shape[0] + ci.draft.shape[0])
+        nset = rotation(share)
+        calls = []
+        for j in range(nset):
+            tg, qg = cols[0] if j == 0 else (cols[0][0].clone(), cols[0][1].clone())
+            calls.append([sv.prepare(sv.sv_shard_stats, tg, qg, bounds, 0, trs, qrs, ids, dl, ci.T, out=st1[0],
+                                     workspace=wss[0])[0],
+                          sv.prepare(sv.sv_shard_residual, tg, qg, bounds, 0, trs, qrs, ids, dl, ci.T, u, all_pairs,
+                                     all_at, mass, workspace=wss[0])[0],
+                          sv.prepare(sv.sv_shard_draw, tg, qg, bounds, 0, trs, qrs, ids, dl, ci.T, u, all_pairs, mass,
+                                     out, workspace=wss[0])[0]])
 
         def step(i):
-            for c in calls:
+            for c in calls[i % nset]:
                 c()
 
         wall, tot_ms, ev_ms = timed(step, args.steps, args.warmup, torch)
         ms = 1e3 * wall / args.steps
-        share = (bounds[1] - bounds[0]) * 2 * (ci.target.shape[0] + ci.draft.shape[0])
         result.update(value=round(B / (ms * 1e-3), 1), unit="rounds/s", ms_per_step=round(ms, 5),
                       config=dict(workload="sampled chain verify on one of 8 vocabulary shards: 64 requests, k=4, "
                                            "31,040 of V=248,320 columns per device, bf16, T=0.7 (the three shard "
                                            "steps of one device; the all-gathers between them not included)",
-                                  batch=B, k=k, vocab=V, shards=G, inputs="bf16"),
+                                  batch=B, k=k, vocab=V, shards=G, inputs="bf16", input_sets=nset),
                       shard_bytes=share,
                       event_ms_per_step=dict(timed_region=round(tot_ms / args.steps, 5),
                                              p50=round(float(np.percentile(ev_ms, 50)), 5)),
@@ -505,24 +526,27 @@ def main():
         nexts = [torch.empty((B, exp), dtype=torch.int32, device=dev) for _ in range(depth)]
         outs = ([torch.empty((B, N), dtype=torch.int32, device=dev) for _ in range(4)]
                 + [torch.empty((B, N, N), dtype=torch.uint8, device=dev)])
+        # device copies of the draft rows rotate (172 MB a build)
+        row_bytes = sum(int(t.numel()) * 2 for t in rounds)
+        nset = rotation(row_bytes)
+        sets = [rounds] + [[t.clone() for t in rounds] for _ in range(nset - 1)]
+        fin = sv.prepare(sv.sv_tree_finalize, state, N, out=outs)[0]
         calls = []
-        for r in range(depth):
-            calls.append(sv.prepare(sv.sv_tree_expand, rounds[r], None if r == 0 else nexts[r - 1], top, exp,
-                                    state, next_exp=nexts[r], workspace=ws)[0])
-        calls.append(sv.prepare(sv.sv_tree_finalize, state, N, out=outs)[0])
+        for rs in sets:
+            calls.append([sv.prepare(sv.sv_tree_expand, rs[r], None if r == 0 else nexts[r - 1], top, exp,
+                                     state, next_exp=nexts[r], workspace=ws)[0] for r in range(depth)] + [fin])
 
         def step(i):
-            for c in calls:
+            for c in calls[i % nset]:
                 c()
 
         wall, tot_ms, ev_ms = timed(step, args.steps, args.warmup, torch)
         ms = 1e3 * wall / args.steps
-        row_bytes = sum(int(t.numel()) * 2 for t in rounds)
         result.update(value=round(B / (ms * 1e-3), 1), unit="trees/s", ms_per_step=round(ms, 5),
                       config=dict(workload="EAGLE-2 draft tree built on the device: 32 requests, V=128,256 bf16 "
                                            "draft rows, top 4 children, 4 nodes expanded per round, 6 rounds, "
                                            "60 nodes kept, ancestor mask", batch=B, vocab=V, top_children=top,
-                                  expand_per_round=exp, rounds=depth, nodes=N, inputs="bf16"),
+                                  expand_per_round=exp, rounds=depth, nodes=N, inputs="bf16", input_sets=nset),
                       draft_row_bytes_per_step=row_bytes,
                       row_GBps=round(row_bytes / (ms * 1e-3) / 1e9, 1),
                       event_ms_per_step=dict(timed_region=round(tot_ms / args.steps, 5),
@@ -537,10 +561,16 @@ def main():
         trs = _i32(np.arange(g.B) * (g.k + 1), torch, dev)
         ws = sv.Workspace(dev)
 
-        draft, (ids, lens) = sv.prepare(sv.sv_ngram_draft, ctx, cl, g.window, g.k)
-        verify = sv.prepare(sv.sv_verify_greedy, tgt, trs, ids, lens, workspace=ws)[0]
+        # device copies of the contexts and target rows rotate (21.5 MB a step)
+        nset = rotation(g.target.size * 2 + g.ctx.size * 4)
+        pairs = []
+        for j in range(nset):
+            c_j, t_j = (ctx, tgt) if j == 0 else (ctx.clone(), tgt.clone())
+            draft, (ids, lens) = sv.prepare(sv.sv_ngram_draft, c_j, cl, g.window, g.k)
+            pairs.append((draft, sv.prepare(sv.sv_verify_greedy, t_j, trs, ids, lens, workspace=ws)[0]))
 
         def step(i):
+            draft, verify = pairs[i % nset]
             draft()
             verify()
 
@@ -550,7 +580,7 @@ def main():
         result.update(value=round(g.B / (ms * 1e-3), 1), unit="rounds/s", ms_per_step=round(ms, 5),
                       config=dict(workload="prompt-lookup draft + greedy verify: 64 requests, contexts of "
                                            "4,096 tokens, window 3, k=4, V=32,000, bf16", batch=64, k=4,
-                                  vocab=32_000, inputs="bf16"),
+                                  vocab=32_000, inputs="bf16", input_sets=nset),
                       formula_bytes_per_step=fb, formula_GBps=round(fb / (ms * 1e-3) / 1e9, 1),
                       dtype="int32+f32", roofline=None)
     print(json.dumps(result), flush=True)

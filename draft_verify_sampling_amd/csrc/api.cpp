@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -50,6 +51,25 @@ sv_status check_workspace(const void* ws, size_t have, size_t need) {
 }
 
 constexpr int64_t kMaxGrid = 0x7fffffff;
+
+// A 64-bit value that no earlier call of this process has used, never 0: the
+// tree walks' per-call ticket.  The start is mixed from the clock and an
+// address (SplitMix64 finaliser), so another process's leftovers in a reused
+// allocation match a ticket only by a 2^-64 chance.
+uint64_t next_ticket() {
+  static std::atomic<uint64_t> next{[] {
+    uint64_t z = static_cast<uint64_t>(std::chrono::steady_clock::now().time_since_epoch().count()) ^
+                 reinterpret_cast<uintptr_t>(&g_err);
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
+  }()};
+  uint64_t t;
+  do {
+    t = next.fetch_add(1, std::memory_order_relaxed);
+  } while (t == 0);
+  return t;
+}
 
 // Compute units of the current device (cached per device; 0 if unknown).
 int cu_count() {
@@ -154,6 +174,17 @@ sv_status launch_walk_call(int mode, int32_t t_dtype, int32_t q_dtype, sv::WalkA
     if (e != hipSuccess) return device_fail(e, what);
     if (chain) stat_event(1, st);
     clear_slots = false;  // the statistics kernel zeroed the exchange words
+  }
+  // Tree walks zero their own exchange words, certified by a ticket unique to
+  // the call.  A captured call would replay one ticket, so under stream
+  // capture the words are zeroed by a kernel before the walk instead.
+  a.arrive = nullptr;
+  a.ticket = 0;
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusActive;
+  if (!chain && a.G > 1 && hipStreamIsCapturing(st, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone) {
+    a.arrive = reinterpret_cast<uint64_t*>(ws + L.arrive_off);
+    a.ticket = next_ticket();
+    clear_slots = false;
   }
   const size_t lds = sv::walk_lds_bytes(a.node_cap, a.tile_cap);
   const hipError_t e = sv::launch_walk(mode, t_dtype, q_dtype, a, lds, clear_slots, st);

@@ -38,9 +38,13 @@
 // through 64-bit words in the workspace: each workgroup stores its words with
 // relaxed agent-scope atomic stores and reads the others' with relaxed
 // agent-scope atomic loads until all carry their valid bit.  The data travels
-// inside the atomic words, so no fence is needed; k_walk_clear zeroes the
-// words before the walk.  Every workgroup combines the G words in the same
-// order, so all of them take the same decisions.  The wait is bounded: on
+// inside the atomic words, so no fence is needed.  The words start at zero:
+// for a chain the statistics kernel (or k_walk_clear) zeroes them before the
+// walk; in a tree walk each workgroup zeroes its own words at its start,
+// waits until those stores have completed, and then stores the call's
+// ticket, and the request's first exchange polls the G tickets before any
+// word, so no word left by an earlier call is read.  Every workgroup combines
+// the G words in the same order, so all of them take the same decisions.  The wait is bounded: on
 // expiry the workgroup sets the sync-timeout status bit and exits.  With G = 1
 // nothing is exchanged through memory.
 //
@@ -97,7 +101,17 @@ __device__ bool exchange(Walk& wk, uint64_t w0, uint64_t w1) {
       const int n = 2 * a.G;
       uint64_t v = 0;
       int done = 0;
-      for (int it = 0; it < a.spin_limit; ++it) {
+      int it = 0;
+      if (wk.nsync == 0 && a.arrive != nullptr) {
+        // the tickets first: a workgroup's words are read only once its
+        // zeroing of them has completed (the polls share one budget)
+        const uint64_t* arr = a.arrive + static_cast<int64_t>(wk.b) * a.G;
+        for (; it < a.spin_limit; ++it) {
+          if (__all(lane >= a.G || load_word(arr + lane) == a.ticket)) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      for (; it < a.spin_limit; ++it) {
         if (lane < n) v = load_word(row + lane);
         if (__all(lane >= n || (v & kValid) != 0)) {
           done = 1;
@@ -380,9 +394,15 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
       }
     }
   } else {
-    // round 1: the tree and the uniforms (the greedy walk has none)
+    // round 1: the tree and the uniforms (the greedy walk has none); this
+    // workgroup's exchange words are zeroed meanwhile
     N = a.N;
     trow0 = qrow0 = static_cast<int64_t>(b) * a.N;
+    if (a.arrive != nullptr) {
+      uint64_t* own = a.slots + static_cast<int64_t>(b) * a.max_sync * 2 * a.G + 2 * wk.g;
+      for (int j = tid; j < 2 * a.max_sync; j += kWalkBlock)
+        store_word(own + static_cast<int64_t>(j >> 1) * 2 * a.G + (j & 1), 0ull);
+    }
     __syncthreads();
     for (int c = tid; c < N; c += kWalkBlock) {
       const int par = a.parent[trow0 + c];
@@ -395,7 +415,11 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
       s_tok[c] = tok;
       s_u[c] = kGreedy ? 0.f : slot_uniform(a.u, a.seed, a.offset, b, N, c);
     }
+    // every thread's zeroing stores have completed before the barrier, so
+    // the ticket stored after it certifies them
+    if (a.arrive != nullptr) asm volatile("s_waitcnt vmcnt(0)");
     __syncthreads();
+    if (a.arrive != nullptr && tid == 0) store_word(a.arrive + static_cast<int64_t>(b) * a.G + wk.g, a.ticket);
     if (const int bad = s_bad) {
       if (wk.g == 0) walk_invalid<kChain>(a, b, (bad & kFlagBadTree) ? kFlagBadTree : bad, tid, kWalkBlock);
       return;

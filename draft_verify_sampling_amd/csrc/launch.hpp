@@ -79,12 +79,13 @@ inline int64_t walk_max_sync(int64_t n_nodes) { return n_nodes + 1; }
 
 // Workspace of the sampled and tree verify, carved per call: softmax
 // partials of every row (shared-row chains and diagnostics), then the walk's
-// exchange words [B, max_sync, 2 G], then the lazy chain statistics: stop
-// words [B], finished-segment counts [B, R], row pairs [B, R] and segment
-// pairs [B, R, nseg] (R = k_max + 1).  Everything from the exchange words on
-// is zeroed before each call.
+// exchange words [B, max_sync, 2 G] and tickets [B, G], then the lazy chain
+// statistics: stop words [B], finished-segment counts [B, R], row pairs
+// [B, R] and segment pairs [B, R, nseg] (R = k_max + 1).  A chain's exchange
+// words and lazy statistics are zeroed before the call's walk; a tree walk's
+// workgroups zero their own exchange words and then store the call's ticket.
 struct WalkLayout {
-  size_t partial_off, slots_off, stop_off, count_off, rows_off, segs_off, end;
+  size_t partial_off, slots_off, arrive_off, stop_off, count_off, rows_off, segs_off, end;
 };
 
 inline WalkLayout walk_layout(int64_t B, int64_t rows, int64_t V, int64_t G, int64_t max_sync,
@@ -93,7 +94,8 @@ inline WalkLayout walk_layout(int64_t B, int64_t rows, int64_t V, int64_t G, int
   const int64_t nseg = row_segments(rows, V);
   L.partial_off = 0;
   L.slots_off = align256(static_cast<size_t>(rows * nseg) * 8);
-  L.stop_off = L.slots_off + align256(G > 1 ? static_cast<size_t>(B * max_sync * 2 * G) * 8 : 0);
+  L.arrive_off = L.slots_off + align256(G > 1 ? static_cast<size_t>(B * max_sync * 2 * G) * 8 : 0);
+  L.stop_off = L.arrive_off + align256(G > 1 ? static_cast<size_t>(B * G) * 8 : 0);
   L.count_off = L.stop_off + align256(static_cast<size_t>(lazy_R > 0 ? B : 0) * 4);
   L.rows_off = L.count_off + align256(static_cast<size_t>(B * lazy_R) * 4);
   L.segs_off = L.rows_off + align256(static_cast<size_t>(B * lazy_R) * 8);
@@ -168,6 +170,11 @@ struct WalkArgs {
   int32_t ntiles;
   int32_t G;
   uint64_t* slots;          // [B, max_sync, 2 G] exchange words (G > 1)
+  // tree walks: each workgroup zeroes its own exchange words, then stores
+  // `ticket` (unique to the call) into arrive[b, g]; the first exchange of a
+  // request waits for all G tickets.  Null: the words were zeroed before.
+  uint64_t* arrive;
+  uint64_t ticket;
   int32_t max_sync;
   int32_t spin_limit;
   int32_t node_cap;         // LDS capacity in nodes (>= nodes of any request)

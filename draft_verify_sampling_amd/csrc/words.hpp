@@ -1,8 +1,9 @@
 // 64-bit words that carry data between workgroups of one kernel: each is
 // stored with a relaxed agent-scope atomic store and polled with relaxed
 // agent-scope atomic loads until its bit 63 is set, so the data itself travels
-// inside the atomic word and no fence is needed.  The words are zeroed before
-// the kernel that writes them.
+// inside the atomic word and no fence is needed.  A word is zero before its
+// writer stores it: zeroed before the kernel, or (tree walks) by its writer,
+// whose completed zeroing a per-call ticket certifies.
 #pragma once
 
 #include "common.hpp"

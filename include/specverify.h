@@ -45,8 +45,10 @@
  * - The caller owns every buffer.  The library allocates nothing, keeps no
  *   pointer after returning, and holds no mutable state that affects results:
  *   only the thread-local text behind sv_last_error(), the thread-local
- *   measurement hook of sv_time_statistics_once(), and per-device caches of
- *   launch parameters (compute-unit counts, kernel occupancy).
+ *   measurement hook of sv_time_statistics_once(), per-device caches of
+ *   launch parameters (compute-unit counts, kernel occupancy), and a
+ *   process-wide counter that gives each tree-walk call a unique 64-bit
+ *   ticket (outputs do not depend on its value).
  * - Row data: `t_dtype` / `q_dtype` select SV_F32 (float) or SV_BF16 (bfloat16
  *   bit patterns).  A row is `vocab` consecutive elements; row r starts at
  *   element r * vocab.  Any alignment is accepted; 16-byte aligned rows take the
