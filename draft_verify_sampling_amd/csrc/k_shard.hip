@@ -27,13 +27,25 @@ namespace {
 constexpr int kShardBlock = 1024;
 constexpr int kShardWaves = kShardBlock / kWave;
 
-// Scaled-domain pair of a row from the G shards' pairs, combined in shard order.
-__device__ __forceinline__ MS shard_combine(const float* all_pairs, int G, int64_t t_rows, int64_t row) {
-  MS acc{-INFINITY, 0.f};
-  for (int g = 0; g < G; ++g) {
-    const float* p = all_pairs + (static_cast<int64_t>(g) * t_rows + row) * 2;
-    acc = ms_combine(acc, MS{p[0], p[1]});
+__device__ __forceinline__ float lane_f(float v, int g) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), g));
+}
+
+__device__ __forceinline__ double lane_d(double v, int g) { return lane_value(v, g); }
+
+// Scaled-domain pair of a row from the G shards' pairs, combined in shard
+// order; valid in every lane of the calling wave.  Lane g loads shard g's pair
+// (one load round), then the wave folds them in shard order.
+__device__ __forceinline__ MS wave_shard_combine(const float* all_pairs, int G, int64_t t_rows, int64_t row) {
+  const int lane = threadIdx.x & (kWave - 1);
+  float pm = -INFINITY, ps = 0.f;
+  if (lane < G) {
+    const float* p = all_pairs + (static_cast<int64_t>(lane) * t_rows + row) * 2;
+    pm = p[0];
+    ps = p[1];
   }
+  MS acc{-INFINITY, 0.f};
+  for (int g = 0; g < G; ++g) acc = ms_combine(acc, MS{lane_f(pm, g), lane_f(ps, g)});
   return acc;
 }
 
@@ -45,36 +57,44 @@ __device__ __forceinline__ int shard_of(const ShardBounds& sb, int64_t x) {
 }
 
 // Emitted tokens of a round (drafts 0..m-1, then y), cut after the first EOS
-// and at the request's budget; one lane writes.
+// and at the request's budget; called by a whole wave (lane i writes slots i,
+// i + 64, ...).
 __device__ void emit_round(const ShardArgs& a, int b, int m, int y, float resid, int flags) {
+  const int lane = threadIdx.x & (kWave - 1);
   const int width = a.k_max + 1;
   int32_t* out = a.out_tok + static_cast<int64_t>(b) * width;
-  int cnt = 0;
-  bool stop = false;
-  for (int i = 0; i < m && !stop; ++i) {
-    const int32_t tok = a.ids[static_cast<int64_t>(b) * a.k_max + i];
-    out[cnt++] = tok;
-    if (a.eos >= 0 && tok == a.eos) stop = true;
+  const int32_t* x = a.ids + static_cast<int64_t>(b) * a.k_max;
+  int stop = m;  // the first EOS among the kept drafts, or m
+  for (int i0 = 0; i0 < m && a.eos >= 0; i0 += kWave) {
+    const int i = i0 + lane;
+    const uint64_t hit = __ballot(i < m && x[i] == a.eos);
+    if (hit != 0) {
+      stop = i0 + __ffsll(static_cast<long long>(hit)) - 1;
+      break;
+    }
   }
-  if (!stop) out[cnt++] = y;
-  if (a.max_new != nullptr) {
-    const int budget = a.max_new[b] > 0 ? a.max_new[b] : 0;
-    if (cnt > budget) cnt = budget;
+  int cnt = stop < m ? stop + 1 : m + 1;
+  if (a.max_new != nullptr) cnt = min(cnt, max(a.max_new[b], 0));
+  for (int i = lane; i < width; i += kWave) out[i] = i < cnt ? (i < m ? x[i] : y) : -1;
+  if (lane == 0) {
+    a.out_cnt[b] = cnt;
+    a.out_acc[b] = m;
+    if (a.resid != nullptr) a.resid[b] = resid;
+    flag(a.status, flags);
   }
-  for (int i = cnt; i < width; ++i) out[i] = -1;
-  a.out_cnt[b] = cnt;
-  a.out_acc[b] = m;
-  if (a.resid != nullptr) a.resid[b] = resid;
-  flag(a.status, flags);
 }
 
+// Outputs of an invalid request; called by a whole wave.
 __device__ void emit_invalid(const ShardArgs& a, int b, int flags) {
+  const int lane = threadIdx.x & (kWave - 1);
   const int width = a.k_max + 1;
-  for (int i = 0; i < width; ++i) a.out_tok[static_cast<int64_t>(b) * width + i] = -1;
-  a.out_cnt[b] = 0;
-  a.out_acc[b] = 0;
-  if (a.resid != nullptr) a.resid[b] = 0.f;
-  flag(a.status, flags);
+  for (int i = lane; i < width; i += kWave) a.out_tok[static_cast<int64_t>(b) * width + i] = -1;
+  if (lane == 0) {
+    a.out_cnt[b] = 0;
+    a.out_acc[b] = 0;
+    if (a.resid != nullptr) a.resid[b] = 0.f;
+    flag(a.status, flags);
+  }
 }
 
 }  // namespace
@@ -136,23 +156,39 @@ __global__ __launch_bounds__(kShardBlock) void k_shard_residual(ShardArgs a) {
     s_bad = 0;
     s_brk = k;
   }
-  if (tid <= k) {
-    const MS st = shard_combine(a.pairs, a.sb.G, a.t_rows, ts + tid);
-    s_m[tid] = st.m;
-    s_S[tid] = st.s;
-  }
   __syncthreads();
-  // accept scan: draft i kept iff u_i q_i(x_i) < p_i(x_i); m = the first not kept
-  if (tid < k) {
-    const int64_t x = a.ids[static_cast<int64_t>(b) * a.k_max + tid];
-    if (x < 0 || x >= a.V) {
-      atomicOr(&s_bad, kFlagBadToken);
-    } else {
-      const int g = shard_of(a.sb, x);
-      const float* v = a.at + ((static_cast<int64_t>(g) * a.B + b) * a.k_max + tid) * 2;
-      const float p = ex2(fmaf(v[0], a.c, -s_m[tid])) * (1.f / s_S[tid]);
-      const float u = slot_uniform(a.u, a.seed, a.offset, b, a.k_max + 1, tid);
-      if (!(u * v[1] < p)) atomicMin(&s_brk, tid);
+  // wave i: row i's pair over the shards and, for i < k, the accept test of
+  // draft i (kept iff u_i q_i(x_i) < p_i(x_i); m = the first not kept); lane g
+  // holds shard g's pair and gathered values, all loaded in one round
+  for (int i = wid; i <= k; i += kShardWaves) {
+    const int G = a.sb.G;
+    float pm = -INFINITY, ps = 0.f, lv = 0.f, qv = 0.f;
+    if (lane < G) {
+      const float* pp = a.pairs + (static_cast<int64_t>(lane) * a.t_rows + ts + i) * 2;
+      pm = pp[0];
+      ps = pp[1];
+      if (i < k) {
+        const float* v = a.at + ((static_cast<int64_t>(lane) * a.B + b) * a.k_max + i) * 2;
+        lv = v[0];
+        qv = v[1];
+      }
+    }
+    const int64_t x = i < k ? a.ids[static_cast<int64_t>(b) * a.k_max + i] : 0;
+    const float u = i < k ? slot_uniform(a.u, a.seed, a.offset, b, a.k_max + 1, i) : 0.f;
+    MS st{-INFINITY, 0.f};
+    for (int g = 0; g < G; ++g) st = ms_combine(st, MS{lane_f(pm, g), lane_f(ps, g)});
+    if (lane == 0) {
+      s_m[i] = st.m;
+      s_S[i] = st.s;
+      if (i < k) {
+        if (x < 0 || x >= a.V) {
+          atomicOr(&s_bad, kFlagBadToken);
+        } else {
+          const int g = shard_of(a.sb, x);
+          const float p = ex2(fmaf(lane_f(lv, g), a.c, -st.m)) * (1.f / st.s);
+          if (!(u * lane_f(qv, g) < p)) atomicMin(&s_brk, i);
+        }
+      }
     }
   }
   __syncthreads();
@@ -218,29 +254,40 @@ __global__ __launch_bounds__(kBlock) void k_shard_draw(ShardArgs a) {
   if (b64 >= a.B) return;
   const int b = static_cast<int>(b64);
   const int64_t* state = a.state + b64 * 2;
+  const int G = a.sb.G;
+  // one load round: the decision, the request, and (lane g) shard g's sums
   const int m = static_cast<int>(state[0]);
   const int bad = static_cast<int>(state[1]);
   const int k = a.dlen[b];
+  const int ts = a.t_rs[b], qs = a.q_rs[b];
+  const float u = k >= 0 && k <= a.k_max ? slot_uniform(a.u, a.seed, a.offset, b, a.k_max + 1, k) : 0.f;
+  double mw = 0.0, mp = 0.0, mq = 0.0;
+  if (lane < G) {
+    const double* ms = a.mass + static_cast<int64_t>(lane * a.B + b) * 3;
+    mw = ms[0];
+    mp = ms[1];
+    mq = ms[2];
+  }
   // more drafts than the budget: reported for every request whose drafts were read
   const int extra = (a.max_new != nullptr && k > a.max_new[b]) ? kFlagOverBudget : 0;
   if (m < 0) {
-    if (a.shard == 0 && lane == 0) emit_invalid(a, b, bad | (bad == kFlagNonfinite ? extra : 0));
+    if (a.shard == 0) emit_invalid(a, b, bad | (bad == kFlagNonfinite ? extra : 0));
     return;
   }
   const bool resid = m < k;
   // totals over the shards, in shard order; the draft row's sum classes
   double W = 0.0, P = 0.0;
   bool qnan = false, qpinf = false, qninf = false;
-  for (int g = 0; g < a.sb.G; ++g) {
-    const double* ms = a.mass + static_cast<int64_t>(g * a.B + b) * 3;
-    W += ms[0];
-    P += ms[1];
-    qnan |= isnan(ms[2]);
-    qpinf |= ms[2] == INFINITY;
-    qninf |= ms[2] == -INFINITY;
+  for (int g = 0; g < G; ++g) {
+    W += lane_d(mw, g);
+    P += lane_d(mp, g);
+    const double q = lane_d(mq, g);
+    qnan |= isnan(q);
+    qpinf |= q == INFINITY;
+    qninf |= q == -INFINITY;
   }
   if (resid && (qnan || (qpinf && qninf) || !isfinite(W))) {
-    if (a.shard == 0 && lane == 0) emit_invalid(a, b, kFlagNonfinite | extra);
+    if (a.shard == 0) emit_invalid(a, b, kFlagNonfinite | extra);
     return;
   }
   int fallback = 0;
@@ -251,13 +298,12 @@ __global__ __launch_bounds__(kBlock) void k_shard_draw(ShardArgs a) {
     use_p = true;
     total = P;
   }
-  const float u = slot_uniform(a.u, a.seed, a.offset, b, a.k_max + 1, k);
   const double target = static_cast<double>(u) * total;
   // the shard holding the target: the first with weight whose running sum exceeds it
   int gs = -1, glast = -1;
   double base = 0.0, run = 0.0, base_last = 0.0;
-  for (int g = 0; g < a.sb.G; ++g) {
-    const double wg = a.mass[static_cast<int64_t>(g * a.B + b) * 3 + (use_p ? 1 : 0)];
+  for (int g = 0; g < G; ++g) {
+    const double wg = use_p ? lane_d(mp, g) : lane_d(mw, g);
     if (wg > 0.0) {
       if (gs < 0 && run + wg > target) {
         gs = g;
@@ -273,12 +319,11 @@ __global__ __launch_bounds__(kBlock) void k_shard_draw(ShardArgs a) {
     base = base_last;
   }
   if (gs < 0) {
-    if (a.shard == 0 && lane == 0) emit_invalid(a, b, kFlagNonfinite | fallback | extra);
+    if (a.shard == 0) emit_invalid(a, b, kFlagNonfinite | fallback | extra);
     return;
   }
   if (gs != a.shard) return;
   const int64_t c0 = a.sb.b[a.shard], vg = a.sb.b[a.shard + 1] - c0;
-  const int ts = a.t_rs[b], qs = a.q_rs[b];
   const int nt = static_cast<int>((vg + kSampleTile - 1) / kSampleTile);
   const double* tw = a.tiles + b64 * a.tile_cap * 2 + (use_p ? 1 : 0);
   int ta, tb;
@@ -287,15 +332,15 @@ __global__ __launch_bounds__(kBlock) void k_shard_draw(ShardArgs a) {
   for (int i = ta; i < tb; ++i) own += tw[i * 2];
   TileHit hit;
   if (!wave_find_tile(tw, 2, nt, own, target - base, hit)) {
-    if (lane == 0) emit_invalid(a, b, kFlagNonfinite | fallback | extra);
+    emit_invalid(a, b, kFlagNonfinite | fallback | extra);
     return;
   }
   hit.base += base;
-  const MS st = shard_combine(a.pairs, a.sb.G, a.t_rows, ts + m);
+  const MS st = wave_shard_combine(a.pairs, G, a.t_rows, ts + m);
   const DrawRow r{row_ptr<DT>(a.tgt, ts + m, vg), use_p ? nullptr : row_ptr<DQ>(a.dq, qs + m, vg), a.c, st.m,
                   1.f / st.s, 1.f, !use_p};
   const int y = wave_pick_in_tile<DT, DQ>(r, vg, hit, target);
-  if (lane == 0) emit_round(a, b, m, static_cast<int>(c0 + y), static_cast<float>(total), fallback | extra);
+  emit_round(a, b, m, static_cast<int>(c0 + y), static_cast<float>(total), fallback | extra);
 }
 
 // ---- host side ----
