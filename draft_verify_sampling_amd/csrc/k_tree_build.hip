@@ -122,13 +122,6 @@ __device__ __forceinline__ void list_insert(uint64_t (&top)[K], uint64_t key) {
   }
 }
 
-// Candidate order of the rerank and the frontier: larger value first, then
-// the shallower, then the earlier created.
-__device__ __forceinline__ bool cand_before(double va, int da, int ia, double vb, int db, int ib) {
-  if (va != vb) return va > vb;
-  if (da != db) return da < db;
-  return ia < ib;
-}
 
 }  // namespace
 
@@ -270,6 +263,21 @@ __global__ __launch_bounds__(kBlock) void k_tree_round(TreeRoundArgs a) {
   const int lane = tid & (kWave - 1), wid = tid / kWave;
   const int64_t c0 = static_cast<int64_t>(b) * a.max_cand;
   const int k = a.top;
+  const int nk = a.nseg * k;  // keys of an expanded row: <= 64 segments x 16 keys, 16 per lane
+  constexpr int kPerLane = 64 * kMaxTreeTop / kWave;
+  const int used = (nk + kWave - 1) / kWave;  // registers of kv holding keys
+  uint64_t kv[kPerLane];
+  auto load_keys = [&](int e) {
+    const uint64_t* keys = a.keys + (static_cast<int64_t>(b) * a.n_exp + e) * nk;
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+      const int idx = lane + j * kWave;
+      kv[j] = j < used && idx < nk ? keys[idx] : 0;
+    }
+  };
+  // wave w's first expanded row's keys: their address depends on the request
+  // only, so they load with the round below
+  if (wid < a.n_exp) load_keys(wid);
 
   // the expanded nodes of this request, one lane each (the first round: the
   // root, created here), checked against the request's candidate count
@@ -318,19 +326,9 @@ __global__ __launch_bounds__(kBlock) void k_tree_round(TreeRoundArgs a) {
     const int node = s_node[e];
     if (node < 0) continue;
     const int slot = s_slot[e];
-    const int64_t row = static_cast<int64_t>(b) * a.n_exp + e;
-    const uint64_t* keys = a.keys + row * a.nseg * k;
-    const int nk = a.nseg * k;  // <= 64 segments x 16 keys: 16 per lane
-    constexpr int kPerLane = 64 * kMaxTreeTop / kWave;
-    uint64_t kv[kPerLane];
-#pragma unroll
-    for (int j = 0; j < kPerLane; ++j) {
-      const int idx = lane + j * kWave;
-      kv[j] = idx < nk ? keys[idx] : 0;
-    }
+    if (e != wid) load_keys(e);
     const double pv = a.value[c0 + node];
     const int pd = a.depth[c0 + node];
-    const int used = (nk + kWave - 1) / kWave;  // registers of kv holding keys
     uint64_t thr = ~0ull;
     for (int r = 0; r < k; ++r) {  // r-th best key of the row: the largest below the previous one
       uint64_t m = 0;
@@ -356,14 +354,30 @@ __global__ __launch_bounds__(kBlock) void k_tree_round(TreeRoundArgs a) {
   }
   __syncthreads();
   const int n_app = s_nv * k;
-  // the next frontier: the best expand_next of the appended candidates
-  for (int i = tid; i < n_app; i += kBlock) {
-    const double vi = s_v[i];
-    const int di = s_d[i];
-    int rank = 0;
-#pragma unroll 8
-    for (int j = 0; j < n_app; ++j) rank += cand_before(s_v[j], s_d[j], j, vi, di, i) ? 1 : 0;
-    if (rank < a.expand_next) a.next[static_cast<int64_t>(b) * a.expand_next + rank] = base + i;
+  // the next frontier: the best expand_next of the appended candidates.  A
+  // candidate's rank is counted by one 16-lane DPP row, each lane over a
+  // sixteenth of the others, and summed along the row.
+  constexpr int kRow = 16;
+  const int chunk = (n_app + kRow - 1) / kRow;
+  for (int i0 = 0; i0 < n_app; i0 += kBlock / kRow) {
+    const int i = i0 + tid / kRow, part = tid % kRow;
+    int r = 0;
+    if (i < n_app) {
+      const double vi = s_v[i];
+      const int di = s_d[i];
+      const int j1 = min(n_app, (part + 1) * chunk);
+      for (int j = part * chunk; j < j1; ++j) {
+        const double vj = s_v[j];
+        const int dj = s_d[j];
+        r += (vj > vi) | ((vj == vi) & ((dj < di) | ((dj == di) & (j < i))));
+      }
+    }
+    r += dpp_i<0x111, 0xf>(r);  // row_shr:1
+    r += dpp_i<0x112, 0xf>(r);  // row_shr:2
+    r += dpp_i<0x114, 0xf>(r);  // row_shr:4
+    r += dpp_i<0x118, 0xf>(r);  // row_shr:8: the row's last lane holds the sum
+    if (i < n_app && part == kRow - 1 && r < a.expand_next)
+      a.next[static_cast<int64_t>(b) * a.expand_next + r] = base + i;
   }
   for (int j = n_app + tid; j < a.expand_next; j += kBlock) a.next[static_cast<int64_t>(b) * a.expand_next + j] = -1;
   if (tid == 0) a.count[b] = base + n_app;
