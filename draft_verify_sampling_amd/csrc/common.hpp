@@ -132,6 +132,32 @@ __device__ __forceinline__ double dpp_d(double v) {
   return __longlong_as_double(static_cast<long long>((static_cast<uint64_t>(hi) << 32) | lo));
 }
 
+template <int ctrl, int row_mask>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), ctrl, row_mask, 0xf, false));
+}
+
+// Largest value over the wave's lanes (0 is the identity), valid in every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0x111, 0xf>(v));  // row_shr:1
+  v = max(v, dpp_u32<0x112, 0xf>(v));  // row_shr:2
+  v = max(v, dpp_u32<0x114, 0xf>(v));  // row_shr:4
+  v = max(v, dpp_u32<0x118, 0xf>(v));  // row_shr:8
+  v = max(v, dpp_u32<0x142, 0xa>(v));  // row_bcast:15 into rows 1 and 3
+  v = max(v, dpp_u32<0x143, 0xc>(v));  // row_bcast:31 into rows 2 and 3
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), kWave - 1));
+}
+
+// Largest 64-bit key over the wave (0 is the identity), valid in every lane:
+// the largest high word, then the largest low word among the lanes holding it.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  const uint32_t hi = static_cast<uint32_t>(v >> 32);
+  const uint32_t mh = wave_max_u32(hi);
+  const uint32_t ml = wave_max_u32(hi == mh ? static_cast<uint32_t>(v) : 0u);
+  return (static_cast<uint64_t>(mh) << 32) | ml;
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave (lane order).
 __device__ __forceinline__ double wave_incl_scan(double x) {
   x += dpp_d<0x111, 0xf>(x);  // row_shr:1

@@ -49,16 +49,6 @@ __device__ __forceinline__ uint64_t best_key(const Best& s) {
          static_cast<uint64_t>(~static_cast<uint32_t>(s.i));
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), off, kWave);
-    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), off, kWave);
-    const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
-}
 
 }  // namespace
 

@@ -60,33 +60,6 @@ __device__ __forceinline__ int32_t key_id(uint64_t k) {
 __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t min_u64(uint64_t a, uint64_t b) { return a < b ? a : b; }
 
-// Wave maxima through DPP row shifts and broadcasts (an inclusive max scan
-// whose last lane holds the wave's maximum), read back from lane 63.
-template <int ctrl, int row_mask>
-__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
-  return static_cast<uint32_t>(
-      __builtin_amdgcn_update_dpp(0, static_cast<int>(v), ctrl, row_mask, 0xf, false));
-}
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {  // 0 is the identity
-  v = max(v, dpp_u32<0x111, 0xf>(v));  // row_shr:1
-  v = max(v, dpp_u32<0x112, 0xf>(v));  // row_shr:2
-  v = max(v, dpp_u32<0x114, 0xf>(v));  // row_shr:4
-  v = max(v, dpp_u32<0x118, 0xf>(v));  // row_shr:8
-  v = max(v, dpp_u32<0x142, 0xa>(v));  // row_bcast:15 into rows 1 and 3
-  v = max(v, dpp_u32<0x143, 0xc>(v));  // row_bcast:31 into rows 2 and 3
-  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), kWave - 1));
-}
-
-// Largest 64-bit key of the wave as two 32-bit maxima: the high words, then
-// the low words of the lanes holding that high word.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {  // 0 is the identity
-  const uint32_t hi = static_cast<uint32_t>(v >> 32);
-  const uint32_t mh = wave_max_u32(hi);
-  const uint32_t ml = wave_max_u32(hi == mh ? static_cast<uint32_t>(v) : 0u);
-  return (static_cast<uint64_t>(mh) << 32) | ml;
-}
-
 __device__ __forceinline__ float wave_max_f32(float v) {
   v = fmaxf(v, dpp_f<0x111, 0xf>(v, -INFINITY));
   v = fmaxf(v, dpp_f<0x112, 0xf>(v, -INFINITY));

@@ -201,14 +201,8 @@ __device__ bool row_argmax(Walk& wk, const void* trow, uint64_t* s_key, uint32_t
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   ArgBest s{-INFINITY, 0x7fffffff, false};
   for (int t = wk.lo + wid; t < wk.hi; t += kWalkWaves) lane_tile_argmax<DT>(trow, a.V, t, s);
-  uint64_t key = (static_cast<uint64_t>(order_bits(s.v)) << 32) | static_cast<uint32_t>(~s.i);
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    const uint32_t lo = __shfl_xor(static_cast<uint32_t>(key), off, kWave);
-    const uint32_t hi = __shfl_xor(static_cast<uint32_t>(key >> 32), off, kWave);
-    const uint64_t o = (static_cast<uint64_t>(hi) << 32) | lo;
-    key = o > key ? o : key;
-  }
+  const uint64_t key =
+      wave_max_u64((static_cast<uint64_t>(order_bits(s.v)) << 32) | static_cast<uint32_t>(~s.i));
   const bool wnan = __ballot(s.nan) != 0;
   if (lane == 0) {
     s_key[wid] = key;
