@@ -780,13 +780,13 @@ __global__ __launch_bounds__(kBlock) void k_walk_small(WalkArgs a) {
     if (st == 0) continue;
     const int j = __ffsll(static_cast<long long>(st)) - 1;
     const int ij = i0 + j;
-    const int fin_j = __shfl(fin ? 1 : 0, j, kWave);
+    const int fin_j = __builtin_amdgcn_readlane(fin ? 1 : 0, j);
     if (!fin_j) {
       nonfinite = true;
     } else {
       m = ij;
-      Mm = __shfl(ms.x, j, kWave);
-      Sm = __shfl(ms.y, j, kWave);
+      Mm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ms.x), j));
+      Sm = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ms.y), j));
     }
     break;
   }

@@ -494,8 +494,8 @@ __device__ __forceinline__ void lane_partial_excl(const DrawRow& r, int64_t V, i
   float sa = 0.f, sb = 0.f;
 #pragma unroll
   for (int k = 0; k < L::kRuns; ++k) {
-    sa += __shfl(pa, k, kWave);
-    sb += __shfl(pb, k, kWave);
+    sa += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pa), k));
+    sb += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(pb), k));
   }
   a = sa;
   b = sb;
