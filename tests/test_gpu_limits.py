@@ -1,9 +1,10 @@
 """The library at its documented limits and on empty batches, on an MI355X,
 through the C ABI, against the float64 oracle: the largest vocabulary
-(4,194,304 ids), the deepest chain (k_max = 255, every draft kept), the
+(4,194,304 ids), the deepest chain (k_max = 255, sampled and greedy), the
 largest tree (1024 nodes, all three walk variants), the most vocabulary
 shards (64), the tree builder's largest candidate set and frontier (1024
-candidates, 64 expanded nodes), and batches of zero requests."""
+candidates, 64 expanded nodes), the prompt-lookup drafter's largest draft
+(k = 1024) over long unaligned contexts, and batches of zero requests."""
 import numpy as np
 import pytest
 import torch
@@ -206,4 +207,64 @@ def test_gpu_empty_batches():
     u = sv.sv_philox_uniforms(1, 2, 0, 5)
     assert u.shape == (0, 5)
     torch.cuda.synchronize()
+    assert int(st.item()) == 0
+
+
+def test_gpu_greedy_deepest_chain():
+    """k_max = 255 in the greedy verify (one block per request, thread i
+    holding row i): a full match, a mismatch at draft 200, an EOS kept at
+    draft 100 (the round ends after it) and a budget cut, over rows of small
+    integers (ties for the maximum are common; the lowest id wins)."""
+    say("greedy chain with k_max = 255")
+    rng = np.random.default_rng(78)
+    B, k, V = 4, 255, 1000
+    eos = V - 1
+    rows = rng.integers(-40, 40, size=(B * (k + 1), V)).astype(np.float32)
+    rows[:, eos] = -1000.0                    # no row picks the EOS id ...
+    rows[2 * (k + 1) + 100, eos] = 1000.0     # ... except request 2's row 100
+    am = np.argmax(rows, axis=1).reshape(B, k + 1)
+    ids = am[:, :k].astype(np.int32).copy()
+    ids[1, 200] = (ids[1, 200] + 1) % (V - 1)
+    ts = np.arange(B, dtype=np.int32) * (k + 1)
+    lens = np.full(B, k, dtype=np.int32)
+    max_new = np.array([300, 300, 300, 57], dtype=np.int32)
+    st = _status()
+    got = run_greedy(rows, "f32", ts, ids, lens, max_new=max_new, eos_id=eos, status=st)
+    want = oracle.verify_greedy(rows, "f32", V, ts, ids, lens, k, max_new=max_new, eos_id=eos)
+    for key in ("tokens", "count", "accepted"):
+        assert np.array_equal(got[key], want[key]), key
+    assert int(st.item()) == _or(want["flags"])
+    assert list(want["accepted"]) == [255, 200, 255, 255]
+    assert list(want["count"]) == [256, 201, 101, 57]
+
+
+def test_gpu_ngram_long_unaligned_contexts():
+    """Contexts of up to 10,003 tokens in rows of an odd stride (no row is
+    16-byte aligned), so the newest-first search crosses several 4,096-start
+    chunks; repeats planted at distances from 10 to 9,000 tokens and contexts
+    without any repeat; k up to 1,024 (the proposal may run to the context's
+    end)."""
+    say("prompt lookup over 10,003-token unaligned contexts")
+    rng = np.random.default_rng(79)
+    B, stride = 24, 10_003
+    ctx = rng.integers(0, 1 << 30, size=(B, stride)).astype(np.int32)  # (almost) no chance repeats
+    lens = rng.integers(stride - 50, stride + 1, size=B).astype(np.int32)
+    lens[0] = 3
+    lens[1] = 4100
+    for b in range(2, B):
+        n = int(lens[b])
+        if b % 6 == 5:
+            continue  # no repeat: every chunk is searched
+        dist = [10, 900, 4100, 6000, 9000][b % 5] + int(rng.integers(0, 7))
+        w = 8
+        src = n - w
+        dst = max(0, src - dist)
+        ctx[b, dst:dst + w] = ctx[b, src:src + w]
+    st = _status()
+    for w, k in ((1, 1), (3, 7), (8, 1024), (64, 300)):
+        got_ids, got_lens = sv.sv_ngram_draft(i32(ctx), i32(lens), w, k, dev_status=st)
+        torch.cuda.synchronize()
+        wi, wl, wf = oracle.ngram_draft(ctx, lens, w, k)
+        assert np.array_equal(got_lens.cpu().numpy(), wl), (w, k)
+        assert np.array_equal(got_ids.cpu().numpy(), wi), (w, k)
     assert int(st.item()) == 0
