@@ -174,8 +174,8 @@ __global__ __launch_bounds__(kBlock) void k_topk_partial(const void* __restrict_
       const int64_t vv = v + j * kBlock;
       w[j] = vv < v1 ? vp[vv] : uint4{0u, 0u, 0u, 0u};
     }
+    float m = -1.f;  // the thread's largest raw value of the first chunk
     if (ch == 0) {
-      float m = -1.f;
 #pragma unroll
       for (int j = 0; j < U; ++j) {
         if (v + j * kBlock >= v1) break;
@@ -189,6 +189,8 @@ __global__ __launch_bounds__(kBlock) void k_topk_partial(const void* __restrict_
       T = block_kth_largest(mc, k, s_tk);
     }
     const bool every = !(T > 0.f);
+    // in the first chunk a wave none of whose threads reached T has no key
+    if (!every && ch == 0 && !__any(m >= T)) continue;
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const int64_t vv = v + j * kBlock;
@@ -208,14 +210,18 @@ __global__ __launch_bounds__(kBlock) void k_topk_partial(const void* __restrict_
 
   // the block's k best: each wave's k best (k rounds of a wave max over its
   // threads' list heads), then the k best of those in wave 0
-  for (int r = 0; r < k; ++r) {
-    const uint64_t m = wave_max_u64(top[0]);
-    if (top[0] == m && m != 0) {  // keys are distinct: one owner
+  if (__any(top[0] != 0)) {
+    for (int r = 0; r < k; ++r) {
+      const uint64_t m = wave_max_u64(top[0]);
+      if (top[0] == m && m != 0) {  // keys are distinct: one owner
 #pragma unroll
-      for (int j = 0; j + 1 < K; ++j) top[j] = top[j + 1];
-      top[K - 1] = 0;
+        for (int j = 0; j + 1 < K; ++j) top[j] = top[j + 1];
+        top[K - 1] = 0;
+      }
+      if (lane == 0) s_w[wid * k + r] = m;
     }
-    if (lane == 0) s_w[wid * k + r] = m;
+  } else if (lane < k) {
+    s_w[wid * k + lane] = 0;  // a wave without keys
   }
   __syncthreads();
   if (wid == 0) {
