@@ -174,27 +174,34 @@ __global__ __launch_bounds__(kBlock) void k_topk_partial(const void* __restrict_
       const int64_t vv = v + j * kBlock;
       w[j] = vv < v1 ? vp[vv] : uint4{0u, 0u, 0u, 0u};
     }
-    float m = -1.f;  // the thread's largest raw value of the first chunk
-    if (ch == 0) {
+    // each vector's largest raw value, and the thread's
+    float vm[U];
+    float m = -1.f;
 #pragma unroll
-      for (int j = 0; j < U; ++j) {
-        if (v + j * kBlock >= v1) break;
+    for (int j = 0; j < U; ++j) {
+      vm[j] = -INFINITY;
+      if (v + j * kBlock < v1) {
         float x[D::kPerVec];
         D::unpack(w[j], x);
 #pragma unroll
-        for (int t = 0; t < D::kPerVec; ++t) m = fmaxf(m, x[t]);
+        for (int t = 0; t < D::kPerVec; ++t) vm[j] = fmaxf(vm[j], x[t]);
+        m = fmaxf(m, vm[j]);
       }
+    }
+    if (ch == 0) {
       // the thread's largest confidence; -1 for a thread with no elements
       const float mc = v < v1 ? fminf(fmaxf(m, 0.f), 1.f) : -1.f;
       T = block_kth_largest(mc, k, s_tk);
     }
     const bool every = !(T > 0.f);
-    // in the first chunk a wave none of whose threads reached T has no key
-    if (!every && ch == 0 && !__any(m >= T)) continue;
+    // a wave none of whose threads reached T has no key in this chunk; in the
+    // others only vectors whose largest value reached T are opened
+    if (!every && !__any(m >= T)) continue;
 #pragma unroll
     for (int j = 0; j < U; ++j) {
       const int64_t vv = v + j * kBlock;
       if (vv >= v1) break;
+      if (!every && !(vm[j] >= T)) continue;
       float x[D::kPerVec];
       D::unpack(w[j], x);
 #pragma unroll
