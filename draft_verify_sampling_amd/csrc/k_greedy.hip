@@ -68,7 +68,9 @@ __global__ __launch_bounds__(kBlock) void k_row_argmax(const void* __restrict__ 
   Best best{-INFINITY, 0x7fffffff, false};
   // chunks of U * kBlock vectors; a chunk's loads are all issued before any
   // is used (non-temporal: the rows are read once), so a slice of up to
-  // U * kBlock vectors costs one load round
+  // U * kBlock vectors costs one load round.  A chunk's largest value first
+  // (fmaxf skips NaN, which only sets the flag), then the first element
+  // holding it, the lowest id, since a thread's elements ascend.
   for (int64_t c0 = v0 + threadIdx.x; c0 < v1; c0 += U * kBlock) {
     uint4 w[U];
 #pragma unroll
@@ -81,16 +83,33 @@ __global__ __launch_bounds__(kBlock) void k_row_argmax(const void* __restrict__ 
                      __builtin_nontemporal_load(q + 2), __builtin_nontemporal_load(q + 3)};
       }
     }
+    float x[U][D::kPerVec];
+    float m = -INFINITY;
+    bool nan = false;
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const int64_t v = c0 + j * kBlock;
-      if (v < v1) {
-        float x[D::kPerVec];
-        D::unpack(w[j], x);
-        const int64_t e = head + v * D::kPerVec;
+      D::unpack(w[j], x[j]);
+      if (c0 + j * kBlock < v1) {
 #pragma unroll
-        for (int t = 0; t < D::kPerVec; ++t) best_update(best, x[t], e + t);
+        for (int t = 0; t < D::kPerVec; ++t) {
+          m = fmaxf(m, x[j][t]);
+          nan |= x[j][t] != x[j][t];
+        }
       }
+    }
+    int32_t at = 0x7fffffff;
+#pragma unroll
+    for (int j = U - 1; j >= 0; --j) {
+      if (c0 + j * kBlock < v1) {
+        const int32_t e = static_cast<int32_t>(head + (c0 + j * kBlock) * D::kPerVec);
+#pragma unroll
+        for (int t = D::kPerVec - 1; t >= 0; --t) at = x[j][t] == m ? e + t : at;
+      }
+    }
+    best.nan |= nan;
+    if (m > best.v || (m == best.v && at < best.i)) {
+      best.v = m;
+      best.i = at;
     }
   }
   if (seg == 0)

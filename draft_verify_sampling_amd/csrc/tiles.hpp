@@ -574,13 +574,32 @@ __device__ __forceinline__ void lane_tile_argmax(const void* row, int64_t V, int
     uint4 w[kRuns];
 #pragma unroll
     for (int k = 0; k < kRuns; ++k) w[k] = ld16<D>(row, t0 + static_cast<int64_t>(k * kWave + lane) * kPer);
+    // the lane's largest value (fmaxf skips NaN, which only sets the flag),
+    // then the first of its elements holding it: the lowest id, as its
+    // elements ascend
+    float x[kRuns][kPer];
+    float m = -INFINITY;
+    bool nan = false;
 #pragma unroll
     for (int k = 0; k < kRuns; ++k) {
-      float x[kPer];
-      D::unpack(w[k], x);
+      D::unpack(w[k], x[k]);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        m = fmaxf(m, x[k][j]);
+        nan |= x[k][j] != x[k][j];
+      }
+    }
+    int32_t at = 0x7fffffff;
+#pragma unroll
+    for (int k = kRuns - 1; k >= 0; --k) {
       const int32_t e = static_cast<int32_t>(t0) + (k * kWave + lane) * kPer;
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) arg_update(s, x[j], e + j);
+      for (int j = kPer - 1; j >= 0; --j) at = x[k][j] == m ? e + j : at;
+    }
+    s.nan |= nan;
+    if (m > s.v || (m == s.v && at < s.i)) {
+      s.v = m;
+      s.i = at;
     }
   } else {
 #pragma unroll 1
