@@ -95,12 +95,28 @@ __global__ __launch_bounds__(kBlock) void k_ngram(const int32_t* __restrict__ ct
         s_end = end;
       }
       __syncthreads();
-      for (int j = hi - tid; j >= lo; j -= kBlock) {
-        bool match = true;
-        for (int i = 0; i < window && match; ++i) match = s_tok[j - lo + i] == s_key[i];
-        if (match) {
-          atomicMax(&s_best, j);
-          break;  // this thread's later starts are older
+      // this thread's starts hi - tid, hi - tid - 256, ... newest first, four
+      // at a time: their first tokens are read together and only a start
+      // whose first token matches is compared in full
+      const int32_t k0 = s_key[0];
+      bool found_here = false;
+      for (int j0 = hi - tid; j0 >= lo && !found_here; j0 -= 4 * kBlock) {
+        int32_t f[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j = j0 - u * kBlock;
+          f[u] = j >= lo ? s_tok[j - lo] : ~k0;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j = j0 - u * kBlock;
+          if (found_here || f[u] != k0) continue;
+          bool match = true;
+          for (int i = 1; i < window && match; ++i) match = s_tok[j - lo + i] == s_key[i];
+          if (match) {
+            atomicMax(&s_best, j);
+            found_here = true;  // this thread's later starts are older
+          }
         }
       }
       __syncthreads();
