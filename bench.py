@@ -9,9 +9,12 @@ sampled chain at B=64 requests, k=4 drafts, V=248,320, bf16 target logits and
 bf16 draft probabilities, T=0.7; three input sets rotate so that no step finds
 its rows in the 256 MB last-level cache.  Prints one JSON line.
 
-Other workloads (``--workload c1|c2|c4|c5``) print the same kind of line for
-the other configurations (fixed-prefix chain, greedy + prompt lookup, ragged
-chain, tree).
+Other workloads (``--workload c1|c2|c3p|c3s|c4|c5|c5g|c5p|tb``) print the same
+kind of line for the other configurations (fixed-prefix chain, greedy + prompt
+lookup, device uniforms, one vocabulary shard, ragged chain, sampled / greedy /
+point-mass tree, EAGLE-2 tree build); their inputs also rotate over device
+copies totalling more than twice that cache (the fixed-prefix chain, whose
+rows are shared by all rounds by construction, excepted).
 """
 import argparse
 import hashlib
