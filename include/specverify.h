@@ -63,6 +63,12 @@
  *   initialised: each call writes everything it later reads, so one buffer
  *   can serve calls of any shape in turn on one stream.  Calls that
  *   may run concurrently (different streams) need separate workspaces.
+ * - HIP graphs: no entry point allocates, synchronises or records a memset,
+ *   so calls can be captured on a stream and replayed.  The tree walks
+ *   certify the zeroing of their exchange words with a ticket unique to the
+ *   call; a captured call would replay its ticket, so under capture they zero
+ *   the words with a kernel before the walk instead (the library asks the
+ *   stream whether it is capturing).
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
