@@ -5,9 +5,10 @@ call and certify that with a ticket unique to the call; the first exchange
 reads no word before every ticket of the request is there.  These tests give
 the walks workspaces whose every byte is 0xFF (every exchange word looks
 written, every ticket is wrong) and require the outputs of a fresh workspace
-and of the float64 oracle; and they replay a captured tree walk (under
-capture the words are zeroed by a kernel instead) with eager tree walks on the
-same workspace in between."""
+and of the float64 oracle; they replay a captured tree walk (under capture
+the words are zeroed by a kernel instead) with eager tree walks on the same
+workspace in between; and they run the walks on one workspace with the shape
+changing from call to call."""
 import numpy as np
 import pytest
 import torch
@@ -137,3 +138,55 @@ def test_gpu_tree_walk_graph_replay():
             assert torch.equal(got, w), rep
         sv.sv_verify_tree(*oargs, T, ub, workspace=ws)   # eager work on the same words in between
         torch.cuda.synchronize()
+
+
+def test_gpu_tree_walks_changing_shapes_one_workspace():
+    """36 calls of the three tree walks on one workspace, each with another
+    shape (B, N, V, dtypes, T), so the split into workgroups, the number of
+    exchanges and the workspace layout change from call to call and every
+    call finds the previous call's words and tickets at other places."""
+    say("tree walks with changing shapes on one workspace")
+    rng = np.random.default_rng(94)
+    ws = sv.Workspace()
+    for case in range(36):
+        B = int(rng.choice([1, 3, 8, 17]))
+        N = int(rng.choice([2, 5, 24, 60]))
+        V = int(rng.choice([2049, 5000, 20000, 70000]))
+        tk, qk = str(rng.choice(["bf16", "f32"])), str(rng.choice(["bf16", "f32"]))
+        T = float(rng.choice([0.5, 1.0, 1.7]))
+        N = min(N, max(2, 12_000_000 // (B * V)))
+        l = rng.standard_normal((B * N, V)) * 2.5
+        for r in range(B * N):
+            l[r, rng.choice(V, size=3, replace=False)] += 5.0
+        q = np.exp((l + rng.standard_normal(l.shape)) / T)
+        q /= q.sum(axis=1, keepdims=True)
+        target, draft = synth.encode(l, tk), synth.encode(q, qk)
+        parent = np.zeros((B, N), dtype=np.int32)
+        token = np.full((B, N), -1, dtype=np.int32)
+        for b in range(B):
+            parent[b, 0] = -1
+            for c in range(1, N):
+                p = int(rng.integers(max(0, c - 6), c))
+                parent[b, c] = p
+                row = synth.decode(target[b * N + p], tk)
+                token[b, c] = int(np.argmax(row)) if rng.random() < 0.5 else int(rng.integers(0, V))
+        u = rng.random((B, N)).astype(np.float32)
+        tgt, dft, par, tok = rows_to_dev(target, tk), rows_to_dev(draft, qk), i32(parent), i32(token)
+        st = torch.zeros(1, dtype=torch.int32, device=DEV)
+        mode = case % 3
+        if mode == 0:
+            o = _np(sv.sv_verify_tree(tgt, dft, par, tok, T, f32(u), dev_status=st, workspace=ws)[:4])
+            want = oracle.verify_tree(target, tk, draft, qk, V, parent, token, T, u, with_diag=False)
+            nb, bad = compare_tokens(dict(tokens=o[0], count=o[1], accepted=o[2], path=o[3]), want)
+            assert bad.size == 0 and nb <= 1, (case, B, N, V, tk, qk, T)
+        elif mode == 1:
+            o = _np(sv.sv_verify_tree_greedy(tgt, par, tok, dev_status=st, workspace=ws))
+            want = oracle.verify_tree_greedy(target, tk, V, parent, token)
+            assert np.array_equal(o[0], want["tokens"]) and np.array_equal(o[3], want["path"]), case
+        else:
+            o = _np(sv.sv_verify_tree_pointmass(tgt, par, tok, T, f32(u), dev_status=st, workspace=ws))
+            want = oracle.verify_tree_pointmass(target, tk, V, parent, token, T, u)
+            nb, bad = compare_tokens(dict(tokens=o[0], count=o[1], accepted=o[2]), want)
+            assert bad.size == 0 and nb <= 1, (case, B, N, V, tk, qk, T)
+        torch.cuda.synchronize()
+        assert int(st.item()) & 64 == 0, case  # no exchange timed out
