@@ -61,6 +61,7 @@ namespace sv {
 namespace {
 
 constexpr int kWalkWaves = kWalkBlock / kWave;
+constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
 constexpr int kMaxNodeGroups = kMaxTreeNodes / kWave;
 static_assert(2 * kMaxWalkGroups <= kWave, "one wave reads every exchanged word");
 static_assert(kMaxChainRows <= kWalkBlock, "one chain row per thread");
@@ -291,8 +292,17 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
   int32_t* s_ex = reinterpret_cast<int32_t*>(s_S + a.node_cap);  // point mass: ids removed at cur
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  Walk wk{&a, static_cast<int>(blockIdx.x) / a.G, static_cast<int>(blockIdx.x) % a.G, 0, 0, 0,
-          &s_x[0][0], s_ok};
+  // Workgroups are dealt to the 8 XCDs in turn (workgroup i to XCD i % 8), so
+  // with B a multiple of 8 the G workgroups of a request are taken from one
+  // XCD: i -> XCD x = i % 8 and rank j = i / 8 there; request (j / G) * 8 + x,
+  // workgroup j % G.  Their exchanges then stay within one L2.
+  int wb = static_cast<int>(blockIdx.x) / a.G, wg = static_cast<int>(blockIdx.x) % a.G;
+  if (a.B % kXcds == 0) {
+    const int x = static_cast<int>(blockIdx.x) % kXcds, j = static_cast<int>(blockIdx.x) / kXcds;
+    wb = (j / a.G) * kXcds + x;
+    wg = j % a.G;
+  }
+  Walk wk{&a, wb, wg, 0, 0, 0, &s_x[0][0], s_ok};
   wk.lo = static_cast<int>(static_cast<int64_t>(wk.g) * a.ntiles / a.G);
   wk.hi = static_cast<int>(static_cast<int64_t>(wk.g + 1) * a.ntiles / a.G);
   const int b = wk.b;
