@@ -35,6 +35,15 @@ print, closed forms, or brute force):
                                  sampling-noise level over 200,000 rounds;
                                  tokens-per-round closed form; alpha=0.8, k=1 ->
                                  1.8 exactly.
+* edge readings of ``verify_sample``, ``verify_greedy`` and the three tree
+  walks (tests/test_oracle_edges.py, hand-worked cases on one-hot rows):
+  the end-token cut (inclusive, first occurrence only), the budget cut and
+  the over-budget bit, the zero-residual fallback (chain: drawn from p_m with
+  the fallback bit; tree: p unchanged for the next sibling), and the outputs
+  and status bits of invalid requests (bad token, draft count, row range,
+  tree shape).  The point-mass walk's fallback cannot occur in exact
+  arithmetic (removing x from p leaves no mass only if p is the point mass
+  on x, which is then always kept), so it has no hand case.
 * ``chain.verify_sample(variant="resample_from_p")``  TV equal to the closed
                                  form 1/2 sum |min(p,q) - alpha p|.
 * ``chain.naive_round``         acceptance = sum p q.
