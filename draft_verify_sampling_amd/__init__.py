@@ -12,6 +12,8 @@ every call raises ``SpecVerifyError``.
 from __future__ import annotations
 
 import ctypes
+import functools
+import inspect
 import os
 import threading
 from typing import Optional
@@ -28,7 +30,7 @@ __all__ = [
     "sv_philox_uniforms", "sv_verify_sample_philox", "DraftTreeState", "sv_tree_expand",
     "sv_tree_finalize", "SV_OP_TREE_EXPAND", "SV_OP_SHARD", "sv_shard_stats", "sv_shard_residual",
     "sv_shard_draw",
-    "prepare_softmax_partials", "sv_time_statistics_once",
+    "prepare_softmax_partials", "sv_debug_time_statistics_once", "sample_workspace_bytes",
 ]
 
 SV_F32, SV_BF16 = 0, 1
@@ -41,7 +43,8 @@ EXPORTS = ("sv_abi_version", "sv_status_string", "sv_last_error", "sv_workspace_
            "sv_ngram_draft", "sv_verify_greedy", "sv_verify_sample", "sv_verify_tree",
            "sv_verify_tree_greedy", "sv_verify_tree_pointmass", "sv_philox_uniforms",
            "sv_verify_sample_philox", "sv_tree_expand", "sv_tree_finalize", "sv_shard_stats",
-           "sv_shard_residual", "sv_shard_draw", "sv_time_statistics_once")
+           "sv_shard_residual", "sv_shard_draw", "sv_sample_workspace_bytes",
+           "sv_debug_time_statistics_once")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -70,7 +73,8 @@ _SIGS = {
                                       P, P, P, P, P, SZ, P]),
     "sv_verify_tree_greedy": (ctypes.c_int, [P, I32, I64, P, P, I32, I32, P, P, P, P, P, P, SZ, P]),
     "sv_philox_uniforms": (ctypes.c_int, [U64, U64, I32, I32, P, P]),
-    "sv_time_statistics_once": (ctypes.c_int, [P, P]),
+    "sv_debug_time_statistics_once": (ctypes.c_int, [P, P]),
+    "sv_sample_workspace_bytes": (SZ, [I64, I64, I64, I32]),
     "sv_tree_expand": (ctypes.c_int, [P, I32, I64, I32, I32, P, I32, I32, I32, P, P, P, P, P, P, P, P,
                                       P, SZ, P]),
     "sv_tree_finalize": (ctypes.c_int, [I32, I32, P, P, P, P, P, P, I32, P, P, P, P, P, P, P]),
@@ -124,10 +128,16 @@ def workspace_bytes(op: int, batch: int, total_rows: int, vocab: int) -> int:
     return int(load().sv_workspace_bytes(op, batch, total_rows, vocab))
 
 
-def sv_time_statistics_once(before=None, after=None):
-    """Arm the measurement hook: the calling thread's next sampled chain call
-    records torch.cuda.Event `before` / `after` around its statistics kernel
-    (None, None disarms).  The events are created here if they are not yet."""
+def sample_workspace_bytes(batch: int, t_rows: int, vocab: int, k_max: int) -> int:
+    """Workspace bytes one sampled chain call with these sizes checks for."""
+    return int(load().sv_sample_workspace_bytes(batch, t_rows, vocab, k_max))
+
+
+def sv_debug_time_statistics_once(before=None, after=None):
+    """Arm the measurement hook (include/specverify_debug.h): the calling
+    thread's next sampled chain call records torch.cuda.Event `before` /
+    `after` around the kernel that streams its target rows (None, None
+    disarms).  The events are created here if they are not yet."""
     if (before is None) != (after is None):
         raise SpecVerifyError("give both events or neither")
     ptrs = []
@@ -138,7 +148,7 @@ def sv_time_statistics_once(before=None, after=None):
         if not e.cuda_event:  # torch creates its events on first use
             e.record()
         ptrs.append(ctypes.c_void_p(e.cuda_event))
-    _check(load().sv_time_statistics_once(*ptrs), "sv_time_statistics_once")
+    _check(load().sv_debug_time_statistics_once(*ptrs), "sv_debug_time_statistics_once")
 
 
 def _check(status: int, what: str):
@@ -194,6 +204,26 @@ def _stream(stream) -> Optional[int]:
     return s.cuda_stream or None
 
 
+def _on_call_stream(fn):
+    """Run a binding call with its `stream` argument as torch's current stream,
+    so that every tensor the binding allocates or fills for the call (outputs,
+    zeroed diagnostics, a grown workspace) is made on the stream the kernels
+    run on: the fills are ordered before the kernels, and the caching
+    allocator hands a freed buffer out again only after the work queued on
+    that stream."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def call(*args, **kwargs):
+        stream = sig.bind_partial(*args, **kwargs).arguments.get("stream")
+        if stream is None:
+            return fn(*args, **kwargs)
+        with torch.cuda.stream(stream):
+            return fn(*args, **kwargs)
+
+    return call
+
+
 class Workspace:
     """Caller-side workspace: a device buffer grown on demand and reused across
     calls on one stream (the library needs no particular initial contents)."""
@@ -202,10 +232,17 @@ class Workspace:
         self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
             else torch.device(device)
         self.buf = None
+        self.last_stream = None
 
     def get(self, nbytes: int) -> torch.Tensor:
+        cur = torch.cuda.current_stream(self.device)
         if self.buf is None or self.buf.numel() < nbytes:
+            if self.buf is not None:
+                # the old buffer may still be in use by work queued on the
+                # stream of its last call: free it only after that work
+                self.buf.record_stream(self.last_stream)
             self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        self.last_stream = cur
         return self.buf
 
 
@@ -269,6 +306,7 @@ def sv_softmax_segments(n_rows: int, vocab: int) -> int:
     return int(load().sv_softmax_segments(n_rows, vocab))
 
 
+@_on_call_stream
 def sv_softmax_partials(rows: torch.Tensor, temperature: float, out: Optional[torch.Tensor] = None,
                         stream=None) -> torch.Tensor:
     """Per-segment softmax pairs of every row: returns float32 [n_rows, nseg, 2]
@@ -289,6 +327,7 @@ def prepare_softmax_partials(rows: torch.Tensor, temperature: float, out: torch.
     return prepare(sv_softmax_partials, rows, temperature, out=out, stream=stream)[0]
 
 
+@_on_call_stream
 def sv_ngram_draft(ctx: torch.Tensor, ctx_len: torch.Tensor, window: int, k: int,
                    dev_status: Optional[torch.Tensor] = None, stream=None):
     """Prompt-lookup drafts: returns (draft_ids int32 [B, k], draft_len int32 [B])."""
@@ -303,6 +342,7 @@ def sv_ngram_draft(ctx: torch.Tensor, ctx_len: torch.Tensor, window: int, k: int
     return _invoke("sv_ngram_draft", args, (ctx, ctx_len, ids, lens, dev_status), (ids, lens))
 
 
+@_on_call_stream
 def sv_verify_greedy(target: torch.Tensor, t_row_start: torch.Tensor, draft_ids: torch.Tensor,
                      draft_len: torch.Tensor, max_new: Optional[torch.Tensor] = None,
                      eos_id: int = -1, dev_status: Optional[torch.Tensor] = None,
@@ -332,6 +372,7 @@ def sv_verify_greedy(target: torch.Tensor, t_row_start: torch.Tensor, draft_ids:
     return _invoke("sv_verify_greedy", args, keep, (tok, cnt, acc))
 
 
+@_on_call_stream
 def sv_verify_sample(target: torch.Tensor, draft: torch.Tensor, t_row_start: torch.Tensor,
                      q_row_start: torch.Tensor, draft_ids: torch.Tensor, draft_len: torch.Tensor,
                      temperature: float, uniforms: torch.Tensor,
@@ -347,6 +388,7 @@ def sv_verify_sample(target: torch.Tensor, draft: torch.Tensor, t_row_start: tor
                    None, max_new, eos_id, diag, dev_status, workspace, stream, out, resid)
 
 
+@_on_call_stream
 def sv_verify_sample_philox(target: torch.Tensor, draft: torch.Tensor, t_row_start: torch.Tensor,
                             q_row_start: torch.Tensor, draft_ids: torch.Tensor, draft_len: torch.Tensor,
                             temperature: float, seed: int, offset: int,
@@ -360,6 +402,7 @@ def sv_verify_sample_philox(target: torch.Tensor, draft: torch.Tensor, t_row_sta
                    (int(seed), int(offset)), max_new, eos_id, diag, dev_status, workspace, stream, out, resid)
 
 
+@_on_call_stream
 def sv_philox_uniforms(seed: int, offset: int, batch: int, slots: int, out: Optional[torch.Tensor] = None,
                        device=None, stream=None) -> torch.Tensor:
     """The verify's uniforms u [batch, slots] of the Philox stream (seed, offset)."""
@@ -401,7 +444,7 @@ def _sample(target, draft, t_row_start, q_row_start, draft_ids, draft_len, tempe
         _shape(acc, "out accepted", (B,), torch.int32)
         _shape(dg, "out diag", (B, k_max + 1, 4), torch.float32)
         _shape(rs, "out resid", (B,), torch.float32)
-    ws = _workspace(workspace, dev, stream, workspace_bytes(SV_OP_SAMPLE, B, t_rows, V))
+    ws = _workspace(workspace, dev, stream, sample_workspace_bytes(B, t_rows, V, k_max))
     head = (_dev(target, "target"), _dtype_code(target), t_rows,
             _dev(draft, "draft"), _dtype_code(draft), q_rows, V,
             _dev(t_row_start, "t_row_start", torch.int32, dev),
@@ -429,6 +472,7 @@ def prepare_verify_sample(*args, **kwargs):
     return prepare(sv_verify_sample, *args, **kwargs)
 
 
+@_on_call_stream
 def sv_verify_tree(target: torch.Tensor, draft: torch.Tensor, parent: torch.Tensor,
                    node_token: torch.Tensor, temperature: float, uniforms: torch.Tensor,
                    diag: bool = False, dev_status: Optional[torch.Tensor] = None,
@@ -475,6 +519,7 @@ def _tree_outputs(B, N, dev, out):
             torch.empty((B,), dtype=torch.int32, device=dev), torch.empty((B, N), dtype=torch.int32, device=dev))
 
 
+@_on_call_stream
 def sv_verify_tree_greedy(target: torch.Tensor, parent: torch.Tensor, node_token: torch.Tensor,
                           dev_status: Optional[torch.Tensor] = None,
                           workspace: Optional[Workspace] = None, stream=None, out=None):
@@ -497,6 +542,7 @@ def sv_verify_tree_greedy(target: torch.Tensor, parent: torch.Tensor, node_token
     return _invoke("sv_verify_tree_greedy", args, keep, (tok, cnt, acc, pth))
 
 
+@_on_call_stream
 def sv_verify_tree_pointmass(target: torch.Tensor, parent: torch.Tensor, node_token: torch.Tensor,
                              temperature: float, uniforms: torch.Tensor,
                              dev_status: Optional[torch.Tensor] = None,
@@ -540,6 +586,7 @@ class DraftTreeState:
         self.count = torch.zeros((batch,), dtype=torch.int32, device=dev)
 
 
+@_on_call_stream
 def sv_tree_expand(draft_rows: torch.Tensor, exp_node: Optional[torch.Tensor], top_children: int,
                    expand_next: int, state: DraftTreeState, next_exp: Optional[torch.Tensor] = None,
                    dev_status: Optional[torch.Tensor] = None, workspace: Optional[Workspace] = None,
@@ -569,6 +616,7 @@ def sv_tree_expand(draft_rows: torch.Tensor, exp_node: Optional[torch.Tensor], t
     return _invoke("sv_tree_expand", args, keep, next_exp)
 
 
+@_on_call_stream
 def sv_tree_finalize(state: DraftTreeState, n_nodes: int, mask: bool = True,
                      dev_status: Optional[torch.Tensor] = None, stream=None, out=None):
     """Rerank and flatten: returns (parent, token, depth, cand [B, n_nodes] int32,
@@ -615,6 +663,7 @@ def _shard_common(target_cols, draft_cols, bounds, shard, t_row_start, q_row_sta
     return head, B, k_max, t_rows, width, G, dev
 
 
+@_on_call_stream
 def sv_shard_stats(target_cols, draft_cols, bounds, shard, t_row_start, q_row_start, draft_ids, draft_len,
                    temperature, out=None, workspace: Optional[Workspace] = None, stream=None):
     """Step 1 of the sharded verify: (pairs [t_rows, 2], at [B, k_max, 2]) of
@@ -634,6 +683,7 @@ def sv_shard_stats(target_cols, draft_cols, bounds, shard, t_row_start, q_row_st
                                             draft_len, pairs, at, ws), (pairs, at))
 
 
+@_on_call_stream
 def sv_shard_residual(target_cols, draft_cols, bounds, shard, t_row_start, q_row_start, draft_ids, draft_len,
                       temperature, uniforms, all_pairs, all_at, mass, workspace: Workspace, stream=None):
     """Step 2: writes this shard's row of mass [G, B, 3] (float64)."""
@@ -650,6 +700,7 @@ def sv_shard_residual(target_cols, draft_cols, bounds, shard, t_row_start, q_row
                                                draft_len, uniforms, all_pairs, all_at, mass, ws), mass)
 
 
+@_on_call_stream
 def sv_shard_draw(target_cols, draft_cols, bounds, shard, t_row_start, q_row_start, draft_ids, draft_len,
                   temperature, uniforms, all_pairs, mass, out, max_new: Optional[torch.Tensor] = None,
                   eos_id: int = -1, dev_status: Optional[torch.Tensor] = None,

@@ -1,6 +1,7 @@
 // libspecverify C ABI: argument checks, workspace layout, kernel launches.
 // The operations and their contracts are documented in include/specverify.h.
 #include "specverify.h"
+#include "specverify_debug.h"
 
 #include <hip/hip_runtime.h>
 
@@ -18,7 +19,7 @@ namespace {
 
 thread_local char g_err[512] = "";
 
-// Measurement hook (sv_time_statistics_once): events recorded around the
+// Measurement hook (sv_debug_time_statistics_once): events recorded around the
 // statistics kernel of this thread's next sampled chain call.
 thread_local hipEvent_t g_stat_ev[2] = {nullptr, nullptr};
 
@@ -86,54 +87,48 @@ int cu_count() {
 }
 
 
-// Shared tail of the sampled and tree verify: the split into G workgroups per
-// request, the workspace carve-up and the launches.  Chains whose requests
-// own their rows take the lazy statistics (rows after the break are skipped);
-// chains with shared rows, and any call asking for diagnostics, take the
-// softmax partials of every row.  Trees compute statistics in the walk.
-sv_status launch_walk_call(int mode, int32_t t_dtype, int32_t q_dtype, sv::WalkArgs& a, int64_t rows,
-                           int64_t nodes, int64_t node_cap, void* workspace, hipStream_t st,
-                           const char* what) {
-  const bool chain = mode == sv::kWalkChain;
+// Whether a sampled chain call takes the lazy statistics (k_chain_stats):
+// requests own their rows (enough rows for every request's own), and a row
+// has at least two waves of statistics blocks (8 resident blocks per CU), so
+// a row's decision is known before the next row's blocks start; with fewer,
+// streaming every row is faster.  Diagnostics need every row's statistics.
+bool chain_lazy(int64_t B, int64_t t_rows, int64_t V, int64_t k_max, bool diag) {
+  const int64_t nseg = sv::row_segments(t_rows, V);
+  return !diag && sv::sample_tiles(V) > 1 && t_rows >= k_max + 1 && 2 * t_rows >= B * (k_max + 1) &&
+         B * nseg >= 2 * 8 * static_cast<int64_t>(std::max(cu_count(), 1)) && (k_max + 1) * B * nseg <= kMaxGrid;
+}
+
+// Workspace of a sampled chain call with these sizes (either statistics path).
+size_t sample_need(int64_t B, int64_t t_rows, int64_t V, int64_t k_max) {
+  if (B == 0) return 0;
+  const int64_t R = std::max<int64_t>(1, std::min<int64_t>(t_rows, k_max + 1));
+  return sv::chain_layout(B, t_rows, V, R).end;
+}
+
+// The sampled chain verify: the statistics kernel (the partials of every
+// row, which zeroes the draw's words on the side, or a fill kernel and the
+// lazy statistics), then the draw (k_chain_draw); a one-tile vocabulary is one
+// wave's work per request (k_walk_small).
+sv_status launch_chain_call(int32_t t_dtype, int32_t q_dtype, sv::WalkArgs& a, void* workspace, hipStream_t st,
+                            const char* what) {
   const int64_t ntiles = sv::sample_tiles(a.V);
-  const int64_t max_sync = sv::walk_max_sync(nodes);
+  const bool lazy = chain_lazy(a.B, a.t_rows, a.V, a.k_max, a.diag != nullptr);
+  const sv::ChainLayout L = sv::chain_layout(a.B, a.t_rows, a.V, lazy ? a.k_max + 1 : 0);
   char* ws = static_cast<char*>(workspace);
-  // G from the occupancy at the largest slice this kernel may get
-  const size_t lds_max = sv::walk_lds_bytes(static_cast<int>(node_cap), static_cast<int>(ntiles));
-  const int occ = sv::walk_occupancy(mode, t_dtype, q_dtype, lds_max);
-  const int64_t resident = static_cast<int64_t>(occ) * std::max(cu_count(), 1);
-  a.G = std::min<int32_t>(sv::walk_groups(a.B, a.V, resident),
-                          static_cast<int32_t>(sv::walk_groups_bound(a.B)));
-  // The point-mass walk makes one pass per visited node and then only
-  // exchanges per rejected candidate: the fewest workgroups that still give
-  // every wave at most one tile per pass (measured 7% faster on the 60-node
-  // trees at V = 128,256 than one workgroup per CU).
-  if (mode == sv::kWalkPoint) {
-    constexpr int kWaves = sv::kWalkBlock / 64;
-    a.G = std::min<int32_t>(a.G, static_cast<int32_t>(std::max<int64_t>(1, (ntiles + kWaves - 1) / kWaves)));
-  }
-  // Lazy statistics skip a row only when its request's decision on the row
-  // before is known by the time the row's blocks start, which needs at least
-  // two waves of statistics blocks per row (8 resident blocks per CU); with
-  // fewer, streaming every row is faster.
-  const bool lazy = chain && a.diag == nullptr && ntiles > 1 && a.t_rows >= a.k_max + 1 &&
-                    2 * static_cast<int64_t>(a.t_rows) >= static_cast<int64_t>(a.B) * (a.k_max + 1) &&
-                    static_cast<int64_t>(a.B) * a.nseg >= 2 * 8 * static_cast<int64_t>(std::max(cu_count(), 1)) &&
-                    static_cast<int64_t>(a.k_max + 1) * a.B * a.nseg <= kMaxGrid;
-  const int64_t lazy_R = lazy ? a.k_max + 1 : 0;
-  const sv::WalkLayout L = sv::walk_layout(a.B, rows, a.V, a.G, max_sync, lazy_R);
-  a.ntiles = static_cast<int32_t>(ntiles);
-  a.tile_cap = static_cast<int32_t>((ntiles + a.G - 1) / a.G);
-  a.node_cap = static_cast<int32_t>(node_cap);
-  a.max_sync = static_cast<int32_t>(max_sync);
-  a.spin_limit = sv::kSpinLimit;
-  a.slots = reinterpret_cast<uint64_t*>(ws + L.slots_off);
-  a.partial = reinterpret_cast<const float2*>(ws + L.partial_off);
-  if (static_cast<int64_t>(a.B) * a.G > kMaxGrid) return fail(SV_E_ARG, "too many requests");
+  float2* partial = reinterpret_cast<float2*>(ws + L.partial_off);
+  // tiles per wave of the draw: the fewest that keep every draw block resident
+  // at once (each block pays its prologue's load rounds once)
+  const size_t draw_lds = static_cast<size_t>(ntiles) * 2 * sizeof(double);
+  const int64_t resident =
+      static_cast<int64_t>(sv::draw_occupancy(t_dtype, q_dtype, draw_lds)) * std::max(cu_count(), 1);
+  const int64_t quads = (ntiles + sv::kDrawTiles - 1) / sv::kDrawTiles;
+  const int64_t tpw = std::min<int64_t>(sv::kMaxDrawTpw, std::max<int64_t>(1, (a.B * quads + resident - 1) / resident));
+  const int64_t nblk = sv::draw_blocks(a.V, tpw);
+  if (static_cast<int64_t>(a.B) * nblk > kMaxGrid) return fail(SV_E_ARG, "too many requests");
   (void)hipGetLastError();
-  bool clear_slots = true;
+  hipError_t e = hipSuccess;
   if (lazy) {
-    hipError_t e = sv::launch_clear(ws + L.slots_off, L.end - L.slots_off, st);
+    e = sv::launch_clear(ws + L.rcnt_off, L.end - L.rcnt_off, st);
     if (e != hipSuccess) return device_fail(e, what);
     sv::ChainStatsArgs c{};
     c.tgt = a.tgt;
@@ -162,26 +157,115 @@ sv_status launch_walk_call(int mode, int32_t t_dtype, int32_t q_dtype, sv::WalkA
     e = sv::launch_chain_stats(t_dtype, q_dtype, c, st);
     if (e != hipSuccess) return device_fail(e, what);
     stat_event(1, st);
-    a.stop = c.stop;
-    a.row_words = c.row_words;
-    clear_slots = false;
-  } else if (chain || a.diag != nullptr) {  // the walk reads every row's partials
-    const int64_t slot_words = static_cast<int64_t>(L.stop_off - L.slots_off) / 8;
-    if (chain) stat_event(0, st);
+  } else {
+    const bool small = ntiles == 1;  // k_walk_small reads only the partials
+    stat_event(0, st);
+    e = sv::launch_row_stats(t_dtype, a.tgt, a.t_rows, a.V, a.nseg, a.c, partial, st,
+                             small ? nullptr : reinterpret_cast<uint64_t*>(ws + L.rcnt_off),
+                             small ? 0 : static_cast<int64_t>(L.stop_off - L.rcnt_off) / 8);
+    if (e != hipSuccess) return device_fail(e, what);
+    stat_event(1, st);
+    if (small) {  // one tile: one wave per request does the whole round
+      a.partial = partial;
+      a.ntiles = 1;
+      e = sv::launch_walk_small(t_dtype, q_dtype, a, st);
+      return e == hipSuccess ? SV_OK : device_fail(e, what);
+    }
+    if (a.diag != nullptr) {
+      a.partial = partial;
+      e = sv::launch_chain_diag(t_dtype, q_dtype, a, st);
+      if (e != hipSuccess) return device_fail(e, what);
+    }
+  }
+  sv::ChainDrawArgs d{};
+  d.tgt = a.tgt;
+  d.dq = a.dq;
+  d.V = a.V;
+  d.c = a.c;
+  d.B = a.B;
+  d.k_max = a.k_max;
+  d.t_rows = a.t_rows;
+  d.q_rows = a.q_rows;
+  d.t_rs = a.t_rs;
+  d.q_rs = a.q_rs;
+  d.ids = a.ids;
+  d.dlen = a.dlen;
+  d.u = a.u;
+  d.seed = a.seed;
+  d.offset = a.offset;
+  d.max_new = a.max_new;
+  d.eos = a.eos;
+  d.nseg = a.nseg;
+  d.ntiles = static_cast<int32_t>(ntiles);
+  d.nblk = static_cast<int32_t>(nblk);
+  d.tpw = static_cast<int32_t>(tpw);
+  d.spin_limit = sv::kSpinLimit;
+  d.partial = lazy ? nullptr : partial;
+  d.stop = lazy ? reinterpret_cast<const uint32_t*>(ws + L.stop_off) : nullptr;
+  d.row_words = lazy ? reinterpret_cast<const uint64_t*>(ws + L.rows_off) : nullptr;
+  d.rcnt = reinterpret_cast<uint32_t*>(ws + L.rcnt_off);
+  d.tile_w = reinterpret_cast<uint64_t*>(ws + L.tw_off);
+  d.tile_p = reinterpret_cast<uint64_t*>(ws + L.tp_off);
+  d.blk_q = reinterpret_cast<uint64_t*>(ws + L.bq_off);
+  d.out_tok = a.out_tok;
+  d.out_cnt = a.out_cnt;
+  d.out_acc = a.out_acc;
+  d.resid = a.resid;
+  d.status = a.status;
+  e = sv::launch_chain_draw(t_dtype, q_dtype, d, st);
+  return e == hipSuccess ? SV_OK : device_fail(e, what);
+}
+
+// Shared tail of the three tree verifies: the split into G workgroups per
+// request, the workspace carve-up and the launches.  The walk computes a
+// node's statistics when it gets there; only diagnostics need the partials
+// of every row.
+sv_status launch_walk_call(int mode, int32_t t_dtype, int32_t q_dtype, sv::WalkArgs& a, int64_t rows,
+                           int64_t nodes, int64_t node_cap, void* workspace, hipStream_t st,
+                           const char* what) {
+  const int64_t ntiles = sv::sample_tiles(a.V);
+  const int64_t max_sync = sv::walk_max_sync(nodes);
+  char* ws = static_cast<char*>(workspace);
+  // G from the occupancy at the largest slice this kernel may get
+  const size_t lds_max = sv::walk_lds_bytes(static_cast<int>(node_cap), static_cast<int>(ntiles));
+  const int occ = sv::walk_occupancy(mode, t_dtype, q_dtype, lds_max);
+  const int64_t resident = static_cast<int64_t>(occ) * std::max(cu_count(), 1);
+  a.G = std::min<int32_t>(sv::walk_groups(a.B, a.V, resident),
+                          static_cast<int32_t>(sv::walk_groups_bound(a.B)));
+  // The point-mass walk makes one pass per visited node and then only
+  // exchanges per rejected candidate: the fewest workgroups that still give
+  // every wave at most one tile per pass (measured 7% faster on the 60-node
+  // trees at V = 128,256 than one workgroup per CU).
+  if (mode == sv::kWalkPoint) {
+    constexpr int kWaves = sv::kWalkBlock / 64;
+    a.G = std::min<int32_t>(a.G, static_cast<int32_t>(std::max<int64_t>(1, (ntiles + kWaves - 1) / kWaves)));
+  }
+  const sv::WalkLayout L = sv::walk_layout(a.B, rows, a.V, a.G, max_sync);
+  a.ntiles = static_cast<int32_t>(ntiles);
+  a.tile_cap = static_cast<int32_t>((ntiles + a.G - 1) / a.G);
+  a.node_cap = static_cast<int32_t>(node_cap);
+  a.max_sync = static_cast<int32_t>(max_sync);
+  a.spin_limit = sv::kSpinLimit;
+  a.slots = reinterpret_cast<uint64_t*>(ws + L.slots_off);
+  a.partial = reinterpret_cast<const float2*>(ws + L.partial_off);
+  if (static_cast<int64_t>(a.B) * a.G > kMaxGrid) return fail(SV_E_ARG, "too many requests");
+  (void)hipGetLastError();
+  bool clear_slots = true;
+  if (a.diag != nullptr) {  // the diagnostics read every row's partials
+    const int64_t slot_words = static_cast<int64_t>(L.end - L.slots_off) / 8;
     const hipError_t e = sv::launch_row_stats(t_dtype, a.tgt, rows, a.V, a.nseg, a.c,
                                               reinterpret_cast<float2*>(ws + L.partial_off), st,
                                               a.slots, slot_words);
     if (e != hipSuccess) return device_fail(e, what);
-    if (chain) stat_event(1, st);
     clear_slots = false;  // the statistics kernel zeroed the exchange words
   }
-  // Tree walks zero their own exchange words, certified by a ticket unique to
+  // The walks zero their own exchange words, certified by a ticket unique to
   // the call.  A captured call would replay one ticket, so under stream
   // capture the words are zeroed by a kernel before the walk instead.
   a.arrive = nullptr;
   a.ticket = 0;
   hipStreamCaptureStatus cap = hipStreamCaptureStatusActive;
-  if (!chain && a.G > 1 && hipStreamIsCapturing(st, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone) {
+  if (a.G > 1 && hipStreamIsCapturing(st, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone) {
     a.arrive = reinterpret_cast<uint64_t*>(ws + L.arrive_off);
     a.ticket = next_ticket();
     clear_slots = false;
@@ -217,7 +301,7 @@ size_t sv_workspace_bytes(int op, int64_t batch, int64_t total_rows, int64_t voc
     case SV_OP_TREE:
       if (batch == 0) return 0;
       return sv::walk_layout(batch, total_rows, vocab, sv::walk_groups_bound(batch),
-                             sv::walk_max_sync(total_rows / batch), 0).end;
+                             sv::walk_max_sync(total_rows / batch)).end;
     case SV_OP_TREE_EXPAND:  // total_rows = batch * expanded nodes per request
       return sv::align256(static_cast<size_t>(total_rows * sv::tree_topk_segments(total_rows, vocab)) *
                           sv::kMaxTreeTop * 8);
@@ -227,18 +311,19 @@ size_t sv_workspace_bytes(int op, int64_t batch, int64_t total_rows, int64_t voc
       const size_t tiles = static_cast<size_t>(batch * sv::sample_tiles(vocab)) * 16;
       return sv::align256(std::max(partials, state + tiles));
     }
-    case SV_OP_SAMPLE: {
-      // a request has at most min(t_rows, 256) rows
-      const int64_t R = std::min<int64_t>(total_rows, sv::kMaxChainRows);
-      return sv::walk_layout(batch, total_rows, vocab, sv::walk_groups_bound(batch), sv::walk_max_sync(R),
-                             R).end;
-    }
+    case SV_OP_SAMPLE:  // any k_max the rows allow (a request has at most min(t_rows, 256) rows)
+      return sample_need(batch, total_rows, vocab, std::min<int64_t>(total_rows, sv::kMaxChainRows) - 1);
     default:
       return 0;
   }
 }
 
-sv_status sv_time_statistics_once(void* before, void* after) {
+size_t sv_sample_workspace_bytes(int64_t batch, int64_t t_rows, int64_t vocab, int32_t k_max) {
+  if (batch < 0 || t_rows < 0 || vocab <= 0 || k_max < 0 || k_max >= sv::kMaxChainRows) return 0;
+  return sample_need(batch, t_rows, vocab, k_max);
+}
+
+sv_status sv_debug_time_statistics_once(void* before, void* after) {
   if ((before == nullptr) != (after == nullptr)) return fail(SV_E_ARG, "give both events or neither");
   g_stat_ev[0] = static_cast<hipEvent_t>(before);
   g_stat_ev[1] = static_cast<hipEvent_t>(after);
@@ -362,7 +447,7 @@ static sv_status sample_impl(const void* target_logits, int32_t t_dtype, int32_t
     return fail(SV_E_ARG, "null pointer argument");
   const int32_t nseg = sv::row_segments(t_rows, vocab);
   if (static_cast<int64_t>(t_rows) * nseg > kMaxGrid) return fail(SV_E_ARG, "too many rows");
-  const size_t need = sv_workspace_bytes(SV_OP_SAMPLE, batch, t_rows, vocab);
+  const size_t need = sample_need(batch, t_rows, vocab, k_max);
   if (sv_status s = check_workspace(workspace, workspace_bytes, need)) return s;
 
   sv::WalkArgs a{};
@@ -390,10 +475,7 @@ static sv_status sample_impl(const void* target_logits, int32_t t_dtype, int32_t
   a.status = dev_status;
   a.diag = out_diag;
   a.nseg = nseg;
-  // a request has at most min(k_max + 1, t_rows) nodes
-  const int64_t nodes = std::min<int64_t>(k_max + 1, t_rows);
-  return launch_walk_call(sv::kWalkChain, t_dtype, q_dtype, a, t_rows, nodes, k_max + 1, workspace,
-                          static_cast<hipStream_t>(stream), what);
+  return launch_chain_call(t_dtype, q_dtype, a, workspace, static_cast<hipStream_t>(stream), what);
 }
 
 sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t_rows,

@@ -19,6 +19,8 @@
 // block whose request has already stopped at an earlier row does nothing.
 // Blocks never wait for a decision: a block that starts before the decision
 // it could use computes its segment anyway, which is only wasted bandwidth.
+// The draw (k_chain_draw) then takes the break row and its pair from the
+// words this kernel leaves.
 #include "common.hpp"
 #include "launch.hpp"
 #include "segment.hpp"
@@ -27,7 +29,8 @@
 namespace sv {
 
 // `clear` (optional, n16 16-byte words) is zeroed on the side, for the exchange
-// words of the walk that follows this kernel on the stream.
+// words of the kernel that follows this one on the stream (the chain draw, or
+// a tree walk asked for diagnostics).
 template <class D, bool NT>
 __global__ __launch_bounds__(kBlock) void k_row_stats(const void* __restrict__ rows, int64_t V,
                                                       int32_t nseg, float c,
@@ -78,7 +81,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
   const uint32_t sv = i > 0 ? __hip_atomic_load(stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
   if (i > k || k > a.k_max || ts < 0 || static_cast<int64_t>(ts) + k >= a.t_rows ||
       (k > 0 && (qs < 0 || static_cast<int64_t>(qs) + k > a.q_rows)))
-    return;  // no such row, or a request the walk reports as invalid
+    return;  // no such row, or a request the draw reports as invalid
   // Row i is not needed.  The stop word can change while the block's waves
   // read it, so some waves may leave and the rest form a partial pair; that
   // happens only once an earlier row has stopped the round, so row i's pair
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
     ok &= done;
     if (s < a.nseg) s_w[s] = v;
   }
-  // the canonical combine of the segment pairs (the walk combines the
+  // the canonical combine of the segment pairs (the draw combines the
   // partials of every row the same way)
   const MS row = wave_combine_segments(a.nseg, [&](int s) { return dec_ms(s_w[s]); });
   if (lane != 0) return;
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
     stop_here = !(row.s > 0.f && row.s < INFINITY);
     if (!stop_here && i < k) {
       if (x < 0 || x >= a.V) {
-        stop_here = true;  // the walk reports the token
+        stop_here = true;  // the draw reports the token
       } else {
         const float p = ex2(fmaf(lx, a.c, -row.m)) * (1.f / row.s);
         stop_here = !(u * qx < p);

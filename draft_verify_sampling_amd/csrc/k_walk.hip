@@ -1,4 +1,5 @@
-// Speculative-sampling verify as a walk: chain drafts and draft trees.
+// Speculative-sampling verify of draft trees as a walk, plus the one-wave
+// chain round for one-tile vocabularies and the diagnostics kernels.
 //
 // Method ("投机解码:为什么一个字都不改", sections "改进:接受概率 min(1, p/q),
 // 拒绝时从残差重采" and "一轮能出几个 token"; "Speculative Decoding II", EAGLE
@@ -9,11 +10,6 @@
 //   kept -> emit x_c, descend, reload p and q; rejected -> p <- norm(max(0, p - q)).
 //   With no child kept (or at a leaf) the last token is drawn from the current
 //   p: the smallest id whose running mass exceeds u times the total.
-// A chain of k drafts is the tree whose node c (c = 0..k) has parent c - 1:
-// node c reads target row t_row_start + c and draft row q_row_start + c, draft
-// x_{c-1} is node c's token, and u[i] tests node i + 1 and u[k] draws, as in
-// the tree.  A chain has at most one rejection; a full accept draws the bonus
-// token from p_k.
 //
 // Repeated residual updates against one q stay in closed form: after j
 // rejections the current distribution is max(0, p - c_j q) / R_j with
@@ -21,13 +17,8 @@
 // so every rejection costs one pass over the node's two rows that yields
 // R_{j+1} and the per-tile sums the final inverse-CDF draw needs.
 //
-// Statistics: a chain takes its rows' softmax pairs from a statistics kernel
-// that runs before the walk -- either the segment pairs of every row, which
-// the prologue combines and decides, or (lazy statistics) the break row and
-// that row's pair, already decided -- so the walk needs no pass before its
-// one weight pass.  A tree walk computes the statistics of a node when it
-// arrives there (one pass over that row), so only the rows of its kept path
-// are read.
+// Statistics: the walk computes the statistics of a node when it arrives there
+// (one pass over that row), so only the rows of its kept path are read.
 //
 // Work split: G workgroups of 1024 threads per request, G chosen by the host
 // from the occupancy of this kernel so that the whole grid is resident at
@@ -39,14 +30,14 @@
 // relaxed agent-scope atomic stores and reads the others' with relaxed
 // agent-scope atomic loads until all carry their valid bit.  The data travels
 // inside the atomic words, so no fence is needed.  The words start at zero:
-// for a chain the statistics kernel (or k_walk_clear) zeroes them before the
-// walk; in a tree walk each workgroup zeroes its own words at its start,
-// waits until those stores have completed, and then stores the call's
-// ticket, and the request's first exchange polls the G tickets before any
-// word, so no word left by an earlier call is read.  Every workgroup combines
-// the G words in the same order, so all of them take the same decisions.  The wait is bounded: on
-// expiry the workgroup sets the sync-timeout status bit and exits.  With G = 1
-// nothing is exchanged through memory.
+// each workgroup zeroes its own words at its start, waits until those stores
+// have completed, and then stores the call's ticket, and the request's first
+// exchange polls the G tickets before any word, so no word left by an earlier
+// call is read (under graph capture k_walk_clear zeroes them before the walk
+// instead).  Every workgroup combines the G words in the same order, so all
+// of them take the same decisions.  The wait is bounded: on expiry the
+// workgroup sets the sync-timeout status bit and exits.  With G = 1 nothing is
+// exchanged through memory.
 //
 // The last token is drawn by the workgroup whose slice holds u * R: one wave
 // scans the slice's tile sums (kept in LDS) and rescans the chosen tile.
@@ -65,7 +56,6 @@ constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
 constexpr int kMaxNodeGroups = kMaxTreeNodes / kWave;
 static_assert(2 * kMaxWalkGroups <= kWave, "one wave reads every exchanged word");
 static_assert(kMaxChainRows <= kWalkBlock, "one chain row per thread");
-constexpr int kPartStage = 2048;  // partials of a chain request staged in LDS
 
 struct Walk {
   const WalkArgs* a;
@@ -239,20 +229,17 @@ __device__ __forceinline__ int tile_owner(int t, int ntiles, int G) {
   return h;
 }
 
-// Outputs of an invalid request: every token slot -1, counts 0, status bits.
-// Threads [first, first + stride, ...) write.
-template <bool kChain>
+// Outputs of an invalid request: every token and path slot -1, counts 0,
+// status bits.  Threads [first, first + stride, ...) write.
 __device__ void walk_invalid(const WalkArgs& a, int b, int bits, int first, int stride) {
-  const int width = kChain ? a.k_max + 1 : a.N;
-  const int64_t o = static_cast<int64_t>(b) * width;
-  for (int c = first; c < width; c += stride) {
+  const int64_t o = static_cast<int64_t>(b) * a.N;
+  for (int c = first; c < a.N; c += stride) {
     a.out_tok[o + c] = -1;
-    if (!kChain) a.out_path[o + c] = -1;
+    a.out_path[o + c] = -1;
   }
   if (first == 0) {
     a.out_cnt[b] = 0;
     a.out_acc[b] = 0;
-    if (kChain && a.resid != nullptr) a.resid[b] = 0.f;
     flag(a.status, bits);
   }
 }
@@ -261,10 +248,9 @@ __device__ void walk_invalid(const WalkArgs& a, int b, int bits, int first, int 
 
 template <int kMode, class DT, class DQ>
 __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
-  constexpr bool kChain = kMode == kWalkChain;
   constexpr bool kPoint = kMode == kWalkPoint;
   constexpr bool kGreedy = kMode == kWalkGreedy;
-  constexpr bool kUseQ = kMode == kWalkChain || kMode == kWalkTree;  // reads draft rows
+  constexpr bool kUseQ = kMode == kWalkTree;  // reads draft rows
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ uint64_t s_kids[2][kMaxNodeGroups];
   __shared__ uint64_t s_x[2][2 * kMaxWalkGroups];
@@ -276,7 +262,6 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
   __shared__ double s_two[2];                            // point mass: one tile's sums
   __shared__ int s_ok[2];
   __shared__ int s_bad;
-  __shared__ float2 s_part[kChain ? kPartStage : 1];  // chain: partials of the request's rows
 
   // dynamic LDS: tile sums [2][tile_cap] doubles, then node arrays [node_cap]
   double* s_wt0 = reinterpret_cast<double*>(smem);
@@ -287,9 +272,7 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
   float* s_px = reinterpret_cast<float*>(s_path + a.node_cap);
   float* s_qx = s_px + a.node_cap;
   float* s_u = s_qx + a.node_cap;
-  float* s_m = s_u + a.node_cap;     // chain: softmax pair of every row, from the partials
-  float* s_S = s_m + a.node_cap;
-  int32_t* s_ex = reinterpret_cast<int32_t*>(s_S + a.node_cap);  // point mass: ids removed at cur
+  int32_t* s_ex = reinterpret_cast<int32_t*>(s_u + a.node_cap);  // point mass: ids removed at cur
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   // Workgroups are dealt to the 8 XCDs in turn (workgroup i to XCD i % 8), so
@@ -308,133 +291,45 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
   const int b = wk.b;
   const int64_t V = a.V;
 
-  // ---- the request: its nodes, rows and uniforms ----
-  int start = 0;           // the walk's first node (a lazy chain starts where it stops)
-  int N;                   // nodes (chain: k_b + 1)
-  int64_t trow0, qrow0;    // node c reads target row trow0 + c and draft row qrow0 + c
-  int extra = 0;           // status bits that do not invalidate
+  // ---- the request: its tree and uniforms ----
+  const int N = a.N;                                     // nodes
+  const int64_t trow0 = static_cast<int64_t>(b) * a.N;   // node c: target / draft row trow0 + c
+  const int64_t qrow0 = trow0;
   if (tid == 0) s_bad = 0;
-  if constexpr (kChain) {
-    // round 1: the request's row starts and draft count, its drafted tokens
-    // and its uniforms (their addresses depend on b only)
-    const int k = a.dlen[b];
-    const int ts = a.t_rs[b], qs = a.q_rs[b];
-    const int tokv = tid < a.k_max ? a.ids[static_cast<int64_t>(b) * a.k_max + tid] : -1;
-    const float uv = tid <= a.k_max ? slot_uniform(a.u, a.seed, a.offset, b, a.k_max + 1, tid) : 0.f;
-    if (k < 0 || k > a.k_max || ts < 0 || static_cast<int64_t>(ts) + k >= a.t_rows ||
-        (k > 0 && (qs < 0 || static_cast<int64_t>(qs) + k > a.q_rows))) {
-      if (wk.g == 0) walk_invalid<kChain>(a, b, kFlagBadRequest, tid, kWalkBlock);
-      return;
-    }
-    N = k + 1;
-    trow0 = ts;
-    qrow0 = qs;
-    if (a.max_new != nullptr && k > a.max_new[b]) extra = kFlagOverBudget;
-    __syncthreads();
-    // node c = draft c - 1 (parent c - 1); thread i holds draft i
-    const bool tok_ok = tokv >= 0 && tokv < V;
-    if (tid < N) {
-      s_par[tid] = tid - 1;
-      s_u[tid] = uv;
-    }
-    if (tid == 0) s_tok[0] = -1;
-    if (tid < k) {
-      s_tok[tid + 1] = tokv;
-      if (!tok_ok) atomicOr(&s_bad, kFlagBadToken);
-    }
-    if (a.stop != nullptr) {
-      // lazy statistics: the statistics kernel decided every row up to the
-      // one where the round stops; only that row's pair is needed here
-      __syncthreads();
-      if (const int bad = s_bad) {
-        if (wk.g == 0) walk_invalid<kChain>(a, b, bad, tid, kWalkBlock);
-        return;
-      }
-      const uint32_t sw = a.stop[b];
-      start = sw != 0 ? kMaxChainRows - static_cast<int>(sw) : k;
-      const uint64_t rw = a.row_words[static_cast<int64_t>(b) * (a.k_max + 1) + start];
-      if (tid == 0) {
-        s_m[start] = __uint_as_float(static_cast<uint32_t>(rw));
-        s_S[start] = (rw >> 63) ? __uint_as_float(static_cast<uint32_t>(rw >> 32) & 0x7fffffffu) : NAN;
-        if (start < k) {  // the draft after the kept prefix was not kept
-          s_px[start + 1] = 0.f;
-          s_qx[start + 1] = 1.f;
-        }
-      }
-      __syncthreads();
-    } else {
-      // round 2: every row's softmax partials (staged in LDS) and the target
-      // logit / draft probability at each drafted token
-      const int np = N * a.nseg;
-      const float2* pbase = a.partial + trow0 * a.nseg;
-      const bool staged = np <= kPartStage;
-      if (staged)
-        for (int i = tid; i < np; i += kWalkBlock) s_part[i] = pbase[i];
-      float lx = 0.f, qv = 0.f;
-      if (tid < k && tok_ok) {
-        lx = DT::at(row_ptr<DT>(a.tgt, trow0 + tid, V), tokv);
-        qv = DQ::at(row_ptr<DQ>(a.dq, qrow0 + tid, V), tokv);
-      }
-      __syncthreads();
-      if (const int bad = s_bad) {
-        if (wk.g == 0) walk_invalid<kChain>(a, b, bad, tid, kWalkBlock);
-        return;
-      }
-      for (int c = wid; c < N; c += kWalkWaves) {  // one wave per row
-        const float2* pp = staged ? s_part + c * a.nseg : pbase + static_cast<int64_t>(c) * a.nseg;
-        const MS acc = wave_combine_segments(a.nseg, [&](int sg) {
-          const float2 v = pp[sg];
-          return MS{v.x, v.y};
-        });
-        if (lane == 0) {
-          s_m[c] = acc.m;
-          s_S[c] = acc.s;
-        }
-      }
-      __syncthreads();
-      if (tid < k) {  // node tid + 1 is tested against row tid (its parent)
-        s_px[tid + 1] = ex2(fmaf(lx, a.c, -s_m[tid])) * (1.f / s_S[tid]);
-        s_qx[tid + 1] = qv;
-      }
-    }
-  } else {
-    // round 1: the tree and the uniforms (the greedy walk has none); this
-    // workgroup's exchange words are zeroed meanwhile
-    N = a.N;
-    trow0 = qrow0 = static_cast<int64_t>(b) * a.N;
-    if (a.arrive != nullptr) {
-      uint64_t* own = a.slots + static_cast<int64_t>(b) * a.max_sync * 2 * a.G + 2 * wk.g;
-      for (int j = tid; j < 2 * a.max_sync; j += kWalkBlock)
-        store_word(own + static_cast<int64_t>(j >> 1) * 2 * a.G + (j & 1), 0ull);
-    }
-    __syncthreads();
-    for (int c = tid; c < N; c += kWalkBlock) {
-      const int par = a.parent[trow0 + c];
-      const int tok = a.token[trow0 + c];
-      int bad = 0;
-      if (c == 0 ? par != -1 : (par < 0 || par >= c)) bad |= kFlagBadTree;
-      if (c > 0 && (tok < 0 || tok >= V)) bad |= kFlagBadToken;
-      if (bad) atomicOr(&s_bad, bad);
-      s_par[c] = par;
-      s_tok[c] = tok;
-      s_u[c] = kGreedy ? 0.f : slot_uniform(a.u, a.seed, a.offset, b, N, c);
-    }
-    // every thread's zeroing stores have completed before the barrier, so
-    // the ticket stored after it certifies them
-    if (a.arrive != nullptr) asm volatile("s_waitcnt vmcnt(0)");
-    __syncthreads();
-    if (a.arrive != nullptr && tid == 0) store_word(a.arrive + static_cast<int64_t>(b) * a.G + wk.g, a.ticket);
-    if (const int bad = s_bad) {
-      if (wk.g == 0) walk_invalid<kChain>(a, b, (bad & kFlagBadTree) ? kFlagBadTree : bad, tid, kWalkBlock);
-      return;
-    }
+  // the tree and the uniforms (the greedy walk has none); this workgroup's
+  // exchange words are zeroed meanwhile
+  if (a.arrive != nullptr) {
+    uint64_t* own = a.slots + static_cast<int64_t>(b) * a.max_sync * 2 * a.G + 2 * wk.g;
+    for (int j = tid; j < 2 * a.max_sync; j += kWalkBlock)
+      store_word(own + static_cast<int64_t>(j >> 1) * 2 * a.G + (j & 1), 0ull);
+  }
+  __syncthreads();
+  for (int c = tid; c < N; c += kWalkBlock) {
+    const int par = a.parent[trow0 + c];
+    const int tok = a.token[trow0 + c];
+    int bad = 0;
+    if (c == 0 ? par != -1 : (par < 0 || par >= c)) bad |= kFlagBadTree;
+    if (c > 0 && (tok < 0 || tok >= V)) bad |= kFlagBadToken;
+    if (bad) atomicOr(&s_bad, bad);
+    s_par[c] = par;
+    s_tok[c] = tok;
+    s_u[c] = kGreedy ? 0.f : slot_uniform(a.u, a.seed, a.offset, b, N, c);
+  }
+  // every thread's zeroing stores have completed before the barrier, so
+  // the ticket stored after it certifies them
+  if (a.arrive != nullptr) asm volatile("s_waitcnt vmcnt(0)");
+  __syncthreads();
+  if (a.arrive != nullptr && tid == 0) store_word(a.arrive + static_cast<int64_t>(b) * a.G + wk.g, a.ticket);
+  if (const int bad = s_bad) {
+    if (wk.g == 0) walk_invalid(a, b, (bad & kFlagBadTree) ? kFlagBadTree : bad, tid, kWalkBlock);
+    return;
   }
 
   // ---- the walk ----
   constexpr int kNodesPerThread = kMaxTreeNodes / kWalkBlock;
   const int ngroups = (N + kWave - 1) / kWave;
-  int n_emit = start, fallback = 0, step = 0, npass = 0, tiles_buf = -1;
-  int cur = start;
+  int n_emit = 0, fallback = 0, step = 0, npass = 0, tiles_buf = -1;
+  int cur = 0;
   bool ok = true, synced = true;
   float coef = 0.f, R = 1.f;
   double Rd = 1.0;
@@ -453,11 +348,7 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
     }
     const void* trow = row_ptr<DT>(a.tgt, trow0 + cur, V);
     const void* qrow = kUseQ ? row_ptr<DQ>(a.dq, qrow0 + cur, V) : nullptr;
-    if constexpr (kChain) {
-      st = MS{s_m[cur], s_S[cur]};
-      ok = st.s > 0.f && st.s < INFINITY;
-      if (!ok) break;
-    } else if constexpr (kGreedy) {
+    if constexpr (kGreedy) {
       bool nan = false;
       if (!row_argmax<DT>(wk, trow, s_key, s_knan, amax, nan)) {
         synced = false;
@@ -616,7 +507,7 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
     return;
   }
   if (!ok) {
-    if (wk.g == 0) walk_invalid<kChain>(a, b, kFlagNonfinite | fallback | extra, tid, kWalkBlock);
+    if (wk.g == 0) walk_invalid(a, b, kFlagNonfinite | fallback, tid, kWalkBlock);
     return;
   }
 
@@ -672,7 +563,7 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
       base_s = base_last;
     }
     if (gs < 0) {  // no mass anywhere: cannot happen with S > 0; defined output
-      if (wk.g == 0) walk_invalid<kChain>(a, b, kFlagNonfinite | fallback | extra, tid, kWalkBlock);
+      if (wk.g == 0) walk_invalid(a, b, kFlagNonfinite | fallback, tid, kWalkBlock);
       return;
     }
     if (wk.g != gs || wid != 0) return;
@@ -684,7 +575,7 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
     for (int i = ta; i < tb; ++i) own += wt[i];
     TileHit hit;
     if (!wave_find_tile(wt, 1, nsl, own, target - base_s, hit)) {
-      walk_invalid<kChain>(a, b, kFlagNonfinite | fallback | extra, lane, kWave);
+      walk_invalid(a, b, kFlagNonfinite | fallback, lane, kWave);
       return;
     }
     hit.tile += wk.lo;
@@ -693,39 +584,15 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
   } else {
     if (wk.g != 0 || wid != 0) return;
   }
-  if constexpr (kChain) {
-    if (lane == 0) {
-      const int width = a.k_max + 1;
-      int32_t* out = a.out_tok + static_cast<int64_t>(b) * width;
-      int cnt = 0;
-      bool stop = false;
-      for (int i = 0; i < n_emit && !stop; ++i) {
-        const int32_t tok = s_tok[i + 1];
-        out[cnt++] = tok;
-        if (a.eos >= 0 && tok == a.eos) stop = true;
-      }
-      if (!stop) out[cnt++] = y;
-      if (a.max_new != nullptr) {
-        const int budget = a.max_new[b] > 0 ? a.max_new[b] : 0;
-        if (cnt > budget) cnt = budget;
-      }
-      for (int i = cnt; i < width; ++i) out[i] = -1;
-      a.out_cnt[b] = cnt;
-      a.out_acc[b] = n_emit;
-      if (a.resid != nullptr) a.resid[b] = static_cast<float>(Rd);
-      flag(a.status, fallback | extra);
-    }
-  } else {
-    const int64_t o = static_cast<int64_t>(b) * N;
-    for (int i = lane; i < N; i += kWave) {
-      a.out_tok[o + i] = i < n_emit ? s_tok[s_path[i]] : (i == n_emit ? y : -1);
-      a.out_path[o + i] = i < n_emit ? s_path[i] : -1;
-    }
-    if (lane == 0) {
-      a.out_cnt[b] = n_emit + 1;
-      a.out_acc[b] = n_emit;
-      flag(a.status, fallback);
-    }
+  const int64_t o = static_cast<int64_t>(b) * N;
+  for (int i = lane; i < N; i += kWave) {
+    a.out_tok[o + i] = i < n_emit ? s_tok[s_path[i]] : (i == n_emit ? y : -1);
+    a.out_path[o + i] = i < n_emit ? s_path[i] : -1;
+  }
+  if (lane == 0) {
+    a.out_cnt[b] = n_emit + 1;
+    a.out_acc[b] = n_emit;
+    flag(a.status, fallback);
   }
 }
 
@@ -971,11 +838,6 @@ const void* walk_fn() {
 const void* pick_walk(int mode, int t_dtype, int q_dtype) {
   const bool tb = t_dtype == kDtypeBF16, qb = q_dtype == kDtypeBF16;
   switch (mode) {
-    case kWalkChain:
-      if (tb && qb) return walk_fn<kWalkChain, BF16, BF16>();
-      if (tb) return walk_fn<kWalkChain, BF16, F32>();
-      if (qb) return walk_fn<kWalkChain, F32, BF16>();
-      return walk_fn<kWalkChain, F32, F32>();
     case kWalkTree:
       if (tb && qb) return walk_fn<kWalkTree, BF16, BF16>();
       if (tb) return walk_fn<kWalkTree, BF16, F32>();
@@ -990,10 +852,8 @@ const void* pick_walk(int mode, int t_dtype, int q_dtype) {
 
 template <int kMode, class DT, class DQ>
 void launch_t(const WalkArgs& a, size_t lds, bool clear_slots, hipStream_t stream) {
-  if (a.diag != nullptr) {
-    if constexpr (kMode == kWalkChain)
-      hipLaunchKernelGGL((k_chain_diag<DT, DQ>), dim3(static_cast<uint32_t>(a.B)), dim3(kWalkBlock), 0, stream, a);
-    else if constexpr (kMode == kWalkTree)
+  if constexpr (kMode == kWalkTree) {
+    if (a.diag != nullptr)
       hipLaunchKernelGGL((k_tree_diag<DT, DQ>), dim3(static_cast<uint32_t>(a.B)), dim3(kMaxTreeNodes), 0, stream, a);
   }
   if (a.G > 1 && clear_slots) {
@@ -1001,13 +861,6 @@ void launch_t(const WalkArgs& a, size_t lds, bool clear_slots, hipStream_t strea
     const int64_t blocks = std::min<int64_t>((n16 + kBlock - 1) / kBlock, 2048);
     hipLaunchKernelGGL(k_walk_clear, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream,
                        reinterpret_cast<uint4*>(a.slots), n16);
-  }
-  if constexpr (kMode == kWalkChain) {
-    if (a.ntiles == 1) {
-      const int64_t blocks = (static_cast<int64_t>(a.B) + kBlock / kWave - 1) / (kBlock / kWave);
-      hipLaunchKernelGGL((k_walk_small<DT, DQ>), dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream, a);
-      return;
-    }
   }
   hipLaunchKernelGGL((k_walk<kMode, DT, DQ>), dim3(static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.G)),
                      dim3(kWalkBlock), lds, stream, a);
@@ -1031,7 +884,7 @@ void launch_mode(int t_dtype, int q_dtype, const WalkArgs& a, size_t lds, bool c
 }  // namespace
 
 size_t walk_lds_bytes(int node_cap, int tile_cap) {
-  return static_cast<size_t>(tile_cap) * 2 * sizeof(double) + static_cast<size_t>(node_cap) * 9 * 4;
+  return static_cast<size_t>(tile_cap) * 2 * sizeof(double) + static_cast<size_t>(node_cap) * 7 * 4;
 }
 
 int walk_occupancy(int mode, int t_dtype, int q_dtype, size_t lds) {
@@ -1052,10 +905,42 @@ int walk_occupancy(int mode, int t_dtype, int q_dtype, size_t lds) {
   return slot;
 }
 
+hipError_t launch_chain_diag(int t_dtype, int q_dtype, const WalkArgs& a, hipStream_t stream) {
+  const bool tb = t_dtype == kDtypeBF16, qb = q_dtype == kDtypeBF16;
+  const dim3 grid(static_cast<uint32_t>(a.B)), block(kWalkBlock);
+  if (tb && qb)
+    hipLaunchKernelGGL((k_chain_diag<BF16, BF16>), grid, block, 0, stream, a);
+  else if (tb)
+    hipLaunchKernelGGL((k_chain_diag<BF16, F32>), grid, block, 0, stream, a);
+  else if (qb)
+    hipLaunchKernelGGL((k_chain_diag<F32, BF16>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_chain_diag<F32, F32>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_walk_small(int t_dtype, int q_dtype, const WalkArgs& a, hipStream_t stream) {
+  const bool tb = t_dtype == kDtypeBF16, qb = q_dtype == kDtypeBF16;
+  const int64_t blocks = (static_cast<int64_t>(a.B) + kBlock / kWave - 1) / (kBlock / kWave);
+  const dim3 grid(static_cast<uint32_t>(blocks)), block(kBlock);
+  if (a.diag != nullptr) {
+    const hipError_t e = launch_chain_diag(t_dtype, q_dtype, a, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (tb && qb)
+    hipLaunchKernelGGL((k_walk_small<BF16, BF16>), grid, block, 0, stream, a);
+  else if (tb)
+    hipLaunchKernelGGL((k_walk_small<BF16, F32>), grid, block, 0, stream, a);
+  else if (qb)
+    hipLaunchKernelGGL((k_walk_small<F32, BF16>), grid, block, 0, stream, a);
+  else
+    hipLaunchKernelGGL((k_walk_small<F32, F32>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_walk(int mode, int t_dtype, int q_dtype, const WalkArgs& a, size_t lds,
                        bool clear_slots, hipStream_t stream) {
   switch (mode) {
-    case kWalkChain: launch_mode<kWalkChain>(t_dtype, q_dtype, a, lds, clear_slots, stream); break;
     case kWalkTree: launch_mode<kWalkTree>(t_dtype, q_dtype, a, lds, clear_slots, stream); break;
     case kWalkPoint: launch_mode<kWalkPoint>(t_dtype, q_dtype, a, lds, clear_slots, stream); break;
     default: launch_mode<kWalkGreedy>(t_dtype, q_dtype, a, lds, clear_slots, stream); break;

@@ -77,29 +77,21 @@ inline int64_t walk_groups_bound(int64_t B) {
 // the visited nodes and the rejected children are distinct nodes, so n + 1.
 inline int64_t walk_max_sync(int64_t n_nodes) { return n_nodes + 1; }
 
-// Workspace of the sampled and tree verify, carved per call: softmax
-// partials of every row (shared-row chains and diagnostics), then the walk's
-// exchange words [B, max_sync, 2 G] and tickets [B, G], then the lazy chain
-// statistics: stop words [B], finished-segment counts [B, R], row pairs
-// [B, R] and segment pairs [B, R, nseg] (R = k_max + 1).  A chain's exchange
-// words and lazy statistics are zeroed before the call's walk; a tree walk's
-// workgroups zero their own exchange words and then store the call's ticket.
+// Workspace of the tree verify, carved per call: softmax partials of every
+// row (diagnostics only), then the walk's exchange words [B, max_sync, 2 G]
+// and tickets [B, G].  A walk's workgroups zero their own exchange words and
+// then store the call's ticket (or a fill kernel zeroes them first).
 struct WalkLayout {
-  size_t partial_off, slots_off, arrive_off, stop_off, count_off, rows_off, segs_off, end;
+  size_t partial_off, slots_off, arrive_off, end;
 };
 
-inline WalkLayout walk_layout(int64_t B, int64_t rows, int64_t V, int64_t G, int64_t max_sync,
-                              int64_t lazy_R) {
+inline WalkLayout walk_layout(int64_t B, int64_t rows, int64_t V, int64_t G, int64_t max_sync) {
   WalkLayout L{};
   const int64_t nseg = row_segments(rows, V);
   L.partial_off = 0;
   L.slots_off = align256(static_cast<size_t>(rows * nseg) * 8);
   L.arrive_off = L.slots_off + align256(G > 1 ? static_cast<size_t>(B * max_sync * 2 * G) * 8 : 0);
-  L.stop_off = L.arrive_off + align256(G > 1 ? static_cast<size_t>(B * G) * 8 : 0);
-  L.count_off = L.stop_off + align256(static_cast<size_t>(lazy_R > 0 ? B : 0) * 4);
-  L.rows_off = L.count_off + align256(static_cast<size_t>(B * lazy_R) * 4);
-  L.segs_off = L.rows_off + align256(static_cast<size_t>(B * lazy_R) * 8);
-  L.end = L.segs_off + align256(static_cast<size_t>(B * lazy_R * nseg) * 8);
+  L.end = L.arrive_off + align256(G > 1 ? static_cast<size_t>(B * G) * 8 : 0);
   return L;
 }
 
@@ -128,12 +120,91 @@ struct ChainStatsArgs {
 };
 
 hipError_t launch_chain_stats(int t_dtype, int q_dtype, const ChainStatsArgs& a, hipStream_t stream);
+
+// ---- the draw of a sampled chain round (k_chain_draw) ----
+// After the statistics kernel: the break row, the residual pass over it and
+// the inverse-CDF draw.  Grid B x nblk blocks; block r of a request sums the
+// kDrawTiles x tpw tiles from kDrawTiles tpw r on of the break row, wave w
+// taking every kDrawTiles-th of them.
+constexpr int kDrawTiles = 4;                  // waves per block
+constexpr int kMaxDrawTpw = 64;                // tiles per wave at most
+inline int32_t draw_blocks(int64_t V, int64_t tpw) {
+  const int64_t per = static_cast<int64_t>(kDrawTiles) * tpw;
+  return static_cast<int32_t>((sample_tiles(V) + per - 1) / per);
+}
+
+struct ChainDrawArgs {
+  const void* tgt;
+  const void* dq;
+  int64_t V;
+  float c;                   // log2(e) / T
+  int32_t B, k_max, t_rows, q_rows;
+  const int32_t* t_rs;
+  const int32_t* q_rs;
+  const int32_t* ids;
+  const int32_t* dlen;
+  const float* u;            // [B, k_max + 1], or null: Philox stream (seed, offset)
+  uint64_t seed, offset;
+  const int32_t* max_new;
+  int32_t eos;
+  int32_t nseg;              // statistics segments per row
+  int32_t ntiles;            // 2048-element tiles per row
+  int32_t nblk;              // draw blocks per request
+  int32_t tpw;               // tiles per wave of a draw block
+  int32_t spin_limit;
+  // the break row: decided here from the partials of every row (partial
+  // non-null), or by the lazy statistics (stop words and row pairs)
+  const float2* partial;     // [t_rows, nseg]
+  const uint32_t* stop;      // [B]
+  const uint64_t* row_words; // [B, k_max + 1]
+  // words zeroed by the statistics kernel (or a fill kernel) before the draw
+  uint32_t* rcnt;            // [B] finished draw blocks
+  uint64_t* tile_w;          // [B, ntiles] tile sums of the draw weights
+  uint64_t* tile_p;          // [B, ntiles] tile sums of p (zero-mass fallback)
+  uint64_t* blk_q;           // [B, nblk] class of the draft row's sum over each block's tiles
+  // outputs
+  int32_t* out_tok;
+  int32_t* out_cnt;
+  int32_t* out_acc;
+  float* resid;
+  int32_t* status;
+};
+
+hipError_t launch_chain_draw(int t_dtype, int q_dtype, const ChainDrawArgs& a, hipStream_t stream);
+// Resident draw blocks per CU (occupancy query, cached per dtype pair and LDS size).
+int draw_occupancy(int t_dtype, int q_dtype, size_t lds);
+
+// Workspace of the sampled chain verify, carved per call (every part 256-byte
+// aligned): softmax partials of every row [t_rows, nseg] float2; then the
+// words zeroed before each call's draw: draw counts [B], tile sums [B, ntiles]
+// twice and block classes [B, nblk]; then, for the lazy statistics (R =
+// k_max + 1 rows per request, 0 otherwise): stop words [B], finished-segment
+// counts [B, R], row pairs [B, R] and segment pairs [B, R, nseg].
+struct ChainLayout {
+  size_t partial_off, rcnt_off, tw_off, tp_off, bq_off, stop_off, count_off, rows_off, segs_off, end;
+};
+
+inline ChainLayout chain_layout(int64_t B, int64_t t_rows, int64_t V, int64_t lazy_R) {
+  ChainLayout L{};
+  // (the draw's block classes are sized for one tile per wave, the most blocks)
+  const int64_t nseg = row_segments(t_rows, V), nt = sample_tiles(V), nblk = draw_blocks(V, 1);
+  L.partial_off = 0;
+  L.rcnt_off = align256(static_cast<size_t>(t_rows * nseg) * 8);
+  L.tw_off = L.rcnt_off + align256(static_cast<size_t>(B) * 4);
+  L.tp_off = L.tw_off + align256(static_cast<size_t>(B * nt) * 8);
+  L.bq_off = L.tp_off + align256(static_cast<size_t>(B * nt) * 8);
+  L.stop_off = L.bq_off + align256(static_cast<size_t>(B * nblk) * 8);
+  L.count_off = L.stop_off + align256(static_cast<size_t>(lazy_R > 0 ? B : 0) * 4);
+  L.rows_off = L.count_off + align256(static_cast<size_t>(B * lazy_R) * 4);
+  L.segs_off = L.rows_off + align256(static_cast<size_t>(B * lazy_R) * 8);
+  L.end = L.segs_off + align256(static_cast<size_t>(B * lazy_R * nseg) * 8);
+  return L;
+}
 hipError_t launch_clear(void* p, size_t bytes, hipStream_t stream);
 
-// Walk variants: speculative sampling over a chain of drafts or a draft tree,
-// the tree with every candidate tested as a point mass on its own token, and
-// the greedy (T = 0) tree.
-enum WalkMode : int { kWalkChain = 0, kWalkTree = 1, kWalkPoint = 2, kWalkGreedy = 3 };
+// Walk variants over a draft tree: speculative sampling, every candidate
+// tested as a point mass on its own token, and the greedy (T = 0) tree.
+enum WalkMode : int { kWalkTree = 1, kWalkPoint = 2, kWalkGreedy = 3 };
 
 struct WalkArgs {
   const void* tgt;
@@ -179,18 +250,22 @@ struct WalkArgs {
   int32_t spin_limit;
   int32_t node_cap;         // LDS capacity in nodes (>= nodes of any request)
   int32_t tile_cap;         // LDS capacity in tiles (>= tiles of any slice)
-  // chain with lazy statistics: where the round stops and that row's pair
-  const uint32_t* stop;     // null: statistics from the partials of every row
-  const uint64_t* row_words;
 };
 
 size_t walk_lds_bytes(int node_cap, int tile_cap);
 int walk_occupancy(int mode, int t_dtype, int q_dtype, size_t lds);
-// Launches the walk (and the diagnostics, when asked for).  clear_slots: zero
-// the exchange words first (not needed when the statistics kernel did it).
-// The point-mass and greedy walks read no draft rows (q_dtype is ignored).
+// Launches a tree walk (and the diagnostics, when asked for).  clear_slots:
+// zero the exchange words first (not needed when the statistics kernel or the
+// walk itself does it).  The point-mass and greedy walks read no draft rows
+// (q_dtype is ignored).
 hipError_t launch_walk(int mode, int t_dtype, int q_dtype, const WalkArgs& a, size_t lds,
                        bool clear_slots, hipStream_t stream);
+// A sampled chain round with a one-tile vocabulary (V <= 2048): one wave per
+// request from the partials of every row (k_walk_small), and the diagnostics
+// when asked for.
+hipError_t launch_walk_small(int t_dtype, int q_dtype, const WalkArgs& a, hipStream_t stream);
+// Diagnostics of a sampled chain (M, S, p(x), q(x) per row) from a.partial.
+hipError_t launch_chain_diag(int t_dtype, int q_dtype, const WalkArgs& a, hipStream_t stream);
 
 struct GreedyArgs {
   const void* tgt;

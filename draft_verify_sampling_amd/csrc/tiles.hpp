@@ -178,13 +178,17 @@ __device__ __forceinline__ void wave_tile_sums_any(const DrawRow& r, int64_t V, 
 // lane's loads for a batch of runs are in flight before the first is used.
 // Falls back to wave_tile_sums_any tile by tile unless every tile is complete
 // and the rows are 16-byte aligned.
-template <class DT, class DQ, int kT, bool kQ = true>
+// kMaxBatch (0: up to 16 vectors) caps the runs whose loads are in flight
+// together, for callers that must keep registers low; the runs are summed in
+// the same order either way, so the sums are the same bits.
+template <class DT, class DQ, int kT, bool kQ = true, int kMaxBatch = 0>
 __device__ __forceinline__ void wave_tile_sums(const DrawRow& r, int64_t V, int t, int tstride,
                                                double (*v)[3]) {
   using L = TileRuns<DT, DQ>;
   constexpr int kPer = L::kPer;
   constexpr int kAll = kT * L::kRuns;                           // runs per lane in total
-  constexpr int kCap = (L::nt + L::nq == 2) ? 8 : 4;            // runs per batch (<= 16 vectors)
+  constexpr int kCap0 = (L::nt + L::nq == 2) ? 8 : 4;           // runs per batch (<= 16 vectors)
+  constexpr int kCap = (kMaxBatch > 0 && kMaxBatch < kCap0) ? kMaxBatch : kCap0;
   constexpr int kBatch = kAll < kCap ? kAll : kCap;
   static_assert(kAll % kBatch == 0, "whole batches");
   const int lane = threadIdx.x & (kWave - 1);

@@ -44,11 +44,12 @@
  *   that stream.
  * - The caller owns every buffer.  The library allocates nothing, keeps no
  *   pointer after returning, and holds no mutable state that affects results:
- *   only the thread-local text behind sv_last_error(), the thread-local
- *   measurement hook of sv_time_statistics_once(), per-device caches of
+ *   only the thread-local text behind sv_last_error(), per-device caches of
  *   launch parameters (compute-unit counts, kernel occupancy), and a
  *   process-wide counter that gives each tree-walk call a unique 64-bit
- *   ticket (outputs do not depend on its value).
+ *   ticket (outputs do not depend on its value).  (A measurement hook for
+ *   timing the statistics kernel inside a call is declared apart, in
+ *   specverify_debug.h; it is not part of the verify operations.)
  * - Row data: `t_dtype` / `q_dtype` select SV_F32 (float) or SV_BF16 (bfloat16
  *   bit patterns).  A row is `vocab` consecutive elements; row r starts at
  *   element r * vocab.  Any alignment is accepted; 16-byte aligned rows take the
@@ -114,10 +115,13 @@ typedef enum {
 #define SV_FLAG_FALLBACK 16     /* a residual max(0, p - q) had zero mass: the token was
                                    drawn from p (chain) / p was left unchanged (tree) */
 #define SV_FLAG_BAD_TREE 32     /* parent[b,0] != -1, or parent[b,c] not in [0,c) */
-#define SV_FLAG_SYNC_TIMEOUT 64 /* sampled / tree: the workgroups sharing a request did
-                                   not all report within the bounded wait (only possible
-                                   when other work keeps some of them from running); that
-                                   request's outputs are undefined */
+#define SV_FLAG_SYNC_TIMEOUT 64 /* tree verifies: the workgroups sharing a request did not
+                                   all report within the bounded wait (only possible when
+                                   other work on the device keeps some of them from being
+                                   scheduled); that request's outputs are undefined.  The
+                                   chain verifies never wait for a workgroup to be
+                                   scheduled and report this bit only if a word another
+                                   workgroup stored never becomes visible */
 
 int sv_abi_version(void);
 const char* sv_status_string(int status);
@@ -130,6 +134,13 @@ const char* sv_last_error(void);
  * tree expand: batch * n_exp draft rows) and `vocab` columns (shard: the
  * shard's column count).  Host function.  0 on bad input. */
 size_t sv_workspace_bytes(int op, int64_t batch, int64_t total_rows, int64_t vocab);
+
+/* Workspace bytes of one sv_verify_sample / sv_verify_sample_philox call with
+ * these sizes (batch requests, t_rows target rows, vocab columns, k_max drafts
+ * per request at most): what the call itself checks for, never more than
+ * sv_workspace_bytes(SV_OP_SAMPLE, batch, t_rows, vocab), which covers any
+ * k_max.  Host function.  0 on bad input (k_max outside [0, 255]) or batch 0. */
+size_t sv_sample_workspace_bytes(int64_t batch, int64_t t_rows, int64_t vocab, int32_t k_max);
 
 /* Streaming first pass of sv_verify_sample and sv_verify_tree, exposed on its
  * own: the temperature softmax of every row needs max(l)/T and
@@ -194,8 +205,10 @@ sv_status sv_verify_greedy(const void* target_logits, int32_t t_dtype, int32_t t
  * mass of the weights the last token was drawn from.
  * The round reads target rows 0..k_b (0..m when the lazy statistics apply:
  * requests own their rows, many statistics blocks per row, no out_diag), draft
- * row m and the entries at the drafted tokens.  temperature must be finite and
- * > 0; 1 <= vocab <= 4194304. */
+ * row m and the entries at the drafted tokens.  No workgroup of the call waits
+ * for another to be scheduled, so the call needs the device to itself in no
+ * way: it gives the same outputs beside any other work.  temperature must be
+ * finite and > 0; 1 <= vocab <= 4194304. */
 sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t_rows,
                            const void* draft_probs, int32_t q_dtype, int32_t q_rows,
                            int64_t vocab, const int32_t* t_row_start,
@@ -206,17 +219,6 @@ sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t
                            int32_t* out_tokens, int32_t* out_count, int32_t* out_accepted,
                            float* out_diag, float* out_resid, int32_t* dev_status,
                            void* workspace, size_t workspace_bytes, void* stream);
-
-/* Measurement hook, not an operation of the method: for the calling thread's
- * next sv_verify_sample or sv_verify_sample_philox call, record `before` (a
- * hipEvent_t) on that call's stream right before its statistics kernel and
- * `after` right after it (every such call with batch > 0 launches one: the
- * partials of every row, or the lazy statistics), so a caller can time that
- * kernel inside a real call.  The hook then disarms, also when that call
- * fails or has no requests.  NULL, NULL disarms it; giving one event only is
- * SV_E_ARG.  The events must stay valid until that call returns.  Host
- * function; thread-local. */
-sv_status sv_time_statistics_once(void* before, void* after);
 
 /* Counter-based uniforms (Philox4x64-10; Salmon, Moraes, Dror and Shaw,
  * "Parallel random numbers: as easy as 1, 2, 3", SC 2011), so that a serving

@@ -9,14 +9,17 @@ import pytest
 
 import draft_verify_sampling_amd as sv
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                      "include", "specverify.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADERS = [os.path.join(INCLUDE, h) for h in ("specverify.h", "specverify_debug.h")]
 
 
 def _declared():
-    text = open(HEADER).read()
-    return set(re.findall(r"^\s*(?:sv_status|int|int32_t|size_t|const char\*)\s+(sv_\w+)\s*\(",
-                          text, flags=re.M))
+    names = set()
+    for h in HEADERS:
+        text = open(h).read()
+        names |= set(re.findall(r"^\s*(?:sv_status|int|int32_t|size_t|const char\*)\s+(sv_\w+)\s*\(",
+                                text, flags=re.M))
+    return names
 
 
 @pytest.fixture(scope="module")
@@ -50,12 +53,33 @@ def test_workspace_sizes(lib):
     assert sv.workspace_bytes(7, 1, 1, 1) == 0
 
 
+def test_sample_workspace_sizes_know_k_max(lib):
+    """The exact query of a sampled chain call: the one-kernel round's words
+    at the headline shape (B = 64, k = 4, V = 248,320) come to well under the
+    any-k_max bound, which must still cover it; the bound covers every
+    k_max; bad sizes give 0."""
+    exact = sv.sample_workspace_bytes(64, 320, 248_320, 4)
+    bound = sv.workspace_bytes(sv.SV_OP_SAMPLE, 64, 320, 248_320)
+    assert exact % 256 == 0 and 0 < exact <= bound
+    # segment pairs [64, 5, 31] and tile sums [64, 122] x 2 at least
+    assert exact >= 64 * 5 * 31 * 8 + 2 * 64 * 122 * 8
+    assert exact < 1 << 20 and bound > 8 * exact
+    for k in (0, 1, 7, 30, 31, 63, 255):
+        rows = 64 * (k + 1)
+        assert 0 < sv.sample_workspace_bytes(64, rows, 151_936, k) <= \
+            sv.workspace_bytes(sv.SV_OP_SAMPLE, 64, rows, 151_936)
+    assert sv.sample_workspace_bytes(64, 320, 248_320, -1) == 0
+    assert sv.sample_workspace_bytes(64, 320, 248_320, 256) == 0
+    assert sv.sample_workspace_bytes(0, 320, 248_320, 4) == 0
+    assert sv.sample_workspace_bytes(64, 320, 0, 4) == 0
+
+
 def test_statistics_timing_hook_arguments(lib):
     # host-only: both events or neither (nothing is recorded without a call)
-    assert lib.sv_time_statistics_once(None, None) == 0
-    assert lib.sv_time_statistics_once(ctypes.c_void_p(256), None) == 1
+    assert lib.sv_debug_time_statistics_once(None, None) == 0
+    assert lib.sv_debug_time_statistics_once(ctypes.c_void_p(256), None) == 1
     assert "both events" in lib.sv_last_error().decode()
-    assert lib.sv_time_statistics_once(None, None) == 0
+    assert lib.sv_debug_time_statistics_once(None, None) == 0
 
 
 def _err(lib):
