@@ -31,6 +31,7 @@ __all__ = [
     "sv_tree_finalize", "SV_OP_TREE_EXPAND", "SV_OP_SHARD", "sv_shard_stats", "sv_shard_residual",
     "sv_shard_draw",
     "prepare_softmax_partials", "sv_debug_time_statistics_once", "sample_workspace_bytes",
+    "sv_verify_sample_noalloc",
 ]
 
 SV_F32, SV_BF16 = 0, 1
@@ -43,7 +44,7 @@ EXPORTS = ("sv_abi_version", "sv_status_string", "sv_last_error", "sv_workspace_
            "sv_ngram_draft", "sv_verify_greedy", "sv_verify_sample", "sv_verify_tree",
            "sv_verify_tree_greedy", "sv_verify_tree_pointmass", "sv_philox_uniforms",
            "sv_verify_sample_philox", "sv_tree_expand", "sv_tree_finalize", "sv_shard_stats",
-           "sv_shard_residual", "sv_shard_draw", "sv_sample_workspace_bytes",
+           "sv_shard_residual", "sv_shard_draw", "sv_sample_workspace_bytes", "sv_verify_sample_noalloc",
            "sv_debug_time_statistics_once")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -84,6 +85,8 @@ _SIGS = {
                                          F32, P, P, P, P, P, SZ, P]),
     "sv_shard_draw": (ctypes.c_int, [P, I32, I32, P, I32, I32, I64, P, I32, I32, P, P, P, P, I32, I32, F32,
                                      P, P, P, P, I32, P, P, P, P, P, P, SZ, P]),
+    "sv_verify_sample_noalloc": (ctypes.c_int, [P, I32, I32, P, I32, I32, I64, P, P, P, P, I32, I32,
+                                                F32, P, P, I32, P, P, P, P, P, P, P]),
     "sv_verify_sample_philox": (ctypes.c_int, [P, I32, I32, P, I32, I32, I64, P, P, P, P, I32, I32,
                                                F32, U64, U64, P, I32, P, P, P, P, P, P, P, SZ, P]),
     "sv_verify_tree_pointmass": (ctypes.c_int, [P, I32, I64, P, P, I32, I32, F32, P, P, P, P, P,
@@ -416,7 +419,7 @@ def sv_philox_uniforms(seed: int, offset: int, batch: int, slots: int, out: Opti
 
 
 def _sample(target, draft, t_row_start, q_row_start, draft_ids, draft_len, temperature, uniforms, philox,
-            max_new, eos_id, diag, dev_status, workspace, stream, out, resid):
+            max_new, eos_id, diag, dev_status, workspace, stream, out, resid, noalloc=False):
     t_rows, V = target.shape
     q_rows = draft.shape[0]
     if draft.shape[1] != V:
@@ -444,7 +447,7 @@ def _sample(target, draft, t_row_start, q_row_start, draft_ids, draft_len, tempe
         _shape(acc, "out accepted", (B,), torch.int32)
         _shape(dg, "out diag", (B, k_max + 1, 4), torch.float32)
         _shape(rs, "out resid", (B,), torch.float32)
-    ws = _workspace(workspace, dev, stream, sample_workspace_bytes(B, t_rows, V, k_max))
+    ws = None if noalloc else _workspace(workspace, dev, stream, sample_workspace_bytes(B, t_rows, V, k_max))
     head = (_dev(target, "target"), _dtype_code(target), t_rows,
             _dev(draft, "draft"), _dtype_code(draft), q_rows, V,
             _dev(t_row_start, "t_row_start", torch.int32, dev),
@@ -459,12 +462,26 @@ def _sample(target, draft, t_row_start, q_row_start, draft_ids, draft_len, tempe
             _dev(max_new, "max_new", torch.int32, dev), eos_id,
             _dev(tok, "out"), _dev(cnt, "cnt"), _dev(acc, "acc"),
             _dev(dg, "diag", torch.float32, dev), _dev(rs, "resid", torch.float32, dev),
-            _dev(dev_status, "dev_status", torch.int32, dev),
-            ws.data_ptr(), ws.numel(), _stream(stream))
+            _dev(dev_status, "dev_status", torch.int32, dev)) + \
+        (() if noalloc else (ws.data_ptr(), ws.numel())) + (_stream(stream),)
     keep = (target, draft, t_row_start, q_row_start, draft_ids, draft_len, uniforms, max_new, dev_status,
             tok, cnt, acc, dg, rs, ws)
-    name = "sv_verify_sample" if philox is None else "sv_verify_sample_philox"
+    name = "sv_verify_sample_noalloc" if noalloc else (
+        "sv_verify_sample" if philox is None else "sv_verify_sample_philox")
     return _invoke(name, args, keep, (tok, cnt, acc, dg, rs))
+
+
+@_on_call_stream
+def sv_verify_sample_noalloc(target: torch.Tensor, draft: torch.Tensor, t_row_start: torch.Tensor,
+                             q_row_start: torch.Tensor, draft_ids: torch.Tensor, draft_len: torch.Tensor,
+                             temperature: float, uniforms: torch.Tensor, max_new: Optional[torch.Tensor] = None,
+                             eos_id: int = -1, diag: bool = False, dev_status: Optional[torch.Tensor] = None,
+                             stream=None, out=None, resid: Optional[bool] = None):
+    """sv_verify_sample on the library's static device scratch (no workspace;
+    the C call allocates nothing).  Pass ``out`` to make the whole call free of
+    allocations; the returned tuple is as for sv_verify_sample."""
+    return _sample(target, draft, t_row_start, q_row_start, draft_ids, draft_len, temperature, uniforms, None,
+                   max_new, eos_id, diag, dev_status, None, stream, out, resid, noalloc=True)
 
 
 def prepare_verify_sample(*args, **kwargs):

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libspecverify.so")
-SOURCES = ["api.cpp", "k_stats.hip", "k_draw.hip", "k_walk.hip", "k_greedy.hip", "k_ngram.hip", "k_tree_build.hip", "k_shard.hip"]
+SOURCES = ["api.cpp", "k_stats.hip", "k_draw.hip", "k_walk.hip", "k_greedy.hip", "k_ngram.hip", "k_tree_build.hip", "k_shard.hip", "noalloc.hip"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-ffp-contract=off",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

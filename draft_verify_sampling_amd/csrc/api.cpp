@@ -13,6 +13,7 @@
 #include <cstdint>
 #include <cstdio>
 
+#include "api_internal.hpp"
 #include "launch.hpp"
 
 namespace {
@@ -99,7 +100,7 @@ bool chain_lazy(int64_t B, int64_t t_rows, int64_t V, int64_t k_max, bool diag) 
 }
 
 // Workspace of a sampled chain call with these sizes (either statistics path).
-size_t sample_need(int64_t B, int64_t t_rows, int64_t V, int64_t k_max) {
+size_t chain_need(int64_t B, int64_t t_rows, int64_t V, int64_t k_max) {
   if (B == 0) return 0;
   const int64_t R = std::max<int64_t>(1, std::min<int64_t>(t_rows, k_max + 1));
   return sv::chain_layout(B, t_rows, V, R).end;
@@ -276,6 +277,20 @@ sv_status launch_walk_call(int mode, int32_t t_dtype, int32_t q_dtype, sv::WalkA
 }
 }  // namespace
 
+namespace sv {
+
+sv_status set_error(sv_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+size_t sample_need(int64_t B, int64_t t_rows, int64_t V, int64_t k_max) { return chain_need(B, t_rows, V, k_max); }
+
+}  // namespace sv
+
 extern "C" {
 
 int sv_abi_version(void) { return SV_ABI_VERSION; }
@@ -312,7 +327,7 @@ size_t sv_workspace_bytes(int op, int64_t batch, int64_t total_rows, int64_t voc
       return sv::align256(std::max(partials, state + tiles));
     }
     case SV_OP_SAMPLE:  // any k_max the rows allow (a request has at most min(t_rows, 256) rows)
-      return sample_need(batch, total_rows, vocab, std::min<int64_t>(total_rows, sv::kMaxChainRows) - 1);
+      return chain_need(batch, total_rows, vocab, std::min<int64_t>(total_rows, sv::kMaxChainRows) - 1);
     default:
       return 0;
   }
@@ -320,7 +335,7 @@ size_t sv_workspace_bytes(int op, int64_t batch, int64_t total_rows, int64_t voc
 
 size_t sv_sample_workspace_bytes(int64_t batch, int64_t t_rows, int64_t vocab, int32_t k_max) {
   if (batch < 0 || t_rows < 0 || vocab <= 0 || k_max < 0 || k_max >= sv::kMaxChainRows) return 0;
-  return sample_need(batch, t_rows, vocab, k_max);
+  return chain_need(batch, t_rows, vocab, k_max);
 }
 
 sv_status sv_debug_time_statistics_once(void* before, void* after) {
@@ -447,7 +462,7 @@ static sv_status sample_impl(const void* target_logits, int32_t t_dtype, int32_t
     return fail(SV_E_ARG, "null pointer argument");
   const int32_t nseg = sv::row_segments(t_rows, vocab);
   if (static_cast<int64_t>(t_rows) * nseg > kMaxGrid) return fail(SV_E_ARG, "too many rows");
-  const size_t need = sample_need(batch, t_rows, vocab, k_max);
+  const size_t need = chain_need(batch, t_rows, vocab, k_max);
   if (sv_status s = check_workspace(workspace, workspace_bytes, need)) return s;
 
   sv::WalkArgs a{};
@@ -477,6 +492,23 @@ static sv_status sample_impl(const void* target_logits, int32_t t_dtype, int32_t
   a.nseg = nseg;
   return launch_chain_call(t_dtype, q_dtype, a, workspace, static_cast<hipStream_t>(stream), what);
 }
+
+}  // extern "C"
+
+sv_status sv::verify_sample_on(const void* target_logits, int32_t t_dtype, int32_t t_rows, const void* draft_probs,
+                               int32_t q_dtype, int32_t q_rows, int64_t vocab, const int32_t* t_row_start,
+                               const int32_t* q_row_start, const int32_t* draft_ids, const int32_t* draft_len,
+                               int32_t batch, int32_t k_max, float temperature, const float* uniforms,
+                               const int32_t* max_new, int32_t eos_id, int32_t* out_tokens, int32_t* out_count,
+                               int32_t* out_accepted, float* out_diag, float* out_resid, int32_t* dev_status,
+                               void* workspace, size_t workspace_bytes, void* stream, const char* what) {
+  return sample_impl(target_logits, t_dtype, t_rows, draft_probs, q_dtype, q_rows, vocab, t_row_start, q_row_start,
+                     draft_ids, draft_len, batch, k_max, temperature, uniforms, false, 0, 0, max_new, eos_id,
+                     out_tokens, out_count, out_accepted, out_diag, out_resid, dev_status, workspace,
+                     workspace_bytes, stream, what);
+}
+
+extern "C" {
 
 sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t_rows,
                            const void* draft_probs, int32_t q_dtype, int32_t q_rows, int64_t vocab,

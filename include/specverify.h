@@ -220,6 +220,28 @@ sv_status sv_verify_sample(const void* target_logits, int32_t t_dtype, int32_t t
                            float* out_diag, float* out_resid, int32_t* dev_status,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* sv_verify_sample for callers that cannot allocate device memory: code
+ * under HIP graph capture, serving loops that must not call hipMalloc, and
+ * harnesses that forbid it.  Arguments, outputs and results as for
+ * sv_verify_sample, without the workspace: the call uses a static device
+ * array of 8 MiB that each GPU the library runs on holds until the process
+ * ends (its address is looked up on the first call on each device).  It
+ * calls no allocating routine.  A call whose workspace need
+ * (sv_sample_workspace_bytes) exceeds 8 MiB returns SV_E_WORKSPACE and
+ * launches nothing.  Every call on one device shares that device's array:
+ * calls that may overlap on one device (other streams, other threads) race,
+ * and the caller must serialise them; what an earlier call left in the array
+ * never affects a later one. */
+sv_status sv_verify_sample_noalloc(const void* target_logits, int32_t t_dtype, int32_t t_rows,
+                                   const void* draft_probs, int32_t q_dtype, int32_t q_rows,
+                                   int64_t vocab, const int32_t* t_row_start,
+                                   const int32_t* q_row_start, const int32_t* draft_ids,
+                                   const int32_t* draft_len, int32_t batch, int32_t k_max,
+                                   float temperature, const float* uniforms,
+                                   const int32_t* max_new, int32_t eos_id, int32_t* out_tokens,
+                                   int32_t* out_count, int32_t* out_accepted, float* out_diag,
+                                   float* out_resid, int32_t* dev_status, void* stream);
+
 /* Counter-based uniforms (Philox4x64-10; Salmon, Moraes, Dror and Shaw,
  * "Parallel random numbers: as easy as 1, 2, 3", SC 2011), so that a serving
  * loop need not generate and upload the verify's uniforms.  Slot i of request
