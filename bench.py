@@ -334,7 +334,7 @@ def main():
                 e1.record()
             torch.cuda.synchronize()
             for i in range(n):
-                sv.sv_debug_time_statistics_once(*ev[i])
+                sv.sv_debug_time_kernel_once(*ev[i])
                 step(i)
             torch.cuda.synchronize()
             in_step = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3

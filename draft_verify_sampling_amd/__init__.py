@@ -30,7 +30,7 @@ __all__ = [
     "sv_philox_uniforms", "sv_verify_sample_philox", "DraftTreeState", "sv_tree_expand",
     "sv_tree_finalize", "SV_OP_TREE_EXPAND", "SV_OP_SHARD", "sv_shard_stats", "sv_shard_residual",
     "sv_shard_draw",
-    "prepare_softmax_partials", "sv_debug_time_statistics_once", "sample_workspace_bytes",
+    "prepare_softmax_partials", "sv_debug_time_kernel_once", "sv_debug_read_ceiling", "sample_workspace_bytes",
     "sv_verify_sample_noalloc",
 ]
 
@@ -45,7 +45,7 @@ EXPORTS = ("sv_abi_version", "sv_status_string", "sv_last_error", "sv_workspace_
            "sv_verify_tree_greedy", "sv_verify_tree_pointmass", "sv_philox_uniforms",
            "sv_verify_sample_philox", "sv_tree_expand", "sv_tree_finalize", "sv_shard_stats",
            "sv_shard_residual", "sv_shard_draw", "sv_sample_workspace_bytes", "sv_verify_sample_noalloc",
-           "sv_debug_time_statistics_once")
+           "sv_debug_time_kernel_once", "sv_debug_read_blocks", "sv_debug_read_ceiling")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -74,7 +74,9 @@ _SIGS = {
                                       P, P, P, P, P, SZ, P]),
     "sv_verify_tree_greedy": (ctypes.c_int, [P, I32, I64, P, P, I32, I32, P, P, P, P, P, P, SZ, P]),
     "sv_philox_uniforms": (ctypes.c_int, [U64, U64, I32, I32, P, P]),
-    "sv_debug_time_statistics_once": (ctypes.c_int, [P, P]),
+    "sv_debug_time_kernel_once": (ctypes.c_int, [P, P]),
+    "sv_debug_read_blocks": (I64, [I64]),
+    "sv_debug_read_ceiling": (ctypes.c_int, [P, I64, P, P]),
     "sv_sample_workspace_bytes": (SZ, [I64, I64, I64, I32]),
     "sv_tree_expand": (ctypes.c_int, [P, I32, I64, I32, I32, P, I32, I32, I32, P, P, P, P, P, P, P, P,
                                       P, SZ, P]),
@@ -136,11 +138,11 @@ def sample_workspace_bytes(batch: int, t_rows: int, vocab: int, k_max: int) -> i
     return int(load().sv_sample_workspace_bytes(batch, t_rows, vocab, k_max))
 
 
-def sv_debug_time_statistics_once(before=None, after=None):
+def sv_debug_time_kernel_once(before=None, after=None):
     """Arm the measurement hook (include/specverify_debug.h): the calling
-    thread's next sampled chain call records torch.cuda.Event `before` /
-    `after` around the kernel that streams its target rows (None, None
-    disarms).  The events are created here if they are not yet."""
+    thread's next verify call records torch.cuda.Event `before` / `after`
+    around the kernel that streams its rows (None, None disarms).  The events
+    are created here if they are not yet."""
     if (before is None) != (after is None):
         raise SpecVerifyError("give both events or neither")
     ptrs = []
@@ -151,7 +153,18 @@ def sv_debug_time_statistics_once(before=None, after=None):
         if not e.cuda_event:  # torch creates its events on first use
             e.record()
         ptrs.append(ctypes.c_void_p(e.cuda_event))
-    _check(load().sv_debug_time_statistics_once(*ptrs), "sv_debug_time_statistics_once")
+    _check(load().sv_debug_time_kernel_once(*ptrs), "sv_debug_time_kernel_once")
+
+
+def sv_debug_read_ceiling(buf: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """A pure streaming read of the bytes of `buf` (a measurement of the HBM
+    read ceiling); returns the per-block fold values (uint32 as int32)."""
+    nbytes = buf.numel() * buf.element_size()
+    nb = int(load().sv_debug_read_blocks(nbytes))
+    if out is None:
+        out = torch.empty((max(nb, 1),), dtype=torch.int32, device=buf.device)
+    args = (_dev(buf, "buf"), nbytes, _dev(out, "out"), _stream(stream))
+    return _invoke("sv_debug_read_ceiling", args, (buf, out), out)
 
 
 def _check(status: int, what: str):

@@ -20,8 +20,8 @@ namespace {
 
 thread_local char g_err[512] = "";
 
-// Measurement hook (sv_debug_time_statistics_once): events recorded around the
-// statistics kernel of this thread's next sampled chain call.
+// Measurement hook (sv_debug_time_kernel_once): events recorded around the
+// streaming kernel of this thread's next verify call.
 thread_local hipEvent_t g_stat_ev[2] = {nullptr, nullptr};
 
 // Records g_stat_ev[which] on `st` if the hook is armed.
@@ -42,6 +42,12 @@ sv_status device_fail(hipError_t e, const char* what) {
 }
 
 bool dtype_ok(int32_t d) { return d == SV_F32 || d == SV_BF16; }
+
+// Disarms the measurement hook when a verify call returns (it serves that
+// call at most).
+struct HookDone {
+  ~HookDone() { g_stat_ev[0] = g_stat_ev[1] = nullptr; }
+};
 
 sv_status check_workspace(const void* ws, size_t have, size_t need) {
   if (need == 0) return SV_OK;
@@ -272,7 +278,7 @@ sv_status launch_walk_call(int mode, int32_t t_dtype, int32_t q_dtype, sv::WalkA
     clear_slots = false;
   }
   const size_t lds = sv::walk_lds_bytes(a.node_cap, a.tile_cap);
-  const hipError_t e = sv::launch_walk(mode, t_dtype, q_dtype, a, lds, clear_slots, st);
+  const hipError_t e = sv::launch_walk(mode, t_dtype, q_dtype, a, lds, clear_slots, st, &stat_event);
   return e == hipSuccess ? SV_OK : device_fail(e, what);
 }
 }  // namespace
@@ -338,11 +344,23 @@ size_t sv_sample_workspace_bytes(int64_t batch, int64_t t_rows, int64_t vocab, i
   return chain_need(batch, t_rows, vocab, k_max);
 }
 
-sv_status sv_debug_time_statistics_once(void* before, void* after) {
+sv_status sv_debug_time_kernel_once(void* before, void* after) {
   if ((before == nullptr) != (after == nullptr)) return fail(SV_E_ARG, "give both events or neither");
   g_stat_ev[0] = static_cast<hipEvent_t>(before);
   g_stat_ev[1] = static_cast<hipEvent_t>(after);
   return SV_OK;
+}
+
+int64_t sv_debug_read_blocks(int64_t bytes) { return bytes <= 0 ? 0 : sv::read_blocks(bytes); }
+
+sv_status sv_debug_read_ceiling(const void* buf, int64_t bytes, uint32_t* out, void* stream) {
+  if (bytes < 0 || (bytes & 15) != 0) return fail(SV_E_ARG, "bytes must be a non-negative multiple of 16");
+  if (bytes == 0) return SV_OK;
+  if (buf == nullptr || out == nullptr || (reinterpret_cast<uintptr_t>(buf) & 15u) != 0)
+    return fail(SV_E_ARG, "buf (16-byte aligned) and out are needed");
+  (void)hipGetLastError();
+  const hipError_t e = sv::launch_read_ceiling(buf, bytes, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SV_OK : device_fail(e, "sv_debug_read_ceiling");
 }
 
 int32_t sv_softmax_segments(int64_t n_rows, int64_t vocab) {
@@ -370,6 +388,7 @@ sv_status sv_softmax_partials(const void* rows, int32_t dtype, int64_t n_rows, i
 sv_status sv_ngram_draft(const int32_t* ctx, const int32_t* ctx_len, int32_t batch,
                          int32_t ctx_stride, int32_t window, int32_t k, int32_t* draft_ids,
                          int32_t* draft_len, int32_t* dev_status, void* stream) {
+  HookDone hook_done;
   if (batch < 0) return fail(SV_E_ARG, "batch < 0");
   if (ctx_stride < 1) return fail(SV_E_ARG, "ctx_stride < 1");
   if (window < 1 || window > sv::kMaxWindow) return fail(SV_E_ARG, "window must be in [1, 64]");
@@ -378,8 +397,10 @@ sv_status sv_ngram_draft(const int32_t* ctx, const int32_t* ctx_len, int32_t bat
   if (ctx == nullptr || ctx_len == nullptr || draft_len == nullptr || (k > 0 && draft_ids == nullptr))
     return fail(SV_E_ARG, "null pointer argument");
   (void)hipGetLastError();
+  stat_event(0, static_cast<hipStream_t>(stream));
   const hipError_t e = sv::launch_ngram(ctx, ctx_len, batch, ctx_stride, window, k, draft_ids, draft_len,
                                         dev_status, static_cast<hipStream_t>(stream));
+  stat_event(1, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SV_OK : device_fail(e, "sv_ngram_draft launch");
 }
 
@@ -389,6 +410,7 @@ sv_status sv_verify_greedy(const void* target_logits, int32_t t_dtype, int32_t t
                            const int32_t* max_new, int32_t eos_id, int32_t* out_tokens,
                            int32_t* out_count, int32_t* out_accepted, int32_t* dev_status,
                            void* workspace, size_t workspace_bytes, void* stream) {
+  HookDone hook_done;
   if (!dtype_ok(t_dtype)) return fail(SV_E_DTYPE, "t_dtype must be SV_F32 or SV_BF16");
   if (batch < 0) return fail(SV_E_ARG, "batch < 0");
   if (vocab < 1 || vocab > INT32_MAX) return fail(SV_E_ARG, "vocab must be in [1, 2^31)");
@@ -408,8 +430,10 @@ sv_status sv_verify_greedy(const void* target_logits, int32_t t_dtype, int32_t t
   const hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   uint64_t* keys = static_cast<uint64_t*>(workspace);
+  stat_event(0, st);
   hipError_t e = sv::launch_row_argmax(t_dtype, target_logits, t_rows, vocab, nseg, keys, st);
   if (e != hipSuccess) return device_fail(e, "sv_verify_greedy argmax launch");
+  stat_event(1, st);
   sv::GreedyArgs a{};
   a.tgt = target_logits;
   a.V = vocab;
@@ -442,9 +466,7 @@ static sv_status sample_impl(const void* target_logits, int32_t t_dtype, int32_t
                              int32_t* out_tokens, int32_t* out_count, int32_t* out_accepted,
                              float* out_diag, float* out_resid, int32_t* dev_status, void* workspace,
                              size_t workspace_bytes, void* stream, const char* what) {
-  struct HookDone {  // the measurement hook serves this call at most
-    ~HookDone() { g_stat_ev[0] = g_stat_ev[1] = nullptr; }
-  } hook_done;
+  HookDone hook_done;
   if (!dtype_ok(t_dtype) || !dtype_ok(q_dtype))
     return fail(SV_E_DTYPE, "t_dtype and q_dtype must be SV_F32 or SV_BF16");
   if (batch < 0) return fail(SV_E_ARG, "batch < 0");
@@ -558,6 +580,7 @@ sv_status sv_verify_tree(const void* target_logits, int32_t t_dtype, const void*
                          int32_t* out_count, int32_t* out_accepted, int32_t* out_path,
                          float* out_diag, int32_t* dev_status, void* workspace,
                          size_t workspace_bytes, void* stream) {
+  HookDone hook_done;
   if (!dtype_ok(t_dtype) || !dtype_ok(q_dtype))
     return fail(SV_E_DTYPE, "t_dtype and q_dtype must be SV_F32 or SV_BF16");
   if (batch < 0) return fail(SV_E_ARG, "batch < 0");
@@ -605,6 +628,7 @@ static sv_status tree_variant(int mode, const void* target_logits, int32_t t_dty
                               int32_t* out_tokens, int32_t* out_count, int32_t* out_accepted,
                               int32_t* out_path, int32_t* dev_status, void* workspace,
                               size_t workspace_bytes, void* stream, const char* what) {
+  HookDone hook_done;
   if (!dtype_ok(t_dtype)) return fail(SV_E_DTYPE, "t_dtype must be SV_F32 or SV_BF16");
   if (batch < 0) return fail(SV_E_ARG, "batch < 0");
   if (n_nodes < 1 || n_nodes > sv::kMaxTreeNodes) return fail(SV_E_ARG, "n_nodes must be in [1, 1024]");

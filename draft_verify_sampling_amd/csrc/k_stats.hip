@@ -59,6 +59,43 @@ hipError_t launch_row_stats(int dtype, const void* rows, int64_t n_rows, int64_t
   return hipGetLastError();
 }
 
+// ---- the HBM read ceiling (a measurement tool) ----
+
+// Every thread issues its 16-byte non-temporal loads of a 64 KiB chunk at once
+// (as the statistics blocks do for a segment) and folds the words with xor;
+// one value per block is written so the loads cannot be dropped.
+__global__ __launch_bounds__(kBlock) void k_read_ceiling(const uint4* __restrict__ buf, int64_t n16,
+                                                         uint32_t* __restrict__ out) {
+  constexpr int U = 4 * kSegElems / 8 / kBlock;  // 16-byte vectors per thread
+  const int64_t v0 = static_cast<int64_t>(blockIdx.x) * (U * kBlock) + threadIdx.x;
+  uint4 w[U];
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    const int64_t v = v0 + j * kBlock;
+    w[j] = uint4{0u, 0u, 0u, 0u};
+    if (v < n16) {
+      const uint32_t* q = reinterpret_cast<const uint32_t*>(buf + v);
+      w[j] = uint4{__builtin_nontemporal_load(q), __builtin_nontemporal_load(q + 1),
+                   __builtin_nontemporal_load(q + 2), __builtin_nontemporal_load(q + 3)};
+    }
+  }
+  uint32_t x = 0;
+#pragma unroll
+  for (int j = 0; j < U; ++j) x ^= w[j].x ^ w[j].y ^ w[j].z ^ w[j].w;
+  __shared__ uint32_t sh[kBlock / kWave];
+  for (int o = 32; o >= 1; o >>= 1) x ^= static_cast<uint32_t>(__shfl_xor(static_cast<int>(x), o));
+  if ((threadIdx.x & (kWave - 1)) == 0) sh[threadIdx.x / kWave] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) out[blockIdx.x] = sh[0] ^ sh[1] ^ sh[2] ^ sh[3];
+}
+
+hipError_t launch_read_ceiling(const void* buf, int64_t bytes, uint32_t* out, hipStream_t stream) {
+  const int64_t blocks = read_blocks(bytes);
+  hipLaunchKernelGGL(k_read_ceiling, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream,
+                     static_cast<const uint4*>(buf), bytes / 16, out);
+  return hipGetLastError();
+}
+
 // ---- the lazy statistics of the chain verify ----
 
 

@@ -258,8 +258,10 @@ int walk_occupancy(int mode, int t_dtype, int q_dtype, size_t lds);
 // zero the exchange words first (not needed when the statistics kernel or the
 // walk itself does it).  The point-mass and greedy walks read no draft rows
 // (q_dtype is ignored).
+// `mark` (optional) is called with 0 right before the walk kernel's launch and
+// with 1 right after it (the measurement hook).
 hipError_t launch_walk(int mode, int t_dtype, int q_dtype, const WalkArgs& a, size_t lds,
-                       bool clear_slots, hipStream_t stream);
+                       bool clear_slots, hipStream_t stream, void (*mark)(int, hipStream_t) = nullptr);
 // A sampled chain round with a one-tile vocabulary (V <= 2048): one wave per
 // request from the partials of every row (k_walk_small), and the diagnostics
 // when asked for.
@@ -291,6 +293,10 @@ struct GreedyArgs {
 hipError_t launch_row_stats(int dtype, const void* rows, int64_t n_rows, int64_t V, int32_t nseg,
                             float c, float2* partial, hipStream_t stream, uint64_t* clear = nullptr,
                             int64_t clear_words = 0);
+// A pure streaming read of `bytes` (a multiple of 16) at buf, one 32-bit fold
+// per block into out: the HBM read ceiling (measurement tool).
+inline int64_t read_blocks(int64_t bytes) { return (bytes / 16 + 4 * kSegElems / 8 - 1) / (4 * kSegElems / 8); }
+hipError_t launch_read_ceiling(const void* buf, int64_t bytes, uint32_t* out, hipStream_t stream);
 hipError_t launch_row_argmax(int dtype, const void* rows, int64_t n_rows, int64_t V, int32_t nseg,
                              uint64_t* keys, hipStream_t stream);
 hipError_t launch_greedy_resolve(const GreedyArgs& a, hipStream_t stream);

@@ -12,16 +12,29 @@
 extern "C" {
 #endif
 
-/* For the calling thread's next sv_verify_sample or sv_verify_sample_philox
- * call, record `before` (a hipEvent_t) on that call's stream right before the
- * kernel that streams the target rows and `after` right after it (every such
- * call with batch > 0 launches one: the one-kernel round, the partials of
- * every row, or the lazy statistics), so a caller can time that kernel inside
- * a real call.  The hook then disarms, also when that call fails or has no
- * requests.  NULL, NULL disarms it; giving one event only is SV_E_ARG.  The
- * events must stay valid until that call returns.  Host function; the armed
- * events are thread-local state of the library. */
-sv_status sv_debug_time_statistics_once(void* before, void* after);
+/* For the calling thread's next call of a verify entry point, record
+ * `before` (a hipEvent_t) on that call's stream right before the kernel that
+ * streams the call's rows and `after` right after it, so a caller can time
+ * that kernel inside a real call:
+ *   sv_verify_sample / _philox / _noalloc   the row statistics (the partials
+ *                                            of every row, or the lazy
+ *                                            statistics);
+ *   sv_verify_greedy                         the row argmax;
+ *   sv_verify_tree / _greedy / _pointmass    the walk;
+ *   sv_ngram_draft                           the prompt-lookup kernel.
+ * The hook then disarms, also when that call fails or has no requests.
+ * NULL, NULL disarms it; giving one event only is SV_E_ARG.  The events must
+ * stay valid until that call returns.  Host function; the armed events are
+ * thread-local state of the library. */
+sv_status sv_debug_time_kernel_once(void* before, void* after);
+
+/* A pure streaming read of `bytes` bytes at `buf` (16-byte aligned, bytes a
+ * multiple of 16) with the same 16-byte non-temporal loads as the row
+ * statistics, each block folding its words into one 32-bit value written to
+ * out[block] (out: at least sv_debug_read_blocks(bytes) uint32 values): the
+ * practical HBM read ceiling the verify kernels are measured against. */
+int64_t sv_debug_read_blocks(int64_t bytes);
+sv_status sv_debug_read_ceiling(const void* buf, int64_t bytes, uint32_t* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -17,7 +17,7 @@ def _declared():
     names = set()
     for h in HEADERS:
         text = open(h).read()
-        names |= set(re.findall(r"^\s*(?:sv_status|int|int32_t|size_t|const char\*)\s+(sv_\w+)\s*\(",
+        names |= set(re.findall(r"^\s*(?:sv_status|int|int32_t|int64_t|size_t|const char\*)\s+(sv_\w+)\s*\(",
                                 text, flags=re.M))
     return names
 
@@ -74,12 +74,12 @@ def test_sample_workspace_sizes_know_k_max(lib):
     assert sv.sample_workspace_bytes(64, 320, 0, 4) == 0
 
 
-def test_statistics_timing_hook_arguments(lib):
+def test_kernel_timing_hook_arguments(lib):
     # host-only: both events or neither (nothing is recorded without a call)
-    assert lib.sv_debug_time_statistics_once(None, None) == 0
-    assert lib.sv_debug_time_statistics_once(ctypes.c_void_p(256), None) == 1
+    assert lib.sv_debug_time_kernel_once(None, None) == 0
+    assert lib.sv_debug_time_kernel_once(ctypes.c_void_p(256), None) == 1
     assert "both events" in lib.sv_last_error().decode()
-    assert lib.sv_debug_time_statistics_once(None, None) == 0
+    assert lib.sv_debug_time_kernel_once(None, None) == 0
 
 
 def _err(lib):
