@@ -2,25 +2,49 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c3]
 
-A step is one sampled chain verify (sv_verify_sample: softmax statistics of
-every target row, accept scan, residual and inverse-CDF draw) over one batch
-of synthetic inputs already resident in HBM.  The default workload is the
-sampled chain at B=64 requests, k=4 drafts, V=248,320, bf16 target logits and
-bf16 draft probabilities, T=0.7; three input sets rotate so that no step finds
-its rows in the 256 MB last-level cache.  Prints one JSON line.
+A step is one pass of the verify path over one batch of synthetic input
+already resident in HBM.  The default workload is the sampled chain verify
+(sv_verify_sample: softmax statistics of the target rows, accept scan,
+residual and inverse-CDF draw) at B=64 requests, k=4 drafts, V=248,320, bf16
+target logits and bf16 draft probabilities, T=0.7; three input sets rotate so
+that no step finds its rows in the 256 MB last-level cache.  Prints one JSON
+line.
 
-Other workloads (``--workload c1|c2|c3p|c3s|c4|c5|c5g|c5p|tb``) print the same
-kind of line for the other configurations (fixed-prefix chain, greedy + prompt
-lookup, device uniforms, one vocabulary shard, ragged chain, sampled / greedy /
-point-mass tree, EAGLE-2 tree build); their inputs also rotate over device
-copies totalling more than twice that cache (the fixed-prefix chain, whose
-rows are shared by all rounds by construction, excepted).
+The other workloads print the same kind of line: c1 (fixed-prefix chain,
+200,000 rounds, V=2048 f32, plus the latency of one B=1 call), c2 (prompt
+lookup + greedy verify), c3p (the default workload with its uniforms drawn on
+the device), c3s (one of 8 vocabulary shards of the default round), c4 (ragged
+chain), c5 / c5g / c5p (sampled / greedy / point-mass tree verify), tb
+(EAGLE-2 tree build) and ceiling (a pure streaming read: the practical HBM
+read ceiling).  Their inputs rotate over device copies totalling more than
+twice that cache (the fixed-prefix chain, whose rows every round shares by
+construction, excepted).
+
+Each line carries:
+* value / unit: rounds (trees) per second, wall clock over the K timed steps,
+  which are bracketed by synchronisations;
+* roofline: the dominant kernel of the step, its algorithmic bytes per launch
+  over its average duration inside the steps (HIP events that the library's
+  measurement hook records on the step's stream around that kernel), against
+  the 8 TB/s HBM peak; where no one kernel dominates (the shard steps, the
+  tree build) the whole step; for the fixed-prefix chain, whose rows stay in
+  cache, its fp32 work against the 157.3 TFLOP/s vector peak; `traffic` is
+  the kernel's HBM bytes per launch from the committed rocprofv3 counter
+  summary, when that summary was taken on the current kernel sources;
+* cpu_baseline: the float64 oracle on the host on a bounded sample of the
+  same requests, on one thread and over a pool of one process per available
+  core (at most 16), with the CPU model.
+
+Order of work: a settle phase of untimed steps (about a second, so the clocks
+have ramped), the per-step event pass and the in-step kernel timing pass, then
+the W warmup steps and the K timed steps.
 """
 import argparse
 import hashlib
 import json
 import os
 import sys
+import tempfile
 import time
 
 import numpy as np
@@ -30,30 +54,52 @@ sys.path.insert(0, ROOT)
 
 METRIC = "verified rounds/s + achieved HBM GB/s (% peak), B=64 k=4 V=248,320 bf16"
 PEAK_HBM_GBPS = 8000.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "row_stats_c3_traffic.json")
-# the sources the row-statistics kernel is compiled from (its counter summary
-# holds while their hash is unchanged)
-STATS_SRCS = [os.path.join(ROOT, "draft_verify_sampling_amd", "csrc", f)
-              for f in ("k_stats.hip", "segment.hpp", "common.hpp", "words.hpp", "launch.hpp")]
+PEAK_FP32_TFLOPS = 157.3
+MAX_POOL = 16  # the host cores one GPU's share of the machine has
+CSRC = os.path.join(ROOT, "draft_verify_sampling_amd", "csrc")
+COMMON_SRCS = ["common.hpp", "words.hpp", "launch.hpp", "tiles.hpp", "segment.hpp"]
+# the sources a kernel is compiled from: its counter summary holds while
+# their hash is unchanged
+KERNEL_SRCS = {
+    "k_row_stats": ["k_stats.hip"],
+    "k_chain_stats": ["k_stats.hip"],
+    "k_read_ceiling": ["k_stats.hip"],
+    "k_row_argmax": ["k_greedy.hip"],
+    "k_walk": ["k_walk.hip"],
+}
 
 
-def stats_source_hash():
+def source_hash(kernel):
     h = hashlib.sha1()
-    for path in STATS_SRCS:
-        with open(path, "rb") as f:
-            h.update(f.read())
+    for f in KERNEL_SRCS[kernel] + COMMON_SRCS:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()
+
+
+def traffic_file(kernel, workload):
+    return os.path.join(ROOT, "profiles", f"{kernel[2:]}_{workload}_traffic.json")
 
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def _rows(a, kind, torch, dev):
     if kind == "f32":
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
-    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).to(dev).view(
-        torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).to(dev).view(torch.bfloat16)
 
 
 def _i32(a, torch, dev):
@@ -69,105 +115,490 @@ def rotation(touched):
     return max(2, -(-2 * MALL_BYTES // max(int(touched), 1)))
 
 
-def chain_formula_bytes(ci):
-    """Logit rows read once + draft rows + draft ids + uniforms."""
-    st = 4 if ci.t_kind == "f32" else 2
-    sq = 4 if ci.q_kind == "f32" else 2
-    ks = ci.draft_len.astype(np.int64)
-    return int(((ks + 1) * ci.V * st).sum() + (ks * ci.V * sq).sum() + 4 * ks.sum() + 4 * (ks + 1).sum())
+# ---------------------------------------------------------------------------
+# timing
+# ---------------------------------------------------------------------------
+def settle(step, seconds, torch):
+    """Untimed steps for about `seconds` of wall clock (the device clocks ramp
+    up under load); synchronises every 256 steps so the queue stays short."""
+    t0, i = time.perf_counter(), 0
+    while True:
+        step(i)
+        i += 1
+        if i % 256 == 0:
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= seconds:
+                break
+    torch.cuda.synchronize()
+    return i
 
 
-def stats_traffic(step_kernel_src_hash):
-    """HBM bytes per launch of the row-statistics kernel from the committed
-    counter summary, or None if absent or taken on a different kernel."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if t.get("kernel_source_sha1") != step_kernel_src_hash:
-        return None
-    return t.get("bytes_per_launch")
+def event_pass(step, n, torch):
+    """n steps, each between a pair of HIP events on the current stream: the
+    per-step duration distribution (ms)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record()
+        step(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
 
 
-def timed(fn, steps, warmup, torch):
-    """W untimed calls, then exactly K timed calls bracketed by synchronisations
-    (host wall clock, and one HIP event pair on the current stream).  A second,
-    untimed-for-the-result pass records an event pair around every call for the
-    per-step distribution.  Returns (wall s, event ms over the K calls, per-call
-    event ms list)."""
+def kernel_pass(step, n, sv, torch, arm_call):
+    """n steps with the library's measurement hook armed right before the
+    step's `arm_call`-th library call: the average duration (us) of the
+    kernel that call streams its rows with, from HIP events on its stream."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:  # the events exist before the hook records them
+        a.record()
+        b.record()
+    torch.cuda.synchronize()
+    for i in range(n):
+        step(i, arm=(arm_call, lambda i=i: sv.sv_debug_time_kernel_once(*ev[i])))
+    torch.cuda.synchronize()
+    return 1e3 * float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def timed(step, steps, warmup, torch):
+    """W untimed steps, then exactly K timed steps bracketed by
+    synchronisations: host wall clock, and one HIP event pair on the current
+    stream.  Returns (wall s, event ms over the K steps)."""
     for i in range(warmup):
-        fn(i)
+        step(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
     for i in range(steps):
-        fn(i)
+        step(i)
     e1.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = e0.elapsed_time(e1)
-    n = min(steps, 200)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-    for i in range(n):
-        ev[i][0].record()
-        fn(i)
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    return wall, total_ms, [a.elapsed_time(b) for a, b in ev]
+    return time.perf_counter() - t0, e0.elapsed_time(e1)
 
 
-def kernel_avg_us(launchers, steps, warmup, torch):
-    """Average duration of one launch of a kernel, launched directly as the
-    step launches it: `steps` back-to-back launches (rotating input sets, each
-    a pre-marshalled call so that the host enqueues faster than the kernel
-    runs and the queue never drains) between a pair of HIP events on the
-    stream they run on."""
-    n = len(launchers)
-    for i in range(warmup):
-        launchers[i % n]()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
-        launchers[i % n]()
-    e1.record()
-    torch.cuda.synchronize()
-    return 1e3 * e0.elapsed_time(e1) / steps
+def traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None if absent or taken on different kernel sources."""
+    try:
+        with open(traffic_file(kernel, workload)) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha1") != source_hash(kernel):
+        return None
+    return t.get("bytes_per_launch")
 
 
-def cpu_baseline_chain(ci, gpu_out, budget_s, philox=None):
-    """The float64 oracle on the host on the same inputs: whole batches of this
-    workload's requests, repeated until about budget_s seconds have passed.
-    philox = (seed, offset): the GPU drew its uniforms on the device; the
-    oracle draws the same ones with its own generator (outside the timing)."""
+# ---------------------------------------------------------------------------
+# the float64 oracle on the host: one thread, and a pool of processes
+# ---------------------------------------------------------------------------
+def oracle_requests(kind, A, P, reqs):
+    """The oracle on requests `reqs` of one input set (A: arrays, P: scalars),
+    one request at a time; used alike by the one-thread run and the pool's
+    workers.  Returns {request: (tokens, count)} for the chain kinds."""
     import oracle
-    u = ci.uniforms if philox is None else oracle.philox_uniforms(philox[0], philox[1], ci.B, ci.k_max + 1)
-    reps, t0 = 0, time.perf_counter()
-    want = None
+    out = {}
+    for b in reqs:
+        b = int(b)
+        if kind == "chain":
+            r = oracle.verify_sample(A["target"], P["t_kind"], A["draft"], P["q_kind"], P["V"], A["t_rs"][b:b + 1],
+                                     A["q_rs"][b:b + 1], A["ids"][b:b + 1], A["dlen"][b:b + 1], P["k_max"], P["T"],
+                                     A["u"][b:b + 1])
+            out[b] = (r["tokens"][0], int(r["count"][0]), float(np.nanmin(np.append(r["margins"][0], np.inf))))
+        elif kind in ("tree", "tree_greedy", "tree_point"):
+            N = P["N"]
+            rows = slice(b * N, (b + 1) * N)
+            if kind == "tree":
+                oracle.verify_tree(A["target"][rows], "bf16", A["draft"][rows], "bf16", P["V"], A["parent"][b:b + 1],
+                                   A["token"][b:b + 1], P["T"], A["u"][b:b + 1], with_diag=False)
+            elif kind == "tree_greedy":
+                oracle.verify_tree_greedy(A["target"][rows], "bf16", P["V"], A["parent"][b:b + 1],
+                                          A["token"][b:b + 1])
+            else:
+                oracle.verify_tree_pointmass(A["target"][rows], "bf16", P["V"], A["parent"][b:b + 1],
+                                             A["token"][b:b + 1], P["T"], A["u"][b:b + 1])
+        elif kind == "greedy":
+            ids, lens, _ = oracle.ngram_draft(A["ctx"][b:b + 1], A["ctx_len"][b:b + 1], P["window"], P["k"])
+            oracle.verify_greedy(A["target"], "bf16", P["V"], np.array([b * (P["k"] + 1)]), ids, lens, P["k"])
+        elif kind == "tree_build":
+            t = oracle.DraftTree()
+            frontier = [0]
+            for r in range(P["rounds"]):
+                rows = A[f"r{r}"][b:b + 1] if r == 0 else A[f"r{r}"][b * P["exp"]:(b + 1) * P["exp"]]
+                frontier = t.expand(frontier, [rows[e] for e in range(len(frontier))], "bf16", P["top"], P["exp"])
+            t.finalize(P["N"])
+        else:
+            raise ValueError(kind)
+    return out
+
+
+_POOL = {}
+
+
+def _pool_init(paths, kind, P):
+    """Pool worker start: map the input arrays from their files (no copies)."""
+    _POOL["A"] = {name: np.load(p, mmap_mode="r") for name, p in paths.items()}
+    _POOL["kind"], _POOL["P"] = kind, P
+
+
+def _pool_run(reqs):
+    oracle_requests(_POOL["kind"], _POOL["A"], _POOL["P"], reqs)
+    return len(reqs)
+
+
+def cpu_baseline(kind, A, P, B, budget_s, unit):
+    """The oracle on this workload's requests (ids cycled over input set 0):
+    one thread for about budget_s seconds, then the same requests spread over a
+    pool of spawned processes, one per available core, each single-threaded.
+    Returns (cpu_baseline object, oracle outputs of the one-thread run)."""
+    import multiprocessing as mp
+    done, t0, outs = 0, time.perf_counter(), {}
     while True:
-        want = oracle.verify_sample(ci.target, ci.t_kind, ci.draft, ci.q_kind, ci.V, ci.t_row_start,
-                                    ci.q_row_start, ci.draft_ids[:, :ci.k_max], ci.draft_len,
-                                    ci.k_max, ci.T, u)
-        reps += 1
+        outs.update(oracle_requests(kind, A, P, [done % B]))
+        done += 1
         if time.perf_counter() - t0 >= budget_s:
             break
-    el = time.perf_counter() - t0
-    tok, cnt = gpu_out
-    same = (cnt == want["count"]) & (tok == want["tokens"]).all(axis=1)
-    near = np.nanmin(np.where(np.isnan(want["margins"]), np.inf, want["margins"]), axis=1) < 1e-6
-    return dict(value=round(reps * ci.B / el, 3), unit="rounds/s", cores=1, kind="oracle",
-                sample=f"{reps} x all {ci.B} requests of input set 0 ({el:.1f} s, numpy float64, "
-                       f"one thread)"), dict(requests=int(ci.B), mismatched=int((~same & ~near).sum()),
-                                             boundary=int((~same & near).sum()))
+    t1 = time.perf_counter() - t0
+    ncores = min(len(os.sched_getaffinity(0)), MAX_POOL)
+    pool = dict(value=None, unit=unit, cores=ncores)
+    try:
+        with tempfile.TemporaryDirectory(prefix="svbench_", dir="/tmp") as tmp:
+            paths = {}
+            for name, arr in A.items():
+                paths[name] = os.path.join(tmp, f"{name}.npy")
+                np.save(paths[name], np.ascontiguousarray(arr))
+            reqs = [i % B for i in range(max(done, ncores))]
+            chunks = [reqs[i::ncores] for i in range(ncores)]
+            old = os.environ.get("OMP_NUM_THREADS")
+            os.environ["OMP_NUM_THREADS"] = "1"
+            try:
+                ctx = mp.get_context("spawn")  # fresh interpreters that never touch the GPU
+                with ctx.Pool(ncores, initializer=_pool_init, initargs=(paths, kind, P)) as p:
+                    p.map(_pool_run, [[0]] * ncores, chunksize=1)  # start-up and imports, untimed
+                    tp = time.perf_counter()
+                    n = sum(p.map(_pool_run, chunks, chunksize=1))
+                    pool_s = time.perf_counter() - tp
+            finally:
+                if old is None:
+                    os.environ.pop("OMP_NUM_THREADS", None)
+                else:
+                    os.environ["OMP_NUM_THREADS"] = old
+        pool.update(value=round(n / pool_s, 3),
+                    sample=f"{n} requests over {ncores} spawned single-threaded processes in {pool_s:.2f} s")
+    except Exception as e:  # the pool figure is an extra; its absence is stated
+        pool["error"] = repr(e)
+        log(f"oracle pool run failed: {e!r}")
+    return dict(value=round(done / t1, 3), unit=unit, cores=1, kind="oracle",
+                sample=f"{done} requests of input set 0, one at a time, in {t1:.1f} s (float64 numpy, one thread)",
+                pool=pool, cpu_model=cpu_model()), outs
 
 
-def summarize_counters(fetch_db, write_db, out_json):
-    """Per-launch HBM traffic of the row-statistics kernel from two rocprofv3
-    --pmc databases (FETCH_SIZE and WRITE_SIZE passes of
-    `bench.py --calibrate-copy`), each counter scaled by what it reads for the
-    run's 256 MiB device-to-device copies; writes a JSON summary."""
+# ---------------------------------------------------------------------------
+# workloads: each builds its inputs and returns a description of its step
+# ---------------------------------------------------------------------------
+def _call_step(calls, graphs=None):
+    """A step runs the pre-marshalled library calls of rotation set i % n (or
+    replays that set's captured graph).  arm = (call index, arming function)
+    arms the measurement hook right before that call (always direct calls)."""
+    def step(i, arm=None):
+        j = i % len(calls)
+        if graphs is not None and arm is None:
+            graphs[j].replay()
+            return
+        for c_idx, c in enumerate(calls[j]):
+            if arm is not None and arm[0] == c_idx:
+                arm[1]()
+            c()
+    return step
+
+
+def _capture(calls, torch):
+    """One captured graph per rotation set (after one direct run of it)."""
+    graphs = []
+    side = torch.cuda.Stream()
+    for group in calls:
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for c in group:
+                c()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in group:
+                c()
+        graphs.append(g)
+    return graphs
+
+
+def w_chain(W, args, torch, sv, synth, dev):
+    philox = W == "c3p"
+    if W in ("c3", "c3p"):
+        sets = [synth.c3_sampled(salt=s) for s in (0, 1, 2)]
+        cfg = dict(workload="sampled chain verify (speculative sampling): 64 requests, k=4 drafts, V=248,320, "
+                            "bf16 target logits ~N(0,2.5^2)+6 on 5 ids, bf16 draft probabilities, T=0.7"
+                            + (", uniforms drawn on the device (Philox4x64-10)" if philox else ""),
+                   batch=64, k=4, vocab=248_320, temperature=0.7, inputs="bf16", input_sets=3)
+    elif W == "c4":
+        sets = [synth.c4_ragged(salt=s) for s in (0, 1, 2)]
+        cfg = dict(workload="ragged sampled chain verify: 256 requests, k in 1..8, V=151,936, bf16, T=1",
+                   batch=256, vocab=151_936, temperature=1.0, inputs="bf16", input_sets=3)
+    else:
+        sets = [synth.c1_chain()]
+        cfg = dict(workload="fixed-prefix sampled chain: 200,000 rounds sharing 5 target and 4 draft rows, k=4, "
+                            "V=2048, fp32, T=1", batch=200_000, k=4, vocab=2048, temperature=1.0, inputs="f32",
+                   input_sets=1)
+    ci0 = sets[0]
+    B, k_max = ci0.B, ci0.k_max
+    ds = [dict(tgt=_rows(c.target, c.t_kind, torch, dev), dft=_rows(c.draft, c.q_kind, torch, dev),
+               trs=_i32(c.t_row_start, torch, dev), qrs=_i32(c.q_row_start, torch, dev),
+               ids=_i32(c.draft_ids[:, :c.k_max], torch, dev), dl=_i32(c.draft_len, torch, dev),
+               u=torch.from_numpy(c.uniforms).to(dev)) for c in sets]
+    out = (torch.empty((B, k_max + 1), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev),
+           torch.empty((B,), dtype=torch.int32, device=dev), None, None)
+    ws = sv.Workspace(dev)
+    if philox:
+        calls = [[sv.prepare(sv.sv_verify_sample_philox, d["tgt"], d["dft"], d["trs"], d["qrs"], d["ids"], d["dl"],
+                             ci0.T, 2026, j, workspace=ws, out=out)[0]] for j, d in enumerate(ds)]
+    else:
+        calls = [[sv.prepare_verify_sample(d["tgt"], d["dft"], d["trs"], d["qrs"], d["ids"], d["dl"], ci0.T, d["u"],
+                                           workspace=ws, out=out)[0]] for d in ds]
+    esz = lambda kind: 4 if kind == "f32" else 2
+
+    def formula(c):  # target rows read once + draft rows + ids + uniforms
+        ks = c.draft_len.astype(np.int64)
+        return int(((ks + 1) * c.V * esz(c.t_kind)).sum() + (ks * c.V * esz(c.q_kind)).sum() + 4 * ks.sum()
+                   + 4 * (ks + 1).sum())
+
+    def roofline_bytes(accepted):
+        """(bytes per launch of the dominant kernel, its name, what they are)."""
+        if W in ("c3", "c3p"):
+            return (int(np.mean([c.target.shape[0] * c.V * esz(c.t_kind) for c in sets])), "k_row_stats",
+                    "every target row of every request, read once (the softmax statistics)")
+        # lazy statistics: the rounds read target rows 0..m of each request
+        nb = [int(((acc.astype(np.int64) + 1) * c.V * esz(c.t_kind)).sum()) for acc, c in zip(accepted, sets)]
+        return int(np.mean(nb)), "k_chain_stats", "target rows 0..m of each request (the rows its round reads)"
+
+    u0 = ci0.uniforms
+    if philox:
+        import oracle  # the device drew the uniforms; the oracle's own generator gives the same ones
+        u0 = oracle.philox_uniforms(2026, 0, B, k_max + 1)
+    A = dict(target=ci0.target, draft=ci0.draft, t_rs=ci0.t_row_start, q_rs=ci0.q_row_start,
+             ids=ci0.draft_ids[:, :max(k_max, 1)], dlen=ci0.draft_len, u=u0)
+    P = dict(t_kind=ci0.t_kind, q_kind=ci0.q_kind, V=ci0.V, k_max=k_max, T=ci0.T)
+    graphs = _capture(calls, torch) if args.graph else None
+    w = dict(step=_call_step(calls, graphs), arm_call=None if W == "c1" else 0, B=B, unit="rounds/s", cfg=cfg,
+             dtype="f32", formula=int(np.mean([formula(c) for c in sets])), out=out, nsets=len(sets),
+             roofline_bytes=None if W == "c1" else roofline_bytes, cpu=("chain", A, P, B), kind="chain")
+    if W == "c1":
+        # one request's call alone: the latency a caller waits for at B=1
+        d = ds[0]
+        one = sv.prepare_verify_sample(d["tgt"], d["dft"], d["trs"][:1], d["qrs"][:1], d["ids"][:1], d["dl"][:1],
+                                       ci0.T, d["u"][:1], workspace=ws)[0]
+        w["b1"] = one
+    return w
+
+
+def w_tree(W, args, torch, sv, synth, dev):
+    ti = synth.c5_tree()
+    B, N, V = ti.B, ti.N, ti.V
+    tgt, dft = _rows(ti.target, "bf16", torch, dev), _rows(ti.draft, "bf16", torch, dev)
+    par, tok = _i32(ti.parent, torch, dev), _i32(ti.token, torch, dev)
+    u = torch.from_numpy(ti.uniforms).to(dev)
+    ws = sv.Workspace(dev)
+    out = (torch.empty((B, N), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev),
+           torch.empty((B,), dtype=torch.int32, device=dev), torch.empty((B, N), dtype=torch.int32, device=dev))
+    nset = rotation(15 << 20)  # a round reads the visited nodes' rows (~15 MB)
+    if W == "c5":
+        copies = [(tgt, dft)] + [(tgt.clone(), dft.clone()) for _ in range(nset - 1)]
+        calls = [[sv.prepare(sv.sv_verify_tree, t, q, par, tok, ti.T, u, workspace=ws, out=out + (None,))[0]]
+                 for t, q in copies]
+        name, kind = "tree verify", "tree"
+    else:
+        tgts = [tgt] + [tgt.clone() for _ in range(nset - 1)]
+        if W == "c5g":
+            calls = [[sv.prepare(sv.sv_verify_tree_greedy, t, par, tok, workspace=ws, out=out)[0]] for t in tgts]
+            name, kind = "greedy tree verify (argmax picks)", "tree_greedy"
+        else:
+            calls = [[sv.prepare(sv.sv_verify_tree_pointmass, t, par, tok, ti.T, u, workspace=ws, out=out)[0]]
+                     for t in tgts]
+            name, kind = "point-mass tree verify (each candidate tested as a point mass)", "tree_point"
+    cfg = dict(workload=f"{name}: 32 requests, 60-node draft trees (depth <= 6, branching <= 4), V=128,256, "
+                        "bf16, T=1", batch=B, nodes=N, vocab=V, temperature=1.0, inputs="bf16", input_sets=nset)
+    kids = [[[c for c in range(1, N) if ti.parent[b, c] == v] for v in range(N)] for b in range(B)]
+
+    def walk_bytes(_accepted):
+        """Bytes the walk must read for this round (from the path it took):
+        per visited node one pass over its target row (its softmax pair, or
+        its argmax); per rejected child one residual pass over the node's
+        target and draft rows (sampled tree), or one pass over its target row
+        at its first rejection (point mass); one pass for the last draw when
+        no pass at the last node preceded it (greedy: none)."""
+        path, acc = out[3].cpu().numpy(), out[2].cpu().numpy()
+        total = 0
+        for b in range(B):
+            visited = [0] + [int(x) for x in path[b, :acc[b]]]
+            for j, v in enumerate(visited):
+                rej = len(kids[b][v]) if j + 1 == len(visited) else kids[b][v].index(visited[j + 1])
+                total += 2 * V
+                if W == "c5":
+                    total += rej * 4 * V
+                elif W == "c5p" and rej:
+                    total += 2 * V
+                if j + 1 == len(visited) and W != "c5g" and rej == 0:
+                    total += 2 * V
+        return (total, "k_walk", "per visited node its target row; per rejected child the node's target and draft "
+                                 "rows (point mass: the target row at the first rejection); the last draw's pass")
+
+    A = dict(target=ti.target, draft=ti.draft, parent=ti.parent, token=ti.token, u=ti.uniforms)
+    return dict(step=_call_step(calls), arm_call=0, B=B, unit="rounds/s", cfg=cfg,
+                dtype="bf16 compares" if W == "c5g" else "f32", formula=2 * B * N * V * 2 + 2 * 4 * B * N,
+                out=out, nsets=1, roofline_bytes=walk_bytes, cpu=(kind, A, dict(N=N, V=V, T=ti.T), B), kind=kind)
+
+
+def w_greedy(W, args, torch, sv, synth, dev):
+    g = synth.c2_greedy()
+    ctx, cl = _i32(g.ctx, torch, dev), _i32(g.ctx_len, torch, dev)
+    tgt = _rows(g.target, "bf16", torch, dev)
+    trs = _i32(np.arange(g.B) * (g.k + 1), torch, dev)
+    ws = sv.Workspace(dev)
+    nset = rotation(g.target.size * 2 + g.ctx.size * 4)
+    calls = []
+    for j in range(nset):
+        c_j, t_j = (ctx, tgt) if j == 0 else (ctx.clone(), tgt.clone())
+        draft, (ids, lens) = sv.prepare(sv.sv_ngram_draft, c_j, cl, g.window, g.k)
+        verify, outs = sv.prepare(sv.sv_verify_greedy, t_j, trs, ids, lens, workspace=ws)
+        calls.append([draft, verify])
+        if j == 0:
+            out0 = outs
+    cfg = dict(workload="prompt-lookup draft + greedy verify: 64 requests, contexts of 4,096 tokens, window 3, "
+                        "k=4, V=32,000, bf16", batch=g.B, k=g.k, vocab=g.V, inputs="bf16", input_sets=nset)
+    rows_bytes = g.target.size * 2
+    A = dict(ctx=g.ctx, ctx_len=g.ctx_len, target=g.target)
+    return dict(step=_call_step(calls), arm_call=1, B=g.B, unit="rounds/s", cfg=cfg, dtype="bf16 compares",
+                formula=rows_bytes + g.ctx.size * 4, out=out0, nsets=1,
+                roofline_bytes=lambda _a: (rows_bytes, "k_row_argmax", "every target row, read once"),
+                cpu=("greedy", A, dict(window=g.window, k=g.k, V=g.V), g.B), kind="greedy")
+
+
+def w_shard(W, args, torch, sv, synth, dev):
+    ci = synth.c3_sampled()
+    G, V, B, k = 8, ci.V, ci.B, ci.k_max
+    bounds = [V * g // G for g in range(G + 1)]
+    trs, qrs = _i32(ci.t_row_start, torch, dev), _i32(ci.q_row_start, torch, dev)
+    ids, dl = _i32(ci.draft_ids[:, :k], torch, dev), _i32(ci.draft_len, torch, dev)
+    u = torch.from_numpy(ci.uniforms).to(dev)
+    cols = [(_rows(np.ascontiguousarray(ci.target[:, bounds[g]:bounds[g + 1]]), "bf16", torch, dev),
+             _rows(np.ascontiguousarray(ci.draft[:, bounds[g]:bounds[g + 1]]), "bf16", torch, dev)) for g in range(G)]
+    # every shard's steps once, so the exchanged arrays (a few KB, stacked as
+    # the all-gathers would leave them) hold a real round's values
+    wss = [sv.Workspace(dev) for _ in range(G)]
+    st1 = [sv.sv_shard_stats(cols[g][0], cols[g][1], bounds, g, trs, qrs, ids, dl, ci.T, workspace=wss[g])
+           for g in range(G)]
+    all_pairs, all_at = torch.stack([p for p, _ in st1]), torch.stack([a for _, a in st1])
+    mass = torch.zeros((G, B, 3), dtype=torch.float64, device=dev)
+    for g in range(G):
+        sv.sv_shard_residual(cols[g][0], cols[g][1], bounds, g, trs, qrs, ids, dl, ci.T, u, all_pairs, all_at, mass,
+                             workspace=wss[g])
+    out = (torch.empty((B, k + 1), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev),
+           torch.empty((B,), dtype=torch.int32, device=dev), None)
+    for g in range(G):
+        sv.sv_shard_draw(cols[g][0], cols[g][1], bounds, g, trs, qrs, ids, dl, ci.T, u, all_pairs, mass, out,
+                         workspace=wss[g])
+    share = (bounds[1] - bounds[0]) * 2 * (ci.target.shape[0] + ci.draft.shape[0])
+    nset = rotation(share)
+    calls = []
+    for j in range(nset):
+        tg, qg = cols[0] if j == 0 else (cols[0][0].clone(), cols[0][1].clone())
+        calls.append([sv.prepare(sv.sv_shard_stats, tg, qg, bounds, 0, trs, qrs, ids, dl, ci.T, out=st1[0],
+                                 workspace=wss[0])[0],
+                      sv.prepare(sv.sv_shard_residual, tg, qg, bounds, 0, trs, qrs, ids, dl, ci.T, u, all_pairs,
+                                 all_at, mass, workspace=wss[0])[0],
+                      sv.prepare(sv.sv_shard_draw, tg, qg, bounds, 0, trs, qrs, ids, dl, ci.T, u, all_pairs, mass,
+                                 out, workspace=wss[0])[0]])
+    cfg = dict(workload="sampled chain verify on one of 8 vocabulary shards: 64 requests, k=4, 31,040 of "
+                        "V=248,320 columns per device, bf16, T=0.7 (one device's three shard steps; the all-gathers "
+                        "between them not included)", batch=B, k=k, vocab=V, shards=G, inputs="bf16",
+               input_sets=nset)
+    A = dict(target=ci.target, draft=ci.draft, t_rs=ci.t_row_start, q_rs=ci.q_row_start, ids=ci.draft_ids[:, :k],
+             dlen=ci.draft_len, u=ci.uniforms)
+    P = dict(t_kind="bf16", q_kind="bf16", V=V, k_max=k, T=ci.T)
+    return dict(step=_call_step(calls), arm_call=None, B=B, unit="rounds/s", cfg=cfg, dtype="f32", formula=share,
+                out=None, nsets=1, roofline_bytes=None, step_bytes=share,
+                step_bytes_are="this shard's columns of every target and draft row, read once",
+                cpu=("chain", A, P, B), kind="shard")
+
+
+def w_tree_build(W, args, torch, sv, synth, dev):
+    B, V, top, exp, depth, N = 32, 128_256, 4, 4, 6, 60
+    rng = np.random.default_rng(2026)
+    host = []
+    for r in range(depth):
+        n = B * (1 if r == 0 else exp)
+        l = rng.standard_normal((n, V)).astype(np.float32) * 1.5
+        p = np.exp(l - l.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        host.append(synth.encode(p, "bf16"))
+    rounds = [_rows(h, "bf16", torch, dev) for h in host]
+    state = sv.DraftTreeState(B, 1 + top + (depth - 1) * exp * top, dev)
+    ws = sv.Workspace(dev)
+    nexts = [torch.empty((B, exp), dtype=torch.int32, device=dev) for _ in range(depth)]
+    outs = [torch.empty((B, N), dtype=torch.int32, device=dev) for _ in range(4)] + \
+           [torch.empty((B, N, N), dtype=torch.uint8, device=dev)]
+    row_bytes = sum(int(t.numel()) * 2 for t in rounds)
+    nset = rotation(row_bytes)
+    sets = [rounds] + [[t.clone() for t in rounds] for _ in range(nset - 1)]
+    fin = sv.prepare(sv.sv_tree_finalize, state, N, out=outs)[0]
+    calls = [[sv.prepare(sv.sv_tree_expand, rs[r], None if r == 0 else nexts[r - 1], top, exp, state,
+                         next_exp=nexts[r], workspace=ws)[0] for r in range(depth)] + [fin] for rs in sets]
+    cfg = dict(workload="EAGLE-2 draft tree built on the device: 32 requests, V=128,256 bf16 draft rows, top 4 "
+                        "children, 4 nodes expanded per round, 6 rounds, 60 nodes kept, ancestor mask", batch=B,
+               vocab=V, top_children=top, expand_per_round=exp, rounds=depth, nodes=N, inputs="bf16",
+               input_sets=nset)
+    A = {f"r{r}": h for r, h in enumerate(host)}
+    return dict(step=_call_step(calls), arm_call=None, B=B, unit="trees/s", cfg=cfg, dtype="f32 / f64 sums",
+                formula=row_bytes, out=None, nsets=1, roofline_bytes=None, step_bytes=row_bytes,
+                step_bytes_are="the expanded nodes' draft rows of the 6 rounds, read once",
+                cpu=("tree_build", A, dict(rounds=depth, exp=exp, top=top, N=N), B), kind="tree_build")
+
+
+WORKLOADS = {"c1": w_chain, "c3": w_chain, "c3p": w_chain, "c4": w_chain, "c5": w_tree, "c5g": w_tree,
+             "c5p": w_tree, "c2": w_greedy, "c3s": w_shard, "tb": w_tree_build}
+
+
+def run_ceiling(args, torch, sv, dev, result):
+    """A pure streaming read of 256 MiB per launch over four rotating buffers
+    (1 GiB, so no launch finds its bytes in the 256 MB cache), each launch
+    timed with HIP events: the practical HBM read ceiling."""
+    part = 256 << 20
+    bufs = [torch.full((part,), 7, dtype=torch.uint8, device=dev) for _ in range(4)]
+    nb = int(sv.load().sv_debug_read_blocks(part))
+    outs = [torch.empty((nb,), dtype=torch.int32, device=dev) for _ in bufs]
+    step = lambda i, arm=None: sv.sv_debug_read_ceiling(bufs[i % 4], out=outs[i % 4])
+    settle(step, args.settle_seconds, torch)
+    ms = event_pass(step, 200, torch)
+    wall, _ = timed(step, args.steps, args.warmup, torch)
+    us = 1e3 * float(np.mean(ms))
+    gbps = part / (us * 1e-6) / 1e9
+    result.update(metric="HBM read ceiling (pure streaming read)", value=round(gbps, 1), unit="GB/s",
+                  ms_per_step=round(1e3 * wall / args.steps, 5), dtype="u32 words",
+                  config=dict(workload="pure streaming read of 256 MiB per launch (16-byte non-temporal loads), four "
+                                       "rotating buffers", bytes_per_launch=part),
+                  roofline=dict(bound="hbm", kernel="k_read_ceiling", achieved=round(gbps, 1), peak=PEAK_HBM_GBPS,
+                                unit="GB/s", frac=round(gbps / PEAK_HBM_GBPS, 4),
+                                traffic=traffic("k_read_ceiling", "ceiling"), algorithmic_bytes_per_launch=part,
+                                avg_launch_us=round(us, 3), timing="HIP events around each of 200 launches"),
+                  cpu_baseline=None)
+
+
+# ---------------------------------------------------------------------------
+# counter summaries (rocprofv3 --pmc databases -> profiles/<kernel>_<w>_traffic.json)
+# ---------------------------------------------------------------------------
+def summarize_counters(workload, kernel, fetch_db, write_db):
+    """Per-launch HBM traffic of `kernel` from two rocprofv3 --pmc databases
+    (FETCH_SIZE and WRITE_SIZE passes of `bench.py --calibrate-copy`), each
+    counter scaled by what it reads for the run's 256 MiB device-to-device
+    copies; writes profiles/<kernel>_<workload>_traffic.json."""
     import sqlite3
 
     def per_kernel(db, counter):
@@ -183,43 +614,45 @@ def summarize_counters(fetch_db, write_db, out_json):
     res = {}
     for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
         k = per_kernel(db, counter)
-        copies = [v for name, vals in k.items() if "copyBuffer" in name for v in vals]
-        big = sorted(copies)[-8:]
-        scale = (sum(big) / len(big)) / ref_kib
-        stats = [vals for name, vals in k.items() if "k_row_stats" in name][0]
-        res[counter] = dict(raw_kib_per_launch=sum(stats) / len(stats), copy_reading_kib=sum(big) / len(big),
-                            copy_true_kib=ref_kib, scale=scale,
-                            bytes_per_launch=sum(stats) / len(stats) / scale * 1024)
+        copies = sorted(v for name, vals in k.items() if "copyBuffer" in name for v in vals)[-8:]
+        scale = (sum(copies) / len(copies)) / ref_kib
+        vals = [v for name, vs in k.items() if f"{kernel}<" in name or name.startswith(f"{kernel}(")
+                or f"::{kernel}(" in name for v in vs]
+        res[counter] = dict(raw_kib_per_launch=sum(vals) / len(vals), copy_reading_kib=sum(copies) / len(copies),
+                            copy_true_kib=ref_kib, scale=scale, launches=len(vals),
+                            bytes_per_launch=sum(vals) / len(vals) / scale * 1024)
         res[counter + "_all_kernels_raw_kib"] = {n[:80]: sum(v) / len(v) for n, v in k.items()}
-    res["kernel_source_sha1"] = stats_source_hash()
-    res["bytes_per_launch"] = int(res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"])
-    with open(out_json, "w") as f:
+    res.update(workload=workload, kernel=kernel, kernel_source_sha1=source_hash(kernel),
+               bytes_per_launch=int(res["FETCH_SIZE"]["bytes_per_launch"] + res["WRITE_SIZE"]["bytes_per_launch"]))
+    with open(traffic_file(kernel, workload), "w") as f:
         json.dump(res, f, indent=1)
-    print(json.dumps({k: res[k] for k in ("bytes_per_launch", "kernel_source_sha1")}))
+    print(json.dumps({k: res[k] for k in ("workload", "kernel", "bytes_per_launch", "kernel_source_sha1")}))
 
 
 def main():
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
-        summarize_counters(sys.argv[2], sys.argv[3], sys.argv[4])
+        summarize_counters(*sys.argv[2:6])
         return
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c3p", "c3s", "c4", "c5", "c5g", "c5p", "tb"])
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--workload", default="c3", choices=sorted(WORKLOADS) + ["ceiling"])
+    ap.add_argument("--settle-seconds", type=float, default=1.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--graph", action="store_true",
-                    help="replay one captured HIP graph per step instead of launching the step's "
-                         "kernels directly (each replay adds a few microseconds on this stack)")
+                    help="chain workloads: replay one captured HIP graph per step instead of launching the step's "
+                         "kernels directly")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="first run plain 256 MiB device-to-device copies (a counter calibration "
-                         "reference for rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
+                    help="first run plain 256 MiB device-to-device copies (the counter calibration reference for "
+                         "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1",
-                          "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on one GPU; --gpus must be 1", "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.graph and args.workload not in ("c1", "c3", "c3p", "c4"):
+        ap.error("--graph is for the chain workloads (c1, c3, c3p, c4)")
 
     import torch
     import draft_verify_sampling_amd as sv
@@ -235,357 +668,105 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    src_hash = stats_source_hash()
 
-    result = dict(metric=METRIC, n_gpus=1, steps=args.steps, warmup=args.warmup,
-                  higher_is_better=True, scaling="weak", vs_baseline=None, dtype="f32",
-                  data="synthetic")
+    result = dict(metric=METRIC, n_gpus=1, steps=args.steps, warmup=args.warmup, higher_is_better=True,
+                  scaling="weak", vs_baseline=None, data="synthetic")
     W = args.workload
-    philox = W == "c3p"  # the headline workload with its uniforms drawn on the device
-    if philox:
-        W = "c3"
-    if W in ("c1", "c3", "c4"):
-        log(f"generating {W} inputs")
-        if W == "c3":
-            sets = [synth.c3_sampled(salt=s) for s in (0, 1, 2)]
-            cfg = dict(workload="sampled chain verify (speculative sampling): 64 requests, k=4 drafts, "
-                                "V=248,320, bf16 target logits ~N(0,2.5^2)+6 on 5 ids, bf16 draft "
-                                "probabilities, T=0.7" + (", uniforms drawn on the device (Philox4x64-10)"
-                                                          if philox else ""),
-                       batch=64, k=4, vocab=248_320, temperature=0.7, inputs="bf16", input_sets=3)
-        elif W == "c4":
-            sets = [synth.c4_ragged(salt=s) for s in (0, 1, 2)]
-            cfg = dict(workload="ragged sampled chain verify: 256 requests, k in 1..8, V=151,936, bf16, "
-                                "T=1", batch=256, vocab=151_936, temperature=1.0, inputs="bf16",
-                       input_sets=3)
-        else:
-            sets = [synth.c1_chain()]
-            cfg = dict(workload="fixed-prefix sampled chain: 200,000 rounds sharing 5 target and 4 draft "
-                                "rows, k=4, V=2048, fp32, T=1", batch=200_000, k=4, vocab=2048,
-                       temperature=1.0, inputs="f32", input_sets=1)
-        ci0 = sets[0]
-        dsets = []
-        for ci in sets:
-            dsets.append(dict(
-                tgt=_rows(ci.target, ci.t_kind, torch, dev), dft=_rows(ci.draft, ci.q_kind, torch, dev),
-                trs=_i32(ci.t_row_start, torch, dev), qrs=_i32(ci.q_row_start, torch, dev),
-                ids=_i32(ci.draft_ids[:, :ci.k_max], torch, dev), dl=_i32(ci.draft_len, torch, dev),
-                u=torch.from_numpy(ci.uniforms).to(dev)))
-        B, k_max = ci0.B, ci0.k_max
-        out = (torch.empty((B, k_max + 1), dtype=torch.int32, device=dev),
-               torch.empty((B,), dtype=torch.int32, device=dev),
-               torch.empty((B,), dtype=torch.int32, device=dev), None, None)
-        ws = sv.Workspace(dev)
-
-        # one pre-marshalled call per input set: the host enqueues a step in a
-        # few microseconds, well below the step's GPU time
-        if philox:
-            calls = [sv.prepare(sv.sv_verify_sample_philox, d["tgt"], d["dft"], d["trs"], d["qrs"], d["ids"],
-                                d["dl"], ci0.T, 2026, j, workspace=ws, out=out)[0] for j, d in enumerate(dsets)]
-        else:
-            calls = [sv.prepare_verify_sample(d["tgt"], d["dft"], d["trs"], d["qrs"], d["ids"], d["dl"], ci0.T,
-                                              d["u"], workspace=ws, out=out)[0] for d in dsets]
-
-        def eager(i):
-            calls[i % len(calls)]()
-
-        step = eager
-        if args.graph:
-            # one captured graph per input set: the step's kernels, replayed
-            # without per-launch host work
-            graphs = []
-            side = torch.cuda.Stream()
-            for j in range(len(dsets)):
-                side.wait_stream(torch.cuda.current_stream())
-                with torch.cuda.stream(side):
-                    eager(j)
-                torch.cuda.current_stream().wait_stream(side)
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g):
-                    eager(j)
-                graphs.append(g)
-
-            def step(i):
-                graphs[i % len(graphs)].replay()
-
-        log(f"timing {args.steps} steps")
-        wall, tot_ms, ev_ms = timed(step, args.steps, args.warmup, torch)
-        # one more call on set 0 for the parity sample and token counts
+    if W == "ceiling":
+        run_ceiling(args, torch, sv, dev, result)
+        print(json.dumps(result), flush=True)
+        return
+    log(f"generating {W} inputs")
+    w = WORKLOADS[W](W, args, torch, sv, synth, dev)
+    step = w["step"]
+    log("settle, event and kernel passes")
+    n_settle = settle(step, args.settle_seconds, torch)
+    n_meas = max(20, min(args.steps, 200))
+    ev_ms = event_pass(step, n_meas, torch)
+    k_us = kernel_pass(step, n_meas, sv, torch, w["arm_call"]) if w["arm_call"] is not None else None
+    log(f"{args.warmup} warmup steps, then {args.steps} timed steps")
+    wall, tot_ms = timed(step, args.steps, args.warmup, torch)
+    ms = 1e3 * wall / args.steps
+    # the outputs of each rotation set (the rows a lazy round read, the tokens)
+    out, accepted, counts = w["out"], [], None
+    if out is not None:
+        for j in range(w["nsets"]):
+            step(j)
+            torch.cuda.synchronize()
+            accepted.append(out[2].cpu().numpy().copy())
         step(0)
         torch.cuda.synchronize()
-        tok0, cnt0 = out[0].cpu().numpy(), out[1].cpu().numpy()
-        ms = 1e3 * wall / args.steps
-        # the dominant kernel, the statistics of every target row: its duration
-        # inside the steps, from HIP events the library records around it
-        # (the measurement hook) over a pass of steps like the timed ones;
-        # and, for reference, back-to-back stand-alone launches of it (the
-        # input sets of a ragged workload differ in row count: one output
-        # buffer per set, and the mean of their bytes per launch)
-        esz = 4 if ci0.t_kind == "f32" else 2
-        rows_bytes = int(round(np.mean([d["tgt"].shape[0] * ci0.V * esz for d in dsets])))
-        in_step = None
-        # (the ragged workload's steps take the lazy statistics, which read
-        # rows 0..m only: there the all-rows kernel is timed stand-alone)
-        if not args.graph and W in ("c1", "c3"):
-            n = min(args.steps, 200)
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-            for e0, e1 in ev:
-                e0.record()
-                e1.record()
+        counts = out[1].cpu().numpy()
+    result.update(value=round(w["B"] / (ms * 1e-3), 1), unit=w["unit"], ms_per_step=round(ms, 5), config=w["cfg"],
+                  dtype=w["dtype"])
+    if counts is not None:
+        result.update(tokens_per_s=round(float(counts.sum()) / (ms * 1e-3), 1),
+                      mean_tokens_per_round=round(float(counts.mean()), 4))
+    fb = w["formula"]
+    result.update(event_ms_per_step=dict(timed_region=round(tot_ms / args.steps, 5),
+                                         mean=round(float(np.mean(ev_ms)), 5),
+                                         p10=round(float(np.percentile(ev_ms, 10)), 5),
+                                         p50=round(float(np.percentile(ev_ms, 50)), 5),
+                                         p90=round(float(np.percentile(ev_ms, 90)), 5)),
+                  settle_steps=n_settle, formula_bytes_per_step=fb, formula_GBps=round(fb / (ms * 1e-3) / 1e9, 1),
+                  formula_frac_of_peak=round(fb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4))
+    if W == "c1":
+        # cache-resident by construction (every round reads the same 9 rows):
+        # one wave per round, bound by its dependent steps; its fp32 work
+        # against the vector peak, the whole step timed
+        B, V = w["B"], w["cfg"]["vocab"]
+        flops = B * V * 12.0
+        tfl = flops / (ms * 1e-3) / 1e12
+        result["roofline"] = dict(bound="alu", kernel="whole step (k_row_stats on the 5 shared rows + k_walk_small)",
+                                  achieved=round(tfl, 3), peak=PEAK_FP32_TFLOPS, unit="TFLOP/s",
+                                  frac=round(tfl / PEAK_FP32_TFLOPS, 4), traffic=None,
+                                  algorithmic_flops_per_launch=flops,
+                                  flops_are="12 fp32 operations per element of each round's drawn row: fma, exp2, "
+                                            "scale, subtract, clamp and add in the weight pass, the same again in "
+                                            "the pick's rescan (exp2 counted as one)",
+                                  timing="wall clock per step")
+        lat = []
+        for _ in range(20):
+            w["b1"]()
+        torch.cuda.synchronize()
+        for _ in range(200):
+            t0 = time.perf_counter()
+            w["b1"]()
             torch.cuda.synchronize()
-            for i in range(n):
-                sv.sv_debug_time_kernel_once(*ev[i])
-                step(i)
-            torch.cuda.synchronize()
-            in_step = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e-3
-        parts = [torch.empty((d["tgt"].shape[0], sv.sv_softmax_segments(d["tgt"].shape[0], ci0.V), 2),
-                             dtype=torch.float32, device=dev) for d in dsets]
-        stats = [sv.prepare_softmax_partials(d["tgt"], ci0.T, p) for d, p in zip(dsets, parts)]
-        alone = kernel_avg_us(stats, args.steps, args.warmup, torch) * 1e-6
-        st_avg = in_step if in_step is not None else alone
-        achieved = rows_bytes / st_avg / 1e9
-        fb = int(round(np.mean([chain_formula_bytes(ci) for ci in sets])))
-        cfg["launch"] = "hip graph per step" if args.graph else "direct kernel launches per step"
-        result.update(
-            value=round(B / (ms * 1e-3), 1), unit="rounds/s", ms_per_step=round(ms, 5), config=cfg,
-            tokens_per_s=round(float(cnt0.sum()) / (ms * 1e-3), 1),
-            mean_tokens_per_round=round(float(cnt0.mean()), 4),
-            event_ms_per_step=dict(timed_region=round(tot_ms / args.steps, 5),
-                                   mean=round(float(np.mean(ev_ms)), 5),
-                                   p10=round(float(np.percentile(ev_ms, 10)), 5),
-                                   p50=round(float(np.percentile(ev_ms, 50)), 5),
-                                   p90=round(float(np.percentile(ev_ms, 90)), 5)),
-            formula_bytes_per_step=fb,
-            formula_GBps=round(fb / (ms * 1e-3) / 1e9, 1),
-            formula_frac_of_peak=round(fb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4),
-            roofline=dict(bound="hbm", kernel="k_row_stats (softmax statistics of every target row)",
-                          achieved=round(achieved, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
-                          frac=round(achieved / PEAK_HBM_GBPS, 4),
-                          traffic=stats_traffic(src_hash) if W == "c3" else None,
-                          algorithmic_bytes_per_launch=rows_bytes,
-                          avg_launch_us=round(st_avg * 1e6, 3),
-                          timing="inside the steps (HIP events around the kernel)" if in_step is not None
-                          else "back-to-back stand-alone launches",
-                          stand_alone_avg_launch_us=round(alone * 1e6, 3)))
-        if not args.no_cpu:
-            log("timing the oracle on the host")
-            cb, par = cpu_baseline_chain(ci0, (tok0, cnt0), args.cpu_seconds, (2026, 0) if philox else None)
-            result["cpu_baseline"] = cb
-            result["parity_sample"] = par
-    elif W == "c5":
-        log("generating c5 inputs")
-        ti = synth.c5_tree()
-        d = dict(tgt=_rows(ti.target, "bf16", torch, dev), dft=_rows(ti.draft, "bf16", torch, dev),
-                 par=_i32(ti.parent, torch, dev), tok=_i32(ti.token, torch, dev),
-                 u=torch.from_numpy(ti.uniforms).to(dev))
-        ws = sv.Workspace(dev)
-        B, N = ti.parent.shape
-        out = (torch.empty((B, N), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev),
-               torch.empty((B,), dtype=torch.int32, device=dev), torch.empty((B, N), dtype=torch.int32, device=dev),
-               None)
-
-        # a round reads the visited nodes' target rows and the rejected children's
-        # draft rows (~15 MB): device copies of both row sets rotate
-        nset = rotation(15 << 20)
-        copies = [(d["tgt"], d["dft"])] + [(d["tgt"].clone(), d["dft"].clone()) for _ in range(nset - 1)]
-        launches = [sv.prepare(sv.sv_verify_tree, t, q, d["par"], d["tok"], ti.T, d["u"], workspace=ws, out=out)[0]
-                    for t, q in copies]
-
-        def step(i):
-            launches[i % nset]()
-
-        wall, tot_ms, ev_ms = timed(step, args.steps, args.warmup, torch)
-        ms = 1e3 * wall / args.steps
-        acc = out[2].cpu().numpy()
-        # rows the walk must read: the target row of every visited node (root and
-        # kept path); draft rows are read only where a child was rejected
-        visited_bytes = int((1 + acc).sum()) * ti.V * 2
-        rows_bytes = B * N * ti.V * 2
-        fb = 2 * rows_bytes + 2 * 4 * B * N
-        result.update(value=round(B / (ms * 1e-3), 1), unit="rounds/s", ms_per_step=round(ms, 5),
-                      config=dict(workload="tree verify: 32 requests, 60-node draft trees (depth <= 6, "
-                                           "branching <= 4), V=128,256, bf16, T=1", batch=32, nodes=60,
-                                  vocab=128_256, temperature=1.0, inputs="bf16", input_sets=nset),
-                      tokens_per_s=round(float(out[1].sum().item()) / (ms * 1e-3), 1),
-                      formula_bytes_per_step=fb, formula_GBps=round(fb / (ms * 1e-3) / 1e9, 1),
-                      visited_target_row_bytes=visited_bytes,
-                      event_ms_per_step=dict(timed_region=round(tot_ms / args.steps, 5),
-                                             p50=round(float(np.percentile(ev_ms, 50)), 5)),
-                      roofline=None)
-    elif W in ("c5g", "c5p"):
-        # the same trees, verified greedily (argmax picks) or with every
-        # candidate tested as a point mass on its own token (no draft rows)
-        log("generating c5 inputs")
-        ti = synth.c5_tree()
-        tgt = _rows(ti.target, "bf16", torch, dev)
-        par, tok = _i32(ti.parent, torch, dev), _i32(ti.token, torch, dev)
-        u = torch.from_numpy(ti.uniforms).to(dev)
-        ws = sv.Workspace(dev)
-        B, N = ti.parent.shape
-        out = (torch.empty((B, N), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev),
-               torch.empty((B,), dtype=torch.int32, device=dev), torch.empty((B, N), dtype=torch.int32, device=dev))
-        # a round reads the visited nodes' target rows (~11 MB): device copies rotate
-        nset = rotation(11 << 20)
-        tgts = [tgt] + [tgt.clone() for _ in range(nset - 1)]
-        if W == "c5g":
-            launches = [sv.prepare(sv.sv_verify_tree_greedy, t, par, tok, workspace=ws, out=out)[0] for t in tgts]
-            name = "greedy tree verify (argmax picks)"
-        else:
-            launches = [sv.prepare(sv.sv_verify_tree_pointmass, t, par, tok, ti.T, u, workspace=ws, out=out)[0]
-                        for t in tgts]
-            name = "point-mass tree verify (each candidate tested as a point mass)"
-
-        def step(i):
-            launches[i % nset]()
-
-        wall, tot_ms, ev_ms = timed(step, args.steps, args.warmup, torch)
-        ms = 1e3 * wall / args.steps
-        acc = out[2].cpu().numpy()
-        visited_bytes = int((1 + acc).sum()) * ti.V * 2
-        result.update(value=round(B / (ms * 1e-3), 1), unit="rounds/s", ms_per_step=round(ms, 5),
-                      config=dict(workload=f"{name}: 32 requests, 60-node draft trees (depth <= 6, "
-                                           "branching <= 4), V=128,256, bf16 target rows, T=1", batch=32,
-                                  nodes=60, vocab=128_256, temperature=1.0, inputs="bf16", input_sets=nset),
-                      tokens_per_s=round(float(out[1].sum().item()) / (ms * 1e-3), 1),
-                      mean_tokens_per_round=round(float(out[1].float().mean().item()), 4),
-                      visited_target_row_bytes=visited_bytes,
-                      visited_GBps=round(visited_bytes / (ms * 1e-3) / 1e9, 1),
-                      event_ms_per_step=dict(timed_region=round(tot_ms / args.steps, 5),
-                                             p50=round(float(np.percentile(ev_ms, 50)), 5)),
-                      roofline=None)
-    elif W == "c3s":
-        # the headline round with the vocabulary split over 8 devices: one
-        # device's share (31,040 columns of every row) through the three shard
-        # steps; the exchanges between them (a few KB) are filled once
-        log("generating c3 inputs for the sharded verify")
-        ci = synth.c3_sampled()
-        G, V, B, k = 8, ci.V, ci.B, ci.k_max
-        bounds = [V * g // G for g in range(G + 1)]
-        trs, qrs = _i32(ci.t_row_start, torch, dev), _i32(ci.q_row_start, torch, dev)
-        ids, dl = _i32(ci.draft_ids[:, :k], torch, dev), _i32(ci.draft_len, torch, dev)
-        u = torch.from_numpy(ci.uniforms).to(dev)
-        cols = [(_rows(np.ascontiguousarray(ci.target[:, bounds[g]:bounds[g + 1]]), "bf16", torch, dev),
-                 _rows(np.ascontiguousarray(ci.draft[:, bounds[g]:bounds[g + 1]]), "bf16", torch, dev))
-                for g in range(G)]
-        wss = [sv.Workspace(dev) for _ in range(G)]
-        st1 = [sv.sv_shard_stats(cols[g][0], cols[g][1], bounds, g, trs, qrs, ids, dl, ci.T, workspace=wss[g])
-               for g in range(G)]
-        all_pairs = torch.stack([p for p, _ in st1])
-        all_at = torch.stack([a for _, a in st1])
-        mass = torch.zeros((G, B, 3), dtype=torch.float64, device=dev)
-        for g in range(G):
-            sv.sv_shard_residual(cols[g][0], cols[g][1], bounds, g, trs, qrs, ids, dl, ci.T, u, all_pairs, all_at,
-                                 mass, workspace=wss[g])
-        out = (torch.empty((B, k + 1), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev),
-               torch.empty((B,), dtype=torch.int32, device=dev), None)
-        for g in range(G):
-            sv.sv_shard_draw(cols[g][0], cols[g][1], bounds, g, trs, qrs, ids, dl, ci.T, u, all_pairs, mass, out,
-                             workspace=wss[g])
-        # device copies of shard 0's columns rotate (40 MB a step)
-        share = (bounds[1] - bounds[0]) * 2 * (ci.target.shape[0] + ci.draft.shape[0])
-        nset = rotation(share)
-        calls = []
-        for j in range(nset):
-            tg, qg = cols[0] if j == 0 else (cols[0][0].clone(), cols[0][1].clone())
-            calls.append([sv.prepare(sv.sv_shard_stats, tg, qg, bounds, 0, trs, qrs, ids, dl, ci.T, out=st1[0],
-                                     workspace=wss[0])[0],
-                          sv.prepare(sv.sv_shard_residual, tg, qg, bounds, 0, trs, qrs, ids, dl, ci.T, u, all_pairs,
-                                     all_at, mass, workspace=wss[0])[0],
-                          sv.prepare(sv.sv_shard_draw, tg, qg, bounds, 0, trs, qrs, ids, dl, ci.T, u, all_pairs, mass,
-                                     out, workspace=wss[0])[0]])
-
-        def step(i):
-            for c in calls[i % nset]:
-                c()
-
-        wall, tot_ms, ev_ms = timed(step, args.steps, args.warmup, torch)
-        ms = 1e3 * wall / args.steps
-        result.update(value=round(B / (ms * 1e-3), 1), unit="rounds/s", ms_per_step=round(ms, 5),
-                      config=dict(workload="sampled chain verify on one of 8 vocabulary shards: 64 requests, k=4, "
-                                           "31,040 of V=248,320 columns per device, bf16, T=0.7 (the three shard "
-                                           "steps of one device; the all-gathers between them not included)",
-                                  batch=B, k=k, vocab=V, shards=G, inputs="bf16", input_sets=nset),
-                      shard_bytes=share,
-                      event_ms_per_step=dict(timed_region=round(tot_ms / args.steps, 5),
-                                             p50=round(float(np.percentile(ev_ms, 50)), 5)),
-                      roofline=None)
-    elif W == "tb":
-        # the EAGLE-2 tree built on the device at the tree workload's shape:
-        # 32 requests, top 4 children, the best 4 of each layer expanded, 6
-        # rounds, 60 nodes kept; a step = the 6 rounds (each a top-k pass over
-        # the expanded nodes' draft rows) and the finalize with the mask
-        log("generating draft rows for the tree builder")
-        B, V, top, exp, depth, N = 32, 128_256, 4, 4, 6, 60
-        rng = np.random.default_rng(2026)
-        rounds = []
-        for r in range(depth):
-            n = B * (1 if r == 0 else exp)
-            l = rng.standard_normal((n, V)).astype(np.float32) * 1.5
-            p = np.exp(l - l.max(axis=1, keepdims=True))
-            p /= p.sum(axis=1, keepdims=True)
-            rounds.append(_rows(synth.encode(p, "bf16"), "bf16", torch, dev))
-        state = sv.DraftTreeState(B, 1 + top + (depth - 1) * exp * top, dev)
-        ws = sv.Workspace(dev)
-        nexts = [torch.empty((B, exp), dtype=torch.int32, device=dev) for _ in range(depth)]
-        outs = ([torch.empty((B, N), dtype=torch.int32, device=dev) for _ in range(4)]
-                + [torch.empty((B, N, N), dtype=torch.uint8, device=dev)])
-        # device copies of the draft rows rotate (172 MB a build)
-        row_bytes = sum(int(t.numel()) * 2 for t in rounds)
-        nset = rotation(row_bytes)
-        sets = [rounds] + [[t.clone() for t in rounds] for _ in range(nset - 1)]
-        fin = sv.prepare(sv.sv_tree_finalize, state, N, out=outs)[0]
-        calls = []
-        for rs in sets:
-            calls.append([sv.prepare(sv.sv_tree_expand, rs[r], None if r == 0 else nexts[r - 1], top, exp,
-                                     state, next_exp=nexts[r], workspace=ws)[0] for r in range(depth)] + [fin])
-
-        def step(i):
-            for c in calls[i % nset]:
-                c()
-
-        wall, tot_ms, ev_ms = timed(step, args.steps, args.warmup, torch)
-        ms = 1e3 * wall / args.steps
-        result.update(value=round(B / (ms * 1e-3), 1), unit="trees/s", ms_per_step=round(ms, 5),
-                      config=dict(workload="EAGLE-2 draft tree built on the device: 32 requests, V=128,256 bf16 "
-                                           "draft rows, top 4 children, 4 nodes expanded per round, 6 rounds, "
-                                           "60 nodes kept, ancestor mask", batch=B, vocab=V, top_children=top,
-                                  expand_per_round=exp, rounds=depth, nodes=N, inputs="bf16", input_sets=nset),
-                      draft_row_bytes_per_step=row_bytes,
-                      row_GBps=round(row_bytes / (ms * 1e-3) / 1e9, 1),
-                      event_ms_per_step=dict(timed_region=round(tot_ms / args.steps, 5),
-                                             p50=round(float(np.percentile(ev_ms, 50)), 5)),
-                      roofline=None)
-    else:  # c2: prompt lookup + greedy verify
-        log("generating c2 inputs")
-        g = synth.c2_greedy()
-        ctx = _i32(g.ctx, torch, dev)
-        cl = _i32(g.ctx_len, torch, dev)
-        tgt = _rows(g.target, "bf16", torch, dev)
-        trs = _i32(np.arange(g.B) * (g.k + 1), torch, dev)
-        ws = sv.Workspace(dev)
-
-        # device copies of the contexts and target rows rotate (21.5 MB a step)
-        nset = rotation(g.target.size * 2 + g.ctx.size * 4)
-        pairs = []
-        for j in range(nset):
-            c_j, t_j = (ctx, tgt) if j == 0 else (ctx.clone(), tgt.clone())
-            draft, (ids, lens) = sv.prepare(sv.sv_ngram_draft, c_j, cl, g.window, g.k)
-            pairs.append((draft, sv.prepare(sv.sv_verify_greedy, t_j, trs, ids, lens, workspace=ws)[0]))
-
-        def step(i):
-            draft, verify = pairs[i % nset]
-            draft()
-            verify()
-
-        wall, tot_ms, ev_ms = timed(step, args.steps, args.warmup, torch)
-        ms = 1e3 * wall / args.steps
-        fb = g.target.size * 2 + g.ctx.size * 4
-        result.update(value=round(g.B / (ms * 1e-3), 1), unit="rounds/s", ms_per_step=round(ms, 5),
-                      config=dict(workload="prompt-lookup draft + greedy verify: 64 requests, contexts of "
-                                           "4,096 tokens, window 3, k=4, V=32,000, bf16", batch=64, k=4,
-                                  vocab=32_000, inputs="bf16", input_sets=nset),
-                      formula_bytes_per_step=fb, formula_GBps=round(fb / (ms * 1e-3) / 1e9, 1),
-                      dtype="int32+f32", roofline=None)
+            lat.append(time.perf_counter() - t0)
+        result["b1_call_latency_us"] = dict(p50=round(1e6 * float(np.percentile(lat, 50)), 2),
+                                            p90=round(1e6 * float(np.percentile(lat, 90)), 2),
+                                            what="one sv_verify_sample call at B=1 (V=2048 f32, k=4), enqueue to "
+                                                 "completion, host wall clock, 200 calls")
+    elif w["roofline_bytes"] is not None and k_us is not None:
+        nbytes, kname, what = w["roofline_bytes"](accepted)
+        gbps = nbytes / (k_us * 1e-6) / 1e9
+        result["roofline"] = dict(bound="hbm", kernel=kname, achieved=round(gbps, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
+                                  frac=round(gbps / PEAK_HBM_GBPS, 4), traffic=traffic(W, kname),
+                                  algorithmic_bytes_per_launch=nbytes, bytes_are=what, avg_launch_us=round(k_us, 3),
+                                  timing=f"inside {n_meas} steps like the timed ones (HIP events the library records "
+                                         "around the kernel on the step's stream)")
+    else:
+        nbytes = w["step_bytes"]
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        result["roofline"] = dict(bound="hbm", kernel="whole step", achieved=round(gbps, 1), peak=PEAK_HBM_GBPS,
+                                  unit="GB/s", frac=round(gbps / PEAK_HBM_GBPS, 4), traffic=None,
+                                  algorithmic_bytes_per_launch=nbytes, bytes_are=w["step_bytes_are"],
+                                  timing="wall clock per step (several dependent kernels)")
+    if not args.no_cpu:
+        log("timing the oracle on the host")
+        kind, A, P, B = w["cpu"]
+        cb, outs = cpu_baseline(kind, A, P, B, args.cpu_seconds, "trees/s" if kind == "tree_build" else "rounds/s")
+        result["cpu_baseline"] = cb
+        if kind == "chain" and w["kind"] == "chain":
+            tok = out[0].cpu().numpy()
+            same = near = 0
+            for b, (t, c, margin) in outs.items():
+                ok = c == counts[b] and np.array_equal(t, tok[b])
+                same += ok
+                near += (not ok) and margin < 1e-6
+            result["parity_sample"] = dict(requests=len(outs), identical=int(same), boundary=int(near),
+                                           mismatched=int(len(outs) - same - near))
     print(json.dumps(result), flush=True)
 
 

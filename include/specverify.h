@@ -116,12 +116,16 @@ typedef enum {
                                    drawn from p (chain) / p was left unchanged (tree) */
 #define SV_FLAG_BAD_TREE 32     /* parent[b,0] != -1, or parent[b,c] not in [0,c) */
 #define SV_FLAG_SYNC_TIMEOUT 64 /* tree verifies: the workgroups sharing a request did not
-                                   all report within the bounded wait (only possible when
-                                   other work on the device keeps some of them from being
-                                   scheduled); that request's outputs are undefined.  The
-                                   chain verifies never wait for a workgroup to be
-                                   scheduled and report this bit only if a word another
-                                   workgroup stored never becomes visible */
+                                   all report within the bounded wait (2^20 polls, about a
+                                   second); that request's outputs are undefined.  The
+                                   walk's grid is sized to be resident at once on an idle
+                                   device; kernels of other streams that hold compute
+                                   units delay the rest of the grid only until they end,
+                                   so the bit needs a kernel that runs (or spins) for the
+                                   whole wait beside the walk.  The chain verifies never
+                                   wait for a workgroup to be scheduled and report this
+                                   bit only if a word another workgroup stored never
+                                   becomes visible */
 
 int sv_abi_version(void);
 const char* sv_status_string(int status);

@@ -49,13 +49,13 @@ def run_sample(ci, status=None, workspace=None, max_new=None, eos_id=-1, diag=Tr
 
 
 def same_round(a, b, keys=("tokens", "count", "accepted")):
-    """The chain's verify paths (statistics of every row then the walk; the
-    one-kernel round) combine the same segment pairs in the same order and
-    form the same per-tile sums, so tokens, counts and accepted counts are
-    identical.  The residual mass totals those tile sums in float64 in a
-    different order on each path (per slice of the walk's workgroups, or
-    across all tiles at once), so its float32 value may differ by one unit in
-    the last place."""
+    """The chain's statistics paths (the partials of every row, with or
+    without the diagnostics kernel, or the lazy statistics of rows 0..m)
+    combine the same segment pairs in the same order, and the draw kernel
+    that follows each forms and totals the same tile sums, so tokens, counts
+    and accepted counts are identical.  The residual mass is held to one unit
+    in the last place of float32 (the bound a change of the totalling order
+    would need)."""
     for k in keys:
         assert np.array_equal(a[k], b[k]), k
     ra, rb = np.asarray(a["resid"], dtype=np.float64), np.asarray(b["resid"], dtype=np.float64)

@@ -54,8 +54,8 @@ def test_workspace_sizes(lib):
 
 
 def test_sample_workspace_sizes_know_k_max(lib):
-    """The exact query of a sampled chain call: the one-kernel round's words
-    at the headline shape (B = 64, k = 4, V = 248,320) come to well under the
+    """The exact query of a sampled chain call: the segment pairs and the
+    draw's tile sums at the headline shape (B = 64, k = 4, V = 248,320) come to well under the
     any-k_max bound, which must still cover it; the bound covers every
     k_max; bad sizes give 0."""
     exact = sv.sample_workspace_bytes(64, 320, 248_320, 4)

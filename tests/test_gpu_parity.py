@@ -393,6 +393,30 @@ def test_gpu_tree_c5_full(c5):
     _same_walk(run_tree(c5, diag=False), got)
 
 
+def test_gpu_tree_beside_another_stream(c5):
+    """The walk's workgroups of one request wait for each other.  Copies
+    queued on another stream just before the walk hold compute units while
+    it starts; they never wait for the walk, so they only delay the rest of
+    its grid: the outputs are the oracle's and no wait runs out (no sync
+    timeout bit)."""
+    say("tree c5 beside another stream's copies")
+    want = _oracle_tree(c5)
+    src = torch.empty(1 << 28, dtype=torch.uint8, device=DEV)
+    dst = torch.empty_like(src)
+    side = torch.cuda.Stream()
+    for rep in range(3):
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(4):
+                dst.copy_(src)
+        st = _status()
+        got = run_tree(c5, status=st, diag=False)
+        nb, bad = compare_tokens(got, want, keys=("tokens", "count", "accepted", "path"))
+        assert bad.size == 0 and nb <= 2, (rep, bad[:10])
+        assert int(st.item()) == _or(want["flags"]), rep
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("B", [1, 3, 300])
 def test_gpu_tree_group_counts(B):
     # the library splits a request over G = min(32, 256 // B, tiles) workgroups:

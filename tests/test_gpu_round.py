@@ -1,13 +1,13 @@
-"""The one-kernel sampled chain round against the float64 oracle (MI355X, through
-the C ABI): long chains whose rows are decided one after another, rounds that
-keep every draft, empty drafts, the vocabulary and draft-count limits of the
-one-kernel path and the calls just past them (which take the statistics-then-
-walk path), and the round running beside another stream's kernels.
+"""The sampled chain round against the float64 oracle (MI355X, through the C
+ABI): long chains (k_max 30 and 31) whose drafts are mostly kept, rounds that
+keep every draft, empty drafts, vocabularies of 2^19 and one past it (a last
+tile of one element), end-token and budget cuts, and the round running beside
+another stream's kernels.
 
-The one-kernel path is taken when no diagnostics are asked for, requests own
-their rows, k_max <= 30 and V <= 524,288; asking for diagnostics takes the
-statistics of every row and the walk, so each case is also compared across
-the two paths."""
+Every case runs twice: without diagnostics (the softmax statistics of every
+target row, then the draw kernel: the accept scan, the residual's tile sums
+and the inverse-CDF pick) and with them (the same statistics, the
+diagnostics kernel, then the draw); the two must give the same round."""
 import numpy as np
 import pytest
 import torch
@@ -48,7 +48,7 @@ def _check(ci, label, max_boundary=2, **kw):
     ok = (want["flags"] & oracle.INVALID_FLAGS) == 0
     assert np.all(close(got["resid"][ok], want["resid"][ok])), label
     assert int(st.item()) == _or(want["flags"]), label
-    # the statistics of every row then the walk: the same round
+    # with diagnostics: the same round
     st2 = _status()
     full = run_sample(ci, status=st2, diag=True, **kw)
     same_round(got, full)
@@ -57,10 +57,10 @@ def _check(ci, label, max_boundary=2, **kw):
 
 
 def test_gpu_round_long_chains_k30():
-    """k_max = 30 (the one-kernel path's limit) with a draft close to the
-    target (sigma 0.15), so many requests keep long runs of drafts and their
-    rows are decided one after another."""
-    say("one-kernel round: k_max = 30, close draft, V = 20,011")
+    """k_max = 30 with a draft close to the target (sigma 0.15), so many
+    requests keep long runs of drafts and the break row lies far down the
+    chain."""
+    say("round: k_max = 30, close draft, V = 20,011")
     rng = np.random.default_rng(7)
     ks = rng.integers(0, 31, size=24)
     ks[0] = 30
@@ -69,8 +69,8 @@ def test_gpu_round_long_chains_k30():
     assert want["accepted"].max() >= 8
 
 
-def test_gpu_round_k31_takes_the_walk():
-    say("k_max = 31: past the one-kernel limit")
+def test_gpu_round_k31():
+    say("round: k_max = 31, V = 9,000")
     rng = np.random.default_rng(8)
     ks = rng.integers(0, 32, size=12)
     ks[0] = 31
@@ -81,7 +81,7 @@ def test_gpu_round_k31_takes_the_walk():
 def test_gpu_round_every_draft_kept_and_empty_drafts():
     """u = 0 keeps every draft with p(x) > 0 (the extra token then comes from
     row k); requests with no draft draw from row 0."""
-    say("one-kernel round: all kept, empty drafts, V = 33,333 f32")
+    say("round: all kept, empty drafts, V = 33,333 f32")
     ks = np.array([0, 3, 5, 0, 1, 5, 2, 4], dtype=np.int64)
     ci = synth.sampled_chain(303, 8, ks, 33_333, 0.8, sd=2.0, n_boost=4, boost=5.0, sigma=1.0, kind="f32")
     ci.uniforms[[1, 2, 5]] = 0.0
@@ -92,16 +92,16 @@ def test_gpu_round_every_draft_kept_and_empty_drafts():
 
 @pytest.mark.parametrize("V", [524_288, 524_289])
 def test_gpu_round_vocab_limit(V):
-    say(f"vocabulary {V} (the one-kernel limit is 524,288)")
+    say(f"round: vocabulary {V}")
     ci = synth.sampled_chain(304, 4, np.array([3, 0, 2, 3]), V, 0.7, sd=2.5, n_boost=5, boost=6.0, sigma=1.5,
                              kind="bf16")
     _check(ci, f"V={V}")
 
 
 def test_gpu_round_edges_eos_budget():
-    """End token and budget cuts through the one-kernel round (drafts drawn
-    from q: the end token is the second draft of request 1)."""
-    say("one-kernel round: end token and budgets")
+    """End token and budget cuts (drafts drawn from q: the end token is the
+    second draft of the request with the most drafts)."""
+    say("round: end token and budgets")
     rng = np.random.default_rng(9)
     ks = rng.integers(0, 7, size=48)
     ci = synth.sampled_chain(305, 48, ks, 12_345, 1.0, sd=1.0, n_boost=3, boost=3.0, sigma=0.3, kind="bf16")
@@ -114,7 +114,7 @@ def test_gpu_round_beside_another_stream():
     """The round's blocks wait only for blocks launched before them, so it
     needs no particular residency: run it while another stream keeps the
     device busy with large copies, and compare with the oracle."""
-    say("one-kernel round beside another stream's copies")
+    say("round beside another stream's copies")
     ci = synth.c3_sampled(B=64, k=4, V=248_320, T=0.7, salt=4)
     want = _oracle(ci)
     src = torch.empty(1 << 28, dtype=torch.uint8, device=DEV)
