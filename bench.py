@@ -25,7 +25,8 @@ Each line carries:
   which are bracketed by synchronisations;
 * roofline: the dominant kernel of the step, its algorithmic bytes per launch
   over its average duration inside the steps (HIP events that the library's
-  measurement hook records on the step's stream around that kernel), against
+  measurement hook hands to that kernel's launch, on the step's stream, so
+  they take the kernel's own start and end), against
   the 8 TB/s HBM peak; where no one kernel dominates (the shard steps, the
   tree build) the whole step; for the fixed-prefix chain, whose rows stay in
   cache, its fp32 work against the 157.3 TFLOP/s vector peak; `traffic` is
@@ -56,6 +57,8 @@ METRIC = "verified rounds/s + achieved HBM GB/s (% peak), B=64 k=4 V=248,320 bf1
 PEAK_HBM_GBPS = 8000.0
 PEAK_FP32_TFLOPS = 157.3
 MAX_POOL = 16  # the host cores one GPU's share of the machine has
+TIMING = ("inside {n} steps like the timed ones: HIP events handed to the kernel's launch on the step's stream "
+          "(the kernel's own start and end)")
 CSRC = os.path.join(ROOT, "draft_verify_sampling_amd", "csrc")
 COMMON_SRCS = ["common.hpp", "words.hpp", "launch.hpp", "tiles.hpp", "segment.hpp"]
 # the sources a kernel is compiled from: its counter summary holds while
@@ -148,7 +151,8 @@ def event_pass(step, n, torch):
 def kernel_pass(step, n, sv, torch, arm_call):
     """n steps with the library's measurement hook armed right before the
     step's `arm_call`-th library call: the average duration (us) of the
-    kernel that call streams its rows with, from HIP events on its stream."""
+    kernel that call streams its rows with (HIP events handed to its launch
+    take its own start and end)."""
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
     for a, b in ev:  # the events exist before the hook records them
         a.record()
@@ -387,7 +391,7 @@ def w_chain(W, args, torch, sv, synth, dev):
              ids=ci0.draft_ids[:, :max(k_max, 1)], dlen=ci0.draft_len, u=u0)
     P = dict(t_kind=ci0.t_kind, q_kind=ci0.q_kind, V=ci0.V, k_max=k_max, T=ci0.T)
     graphs = _capture(calls, torch) if args.graph else None
-    w = dict(step=_call_step(calls, graphs), arm_call=None if W == "c1" else 0, B=B, unit="rounds/s", cfg=cfg,
+    w = dict(step=_call_step(calls, graphs), arm_call=0, B=B, unit="rounds/s", cfg=cfg,
              dtype="f32", formula=int(np.mean([formula(c) for c in sets])), out=out, nsets=len(sets),
              roofline_bytes=None if W == "c1" else roofline_bytes, cpu=("chain", A, P, B), kind="chain")
     if W == "c1":
@@ -428,12 +432,12 @@ def w_tree(W, args, torch, sv, synth, dev):
     kids = [[[c for c in range(1, N) if ti.parent[b, c] == v] for v in range(N)] for b in range(B)]
 
     def walk_bytes(_accepted):
-        """Bytes the walk must read for this round (from the path it took):
-        per visited node one pass over its target row (its softmax pair, or
-        its argmax); per rejected child one residual pass over the node's
-        target and draft rows (sampled tree), or one pass over its target row
-        at its first rejection (point mass); one pass for the last draw when
-        no pass at the last node preceded it (greedy: none)."""
+        """The bytes this round must bring from HBM, from the path it took:
+        the target row of every visited node (its softmax pair, or its
+        argmax) and, in the sampled tree, the draft row of every visited
+        node where a child was rejected (the residual passes).  A node's
+        further passes over the same rows (one per rejected child, the last
+        draw's, the pick's tile) re-read rows the walk has just read."""
         path, acc = out[3].cpu().numpy(), out[2].cpu().numpy()
         total = 0
         for b in range(B):
@@ -441,14 +445,10 @@ def w_tree(W, args, torch, sv, synth, dev):
             for j, v in enumerate(visited):
                 rej = len(kids[b][v]) if j + 1 == len(visited) else kids[b][v].index(visited[j + 1])
                 total += 2 * V
-                if W == "c5":
-                    total += rej * 4 * V
-                elif W == "c5p" and rej:
+                if W == "c5" and rej:
                     total += 2 * V
-                if j + 1 == len(visited) and W != "c5g" and rej == 0:
-                    total += 2 * V
-        return (total, "k_walk", "per visited node its target row; per rejected child the node's target and draft "
-                                 "rows (point mass: the target row at the first rejection); the last draw's pass")
+        return (total, "k_walk", "the target row of every visited node" +
+                ("; the draft row of every visited node with a rejected child" if W == "c5" else ""))
 
     A = dict(target=ti.target, draft=ti.draft, parent=ti.parent, token=ti.token, u=ti.uniforms)
     return dict(step=_call_step(calls), arm_call=0, B=B, unit="rounds/s", cfg=cfg,
@@ -574,11 +574,14 @@ def run_ceiling(args, torch, sv, dev, result):
     bufs = [torch.full((part,), 7, dtype=torch.uint8, device=dev) for _ in range(4)]
     nb = int(sv.load().sv_debug_read_blocks(part))
     outs = [torch.empty((nb,), dtype=torch.int32, device=dev) for _ in bufs]
-    step = lambda i, arm=None: sv.sv_debug_read_ceiling(bufs[i % 4], out=outs[i % 4])
+    def step(i, arm=None):
+        if arm is not None:
+            arm[1]()
+        sv.sv_debug_read_ceiling(bufs[i % 4], out=outs[i % 4])
+
     settle(step, args.settle_seconds, torch)
-    ms = event_pass(step, 200, torch)
+    us = kernel_pass(step, 200, sv, torch, 0)
     wall, _ = timed(step, args.steps, args.warmup, torch)
-    us = 1e3 * float(np.mean(ms))
     gbps = part / (us * 1e-6) / 1e9
     result.update(metric="HBM read ceiling (pure streaming read)", value=round(gbps, 1), unit="GB/s",
                   ms_per_step=round(1e3 * wall / args.steps, 5), dtype="u32 words",
@@ -586,35 +589,42 @@ def run_ceiling(args, torch, sv, dev, result):
                                        "rotating buffers", bytes_per_launch=part),
                   roofline=dict(bound="hbm", kernel="k_read_ceiling", achieved=round(gbps, 1), peak=PEAK_HBM_GBPS,
                                 unit="GB/s", frac=round(gbps / PEAK_HBM_GBPS, 4),
-                                traffic=traffic("k_read_ceiling", "ceiling"), algorithmic_bytes_per_launch=part,
-                                avg_launch_us=round(us, 3), timing="HIP events around each of 200 launches"),
+                                traffic=traffic("ceiling", "k_read_ceiling"), algorithmic_bytes_per_launch=part,
+                                avg_launch_us=round(us, 3),
+                                timing="200 launches, each timed by HIP events given to the launch (the kernel's own "
+                                       "start and end)"),
                   cpu_baseline=None)
 
 
 # ---------------------------------------------------------------------------
-# counter summaries (rocprofv3 --pmc databases -> profiles/<kernel>_<w>_traffic.json)
+# counter summaries (rocprofv3 --pmc csv -> profiles/<kernel>_<w>_traffic.json)
 # ---------------------------------------------------------------------------
-def summarize_counters(workload, kernel, fetch_db, write_db):
-    """Per-launch HBM traffic of `kernel` from two rocprofv3 --pmc databases
-    (FETCH_SIZE and WRITE_SIZE passes of `bench.py --calibrate-copy`), each
+def summarize_counters(workload, kernel, fetch_csv, write_csv):
+    """Per-launch HBM traffic of `kernel` from two rocprofv3 --pmc runs (the
+    counter_collection.csv of a FETCH_SIZE and of a WRITE_SIZE pass of
+    `bench.py --calibrate-copy`, --output-format csv), each
     counter scaled by what it reads for the run's 256 MiB device-to-device
     copies; writes profiles/<kernel>_<workload>_traffic.json."""
-    import sqlite3
+    import csv
 
-    def per_kernel(db, counter):
-        cur = sqlite3.connect(db).cursor()
-        rows = cur.execute("select kernel_name, value from counters_collection where counter_name = ?",
-                           (counter,)).fetchall()
-        out = {}
-        for name, v in rows:
-            out.setdefault(name, []).append(float(v))
-        return out
+    def per_kernel(path, counter):
+        """{kernel name: [value per dispatch]} from a counter_collection.csv,
+        and the values of the run's first 8 copies (the calibration copies
+        `--calibrate-copy` runs before anything else)."""
+        out, copies = {}, []
+        with open(path, newline="") as f:
+            rows = [r for r in csv.DictReader(f) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        for r in rows:
+            out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+            if "copyBuffer" in r["Kernel_Name"] and len(copies) < 8:
+                copies.append(float(r["Counter_Value"]))
+        return out, copies
 
     ref_kib = 256 * 1024
     res = {}
-    for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
-        k = per_kernel(db, counter)
-        copies = sorted(v for name, vals in k.items() if "copyBuffer" in name for v in vals)[-8:]
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        k, copies = per_kernel(path, counter)
         scale = (sum(copies) / len(copies)) / ref_kib
         vals = [v for name, vs in k.items() if f"{kernel}<" in name or name.startswith(f"{kernel}(")
                 or f"::{kernel}(" in name for v in vs]
@@ -712,19 +722,18 @@ def main():
                   formula_frac_of_peak=round(fb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4))
     if W == "c1":
         # cache-resident by construction (every round reads the same 9 rows):
-        # one wave per round, bound by its dependent steps; its fp32 work
-        # against the vector peak, the whole step timed
+        # one wave per round, bound by its dependent steps; the one-wave
+        # round's fp32 work against the vector peak
         B, V = w["B"], w["cfg"]["vocab"]
         flops = B * V * 12.0
-        tfl = flops / (ms * 1e-3) / 1e12
-        result["roofline"] = dict(bound="alu", kernel="whole step (k_row_stats on the 5 shared rows + k_walk_small)",
-                                  achieved=round(tfl, 3), peak=PEAK_FP32_TFLOPS, unit="TFLOP/s",
-                                  frac=round(tfl / PEAK_FP32_TFLOPS, 4), traffic=None,
+        tfl = flops / (k_us * 1e-6) / 1e12
+        result["roofline"] = dict(bound="alu", kernel="k_walk_small", achieved=round(tfl, 3), peak=PEAK_FP32_TFLOPS,
+                                  unit="TFLOP/s", frac=round(tfl / PEAK_FP32_TFLOPS, 4), traffic=None,
                                   algorithmic_flops_per_launch=flops,
                                   flops_are="12 fp32 operations per element of each round's drawn row: fma, exp2, "
                                             "scale, subtract, clamp and add in the weight pass, the same again in "
                                             "the pick's rescan (exp2 counted as one)",
-                                  timing="wall clock per step")
+                                  avg_launch_us=round(k_us, 3), timing=TIMING.format(n=n_meas))
         lat = []
         for _ in range(20):
             w["b1"]()
@@ -744,8 +753,7 @@ def main():
         result["roofline"] = dict(bound="hbm", kernel=kname, achieved=round(gbps, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
                                   frac=round(gbps / PEAK_HBM_GBPS, 4), traffic=traffic(W, kname),
                                   algorithmic_bytes_per_launch=nbytes, bytes_are=what, avg_launch_us=round(k_us, 3),
-                                  timing=f"inside {n_meas} steps like the timed ones (HIP events the library records "
-                                         "around the kernel on the step's stream)")
+                                  timing=TIMING.format(n=n_meas))
     else:
         nbytes = w["step_bytes"]
         gbps = nbytes / (ms * 1e-3) / 1e9

@@ -140,9 +140,10 @@ def sample_workspace_bytes(batch: int, t_rows: int, vocab: int, k_max: int) -> i
 
 def sv_debug_time_kernel_once(before=None, after=None):
     """Arm the measurement hook (include/specverify_debug.h): the calling
-    thread's next verify call records torch.cuda.Event `before` / `after`
-    around the kernel that streams its rows (None, None disarms).  The events
-    are created here if they are not yet."""
+    thread's next verify call hands torch.cuda.Event `before` / `after` to
+    the launch of the kernel that streams its rows, so they take that
+    kernel's own start and end (None, None disarms).  The events are created
+    here if they are not yet."""
     if (before is None) != (after is None):
         raise SpecVerifyError("give both events or neither")
     ptrs = []

@@ -20,13 +20,15 @@ namespace {
 
 thread_local char g_err[512] = "";
 
-// Measurement hook (sv_debug_time_kernel_once): events recorded around the
-// streaming kernel of this thread's next verify call.
+// Measurement hook (sv_debug_time_kernel_once): the events that take the
+// start and end times of the streaming kernel of this thread's next verify
+// call.
 thread_local hipEvent_t g_stat_ev[2] = {nullptr, nullptr};
 
-// Records g_stat_ev[which] on `st` if the hook is armed.
-void stat_event(int which, hipStream_t st) {
-  if (g_stat_ev[which] != nullptr) (void)hipEventRecord(g_stat_ev[which], st);
+// Hands the armed hook's events to this thread's next timed kernel launch
+// (the call's streaming kernel launches next).
+void time_next_kernel() {
+  if (g_stat_ev[0] != nullptr) sv::g_timed = sv::TimedEvents{g_stat_ev[0], g_stat_ev[1]};
 }
 
 sv_status fail(sv_status s, const char* fmt, ...) {
@@ -46,7 +48,10 @@ bool dtype_ok(int32_t d) { return d == SV_F32 || d == SV_BF16; }
 // Disarms the measurement hook when a verify call returns (it serves that
 // call at most).
 struct HookDone {
-  ~HookDone() { g_stat_ev[0] = g_stat_ev[1] = nullptr; }
+  ~HookDone() {
+    g_stat_ev[0] = g_stat_ev[1] = nullptr;
+    sv::g_timed = sv::TimedEvents{};
+  }
 };
 
 sv_status check_workspace(const void* ws, size_t have, size_t need) {
@@ -160,21 +165,20 @@ sv_status launch_chain_call(int32_t t_dtype, int32_t q_dtype, sv::WalkArgs& a, v
     c.seg_words = reinterpret_cast<uint64_t*>(ws + L.segs_off);
     c.status = a.status;
     c.spin_limit = sv::kSpinLimit;
-    stat_event(0, st);
+    time_next_kernel();
     e = sv::launch_chain_stats(t_dtype, q_dtype, c, st);
     if (e != hipSuccess) return device_fail(e, what);
-    stat_event(1, st);
   } else {
     const bool small = ntiles == 1;  // k_walk_small reads only the partials
-    stat_event(0, st);
+    if (!small) time_next_kernel();
     e = sv::launch_row_stats(t_dtype, a.tgt, a.t_rows, a.V, a.nseg, a.c, partial, st,
                              small ? nullptr : reinterpret_cast<uint64_t*>(ws + L.rcnt_off),
                              small ? 0 : static_cast<int64_t>(L.stop_off - L.rcnt_off) / 8);
     if (e != hipSuccess) return device_fail(e, what);
-    stat_event(1, st);
     if (small) {  // one tile: one wave per request does the whole round
       a.partial = partial;
       a.ntiles = 1;
+      time_next_kernel();
       e = sv::launch_walk_small(t_dtype, q_dtype, a, st);
       return e == hipSuccess ? SV_OK : device_fail(e, what);
     }
@@ -278,12 +282,15 @@ sv_status launch_walk_call(int mode, int32_t t_dtype, int32_t q_dtype, sv::WalkA
     clear_slots = false;
   }
   const size_t lds = sv::walk_lds_bytes(a.node_cap, a.tile_cap);
-  const hipError_t e = sv::launch_walk(mode, t_dtype, q_dtype, a, lds, clear_slots, st, &stat_event);
+  time_next_kernel();
+  const hipError_t e = sv::launch_walk(mode, t_dtype, q_dtype, a, lds, clear_slots, st);
   return e == hipSuccess ? SV_OK : device_fail(e, what);
 }
 }  // namespace
 
 namespace sv {
+
+thread_local TimedEvents g_timed;
 
 sv_status set_error(sv_status s, const char* fmt, ...) {
   va_list ap;
@@ -354,11 +361,13 @@ sv_status sv_debug_time_kernel_once(void* before, void* after) {
 int64_t sv_debug_read_blocks(int64_t bytes) { return bytes <= 0 ? 0 : sv::read_blocks(bytes); }
 
 sv_status sv_debug_read_ceiling(const void* buf, int64_t bytes, uint32_t* out, void* stream) {
+  HookDone hook_done;
   if (bytes < 0 || (bytes & 15) != 0) return fail(SV_E_ARG, "bytes must be a non-negative multiple of 16");
   if (bytes == 0) return SV_OK;
   if (buf == nullptr || out == nullptr || (reinterpret_cast<uintptr_t>(buf) & 15u) != 0)
     return fail(SV_E_ARG, "buf (16-byte aligned) and out are needed");
   (void)hipGetLastError();
+  time_next_kernel();
   const hipError_t e = sv::launch_read_ceiling(buf, bytes, out, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SV_OK : device_fail(e, "sv_debug_read_ceiling");
 }
@@ -397,10 +406,9 @@ sv_status sv_ngram_draft(const int32_t* ctx, const int32_t* ctx_len, int32_t bat
   if (ctx == nullptr || ctx_len == nullptr || draft_len == nullptr || (k > 0 && draft_ids == nullptr))
     return fail(SV_E_ARG, "null pointer argument");
   (void)hipGetLastError();
-  stat_event(0, static_cast<hipStream_t>(stream));
+  time_next_kernel();
   const hipError_t e = sv::launch_ngram(ctx, ctx_len, batch, ctx_stride, window, k, draft_ids, draft_len,
                                         dev_status, static_cast<hipStream_t>(stream));
-  stat_event(1, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SV_OK : device_fail(e, "sv_ngram_draft launch");
 }
 
@@ -430,10 +438,9 @@ sv_status sv_verify_greedy(const void* target_logits, int32_t t_dtype, int32_t t
   const hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   uint64_t* keys = static_cast<uint64_t*>(workspace);
-  stat_event(0, st);
+  time_next_kernel();
   hipError_t e = sv::launch_row_argmax(t_dtype, target_logits, t_rows, vocab, nseg, keys, st);
   if (e != hipSuccess) return device_fail(e, "sv_verify_greedy argmax launch");
-  stat_event(1, st);
   sv::GreedyArgs a{};
   a.tgt = target_logits;
   a.V = vocab;

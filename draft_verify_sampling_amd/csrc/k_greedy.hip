@@ -198,9 +198,9 @@ hipError_t launch_row_argmax(int dtype, const void* rows, int64_t n_rows, int64_
                              uint64_t* keys, hipStream_t stream) {
   const dim3 grid(static_cast<uint32_t>(n_rows * nseg)), block(kBlock);
   if (dtype == kDtypeBF16)
-    hipLaunchKernelGGL((k_row_argmax<BF16, 4>), grid, block, 0, stream, rows, V, nseg, keys);
+    launch_timed((k_row_argmax<BF16, 4>), grid, block, 0, stream, rows, V, nseg, keys);
   else
-    hipLaunchKernelGGL((k_row_argmax<F32, 4>), grid, block, 0, stream, rows, V, nseg, keys);
+    launch_timed((k_row_argmax<F32, 4>), grid, block, 0, stream, rows, V, nseg, keys);
   return hipGetLastError();
 }
 

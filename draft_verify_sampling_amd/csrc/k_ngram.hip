@@ -145,8 +145,8 @@ __global__ __launch_bounds__(kBlock) void k_ngram(const int32_t* __restrict__ ct
 hipError_t launch_ngram(const int32_t* ctx, const int32_t* ctx_len, int32_t B, int32_t stride,
                         int32_t window, int32_t k, int32_t* ids, int32_t* lens, int32_t* status,
                         hipStream_t stream) {
-  hipLaunchKernelGGL(k_ngram, dim3(static_cast<uint32_t>(B)), dim3(kBlock), 0, stream, ctx, ctx_len,
-                     stride, window, k, ids, lens, status);
+  launch_timed(k_ngram, dim3(static_cast<uint32_t>(B)), dim3(kBlock), 0, stream, ctx, ctx_len,
+               stride, window, k, ids, lens, status);
   return hipGetLastError();
 }
 

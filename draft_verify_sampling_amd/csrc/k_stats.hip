@@ -53,9 +53,9 @@ hipError_t launch_row_stats(int dtype, const void* rows, int64_t n_rows, int64_t
   uint4* c16 = reinterpret_cast<uint4*>(clear);
   const int64_t n16 = clear != nullptr ? (clear_words + 1) / 2 : 0;
   if (dtype == kDtypeBF16)
-    hipLaunchKernelGGL((k_row_stats<BF16, true>), grid, block, 0, stream, rows, V, nseg, c, partial, c16, n16);
+    launch_timed((k_row_stats<BF16, true>), grid, block, 0, stream, rows, V, nseg, c, partial, c16, n16);
   else
-    hipLaunchKernelGGL((k_row_stats<F32, true>), grid, block, 0, stream, rows, V, nseg, c, partial, c16, n16);
+    launch_timed((k_row_stats<F32, true>), grid, block, 0, stream, rows, V, nseg, c, partial, c16, n16);
   return hipGetLastError();
 }
 
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kBlock) void k_read_ceiling(const uint4* __restrict
 
 hipError_t launch_read_ceiling(const void* buf, int64_t bytes, uint32_t* out, hipStream_t stream) {
   const int64_t blocks = read_blocks(bytes);
-  hipLaunchKernelGGL(k_read_ceiling, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream,
+  launch_timed(k_read_ceiling, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream,
                      static_cast<const uint4*>(buf), bytes / 16, out);
   return hipGetLastError();
 }
@@ -196,13 +196,13 @@ hipError_t launch_chain_stats(int t_dtype, int q_dtype, const ChainStatsArgs& a,
   const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.k_max + 1) * a.B * a.nseg)), block(kBlock);
   const bool tb = t_dtype == kDtypeBF16, qb = q_dtype == kDtypeBF16;
   if (tb && qb)
-    hipLaunchKernelGGL((k_chain_stats<BF16, BF16>), grid, block, 0, stream, a);
+    launch_timed((k_chain_stats<BF16, BF16>), grid, block, 0, stream, a);
   else if (tb)
-    hipLaunchKernelGGL((k_chain_stats<BF16, F32>), grid, block, 0, stream, a);
+    launch_timed((k_chain_stats<BF16, F32>), grid, block, 0, stream, a);
   else if (qb)
-    hipLaunchKernelGGL((k_chain_stats<F32, BF16>), grid, block, 0, stream, a);
+    launch_timed((k_chain_stats<F32, BF16>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((k_chain_stats<F32, F32>), grid, block, 0, stream, a);
+    launch_timed((k_chain_stats<F32, F32>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -851,8 +851,7 @@ const void* pick_walk(int mode, int t_dtype, int q_dtype) {
 }
 
 template <int kMode, class DT, class DQ>
-void launch_t(const WalkArgs& a, size_t lds, bool clear_slots, hipStream_t stream,
-              void (*mark)(int, hipStream_t)) {
+void launch_t(const WalkArgs& a, size_t lds, bool clear_slots, hipStream_t stream) {
   if constexpr (kMode == kWalkTree) {
     if (a.diag != nullptr)
       hipLaunchKernelGGL((k_tree_diag<DT, DQ>), dim3(static_cast<uint32_t>(a.B)), dim3(kMaxTreeNodes), 0, stream, a);
@@ -863,24 +862,22 @@ void launch_t(const WalkArgs& a, size_t lds, bool clear_slots, hipStream_t strea
     hipLaunchKernelGGL(k_walk_clear, dim3(static_cast<uint32_t>(blocks)), dim3(kBlock), 0, stream,
                        reinterpret_cast<uint4*>(a.slots), n16);
   }
-  if (mark != nullptr) mark(0, stream);
-  hipLaunchKernelGGL((k_walk<kMode, DT, DQ>), dim3(static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.G)),
-                     dim3(kWalkBlock), lds, stream, a);
-  if (mark != nullptr) mark(1, stream);
+  launch_timed(k_walk<kMode, DT, DQ>, dim3(static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.G)), dim3(kWalkBlock),
+               lds, stream, a);
 }
 
 template <int kMode>
 void launch_mode(int t_dtype, int q_dtype, const WalkArgs& a, size_t lds, bool clear_slots,
-                 hipStream_t stream, void (*mark)(int, hipStream_t)) {
+                 hipStream_t stream) {
   const bool tb = t_dtype == kDtypeBF16, qb = q_dtype == kDtypeBF16;
   if constexpr (kMode == kWalkPoint || kMode == kWalkGreedy) {
-    if (tb) launch_t<kMode, BF16, BF16>(a, lds, clear_slots, stream, mark);
-    else launch_t<kMode, F32, F32>(a, lds, clear_slots, stream, mark);
+    if (tb) launch_t<kMode, BF16, BF16>(a, lds, clear_slots, stream);
+    else launch_t<kMode, F32, F32>(a, lds, clear_slots, stream);
   } else {
-    if (tb && qb) launch_t<kMode, BF16, BF16>(a, lds, clear_slots, stream, mark);
-    else if (tb) launch_t<kMode, BF16, F32>(a, lds, clear_slots, stream, mark);
-    else if (qb) launch_t<kMode, F32, BF16>(a, lds, clear_slots, stream, mark);
-    else launch_t<kMode, F32, F32>(a, lds, clear_slots, stream, mark);
+    if (tb && qb) launch_t<kMode, BF16, BF16>(a, lds, clear_slots, stream);
+    else if (tb) launch_t<kMode, BF16, F32>(a, lds, clear_slots, stream);
+    else if (qb) launch_t<kMode, F32, BF16>(a, lds, clear_slots, stream);
+    else launch_t<kMode, F32, F32>(a, lds, clear_slots, stream);
   }
 }
 
@@ -931,22 +928,22 @@ hipError_t launch_walk_small(int t_dtype, int q_dtype, const WalkArgs& a, hipStr
     if (e != hipSuccess) return e;
   }
   if (tb && qb)
-    hipLaunchKernelGGL((k_walk_small<BF16, BF16>), grid, block, 0, stream, a);
+    launch_timed((k_walk_small<BF16, BF16>), grid, block, 0, stream, a);
   else if (tb)
-    hipLaunchKernelGGL((k_walk_small<BF16, F32>), grid, block, 0, stream, a);
+    launch_timed((k_walk_small<BF16, F32>), grid, block, 0, stream, a);
   else if (qb)
-    hipLaunchKernelGGL((k_walk_small<F32, BF16>), grid, block, 0, stream, a);
+    launch_timed((k_walk_small<F32, BF16>), grid, block, 0, stream, a);
   else
-    hipLaunchKernelGGL((k_walk_small<F32, F32>), grid, block, 0, stream, a);
+    launch_timed((k_walk_small<F32, F32>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_walk(int mode, int t_dtype, int q_dtype, const WalkArgs& a, size_t lds,
-                       bool clear_slots, hipStream_t stream, void (*mark)(int, hipStream_t)) {
+                       bool clear_slots, hipStream_t stream) {
   switch (mode) {
-    case kWalkTree: launch_mode<kWalkTree>(t_dtype, q_dtype, a, lds, clear_slots, stream, mark); break;
-    case kWalkPoint: launch_mode<kWalkPoint>(t_dtype, q_dtype, a, lds, clear_slots, stream, mark); break;
-    default: launch_mode<kWalkGreedy>(t_dtype, q_dtype, a, lds, clear_slots, stream, mark); break;
+    case kWalkTree: launch_mode<kWalkTree>(t_dtype, q_dtype, a, lds, clear_slots, stream); break;
+    case kWalkPoint: launch_mode<kWalkPoint>(t_dtype, q_dtype, a, lds, clear_slots, stream); break;
+    default: launch_mode<kWalkGreedy>(t_dtype, q_dtype, a, lds, clear_slots, stream); break;
   }
   return hipGetLastError();
 }

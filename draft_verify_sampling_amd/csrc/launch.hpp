@@ -1,6 +1,7 @@
 // Host-side launchers of the verify kernels and the workspace layout.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -8,6 +9,25 @@
 #include <stdint.h>
 
 namespace sv {
+
+// The measurement hook: HIP events that the next launch_timed on this thread
+// hands to the kernel launch itself, so that they take the kernel's own start
+// and end times; that launch disarms it.
+struct TimedEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+extern thread_local TimedEvents g_timed;
+
+template <class F, class... A>
+inline void launch_timed(F kernel, dim3 grid, dim3 block, size_t lds, hipStream_t stream, A... args) {
+  if (g_timed.start != nullptr) {
+    const TimedEvents ev = g_timed;
+    g_timed = TimedEvents{};
+    hipExtLaunchKernelGGL(kernel, grid, block, static_cast<uint32_t>(lds), stream, ev.start, ev.stop, 0u, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, stream, args...);
+  }
+}
 
 constexpr int kDtypeF32 = 0;
 constexpr int kDtypeBF16 = 1;
@@ -258,10 +278,8 @@ int walk_occupancy(int mode, int t_dtype, int q_dtype, size_t lds);
 // zero the exchange words first (not needed when the statistics kernel or the
 // walk itself does it).  The point-mass and greedy walks read no draft rows
 // (q_dtype is ignored).
-// `mark` (optional) is called with 0 right before the walk kernel's launch and
-// with 1 right after it (the measurement hook).
 hipError_t launch_walk(int mode, int t_dtype, int q_dtype, const WalkArgs& a, size_t lds,
-                       bool clear_slots, hipStream_t stream, void (*mark)(int, hipStream_t) = nullptr);
+                       bool clear_slots, hipStream_t stream);
 // A sampled chain round with a one-tile vocabulary (V <= 2048): one wave per
 // request from the partials of every row (k_walk_small), and the diagnostics
 // when asked for.

@@ -12,16 +12,19 @@
 extern "C" {
 #endif
 
-/* For the calling thread's next call of a verify entry point, record
- * `before` (a hipEvent_t) on that call's stream right before the kernel that
- * streams the call's rows and `after` right after it, so a caller can time
- * that kernel inside a real call:
+/* For the calling thread's next call of a verify entry point (or of
+ * sv_debug_read_ceiling), hand `before` and `after` (hipEvent_t) to the launch
+ * of the kernel that streams the call's rows, so that they take that kernel's
+ * own start and end times (the timestamps of its dispatch, as a profiler's
+ * kernel trace reports them) on the call's stream:
  *   sv_verify_sample / _philox / _noalloc   the row statistics (the partials
  *                                            of every row, or the lazy
- *                                            statistics);
+ *                                            statistics); with a one-tile
+ *                                            vocabulary, the one-wave round;
  *   sv_verify_greedy                         the row argmax;
  *   sv_verify_tree / _greedy / _pointmass    the walk;
- *   sv_ngram_draft                           the prompt-lookup kernel.
+ *   sv_ngram_draft                           the prompt-lookup kernel;
+ *   sv_debug_read_ceiling                    the streaming read.
  * The hook then disarms, also when that call fails or has no requests.
  * NULL, NULL disarms it; giving one event only is SV_E_ARG.  The events must
  * stay valid until that call returns.  Host function; the armed events are
