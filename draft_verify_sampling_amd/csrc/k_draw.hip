@@ -302,21 +302,26 @@ __global__ __launch_bounds__(kBlock) void k_chain_draw(ChainDrawArgs a) {
       mine = psum;
     }
   }
-  const double target = static_cast<double>(slot_uniform(a.u, a.seed, a.offset, b, a.k_max + 1, k)) * W;
+  // the last token's uniform: lane k of this wave loaded it at the start
+  const float uk = k < kWave ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u0), k))
+                             : slot_uniform(a.u, a.seed, a.offset, b, a.k_max + 1, k);
+  const double target = static_cast<double>(uk) * W;
   TileHit hit;
   if (!wave_find_tile(ts_w, 1, a.ntiles, mine, target, hit)) {
     draw_invalid(a, b, kFlagNonfinite | bits);
     return;
   }
   const int y = wave_pick_in_tile<DT, DQ>(row, a.V, hit, target);
-  // emission: drafts 0..m-1 then y, cut after the first end token and at the budget
+  // emission: drafts 0..m-1 then y, cut after the first end token and at the
+  // budget (lane c of this wave holds draft c from the start, c < 64)
   const int width = a.k_max + 1;
   int32_t* out = a.out_tok + static_cast<int64_t>(b) * width;
   const int32_t* xs = a.ids + static_cast<int64_t>(b) * a.k_max;
+  auto draft_at = [&](int c) { return c < kWave ? x0 : xs[c]; };  // c = c0 + lane
   int cnt = m + 1;
   for (int c0 = 0; c0 <= m; c0 += kWave) {  // the first end token among positions 0..m
     const int c = c0 + lane;
-    const int tok = c < m ? xs[c] : y;
+    const int tok = c < m ? draft_at(c) : y;
     const uint64_t hit_eos = a.eos >= 0 ? __ballot(c <= m && tok == a.eos) : 0ull;
     if (hit_eos) {
       cnt = c0 + __ffsll(static_cast<long long>(hit_eos));
@@ -327,7 +332,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_draw(ChainDrawArgs a) {
     const int budget = a.max_new[b] > 0 ? a.max_new[b] : 0;
     cnt = cnt < budget ? cnt : budget;
   }
-  for (int c = lane; c < width; c += kWave) out[c] = c < cnt ? (c < m ? xs[c] : y) : -1;
+  for (int c = lane; c < width; c += kWave) out[c] = c < cnt ? (c < m ? draft_at(c) : y) : -1;
   if (lane == 0) {
     a.out_cnt[b] = cnt;
     a.out_acc[b] = m;

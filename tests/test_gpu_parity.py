@@ -603,3 +603,37 @@ def test_gpu_prepared_calls_match_direct_calls():
             assert torch.equal(got, w), rep
         for got, w in zip(gouts, gd):
             assert torch.equal(got, w), rep
+
+
+def test_gpu_calls_on_a_side_stream():
+    """Calls given a stream that is not torch's current one: the binding makes
+    and fills their outputs, diagnostics and a fresh workspace on that stream,
+    so they equal the same calls on the current stream, bit for bit, while the
+    current stream is kept busy with copies."""
+    import draft_verify_sampling_amd as sv
+    say("sample and tree calls with diagnostics on a side stream")
+    rng = np.random.default_rng(21)
+    ks = rng.integers(0, 7, size=16)
+    ci = synth.sampled_chain(311, 16, ks, 30_011, 0.9, sd=2.0, n_boost=3, boost=4.0, sigma=1.0, kind="bf16")
+    sargs = (rows_to_dev(ci.target, ci.t_kind), rows_to_dev(ci.draft, ci.q_kind), i32(ci.t_row_start),
+             i32(ci.q_row_start), i32(ci.draft_ids[:, :ci.k_max]), i32(ci.draft_len), ci.T, f32(ci.uniforms))
+    ti = synth.c5_tree(B=8, N=20, V=30_000, top_children=3, expand_per_layer=3, max_depth=4, salt=5)
+    targs = (rows_to_dev(ti.target, ti.t_kind), rows_to_dev(ti.draft, ti.q_kind), i32(ti.parent),
+             i32(ti.token), ti.T, f32(ti.uniforms))
+    ref_s = [t.cpu().numpy() for t in sv.sv_verify_sample(*sargs, diag=True)]
+    ref_t = [t.cpu().numpy() for t in sv.sv_verify_tree(*targs, diag=True)]
+    torch.cuda.synchronize()
+    busy = torch.empty(1 << 28, dtype=torch.uint8, device=DEV)
+    busy2 = torch.empty_like(busy)
+    side = torch.cuda.Stream()
+    for rep in range(3):
+        for _ in range(4):
+            busy2.copy_(busy)
+        got_s = sv.sv_verify_sample(*sargs, diag=True, stream=side, workspace=sv.Workspace(DEV))
+        got_t = sv.sv_verify_tree(*targs, diag=True, stream=side, workspace=sv.Workspace(DEV))
+        side.synchronize()
+        for name, g, w in zip(("tokens", "count", "accepted", "diag", "resid"), got_s, ref_s):
+            assert np.array_equal(g.cpu().numpy(), w), ("sample", name, rep)
+        for name, g, w in zip(("tokens", "count", "accepted", "path", "diag"), got_t, ref_t):
+            assert np.array_equal(g.cpu().numpy(), w), ("tree", name, rep)
+    torch.cuda.synchronize()
