@@ -136,7 +136,9 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
       qx = DQ::at(row_ptr<DQ>(a.dq, qs + i, a.V), x);
     }
   }
-  const MS t = segment_ms<DT, true>(row_ptr<DT>(a.tgt, ts + i, a.V), a.V, seg, a.nseg, a.c, sh);
+  // ordinary (not non-temporal) loads: the draw re-reads the break row, which
+  // the last-level cache then still holds
+  const MS t = segment_ms<DT, false>(row_ptr<DT>(a.tgt, ts + i, a.V), a.V, seg, a.nseg, a.c, sh);
   uint64_t* words = a.seg_words + (static_cast<int64_t>(b) * R + i) * a.nseg;
   if (threadIdx.x == 0) {
     store_word(words + seg, enc_ms(t));
