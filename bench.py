@@ -44,6 +44,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import tempfile
 import time
@@ -62,7 +63,7 @@ TIMING = ("inside {n} steps like the timed ones: HIP events handed to the kernel
 CSRC = os.path.join(ROOT, "draft_verify_sampling_amd", "csrc")
 COMMON_SRCS = ["common.hpp", "words.hpp", "launch.hpp", "tiles.hpp", "segment.hpp"]
 # the sources a kernel is compiled from: its counter summary holds while
-# their hash is unchanged
+# their code is unchanged
 KERNEL_SRCS = {
     "k_row_stats": ["k_stats.hip"],
     "k_chain_stats": ["k_stats.hip"],
@@ -72,11 +73,22 @@ KERNEL_SRCS = {
 }
 
 
+def _code_only(text):
+    """C++ source without its comments and blank space (so a comment edit
+    keeps a counter summary valid).  String literals in these sources hold no
+    comment markers."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash(kernel):
+    """sha1 of the code (comments and blank space stripped) of the sources the
+    kernel is compiled from."""
     h = hashlib.sha1()
     for f in KERNEL_SRCS[kernel] + COMMON_SRCS:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 

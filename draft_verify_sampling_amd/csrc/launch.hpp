@@ -67,8 +67,8 @@ constexpr int kSampleTile = 2048;
 inline int64_t sample_tiles(int64_t V) { return (V + kSampleTile - 1) / kSampleTile; }
 constexpr int64_t kMaxSampleVocab = 4194304;   // 2048 tiles: their sums fit in LDS
 
-// The walk (chain and tree verify): G workgroups of kWalkBlock threads per
-// request, each owning a slice of the tiles, exchanging 64-bit words.
+// The tree walk: G workgroups of kWalkBlock threads per request, each owning
+// a slice of the tiles, exchanging 64-bit words.
 constexpr int kWalkBlock = 1024;
 constexpr int kMaxWalkGroups = 32;
 constexpr int64_t kMaxCoopBlocks = 2048;       // B * G never exceeds this

@@ -47,9 +47,9 @@
  *   only the thread-local text behind sv_last_error(), per-device caches of
  *   launch parameters (compute-unit counts, kernel occupancy), and a
  *   process-wide counter that gives each tree-walk call a unique 64-bit
- *   ticket (outputs do not depend on its value).  (A measurement hook for
- *   timing the statistics kernel inside a call is declared apart, in
- *   specverify_debug.h; it is not part of the verify operations.)
+ *   ticket (outputs do not depend on its value).  (Measurement hooks for
+ *   timing a call's streaming kernel and the read ceiling are declared apart,
+ *   in specverify_debug.h; they are not part of the verify operations.)
  * - Row data: `t_dtype` / `q_dtype` select SV_F32 (float) or SV_BF16 (bfloat16
  *   bit patterns).  A row is `vocab` consecutive elements; row r starts at
  *   element r * vocab.  Any alignment is accepted; 16-byte aligned rows take the
@@ -60,7 +60,8 @@
  *   gets a defined output.  A request with SV_FLAG_BAD_REQUEST, BAD_TOKEN,
  *   NONFINITE or BAD_TREE is invalid: count 0, accepted 0, all tokens -1.
  * - Workspace (greedy, sample, tree): caller-owned device memory of at least
- *   sv_workspace_bytes(...) bytes, 256-byte aligned.  Its contents need not be
+ *   sv_workspace_bytes(...) bytes (sampled chains: sv_sample_workspace_bytes,
+ *   which also knows k_max), 256-byte aligned.  Its contents need not be
  *   initialised: each call writes everything it later reads, so one buffer
  *   can serve calls of any shape in turn on one stream.  Calls that
  *   may run concurrently (different streams) need separate workspaces.
