@@ -85,17 +85,28 @@ uint64_t next_ticket() {
 }
 
 // Compute units of the current device (cached per device; 0 if unknown).
-int cu_count() {
-  static std::atomic<int> cache[64];
+// A device attribute of the current device, cached per device (0 on error).
+int device_attr(hipDeviceAttribute_t attr, std::atomic<int>* cache) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return 0;
   if (dev >= 0 && dev < 64) {
     if (const int n = cache[dev].load(std::memory_order_relaxed)) return n;
   }
   int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, attr, dev) != hipSuccess) return 0;
   if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
   return n;
+}
+
+int cu_count() {
+  static std::atomic<int> cache[64];
+  return device_attr(hipDeviceAttributeMultiprocessorCount, cache);
+}
+
+// LDS bytes one workgroup may allocate.
+int max_lds_per_block() {
+  static std::atomic<int> cache[64];
+  return device_attr(hipDeviceAttributeMaxSharedMemoryPerBlock, cache);
 }
 
 
@@ -281,7 +292,19 @@ sv_status launch_walk_call(int mode, int32_t t_dtype, int32_t q_dtype, sv::WalkA
     a.ticket = next_ticket();
     clear_slots = false;
   }
-  const size_t lds = sv::walk_lds_bytes(a.node_cap, a.tile_cap);
+  // The sampled tree walk keeps its slice's p and q in LDS for a node's later
+  // residual passes when that fits and leaves the grid resident.
+  size_t lds = sv::walk_lds_bytes(a.node_cap, a.tile_cap);
+  a.cache = 0;
+  if (mode == sv::kWalkTree) {
+    const size_t with = sv::walk_lds_bytes(a.node_cap, a.tile_cap, true);
+    if (with <= static_cast<size_t>(max_lds_per_block()) &&
+        static_cast<int64_t>(a.B) * a.G <=
+            static_cast<int64_t>(sv::walk_occupancy(mode, t_dtype, q_dtype, with)) * std::max(cu_count(), 1)) {
+      a.cache = 1;
+      lds = with;
+    }
+  }
   time_next_kernel();
   const hipError_t e = sv::launch_walk(mode, t_dtype, q_dtype, a, lds, clear_slots, st);
   return e == hipSuccess ? SV_OK : device_fail(e, what);

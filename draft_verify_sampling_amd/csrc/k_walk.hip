@@ -20,7 +20,7 @@
 // Statistics: the walk computes the statistics of a node when it arrives there
 // (one pass over that row), so only the rows of its kept path are read.
 //
-// Work split: G workgroups of 1024 threads per request, G chosen by the host
+// Work split: G workgroups of 512 threads per request, G chosen by the host
 // from the occupancy of this kernel so that the whole grid is resident at
 // once (G = resident workgroups / requests, at most 32).  Workgroup g owns a
 // contiguous slice of the vocabulary's 2048-element tiles; each pass (softmax
@@ -69,7 +69,7 @@ struct Walk {
 // Publish (w0, w1) and collect every workgroup's pair into the LDS words
 // [2h], [2h + 1] of the current buffer.  Returns false when the bounded wait
 // expired.  Ends with a block barrier.
-__device__ bool exchange(Walk& wk, uint64_t w0, uint64_t w1) {
+__device__ __forceinline__ bool exchange(Walk& wk, uint64_t w0, uint64_t w1) {
   const WalkArgs& a = *wk.a;
   const int lane = threadIdx.x & (kWave - 1);
   const int buf = wk.nsync & 1;
@@ -125,7 +125,7 @@ __device__ __forceinline__ const uint64_t* last_words(const Walk& wk) {
 
 // Softmax pair of a target row over the slice, combined across the request.
 template <class DT>
-__device__ bool row_stats(Walk& wk, const void* trow, MS* s_wms, MS& out) {
+__device__ __forceinline__ bool row_stats(Walk& wk, const void* trow, MS* s_wms, MS& out) {
   const WalkArgs& a = *wk.a;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   MS acc{-INFINITY, 0.f};
@@ -146,20 +146,41 @@ __device__ bool row_stats(Walk& wk, const void* trow, MS* s_wms, MS& out) {
   return true;
 }
 
+// How a residual weight pass of the sampled tree walk uses the LDS copy of
+// its slice's draw inputs: not at all, filling it (the node's first residual
+// pass), or reading it instead of the rows (the node's later passes).
+constexpr int kCacheNone = 0, kCacheFill = 1, kCacheUse = 2;
+
 // One weight pass over the slice: per-tile weight sums into wt[] (slice-local
 // index); then, across the request, the total W and the NaN-ness of the draft
 // row's sum.  Every slice's total stays readable in the exchanged words until
-// the next exchange.
-template <class DT, class DQ, bool kQ = true>
-__device__ bool weight_pass(Walk& wk, const DrawRow& r, double* wt, double* s_wq, double& W, bool& qnan) {
+// the next exchange.  With kCacheFill / kCacheUse, `cache` is the slice's LDS
+// copy (tile i: p, then q) and *qcls the draft-sum class word of this
+// workgroup's slice, stored by the fill and sent again by later passes (the
+// draft row is the same, so is its class).
+template <class DT, class DQ, bool kQ = true, int kCache = kCacheNone>
+__device__ __forceinline__ bool weight_pass(Walk& wk, const DrawRow& r, double* wt, double* s_wq, double& W, bool& qnan,
+                                            float4* cache = nullptr, uint64_t* qcls = nullptr) {
   const WalkArgs& a = *wk.a;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  using TC = TileCache<DT, DQ>;
   double qw = 0.0;
   for (int t = wk.lo + wid; t < wk.hi; t += kWalkWaves) {
-    double v[1][3];
-    wave_tile_sums<DT, DQ, 1, kQ>(r, a.V, t, 0, v);
-    if (lane == 0) wt[t - wk.lo] = v[0][0];
-    qw += v[0][2];
+    const int i = t - wk.lo;
+    TC tc;
+    if constexpr (kCache != kCacheNone) {
+      tc.p = cache + static_cast<int64_t>(2 * i) * TC::kFloat4;
+      tc.q = tc.p + TC::kFloat4;
+    }
+    if constexpr (kCache == kCacheUse) {
+      const double s = wave_tile_wsum_cached<DT, DQ>(tc, r.coef);
+      if (lane == 0) wt[i] = s;
+    } else {
+      double v[1][3];
+      wave_tile_sums<DT, DQ, 1, kQ, 0, kCache == kCacheFill>(r, a.V, t, 0, v, tc);
+      if (lane == 0) wt[i] = v[0][0];
+      qw += v[0][2];
+    }
   }
   if (lane == 0) s_wq[wid] = qw;
   __syncthreads();
@@ -168,9 +189,16 @@ __device__ bool weight_pass(Walk& wk, const DrawRow& r, double* wt, double* s_wq
   double w = 0.0;
   for (int i = ta; i < tb; ++i) w += wt[i];
   w = wave_total(w);
-  double q = s_wq[0];
-  for (int i = 1; i < kWalkWaves; ++i) q += s_wq[i];
-  if (!exchange(wk, enc_sum(w), enc_qclass(q))) return false;
+  uint64_t w1;
+  if constexpr (kCache == kCacheUse) {
+    w1 = *qcls;
+  } else {
+    double q = s_wq[0];
+    for (int i = 1; i < kWalkWaves; ++i) q += s_wq[i];
+    w1 = enc_qclass(q);
+    if constexpr (kCache == kCacheFill) *qcls = w1;
+  }
+  if (!exchange(wk, enc_sum(w), w1)) return false;
   const uint64_t* x = last_words(wk);
   double tot = 0.0;
   uint64_t cls = 0;
@@ -186,7 +214,7 @@ __device__ bool weight_pass(Walk& wk, const DrawRow& r, double* wt, double* s_wq
 // Argmax of a target row over the slice, combined across the request (the
 // largest value, the lowest id among equal values); nan: the row holds a NaN.
 template <class DT>
-__device__ bool row_argmax(Walk& wk, const void* trow, uint64_t* s_key, uint32_t* s_knan, int& amax,
+__device__ __forceinline__ bool row_argmax(Walk& wk, const void* trow, uint64_t* s_key, uint32_t* s_knan, int& amax,
                            bool& nan) {
   const WalkArgs& a = *wk.a;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
@@ -231,7 +259,7 @@ __device__ __forceinline__ int tile_owner(int t, int ntiles, int G) {
 
 // Outputs of an invalid request: every token and path slot -1, counts 0,
 // status bits.  Threads [first, first + stride, ...) write.
-__device__ void walk_invalid(const WalkArgs& a, int b, int bits, int first, int stride) {
+__device__ __forceinline__ void walk_invalid(const WalkArgs& a, int b, int bits, int first, int stride) {
   const int64_t o = static_cast<int64_t>(b) * a.N;
   for (int c = first; c < a.N; c += stride) {
     a.out_tok[o + c] = -1;
@@ -273,6 +301,9 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
   float* s_qx = s_px + a.node_cap;
   float* s_u = s_qx + a.node_cap;
   int32_t* s_ex = reinterpret_cast<int32_t*>(s_u + a.node_cap);  // point mass: ids removed at cur
+  // sampled tree walk: the LDS copy of the slice's p and q (16 KB per tile)
+  float4* s_cache = reinterpret_cast<float4*>(
+      smem + ((reinterpret_cast<unsigned char*>(s_ex + a.node_cap) - smem + 15) & ~static_cast<intptr_t>(15)));
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   // Workgroups are dealt to the 8 XCDs in turn (workgroup i to XCD i % 8), so
@@ -338,6 +369,8 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
   int n_ex = 0;            // point mass: ids removed from cur's distribution (s_ex)
   bool have_pass = false;  // point mass: cur's tile sums are in s_wt0, slice totals in s_tot
   double Wrest = 1.0;      // point mass: mass of cur's distribution left after the removals
+  bool cached = false;     // sampled: s_cache holds cur's p and q (from cur's first residual pass)
+  uint64_t own_qcls = 0;   // sampled: this slice's draft-sum class word from that pass
   while (true) {
     // children of cur (one bit mask per 64 nodes, index order), and the target
     // logit / draft probability at their tokens, in flight during the pass
@@ -473,7 +506,17 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
           ++npass;
           double W;
           bool qnan;
-          if (!weight_pass<DT, DQ>(wk, rr, nb ? s_wt1 : s_wt0, s_wq, W, qnan)) {
+          double* wt = nb ? s_wt1 : s_wt0;
+          bool passed;
+          if (a.cache == 0) {
+            passed = weight_pass<DT, DQ>(wk, rr, wt, s_wq, W, qnan);
+          } else if (!cached) {
+            passed = weight_pass<DT, DQ, true, kCacheFill>(wk, rr, wt, s_wq, W, qnan, s_cache, &own_qcls);
+            cached = true;
+          } else {
+            passed = weight_pass<DT, DQ, true, kCacheUse>(wk, rr, wt, s_wq, W, qnan, s_cache, &own_qcls);
+          }
+          if (!passed) {
             synced = false;
           } else if (qnan || !isfinite(W)) {
             ok = false;
@@ -501,6 +544,7 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
     n_ex = 0;
     have_pass = false;
     Wrest = 1.0;
+    cached = false;
   }
   if (!synced) {
     if (tid == 0) flag(a.status, kFlagSyncTimeout);
@@ -883,14 +927,17 @@ void launch_mode(int t_dtype, int q_dtype, const WalkArgs& a, size_t lds, bool c
 
 }  // namespace
 
-size_t walk_lds_bytes(int node_cap, int tile_cap) {
-  return static_cast<size_t>(tile_cap) * 2 * sizeof(double) + static_cast<size_t>(node_cap) * 7 * 4;
+size_t walk_lds_bytes(int node_cap, int tile_cap, bool with_cache) {
+  const size_t base = static_cast<size_t>(tile_cap) * 2 * sizeof(double) + static_cast<size_t>(node_cap) * 7 * 4;
+  if (!with_cache) return base;
+  return ((base + 15) & ~static_cast<size_t>(15)) + static_cast<size_t>(tile_cap) * 2 * kSampleTile * sizeof(float);
 }
 
 int walk_occupancy(int mode, int t_dtype, int q_dtype, size_t lds) {
   static std::mutex mu;
-  static int cache[4][2][2][9] = {};  // by mode, dtypes, lds bucket of 8 KB
-  const size_t bucket = std::min<size_t>(lds / 8192, 8);
+  // by mode, dtypes and LDS rounded up to 8 KB (up to 168 KB); n + 1 once known
+  static int cache[4][2][2][21] = {};
+  const size_t bucket = std::min<size_t>((lds + 8191) / 8192, 21) - (lds == 0 ? 0 : 1);
   const size_t lds_key = (bucket + 1) * 8192;
   const int m = mode < 0 || mode > 3 ? 0 : mode;
   std::lock_guard<std::mutex> lock(mu);
@@ -899,10 +946,10 @@ int walk_occupancy(int mode, int t_dtype, int q_dtype, size_t lds) {
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, pick_walk(m, t_dtype, q_dtype), kWalkBlock,
                                                      lds_key) != hipSuccess)
-      n = 1;
-    slot = n < 1 ? 1 : n;
+      n = 0;
+    slot = (n < 0 ? 0 : n) + 1;
   }
-  return slot;
+  return slot - 1;
 }
 
 hipError_t launch_chain_diag(int t_dtype, int q_dtype, const WalkArgs& a, hipStream_t stream) {

@@ -69,7 +69,7 @@ constexpr int64_t kMaxSampleVocab = 4194304;   // 2048 tiles: their sums fit in 
 
 // The tree walk: G workgroups of kWalkBlock threads per request, each owning
 // a slice of the tiles, exchanging 64-bit words.
-constexpr int kWalkBlock = 1024;
+constexpr int kWalkBlock = 512;
 constexpr int kMaxWalkGroups = 32;
 constexpr int64_t kMaxCoopBlocks = 2048;       // B * G never exceeds this
 constexpr int kSpinLimit = 1 << 20;            // polls of one exchange before giving up
@@ -270,9 +270,13 @@ struct WalkArgs {
   int32_t spin_limit;
   int32_t node_cap;         // LDS capacity in nodes (>= nodes of any request)
   int32_t tile_cap;         // LDS capacity in tiles (>= tiles of any slice)
+  int32_t cache;            // sampled tree walk: nonzero when LDS holds a copy of the slice's draw inputs
 };
 
-size_t walk_lds_bytes(int node_cap, int tile_cap);
+// Dynamic LDS of a walk workgroup; with_cache adds the sampled tree walk's
+// copy of its slice's p and q (16 KB per tile).
+size_t walk_lds_bytes(int node_cap, int tile_cap, bool with_cache = false);
+// Resident walk workgroups per CU at this much dynamic LDS (0: none fits).
 int walk_occupancy(int mode, int t_dtype, int q_dtype, size_t lds);
 // Launches a tree walk (and the diagnostics, when asked for).  clear_slots:
 // zero the exchange words first (not needed when the statistics kernel or the

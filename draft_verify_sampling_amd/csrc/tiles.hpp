@@ -79,14 +79,48 @@ struct TileRuns {
   static_assert(nt >= 1 && nq >= 1, "a run must cover whole vectors of both rows");
 };
 
+// An LDS copy of one tile's draw inputs under a residual pass: p (draw_p of
+// each element) and the draft probability q, as floats, laid out as the tile
+// sums visit them (run k, group j4 of four elements of the run, lane), so a
+// later residual pass over the same row pair rebuilds the same weights in the
+// same order, and so the same sums, without reading or exponentiating the
+// rows again.  Elements beyond the row's end hold p = q = 0, which adds zero.
+template <class DT, class DQ>
+struct TileCache {
+  using L = TileRuns<DT, DQ>;
+  static constexpr int kVec = L::kPer / 4;                  // float4 per run and lane
+  static constexpr int kFloat4 = L::kRuns * kVec * kWave;  // float4 per tile and array
+  static_assert(L::kPer % 4 == 0, "runs of whole float4");
+  float4* p = nullptr;
+  float4* q = nullptr;
+  __device__ __forceinline__ void put(int run, int lane, const float* pv, const float* qv) const {
+#pragma unroll
+    for (int j4 = 0; j4 < kVec; ++j4) {
+      const int i = (run * kVec + j4) * kWave + lane;
+      p[i] = make_float4(pv[4 * j4], pv[4 * j4 + 1], pv[4 * j4 + 2], pv[4 * j4 + 3]);
+      q[i] = make_float4(qv[4 * j4], qv[4 * j4 + 1], qv[4 * j4 + 2], qv[4 * j4 + 3]);
+    }
+  }
+  __device__ __forceinline__ void put_zero(int run, int lane) const {
+#pragma unroll
+    for (int j4 = 0; j4 < kVec; ++j4) {
+      const int i = (run * kVec + j4) * kWave + lane;
+      p[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      q[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
+};
+
 // Sums (w, p, q) of tile t, in fp32 within a lane and fp64 across lanes; valid
 // in every lane.  Handles any tile.  On 16-byte aligned rows every complete
 // run is one predicated vector load, all in flight at once (the row's last
 // partial tile costs one load round like any other); a run that the row's
 // end cuts (rows whose length is not a multiple of the vector width) and
 // unaligned rows take element loads.
-template <class DT, class DQ, bool kQ = true>
-__device__ __forceinline__ void wave_tile_sums_any(const DrawRow& r, int64_t V, int t, double* v) {
+// kFill: also leave the tile's p and q in `cache` (residual passes only).
+template <class DT, class DQ, bool kQ = true, bool kFill = false>
+__device__ __forceinline__ void wave_tile_sums_any(const DrawRow& r, int64_t V, int t, double* v,
+                                                   TileCache<DT, DQ> cache = {}) {
   using L = TileRuns<DT, DQ>;
   constexpr int kPer = L::kPer;
   const int lane = threadIdx.x & (kWave - 1);
@@ -141,6 +175,7 @@ __device__ __forceinline__ void wave_tile_sums_any(const DrawRow& r, int64_t V, 
         p[j] = draw_p(r, l[j]);
         w[j] = draw_w(r, p[j], q[j]);
       }
+      if constexpr (kFill) cache.put(k0 + kk, lane, p, q);
       ws += pairwise<kPer>(w);
       ps += pairwise<kPer>(p);
       qs += pairwise<kPer>(q);
@@ -164,10 +199,16 @@ __device__ __forceinline__ void wave_tile_sums_any(const DrawRow& r, int64_t V, 
         p[j] = draw_p(r, l[j]);
         w[j] = draw_w(r, p[j], q[j]);
       }
+      if constexpr (kFill) cache.put(k, lane, p, q);
       ws += pairwise<kPer>(w);
       ps += pairwise<kPer>(p);
       qs += pairwise<kPer>(q);
     }
+  }
+  if constexpr (kFill) {  // runs wholly beyond the row's end were skipped above
+#pragma unroll 1
+    for (int k = 0; k < L::kRuns; ++k)
+      if (t0 + static_cast<int64_t>(k * kWave + lane) * kPer >= V) cache.put_zero(k, lane);
   }
   v[0] = wave_total(static_cast<double>(ws));
   v[1] = wave_total(static_cast<double>(ps));
@@ -180,10 +221,12 @@ __device__ __forceinline__ void wave_tile_sums_any(const DrawRow& r, int64_t V, 
 // and the rows are 16-byte aligned.
 // kMaxBatch (0: up to 16 vectors) caps the runs whose loads are in flight
 // together, for callers that must keep registers low; the runs are summed in
-// the same order either way, so the sums are the same bits.
-template <class DT, class DQ, int kT, bool kQ = true, int kMaxBatch = 0>
+// the same order either way, so the sums are the same bits.  kFill (one tile):
+// also leave the tile's p and q in `cache`.
+template <class DT, class DQ, int kT, bool kQ = true, int kMaxBatch = 0, bool kFill = false>
 __device__ __forceinline__ void wave_tile_sums(const DrawRow& r, int64_t V, int t, int tstride,
-                                               double (*v)[3]) {
+                                               double (*v)[3], TileCache<DT, DQ> cache = {}) {
+  static_assert(!kFill || kT == 1, "the cache holds one tile");
   using L = TileRuns<DT, DQ>;
   constexpr int kPer = L::kPer;
   constexpr int kAll = kT * L::kRuns;                           // runs per lane in total
@@ -198,7 +241,7 @@ __device__ __forceinline__ void wave_tile_sums(const DrawRow& r, int64_t V, int 
                     (!use_q || aligned16<DQ>(r.q, 0));
   if (!fast) {
 #pragma unroll 1
-    for (int i = 0; i < kT; ++i) wave_tile_sums_any<DT, DQ, kQ>(r, V, t + i * tstride, v[i]);
+    for (int i = 0; i < kT; ++i) wave_tile_sums_any<DT, DQ, kQ, kFill>(r, V, t + i * tstride, v[i], cache);
     return;
   }
   float ws[kT], ps[kT], qs[kT];
@@ -238,6 +281,7 @@ __device__ __forceinline__ void wave_tile_sums(const DrawRow& r, int64_t V, int 
         p[j] = draw_p(r, l[j]);
         w[j] = draw_w(r, p[j], q[j]);
       }
+      if constexpr (kFill) cache.put(r0 + k, lane, p, q);
       ws[ti] += pairwise<kPer>(w);
       ps[ti] += pairwise<kPer>(p);
       qs[ti] += pairwise<kPer>(q);
@@ -249,6 +293,39 @@ __device__ __forceinline__ void wave_tile_sums(const DrawRow& r, int64_t V, int 
     v[i][1] = wave_total(static_cast<double>(ps[i]));
     v[i][2] = wave_total(static_cast<double>(qs[i]));
   }
+}
+
+// Weight sum of a tile from its LDS copy under the residual max(0, p - coef q):
+// the same weights summed in the same order as the pass that filled the copy,
+// so the same bits as wave_tile_sums would give; valid in every lane.
+template <class DT, class DQ>
+__device__ __forceinline__ double wave_tile_wsum_cached(const TileCache<DT, DQ>& c, float coef) {
+  using C = TileCache<DT, DQ>;
+  constexpr int kPer = C::L::kPer, kRuns = C::L::kRuns, kVec = C::kVec;
+  const int lane = threadIdx.x & (kWave - 1);
+  float4 pv[kRuns][kVec], qv[kRuns][kVec];
+#pragma unroll
+  for (int k = 0; k < kRuns; ++k) {
+#pragma unroll
+    for (int j4 = 0; j4 < kVec; ++j4) {
+      pv[k][j4] = c.p[(k * kVec + j4) * kWave + lane];
+      qv[k][j4] = c.q[(k * kVec + j4) * kWave + lane];
+    }
+  }
+  float ws = 0.f;
+#pragma unroll
+  for (int k = 0; k < kRuns; ++k) {
+    float w[kPer];
+#pragma unroll
+    for (int j4 = 0; j4 < kVec; ++j4) {
+      w[4 * j4] = fmaxf(fmaf(-coef, qv[k][j4].x, pv[k][j4].x), 0.f);
+      w[4 * j4 + 1] = fmaxf(fmaf(-coef, qv[k][j4].y, pv[k][j4].y), 0.f);
+      w[4 * j4 + 2] = fmaxf(fmaf(-coef, qv[k][j4].z, pv[k][j4].z), 0.f);
+      w[4 * j4 + 3] = fmaxf(fmaf(-coef, qv[k][j4].w, pv[k][j4].w), 0.f);
+    }
+    ws += pairwise<kPer>(w);
+  }
+  return wave_total(static_cast<double>(ws));
 }
 
 // Online-softmax pair (scaled domain, as in common.hpp) of tile t of a target
