@@ -15,7 +15,11 @@
 // rejections the current distribution is max(0, p - c_j q) / R_j with
 // c_0 = 0, R_0 = 1, c_{j+1} = c_j + R_j and R_{j+1} = sum max(0, p - c_{j+1} q),
 // so every rejection costs one pass over the node's two rows that yields
-// R_{j+1} and the per-tile sums the final inverse-CDF draw needs.
+// R_{j+1} and the per-tile sums the final inverse-CDF draw needs.  The
+// node's first such pass also leaves p and q of the workgroup's slice in LDS
+// (when the host finds room: 16 KB per tile), and its later passes read that
+// copy instead of the rows: the same weights in the same order, so the same
+// sums, without the loads or the exponentials.
 //
 // Statistics: the walk computes the statistics of a node when it arrives there
 // (one pass over that row), so only the rows of its kept path are read.
