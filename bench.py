@@ -402,7 +402,8 @@ def w_chain(W, args, torch, sv, synth, dev):
     P = dict(t_kind=ci0.t_kind, q_kind=ci0.q_kind, V=ci0.V, k_max=k_max, T=ci0.T)
     graphs = _capture(calls, torch) if args.graph else None
     w = dict(step=_call_step(calls, graphs), arm_call=0, B=B, unit="rounds/s", cfg=cfg,
-             dtype="f32", formula=int(np.mean([formula(c) for c in sets])), out=out, nsets=len(sets),
+             dtype="f32", formula=int(np.mean([formula(c) for c in sets])) if W in ("c3", "c3p") else None,
+             out=out, nsets=len(sets),
              roofline_bytes=None if W == "c1" else roofline_bytes, cpu=("chain", A, P, B), kind="chain")
     if W == "c1":
         # one request's call alone: the latency a caller waits for at B=1
@@ -462,7 +463,7 @@ def w_tree(W, args, torch, sv, synth, dev):
 
     A = dict(target=ti.target, draft=ti.draft, parent=ti.parent, token=ti.token, u=ti.uniforms)
     return dict(step=_call_step(calls), arm_call=0, B=B, unit="rounds/s", cfg=cfg,
-                dtype="bf16 compares" if W == "c5g" else "f32", formula=2 * B * N * V * 2 + 2 * 4 * B * N,
+                dtype="bf16 compares" if W == "c5g" else "f32", formula=None,
                 out=out, nsets=1, roofline_bytes=walk_bytes, cpu=(kind, A, dict(N=N, V=V, T=ti.T), B), kind=kind)
 
 
@@ -727,8 +728,12 @@ def main():
                                          p10=round(float(np.percentile(ev_ms, 10)), 5),
                                          p50=round(float(np.percentile(ev_ms, 50)), 5),
                                          p90=round(float(np.percentile(ev_ms, 90)), 5)),
-                  settle_steps=n_settle, formula_bytes_per_step=fb, formula_GBps=round(fb / (ms * 1e-3) / 1e9, 1),
-                  formula_frac_of_peak=round(fb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4))
+                  settle_steps=n_settle)
+    if fb is not None:
+        # bytes the step's inputs occupy when every row is read once (the
+        # lazy and tree workloads read fewer, so they carry only the roofline)
+        result.update(formula_bytes_per_step=fb, formula_GBps=round(fb / (ms * 1e-3) / 1e9, 1),
+                      formula_frac_of_peak=round(fb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4))
     if W == "c1":
         # cache-resident by construction (every round reads the same 9 rows):
         # one wave per round, bound by its dependent steps; the one-wave

@@ -84,7 +84,6 @@ uint64_t next_ticket() {
   return t;
 }
 
-// Compute units of the current device (cached per device; 0 if unknown).
 // A device attribute of the current device, cached per device (0 on error).
 int device_attr(hipDeviceAttribute_t attr, std::atomic<int>* cache) {
   int dev = 0;
@@ -98,6 +97,7 @@ int device_attr(hipDeviceAttribute_t attr, std::atomic<int>* cache) {
   return n;
 }
 
+// Compute units of the current device (0 if unknown).
 int cu_count() {
   static std::atomic<int> cache[64];
   return device_attr(hipDeviceAttributeMultiprocessorCount, cache);
