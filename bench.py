@@ -61,7 +61,7 @@ MAX_POOL = 16  # the host cores one GPU's share of the machine has
 TIMING = ("inside {n} steps like the timed ones: HIP events handed to the kernel's launch on the step's stream "
           "(the kernel's own start and end)")
 CSRC = os.path.join(ROOT, "draft_verify_sampling_amd", "csrc")
-COMMON_SRCS = ["common.hpp", "words.hpp", "launch.hpp", "tiles.hpp", "segment.hpp"]
+COMMON_SRCS = ["common.hpp", "words.hpp", "launch.hpp", "tiles.hpp", "segment.hpp", "timeline.hpp"]
 # the sources a kernel is compiled from: its counter summary holds while
 # their code is unchanged
 KERNEL_SRCS = {
@@ -573,6 +573,242 @@ def w_tree_build(W, args, torch, sv, synth, dev):
                 cpu=("tree_build", A, dict(rounds=depth, exp=exp, top=top, N=N), B), kind="tree_build")
 
 
+# ---------------------------------------------------------------------------
+# in-kernel time lines (the timestamped copy of the library)
+# ---------------------------------------------------------------------------
+TL_TICK_US = 0.01  # the real-time counter runs at 100 MHz
+
+
+def _tl_read(lib, name, n=16384, slots=64):
+    """Records [n, slots] of one time-line array (0: point not reached)."""
+    import ctypes
+    buf = (ctypes.c_ulonglong * (n * slots))()
+    rc = getattr(lib, name + "_read")(buf, ctypes.c_int64(n))
+    if rc != 0:
+        raise RuntimeError(f"{name}_read failed ({rc})")
+    return np.frombuffer(buf, dtype=np.uint64).reshape(n, slots).astype(np.int64)
+
+
+def _stats(x):
+    x = np.asarray([v for v in x if np.isfinite(v)], dtype=np.float64)
+    if x.size == 0:
+        return None
+    return dict(n=int(x.size), mean=round(float(x.mean()), 2), p50=round(float(np.percentile(x, 50)), 2),
+                p90=round(float(np.percentile(x, 90)), 2), max=round(float(x.max()), 2))
+
+
+def timeline_walk(A, B):
+    """Phases of the sampled tree walk's exchanges from its records (us)."""
+    n = int((A[:, 0] > 0).sum())
+    G = n // B
+    R = A[:B * G].reshape(B, G, 64).astype(np.float64)
+    R[R <= 0] = np.nan
+    t0 = np.nanmin(R[:, :, 0])
+    R = (R - t0) * TL_TICK_US
+    ph = {k: [] for k in ("pass", "fold_waves", "exchange", "barrier", "fold_words", "decide")}
+    rounds, ends = [], []
+    for b in range(B):
+        nx = 0
+        while nx < 9 and np.isfinite(R[b, :, 2 + 6 * nx + 5]).all():
+            nx += 1
+        rounds.append(nx)
+        ends.append(np.nanmax(R[b, :, 63]))
+        for x in range(nx):
+            s = 2 + 6 * x
+            ph["pass"].append(np.nanmax(R[b, :, s + 1] - R[b, :, s]))
+            ph["fold_waves"].append(np.nanmax(R[b, :, s + 2] - R[b, :, s + 1]))
+            ph["exchange"].append(np.nanmax(R[b, :, s + 3]) - np.nanmax(R[b, :, s + 2]))
+            ph["barrier"].append(np.nanmax(R[b, :, s + 4] - R[b, :, s + 3]))
+            ph["fold_words"].append(np.nanmax(R[b, :, s + 5] - R[b, :, s + 4]))
+            if x + 1 < nx:
+                ph["decide"].append(np.nanmax(R[b, :, s + 6] - R[b, :, s + 5]))
+    slow = int(np.nanargmax(ends))
+    path = []
+    for x in range(rounds[slow]):
+        s = 2 + 6 * x
+        path.append(dict(start=round(float(np.nanmin(R[slow, :, s])), 2),
+                         pass_us=round(float(np.nanmax(R[slow, :, s + 1] - R[slow, :, s])), 2),
+                         words_seen=round(float(np.nanmax(R[slow, :, s + 3])), 2)))
+    return dict(requests=B, workgroups_per_request=G, span_us=round(float(np.nanmax(ends)), 2),
+                prologue_us=_stats(np.nanmax(R[:, :, 1], axis=1)),
+                rounds=dict(mean=round(float(np.mean(rounds)), 2), max=int(max(rounds))),
+                phases_us={k: _stats(v) for k, v in ph.items()},
+                last_draw_us=dict(after_last_exchange=_stats([np.nanmax(R[b, :, 63]) - np.nanmax(
+                    R[b, :, 2 + 6 * (rounds[b] - 1) + 5]) for b in range(B) if rounds[b] > 0]),
+                    tile_search=_stats(np.nanmax(R[:, :, 62] - R[:, :, 61], axis=1)),
+                    pick_and_write=_stats(np.nanmax(R[:, :, 63] - R[:, :, 62], axis=1))),
+                slowest_request=dict(index=slow, end_us=round(float(ends[slow]), 2), exchanges=path))
+
+
+def _tl_draw(D, t0):
+    """The draw's phases from its records (us from t0)."""
+    d0 = D[:, 0][D[:, 0] > 0].min()
+    D = D.astype(np.float64)
+    D[D < d0] = np.nan  # unreached points, and stamps of earlier steps' last blocks
+    D = (D - t0) * TL_TICK_US
+    last = np.isfinite(D[:, 7])
+    return dict(first_start=round(float(np.nanmin(D[:, 0])), 2),
+                last_end=round(float(np.nanmax(D[:, 7])), 2),
+                break_row_us=_stats(D[:, 1] - D[:, 0]), tiles_us=_stats(D[:, 2] - D[:, 1]),
+                count_us=_stats(D[:, 3] - D[:, 2]), tiles_done_at=_stats(D[:, 2]),
+                last_block=dict(gather_us=_stats(D[last, 4] - D[last, 3]),
+                                find_tile_us=_stats(D[last, 5] - D[last, 4]),
+                                pick_us=_stats(D[last, 6] - D[last, 5]),
+                                write_us=_stats(D[last, 7] - D[last, 6]),
+                                end_at=_stats(D[last, 7])))
+
+
+def timeline_chain(S, D, n_stats, n_draw):
+    """Phases of the headline step (statistics, then the draw) from the
+    records of both kernels (us)."""
+    S = S[:n_stats].astype(np.float64)
+    t0 = S[:, 0][S[:, 0] > 0].min()
+    S[S <= 0] = np.nan
+    S = (S - t0) * TL_TICK_US
+    return dict(stats_blocks=n_stats, draw_blocks=n_draw,
+                stats=dict(first_start=round(float(np.nanmin(S[:, 0])), 2),
+                           last_start=round(float(np.nanmax(S[:, 0])), 2),
+                           last_end=round(float(np.nanmax(S[:, 1])), 2), block_us=_stats(S[:, 1] - S[:, 0])),
+                draw=_tl_draw(D[:n_draw], t0))
+
+
+def timeline_ragged(L, D, rows, per_row, n_draw):
+    """Phases of the ragged step (lazy statistics, then the draw) from the
+    records of both kernels (us), row by row of the statistics grid."""
+    L = L[:rows * per_row].astype(np.float64)
+    t0 = L[:, 0][L[:, 0] > 0].min()
+    L[L <= 0] = np.nan
+    L = (L - t0) * TL_TICK_US
+    out = []
+    for i in range(rows):
+        r = L[i * per_row:(i + 1) * per_row]
+        live = np.isfinite(r[:, 1])
+        out.append(dict(row=i, blocks=per_row, loaded=int(live.sum()),
+                        start_first=round(float(np.nanmin(r[:, 0])), 2),
+                        start_last=round(float(np.nanmax(r[:, 0])), 2),
+                        loaded_end_last=round(float(np.nanmax(r[live, 2])), 2) if live.any() else None,
+                        decided=int(np.isfinite(r[:, 3]).sum())))
+    dead = ~np.isfinite(L[:, 1])
+    return dict(stats_blocks=rows * per_row, draw_blocks=n_draw,
+                stats=dict(last_start=round(float(np.nanmax(L[:, 0])), 2),
+                           last_stamp=round(float(np.nanmax(L)), 2),
+                           blocks_not_loading=int(dead.sum()), rows=out),
+                draw=_tl_draw(D[:n_draw], t0))
+
+
+def run_timeline(kind, args, torch, sv, synth, dev):
+    """The time line of one step (the last of 20 back-to-back steps after the
+    settle phase) of the sampled tree walk (kind "walk", the C5 trees), the
+    headline chain ("chain") or the ragged chain ("ragged"), from the
+    timestamped library."""
+    W = {"walk": "c5", "chain": "c3", "ragged": "c4"}[kind]
+    w = WORKLOADS[W](W, args, torch, sv, synth, dev)
+    step = w["step"]
+    settle(step, args.settle_seconds, torch)
+    lib = sv.load()
+    names = {"walk": [("sv_timeline_walk", 16384, 64)],
+             "chain": [("sv_timeline_stats", 16384, 64), ("sv_timeline_draw", 16384, 64)],
+             "ragged": [("sv_timeline_lazy", 65536, 4), ("sv_timeline_draw", 16384, 64)]}[kind]
+    for i in range(19):
+        step(i)
+    torch.cuda.synchronize()
+    # records are overwritten in place, and a block that stops early in one
+    # step keeps an earlier step's later readings: clear just before the last
+    for nm, _, _ in names:
+        if getattr(lib, nm + "_clear")() != 0:
+            raise RuntimeError(f"{nm}_clear failed")
+    step(19)
+    torch.cuda.synchronize()
+    recs = [_tl_read(lib, nm, n, slots) for nm, n, slots in names]
+    if kind == "walk":
+        out = timeline_walk(recs[0], w["B"])
+    elif kind == "chain":
+        n_stats = int((recs[0][:, 0] > 0).sum())
+        n_draw = int((recs[1][:, 0] > 0).sum())
+        out = timeline_chain(recs[0], recs[1], n_stats, n_draw)
+    else:
+        per_row = w["B"] * ((w["cfg"]["vocab"] + 8191) // 8192)  # every block stamps its start
+        rows = int((recs[0][:, 0] > 0).sum()) // per_row
+        out = timeline_ragged(recs[0], recs[1], rows, per_row, int((recs[1][:, 0] > 0).sum()))
+    return dict(timeline=kind, workload=W, step="the last of 20 steps after the settle phase (records cleared before it)",
+                unit="us from the first block's start", **out)
+
+
+TIMELINE_TITLES = {
+    "walk": "sampled tree walk, C5 trees (B=32, N=60, V=128,256 bf16, T=1)",
+    "chain": "headline sampled chain (B=64, k=4, V=248,320 bf16, T=0.7)",
+    "ragged": "ragged sampled chain, lazy statistics (B=256, k in 1..8, V=151,936 bf16, T=1)"}
+
+
+TIMELINE_LEGEND = {
+    "walk": [
+        "prologue_us: the tree and uniforms loaded, the exchange words zeroed, the ticket stored",
+        "rounds: exchanges per request (one per pass over the vocabulary)",
+        "phases_us (per request, the slowest of its workgroups, per exchange): pass = the pass over the "
+        "workgroup's slice (a node's statistics, or a residual pass from the rows or the LDS copy); "
+        "fold_waves = the waves' sums folded and the slice's words built; exchange = from the last "
+        "workgroup's store until every workgroup has seen all words; barrier = the exchange's barrier; "
+        "fold_words = the request's words folded; decide = the next child's test up to the next pass",
+        "last_draw_us: from the last exchange's fold to the outputs; tile_search = the drawing wave's "
+        "search for the tile; pick_and_write = the id picked from one re-read tile, and the writes",
+        "slowest_request.exchanges: each exchange's start, its pass and the time all words were seen"],
+    "chain": [
+        "stats: the all-rows statistics kernel; block_us = one block's life",
+        "draw.break_row_us: the break row and its pair known (two dependent load rounds, the rows' "
+        "combines); tiles_us: the block's tiles summed; count_us: its count returned; tiles_done_at: "
+        "when a block's tiles are done",
+        "draw.last_block (the request's last block): gather = the tile sums gathered; find_tile; pick = "
+        "the id picked from one re-read tile; write = the outputs written; end_at = when they are"],
+    "ragged": [
+        "stats: the lazy statistics kernel, row-major grid (all requests' row 0 first); blocks_not_loading "
+        "= blocks that left without streaming (row past the request's draft length, or its round stopped)",
+        "stats.rows: per row of the grid: its blocks, those that streamed their segment, the first and "
+        "last block starts, the last streaming block's word stored, and the requests whose row was decided",
+        "draw: as for the headline chain's draw (break row, tiles, count; the last block's gather, tile "
+        "search, pick and writes)"]}
+
+
+def timeline_markdown(d):
+    """The time line `d` (from run_timeline) as a markdown summary: every
+    distribution as median (mean, p90, max) over n, every row list as a
+    table."""
+    out = [f"# In-kernel time line: {TIMELINE_TITLES[d['timeline']]}", "",
+           "Commands (the timestamped copy of the library, then one step's records):", "",
+           "    python -m draft_verify_sampling_amd.build --timeline",
+           f"    python bench.py --timeline {d['timeline']} --markdown", "",
+           f"Step: {d['step']}.  Unit: {d['unit']} (100 MHz real-time counter, 0.01 us).  "
+           "Distributions: median (mean, p90, max) over n.", ""]
+    out += [f"- {x}" for x in TIMELINE_LEGEND[d["timeline"]]] + [""]
+
+    def dist(v):
+        return f"{v['p50']:.2f} (mean {v['mean']:.2f}, p90 {v['p90']:.2f}, max {v['max']:.2f}; n={v['n']})"
+
+    def walk(prefix, obj, rows):
+        for k, v in obj.items():
+            name = f"{prefix}{k}"
+            if isinstance(v, dict) and set(v) == {"n", "mean", "p50", "p90", "max"}:
+                rows.append((name, dist(v)))
+            elif isinstance(v, dict):
+                walk(name + ".", v, rows)
+            elif isinstance(v, list):
+                tables.append((name, v))
+            elif v is None:
+                rows.append((name, "-"))
+            else:
+                rows.append((name, str(v)))
+
+    rows, tables = [], []
+    walk("", {k: v for k, v in d.items() if k not in ("timeline", "step", "unit")}, rows)
+    out += ["| quantity | value |", "|---|---|"] + [f"| {a} | {b} |" for a, b in rows]
+    for name, lst in tables:
+        if not lst:
+            continue
+        keys = list(lst[0])
+        out += ["", f"{name}:", "", "| " + " | ".join(keys) + " |", "|" + "---|" * len(keys)]
+        out += ["| " + " | ".join("-" if r[k] is None else str(r[k]) for k in keys) + " |" for r in lst]
+    return "\n".join(out) + "\n"
+
+
 WORKLOADS = {"c1": w_chain, "c3": w_chain, "c3p": w_chain, "c4": w_chain, "c5": w_tree, "c5g": w_tree,
              "c5p": w_tree, "c2": w_greedy, "c3s": w_shard, "tb": w_tree_build}
 
@@ -665,6 +901,12 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="chain workloads: replay one captured HIP graph per step instead of launching the step's "
                          "kernels directly")
+    ap.add_argument("--timeline", choices=["walk", "chain", "ragged"],
+                    help="print the in-kernel time line of one step of the sampled tree walk (C5), the headline "
+                         "chain (C3) or the ragged chain (C4) instead of the bench line; needs the timestamped "
+                         "library (python -m draft_verify_sampling_amd.build --timeline)")
+    ap.add_argument("--markdown", action="store_true",
+                    help="with --timeline: print the time line as a markdown summary instead of JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run plain 256 MiB device-to-device copies (the counter calibration reference for "
                          "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
@@ -675,6 +917,11 @@ def main():
     if args.graph and args.workload not in ("c1", "c3", "c3p", "c4"):
         ap.error("--graph is for the chain workloads (c1, c3, c3p, c4)")
 
+    if args.timeline:
+        lib = os.path.join(ROOT, "draft_verify_sampling_amd", "libspecverify_timeline.so")
+        if not os.path.exists(lib):
+            ap.error("build the timestamped library first: python -m draft_verify_sampling_amd.build --timeline")
+        os.environ["SPECVERIFY_LIB"] = lib
     import torch
     import draft_verify_sampling_amd as sv
     import synth
@@ -693,6 +940,11 @@ def main():
     result = dict(metric=METRIC, n_gpus=1, steps=args.steps, warmup=args.warmup, higher_is_better=True,
                   scaling="weak", vs_baseline=None, data="synthetic")
     W = args.workload
+    if args.timeline:
+        tl = run_timeline(args.timeline, args, torch, sv, synth, dev)
+        print(timeline_markdown(tl) if args.markdown else json.dumps(tl), end="\n" if not args.markdown else "",
+              flush=True)
+        return
     if W == "ceiling":
         run_ceiling(args, torch, sv, dev, result)
         print(json.dumps(result), flush=True)

@@ -1,6 +1,6 @@
 """Build libspecverify.so (gfx950) in-tree with hipcc.
 
-    python -m draft_verify_sampling_amd.build [--sanitize]
+    python -m draft_verify_sampling_amd.build [--sanitize | --timeline]
 
 Every HIP translation unit is compiled with packed fp32 instructions turned
 off (``-Xclang -target-feature -Xclang -packed-fp32-ops``); hipcc's host pass
@@ -11,6 +11,11 @@ workspace carve-up, the launch set-up) carries AddressSanitizer and
 UndefinedBehaviorSanitizer checks, into _build/san/libspecverify.so; the
 device code is built as usual.  A process loads it with the sanitizer
 runtime preloaded (see sanitizer_env).
+
+--timeline builds a copy whose walk, statistics and draw kernels record
+in-kernel timestamps (csrc/timeline.hpp), into
+draft_verify_sampling_amd/libspecverify_timeline.so; `bench.py --timeline`
+loads it.  The normal library's kernels are the same code without them.
 """
 import os
 import shutil
@@ -24,6 +29,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libspecverify.so")
 SAN_LIB = os.path.join(ROOT, "_build", "san", "libspecverify.so")
+TIMELINE_LIB = os.path.join(HERE, "libspecverify_timeline.so")
 # host-side sanitizers only: each flag applies to the host compilation pass
 SAN_FLAGS = ["-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
              "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
@@ -41,16 +47,17 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False, out: str = None, sanitize: bool = False) -> str:
+def build(verbose: bool = False, out: str = None, sanitize: bool = False, timeline: bool = False) -> str:
     """Compile every source to an object under _build/ (_build/san/ for the
-    sanitized copy) and link the shared library; returns its path.  Always
-    recompiles."""
-    out = out or (SAN_LIB if sanitize else LIB)
-    bdir = os.path.join(ROOT, "_build", "san") if sanitize else os.path.join(ROOT, "_build")
+    sanitized copy, _build/timeline/ for the timestamped one) and link the
+    shared library; returns its path.  Always recompiles."""
+    out = out or (SAN_LIB if sanitize else TIMELINE_LIB if timeline else LIB)
+    sub = "san" if sanitize else "timeline" if timeline else ""
+    bdir = os.path.join(ROOT, "_build", sub) if sub else os.path.join(ROOT, "_build")
     os.makedirs(bdir, exist_ok=True)
     os.makedirs(os.path.dirname(out), exist_ok=True)
     cc = hipcc()
-    extra = SAN_FLAGS if sanitize else []
+    extra = SAN_FLAGS if sanitize else ["-DSV_TIMELINE"] if timeline else []
 
     def one(src):
         obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
@@ -96,4 +103,4 @@ def sanitizer_env(env: dict) -> dict:
 
 
 if __name__ == "__main__":
-    build(verbose=True, sanitize="--sanitize" in sys.argv[1:])
+    build(verbose=True, sanitize="--sanitize" in sys.argv[1:], timeline="--timeline" in sys.argv[1:])

@@ -35,7 +35,14 @@
 
 #include "launch.hpp"
 #include "tiles.hpp"
+#include "timeline.hpp"
 #include "words.hpp"
+
+// Time line of each draw block (builds with -DSV_TIMELINE only): record =
+// block index; slot 0 its start, 1 the break row known, 2 its tiles summed, 3
+// its count returned; the request's last block: 4 the tile sums gathered, 5
+// the tile found, 6 the id picked, 7 the outputs written.
+SV_TIMELINE_ARRAY(sv_timeline_draw)
 
 namespace sv {
 
@@ -148,6 +155,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_draw(ChainDrawArgs a) {
   const int b = static_cast<int>(blockIdx.x / a.nblk);
   const int r = static_cast<int>(blockIdx.x - static_cast<int64_t>(b) * a.nblk);
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  if (threadIdx.x == 0) SV_STAMP(sv_timeline_draw, blockIdx.x, 0);
   // the first wave's draft tokens and uniforms are loaded with the request's
   // row starts and draft count (they depend on b alone)
   int x0 = -1;
@@ -188,6 +196,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_draw(ChainDrawArgs a) {
     if (lane == 0) s_br = br;
   }
   __syncthreads();
+  if (threadIdx.x == 0) SV_STAMP(sv_timeline_draw, blockIdx.x, 1);
   const BreakRow br = s_br;
   if (br.bad) {
     if (r == 0 && wid == 0) draw_invalid(a, b, kFlagBadToken);
@@ -221,11 +230,13 @@ __global__ __launch_bounds__(kBlock) void k_chain_draw(ChainDrawArgs a) {
   if (lane == 0) s_q[wid] = enc_qclass(qsum);
   __syncthreads();
   if (threadIdx.x == 0) {
+    SV_STAMP(sv_timeline_draw, blockIdx.x, 2);
     uint64_t cls = 0;
     for (int w = 0; w < kDrawTiles; ++w) cls |= s_q[w];
     store_word(a.blk_q + static_cast<int64_t>(b) * a.nblk + r, cls);
     const uint32_t done = __hip_atomic_fetch_add(a.rcnt + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = done == static_cast<uint32_t>(a.nblk - 1);
+    SV_STAMP(sv_timeline_draw, blockIdx.x, 3);
   }
   __syncthreads();
   if (!s_last || wid != 0) return;
@@ -283,6 +294,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_draw(ChainDrawArgs a) {
     if (lane == 0) flag(a.status, kFlagSyncTimeout);
     return;
   }
+  if (lane == 0) SV_STAMP(sv_timeline_draw, blockIdx.x, 4);
   for (int sft = 32; sft >= 1; sft >>= 1)
     cls |= static_cast<uint64_t>(__shfl_xor(static_cast<long long>(cls), sft));
   double W = wave_total(wsum);
@@ -311,7 +323,9 @@ __global__ __launch_bounds__(kBlock) void k_chain_draw(ChainDrawArgs a) {
     draw_invalid(a, b, kFlagNonfinite | bits);
     return;
   }
+  if (lane == 0) SV_STAMP(sv_timeline_draw, blockIdx.x, 5);
   const int y = wave_pick_in_tile<DT, DQ>(row, a.V, hit, target);
+  if (lane == 0) SV_STAMP(sv_timeline_draw, blockIdx.x, 6);
   // emission: drafts 0..m-1 then y, cut after the first end token and at the
   // budget (lane c of this wave holds draft c from the start, c < 64)
   const int width = a.k_max + 1;
@@ -338,6 +352,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_draw(ChainDrawArgs a) {
     a.out_acc[b] = m;
     if (a.resid != nullptr) a.resid[b] = static_cast<float>(W);
     flag(a.status, bits);
+    SV_STAMP(sv_timeline_draw, blockIdx.x, 7);
   }
 }
 

@@ -24,7 +24,16 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "segment.hpp"
+#include "timeline.hpp"
 #include "words.hpp"
+
+// Time lines (builds with -DSV_TIMELINE only), record = block index.
+// k_row_stats: slot 0 the block's start, 1 its pair written.
+// k_chain_stats: slot 0 the block's start, 1 it is to load its segment (a
+// block of a row that is not needed has slot 0 only), 2 its word stored and
+// its count returned, 3 the row decided (the row's last block).
+SV_TIMELINE_ARRAY(sv_timeline_stats)
+SV_TIMELINE_ARRAY_SIZED(sv_timeline_lazy, 65536, 4)
 
 namespace sv {
 
@@ -40,10 +49,14 @@ __global__ __launch_bounds__(kBlock) void k_row_stats(const void* __restrict__ r
        i += static_cast<int64_t>(gridDim.x) * kBlock)
     clear[i] = uint4{0u, 0u, 0u, 0u};
   __shared__ float sh[2 * (kBlock / kWave)];
+  if (threadIdx.x == 0) SV_STAMP(sv_timeline_stats, blockIdx.x, 0);
   const int64_t row = blockIdx.x / nseg;
   const int32_t seg = blockIdx.x - static_cast<int32_t>(row) * nseg;
   const MS t = segment_ms<D, NT>(row_ptr<D>(rows, row, V), V, seg, nseg, c, sh);
-  if (threadIdx.x == 0) partial[blockIdx.x] = make_float2(t.m, t.s);
+  if (threadIdx.x == 0) {
+    partial[blockIdx.x] = make_float2(t.m, t.s);
+    SV_STAMP(sv_timeline_stats, blockIdx.x, 1);
+  }
 }
 
 hipError_t launch_row_stats(int dtype, const void* rows, int64_t n_rows, int64_t V, int32_t nseg,
@@ -111,6 +124,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
   const int seg = static_cast<int>(rem - static_cast<int64_t>(b) * a.nseg);
   const int R = a.k_max + 1;
   uint32_t* stop = a.stop + b;
+  if (threadIdx.x == 0) SV_STAMP(sv_timeline_lazy, blockIdx.x, 0);
   // one round: the request's metadata and, past row 0, whether its round has
   // already stopped at an earlier row
   const int k = a.dlen[b];
@@ -124,6 +138,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
   // happens only once an earlier row has stopped the round, so row i's pair
   // and decision are never used (the stop word keeps the earliest row).
   if (sv > static_cast<uint32_t>(kMaxChainRows - i)) return;
+  if (threadIdx.x == 0) SV_STAMP(sv_timeline_lazy, blockIdx.x, 1);
 
   // thread 0 fetches what the decision needs together with the segment
   int x = -1;
@@ -145,6 +160,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
     const uint32_t done = __hip_atomic_fetch_add(a.count + static_cast<int64_t>(b) * R + i, 1u,
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_last = done == static_cast<uint32_t>(a.nseg - 1);
+    SV_STAMP(sv_timeline_lazy, blockIdx.x, 2);
   }
   __syncthreads();
   if (!s_last || threadIdx.x >= kWave) return;
@@ -192,6 +208,7 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
   if (stop_here)
     __hip_atomic_fetch_max(stop, static_cast<uint32_t>(kMaxChainRows - i), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+  SV_STAMP(sv_timeline_lazy, blockIdx.x, 3);
 }
 
 hipError_t launch_chain_stats(int t_dtype, int q_dtype, const ChainStatsArgs& a, hipStream_t stream) {

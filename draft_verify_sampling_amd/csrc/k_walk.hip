@@ -49,7 +49,31 @@
 #include <mutex>
 
 #include "tiles.hpp"
+#include "timeline.hpp"
 #include "words.hpp"
+
+// Time line of each workgroup (builds with -DSV_TIMELINE only): record
+// b * G + g; slot 0 the start, 1 the end of the prologue; for exchange n < 9
+// the slots 2 + 6 n + (0 the pass starts, 1 its tile sums are in LDS, 2 the
+// exchange starts, 3 wave 0 has seen every word, 4 the exchange's barrier is
+// passed, 5 the words are folded); 60 the slice of the last draw is known, 61
+// the drawing wave starts, 62 its tile is found, 63 the outputs are written.
+// The readings go to LDS first and to the record at the workgroup's end.
+SV_TIMELINE_ARRAY(sv_timeline_walk)
+#ifdef SV_TIMELINE
+__shared__ uint64_t sv_walk_tl[sv::kTimelineSlots];
+#define WALK_TL(slot)                                                                 \
+  do {                                                                                \
+    if (threadIdx.x == 0 && (slot) < 60) sv_walk_tl[(slot)] = sv::timeline_now();     \
+  } while (0)
+#define WALK_TL_DRAW(slot)                                                            \
+  do {                                                                                \
+    if ((threadIdx.x & 63) == 0) sv_walk_tl[(slot)] = sv::timeline_now();             \
+  } while (0)
+#else
+#define WALK_TL(slot) ((void)0)
+#define WALK_TL_DRAW(slot) ((void)0)
+#endif
 
 namespace sv {
 
@@ -78,6 +102,7 @@ __device__ __forceinline__ bool exchange(Walk& wk, uint64_t w0, uint64_t w1) {
   const int lane = threadIdx.x & (kWave - 1);
   const int buf = wk.nsync & 1;
   uint64_t* x = wk.s_x + buf * 2 * kMaxWalkGroups;
+  WALK_TL(2 + 6 * wk.nsync + 2);
   if (a.G == 1) {
     if (threadIdx.x == 0) {
       x[0] = w0;
@@ -116,10 +141,12 @@ __device__ __forceinline__ bool exchange(Walk& wk, uint64_t w0, uint64_t w1) {
       }
       if (lane < n) x[lane] = v;
       if (lane == 0) wk.s_ok[buf] = done;
+      WALK_TL(2 + 6 * wk.nsync + 3);
     }
   }
-  ++wk.nsync;
   __syncthreads();
+  WALK_TL(2 + 6 * wk.nsync + 4);
+  ++wk.nsync;
   return wk.s_ok[buf] != 0;
 }
 
@@ -133,6 +160,7 @@ __device__ __forceinline__ bool row_stats(Walk& wk, const void* trow, MS* s_wms,
   const WalkArgs& a = *wk.a;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   MS acc{-INFINITY, 0.f};
+  WALK_TL(2 + 6 * wk.nsync + 0);
   for (int t = wk.lo + wid; t < wk.hi; t += kWalkWaves) {
     MS v, unused;
     wave_tile_ms<DT, false>(trow, nullptr, a.V, a.c, t, v, unused);
@@ -140,6 +168,7 @@ __device__ __forceinline__ bool row_stats(Walk& wk, const void* trow, MS* s_wms,
   }
   if (lane == 0) s_wms[wid] = acc;
   __syncthreads();
+  WALK_TL(2 + 6 * wk.nsync + 1);
   MS r = s_wms[0];
   for (int w = 1; w < kWalkWaves; ++w) r = ms_combine(r, s_wms[w]);
   if (!exchange(wk, enc_ms(r), kValid)) return false;
@@ -147,6 +176,7 @@ __device__ __forceinline__ bool row_stats(Walk& wk, const void* trow, MS* s_wms,
   MS m = dec_ms(x[0]);
   for (int h = 1; h < a.G; ++h) m = ms_combine(m, dec_ms(x[2 * h]));
   out = m;
+  WALK_TL(2 + 6 * (wk.nsync - 1) + 5);
   return true;
 }
 
@@ -169,6 +199,7 @@ __device__ __forceinline__ bool weight_pass(Walk& wk, const DrawRow& r, double* 
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   using TC = TileCache<DT, DQ>;
   double qw = 0.0;
+  WALK_TL(2 + 6 * wk.nsync + 0);
   for (int t = wk.lo + wid; t < wk.hi; t += kWalkWaves) {
     const int i = t - wk.lo;
     TC tc;
@@ -188,6 +219,7 @@ __device__ __forceinline__ bool weight_pass(Walk& wk, const DrawRow& r, double* 
   }
   if (lane == 0) s_wq[wid] = qw;
   __syncthreads();
+  WALK_TL(2 + 6 * wk.nsync + 1);
   int ta, tb;
   lane_tiles(wk.hi - wk.lo, lane, ta, tb);
   double w = 0.0;
@@ -212,6 +244,7 @@ __device__ __forceinline__ bool weight_pass(Walk& wk, const DrawRow& r, double* 
   }
   W = tot;
   qnan = qclass_nan(cls);
+  WALK_TL(2 + 6 * (wk.nsync - 1) + 5);
   return true;
 }
 
@@ -223,6 +256,7 @@ __device__ __forceinline__ bool row_argmax(Walk& wk, const void* trow, uint64_t*
   const WalkArgs& a = *wk.a;
   const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
   ArgBest s{-INFINITY, 0x7fffffff, false};
+  WALK_TL(2 + 6 * wk.nsync + 0);
   for (int t = wk.lo + wid; t < wk.hi; t += kWalkWaves) lane_tile_argmax<DT>(trow, a.V, t, s);
   const uint64_t key =
       wave_max_u64((static_cast<uint64_t>(order_bits(s.v)) << 32) | static_cast<uint32_t>(~s.i));
@@ -232,6 +266,7 @@ __device__ __forceinline__ bool row_argmax(Walk& wk, const void* trow, uint64_t*
     s_knan[wid] = wnan ? 1u : 0u;
   }
   __syncthreads();
+  WALK_TL(2 + 6 * wk.nsync + 1);
   uint64_t k = s_key[0];
   uint32_t n = s_knan[0];
   for (int w = 1; w < kWalkWaves; ++w) {
@@ -250,6 +285,7 @@ __device__ __forceinline__ bool row_argmax(Walk& wk, const void* trow, uint64_t*
   }
   amax = static_cast<int>(~static_cast<uint32_t>(best));
   nan = any_nan;
+  WALK_TL(2 + 6 * (wk.nsync - 1) + 5);
   return true;
 }
 
@@ -325,6 +361,10 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
   wk.hi = static_cast<int>(static_cast<int64_t>(wk.g + 1) * a.ntiles / a.G);
   const int b = wk.b;
   const int64_t V = a.V;
+#ifdef SV_TIMELINE
+  if (tid < kTimelineSlots) sv_walk_tl[tid] = 0;
+#endif
+  WALK_TL(0);
 
   // ---- the request: its tree and uniforms ----
   const int N = a.N;                                     // nodes
@@ -355,6 +395,7 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
   if (a.arrive != nullptr) asm volatile("s_waitcnt vmcnt(0)");
   __syncthreads();
   if (a.arrive != nullptr && tid == 0) store_word(a.arrive + static_cast<int64_t>(b) * a.G + wk.g, a.ticket);
+  WALK_TL(1);
   if (const int bad = s_bad) {
     if (wk.g == 0) walk_invalid(a, b, (bad & kFlagBadTree) ? kFlagBadTree : bad, tid, kWalkBlock);
     return;
@@ -614,7 +655,17 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
       if (wk.g == 0) walk_invalid(a, b, kFlagNonfinite | fallback, tid, kWalkBlock);
       return;
     }
+#ifdef SV_TIMELINE
+    if (tid == 0) sv_walk_tl[60] = timeline_now();
+    if (wk.g != gs) {  // the other workgroups' records (the drawing wave writes its own below)
+      __syncthreads();
+      if (tid < kTimelineSlots && static_cast<int64_t>(b) * a.G + wk.g < kTimelineRecords)
+        sv_timeline_walk_records[(static_cast<int64_t>(b) * a.G + wk.g) * kTimelineSlots + tid] = sv_walk_tl[tid];
+      return;
+    }
+#endif
     if (wk.g != gs || wid != 0) return;
+    WALK_TL_DRAW(61);
     const double* wt = tiles_buf ? s_wt1 : s_wt0;
     const int nsl = wk.hi - wk.lo;
     int ta, tb;
@@ -628,8 +679,17 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
     }
     hit.tile += wk.lo;
     hit.base += base_s;
+    WALK_TL_DRAW(62);
     y = wave_pick_in_tile<DT, DQ, kPoint>(row, V, hit, target);
   } else {
+#ifdef SV_TIMELINE
+    if (wk.g != 0) {
+      __syncthreads();
+      if (tid < kTimelineSlots && static_cast<int64_t>(b) * a.G + wk.g < kTimelineRecords)
+        sv_timeline_walk_records[(static_cast<int64_t>(b) * a.G + wk.g) * kTimelineSlots + tid] = sv_walk_tl[tid];
+      return;
+    }
+#endif
     if (wk.g != 0 || wid != 0) return;
   }
   const int64_t o = static_cast<int64_t>(b) * N;
@@ -642,6 +702,11 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
     a.out_acc[b] = n_emit;
     flag(a.status, fallback);
   }
+#ifdef SV_TIMELINE
+  WALK_TL_DRAW(63);
+  if (static_cast<int64_t>(b) * a.G + wk.g < kTimelineRecords)
+    sv_timeline_walk_records[(static_cast<int64_t>(b) * a.G + wk.g) * kTimelineSlots + lane] = sv_walk_tl[lane];
+#endif
 }
 
 // Chains whose vocabulary is one tile (V <= 2048): one wave per request does
