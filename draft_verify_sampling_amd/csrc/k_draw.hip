@@ -142,6 +142,102 @@ __device__ BreakRow break_from_partials(const ChainDrawArgs& a, int b, int k, in
   return br;
 }
 
+// The last block's wave 0: gathers the request's tile sums and block classes,
+// totals them (W, with the fallback to p when the residual has no mass) and
+// finds the tile holding u_k W.  Returns 0 when the request's outputs are
+// already written (invalid) or the gather timed out, else 1 (pick from the
+// residual) or 2 (from p), with the tile and the target in s_hit, s_target.
+template <class DT, class DQ>
+__device__ __forceinline__ int last_block_find(const ChainDrawArgs& a, int b, int k, int extra, float u0,
+                                               bool resid, double* s_tw, DrawRow& row, int& bits, double& W,
+                                               TileHit& s_hit, double& s_target) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const uint64_t* tw = a.tile_w + static_cast<int64_t>(b) * a.ntiles;
+  const uint64_t* tp = a.tile_p + static_cast<int64_t>(b) * a.ntiles;
+  const uint64_t* bq = a.blk_q + static_cast<int64_t>(b) * a.nblk;
+  int ta, tb;
+  lane_tiles(a.ntiles, lane, ta, tb);
+  constexpr int kBatch = 4;
+  double wsum = 0.0, psum = 0.0;
+  uint64_t cls = 0;
+  bool ok = true;
+  for (int t0 = ta, first = 1; ok && (t0 < tb || first); t0 += kBatch, first = 0) {
+    uint64_t vw[kBatch], vp[kBatch], vq = kValid;
+    int it = 0;
+    for (; it < a.spin_limit; ++it) {
+      bool mine = true;
+      if (first) {
+        for (int j = lane; j < a.nblk; j += kWave) {
+          const uint64_t v = load_word(bq + j);
+          mine = mine && (v & kValid) != 0;
+          vq = j == lane ? v : (vq | v);
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < kBatch; ++x) {
+        vw[x] = vp[x] = kValid;
+        if (t0 + x < tb) {
+          vw[x] = load_word(tw + t0 + x);
+          vp[x] = load_word(tp + t0 + x);
+        }
+        mine = mine && (vw[x] & kValid) && (vp[x] & kValid);
+      }
+      if (__all(mine)) break;
+      __builtin_amdgcn_s_sleep(1);
+    }
+    ok = it < a.spin_limit;
+    if (first) cls = lane < a.nblk ? vq : 0ull;
+#pragma unroll
+    for (int x = 0; x < kBatch; ++x) {
+      if (t0 + x < tb) {
+        const double dw = dec_sum(vw[x]), dp = dec_sum(vp[x]);
+        s_tw[t0 + x] = dw;
+        s_tw[a.ntiles + t0 + x] = dp;
+        wsum += dw;
+        psum += dp;
+      }
+    }
+  }
+  if (!__all(ok)) {
+    if (lane == 0) flag(a.status, kFlagSyncTimeout);
+    return 0;
+  }
+  if (lane == 0) SV_STAMP(sv_timeline_draw, blockIdx.x, 4);
+  for (int sft = 32; sft >= 1; sft >>= 1)
+    cls |= static_cast<uint64_t>(__shfl_xor(static_cast<long long>(cls), sft));
+  W = wave_total(wsum);
+  bits = extra;
+  const double* ts_w = s_tw;
+  double mine = wsum;
+  if (resid) {
+    if (qclass_nan(cls) || !isfinite(W)) {
+      draw_invalid(a, b, kFlagNonfinite | extra);
+      return 0;
+    }
+    if (!(W > 0.0)) {  // no residual mass: draw from p_m
+      bits |= kFlagFallback;
+      row.use_q = false;
+      W = wave_total(psum);
+      ts_w = s_tw + a.ntiles;
+      mine = psum;
+    }
+  }
+  // the last token's uniform: lane k of this wave loaded it at the start
+  const float uk = k < kWave ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u0), k))
+                             : slot_uniform(a.u, a.seed, a.offset, b, a.k_max + 1, k);
+  const double target = static_cast<double>(uk) * W;
+  TileHit hit;
+  if (!wave_find_tile(ts_w, 1, a.ntiles, mine, target, hit)) {
+    draw_invalid(a, b, kFlagNonfinite | bits);
+    return 0;
+  }
+  if (lane == 0) {
+    s_hit = hit;
+    s_target = target;
+    SV_STAMP(sv_timeline_draw, blockIdx.x, 5);
+  }
+  return row.use_q ? 1 : 2;
+}
 }  // namespace
 
 // Dynamic LDS: the gathered tile sums, 2 x ntiles doubles (w, then p).
@@ -239,92 +335,28 @@ __global__ __launch_bounds__(kBlock) void k_chain_draw(ChainDrawArgs a) {
     SV_STAMP(sv_timeline_draw, blockIdx.x, 3);
   }
   __syncthreads();
-  if (!s_last || wid != 0) return;
+  if (!s_last) return;
 
-  // 3. the request's last block: gather the tile sums and the classes of the
-  // draft row's block sums (loads in flight a batch at a time, waiting only
-  // for their visibility), total them, find the tile and the id.
-  const uint64_t* tw = a.tile_w + static_cast<int64_t>(b) * a.ntiles;
-  const uint64_t* tp = a.tile_p + static_cast<int64_t>(b) * a.ntiles;
-  const uint64_t* bq = a.blk_q + static_cast<int64_t>(b) * a.nblk;
-  int ta, tb;
-  lane_tiles(a.ntiles, lane, ta, tb);
-  constexpr int kBatch = 4;
-  double wsum = 0.0, psum = 0.0;
-  uint64_t cls = 0;
-  bool ok = true;
-  for (int t0 = ta, first = 1; ok && (t0 < tb || first); t0 += kBatch, first = 0) {
-    uint64_t vw[kBatch], vp[kBatch], vq = kValid;
-    int it = 0;
-    for (; it < a.spin_limit; ++it) {
-      bool mine = true;
-      if (first) {
-        for (int j = lane; j < a.nblk; j += kWave) {
-          const uint64_t v = load_word(bq + j);
-          mine = mine && (v & kValid) != 0;
-          vq = j == lane ? v : (vq | v);
-        }
-      }
-#pragma unroll
-      for (int x = 0; x < kBatch; ++x) {
-        vw[x] = vp[x] = kValid;
-        if (t0 + x < tb) {
-          vw[x] = load_word(tw + t0 + x);
-          vp[x] = load_word(tp + t0 + x);
-        }
-        mine = mine && (vw[x] & kValid) && (vp[x] & kValid);
-      }
-      if (__all(mine)) break;
-      __builtin_amdgcn_s_sleep(1);
-    }
-    ok = it < a.spin_limit;
-    if (first) cls = lane < a.nblk ? vq : 0ull;
-#pragma unroll
-    for (int x = 0; x < kBatch; ++x) {
-      if (t0 + x < tb) {
-        const double dw = dec_sum(vw[x]), dp = dec_sum(vp[x]);
-        s_tw[t0 + x] = dw;
-        s_tw[a.ntiles + t0 + x] = dp;
-        wsum += dw;
-        psum += dp;
-      }
-    }
-  }
-  if (!__all(ok)) {
-    if (lane == 0) flag(a.status, kFlagSyncTimeout);
-    return;
-  }
-  if (lane == 0) SV_STAMP(sv_timeline_draw, blockIdx.x, 4);
-  for (int sft = 32; sft >= 1; sft >>= 1)
-    cls |= static_cast<uint64_t>(__shfl_xor(static_cast<long long>(cls), sft));
-  double W = wave_total(wsum);
+  // 3. the request's last block: wave 0 gathers the tile sums and the classes
+  // of the draft row's block sums (loads in flight a batch at a time, waiting
+  // only for their visibility), totals them and finds the tile; the block's
+  // four waves then pick the id in it.
+  __shared__ PickLds s_pick;
+  __shared__ TileHit s_hit;
+  __shared__ double s_target;
+  __shared__ int s_go;  // 0: done (invalid), 1: pick from the residual, 2: from p
   int bits = extra;
-  const double* ts_w = s_tw;
-  double mine = wsum;
-  if (resid) {
-    if (qclass_nan(cls) || !isfinite(W)) {
-      draw_invalid(a, b, kFlagNonfinite | extra);
-      return;
-    }
-    if (!(W > 0.0)) {  // no residual mass: draw from p_m
-      bits |= kFlagFallback;
-      row.use_q = false;
-      W = wave_total(psum);
-      ts_w = s_tw + a.ntiles;
-      mine = psum;
-    }
+  double W = 0.0;
+  if (wid == 0) {
+    const int go = last_block_find<DT, DQ>(a, b, k, extra, u0, resid, s_tw, row, bits, W, s_hit, s_target);
+    if (lane == 0) s_go = go;
   }
-  // the last token's uniform: lane k of this wave loaded it at the start
-  const float uk = k < kWave ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u0), k))
-                             : slot_uniform(a.u, a.seed, a.offset, b, a.k_max + 1, k);
-  const double target = static_cast<double>(uk) * W;
-  TileHit hit;
-  if (!wave_find_tile(ts_w, 1, a.ntiles, mine, target, hit)) {
-    draw_invalid(a, b, kFlagNonfinite | bits);
-    return;
-  }
-  if (lane == 0) SV_STAMP(sv_timeline_draw, blockIdx.x, 5);
-  const int y = wave_pick_in_tile<DT, DQ>(row, a.V, hit, target);
+  __syncthreads();
+  const int go = s_go;
+  if (go == 0) return;
+  row.use_q = go == 1;
+  const int y = block_pick_in_tile<DT, DQ>(row, a.V, s_hit, s_target, s_pick);
+  if (wid != 0) return;
   if (lane == 0) SV_STAMP(sv_timeline_draw, blockIdx.x, 6);
   // emission: drafts 0..m-1 then y, cut after the first end token and at the
   // budget (lane c of this wave holds draft c from the start, c < 64)

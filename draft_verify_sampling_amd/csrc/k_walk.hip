@@ -47,6 +47,7 @@
 // scans the slice's tile sums (kept in LDS) and rescans the chosen tile.
 #include <algorithm>
 #include <mutex>
+#include <type_traits>
 
 #include "tiles.hpp"
 #include "timeline.hpp"
@@ -68,7 +69,7 @@ __shared__ uint64_t sv_walk_tl[sv::kTimelineSlots];
   } while (0)
 #define WALK_TL_DRAW(slot)                                                            \
   do {                                                                                \
-    if ((threadIdx.x & 63) == 0) sv_walk_tl[(slot)] = sv::timeline_now();             \
+    if (threadIdx.x == 0) sv_walk_tl[(slot)] = sv::timeline_now();                     \
   } while (0)
 #else
 #define WALK_TL(slot) ((void)0)
@@ -330,6 +331,9 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
   __shared__ double s_two[2];                            // point mass: one tile's sums
   __shared__ int s_ok[2];
   __shared__ int s_bad;
+  __shared__ std::conditional_t<kGreedy, char, PickLds> s_pick;  // the last draw's pick
+  __shared__ TileHit s_hit;
+  __shared__ int s_pick_go;
 
   // dynamic LDS: tile sums [2][tile_cap] doubles, then node arrays [node_cap]
   double* s_wt0 = reinterpret_cast<double*>(smem);
@@ -664,23 +668,31 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
       return;
     }
 #endif
-    if (wk.g != gs || wid != 0) return;
+    if (wk.g != gs) return;
+    // the owning workgroup: wave 0 finds the tile, waves 0..3 pick the id
     WALK_TL_DRAW(61);
-    const double* wt = tiles_buf ? s_wt1 : s_wt0;
-    const int nsl = wk.hi - wk.lo;
-    int ta, tb;
-    lane_tiles(nsl, lane, ta, tb);
-    double own = 0.0;
-    for (int i = ta; i < tb; ++i) own += wt[i];
-    TileHit hit;
-    if (!wave_find_tile(wt, 1, nsl, own, target - base_s, hit)) {
-      walk_invalid(a, b, kFlagNonfinite | fallback, lane, kWave);
-      return;
+    if (wid == 0) {
+      const double* wt = tiles_buf ? s_wt1 : s_wt0;
+      const int nsl = wk.hi - wk.lo;
+      int ta, tb;
+      lane_tiles(nsl, lane, ta, tb);
+      double own = 0.0;
+      for (int i = ta; i < tb; ++i) own += wt[i];
+      TileHit hit;
+      const bool found = wave_find_tile(wt, 1, nsl, own, target - base_s, hit);
+      if (!found) walk_invalid(a, b, kFlagNonfinite | fallback, lane, kWave);
+      hit.tile += wk.lo;
+      hit.base += base_s;
+      if (lane == 0) {
+        s_pick_go = found ? 1 : 0;
+        s_hit = hit;
+      }
     }
-    hit.tile += wk.lo;
-    hit.base += base_s;
+    __syncthreads();
+    if (!s_pick_go) return;
     WALK_TL_DRAW(62);
-    y = wave_pick_in_tile<DT, DQ, kPoint>(row, V, hit, target);
+    y = block_pick_in_tile<DT, DQ, kPoint>(row, V, s_hit, target, s_pick);
+    if (wid != 0) return;
   } else {
 #ifdef SV_TIMELINE
     if (wk.g != 0) {

@@ -471,28 +471,29 @@ __device__ __forceinline__ bool wave_find_tile(const double* ts, int stride, int
   return true;
 }
 
-// Bit i set: element e0 + i of the lane's 32 is one of the ids r.excl.
-__device__ __forceinline__ uint32_t lane_excl_mask(const DrawRow& r, int64_t e0) {
+// Bit i set: element e0 + i (i < kG) is one of the ids r.excl.
+template <int kG>
+__device__ __forceinline__ uint32_t run_excl_mask(const DrawRow& r, int64_t e0) {
+  static_assert(kG <= 32, "one bit per element");
   uint32_t m = 0;
   for (int x = 0; x < r.nexcl; ++x) {
     const int64_t off = static_cast<int64_t>(r.excl[x]) - e0;
-    if (off >= 0 && off < kSampleTile / kWave) m |= 1u << off;
+    if (off >= 0 && off < kG) m |= 1u << off;
   }
   return m;
 }
 
-// Weights of the 32 contiguous elements [32 l, 32 l + 32) of tile `tile` in
-// lane l, read in one round (16-byte vectors when aligned and complete);
-// elements past the row's end weigh 0, and with kExcl the ids in r.excl too.
-template <class DT, class DQ, bool kExcl = false>
-__device__ __forceinline__ void lane_tile_weights(const DrawRow& r, int64_t V, int tile,
-                                                  float (&wv)[kSampleTile / kWave]) {
-  constexpr int kLane = kSampleTile / kWave;  // 32
-  const int lane = threadIdx.x & (kWave - 1);
-  const int64_t e0 = static_cast<int64_t>(tile) * kSampleTile + lane * kLane;
-  constexpr int kTV = kLane / DT::kPerVec, kQV = kLane / DQ::kPerVec;
+// Weights of the kG contiguous elements [e0, e0 + kG) of the row (kG a
+// multiple of 8), read in one round (16-byte vectors when aligned and
+// complete); elements past the row's end weigh 0, and with kExcl the ids in
+// r.excl too.  Each weight depends on its element alone, so any split of a
+// tile into runs gives the same weights.
+template <class DT, class DQ, int kG, bool kExcl = false>
+__device__ __forceinline__ void run_weights(const DrawRow& r, int64_t V, int64_t e0, float (&wv)[kG]) {
+  static_assert(kG % 8 == 0, "whole 8-element groups");
+  constexpr int kTV = kG / DT::kPerVec, kQV = kG / DQ::kPerVec;
   uint4 tv[kTV], qv[kQV];
-  const bool fast = e0 + kLane <= V && aligned16<DT>(r.t, e0) && (!r.use_q || aligned16<DQ>(r.q, e0));
+  const bool fast = e0 + kG <= V && aligned16<DT>(r.t, e0) && (!r.use_q || aligned16<DQ>(r.q, e0));
   if (fast) {
 #pragma unroll
     for (int j = 0; j < kTV; ++j) tv[j] = ld16<DT>(r.t, e0 + j * DT::kPerVec);
@@ -502,7 +503,7 @@ __device__ __forceinline__ void lane_tile_weights(const DrawRow& r, int64_t V, i
     }
   }
 #pragma unroll
-  for (int g = 0; g < kLane / 8; ++g) {
+  for (int g = 0; g < kG / 8; ++g) {
     float l[8], q[8];
     if (fast) {
       if (DT::kPerVec == 8) {
@@ -535,9 +536,9 @@ __device__ __forceinline__ void lane_tile_weights(const DrawRow& r, int64_t V, i
     for (int j = 0; j < 8; ++j) wv[8 * g + j] = draw_w(r, draw_p(r, l[j]), q[j]);
   }
   if constexpr (kExcl) {
-    const uint32_t xm = lane_excl_mask(r, e0);
+    const uint32_t xm = run_excl_mask<kG>(r, e0);
 #pragma unroll
-    for (int i = 0; i < kLane; ++i) wv[i] = ((xm >> i) & 1u) ? 0.f : wv[i];
+    for (int i = 0; i < kG; ++i) wv[i] = ((xm >> i) & 1u) ? 0.f : wv[i];
   }
 }
 
@@ -582,29 +583,58 @@ __device__ __forceinline__ void lane_partial_excl(const DrawRow& r, int64_t V, i
   b = sb;
 }
 
-// The id inside tile h.tile: running weights in fp32 within a lane's 32
-// contiguous elements and fp64 across lanes.
+// The id inside tile h.tile.  Lane l of the tile's 64 lanes owns the 32
+// contiguous elements [32 l, 32 l + 32), in four groups of 8: g_j is the
+// pairwise fp32 sum of group j, the lane's weight (g_0 + g_1) + (g_2 + g_3)
+// (its pairwise sum of 32), and the lanes' running bases are an fp64 scan.
+// Inside group j the running weight starts from the fp32 sum of the groups
+// before it (0, g_0, g_0 + g_1, (g_0 + g_1) + g_2) and adds the group's
+// weights in order.  The id is the first element of positive weight where
+// that running weight exceeds target - base (in fp32), else (or when h
+// overshoots) the last element of positive weight.  wave_pick_in_tile does
+// it in one wave, block_pick_in_tile over four waves, with identical results.
+__device__ __forceinline__ float group_start(const float (&g)[4], int j) {
+  const float g01 = g[0] + g[1];
+  return j == 0 ? 0.f : (j == 1 ? g[0] : (j == 2 ? g01 : g01 + g[2]));
+}
+
+__device__ __forceinline__ void group_cross(const float* w, float start, float thr, bool overshoot, int idx0,
+                                            int& first, int& lastw) {
+  float lrun = start;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float wj = w[i];
+    if (wj > 0.f) {
+      if (first < 0 && !overshoot && lrun + wj > thr) first = idx0 + i;
+      lastw = idx0 + i;
+    }
+    lrun += wj;
+  }
+}
+
+// The lane's fp32 threshold: target minus the running weight of the lanes
+// before it.
+__device__ __forceinline__ float lane_threshold(const float (&g)[4], const TileHit& h, double target) {
+  const float lw = (g[0] + g[1]) + (g[2] + g[3]);
+  const double base = h.base + wave_exclusive_from_inclusive(wave_incl_scan(static_cast<double>(lw)));
+  return static_cast<float>(target - base);
+}
+
 template <class DT, class DQ, bool kExcl = false>
 __device__ __forceinline__ int wave_pick_in_tile(const DrawRow& r, int64_t V, const TileHit& h,
                                                  double target) {
   constexpr int kLane = kSampleTile / kWave;  // 32
+  static_assert(kLane == 32, "four groups of 8 per lane");
   const int lane = threadIdx.x & (kWave - 1);
   float wv[kLane];
-  lane_tile_weights<DT, DQ, kExcl>(r, V, h.tile, wv);
-  const double lane_base =
-      h.base + wave_exclusive_from_inclusive(wave_incl_scan(static_cast<double>(pairwise<kLane>(wv))));
-  const float thr = static_cast<float>(target - lane_base);  // crossing: running weight > thr
-  int first = -1, lastw = -1;
-  float lrun = 0.f;
+  run_weights<DT, DQ, kLane, kExcl>(r, V, static_cast<int64_t>(h.tile) * kSampleTile + lane * kLane, wv);
+  float g[4];
 #pragma unroll
-  for (int i = 0; i < kLane; ++i) {
-    const float wj = wv[i];
-    if (wj > 0.f) {
-      if (first < 0 && !h.overshoot && lrun + wj > thr) first = lane * kLane + i;
-      lastw = lane * kLane + i;
-    }
-    lrun += wj;
-  }
+  for (int j = 0; j < 4; ++j) g[j] = pairwise<8>(wv + 8 * j);
+  const float thr = lane_threshold(g, h, target);
+  int first = -1, lastw = -1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) group_cross(wv + 8 * j, group_start(g, j), thr, h.overshoot, lane * kLane + 8 * j, first, lastw);
   int pick;
   const uint64_t found = __ballot(first >= 0);
   if (found) {
@@ -613,6 +643,58 @@ __device__ __forceinline__ int wave_pick_in_tile(const DrawRow& r, int64_t V, co
     const uint64_t any = __ballot(lastw >= 0);
     pick = any ? __builtin_amdgcn_readlane(lastw, 63 - __clzll(static_cast<long long>(any))) : 0;
   }
+  return static_cast<int>(static_cast<int64_t>(h.tile) * kSampleTile + pick);
+}
+
+// LDS of block_pick_in_tile: the groups' sums and each wave's candidates.
+struct PickLds {
+  float g[4][kWave];
+  int first[4];
+  int last[4];
+};
+
+// wave_pick_in_tile over waves 0..3 of the block, wave j taking group j of
+// every lane's 32 elements (one 8-element run per thread).  Every thread of
+// the block calls it (it holds two block barriers; waves past 3 only wait)
+// with the same arguments; the id is returned in every thread.
+template <class DT, class DQ, bool kExcl = false>
+__device__ __forceinline__ int block_pick_in_tile(const DrawRow& r, int64_t V, const TileHit& h, double target,
+                                                  PickLds& s) {
+  const int lane = threadIdx.x & (kWave - 1), wid = static_cast<int>(threadIdx.x / kWave);
+  const bool act = wid < 4;
+  const int idx0 = lane * (kSampleTile / kWave) + 8 * wid;
+  float wv[8];
+  if (act) {
+    run_weights<DT, DQ, 8, kExcl>(r, V, static_cast<int64_t>(h.tile) * kSampleTile + idx0, wv);
+    s.g[wid][lane] = pairwise<8>(wv);
+  }
+  __syncthreads();
+  if (act) {
+    float g[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) g[j] = s.g[j][lane];
+    const float thr = lane_threshold(g, h, target);
+    int first = -1, lastw = -1;
+    group_cross(wv, group_start(g, wid), thr, h.overshoot, idx0, first, lastw);
+    const uint64_t found = __ballot(first >= 0), any = __ballot(lastw >= 0);
+    const int f = found ? __builtin_amdgcn_readlane(first, __ffsll(static_cast<long long>(found)) - 1) : -1;
+    const int l = any ? __builtin_amdgcn_readlane(lastw, 63 - __clzll(static_cast<long long>(any))) : -1;
+    if (lane == 0) {
+      s.first[wid] = f;
+      s.last[wid] = l;
+    }
+  }
+  __syncthreads();
+  // the lowest crossing over the tile (index order is lane-major, then
+  // group), else the highest element of positive weight
+  int pick = -1, last = -1;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int f = s.first[j];
+    if (f >= 0 && (pick < 0 || f < pick)) pick = f;
+    last = max(last, s.last[j]);
+  }
+  if (pick < 0) pick = last >= 0 ? last : 0;
   return static_cast<int>(static_cast<int64_t>(h.tile) * kSampleTile + pick);
 }
 
