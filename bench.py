@@ -389,9 +389,13 @@ def w_chain(W, args, torch, sv, synth, dev):
         if W in ("c3", "c3p"):
             return (int(np.mean([c.target.shape[0] * c.V * esz(c.t_kind) for c in sets])), "k_row_stats",
                     "every target row of every request, read once (the softmax statistics)")
-        # lazy statistics: the rounds read target rows 0..m of each request
-        nb = [int(((acc.astype(np.int64) + 1) * c.V * esz(c.t_kind)).sum()) for acc, c in zip(accepted, sets)]
-        return int(np.mean(nb)), "k_chain_stats", "target rows 0..m of each request (the rows its round reads)"
+        # lazy statistics: rows 0 and 1 are decided one by one (k_chain_stats,
+        # the timed kernel), so of the rows 0..m a round reads, it streams
+        # rows 0..min(m, 1); the later ones go to k_chain_stats_tail
+        nb = [int(((np.minimum(acc.astype(np.int64), 1) + 1) * c.V * esz(c.t_kind)).sum())
+              for acc, c in zip(accepted, sets)]
+        return (int(np.mean(nb)), "k_chain_stats",
+                "target rows 0..min(m, 1) of each request (the rows of its round decided one by one)")
 
     u0 = ci0.uniforms
     if philox:
@@ -672,13 +676,26 @@ def timeline_chain(S, D, n_stats, n_draw):
                 draw=_tl_draw(D[:n_draw], t0))
 
 
-def timeline_ragged(L, D, rows, per_row, n_draw):
+def timeline_ragged(L, D, rows, per_row, n_draw, n_tail=0):
     """Phases of the ragged step (lazy statistics, then the draw) from the
-    records of both kernels (us), row by row of the statistics grid."""
+    records of both kernels (us), row by row of the row-major statistics
+    grid, and the items of the later rows taken at once (n_tail records
+    after the grid's)."""
+    T = L[rows * per_row:rows * per_row + n_tail].astype(np.float64)
     L = L[:rows * per_row].astype(np.float64)
     t0 = L[:, 0][L[:, 0] > 0].min()
     L[L <= 0] = np.nan
     L = (L - t0) * TL_TICK_US
+    T[T <= 0] = np.nan
+    T = (T - t0) * TL_TICK_US
+    tail = None
+    if n_tail:
+        tail = dict(items=n_tail, start_first=round(float(np.nanmin(T[:, 0])), 2),
+                    start_last=round(float(np.nanmax(T[:, 0])), 2), start_at=_stats(T[:, 0]),
+                    item_us=_stats(T[:, 2] - T[:, 0]), word_at=_stats(T[:, 2]),
+                    last_word=round(float(np.nanmax(T[:, 2])), 2),
+                    rows_decided=int(np.isfinite(T[:, 3]).sum()),
+                    last_stamp=round(float(np.nanmax(T)), 2))
     out = []
     for i in range(rows):
         r = L[i * per_row:(i + 1) * per_row]
@@ -693,7 +710,7 @@ def timeline_ragged(L, D, rows, per_row, n_draw):
                 stats=dict(last_start=round(float(np.nanmax(L[:, 0])), 2),
                            last_stamp=round(float(np.nanmax(L)), 2),
                            blocks_not_loading=int(dead.sum()), rows=out),
-                draw=_tl_draw(D[:n_draw], t0))
+                tail=tail, draw=_tl_draw(D[:n_draw], t0))
 
 
 def run_timeline(kind, args, torch, sv, synth, dev):
@@ -728,8 +745,10 @@ def run_timeline(kind, args, torch, sv, synth, dev):
         out = timeline_chain(recs[0], recs[1], n_stats, n_draw)
     else:
         per_row = w["B"] * ((w["cfg"]["vocab"] + 8191) // 8192)  # every block stamps its start
-        rows = int((recs[0][:, 0] > 0).sum()) // per_row
-        out = timeline_ragged(recs[0], recs[1], rows, per_row, int((recs[1][:, 0] > 0).sum()))
+        k_max = 8
+        rows = min(k_max + 1, 2)  # rows decided one by one; the later ones' items follow
+        n_tail = int((recs[0][rows * per_row:, 0] > 0).sum())
+        out = timeline_ragged(recs[0], recs[1], rows, per_row, int((recs[1][:, 0] > 0).sum()), n_tail)
     return dict(timeline=kind, workload=W, step="the last of 20 steps after the settle phase (records cleared before it)",
                 unit="us from the first block's start", **out)
 

@@ -176,9 +176,21 @@ sv_status launch_chain_call(int32_t t_dtype, int32_t q_dtype, sv::WalkArgs& a, v
     c.seg_words = reinterpret_cast<uint64_t*>(ws + L.segs_off);
     c.status = a.status;
     c.spin_limit = sv::kSpinLimit;
+    // rows 0 .. kLazyRows - 1 one by one, then the rest of every round still
+    // running at once (a fixed grid of blocks taking their segments in turn)
+    const int R = a.k_max + 1;
+    const bool tail = R > sv::kLazyRows && a.B <= sv::kMaxTailRequests;
+    c.row_hi = tail ? sv::kLazyRows : R;
+    c.row_lo = sv::kLazyRows;
     time_next_kernel();
     e = sv::launch_chain_stats(t_dtype, q_dtype, c, st);
     if (e != hipSuccess) return device_fail(e, what);
+    if (tail) {
+      const int64_t items = static_cast<int64_t>(a.B) * (R - sv::kLazyRows) * ((a.nseg + sv::kTailSegs - 1) / sv::kTailSegs);
+      e = sv::launch_chain_stats_tail(t_dtype, q_dtype, c,
+                                      std::min<int64_t>(items, 8 * static_cast<int64_t>(std::max(cu_count(), 1))), st);
+      if (e != hipSuccess) return device_fail(e, what);
+    }
   } else {
     const bool small = ntiles == 1;  // k_walk_small reads only the partials
     if (!small) time_next_kernel();

@@ -112,35 +112,28 @@ hipError_t launch_read_ceiling(const void* buf, int64_t bytes, uint32_t* out, hi
 // ---- the lazy statistics of the chain verify ----
 
 
-template <class DT, class DQ>
-__global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
-  __shared__ float sh[2 * (kBlock / kWave)];
-  __shared__ uint64_t s_w[kMaxChainSegs];
-  __shared__ int s_last;
-  const int64_t per_row = static_cast<int64_t>(a.B) * a.nseg;
-  const int i = static_cast<int>(blockIdx.x / per_row);
-  const int64_t rem = blockIdx.x - static_cast<int64_t>(i) * per_row;
-  const int b = static_cast<int>(rem / a.nseg);
-  const int seg = static_cast<int>(rem - static_cast<int64_t>(b) * a.nseg);
-  const int R = a.k_max + 1;
-  uint32_t* stop = a.stop + b;
-  if (threadIdx.x == 0) SV_STAMP(sv_timeline_lazy, blockIdx.x, 0);
-  // one round: the request's metadata and, past row 0, whether its round has
-  // already stopped at an earlier row
-  const int k = a.dlen[b];
-  const int ts = a.t_rs[b], qs = a.q_rs[b];
-  const uint32_t sv = i > 0 ? __hip_atomic_load(stop, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-  if (i > k || k > a.k_max || ts < 0 || static_cast<int64_t>(ts) + k >= a.t_rows ||
-      (k > 0 && (qs < 0 || static_cast<int64_t>(qs) + k > a.q_rows)))
-    return;  // no such row, or a request the draw reports as invalid
-  // Row i is not needed.  The stop word can change while the block's waves
-  // read it, so some waves may leave and the rest form a partial pair; that
-  // happens only once an earlier row has stopped the round, so row i's pair
-  // and decision are never used (the stop word keeps the earliest row).
-  if (sv > static_cast<uint32_t>(kMaxChainRows - i)) return;
-  if (threadIdx.x == 0) SV_STAMP(sv_timeline_lazy, blockIdx.x, 1);
+// Whether request b's metadata is usable (the draw reports the others);
+// k, ts, qs: its draft count and row starts.
+__device__ __forceinline__ bool chain_request_ok(const ChainStatsArgs& a, int b, int& k, int& ts, int& qs) {
+  k = a.dlen[b];
+  ts = a.t_rs[b];
+  qs = a.q_rs[b];
+  return !(k > a.k_max || k < 0 || ts < 0 || static_cast<int64_t>(ts) + k >= a.t_rows ||
+           (k > 0 && (qs < 0 || static_cast<int64_t>(qs) + k > a.q_rows)));
+}
 
-  // thread 0 fetches what the decision needs together with the segment
+// Segments seg .. seg + kN - 1 of target row i of request b (those before
+// nseg; a usable request, i <= k): their pairs go out as words and count on
+// the row's counter, and the row's last segment combines the row's pairs in
+// segment order and decides the row (the stop word keeps the earliest row
+// that stops).  Every thread of the block calls it; it returns in every
+// thread, wave 0 of the deciding block last.  sh: kN * 8 floats.
+template <class DT, class DQ, int kN = 1>
+__device__ __forceinline__ void chain_segment(const ChainStatsArgs& a, int i, int b, int seg, int k, int ts, int qs,
+                                              float* sh, uint64_t* s_w, int& s_last, int64_t rec) {
+  static_assert(kN >= 1 && kN <= 4, "one to four segments");
+  const int R = a.k_max + 1;
+  // thread 0 fetches what the decision needs together with the segments
   int x = -1;
   float lx = 0.f, qx = 0.f, u = 0.f;
   if (threadIdx.x == 0 && i < k) {
@@ -151,16 +144,25 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
       qx = DQ::at(row_ptr<DQ>(a.dq, qs + i, a.V), x);
     }
   }
-  // ordinary (not non-temporal) loads: the draw re-reads the break row, which
-  // the last-level cache then still holds
-  const MS t = segment_ms<DT, false>(row_ptr<DT>(a.tgt, ts + i, a.V), a.V, seg, a.nseg, a.c, sh);
+  // Rows decided one by one (kN = 1) are read with ordinary loads: most
+  // rounds break at them, and the draw's re-read of the break row then finds
+  // it in the last-level cache.  The later rows (read speculatively, kN > 1)
+  // are mostly not break rows and stream non-temporally.
+  MS t[kN];
+  if constexpr (kN == 1)
+    t[0] = segment_ms<DT, false>(row_ptr<DT>(a.tgt, ts + i, a.V), a.V, seg, a.nseg, a.c, sh);
+  else
+    segment_ms_n<DT, true, kN>(row_ptr<DT>(a.tgt, ts + i, a.V), a.V, seg, a.nseg, a.c, sh, t);
+  const int n = min(kN, a.nseg - seg);
   uint64_t* words = a.seg_words + (static_cast<int64_t>(b) * R + i) * a.nseg;
   if (threadIdx.x == 0) {
-    store_word(words + seg, enc_ms(t));
-    const uint32_t done = __hip_atomic_fetch_add(a.count + static_cast<int64_t>(b) * R + i, 1u,
+#pragma unroll
+    for (int j = 0; j < kN; ++j)
+      if (j < n) store_word(words + seg + j, enc_ms(t[j]));
+    const uint32_t done = __hip_atomic_fetch_add(a.count + static_cast<int64_t>(b) * R + i, static_cast<uint32_t>(n),
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = done == static_cast<uint32_t>(a.nseg - 1);
-    SV_STAMP(sv_timeline_lazy, blockIdx.x, 2);
+    s_last = done + n == static_cast<uint32_t>(a.nseg);
+    SV_STAMP(sv_timeline_lazy, rec, 2);
   }
   __syncthreads();
   if (!s_last || threadIdx.x >= kWave) return;
@@ -206,13 +208,117 @@ __global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
     }
   }
   if (stop_here)
-    __hip_atomic_fetch_max(stop, static_cast<uint32_t>(kMaxChainRows - i), __ATOMIC_RELAXED,
+    __hip_atomic_fetch_max(a.stop + b, static_cast<uint32_t>(kMaxChainRows - i), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-  SV_STAMP(sv_timeline_lazy, blockIdx.x, 3);
+  SV_STAMP(sv_timeline_lazy, rec, 3);
+}
+
+// Rows 0 .. a.row_hi - 1, one block per segment, row-major over requests (all
+// requests' row 0 first), so that a row's blocks mostly start after the
+// previous row's decision and skip their loads when the round has stopped.
+template <class DT, class DQ>
+__global__ __launch_bounds__(kBlock) void k_chain_stats(ChainStatsArgs a) {
+  __shared__ float sh[2 * (kBlock / kWave)];
+  __shared__ uint64_t s_w[kMaxChainSegs];
+  __shared__ int s_last;
+  const int64_t per_row = static_cast<int64_t>(a.B) * a.nseg;
+  const int i = static_cast<int>(blockIdx.x / per_row);
+  const int64_t rem = blockIdx.x - static_cast<int64_t>(i) * per_row;
+  const int b = static_cast<int>(rem / a.nseg);
+  const int seg = static_cast<int>(rem - static_cast<int64_t>(b) * a.nseg);
+  if (threadIdx.x == 0) SV_STAMP(sv_timeline_lazy, blockIdx.x, 0);
+  // one round: the request's metadata and, past row 0, whether its round has
+  // already stopped at an earlier row
+  int k, ts, qs;
+  const bool ok = chain_request_ok(a, b, k, ts, qs);
+  const uint32_t sv = i > 0 ? __hip_atomic_load(a.stop + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+  if (!ok || i > k) return;  // a request the draw reports as invalid, or no such row
+  // Row i is not needed.  The stop word can change while the block's waves
+  // read it, so some waves may leave and the rest form a partial pair; that
+  // happens only once an earlier row has stopped the round, so row i's pair
+  // and decision are never used (the stop word keeps the earliest row).
+  if (sv > static_cast<uint32_t>(kMaxChainRows - i)) return;
+  if (threadIdx.x == 0) SV_STAMP(sv_timeline_lazy, blockIdx.x, 1);
+  chain_segment<DT, DQ>(a, i, b, seg, k, ts, qs, sh, s_w, s_last, blockIdx.x);
+}
+
+// Rows a.row_lo .. k_b of every usable request whose round has not stopped
+// before row a.row_lo, all at once: the grid's blocks take the items
+// (request, row, kTailSegs consecutive segments), request-major, in turn.  Rows are decided
+// independently (a later row's decision may go unused); the stop word keeps
+// the earliest row that stops, so the outcome is the one of deciding them in
+// order.  Each block first lays out the items itself: the requests' row
+// counts and their exclusive scan, with their row starts, in LDS (B <=
+// kMaxTailRequests).  Stop words set during this kernel come from rows >=
+// a.row_lo, so every block sees the same requests running.
+template <class DT, class DQ>
+__global__ __launch_bounds__(kBlock) void k_chain_stats_tail(ChainStatsArgs a) {
+  __shared__ float sh[kTailSegs * 2 * (kBlock / kWave)];
+  __shared__ uint64_t s_w[kMaxChainSegs];
+  __shared__ int s_last;
+  __shared__ int32_t s_first[kMaxTailRequests + 1];  // first row slot of each request
+  __shared__ int2 s_rs[kMaxTailRequests];            // its target and draft row starts
+  __shared__ int32_t s_wsum[kBlock / kWave];
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const uint32_t running = static_cast<uint32_t>(kMaxChainRows - a.row_lo);  // stop words up to this
+  // each thread counts the rows of its requests b = per t .. per (t + 1) - 1
+  const int per = (a.B + kBlock - 1) / kBlock;
+  const int b0 = min(a.B, static_cast<int>(threadIdx.x) * per), b1 = min(a.B, b0 + per);
+  int mine = 0;
+  for (int b = b0; b < b1; ++b) {
+    int k, ts, qs;
+    const bool ok = chain_request_ok(a, b, k, ts, qs);
+    const uint32_t sv = __hip_atomic_load(a.stop + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int n = (ok && sv <= running && k >= a.row_lo) ? k - a.row_lo + 1 : 0;
+    s_first[b] = n;
+    s_rs[b] = int2{ts, qs};
+    mine += n;
+  }
+  // block-wide exclusive scan of the threads' counts
+  int incl = mine;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == kWave - 1) s_wsum[wid] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wid; ++w) base += s_wsum[w];
+  int run = base + incl - mine;
+  for (int b = b0; b < b1; ++b) {
+    const int n = s_first[b];
+    s_first[b] = run;
+    run += n;
+  }
+  if (threadIdx.x == kBlock - 1) s_first[a.B] = run;
+  __syncthreads();
+  const int npair = (a.nseg + kTailSegs - 1) / kTailSegs;
+  const int64_t total = static_cast<int64_t>(s_first[a.B]) * npair;
+  // time-line records of the items follow those of the row-major kernel
+  const int64_t rec0 = static_cast<int64_t>(a.row_hi) * a.B * a.nseg;
+  (void)rec0;
+  for (int64_t it = blockIdx.x; it < total; it += gridDim.x) {
+    if (threadIdx.x == 0) SV_STAMP(sv_timeline_lazy, rec0 + it, 0);
+    const int slot = static_cast<int>(it / npair);
+    const int seg = kTailSegs * static_cast<int>(it - static_cast<int64_t>(slot) * npair);
+    // the request owning row slot `slot`: the last b with s_first[b] <= slot
+    int lo = 0, hi = a.B - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_first[mid] <= slot) lo = mid; else hi = mid - 1;
+    }
+    const int b = lo;
+    const int i = a.row_lo + (slot - s_first[b]);
+    const int k = a.row_lo + (s_first[b + 1] - s_first[b]) - 1;  // rows row_lo .. k
+    const int2 rs = s_rs[b];
+    if (threadIdx.x == 0) SV_STAMP(sv_timeline_lazy, rec0 + it, 1);
+    chain_segment<DT, DQ, kTailSegs>(a, i, b, seg, k, rs.x, rs.y, sh, s_w, s_last, rec0 + it);
+  }
 }
 
 hipError_t launch_chain_stats(int t_dtype, int q_dtype, const ChainStatsArgs& a, hipStream_t stream) {
-  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.k_max + 1) * a.B * a.nseg)), block(kBlock);
+  const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.row_hi) * a.B * a.nseg)), block(kBlock);
   const bool tb = t_dtype == kDtypeBF16, qb = q_dtype == kDtypeBF16;
   if (tb && qb)
     launch_timed((k_chain_stats<BF16, BF16>), grid, block, 0, stream, a);
@@ -222,6 +328,22 @@ hipError_t launch_chain_stats(int t_dtype, int q_dtype, const ChainStatsArgs& a,
     launch_timed((k_chain_stats<F32, BF16>), grid, block, 0, stream, a);
   else
     launch_timed((k_chain_stats<F32, F32>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_chain_stats_tail(int t_dtype, int q_dtype, const ChainStatsArgs& a, int64_t blocks,
+                                   hipStream_t stream) {
+  if (a.B > kMaxTailRequests || blocks < 1) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<uint32_t>(blocks)), block(kBlock);
+  const bool tb = t_dtype == kDtypeBF16, qb = q_dtype == kDtypeBF16;
+  if (tb && qb)
+    launch_timed((k_chain_stats_tail<BF16, BF16>), grid, block, 0, stream, a);
+  else if (tb)
+    launch_timed((k_chain_stats_tail<BF16, F32>), grid, block, 0, stream, a);
+  else if (qb)
+    launch_timed((k_chain_stats_tail<F32, BF16>), grid, block, 0, stream, a);
+  else
+    launch_timed((k_chain_stats_tail<F32, F32>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

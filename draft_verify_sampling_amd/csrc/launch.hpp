@@ -131,6 +131,8 @@ struct ChainStatsArgs {
   const float* u;        // [B, k_max + 1], or null: Philox stream (seed, offset)
   uint64_t seed, offset;
   int32_t nseg;
+  int32_t row_hi;        // k_chain_stats: rows 0 .. row_hi - 1
+  int32_t row_lo;        // k_chain_stats_tail: rows row_lo .. k_b
   uint32_t* stop;        // [B] kMaxChainRows - (first row that stops the round); 0: none
   uint32_t* count;       // [B, R] finished segments
   uint64_t* row_words;   // [B, R] row pairs
@@ -140,6 +142,16 @@ struct ChainStatsArgs {
 };
 
 hipError_t launch_chain_stats(int t_dtype, int q_dtype, const ChainStatsArgs& a, hipStream_t stream);
+// The rows from row_lo on of the requests still running, `blocks` blocks
+// taking the items (kTailSegs segments of a row each) in turn (B <=
+// kMaxTailRequests).
+constexpr int kMaxTailRequests = 1024;
+// Rows decided one by one (row-major blocks) before the rest of a lazy round
+// go at once.
+constexpr int kLazyRows = 2;
+constexpr int kTailSegs = 4;  // segments per item of the rows after them
+hipError_t launch_chain_stats_tail(int t_dtype, int q_dtype, const ChainStatsArgs& a, int64_t blocks,
+                                   hipStream_t stream);
 
 // ---- the draw of a sampled chain round (k_chain_draw) ----
 // After the statistics kernel: the break row, the residual pass over it and

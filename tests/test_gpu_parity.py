@@ -257,9 +257,9 @@ def test_gpu_sample_c4_full(c4):
     assert int(st.item()) == 0
 
 
-def _edge_batch(B):
+def _edge_batch(B, V=5000):
     """Requests 0..12 are the edge cases below; the rest are ordinary rounds."""
-    V, k = 5000, 3
+    k = 3
     ks = np.full(B, 3, dtype=np.int32)
     ks[[0, 10]] = [0, 2]
     ci = synth.sampled_chain(90, B, ks, V, 1.0, sd=2.0, n_boost=3, boost=5.0, sigma=1.0, kind="f32")
@@ -299,11 +299,13 @@ def _edge_batch(B):
     return ci, max_new, eos
 
 
-@pytest.mark.parametrize("B", [13, 4200])
-def test_gpu_sample_edge_cases(B):
-    # B = 4200 has enough statistics blocks per row for the lazy statistics
-    say(f"sampled chain edge cases, B={B}")
-    ci, max_new, eos = _edge_batch(B)
+@pytest.mark.parametrize("B,V", [(13, 5000), (4200, 5000), (900, 40_000)])
+def test_gpu_sample_edge_cases(B, V):
+    # B = 4200 (one segment a row) and B = 900 (five) have enough statistics
+    # blocks per row for the lazy statistics; with B = 900 rows 2 and 3 go to
+    # the kernel that reads every remaining row of the running rounds at once
+    say(f"sampled chain edge cases, B={B}, V={V}")
+    ci, max_new, eos = _edge_batch(B, V)
     seen = {}
     for mn, eo, dg in ((None, -1, True), (max_new, eos, True), (None, -1, False), (max_new, eos, False)):
         st = _status()
