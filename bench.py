@@ -783,6 +783,9 @@ TIMELINE_LEGEND = {
         "= blocks that left without streaming (row past the request's draft length, or its round stopped)",
         "stats.rows: per row of the grid: its blocks, those that streamed their segment, the first and "
         "last block starts, the last streaming block's word stored, and the requests whose row was decided",
+        "tail: the kernel that reads rows 2..k_b of the rounds still running at once (items of four "
+        "segments of a row): its items' starts, item_us = start to word stored, word_at = when, and the "
+        "rows it decided",
         "draw: as for the headline chain's draw (break row, tiles, count; the last block's gather, tile "
         "search, pick and writes)"]}
 
