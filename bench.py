@@ -61,16 +61,29 @@ MAX_POOL = 16  # the host cores one GPU's share of the machine has
 TIMING = ("inside {n} steps like the timed ones: HIP events handed to the kernel's launch on the step's stream "
           "(the kernel's own start and end)")
 CSRC = os.path.join(ROOT, "draft_verify_sampling_amd", "csrc")
-COMMON_SRCS = ["common.hpp", "words.hpp", "launch.hpp", "tiles.hpp", "segment.hpp", "timeline.hpp"]
-# the sources a kernel is compiled from: its counter summary holds while
-# their code is unchanged
+# the source a kernel is compiled from: its counter summary holds while the
+# code of that file and of the headers it includes (transitively) is unchanged
 KERNEL_SRCS = {
-    "k_row_stats": ["k_stats.hip"],
-    "k_chain_stats": ["k_stats.hip"],
-    "k_read_ceiling": ["k_stats.hip"],
-    "k_row_argmax": ["k_greedy.hip"],
-    "k_walk": ["k_walk.hip"],
+    "k_row_stats": "k_stats.hip",
+    "k_chain_stats": "k_stats.hip",
+    "k_read_ceiling": "k_stats.hip",
+    "k_row_argmax": "k_greedy.hip",
+    "k_walk": "k_walk.hip",
 }
+
+
+def source_files(src):
+    """`src` and the csrc headers it includes, transitively, in first-include
+    order (each once)."""
+    out, todo = [], [src]
+    while todo:
+        f = todo.pop(0)
+        if f in out or not os.path.exists(os.path.join(CSRC, f)):
+            continue
+        out.append(f)
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            todo += re.findall(r'^\s*#include\s+"([^"]+)"', fh.read(), flags=re.M)
+    return out
 
 
 def _code_only(text):
@@ -86,7 +99,7 @@ def source_hash(kernel):
     """sha1 of the code (comments and blank space stripped) of the sources the
     kernel is compiled from."""
     h = hashlib.sha1()
-    for f in KERNEL_SRCS[kernel] + COMMON_SRCS:
+    for f in source_files(KERNEL_SRCS[kernel]):
         with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
             h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
