@@ -141,7 +141,7 @@ sv_status launch_chain_call(int32_t t_dtype, int32_t q_dtype, sv::WalkArgs& a, v
   float2* partial = reinterpret_cast<float2*>(ws + L.partial_off);
   // tiles per wave of the draw: the fewest that keep every draw block resident
   // at once (each block pays its prologue's load rounds once)
-  const size_t draw_lds = static_cast<size_t>(ntiles) * 2 * sizeof(double);
+  const size_t draw_lds = static_cast<size_t>(ntiles) * sizeof(double);
   const int64_t resident =
       static_cast<int64_t>(sv::draw_occupancy(t_dtype, q_dtype, draw_lds)) * std::max(cu_count(), 1);
   const int64_t quads = (ntiles + sv::kDrawTiles - 1) / sv::kDrawTiles;

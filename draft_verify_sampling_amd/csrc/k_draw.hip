@@ -142,27 +142,51 @@ __device__ BreakRow break_from_partials(const ChainDrawArgs& a, int b, int k, in
   return br;
 }
 
-// The last block's wave 0: gathers the request's tile sums and block classes,
-// totals them (W, with the fallback to p when the residual has no mass) and
-// finds the tile holding u_k W.  Returns 0 when the request's outputs are
-// already written (invalid) or the gather timed out, else 1 (pick from the
-// residual) or 2 (from p), with the tile and the target in s_hit, s_target.
+// Wave 0 of the last block: the tile holding u_k W among the tile sums
+// s_tw[0, ntiles) (mine: the lane's own sum over lane_tiles, in order).
+// Returns 1, or 0 when no tile has weight (the outputs are then written).
+__device__ __forceinline__ int last_block_pick_tile(const ChainDrawArgs& a, int b, int k, float u0,
+                                                    const double* s_tw, double mine, double W, int bits,
+                                                    TileHit& s_hit, double& s_target) {
+  const int lane = threadIdx.x & (kWave - 1);
+  // the last token's uniform: lane k of this wave loaded it at the start
+  const float uk = k < kWave ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u0), k))
+                             : slot_uniform(a.u, a.seed, a.offset, b, a.k_max + 1, k);
+  const double target = static_cast<double>(uk) * W;
+  TileHit hit;
+  if (!wave_find_tile(s_tw, 1, a.ntiles, mine, target, hit)) {
+    draw_invalid(a, b, kFlagNonfinite | bits);
+    return 0;
+  }
+  if (lane == 0) {
+    s_hit = hit;
+    s_target = target;
+    SV_STAMP(sv_timeline_draw, blockIdx.x, 5);
+  }
+  return 1;
+}
+
+// The last block's wave 0: gathers the request's tile sums of the draw
+// weights and the block classes, and totals them (W).  Returns 0 when the
+// request's outputs are already written (invalid) or the gather timed out,
+// 3 when the residual has no mass (the caller then sums p over the row, the
+// zero-mass fallback), else 1 after finding the tile holding u_k W (s_hit,
+// s_target).  s_tw[t]: the tile sums (the first ntiles doubles).
 template <class DT, class DQ>
 __device__ __forceinline__ int last_block_find(const ChainDrawArgs& a, int b, int k, int extra, float u0,
-                                               bool resid, double* s_tw, DrawRow& row, int& bits, double& W,
+                                               bool resid, double* s_tw, int& bits, double& W,
                                                TileHit& s_hit, double& s_target) {
   const int lane = threadIdx.x & (kWave - 1);
   const uint64_t* tw = a.tile_w + static_cast<int64_t>(b) * a.ntiles;
-  const uint64_t* tp = a.tile_p + static_cast<int64_t>(b) * a.ntiles;
   const uint64_t* bq = a.blk_q + static_cast<int64_t>(b) * a.nblk;
   int ta, tb;
   lane_tiles(a.ntiles, lane, ta, tb);
   constexpr int kBatch = 4;
-  double wsum = 0.0, psum = 0.0;
+  double wsum = 0.0;
   uint64_t cls = 0;
   bool ok = true;
   for (int t0 = ta, first = 1; ok && (t0 < tb || first); t0 += kBatch, first = 0) {
-    uint64_t vw[kBatch], vp[kBatch], vq = kValid;
+    uint64_t vw[kBatch], vq = kValid;
     int it = 0;
     for (; it < a.spin_limit; ++it) {
       bool mine = true;
@@ -175,12 +199,9 @@ __device__ __forceinline__ int last_block_find(const ChainDrawArgs& a, int b, in
       }
 #pragma unroll
       for (int x = 0; x < kBatch; ++x) {
-        vw[x] = vp[x] = kValid;
-        if (t0 + x < tb) {
-          vw[x] = load_word(tw + t0 + x);
-          vp[x] = load_word(tp + t0 + x);
-        }
-        mine = mine && (vw[x] & kValid) && (vp[x] & kValid);
+        vw[x] = kValid;
+        if (t0 + x < tb) vw[x] = load_word(tw + t0 + x);
+        mine = mine && (vw[x] & kValid);
       }
       if (__all(mine)) break;
       __builtin_amdgcn_s_sleep(1);
@@ -190,11 +211,9 @@ __device__ __forceinline__ int last_block_find(const ChainDrawArgs& a, int b, in
 #pragma unroll
     for (int x = 0; x < kBatch; ++x) {
       if (t0 + x < tb) {
-        const double dw = dec_sum(vw[x]), dp = dec_sum(vp[x]);
+        const double dw = dec_sum(vw[x]);
         s_tw[t0 + x] = dw;
-        s_tw[a.ntiles + t0 + x] = dp;
         wsum += dw;
-        psum += dp;
       }
     }
   }
@@ -207,40 +226,19 @@ __device__ __forceinline__ int last_block_find(const ChainDrawArgs& a, int b, in
     cls |= static_cast<uint64_t>(__shfl_xor(static_cast<long long>(cls), sft));
   W = wave_total(wsum);
   bits = extra;
-  const double* ts_w = s_tw;
-  double mine = wsum;
   if (resid) {
     if (qclass_nan(cls) || !isfinite(W)) {
       draw_invalid(a, b, kFlagNonfinite | extra);
       return 0;
     }
-    if (!(W > 0.0)) {  // no residual mass: draw from p_m
-      bits |= kFlagFallback;
-      row.use_q = false;
-      W = wave_total(psum);
-      ts_w = s_tw + a.ntiles;
-      mine = psum;
-    }
+    if (!(W > 0.0)) return 3;  // no residual mass: the row's p sums are needed
   }
-  // the last token's uniform: lane k of this wave loaded it at the start
-  const float uk = k < kWave ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(u0), k))
-                             : slot_uniform(a.u, a.seed, a.offset, b, a.k_max + 1, k);
-  const double target = static_cast<double>(uk) * W;
-  TileHit hit;
-  if (!wave_find_tile(ts_w, 1, a.ntiles, mine, target, hit)) {
-    draw_invalid(a, b, kFlagNonfinite | bits);
-    return 0;
-  }
-  if (lane == 0) {
-    s_hit = hit;
-    s_target = target;
-    SV_STAMP(sv_timeline_draw, blockIdx.x, 5);
-  }
-  return row.use_q ? 1 : 2;
+  return last_block_pick_tile(a, b, k, u0, s_tw, wsum, W, bits, s_hit, s_target);
 }
+
 }  // namespace
 
-// Dynamic LDS: the gathered tile sums, 2 x ntiles doubles (w, then p).
+// Dynamic LDS: the gathered tile sums, ntiles doubles.
 template <class DT, class DQ>
 __global__ __launch_bounds__(kBlock) void k_chain_draw(ChainDrawArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -308,20 +306,19 @@ __global__ __launch_bounds__(kBlock) void k_chain_draw(ChainDrawArgs a) {
               1.f / br.ps, 1.f, resid};
 
   // 2. the block's tiles, wave w taking tiles w, w + 4, ...: sums of
-  // max(0, p - q) (or p), of p, and of q
+  // max(0, p - q) (or p) and of q
   double qsum = 0.0;
   const int t_first = r * kDrawTiles * a.tpw;
   for (int i = 0; i < a.tpw; ++i) {
     const int t = t_first + i * kDrawTiles + wid;
     if (t >= a.ntiles) break;
     double v[1][3];
-    wave_tile_sums<DT, DQ, 1>(row, a.V, t, 0, v);
+    if (resid)
+      wave_tile_sums<DT, DQ, 1, true, 0, false, false, true>(row, a.V, t, 0, v);
+    else
+      wave_tile_sums<DT, DQ, 1, false, 0, false, false>(row, a.V, t, 0, v);
     qsum += v[0][2];
-    if (lane == 0) {
-      const int64_t o = static_cast<int64_t>(b) * a.ntiles + t;
-      store_word(a.tile_w + o, enc_sum(v[0][0]));
-      store_word(a.tile_p + o, enc_sum(v[0][1]));
-    }
+    if (lane == 0) store_word(a.tile_w + static_cast<int64_t>(b) * a.ntiles + t, enc_sum(v[0][0]));
   }
   if (lane == 0) s_q[wid] = enc_qclass(qsum);
   __syncthreads();
@@ -340,21 +337,44 @@ __global__ __launch_bounds__(kBlock) void k_chain_draw(ChainDrawArgs a) {
   // 3. the request's last block: wave 0 gathers the tile sums and the classes
   // of the draft row's block sums (loads in flight a batch at a time, waiting
   // only for their visibility), totals them and finds the tile; the block's
-  // four waves then pick the id in it.
+  // four waves then pick the id in it.  When the residual has no mass the
+  // four waves first sum p over the break row's tiles (the zero-mass
+  // fallback draws from p_m).
   __shared__ PickLds s_pick;
   __shared__ TileHit s_hit;
   __shared__ double s_target;
-  __shared__ int s_go;  // 0: done (invalid), 1: pick from the residual, 2: from p
+  __shared__ int s_go;  // 0: done (invalid), 1: pick from the row's weights, 2: from p_m, 3: p sums needed
   int bits = extra;
   double W = 0.0;
   if (wid == 0) {
-    const int go = last_block_find<DT, DQ>(a, b, k, extra, u0, resid, s_tw, row, bits, W, s_hit, s_target);
+    const int go = last_block_find<DT, DQ>(a, b, k, extra, u0, resid, s_tw, bits, W, s_hit, s_target);
     if (lane == 0) s_go = go;
   }
   __syncthreads();
+  if (s_go == 3) {
+    DrawRow prow = row;
+    prow.use_q = false;
+    for (int t = wid; t < a.ntiles; t += kDrawTiles) {
+      double v[1][3];
+      wave_tile_sums<DT, DQ, 1, false, 0, false, false>(prow, a.V, t, 0, v);
+      if (lane == 0) s_tw[t] = v[0][0];
+    }
+    __syncthreads();
+    if (wid == 0) {
+      int ta, tb;
+      lane_tiles(a.ntiles, lane, ta, tb);
+      double psum = 0.0;
+      for (int t = ta; t < tb; ++t) psum += s_tw[t];
+      bits |= kFlagFallback;
+      W = wave_total(psum);
+      const int go = last_block_pick_tile(a, b, k, u0, s_tw, psum, W, bits, s_hit, s_target);
+      if (lane == 0) s_go = go == 1 ? 2 : 0;
+    }
+    __syncthreads();
+  }
   const int go = s_go;
   if (go == 0) return;
-  row.use_q = go == 1;
+  if (go == 2) row.use_q = false;  // the zero-mass fallback draws from p_m
   const int y = block_pick_in_tile<DT, DQ>(row, a.V, s_hit, s_target, s_pick);
   if (wid != 0) return;
   if (lane == 0) SV_STAMP(sv_timeline_draw, blockIdx.x, 6);
@@ -412,7 +432,7 @@ int draw_occupancy(int t_dtype, int q_dtype, size_t lds) {
 
 hipError_t launch_chain_draw(int t_dtype, int q_dtype, const ChainDrawArgs& a, hipStream_t stream) {
   const dim3 grid(static_cast<uint32_t>(static_cast<int64_t>(a.B) * a.nblk)), block(kBlock);
-  const size_t lds = static_cast<size_t>(a.ntiles) * 2 * sizeof(double);
+  const size_t lds = static_cast<size_t>(a.ntiles) * sizeof(double);
   const bool tb = t_dtype == kDtypeBF16, qb = q_dtype == kDtypeBF16;
   if (tb && qb)
     hipLaunchKernelGGL((k_chain_draw<BF16, BF16>), grid, block, lds, stream, a);

@@ -118,14 +118,16 @@ struct TileCache {
 // end cuts (rows whose length is not a multiple of the vector width) and
 // unaligned rows take element loads.
 // kFill: also leave the tile's p and q in `cache` (residual passes only).
-template <class DT, class DQ, bool kQ = true, bool kFill = false>
+// kPSum false: the p sum is not formed (v[1] = 0).  kQAlways: the row is a
+// residual row (r.use_q holds), so w = max(0, p - coef q) without a select.
+template <class DT, class DQ, bool kQ = true, bool kFill = false, bool kPSum = true, bool kQAlways = false>
 __device__ __forceinline__ void wave_tile_sums_any(const DrawRow& r, int64_t V, int t, double* v,
                                                    TileCache<DT, DQ> cache = {}) {
   using L = TileRuns<DT, DQ>;
   constexpr int kPer = L::kPer;
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t t0 = static_cast<int64_t>(t) * kSampleTile;
-  const bool use_q = kQ && r.use_q;
+  const bool use_q = kQ && (kQAlways || r.use_q);
   const bool al = aligned16<DT>(r.t, t0) && (!use_q || aligned16<DQ>(r.q, t0));
   float ws = 0.f, ps = 0.f, qs = 0.f;
   constexpr int kAB = (L::nt + L::nq == 2) ? 4 : 2;  // runs per load round (<= 8 vectors)
@@ -173,11 +175,11 @@ __device__ __forceinline__ void wave_tile_sums_any(const DrawRow& r, int64_t V, 
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
         p[j] = draw_p(r, l[j]);
-        w[j] = draw_w(r, p[j], q[j]);
+        w[j] = kQAlways ? fmaxf(fmaf(-r.coef, q[j], p[j]), 0.f) : draw_w(r, p[j], q[j]);
       }
       if constexpr (kFill) cache.put(k0 + kk, lane, p, q);
       ws += pairwise<kPer>(w);
-      ps += pairwise<kPer>(p);
+      if constexpr (kPSum) ps += pairwise<kPer>(p);
       qs += pairwise<kPer>(q);
     }
     }
@@ -197,11 +199,11 @@ __device__ __forceinline__ void wave_tile_sums_any(const DrawRow& r, int64_t V, 
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
         p[j] = draw_p(r, l[j]);
-        w[j] = draw_w(r, p[j], q[j]);
+        w[j] = kQAlways ? fmaxf(fmaf(-r.coef, q[j], p[j]), 0.f) : draw_w(r, p[j], q[j]);
       }
       if constexpr (kFill) cache.put(k, lane, p, q);
       ws += pairwise<kPer>(w);
-      ps += pairwise<kPer>(p);
+      if constexpr (kPSum) ps += pairwise<kPer>(p);
       qs += pairwise<kPer>(q);
     }
   }
@@ -211,7 +213,7 @@ __device__ __forceinline__ void wave_tile_sums_any(const DrawRow& r, int64_t V, 
       if (t0 + static_cast<int64_t>(k * kWave + lane) * kPer >= V) cache.put_zero(k, lane);
   }
   v[0] = wave_total(static_cast<double>(ws));
-  v[1] = wave_total(static_cast<double>(ps));
+  v[1] = kPSum ? wave_total(static_cast<double>(ps)) : 0.0;
   v[2] = wave_total(static_cast<double>(qs));
 }
 
@@ -222,8 +224,10 @@ __device__ __forceinline__ void wave_tile_sums_any(const DrawRow& r, int64_t V, 
 // kMaxBatch (0: up to 16 vectors) caps the runs whose loads are in flight
 // together, for callers that must keep registers low; the runs are summed in
 // the same order either way, so the sums are the same bits.  kFill (one tile):
-// also leave the tile's p and q in `cache`.
-template <class DT, class DQ, int kT, bool kQ = true, int kMaxBatch = 0, bool kFill = false>
+// also leave the tile's p and q in `cache`.  kPSum, kQAlways: as for
+// wave_tile_sums_any.
+template <class DT, class DQ, int kT, bool kQ = true, int kMaxBatch = 0, bool kFill = false, bool kPSum = true,
+          bool kQAlways = false>
 __device__ __forceinline__ void wave_tile_sums(const DrawRow& r, int64_t V, int t, int tstride,
                                                double (*v)[3], TileCache<DT, DQ> cache = {}) {
   static_assert(!kFill || kT == 1, "the cache holds one tile");
@@ -236,12 +240,13 @@ __device__ __forceinline__ void wave_tile_sums(const DrawRow& r, int64_t V, int 
   static_assert(kAll % kBatch == 0, "whole batches");
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t tlast = static_cast<int64_t>(t + (kT - 1) * tstride);
-  const bool use_q = kQ && r.use_q;
+  const bool use_q = kQ && (kQAlways || r.use_q);
   const bool fast = (tlast + 1) * kSampleTile <= V && aligned16<DT>(r.t, 0) &&
                     (!use_q || aligned16<DQ>(r.q, 0));
   if (!fast) {
 #pragma unroll 1
-    for (int i = 0; i < kT; ++i) wave_tile_sums_any<DT, DQ, kQ, kFill>(r, V, t + i * tstride, v[i], cache);
+    for (int i = 0; i < kT; ++i)
+      wave_tile_sums_any<DT, DQ, kQ, kFill, kPSum, kQAlways>(r, V, t + i * tstride, v[i], cache);
     return;
   }
   float ws[kT], ps[kT], qs[kT];
@@ -279,18 +284,18 @@ __device__ __forceinline__ void wave_tile_sums(const DrawRow& r, int64_t V, int 
 #pragma unroll
       for (int j = 0; j < kPer; ++j) {
         p[j] = draw_p(r, l[j]);
-        w[j] = draw_w(r, p[j], q[j]);
+        w[j] = kQAlways ? fmaxf(fmaf(-r.coef, q[j], p[j]), 0.f) : draw_w(r, p[j], q[j]);
       }
       if constexpr (kFill) cache.put(r0 + k, lane, p, q);
       ws[ti] += pairwise<kPer>(w);
-      ps[ti] += pairwise<kPer>(p);
+      if constexpr (kPSum) ps[ti] += pairwise<kPer>(p);
       qs[ti] += pairwise<kPer>(q);
     }
   }
 #pragma unroll
   for (int i = 0; i < kT; ++i) {
     v[i][0] = wave_total(static_cast<double>(ws[i]));
-    v[i][1] = wave_total(static_cast<double>(ps[i]));
+    v[i][1] = kPSum ? wave_total(static_cast<double>(ps[i])) : 0.0;
     v[i][2] = wave_total(static_cast<double>(qs[i]));
   }
 }
