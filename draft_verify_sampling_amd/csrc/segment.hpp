@@ -64,13 +64,21 @@ __device__ __forceinline__ MS segment_fold(const void* base, int64_t V, const Ro
   const int64_t v0 = static_cast<int64_t>(seg) * kSegVecs + threadIdx.x;
   MS acc{-INFINITY, 0.f};
   {
+    // only a segment that reaches past the row's vectors masks them (a
+    // block-uniform test, so full segments carry no per-element select)
+    const bool full = static_cast<int64_t>(seg + 1) * kSegVecs <= r.nvec;
     float x[U * D::kPerVec];
+    if (full) {
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      D::unpack(sh.w[j], x + j * D::kPerVec);
-      if (v0 + j * kBlock >= r.nvec) {
+      for (int j = 0; j < U; ++j) D::unpack(sh.w[j], x + j * D::kPerVec);
+    } else {
 #pragma unroll
-        for (int t = 0; t < D::kPerVec; ++t) x[j * D::kPerVec + t] = -INFINITY;
+      for (int j = 0; j < U; ++j) {
+        D::unpack(sh.w[j], x + j * D::kPerVec);
+        if (v0 + j * kBlock >= r.nvec) {
+#pragma unroll
+          for (int t = 0; t < D::kPerVec; ++t) x[j * D::kPerVec + t] = -INFINITY;
+        }
       }
     }
     ms_fold<U * D::kPerVec>(acc, x, c);
