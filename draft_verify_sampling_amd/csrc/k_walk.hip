@@ -193,7 +193,9 @@ constexpr int kCacheNone = 0, kCacheFill = 1, kCacheUse = 2;
 // copy (tile i: p, then q) and *qcls the draft-sum class word of this
 // workgroup's slice, stored by the fill and sent again by later passes (the
 // draft row is the same, so is its class).
-template <class DT, class DQ, bool kQ = true, int kCache = kCacheNone>
+// kResid: a residual pass (r.use_q holds): the weights take the draft row
+// without a per-element select.  (No pass reads the p sums, so none forms them.)
+template <class DT, class DQ, bool kQ = true, int kCache = kCacheNone, bool kResid = false>
 __device__ __forceinline__ bool weight_pass(Walk& wk, const DrawRow& r, double* wt, double* s_wq, double& W, bool& qnan,
                                             float4* cache = nullptr, uint64_t* qcls = nullptr) {
   const WalkArgs& a = *wk.a;
@@ -213,7 +215,7 @@ __device__ __forceinline__ bool weight_pass(Walk& wk, const DrawRow& r, double* 
       if (lane == 0) wt[i] = s;
     } else {
       double v[1][3];
-      wave_tile_sums<DT, DQ, 1, kQ, 0, kCache == kCacheFill>(r, a.V, t, 0, v, tc);
+      wave_tile_sums<DT, DQ, 1, kQ, 0, kCache == kCacheFill, false, kResid>(r, a.V, t, 0, v, tc);
       if (lane == 0) wt[i] = v[0][0];
       qw += v[0][2];
     }
@@ -558,12 +560,12 @@ __global__ __launch_bounds__(kWalkBlock) void k_walk(WalkArgs a) {
           double* wt = nb ? s_wt1 : s_wt0;
           bool passed;
           if (a.cache == 0) {
-            passed = weight_pass<DT, DQ>(wk, rr, wt, s_wq, W, qnan);
+            passed = weight_pass<DT, DQ, true, kCacheNone, true>(wk, rr, wt, s_wq, W, qnan);
           } else if (!cached) {
-            passed = weight_pass<DT, DQ, true, kCacheFill>(wk, rr, wt, s_wq, W, qnan, s_cache, &own_qcls);
+            passed = weight_pass<DT, DQ, true, kCacheFill, true>(wk, rr, wt, s_wq, W, qnan, s_cache, &own_qcls);
             cached = true;
           } else {
-            passed = weight_pass<DT, DQ, true, kCacheUse>(wk, rr, wt, s_wq, W, qnan, s_cache, &own_qcls);
+            passed = weight_pass<DT, DQ, true, kCacheUse, true>(wk, rr, wt, s_wq, W, qnan, s_cache, &own_qcls);
           }
           if (!passed) {
             synced = false;
