@@ -329,6 +329,33 @@ def test_gpu_sample_edge_cases(B, V):
     assert fl[12] == 0 and want["accepted"][12] == 0 and got["count"][12] == 1
 
 
+@pytest.mark.parametrize("V", [151_936, 248_320])
+def test_gpu_sample_zero_mass_fallback_bf16(V):
+    """bf16 rows at the large vocabularies: a draft row of all ones (q >= p
+    everywhere) leaves the residual without mass, so the last token is drawn
+    from p of the break row (the request's last draw block sums p over every
+    tile of that row: 75 or 122 tiles)."""
+    say(f"zero-mass residual fallback, bf16, V={V}")
+    B = 24
+    ci = synth.sampled_chain(93, B, np.full(B, 2, dtype=np.int32), V, 1.0, sd=2.0, n_boost=3, boost=5.0,
+                             sigma=1.0, kind="bf16")
+    one = 0x3F80                                      # 1.0 in bfloat16
+    for b in range(8):                                # break at row 0
+        ci.draft[ci.q_row_start[b]] = one
+        ci.uniforms[b, 0] = 0.99
+    for b in range(8, 12):                            # draft 0 kept, break at row 1
+        ci.uniforms[b, 0] = 0.0
+        ci.draft[ci.q_row_start[b] + 1] = one
+        ci.uniforms[b, 1] = 0.99
+    want = _oracle_sample(ci)
+    assert all(f & oracle.FLAG_FALLBACK for f in want["flags"][:12])
+    for dg in (True, False):
+        st = _status()
+        got = run_sample(ci, status=st, diag=dg)
+        _check_chain(ci, got, want, f"fallback V={V}")
+        assert int(st.item()) == _or(want["flags"])
+
+
 def test_gpu_greedy_equals_sampling_on_one_hot():
     say("one-hot targets: sampled == greedy")
     rng = np.random.default_rng(31)
