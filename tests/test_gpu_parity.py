@@ -299,11 +299,13 @@ def _edge_batch(B, V=5000):
     return ci, max_new, eos
 
 
-@pytest.mark.parametrize("B,V", [(13, 5000), (4200, 5000), (900, 40_000)])
+@pytest.mark.parametrize("B,V", [(13, 5000), (4200, 5000), (900, 40_000), (1024, 40_000), (1025, 40_000)])
 def test_gpu_sample_edge_cases(B, V):
-    # B = 4200 (one segment a row) and B = 900 (five) have enough statistics
-    # blocks per row for the lazy statistics; with B = 900 rows 2 and 3 go to
-    # the kernel that reads every remaining row of the running rounds at once
+    # B = 4200 (one segment a row) and B = 900 or more (five) have enough
+    # statistics blocks per row for the lazy statistics; with B = 900 and
+    # 1024 (the most requests its LDS layout holds) rows 2 and 3 go to the
+    # kernel that reads every remaining row of the running rounds at once,
+    # with B = 1025 every row is decided row-major
     say(f"sampled chain edge cases, B={B}, V={V}")
     ci, max_new, eos = _edge_batch(B, V)
     seen = {}
